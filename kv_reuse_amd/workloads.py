@@ -1,0 +1,203 @@
+"""Seeded synthetic inputs for the HySparse2 Cross-Decoder hot path.
+
+This module only *builds inputs*: it draws seeded random tensors, plants
+"needle" keys, adds the slow drift or the heavy tail that a workload asks for,
+and rounds everything to bfloat16 bit patterns.  It computes nothing that the
+method computes (no attention, no softmax, no selection), so that both the CPU
+oracle and the HIP path can take their inputs from here without sharing any
+of the method's arithmetic.
+
+The five named workloads follow the five benchmark shapes of the project
+(decode at 2K / 32K / 256K / 1M context and a 4096-token prefill chunk over a
+128K context).  The needles stand in for the retrieval structure ("the needle
+in the haystack") that the news page "两天两连更：小米提前亮出V3底牌"
+describes in its section "Token级选择：精准定位大海里的那根针"; the long-context
+benchmarks that page reports on are not available and are not reproduced.
+
+Recipe (the same for every workload; sizes per workload below):
+
+* one ``numpy.random.SeedSequence(seed)`` spawns independent child streams in
+  this fixed order: q_full, k, v, needle positions, drift, heavy-tail
+  positions, then one stream per sparse layer for q_sparse[n];
+* every tensor entry is a float32 standard normal, rounded to bfloat16 with
+  round-to-nearest-even;
+* drift (256K workload): per (batch, kv head, dim) a random walk along the
+  sequence with N(0, sd^2) steps, added to the N(0,1) draw before rounding;
+* heavy tail (1M workload): round(frac * S) key rows per (batch, kv head),
+  drawn without replacement, are multiplied by ``heavy_mult`` before rounding;
+* needles (decode): ``n_needles`` positions per (batch, kv head) drawn
+  uniformly without replacement from [0, S); each such key row is set to
+  bf16(4 * mean over the group's query heads of q_full) (mean in float64 over
+  the bf16 query values, rounded float64 -> float32 -> bf16).  Needles are
+  written last and overwrite drift / heavy-tail rows;
+* needles (prefill chunk): needle i draws a query token t_i uniformly in
+  [0, T) and a position p_i uniformly in [0, P_{t_i} - w + 1) (an older token
+  that query t_i may select), and sets K[b, g, p_i] = bf16(4 * mean of that
+  token's group queries).
+"""
+from __future__ import annotations
+
+import dataclasses
+from dataclasses import dataclass
+from typing import Dict, Optional
+
+import numpy as np
+
+BASE_SEED = 20260900
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    n_q_tokens: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    ctx_len: int
+    n_sparse_layers: int
+    top_k: int = 1024
+    window: int = 128
+    n_needles: int = 0          # per (batch, kv head)
+    drift_sd: float = 0.0       # random-walk step sd along the sequence
+    heavy_frac: float = 0.0     # fraction of key rows scaled by heavy_mult
+    heavy_mult: float = 3.0
+    needle_scale: float = 4.0
+    config_id: int = 0          # seed offset
+
+    @property
+    def group(self) -> int:
+        return self.n_q_heads // self.n_kv_heads
+
+    @property
+    def scale(self) -> float:
+        return float(1.0 / np.sqrt(self.head_dim))
+
+    @property
+    def seed(self) -> int:
+        return BASE_SEED + self.config_id
+
+    def positions(self) -> np.ndarray:
+        """Position P_t of each query token: the chunk is the last T tokens."""
+        return self.ctx_len - self.n_q_tokens + np.arange(self.n_q_tokens, dtype=np.int64)
+
+    def rows(self) -> int:
+        return self.batch * self.n_q_tokens * self.n_kv_heads
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS: Dict[str, Workload] = {
+    "decode_2k_b4": Workload(
+        name="decode_2k_b4", batch=4, n_q_tokens=1, n_q_heads=16, n_kv_heads=2,
+        head_dim=128, ctx_len=2048, n_sparse_layers=3, n_needles=16, config_id=1),
+    "decode_32k_b16": Workload(
+        name="decode_32k_b16", batch=16, n_q_tokens=1, n_q_heads=32, n_kv_heads=4,
+        head_dim=128, ctx_len=32768, n_sparse_layers=4, n_needles=64, config_id=2),
+    "decode_256k_b4_drift": Workload(
+        name="decode_256k_b4_drift", batch=4, n_q_tokens=1, n_q_heads=32, n_kv_heads=4,
+        head_dim=128, ctx_len=262144, n_sparse_layers=4, n_needles=256, drift_sd=0.01,
+        config_id=3),
+    "decode_1m_b1_heavy": Workload(
+        name="decode_1m_b1_heavy", batch=1, n_q_tokens=1, n_q_heads=32, n_kv_heads=4,
+        head_dim=128, ctx_len=1048576, n_sparse_layers=8, n_needles=1024, heavy_frac=0.01,
+        config_id=4),
+    "prefill_4k_over_128k": Workload(
+        name="prefill_4k_over_128k", batch=1, n_q_tokens=4096, n_q_heads=32, n_kv_heads=4,
+        head_dim=128, ctx_len=131072, n_sparse_layers=4, n_needles=512, config_id=5),
+}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (round-to-nearest-even); return uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = u + (((u >> 16) & 1) + 0x7FFF)
+    return (u >> 16).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Exact widening of bfloat16 bit patterns to float32 (input construction only)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _normal_f32(rng: np.random.Generator, shape) -> np.ndarray:
+    return rng.standard_normal(size=shape, dtype=np.float32)
+
+
+def generate(w: Workload, seed: Optional[int] = None,
+             with_sparse: bool = True) -> Dict[str, np.ndarray]:
+    """Build the inputs of one workload as bf16 bit arrays (numpy uint16).
+
+    Returns a dict with
+      q_full   [B][T][Hq][D]
+      k, v     [B][Hkv][S][D]
+      q_sparse [N][B][T][Hq][D]   (if with_sparse)
+    """
+    seed = w.seed if seed is None else seed
+    B, T, Hq, Hkv, D, S, G = (w.batch, w.n_q_tokens, w.n_q_heads, w.n_kv_heads,
+                              w.head_dim, w.ctx_len, w.group)
+    if Hq % Hkv:
+        raise ValueError("n_q_heads must be a multiple of n_kv_heads")
+    children = np.random.SeedSequence(seed).spawn(6 + w.n_sparse_layers)
+    rq, rk, rv, rneedle, rdrift, rheavy = (np.random.Generator(np.random.PCG64(c))
+                                            for c in children[:6])
+
+    q_full = f32_to_bf16_bits(_normal_f32(rq, (B, T, Hq, D)))
+    k = np.empty((B, Hkv, S, D), dtype=np.uint16)
+    v = np.empty((B, Hkv, S, D), dtype=np.uint16)
+    for b in range(B):
+        for g in range(Hkv):
+            z = _normal_f32(rk, (S, D))
+            if w.drift_sd > 0.0:
+                steps = rdrift.standard_normal(size=(S, D)) * w.drift_sd
+                z = (z.astype(np.float64) + np.cumsum(steps, axis=0)).astype(np.float32)
+                del steps
+            if w.heavy_frac > 0.0:
+                n_heavy = int(round(w.heavy_frac * S))
+                pos = rheavy.choice(S, size=n_heavy, replace=False)
+                z[pos] *= np.float32(w.heavy_mult)
+            k[b, g] = f32_to_bf16_bits(z)
+            del z
+            v[b, g] = f32_to_bf16_bits(_normal_f32(rv, (S, D)))
+
+    if w.n_needles > 0:
+        qf = bf16_bits_to_f32(q_full).astype(np.float64)
+        pos_all = w.positions()
+        for b in range(B):
+            for g in range(Hkv):
+                heads = slice(g * G, (g + 1) * G)
+                if T == 1:
+                    n = min(w.n_needles, S)
+                    pos = rneedle.choice(S, size=n, replace=False)
+                    vec = w.needle_scale * qf[b, 0, heads, :].mean(axis=0)
+                    k[b, g, pos] = f32_to_bf16_bits(vec.astype(np.float32))[None, :]
+                else:
+                    for _ in range(w.n_needles):
+                        t = int(rneedle.integers(0, T))
+                        hi = int(pos_all[t]) - w.window + 1
+                        if hi <= 0:
+                            continue
+                        p = int(rneedle.integers(0, hi))
+                        vec = w.needle_scale * qf[b, t, heads, :].mean(axis=0)
+                        k[b, g, p] = f32_to_bf16_bits(vec.astype(np.float32))
+
+    out = {"q_full": q_full, "k": k, "v": v}
+    if with_sparse:
+        qs = np.empty((w.n_sparse_layers, B, T, Hq, D), dtype=np.uint16)
+        for n in range(w.n_sparse_layers):
+            r = np.random.Generator(np.random.PCG64(children[6 + n]))
+            qs[n] = f32_to_bf16_bits(_normal_f32(r, (B, T, Hq, D)))
+        out["q_sparse"] = qs
+    return out
+
+
+def small(name: str = "small", *, batch=1, n_q_tokens=1, n_q_heads=8, n_kv_heads=1,
+          head_dim=128, ctx_len=256, n_sparse_layers=2, top_k=16, window=8,
+          n_needles=0, drift_sd=0.0, heavy_frac=0.0, config_id=100) -> Workload:
+    """A small workload for tests (any shape the oracle finishes in seconds)."""
+    return Workload(name=name, batch=batch, n_q_tokens=n_q_tokens, n_q_heads=n_q_heads,
+                    n_kv_heads=n_kv_heads, head_dim=head_dim, ctx_len=ctx_len,
+                    n_sparse_layers=n_sparse_layers, top_k=top_k, window=window,
+                    n_needles=n_needles, drift_sd=drift_sd, heavy_frac=heavy_frac,
+                    config_id=config_id)

@@ -1,0 +1,274 @@
+"""Pins that tie the CPU oracle to something other than itself.
+
+Each pin takes the oracle module (so that the mutation test can hand in a copy
+with a planted mistake) and raises AssertionError when the oracle disagrees
+with a library routine, a closed form, a brute-force enumeration or an
+invariant that the mathematics fixes.  None of them retypes the oracle's own
+formula.
+"""
+from __future__ import annotations
+
+import itertools
+
+import numpy as np
+import torch
+from scipy.special import logsumexp
+
+from kv_reuse_amd import workloads as wl
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _bits(x):
+    return wl.f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def _f64(bits):
+    return wl.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def _sdpa(q, k, v, scale, mask=None):
+    """torch SDPA in float64 on CPU. q [H, Lq, D], k/v [H, Lk, D], mask [Lq, Lk] bool (True = keep)."""
+    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(a)) for a in (q, k, v))
+    m = None if mask is None else torch.from_numpy(mask)
+    return torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, attn_mask=m, scale=scale).numpy()
+
+
+# ---------------------------------------------------------------------------
+# full attention
+# ---------------------------------------------------------------------------
+
+def pin_full_attention_vs_sdpa(orc, seed=1):
+    """Whole step's full-attention output on a tiny GQA prefill chunk vs SDPA (float64)."""
+    w = wl.small(batch=2, n_q_tokens=3, n_q_heads=4, n_kv_heads=2, head_dim=8,
+                 ctx_len=11, n_sparse_layers=0, top_k=3, window=2, config_id=seed)
+    x = wl.generate(w, with_sparse=False)
+    res = orc.cross_decoder_step(x["q_full"], x["k"], x["v"], None, top_k=w.top_k,
+                                 window=w.window, scale=w.scale)
+    G = w.group
+    pos = w.positions()
+    for b in range(w.batch):
+        kk = np.repeat(_f64(x["k"][b]), G, axis=0)          # [Hq, S, D]
+        vv = np.repeat(_f64(x["v"][b]), G, axis=0)
+        q = _f64(x["q_full"][b]).transpose(1, 0, 2)         # [Hq, T, D]
+        mask = np.arange(w.ctx_len)[None, :] <= pos[:, None]
+        ref = _sdpa(q, kk, vv, w.scale, mask)               # [Hq, T, D]
+        for t in range(w.n_q_tokens):
+            for g in range(w.n_kv_heads):
+                got = res[(b, t, g)]["out_full"]
+                np.testing.assert_allclose(got, ref[g * G:(g + 1) * G, t], rtol=1e-10, atol=1e-12)
+                s = w.scale * (q[g * G:(g + 1) * G, t] @ kk[g * G, : pos[t] + 1].T)
+                np.testing.assert_allclose(res[(b, t, g)]["lse"], logsumexp(s, axis=1),
+                                           rtol=1e-12, atol=1e-12)
+
+
+def pin_attention_closed_forms(orc, seed=2):
+    r = _rng(seed)
+    G, n, D = 3, 9, 8
+    q = r.standard_normal((G, D))
+    k = r.standard_normal((n, D))
+    # constant V => output equals that constant for every head
+    v = np.full((n, D), 0.625)
+    out, _, p = orc.full_attention_row(q, k, v, 0.3)
+    np.testing.assert_allclose(out, 0.625, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-13)
+    # identical keys => uniform weights => output is the mean of V, lse = s + ln n
+    kid = np.tile(k[:1], (n, 1))
+    v = r.standard_normal((n, D))
+    out, lse, p = orc.full_attention_row(q, kid, v, 0.3)
+    np.testing.assert_allclose(p, 1.0 / n, rtol=1e-12)
+    np.testing.assert_allclose(out, np.tile(v.mean(axis=0), (G, 1)), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, 0.3 * (q @ k[0]) + np.log(n), rtol=1e-12, atol=1e-12)
+    # a hand-worked case: one head, logits 0, ln2, ln4 (scale 1, D = 1) => p = 1/7, 2/7, 4/7
+    out, lse, p = orc.full_attention_row(np.array([[1.0]]), np.log(np.array([[1.0], [2.0], [4.0]])),
+                                         np.array([[1.0], [0.0], [0.0]]), 1.0)
+    np.testing.assert_allclose(p[0], [1 / 7, 2 / 7, 4 / 7], rtol=1e-14)
+    np.testing.assert_allclose(lse, [np.log(7.0)], rtol=1e-14)
+    np.testing.assert_allclose(out, [[1 / 7]], rtol=1e-14)
+    # one dominant key: its value row comes out
+    k2 = r.standard_normal((n, D))
+    k2[4] = 100.0 * q[0] / np.linalg.norm(q[0])
+    v = r.standard_normal((n, D))
+    out, _, _ = orc.full_attention_row(q[:1], k2, v, 1.0)
+    np.testing.assert_allclose(out[0], v[4], atol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# importance scores
+# ---------------------------------------------------------------------------
+
+def pin_score_invariants(orc, seed=3):
+    w = wl.small(batch=1, n_q_tokens=2, n_q_heads=8, n_kv_heads=2, head_dim=16,
+                 ctx_len=40, n_sparse_layers=0, top_k=5, window=4, n_needles=2,
+                 config_id=seed)
+    x = wl.generate(w, with_sparse=False)
+    res = orc.cross_decoder_step(x["q_full"], x["k"], x["v"], None, top_k=w.top_k,
+                                 window=w.window, scale=w.scale)
+    G = w.group
+    for (b, t, g), rr in res.items():
+        sc = rr["score"]
+        pos = rr["pos"]
+        assert sc.shape == (pos + 1,)
+        assert np.all(sc > 0) and np.all(sc <= 1.0 + 1e-15)
+        assert 1.0 - 1e-12 <= sc.sum() <= G + 1e-12
+        q = _f64(x["q_full"][b, t, g * G:(g + 1) * G])
+        kk = _f64(x["k"][b, g, : pos + 1])
+        s = w.scale * (q @ kk.T)
+        p = np.exp(s - logsumexp(s, axis=1, keepdims=True))
+        assert np.all(sc >= p - 1e-15)                      # score dominates every head
+        np.testing.assert_allclose(sc, p.max(axis=0), rtol=1e-12)
+    # G = 1: the score is the head's own softmax probability
+    q = _rng(seed).standard_normal((1, 8))
+    k = _rng(seed + 1).standard_normal((12, 8))
+    _, _, p = orc.full_attention_row(q, k, k, 0.5)
+    np.testing.assert_allclose(orc.importance_scores(p), torch.softmax(
+        torch.from_numpy(0.5 * (q @ k.T)), dim=-1).numpy()[0], rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# selection
+# ---------------------------------------------------------------------------
+
+def _brute_force_select(score, pos, k, w):
+    """Enumerate every size-m subset of the candidates and keep the one that
+    beats every left-out candidate (larger score, or equal score and lower index)."""
+    first = max(0, pos - w + 1)
+    cand = list(range(first))
+    m = min(k, len(cand))
+    winners = []
+    for sub in itertools.combinations(cand, m):
+        s = set(sub)
+        ok = all(score[i] > score[j] or (score[i] == score[j] and i < j)
+                 for i in s for j in cand if j not in s)
+        if ok:
+            winners.append(s)
+    assert len(winners) == 1, "the definition must single out one set"
+    return sorted(winners[0] | set(range(first, pos + 1)))
+
+
+def pin_selection_brute_force(orc, seed=4, trials=60):
+    r = _rng(seed)
+    for _ in range(trials):
+        pos = int(r.integers(0, 14))
+        w = int(r.integers(0, 5))
+        k = int(r.integers(0, 8))
+        # few distinct values so that ties are common
+        score = r.integers(0, 4, size=pos + 1).astype(np.float64) / 8.0 + 1e-3
+        idx, tau, sigma = orc.select_tokens(score, pos, k, w)
+        assert list(idx) == _brute_force_select(score, pos, k, w)
+        first = max(0, pos - w + 1)
+        taken = [i for i in idx if i < first]
+        if taken:
+            assert tau == min(score[i] for i in taken)
+        left = [j for j in range(first) if j not in set(idx)]
+        if left:
+            assert sigma == max(score[j] for j in left)
+
+
+def pin_selection_invariants(orc, seed=5):
+    r = _rng(seed)
+    for pos, k, w in [(50, 10, 8), (7, 10, 8), (100, 0, 8), (30, 5, 0), (3, 2, 1), (0, 4, 4)]:
+        score = r.random(pos + 1)
+        idx, tau, sigma = orc.select_tokens(score, pos, k, w)
+        first = max(0, pos - w + 1)
+        win = set(range(first, pos + 1))
+        assert win <= set(idx.tolist()), "forced window always present"
+        assert len(win) == min(w, pos + 1)
+        assert len(idx) == min(k, first) + len(win)
+        assert np.all(np.diff(idx) > 0), "ascending, no duplicates"
+        sel = [i for i in idx if i < first]
+        rest = [j for j in range(first) if j not in set(sel)]
+        if sel and rest:
+            assert min(score[sel]) >= max(score[rest])
+    # identical scores => the lowest indices win
+    pos, k, w = 40, 7, 5
+    idx, _, _ = orc.select_tokens(np.full(pos + 1, 0.25), pos, k, w)
+    assert idx.tolist() == list(range(k)) + list(range(pos - w + 1, pos + 1))
+
+
+def pin_identical_keys_select_prefix(orc, seed=6):
+    """All keys equal => all scores tie => idx = [0, k) followed by the window."""
+    w = wl.small(batch=1, n_q_tokens=1, n_q_heads=4, n_kv_heads=1, head_dim=8, ctx_len=30,
+                 n_sparse_layers=0, top_k=6, window=5, config_id=seed)
+    x = wl.generate(w, with_sparse=False)
+    x["k"][:] = x["k"][:, :, :1, :]
+    res = orc.cross_decoder_step(x["q_full"], x["k"], x["v"], None, top_k=6, window=5,
+                                 scale=w.scale)
+    assert res[(0, 0, 0)]["idx"].tolist() == list(range(6)) + list(range(25, 30))
+
+
+# ---------------------------------------------------------------------------
+# sparse layers
+# ---------------------------------------------------------------------------
+
+def pin_sparse_dense_equivalence(orc, seed=7):
+    """k >= |C| keeps every key, so a sparse layer with the full layer's
+    queries reproduces the dense output exactly (up to rounding)."""
+    w = wl.small(batch=1, n_q_tokens=2, n_q_heads=4, n_kv_heads=2, head_dim=8, ctx_len=25,
+                 n_sparse_layers=1, top_k=100, window=3, config_id=seed)
+    x = wl.generate(w)
+    qs = x["q_full"][None].copy()
+    res = orc.cross_decoder_step(x["q_full"], x["k"], x["v"], qs, top_k=w.top_k,
+                                 window=w.window, scale=w.scale)
+    for key, rr in res.items():
+        assert rr["idx"].size == rr["pos"] + 1
+        np.testing.assert_allclose(rr["out_sparse"][0], rr["out_full"], rtol=1e-11, atol=1e-13)
+
+
+def pin_sparse_sliding_window(orc, seed=8):
+    """k = 0 leaves only the forced window: SDPA with a band mask."""
+    w = wl.small(batch=1, n_q_tokens=3, n_q_heads=2, n_kv_heads=1, head_dim=8, ctx_len=20,
+                 n_sparse_layers=2, top_k=0, window=4, config_id=seed)
+    x = wl.generate(w)
+    res = orc.cross_decoder_step(x["q_full"], x["k"], x["v"], x["q_sparse"], top_k=0,
+                                 window=4, scale=w.scale)
+    pos = w.positions()
+    kk = _f64(x["k"][0])
+    vv = _f64(x["v"][0])
+    j = np.arange(w.ctx_len)
+    mask = (j[None, :] <= pos[:, None]) & (j[None, :] > pos[:, None] - 4)
+    for n in range(2):
+        q = _f64(x["q_sparse"][n, 0]).transpose(1, 0, 2)     # [Hq, T, D]
+        ref = _sdpa(q, np.repeat(kk, 2, axis=0), np.repeat(vv, 2, axis=0), w.scale, mask)
+        for t in range(3):
+            np.testing.assert_allclose(res[(0, t, 0)]["out_sparse"][n], ref[:, t],
+                                       rtol=1e-11, atol=1e-13)
+
+
+def pin_sparse_permutation_invariance(orc, seed=9):
+    r = _rng(seed)
+    q = r.standard_normal((3, 8))
+    k = r.standard_normal((30, 8))
+    v = r.standard_normal((30, 8))
+    idx = np.array([0, 3, 4, 9, 17, 29])
+    a = orc.sparse_attention_row(q, k, v, idx, 0.4)
+    b = orc.sparse_attention_row(q, k, v, idx[r.permutation(idx.size)], 0.4)
+    np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-14)
+    # and it equals SDPA restricted to those rows
+    ref = _sdpa(q[:, None, :], np.repeat(k[idx][None], 3, 0), np.repeat(v[idx][None], 3, 0), 0.4)
+    np.testing.assert_allclose(a, ref[:, 0], rtol=1e-12, atol=1e-13)
+
+
+def pin_widening(orc, seed=10):
+    r = _rng(seed)
+    x = r.standard_normal(1000).astype(np.float32) * 10
+    bits = _bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(orc.widen_bf16(bits), ref)
+
+
+ALL_PINS = [
+    pin_full_attention_vs_sdpa,
+    pin_attention_closed_forms,
+    pin_score_invariants,
+    pin_selection_brute_force,
+    pin_selection_invariants,
+    pin_identical_keys_select_prefix,
+    pin_sparse_dense_equivalence,
+    pin_sparse_sliding_window,
+    pin_sparse_permutation_invariance,
+    pin_widening,
+]
