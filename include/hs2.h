@@ -1,0 +1,160 @@
+/*
+ * hs2.h — C ABI of libhs2.so: the HySparse2 Cross-Decoder attention hot path
+ * (one full-attention layer that also scores every key, a token-level top-k
+ * with a forced recent window, and several sparse-attention layers that reuse
+ * the same KV cache and the same index list) for AMD Instinct MI355X (gfx950).
+ *
+ * Where the method comes from
+ *   - KV Reuse: the KV cache and the token-selection result of one full
+ *     attention layer are handed to the sparse layers that follow it
+ *     (news page "两天两连更：小米提前亮出V3底牌", section
+ *     "两级KV共享：让模型少跑一半").
+ *   - Token-level selection, a fixed window of the most recent tokens plus a
+ *     chosen set of older tokens, one shared cache for both (same page,
+ *     section "Token级选择：精准定位大海里的那根针"; the experiments there keep
+ *     128 recent tokens and choose 1024 older ones).
+ *   - The selection comes from the full layer's own attention, with no
+ *     separately trained indexer (video page "小米 MiMo-V3 HySparse2
+ *     架构：读长文省一半", section "HySparse2 的解法：两派都用，还改了流程").
+ *   The pages do not say how the query heads of a GQA group combine into one
+ *   importance per key; this library uses the largest softmax probability any
+ *   head of the group gives the key, ties going to the lower key index, one
+ *   selection per (batch, query token, KV head).
+ *
+ * Conventions shared by every call
+ *   - All tensors are dense, row-major, in device memory of the current HIP
+ *     device, allocated and owned by the caller; the library never allocates,
+ *     frees or synchronises on these calls and keeps no global mutable state
+ *     (the last HIP error code is thread-local).  Outputs must not overlap
+ *     inputs or each other.
+ *   - bf16 tensors hold raw bfloat16 bit patterns (hs2_bf16).
+ *   - Query token t of a chunk of T tokens sits at position P_t = S - T + t
+ *     and sees keys 0..P_t (its own key included).  Decode is T = 1.
+ *   - Layouts:  q, out            [B][T][Hq][D]
+ *               q_sparse, out_sp  [N][B][T][Hq][D]
+ *               k, v (KV cache)   [B][Hkv][S][D]   token-major per KV head
+ *               lse               [B][T][Hq]        natural log, float32
+ *               scores            [B][T][Hkv][S]    float32, 0 past P_t
+ *               idx               [B][T][Hkv][k+w]  int32, ascending, -1 past n_sel
+ *               n_sel             [B][T][Hkv]       int32
+ *   - `ws` is a caller-owned device workspace of at least
+ *     hs2_workspace_bytes(shape, n_layers) bytes, 256-byte aligned; its
+ *     contents need no initialisation and are scratch after the call.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Work is only
+ *     enqueued; results are ready when the stream reaches that point.
+ *   - Errors: argument and shape errors are detected on the host before
+ *     anything is enqueued (HS2_ERR_INVALID_ARG, HS2_ERR_UNSUPPORTED,
+ *     HS2_ERR_WORKSPACE).  A failed launch returns HS2_ERR_HIP and keeps the
+ *     hipError_t in hs2_last_hip_error().  Faults inside kernels surface at the
+ *     caller's next synchronisation, as HIP reports them.
+ *   - v1 supports head_dim = 128 and Hq = 8 * Hkv exactly, S < 2^31,
+ *     top_k + window <= 4096.
+ */
+#ifndef HS2_H_
+#define HS2_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t hs2_bf16; /* raw bfloat16 bits */
+
+typedef struct hs2_shape {
+  int64_t ctx_len;    /* S: keys 0..S-1, including the query tokens' own keys */
+  double scale;       /* softmax scale, normally 1/sqrt(D); kept in double because the
+                         float64 re-ranking near the k-th threshold needs it exactly */
+  int32_t batch;      /* B */
+  int32_t n_q_tokens; /* T: 1 = decode; > 1 = a prefill chunk (the last T positions) */
+  int32_t n_q_heads;  /* Hq */
+  int32_t n_kv_heads; /* Hkv; the GQA group size is G = Hq / Hkv */
+  int32_t head_dim;   /* D */
+  int32_t top_k;      /* k: older tokens chosen per row (1024 in the pages' experiments) */
+  int32_t window;     /* w: most recent tokens always kept (128 in the pages' experiments) */
+  int32_t reserved;   /* must be 0 */
+} hs2_shape;          /* 48 bytes, no padding */
+
+enum {
+  HS2_OK = 0,
+  HS2_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, bad workspace alignment */
+  HS2_ERR_UNSUPPORTED = -2, /* a valid shape this build does not implement */
+  HS2_ERR_WORKSPACE = -3,   /* ws_bytes smaller than hs2_workspace_bytes() */
+  HS2_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+};
+
+/* Bytes of workspace any call below needs for this shape and number of sparse
+ * layers (the maximum over the calls, so one buffer serves all of them).
+ * Returns 0 if the shape is invalid or unsupported. */
+size_t hs2_workspace_bytes(const hs2_shape* shape, int32_t n_sparse_layers);
+
+/* Full attention over the shared cache, with per-key importance.
+ * For every (b, t, KV head g) and query head h of the group:
+ *   s_h[j] = scale * <q_h, k_j> for j <= P_t,  out_h = softmax(s_h) . V,
+ *   lse_h  = log sum_j exp(s_h[j]),  scores[j] = max_h softmax(s_h)[j].
+ * q [B][T][Hq][D], k/v [B][Hkv][S][D] in; out [B][T][Hq][D] out.
+ * lse (nullable) [B][T][Hq]; scores (nullable) [B][T][Hkv][S] (0 past P_t).
+ * This is the group's full-attention layer: news page, section
+ * "两级KV共享：让模型少跑一半" (KV Reuse), and video page, section
+ * "HySparse2 的解法：两派都用，还改了流程" (selection from the attention). */
+int hs2_full_attn_scores(const hs2_shape* shape, const hs2_bf16* q, const hs2_bf16* k,
+                         const hs2_bf16* v, hs2_bf16* out, float* lse, float* scores,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* Token-level selection from given scores [B][T][Hkv][S] (float32, compared
+ * exactly as given).  For each row: keep the window [max(0, P_t-w+1), P_t];
+ * from the older keys [0, P_t-w+1) keep the top_k with the largest score,
+ * ties to the lower index (all of them if fewer than top_k).  Writes idx
+ * [B][T][Hkv][k+w] ascending (-1 past n_sel) and n_sel [B][T][Hkv].
+ * News page, section "Token级选择：精准定位大海里的那根针". */
+int hs2_topk_select(const hs2_shape* shape, const float* scores, int32_t* idx, int32_t* n_sel,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* Sparse attention of n_layers layers that reuse one KV cache and one index
+ * list per row: for layer n, out^(n)_h = softmax_i(scale * <q^(n)_h, k_i>) . V_i
+ * over i in idx[b][t][g][0..n_sel).  q [N][B][T][Hq][D], out [N][B][T][Hq][D];
+ * idx / n_sel as written by hs2_topk_select (entries must be in [0, P_t]).
+ * Rows with n_sel = 0 get zero outputs.  News page, section
+ * "两级KV共享：让模型少跑一半" (the sparse layers reuse the cache and the
+ * selection). */
+int hs2_sparse_attn(const hs2_shape* shape, int32_t n_layers, const hs2_bf16* q,
+                    const hs2_bf16* k, const hs2_bf16* v, const int32_t* idx,
+                    const int32_t* n_sel, hs2_bf16* out, void* ws, size_t ws_bytes,
+                    void* stream);
+
+/* One Cross-Decoder group step: full attention with importance, selection,
+ * then n_sparse_layers sparse layers — the same results as the three calls
+ * above in sequence, except that the selection here ranks keys by importance
+ * recomputed in float64 near the k-th threshold (so that keys are ordered by
+ * their exact importance, not by its float32 rounding).  scores and lse are
+ * nullable.  q_sparse / out_sparse may be NULL when n_sparse_layers = 0. */
+int hs2_cross_decoder_step(const hs2_shape* shape, int32_t n_sparse_layers,
+                           const hs2_bf16* q_full, const hs2_bf16* q_sparse,
+                           const hs2_bf16* k, const hs2_bf16* v, hs2_bf16* out_full,
+                           hs2_bf16* out_sparse, int32_t* idx, int32_t* n_sel, float* lse,
+                           float* scores, void* ws, size_t ws_bytes, void* stream);
+
+/* The step above, with HIP events recorded on `stream` between its phases,
+ * for measurement: phase_ms[0] = full-attention split kernel, [1] = combine,
+ * [2] = selection (all its kernels), [3] = sparse layers (kernel + combine).
+ * Runs `iters` steps back to back, synchronises the stream and returns the
+ * average milliseconds of each phase.  Not for the serving loop. */
+int hs2_cross_decoder_step_timed(const hs2_shape* shape, int32_t n_sparse_layers,
+                                 const hs2_bf16* q_full, const hs2_bf16* q_sparse,
+                                 const hs2_bf16* k, const hs2_bf16* v, hs2_bf16* out_full,
+                                 hs2_bf16* out_sparse, int32_t* idx, int32_t* n_sel,
+                                 void* ws, size_t ws_bytes, void* stream, int32_t iters,
+                                 float* phase_ms /* [4] */);
+
+/* Human-readable text for a status code (static storage). */
+const char* hs2_status_string(int status);
+
+/* hipError_t of the last HS2_ERR_HIP on the calling thread (0 if none). */
+int hs2_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HS2_H_ */

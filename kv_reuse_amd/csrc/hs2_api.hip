@@ -1,0 +1,279 @@
+// Host side of the C ABI declared in include/hs2.h: argument validation, the
+// workspace plan, and the launch sequence of each entry point.  Nothing here
+// allocates, frees or synchronises, except the measurement entry point
+// hs2_cross_decoder_step_timed, which synchronises its stream at the end.
+
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "hs2_internal.h"
+
+namespace hs2 {
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Validate a shape and lay out the workspace.  Returns HS2_OK or an error code.
+int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
+  if (!sh || !p) return HS2_ERR_INVALID_ARG;
+  if (sh->ctx_len < 1 || sh->batch < 1 || sh->n_q_tokens < 1 || sh->n_q_heads < 1 ||
+      sh->n_kv_heads < 1 || sh->head_dim < 1 || sh->top_k < 0 || sh->window < 0 ||
+      n_layers < 0 || sh->reserved != 0)
+    return HS2_ERR_INVALID_ARG;
+  if (!(sh->scale > 0.0) || !isfinite(sh->scale)) return HS2_ERR_INVALID_ARG;
+  if (sh->n_q_tokens > sh->ctx_len) return HS2_ERR_INVALID_ARG;
+  if (sh->n_q_heads % sh->n_kv_heads != 0) return HS2_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(sh->top_k) + sh->window < 1) return HS2_ERR_INVALID_ARG;
+  if (sh->head_dim != kD || sh->n_q_heads != kG * sh->n_kv_heads) return HS2_ERR_UNSUPPORTED;
+  if (sh->ctx_len >= (int64_t{1} << 31)) return HS2_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(sh->top_k) + sh->window > kMaxSel) return HS2_ERR_UNSUPPORTED;
+  const int64_t R = static_cast<int64_t>(sh->batch) * sh->n_q_tokens * sh->n_kv_heads;
+  if (R > 65535) return HS2_ERR_UNSUPPORTED;
+
+  Plan q{};
+  q.S = sh->ctx_len;
+  q.Spad = static_cast<int64_t>(align_up(static_cast<size_t>(q.S), 64));
+  q.B = sh->batch;
+  q.T = sh->n_q_tokens;
+  q.Hq = sh->n_q_heads;
+  q.Hkv = sh->n_kv_heads;
+  q.R = static_cast<int>(R);
+  q.k = sh->top_k;
+  q.w = sh->window;
+  q.cap = sh->top_k + sh->window;
+  q.n_layers = n_layers;
+  q.scale = sh->scale;
+
+  // full attention, decode: enough splits for ~4 work-groups per CU
+  {
+    const int64_t target = 1024;
+    int64_t ns = ceil_div(target, R);
+    ns = std::max<int64_t>(1, std::min<int64_t>(ns, ceil_div(q.S, 256)));
+    int64_t kps = align_up(static_cast<size_t>(ceil_div(q.S, ns)), 128);
+    q.kps = static_cast<int>(kps);
+    q.n_split = static_cast<int>(ceil_div(q.S, kps));
+  }
+  // selection: ~512 work-groups in total over the rows
+  {
+    int64_t chunk = align_up(static_cast<size_t>(ceil_div(q.S * R, 512)), 256);
+    chunk = std::max<int64_t>(chunk, 2048);
+    chunk = std::min<int64_t>(chunk, align_up(static_cast<size_t>(q.S), 256));
+    q.sel_chunk = static_cast<int>(chunk);
+    q.sel_nchunk = static_cast<int>(ceil_div(q.S, chunk));
+  }
+  // sparse: slices of 128 keys over work-groups when rows are few
+  q.sp_nch = (R >= 256) ? 1 : static_cast<int>(ceil_div(q.cap, 128));
+
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes, kAlign);
+    return o;
+  };
+  const size_t nsplit_rows = static_cast<size_t>(R) * q.n_split;
+  const bool decode = q.T == 1;
+  q.off_part_m = take(decode ? nsplit_rows * kG * sizeof(float) : 0);
+  q.off_part_l = take(decode ? nsplit_rows * kG * sizeof(double) : 0);
+  q.off_part_o = take(decode ? nsplit_rows * kG * kD * sizeof(float) : 0);
+  q.off_logits = take(decode ? static_cast<size_t>(R) * kG * q.Spad * sizeof(float) : 0);
+  q.off_lse2 = take(static_cast<size_t>(R) * kG * sizeof(double));
+  q.off_ytop = take(static_cast<size_t>(R) * sizeof(float));
+  q.off_ukey = take(static_cast<size_t>(R) * q.Spad * sizeof(uint32_t));
+  q.off_hist = take(static_cast<size_t>(R) * kNB * sizeof(uint32_t));
+  q.off_info = take(static_cast<size_t>(R) * sizeof(RowInfo));
+  q.off_cert = take(static_cast<size_t>(R) * align_up(static_cast<size_t>(q.k), 64) * sizeof(int32_t));
+  q.off_unc = take(static_cast<size_t>(R) * kUncCap * sizeof(int32_t));
+  const size_t sp_parts = q.sp_nch > 1 ? static_cast<size_t>(R) * q.sp_nch * n_layers * kG : 0;
+  q.off_sp_m = take(sp_parts * sizeof(float));
+  q.off_sp_l = take(sp_parts * sizeof(float));
+  q.off_sp_o = take(sp_parts * kD * sizeof(float));
+  q.total = off;
+  *p = q;
+  return HS2_OK;
+}
+
+int check_ws(const Plan& p, void* ws, size_t ws_bytes) {
+  if (!ws) return HS2_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return HS2_ERR_INVALID_ARG;
+  if (ws_bytes < p.total) return HS2_ERR_WORKSPACE;
+  return HS2_OK;
+}
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return HS2_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return HS2_ERR_HIP;
+}
+
+#define HS2_TRY(expr)                        \
+  do {                                       \
+    const int st_ = hip_status((expr));      \
+    if (st_ != HS2_OK) return st_;           \
+  } while (0)
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int run_full(const Plan& p, const u16* q, const u16* k, const u16* v, u16* out, float* lse,
+             void* ws, hipStream_t st) {
+  HS2_TRY(launch_full_decode_split(p, q, k, v, ws, st));
+  HS2_TRY(launch_full_combine(p, out, lse, ws, st));
+  return HS2_OK;
+}
+
+int run_select_from_logits(const Plan& p, const u16* q, const u16* k, float* scores,
+                           int32_t* idx, int32_t* n_sel, void* ws, hipStream_t st) {
+  HS2_TRY(launch_select_hist(p, true, nullptr, scores, true, ws, st));
+  HS2_TRY(launch_select_compact(p, true, ws, st));
+  HS2_TRY(launch_select_finish(p, true, nullptr, q, k, idx, n_sel, ws, st));
+  return HS2_OK;
+}
+
+}  // namespace
+}  // namespace hs2
+
+using namespace hs2;
+
+extern "C" {
+
+size_t hs2_workspace_bytes(const hs2_shape* shape, int32_t n_sparse_layers) {
+  Plan p;
+  if (make_plan(shape, n_sparse_layers, &p) != HS2_OK) return 0;
+  return p.total;
+}
+
+int hs2_full_attn_scores(const hs2_shape* shape, const hs2_bf16* q, const hs2_bf16* k,
+                         const hs2_bf16* v, hs2_bf16* out, float* lse, float* scores, void* ws,
+                         size_t ws_bytes, void* stream) {
+  Plan p;
+  int st = make_plan(shape, 0, &p);
+  if (st != HS2_OK) return st;
+  if (!q || !k || !v || !out) return HS2_ERR_INVALID_ARG;
+  if ((st = check_ws(p, ws, ws_bytes)) != HS2_OK) return st;
+  if (p.T != 1) return HS2_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  const hipStream_t s = as_stream(stream);
+  if ((st = run_full(p, q, k, v, out, lse, ws, s)) != HS2_OK) return st;
+  if (scores) HS2_TRY(launch_select_hist(p, true, nullptr, scores, false, ws, s));
+  return HS2_OK;
+}
+
+int hs2_topk_select(const hs2_shape* shape, const float* scores, int32_t* idx, int32_t* n_sel,
+                    void* ws, size_t ws_bytes, void* stream) {
+  Plan p;
+  int st = make_plan(shape, 0, &p);
+  if (st != HS2_OK) return st;
+  if (!scores || !idx || !n_sel) return HS2_ERR_INVALID_ARG;
+  if ((st = check_ws(p, ws, ws_bytes)) != HS2_OK) return st;
+  (void)hipGetLastError();
+  const hipStream_t s = as_stream(stream);
+  HS2_TRY(launch_select_clear(p, ws, s));
+  HS2_TRY(launch_select_hist(p, false, scores, nullptr, true, ws, s));
+  HS2_TRY(launch_select_compact(p, false, ws, s));
+  HS2_TRY(launch_select_finish(p, false, scores, nullptr, nullptr, idx, n_sel, ws, s));
+  return HS2_OK;
+}
+
+int hs2_sparse_attn(const hs2_shape* shape, int32_t n_layers, const hs2_bf16* q,
+                    const hs2_bf16* k, const hs2_bf16* v, const int32_t* idx,
+                    const int32_t* n_sel, hs2_bf16* out, void* ws, size_t ws_bytes,
+                    void* stream) {
+  Plan p;
+  int st = make_plan(shape, n_layers, &p);
+  if (st != HS2_OK) return st;
+  if (n_layers < 1 || !q || !k || !v || !idx || !n_sel || !out) return HS2_ERR_INVALID_ARG;
+  if ((st = check_ws(p, ws, ws_bytes)) != HS2_OK) return st;
+  (void)hipGetLastError();
+  HS2_TRY(launch_sparse(p, q, k, v, idx, n_sel, out, ws, as_stream(stream)));
+  return HS2_OK;
+}
+
+int hs2_cross_decoder_step(const hs2_shape* shape, int32_t n_sparse_layers,
+                           const hs2_bf16* q_full, const hs2_bf16* q_sparse, const hs2_bf16* k,
+                           const hs2_bf16* v, hs2_bf16* out_full, hs2_bf16* out_sparse,
+                           int32_t* idx, int32_t* n_sel, float* lse, float* scores, void* ws,
+                           size_t ws_bytes, void* stream) {
+  Plan p;
+  int st = make_plan(shape, n_sparse_layers, &p);
+  if (st != HS2_OK) return st;
+  if (!q_full || !k || !v || !out_full || !idx || !n_sel) return HS2_ERR_INVALID_ARG;
+  if (n_sparse_layers > 0 && (!q_sparse || !out_sparse)) return HS2_ERR_INVALID_ARG;
+  if ((st = check_ws(p, ws, ws_bytes)) != HS2_OK) return st;
+  if (p.T != 1) return HS2_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  const hipStream_t s = as_stream(stream);
+  if ((st = run_full(p, q_full, k, v, out_full, lse, ws, s)) != HS2_OK) return st;
+  if ((st = run_select_from_logits(p, q_full, k, scores, idx, n_sel, ws, s)) != HS2_OK) return st;
+  if (n_sparse_layers > 0)
+    HS2_TRY(launch_sparse(p, q_sparse, k, v, idx, n_sel, out_sparse, ws, s));
+  return HS2_OK;
+}
+
+int hs2_cross_decoder_step_timed(const hs2_shape* shape, int32_t n_sparse_layers,
+                                 const hs2_bf16* q_full, const hs2_bf16* q_sparse,
+                                 const hs2_bf16* k, const hs2_bf16* v, hs2_bf16* out_full,
+                                 hs2_bf16* out_sparse, int32_t* idx, int32_t* n_sel, void* ws,
+                                 size_t ws_bytes, void* stream, int32_t iters, float* phase_ms) {
+  Plan p;
+  int st = make_plan(shape, n_sparse_layers, &p);
+  if (st != HS2_OK) return st;
+  if (!q_full || !k || !v || !out_full || !idx || !n_sel || !phase_ms || iters < 1)
+    return HS2_ERR_INVALID_ARG;
+  if (n_sparse_layers > 0 && (!q_sparse || !out_sparse)) return HS2_ERR_INVALID_ARG;
+  if ((st = check_ws(p, ws, ws_bytes)) != HS2_OK) return st;
+  if (p.T != 1) return HS2_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  const hipStream_t s = as_stream(stream);
+  hipEvent_t ev[5];
+  for (int i = 0; i < 5; ++i) {
+    const hipError_t e = hipEventCreate(&ev[i]);
+    if (e != hipSuccess) {
+      for (int j = 0; j < i; ++j) (void)hipEventDestroy(ev[j]);
+      return hip_status(e);
+    }
+  }
+  double acc[4] = {0, 0, 0, 0};
+  int rc = HS2_OK;
+  for (int it = 0; it < iters && rc == HS2_OK; ++it) {
+    float ms[4] = {0, 0, 0, 0};
+    rc = hip_status(hipEventRecord(ev[0], s));
+    if (rc == HS2_OK) rc = hip_status(launch_full_decode_split(p, q_full, k, v, ws, s));
+    if (rc == HS2_OK) rc = hip_status(hipEventRecord(ev[1], s));
+    if (rc == HS2_OK) rc = hip_status(launch_full_combine(p, out_full, nullptr, ws, s));
+    if (rc == HS2_OK) rc = hip_status(hipEventRecord(ev[2], s));
+    if (rc == HS2_OK) rc = run_select_from_logits(p, q_full, k, nullptr, idx, n_sel, ws, s);
+    if (rc == HS2_OK) rc = hip_status(hipEventRecord(ev[3], s));
+    if (rc == HS2_OK && n_sparse_layers > 0)
+      rc = hip_status(launch_sparse(p, q_sparse, k, v, idx, n_sel, out_sparse, ws, s));
+    if (rc == HS2_OK) rc = hip_status(hipEventRecord(ev[4], s));
+    if (rc == HS2_OK) rc = hip_status(hipEventSynchronize(ev[4]));
+    for (int i = 0; i < 4 && rc == HS2_OK; ++i) {
+      rc = hip_status(hipEventElapsedTime(&ms[i], ev[i], ev[i + 1]));
+      acc[i] += ms[i];
+    }
+  }
+  for (int i = 0; i < 5; ++i) (void)hipEventDestroy(ev[i]);
+  if (rc != HS2_OK) return rc;
+  for (int i = 0; i < 4; ++i) phase_ms[i] = static_cast<float>(acc[i] / iters);
+  return HS2_OK;
+}
+
+const char* hs2_status_string(int status) {
+  switch (status) {
+    case HS2_OK: return "ok";
+    case HS2_ERR_INVALID_ARG: return "invalid argument";
+    case HS2_ERR_UNSUPPORTED: return "unsupported shape";
+    case HS2_ERR_WORKSPACE: return "workspace too small";
+    case HS2_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int hs2_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,120 @@
+// Internal declarations shared by the HIP sources of libhs2.so (not installed).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/hs2.h"
+
+namespace hs2 {
+
+constexpr int kD = 128;          // head dim (v1)
+constexpr int kG = 8;            // query heads per KV head (v1)
+constexpr int kNB = 2048;        // selection histogram bins (top 11 bits of a 32-bit key)
+constexpr int kBinShift = 21;    // 32 - 11
+constexpr int kUncCap = 2048;    // near-threshold keys handled in LDS; more take the slow path
+constexpr int kMaxSel = 4096;    // top_k + window limit (index list kept in LDS)
+constexpr int kSparseChunk = 128;  // selected keys per sparse work-group (4 waves x 32)
+constexpr float kYRange = 64.0f;   // log2 range below the row's top score that the bins span
+
+typedef unsigned short u16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Per-row selection bookkeeping (lives in the workspace).
+struct RowInfo {
+  int32_t bstar;       // histogram bin holding the k-th largest key
+  int32_t n_cert;      // candidates certainly selected (bins above the uncertain band)
+  int32_t n_unc;       // candidates in the uncertain band
+  int32_t mode;        // kModeNormal / kModeAll / kModeNone
+  uint32_t cert_count; // append counters (compaction)
+  uint32_t unc_count;
+  uint32_t arrive;     // work-groups of this row done with the histogram
+  int32_t band;        // 1 = uncertain band is bins [b*-1, b*+1]; 0 = bin b* only
+};
+enum { kModeNormal = 0, kModeAll = 1, kModeNone = 2 };
+
+// Where each piece of the workspace sits, for one shape.
+struct Plan {
+  int64_t S, Spad;
+  int B, T, Hq, Hkv, R;      // R = B*T*Hkv rows
+  int k, w, cap;             // cap = k + w (index list capacity per row)
+  int n_layers;
+  double scale;
+  // full attention (decode split kernel)
+  int n_split, kps;
+  size_t off_part_m, off_part_l, off_part_o, off_logits, off_lse2, off_ytop;
+  // selection
+  int sel_chunk, sel_nchunk;
+  size_t off_ukey, off_hist, off_info, off_cert, off_unc;
+  // sparse
+  int sp_nch;
+  size_t off_sp_m, off_sp_l, off_sp_o;
+  size_t total;
+};
+
+// ---------------------------------------------------------------- launchers
+// Each returns the hipError_t of its launch (hipGetLastError()).
+
+// Full attention, decode (T == 1): split-context flash-decode writing per-split
+// partial (m, l, O) and the float32 base-2 logits of every key and head.
+hipError_t launch_full_decode_split(const Plan& p, const u16* q, const u16* k, const u16* v,
+                                    void* ws, hipStream_t st);
+// Merge the splits: out (bf16), lse (nullable), lse2 (fp64, base 2) and the row's
+// top score bound; also clears this row's selection counters and histogram.
+hipError_t launch_full_combine(const Plan& p, u16* out, float* lse, void* ws, hipStream_t st);
+
+// Selection.  from_logits: keys are ranked by importance computed from the
+// stored logits and lse2, then re-ranked in float64 near the threshold using
+// q and k.  Otherwise keys are the given float32 scores, compared exactly.
+hipError_t launch_select_clear(const Plan& p, void* ws, hipStream_t st);
+hipError_t launch_select_hist(const Plan& p, bool from_logits, const float* scores_in,
+                              float* scores_out, bool do_select, void* ws, hipStream_t st);
+hipError_t launch_select_compact(const Plan& p, bool from_logits, void* ws, hipStream_t st);
+hipError_t launch_select_finish(const Plan& p, bool from_logits, const float* scores_in,
+                                const u16* q, const u16* k, int32_t* idx, int32_t* n_sel,
+                                void* ws, hipStream_t st);
+
+// Sparse layers (all n_layers fused: one gather of the selected K/V rows).
+hipError_t launch_sparse(const Plan& p, const u16* q, const u16* k, const u16* v,
+                         const int32_t* idx, const int32_t* n_sel, u16* out, void* ws,
+                         hipStream_t st);
+
+// ---------------------------------------------------------------- device helpers
+#ifdef __HIPCC__
+__device__ __forceinline__ float bf16_bits_to_f32(u16 b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ u16 f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<u16>(u >> 16);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16_rne(lo)) |
+         (static_cast<uint32_t>(f32_to_bf16_rne(hi)) << 16);
+}
+__device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
+__device__ __forceinline__ u32x4 load_u32x4(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+// Order-preserving maps from floats to unsigned integers (larger value -> larger key).
+__device__ __forceinline__ uint32_t ordered_u32(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ uint64_t ordered_u64(double d) {
+  uint64_t u = static_cast<uint64_t>(__double_as_longlong(d));
+  return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
+}
+// Wait until this wave's outstanding LDS operations are done, and keep the
+// compiler from moving memory accesses across this point.
+__device__ __forceinline__ void lds_fence_wave() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+#endif
+
+}  // namespace hs2

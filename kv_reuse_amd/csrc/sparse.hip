@@ -1,0 +1,228 @@
+// Sparse-attention layers that reuse the full layer's KV cache and index list
+// (news page "两天两连更：小米提前亮出V3底牌", section "两级KV共享：让模型少跑一半",
+// item KV Reuse; the window and the chosen older tokens share one cache and one
+// softmax, section "Token级选择：精准定位大海里的那根针").
+//
+// Design (gfx950):
+//  * One work-group serves one row (batch, query token, KV head) and a slice of
+//    its index list.  The slice's indices go to LDS; the work-group gathers the
+//    selected K and V rows (256 contiguous bytes each) into LDS once, in
+//    sub-chunks of 128 keys, and every layer of the launch reads them there:
+//    the N layers cost one gather, not N.
+//  * Wave c handles column tile c = two layers x 8 query heads (16 MFMA
+//    columns): S^T = K_sel . Q^T and O^T = V_sel^T . P^T on MFMA 16x16x32 bf16,
+//    online softmax in base 2 across the sub-chunks.
+//  * Decode has few rows, so the index list is cut into slices of 128 keys
+//    spread over work-groups, and a combine kernel merges the slices; a
+//    prefill chunk has enough rows to give each row one work-group.
+
+#include "hs2_internal.h"
+
+namespace hs2 {
+namespace {
+
+constexpr int kSub = 128;     // keys gathered into LDS at a time
+constexpr int kPitch = 136;   // u16 per LDS row (272 bytes)
+
+template <int NCT>
+__global__ __launch_bounds__(NCT * 64) void sparse_kernel(
+    const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ n_sel, u16* __restrict__ out,
+    float* __restrict__ part_m, float* __restrict__ part_l, float* __restrict__ part_o,
+    int64_t S, int T, int Hkv, int L, int layer0, int cap, int nch, int keys_per_wg,
+    float c2_hi, float c2_lo, size_t layer_stride) {
+  __shared__ __align__(16) u16 klds[kSub * kPitch];
+  __shared__ __align__(16) u16 vlds[kSub * kPitch];
+  __shared__ int32_t sidx[kSub];
+
+  const int r = blockIdx.y;
+  const int ch = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const int b = r / (T * Hkv);
+  const int g = r % Hkv;
+  const size_t kvrow = static_cast<size_t>(b) * Hkv + g;
+  const u16* kr = k + kvrow * static_cast<size_t>(S) * kD;
+  const u16* vr = v + kvrow * static_cast<size_t>(S) * kD;
+  const int ns = n_sel[r];
+  const int pos_begin = ch * keys_per_wg;
+  const int pos_end = min(ns, pos_begin + keys_per_wg);
+
+  const int layer = layer0 + 2 * wave + (col >> 3);  // this lane's column
+  const int head = col & 7;
+  const bool col_ok = layer < L;
+  bf16x8 qb[4];
+  {
+    const u16* qr = q + static_cast<size_t>(col_ok ? layer : 0) * layer_stride +
+                    (static_cast<size_t>(r) * kG + head) * kD;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      qb[c] = col_ok ? as_bf16x8(load_u32x4(qr + 32 * c + 8 * grp))
+                     : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+  }
+  f32x4 o[8];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int sc = pos_begin; sc < pos_end; sc += kSub) {
+    const int n_here = min(kSub, pos_end - sc);
+    __syncthreads();  // the previous sub-chunk is consumed
+    for (int i = tid; i < kSub; i += blockDim.x)
+      sidx[i] = i < n_here ? idx[static_cast<size_t>(r) * cap + sc + i] : -1;
+    __syncthreads();
+    for (int pc = tid; pc < kSub * 16; pc += blockDim.x) {
+      const int key = pc >> 4, c16 = pc & 15;
+      const int j = sidx[key];
+      const size_t jj = j < 0 ? 0 : static_cast<size_t>(j);
+      *reinterpret_cast<u32x4*>(klds + key * kPitch + 8 * c16) = load_u32x4(kr + jj * kD + 8 * c16);
+      *reinterpret_cast<u32x4*>(vlds + key * kPitch + 8 * c16) = load_u32x4(vr + jj * kD + 8 * c16);
+    }
+    __syncthreads();
+    for (int kb = 0; kb < n_here; kb += 32) {
+      f32x4 sacc[2];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        sacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const u16* krow = klds + (kb + 16 * mt + col) * kPitch + 8 * grp;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          sacc[mt] = mfma_16x16x32(as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 32 * c)),
+                                   qb[c], sacc[mt]);
+      }
+      float sv[8];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kk = kb + 16 * mt + 4 * grp + i;
+          const float a = sacc[mt][i];
+          sv[mt * 4 + i] = kk < n_here ? fmaf(a, c2_hi, a * c2_lo) : -INFINITY;
+        }
+      float tm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                       fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+      tm = fmaxf(tm, __shfl_xor(tm, 16));
+      tm = fmaxf(tm, __shfl_xor(tm, 32));
+      const float m_new = fmaxf(m_run, tm);
+      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(sv[e] - m_new);
+      l_run = l_run * alpha + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
+      m_run = m_new;
+      const bf16x8 pb = as_bf16x8(u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                        pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])});
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        o[nb] *= alpha;
+        const u16* vc = vlds + kb * kPitch + 16 * nb + col;
+        uint32_t a[4];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const int e0 = 2 * e2, e1 = 2 * e2 + 1;
+          const int k0 = 16 * (e0 >> 2) + 4 * grp + (e0 & 3);
+          const int k1 = 16 * (e1 >> 2) + 4 * grp + (e1 & 3);
+          a[e2] = static_cast<uint32_t>(vc[k0 * kPitch]) |
+                  (static_cast<uint32_t>(vc[k1 * kPitch]) << 16);
+        }
+        o[nb] = mfma_16x16x32(as_bf16x8(u32x4{a[0], a[1], a[2], a[3]}), pb, o[nb]);
+      }
+    }
+  }
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (!col_ok) return;
+  if (nch == 1) {
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    u16* orow = out + static_cast<size_t>(layer) * layer_stride + (static_cast<size_t>(r) * kG + head) * kD;
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) orow[16 * nb + 4 * grp + i] = f32_to_bf16_rne(o[nb][i] * inv);
+  } else {
+    const size_t pb = ((static_cast<size_t>(r) * nch + ch) * L + layer) * kG + head;
+    if (grp == 0) {
+      part_m[pb] = m_run;
+      part_l[pb] = l_run;
+    }
+    float* po = part_o + pb * kD;
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) po[16 * nb + 4 * grp + i] = o[nb][i];
+  }
+}
+
+// grid (R, L): merge the slices of one row and layer.
+__global__ __launch_bounds__(256) void sparse_combine_kernel(
+    const float* __restrict__ part_m, const float* __restrict__ part_l,
+    const float* __restrict__ part_o, u16* __restrict__ out, int L, int nch,
+    size_t layer_stride) {
+  const int r = blockIdx.x;
+  const int layer = blockIdx.y;
+  for (int i = threadIdx.x; i < kG * kD; i += blockDim.x) {
+    const int h = i >> 7, d = i & 127;
+    float M = -INFINITY;
+    for (int c = 0; c < nch; ++c)
+      M = fmaxf(M, part_m[((static_cast<size_t>(r) * nch + c) * L + layer) * kG + h]);
+    float acc = 0.f, l = 0.f;
+    if (M != -INFINITY) {
+      for (int c = 0; c < nch; ++c) {
+        const size_t pb = ((static_cast<size_t>(r) * nch + c) * L + layer) * kG + h;
+        const float mc = part_m[pb];
+        if (mc == -INFINITY) continue;
+        const float f = __builtin_amdgcn_exp2f(mc - M);
+        l += part_l[pb] * f;
+        acc += part_o[pb * kD + d] * f;
+      }
+    }
+    const float res = l > 0.f ? acc / l : 0.f;
+    out[static_cast<size_t>(layer) * layer_stride + (static_cast<size_t>(r) * kG + h) * kD + d] =
+        f32_to_bf16_rne(res);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_sparse(const Plan& p, const u16* q, const u16* k, const u16* v,
+                         const int32_t* idx, const int32_t* n_sel, u16* out, void* ws,
+                         hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  const double c2 = p.scale * 1.4426950408889634;
+  const float c2_hi = static_cast<float>(c2);
+  const float c2_lo = static_cast<float>(c2 - static_cast<double>(c2_hi));
+  const size_t layer_stride = static_cast<size_t>(p.B) * p.T * p.Hq * kD;
+  const int keys_per_wg = p.sp_nch == 1 ? ((p.cap + kSub - 1) / kSub) * kSub : kSub;
+  float* pm = reinterpret_cast<float*>(w + p.off_sp_m);
+  float* pl = reinterpret_cast<float*>(w + p.off_sp_l);
+  float* po = reinterpret_cast<float*>(w + p.off_sp_o);
+  for (int layer0 = 0; layer0 < p.n_layers; layer0 += 8) {
+    const int nl = min(8, p.n_layers - layer0);
+    const int nct = (nl + 1) / 2;
+    dim3 grid(p.sp_nch, p.R);
+    auto go = [&](auto kern) {
+      hipLaunchKernelGGL(kern, grid, dim3(nct * 64), 0, st, q, k, v, idx, n_sel, out, pm, pl, po,
+                         p.S, p.T, p.Hkv, p.n_layers, layer0, p.cap, p.sp_nch, keys_per_wg, c2_hi,
+                         c2_lo, layer_stride);
+    };
+    switch (nct) {
+      case 1: go(sparse_kernel<1>); break;
+      case 2: go(sparse_kernel<2>); break;
+      case 3: go(sparse_kernel<3>); break;
+      default: go(sparse_kernel<4>); break;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (p.sp_nch > 1) {
+    hipLaunchKernelGGL(sparse_combine_kernel, dim3(p.R, p.n_layers), dim3(256), 0, st, pm, pl, po,
+                       out, p.n_layers, p.sp_nch, layer_stride);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+}  // namespace hs2

@@ -1,0 +1,223 @@
+"""Thin ctypes binding of libhs2.so (include/hs2.h), with the same entry-point names.
+
+Only argument marshalling happens here: shapes and dtypes are checked, torch
+tensors are passed as device pointers, and torch's current HIP stream is
+passed as the stream.  Every step of the computation runs in the library's
+HIP kernels.  If the library has not been built, importing this module fails.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libhs2.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it first (python -m kv_reuse_amd.build "
+                      "or __graft_entry__.build())")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+HS2_OK, HS2_ERR_INVALID_ARG, HS2_ERR_UNSUPPORTED, HS2_ERR_WORKSPACE, HS2_ERR_HIP = 0, -1, -2, -3, -4
+EXPORTED = ["hs2_workspace_bytes", "hs2_full_attn_scores", "hs2_topk_select", "hs2_sparse_attn",
+            "hs2_cross_decoder_step", "hs2_cross_decoder_step_timed", "hs2_status_string",
+            "hs2_last_hip_error"]
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("ctx_len", ctypes.c_int64), ("scale", ctypes.c_double),
+                ("batch", ctypes.c_int32), ("n_q_tokens", ctypes.c_int32),
+                ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_SP = ctypes.POINTER(Shape)
+_lib.hs2_workspace_bytes.argtypes = [_SP, ctypes.c_int32]
+_lib.hs2_workspace_bytes.restype = ctypes.c_size_t
+_lib.hs2_full_attn_scores.argtypes = [_SP, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+_lib.hs2_full_attn_scores.restype = ctypes.c_int
+_lib.hs2_topk_select.argtypes = [_SP, _P, _P, _P, _P, ctypes.c_size_t, _P]
+_lib.hs2_topk_select.restype = ctypes.c_int
+_lib.hs2_sparse_attn.argtypes = [_SP, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]
+_lib.hs2_sparse_attn.restype = ctypes.c_int
+_lib.hs2_cross_decoder_step.argtypes = [_SP, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                        _P, _P, ctypes.c_size_t, _P]
+_lib.hs2_cross_decoder_step.restype = ctypes.c_int
+_lib.hs2_cross_decoder_step_timed.argtypes = [_SP, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P,
+                                              _P, _P, ctypes.c_size_t, _P, ctypes.c_int32,
+                                              ctypes.POINTER(ctypes.c_float)]
+_lib.hs2_cross_decoder_step_timed.restype = ctypes.c_int
+_lib.hs2_status_string.argtypes = [ctypes.c_int]
+_lib.hs2_status_string.restype = ctypes.c_char_p
+_lib.hs2_last_hip_error.argtypes = []
+_lib.hs2_last_hip_error.restype = ctypes.c_int
+
+
+class HS2Error(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = _lib.hs2_status_string(status).decode()
+        if status == HS2_ERR_HIP:
+            msg += f" (hipError {_lib.hs2_last_hip_error()})"
+        super().__init__(f"{fn}: {msg} [{status}]")
+        self.status = status
+
+
+@dataclass(frozen=True)
+class ShapeArgs:
+    batch: int
+    n_q_tokens: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    ctx_len: int
+    top_k: int = 1024
+    window: int = 128
+    scale: Optional[float] = None
+
+    def c(self) -> Shape:
+        scale = self.scale if self.scale is not None else 1.0 / math.sqrt(self.head_dim)
+        return Shape(ctx_len=self.ctx_len, scale=scale, batch=self.batch,
+                     n_q_tokens=self.n_q_tokens, n_q_heads=self.n_q_heads,
+                     n_kv_heads=self.n_kv_heads, head_dim=self.head_dim, top_k=self.top_k,
+                     window=self.window, reserved=0)
+
+    @property
+    def rows(self) -> int:
+        return self.batch * self.n_q_tokens * self.n_kv_heads
+
+    @property
+    def cap(self) -> int:
+        return self.top_k + self.window
+
+
+def shape_of(workload) -> ShapeArgs:
+    """ShapeArgs of a kv_reuse_amd.workloads.Workload."""
+    w = workload
+    return ShapeArgs(batch=w.batch, n_q_tokens=w.n_q_tokens, n_q_heads=w.n_q_heads,
+                     n_kv_heads=w.n_kv_heads, head_dim=w.head_dim, ctx_len=w.ctx_len,
+                     top_k=w.top_k, window=w.window, scale=w.scale)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(t: Optional[torch.Tensor], name: str, dtype, shape, allow_none=False):
+    if t is None:
+        if allow_none:
+            return
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU")
+
+
+def _call(fn: str, status: int):
+    if status != HS2_OK:
+        raise HS2Error(fn, status)
+
+
+def workspace_bytes(s: ShapeArgs, n_sparse_layers: int = 0) -> int:
+    return int(_lib.hs2_workspace_bytes(ctypes.byref(s.c()), int(n_sparse_layers)))
+
+
+def alloc_workspace(s: ShapeArgs, n_sparse_layers: int = 0, device="cuda") -> torch.Tensor:
+    n = workspace_bytes(s, n_sparse_layers)
+    if n == 0:
+        raise HS2Error("hs2_workspace_bytes", HS2_ERR_UNSUPPORTED)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def full_attn_scores(s: ShapeArgs, q, k, v, out, lse=None, scores=None, ws=None):
+    B, T, Hq, Hkv, D, S = s.batch, s.n_q_tokens, s.n_q_heads, s.n_kv_heads, s.head_dim, s.ctx_len
+    _check(q, "q", torch.bfloat16, (B, T, Hq, D))
+    _check(k, "k", torch.bfloat16, (B, Hkv, S, D))
+    _check(v, "v", torch.bfloat16, (B, Hkv, S, D))
+    _check(out, "out", torch.bfloat16, (B, T, Hq, D))
+    _check(lse, "lse", torch.float32, (B, T, Hq), allow_none=True)
+    _check(scores, "scores", torch.float32, (B, T, Hkv, S), allow_none=True)
+    ws = alloc_workspace(s, 0) if ws is None else ws
+    _call("hs2_full_attn_scores", _lib.hs2_full_attn_scores(
+        ctypes.byref(s.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(scores),
+        _ptr(ws), ws.numel(), _stream()))
+
+
+def topk_select(s: ShapeArgs, scores, idx, n_sel, ws=None):
+    B, T, Hkv, S = s.batch, s.n_q_tokens, s.n_kv_heads, s.ctx_len
+    _check(scores, "scores", torch.float32, (B, T, Hkv, S))
+    _check(idx, "idx", torch.int32, (B, T, Hkv, s.cap))
+    _check(n_sel, "n_sel", torch.int32, (B, T, Hkv))
+    ws = alloc_workspace(s, 0) if ws is None else ws
+    _call("hs2_topk_select", _lib.hs2_topk_select(
+        ctypes.byref(s.c()), _ptr(scores), _ptr(idx), _ptr(n_sel), _ptr(ws), ws.numel(),
+        _stream()))
+
+
+def sparse_attn(s: ShapeArgs, q, k, v, idx, n_sel, out, ws=None):
+    B, T, Hq, Hkv, D, S = s.batch, s.n_q_tokens, s.n_q_heads, s.n_kv_heads, s.head_dim, s.ctx_len
+    L = q.shape[0]
+    _check(q, "q", torch.bfloat16, (L, B, T, Hq, D))
+    _check(k, "k", torch.bfloat16, (B, Hkv, S, D))
+    _check(v, "v", torch.bfloat16, (B, Hkv, S, D))
+    _check(idx, "idx", torch.int32, (B, T, Hkv, s.cap))
+    _check(n_sel, "n_sel", torch.int32, (B, T, Hkv))
+    _check(out, "out", torch.bfloat16, (L, B, T, Hq, D))
+    ws = alloc_workspace(s, L) if ws is None else ws
+    _call("hs2_sparse_attn", _lib.hs2_sparse_attn(
+        ctypes.byref(s.c()), L, _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(n_sel), _ptr(out),
+        _ptr(ws), ws.numel(), _stream()))
+
+
+def cross_decoder_step(s: ShapeArgs, q_full, q_sparse, k, v, out_full, out_sparse, idx, n_sel,
+                       lse=None, scores=None, ws=None):
+    B, T, Hq, Hkv, D, S = s.batch, s.n_q_tokens, s.n_q_heads, s.n_kv_heads, s.head_dim, s.ctx_len
+    L = 0 if q_sparse is None else q_sparse.shape[0]
+    _check(q_full, "q_full", torch.bfloat16, (B, T, Hq, D))
+    _check(k, "k", torch.bfloat16, (B, Hkv, S, D))
+    _check(v, "v", torch.bfloat16, (B, Hkv, S, D))
+    _check(out_full, "out_full", torch.bfloat16, (B, T, Hq, D))
+    if L:
+        _check(q_sparse, "q_sparse", torch.bfloat16, (L, B, T, Hq, D))
+        _check(out_sparse, "out_sparse", torch.bfloat16, (L, B, T, Hq, D))
+    _check(idx, "idx", torch.int32, (B, T, Hkv, s.cap))
+    _check(n_sel, "n_sel", torch.int32, (B, T, Hkv))
+    _check(lse, "lse", torch.float32, (B, T, Hq), allow_none=True)
+    _check(scores, "scores", torch.float32, (B, T, Hkv, S), allow_none=True)
+    ws = alloc_workspace(s, L) if ws is None else ws
+    _call("hs2_cross_decoder_step", _lib.hs2_cross_decoder_step(
+        ctypes.byref(s.c()), L, _ptr(q_full), _ptr(q_sparse), _ptr(k), _ptr(v), _ptr(out_full),
+        _ptr(out_sparse), _ptr(idx), _ptr(n_sel), _ptr(lse), _ptr(scores), _ptr(ws), ws.numel(),
+        _stream()))
+
+
+def cross_decoder_step_timed(s: ShapeArgs, q_full, q_sparse, k, v, out_full, out_sparse, idx,
+                             n_sel, ws, iters: int):
+    """Per-phase average milliseconds [full split kernel, combine, selection, sparse]."""
+    L = 0 if q_sparse is None else q_sparse.shape[0]
+    ms = (ctypes.c_float * 4)()
+    _call("hs2_cross_decoder_step_timed", _lib.hs2_cross_decoder_step_timed(
+        ctypes.byref(s.c()), L, _ptr(q_full), _ptr(q_sparse), _ptr(k), _ptr(v), _ptr(out_full),
+        _ptr(out_sparse), _ptr(idx), _ptr(n_sel), _ptr(ws), ws.numel(), _stream(), int(iters), ms))
+    return [float(x) for x in ms]
+
+
+def raw():
+    """The ctypes library handle (for ABI tests)."""
+    return _lib

@@ -1,0 +1,127 @@
+"""Shared helpers of the GPU parity tests: run the HIP path through the C ABI
+(via the ctypes binding) and compare it with the CPU oracle on the same seeded
+inputs, to the project's acceptance rules:
+
+* index sets: same size as the oracle's, the forced window present, and every
+  key in the symmetric difference a candidate whose oracle score lies within
+  1e-6 (relative) of the k-th threshold tau;
+* bf16 outputs: max |err| <= 2e-2 and mean |err| <= 1e-2 against float64;
+* sparse outputs checked twice: against the oracle with its own indices, and
+  against the oracle run on the GPU's indices (separates selection from
+  arithmetic).
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle.hs2_oracle as orc
+from kv_reuse_amd import workloads as wl
+
+MAX_ABS = 2e-2
+MEAN_ABS = 1e-2
+BAND = 1e-6
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def dev(bits: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def host_f64(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def run_step(w: wl.Workload, x, with_scores=True, with_lse=True):
+    from kv_reuse_amd import hs2
+    s = hs2.shape_of(w)
+    B, T, Hq, Hkv, D, S, L = (w.batch, w.n_q_tokens, w.n_q_heads, w.n_kv_heads, w.head_dim,
+                              w.ctx_len, w.n_sparse_layers)
+    q = dev(x["q_full"])
+    k = dev(x["k"])
+    v = dev(x["v"])
+    qs = dev(x["q_sparse"]) if L else None
+    out = torch.empty((B, T, Hq, D), dtype=torch.bfloat16, device="cuda")
+    outs = torch.empty((L, B, T, Hq, D), dtype=torch.bfloat16, device="cuda") if L else None
+    idx = torch.empty((B, T, Hkv, s.cap), dtype=torch.int32, device="cuda")
+    nsel = torch.empty((B, T, Hkv), dtype=torch.int32, device="cuda")
+    lse = torch.empty((B, T, Hq), dtype=torch.float32, device="cuda") if with_lse else None
+    sc = torch.empty((B, T, Hkv, S), dtype=torch.float32, device="cuda") if with_scores else None
+    ws = hs2.alloc_workspace(s, L)
+    hs2.cross_decoder_step(s, q, qs, k, v, out, outs, idx, nsel, lse=lse, scores=sc, ws=ws)
+    torch.cuda.synchronize()
+    res = {"out_full": host_f64(out), "idx": idx.cpu().numpy(), "n_sel": nsel.cpu().numpy()}
+    if L:
+        res["out_sparse"] = host_f64(outs)
+    if with_lse:
+        res["lse"] = lse.cpu().numpy().astype(np.float64)
+    if with_scores:
+        res["scores"] = sc.cpu().numpy().astype(np.float64)
+    return res
+
+
+def check_outputs(got: np.ndarray, ref: np.ndarray, what: str):
+    err = np.abs(got - ref)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    assert err.max() <= MAX_ABS, f"{what}: max abs err {err.max():.3g}"
+    assert err.mean() <= MEAN_ABS, f"{what}: mean abs err {err.mean():.3g}"
+    return float(err.max()), float(err.mean())
+
+
+def check_index_row(gi: np.ndarray, n: int, ref: dict, what: str, top_k: int, window: int):
+    """gi: the GPU's idx row (cap entries), n: its n_sel; ref: the oracle row dict."""
+    pos = ref["pos"]
+    row = gi[:n]
+    assert np.all(gi[n:] == -1), f"{what}: padding must be -1"
+    assert np.all(np.diff(row) > 0), f"{what}: indices must be strictly ascending"
+    assert n == ref["idx"].size, f"{what}: n_sel {n} vs oracle {ref['idx'].size}"
+    first = max(0, pos - window + 1)
+    assert set(range(first, pos + 1)) <= set(row.tolist()), f"{what}: window missing"
+    sym = set(row.tolist()) ^ set(ref["idx"].tolist())
+    if sym:
+        tau = ref["tau"]
+        sc = ref["score"]
+        bad = [j for j in sym if j >= first or abs(sc[j] - tau) > BAND * tau]
+        assert not bad, (f"{what}: {len(bad)} keys differ outside the 1e-6 band, e.g. "
+                         f"{[(j, sc[j], tau) for j in bad[:3]]}")
+    return len(sym)
+
+
+def compare_step(w: wl.Workload, x, res, check_scores=True):
+    """Compare a whole step's GPU results with the oracle; returns summary stats."""
+    ref = orc.cross_decoder_step(x["q_full"], x["k"], x["v"],
+                                 x["q_sparse"] if w.n_sparse_layers else None,
+                                 top_k=w.top_k, window=w.window, scale=w.scale)
+    G = w.group
+    stats = {"max_full": 0.0, "max_sparse": 0.0, "sym": 0}
+    gpu_idx_oracle_sparse = []
+    for (b, t, g), rr in ref.items():
+        heads = slice(g * G, (g + 1) * G)
+        e, _ = check_outputs(res["out_full"][b, t, heads], rr["out_full"], f"out_full{(b, t, g)}")
+        stats["max_full"] = max(stats["max_full"], e)
+        if "lse" in res:
+            np.testing.assert_allclose(res["lse"][b, t, heads], rr["lse"], rtol=0, atol=2e-5)
+        n = int(res["n_sel"][b, t, g])
+        stats["sym"] += check_index_row(res["idx"][b, t, g], n, rr, f"idx{(b, t, g)}",
+                                        w.top_k, w.window)
+        if check_scores and "scores" in res:
+            pos = rr["pos"]
+            gs = res["scores"][b, t, g]
+            np.testing.assert_allclose(gs[: pos + 1], rr["score"], rtol=5e-5, atol=1e-30)
+            assert np.all(gs[pos + 1:] == 0.0)
+        if w.n_sparse_layers:
+            for n_l in range(w.n_sparse_layers):
+                e, _ = check_outputs(res["out_sparse"][n_l, b, t, heads], rr["out_sparse"][n_l],
+                                     f"out_sparse[{n_l}]{(b, t, g)}")
+                stats["max_sparse"] = max(stats["max_sparse"], e)
+            gpu_idx_oracle_sparse.append((b, t, g))
+    if w.n_sparse_layers and stats["sym"]:
+        # the oracle's sparse layers on the GPU's own index lists
+        ref2 = orc.sparse_step(x["q_sparse"], x["k"], x["v"], res["idx"], res["n_sel"], scale=w.scale)
+        check_outputs(res["out_sparse"], ref2, "out_sparse on GPU indices")
+    return stats

@@ -1,0 +1,130 @@
+"""C ABI of libhs2.so on the host: exported symbols, workspace sizing and argument
+validation.  Nothing here launches a kernel on a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+hs2 = pytest.importorskip("kv_reuse_amd.hs2")
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "hs2.h")
+
+FAKE = ctypes.c_void_p(0x10000)     # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    src = open(HEADER, encoding="utf-8").read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(hs2_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_function_is_exported():
+    names = declared_functions()
+    assert len(names) == 8
+    lib = hs2.raw()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(hs2.EXPORTED) == names
+
+
+def test_shape_struct_layout():
+    assert ctypes.sizeof(hs2.Shape) == 48
+    assert hs2.Shape.scale.offset == 8 and hs2.Shape.batch.offset == 16
+
+
+def good():
+    return hs2.ShapeArgs(batch=2, n_q_tokens=1, n_q_heads=16, n_kv_heads=2, head_dim=128,
+                         ctx_len=5000, top_k=64, window=16)
+
+
+def test_workspace_bytes_valid_and_monotone():
+    s = good()
+    n0 = hs2.workspace_bytes(s, 0)
+    n4 = hs2.workspace_bytes(s, 4)
+    assert n0 > 0 and n4 >= n0
+    big = hs2.ShapeArgs(batch=1, n_q_tokens=1, n_q_heads=32, n_kv_heads=4, head_dim=128,
+                        ctx_len=1 << 20)
+    # 8 float32 logits + a 32-bit selection key per key row dominate: > 36 bytes per key row
+    assert hs2.workspace_bytes(big, 8) > 36 * 4 * (1 << 20)
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("head_dim", 64, hs2.HS2_ERR_UNSUPPORTED),
+    ("n_q_heads", 8, hs2.HS2_ERR_UNSUPPORTED),        # G = 4
+    ("n_q_heads", 17, hs2.HS2_ERR_INVALID_ARG),       # not a multiple of Hkv
+    ("top_k", 5000, hs2.HS2_ERR_UNSUPPORTED),         # k + w > 4096
+    ("top_k", -1, hs2.HS2_ERR_INVALID_ARG),
+    ("window", -3, hs2.HS2_ERR_INVALID_ARG),
+    ("ctx_len", 0, hs2.HS2_ERR_INVALID_ARG),
+    ("ctx_len", 1 << 31, hs2.HS2_ERR_UNSUPPORTED),
+    ("n_q_tokens", 6000, hs2.HS2_ERR_INVALID_ARG),    # T > S
+    ("batch", 0, hs2.HS2_ERR_INVALID_ARG),
+    ("scale", -1.0, hs2.HS2_ERR_INVALID_ARG),
+    ("scale", float("nan"), hs2.HS2_ERR_INVALID_ARG),
+    ("reserved", 7, hs2.HS2_ERR_INVALID_ARG),
+])
+def test_bad_shapes_rejected(field, value, code):
+    c = good().c()
+    setattr(c, field, value)
+    lib = hs2.raw()
+    assert lib.hs2_workspace_bytes(ctypes.byref(c), 2) == 0
+    st = lib.hs2_full_attn_scores(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 1 << 40, None)
+    assert st == code
+    st = lib.hs2_cross_decoder_step(ctypes.byref(c), 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                    FAKE, None, None, FAKE, 1 << 40, None)
+    assert st == code
+
+
+def test_null_pointers_and_workspace_errors():
+    lib = hs2.raw()
+    c = good().c()
+    need = lib.hs2_workspace_bytes(ctypes.byref(c), 3)
+    E = hs2.HS2_ERR_INVALID_ARG
+    assert lib.hs2_full_attn_scores(None, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, need, None) == E
+    assert lib.hs2_full_attn_scores(ctypes.byref(c), None, FAKE, FAKE, FAKE, None, None, FAKE, need, None) == E
+    assert lib.hs2_full_attn_scores(ctypes.byref(c), FAKE, FAKE, FAKE, None, None, None, FAKE, need, None) == E
+    assert lib.hs2_topk_select(ctypes.byref(c), None, FAKE, FAKE, FAKE, need, None) == E
+    assert lib.hs2_topk_select(ctypes.byref(c), FAKE, FAKE, None, FAKE, need, None) == E
+    assert lib.hs2_sparse_attn(ctypes.byref(c), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == E
+    assert lib.hs2_sparse_attn(ctypes.byref(c), 3, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, need, None) == E
+    # sparse layers requested without their tensors
+    assert lib.hs2_cross_decoder_step(ctypes.byref(c), 3, FAKE, None, FAKE, FAKE, FAKE, None, FAKE,
+                                      FAKE, None, None, FAKE, need, None) == E
+    # workspace: too small, missing, misaligned
+    W = hs2.HS2_ERR_WORKSPACE
+    assert lib.hs2_cross_decoder_step(ctypes.byref(c), 3, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      FAKE, None, None, FAKE, need - 1, None) == W
+    assert lib.hs2_topk_select(ctypes.byref(c), FAKE, FAKE, FAKE, None, need, None) == E
+    assert lib.hs2_topk_select(ctypes.byref(c), FAKE, FAKE, FAKE, ctypes.c_void_p(0x10010), need, None) == E
+    # timed variant validates the same way
+    ms = (ctypes.c_float * 4)()
+    assert lib.hs2_cross_decoder_step_timed(ctypes.byref(c), 3, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                            FAKE, FAKE, FAKE, need, None, 0, ms) == E
+
+
+def test_prefill_chunk_full_layer_reported_unsupported_or_accepted():
+    lib = hs2.raw()
+    c = good().c()
+    c.n_q_tokens = 4
+    need = lib.hs2_workspace_bytes(ctypes.byref(c), 0)
+    assert need > 0
+
+
+def test_status_strings():
+    lib = hs2.raw()
+    for code in (0, -1, -2, -3, -4):
+        assert lib.hs2_status_string(code).decode() != "unknown status"
+    assert lib.hs2_status_string(99).decode() == "unknown status"
+
+
+def test_valid_call_without_gpu_reports_hip_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    lib = hs2.raw()
+    c = good().c()
+    need = lib.hs2_workspace_bytes(ctypes.byref(c), 0)
+    st = lib.hs2_topk_select(ctypes.byref(c), FAKE, FAKE, FAKE, ctypes.c_void_p(0x100000), need, None)
+    assert st == hs2.HS2_ERR_HIP
+    assert lib.hs2_last_hip_error() != 0
