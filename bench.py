@@ -1,0 +1,200 @@
+"""Benchmark: one Cross-Decoder group step (full attention + importance, token
+top-k with the forced window, N KV-reusing sparse layers) on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+Prints ONE JSON line.  The default workload is decode at 1M context (batch 1,
+32 query / 4 KV heads, head dim 128, 8 sparse layers, top-1024 + recent 128).
+`value` is query tokens per second of the whole step with inputs resident in
+HBM; `roofline` rates the dominant kernel (the full layer's split-context
+stream) by its algorithmic bytes (K + V + Q + O + 4 bytes of importance per key
+row) over its own average duration, timed with HIP events on the stream it runs
+on; `cpu_baseline` is the float64 CPU oracle on a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "query tokens/s, full+sparse Cross-Decoder attn at 1M ctx; HBM TB/s vs peak"
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "full_decode_split_decode_1m_pmc.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "kv_reuse_amd", "csrc", f)
+                  for f in ("full_decode.hip", "hs2_internal.h")]
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the full-layer kernel from the committed rocprofv3
+    counter summary, if it was taken on this workload and this kernel source."""
+    try:
+        txt = open(TRAFFIC_SUMMARY, encoding="utf-8").read()
+    except OSError:
+        return None
+    m = re.search(r"traffic_record: workload=(\S+) source=(\S+) fetch_bytes=(\d+) "
+                  r"write_bytes=(\d+)", txt)
+    if not m or m.group(1) != workload or m.group(2) != kernel_source_hash():
+        return None
+    return int(m.group(3)) + int(m.group(4))
+
+
+def algorithmic_full_layer_bytes(w) -> int:
+    """K + V once, Q in, O out, and 4 bytes of importance per (row, key)."""
+    rows = w.batch * w.n_q_tokens * w.n_kv_heads
+    kv = 2 * w.batch * w.n_kv_heads * w.ctx_len * w.head_dim * 2
+    qo = 2 * w.batch * w.n_q_tokens * w.n_q_heads * w.head_dim * 2
+    return kv + qo + 4 * rows * w.ctx_len
+
+
+def cpu_baseline(w, x, budget_s: float = 20.0):
+    """Time the CPU oracle (as it stands) on whole (batch, KV head) rows of the
+    same inputs until the budget is used; scale to query tokens per second."""
+    import numpy as np  # noqa: F401
+    from threadpoolctl import threadpool_info
+    import oracle.hs2_oracle as orc
+    rows = [(b, 0, g) for b in range(w.batch) for g in range(w.n_kv_heads)]
+    done = 0
+    t0 = time.perf_counter()
+    for r in rows:
+        orc.cross_decoder_step(x["q_full"], x["k"], x["v"], x["q_sparse"], top_k=w.top_k,
+                               window=w.window, scale=w.scale, rows=[r], keep_scores=False)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    tokens = done / w.n_kv_heads          # one query token spans all KV heads of its batch row
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    return {"value": tokens / dt, "unit": "query tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {len(rows)} (batch, KV head) rows of {w.name}: full float64 "
+                      f"attention over all {w.ctx_len} keys, group-max importance, full sort, "
+                      f"{w.n_sparse_layers} sparse layers; {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_1m_b1_heavy")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this path has no multi-GPU form in this build "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from kv_reuse_amd import hs2
+    from kv_reuse_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    w = wl.WORKLOADS[args.workload]
+    if w.n_q_tokens != 1:
+        print("bench.py times the decode workloads", file=sys.stderr)
+        sys.exit(1)
+    log(f"[bench] generating {w.name}")
+    x = wl.generate(w)
+    s = hs2.shape_of(w)
+    B, T, Hq, Hkv, D, S, L = (w.batch, w.n_q_tokens, w.n_q_heads, w.n_kv_heads, w.head_dim,
+                              w.ctx_len, w.n_sparse_layers)
+
+    def dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    q, k, v, qs = dev(x["q_full"]), dev(x["k"]), dev(x["v"]), dev(x["q_sparse"])
+    out = torch.empty((B, T, Hq, D), dtype=torch.bfloat16, device="cuda")
+    outs = torch.empty((L, B, T, Hq, D), dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty((B, T, Hkv, s.cap), dtype=torch.int32, device="cuda")
+    nsel = torch.empty((B, T, Hkv), dtype=torch.int32, device="cuda")
+    ws = hs2.alloc_workspace(s, L)
+    torch.cuda.synchronize()
+
+    def step():
+        hs2.cross_decoder_step(s, q, qs, k, v, out, outs, idx, nsel, ws=ws)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    tokens_per_s = B * T / (ms_step / 1e3)
+
+    log("[bench] per-phase timing")
+    phases = hs2.cross_decoder_step_timed(s, q, qs, k, v, out, outs, idx, nsel, ws,
+                                          max(args.steps, 10))
+    full_ms = phases[0]
+    algo = algorithmic_full_layer_bytes(w)
+    achieved = algo / (full_ms * 1e-3) / 1e9
+    traffic = measured_traffic(w.name)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 2),
+        "unit": "query tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "n_q_tokens": T, "ctx_len": S,
+                   "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": D, "top_k": w.top_k,
+                   "window": w.window, "n_sparse_layers": L},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "full_decode_split_kernel",
+                     "algorithmic_bytes": algo, "kernel_ms": round(full_ms, 5)},
+        "phases_ms": {"full_split": round(phases[0], 5), "full_combine": round(phases[1], 5),
+                      "select": round(phases[2], 5), "sparse": round(phases[3], 5)},
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        rec["cpu_baseline"] = cpu_baseline(w, x)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -18,8 +18,8 @@
 //    padding; the kernel is bound by HBM bytes, not by MFMA issue.
 //  * O^T = V^T . P^T on MFMA: P^T comes out of the S^T accumulators already in
 //    the B-operand lane layout (head = lane % 16), so only V needs a transpose;
-//    it goes through a per-wave LDS tile with a 272-byte row pitch that makes
-//    the column reads conflict-free.
+//    it goes through a per-wave LDS tile (272-byte row pitch) and comes back
+//    transposed with two ds_read_b64_tr_b16 per MFMA operand.
 //  * Online softmax in base 2 with the running max rounded up to an integer:
 //    every rescale factor is an exact power of two, and the normaliser l is
 //    accumulated in float64, so the only error left in log-sum-exp comes from
@@ -138,20 +138,8 @@ __device__ __forceinline__ void process_tile(const KVTile& t, SoftmaxState& st,
                  pack_bf16x2(p[6], p[7])};
   const bf16x8 pb = as_bf16x8(pp);
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) {
-    const u16* vc = vw + 16 * nb + col;
-    uint32_t a[4];
-#pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-      // elements e = 2*e2, 2*e2+1 -> keys 16*(e>>2) + 4*grp + (e&3)
-      const int e0 = 2 * e2, e1 = 2 * e2 + 1;
-      const int k0 = 16 * (e0 >> 2) + 4 * grp + (e0 & 3);
-      const int k1 = 16 * (e1 >> 2) + 4 * grp + (e1 & 3);
-      a[e2] = static_cast<uint32_t>(vc[k0 * kVPitch]) |
-              (static_cast<uint32_t>(vc[k1 * kVPitch]) << 16);
-    }
-    st.o[nb] = mfma_16x16x32(as_bf16x8(u32x4{a[0], a[1], a[2], a[3]}), pb, st.o[nb]);
-  }
+  for (int nb = 0; nb < 8; ++nb)
+    st.o[nb] = mfma_16x16x32(lds_vt_operand(vw, kVPitch, nb, col, grp), pb, st.o[nb]);
 }
 
 __global__ __launch_bounds__(kWaves * 64, 2) void full_decode_split_kernel(

@@ -112,6 +112,27 @@ __device__ __forceinline__ uint64_t ordered_u64(double d) {
   uint64_t u = static_cast<uint64_t>(__double_as_longlong(d));
   return (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
 }
+// LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane i receives element (i & 3) of the 8-byte chunk addressed by lane
+// 4*e + (i >> 2), for e = 0..3.  So if lane i of a group addresses row
+// base_row + (i >> 2), column c0 + 4*(i & 3) of a row-major bf16 tile, lane i
+// gets column c0 + i of rows base_row .. base_row + 3.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16_b64(const u16* p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(uint2, r);
+}
+// V^T operand (A of O^T = V^T P^T) for d-block nb from a row-major V tile in
+// LDS with row pitch `pitch`: lane (grp, col) gets V[key(grp, e)][16*nb + col]
+// for e = 0..7 with key(grp, e) = 16*(e >> 2) + 4*grp + (e & 3).
+__device__ __forceinline__ bf16x8 lds_vt_operand(const u16* tile, int pitch, int nb, int col,
+                                                 int grp) {
+  const u16* p0 = tile + (4 * grp + (col >> 2)) * pitch + 16 * nb + 4 * (col & 3);
+  const uint2 a = lds_read_tr16_b64(p0);
+  const uint2 b = lds_read_tr16_b64(p0 + 16 * pitch);
+  return as_bf16x8(u32x4{a.x, a.y, b.x, b.y});
+}
 // Wait until this wave's outstanding LDS operations are done, and keep the
 // compiler from moving memory accesses across this point.
 __device__ __forceinline__ void lds_fence_wave() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }

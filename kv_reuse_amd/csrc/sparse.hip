@@ -118,17 +118,7 @@ __global__ __launch_bounds__(NCT * 64) void sparse_kernel(
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) {
         o[nb] *= alpha;
-        const u16* vc = vlds + kb * kPitch + 16 * nb + col;
-        uint32_t a[4];
-#pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const int e0 = 2 * e2, e1 = 2 * e2 + 1;
-          const int k0 = 16 * (e0 >> 2) + 4 * grp + (e0 & 3);
-          const int k1 = 16 * (e1 >> 2) + 4 * grp + (e1 & 3);
-          a[e2] = static_cast<uint32_t>(vc[k0 * kPitch]) |
-                  (static_cast<uint32_t>(vc[k1 * kPitch]) << 16);
-        }
-        o[nb] = mfma_16x16x32(as_bf16x8(u32x4{a[0], a[1], a[2], a[3]}), pb, o[nb]);
+        o[nb] = mfma_16x16x32(lds_vt_operand(vlds + kb * kPitch, kPitch, nb, col, grp), pb, o[nb]);
       }
     }
   }

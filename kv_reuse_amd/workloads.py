@@ -18,11 +18,13 @@ Recipe (the same for every workload; sizes per workload below):
 
 * one ``numpy.random.SeedSequence(seed)`` spawns independent child streams in
   this fixed order: q_full, k, v, needle positions, drift, heavy-tail
-  positions, then one stream per sparse layer for q_sparse[n];
+  positions, then one stream per sparse layer for q_sparse[n]; the k, v,
+  drift and heavy-tail streams each spawn one grandchild per (batch, kv head)
+  row, in row-major order, so that rows can be drawn in parallel threads;
 * every tensor entry is a float32 standard normal, rounded to bfloat16 with
   round-to-nearest-even;
-* drift (256K workload): per (batch, kv head, dim) a random walk along the
-  sequence with N(0, sd^2) steps, added to the N(0,1) draw before rounding;
+* drift (256K workload): per (batch, kv head, dim) a float32 random walk along
+  the sequence with N(0, sd^2) steps, added to the N(0,1) draw before rounding;
 * heavy tail (1M workload): round(frac * S) key rows per (batch, kv head),
   drawn without replacement, are multiplied by ``heavy_mult`` before rounding;
 * needles (decode): ``n_needles`` positions per (batch, kv head) drawn
@@ -37,7 +39,9 @@ Recipe (the same for every workload; sizes per workload below):
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import dataclasses
+import os
 from dataclasses import dataclass
 from typing import Dict, Optional
 
@@ -110,10 +114,16 @@ WORKLOADS: Dict[str, Workload] = {
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to bfloat16 (round-to-nearest-even); return uint16 bits."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    u = u + (((u >> 16) & 1) + 0x7FFF)
-    return (u >> 16).astype(np.uint16)
+    """Round float32 values to bfloat16 (round-to-nearest-even); return uint16 bits.
+
+    Finite inputs only (the sum below cannot overflow 32 bits for them)."""
+    u = np.array(x, dtype=np.float32, copy=True).view(np.uint32)
+    lsb = u >> np.uint32(16)
+    lsb &= np.uint32(1)
+    u += np.uint32(0x7FFF)
+    u += lsb
+    u >>= np.uint32(16)
+    return u.astype(np.uint16)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -140,26 +150,42 @@ def generate(w: Workload, seed: Optional[int] = None,
     if Hq % Hkv:
         raise ValueError("n_q_heads must be a multiple of n_kv_heads")
     children = np.random.SeedSequence(seed).spawn(6 + w.n_sparse_layers)
-    rq, rk, rv, rneedle, rdrift, rheavy = (np.random.Generator(np.random.PCG64(c))
-                                            for c in children[:6])
+    rq = np.random.Generator(np.random.PCG64(children[0]))
+    rneedle = np.random.Generator(np.random.PCG64(children[3]))
 
     q_full = f32_to_bf16_bits(_normal_f32(rq, (B, T, Hq, D)))
     k = np.empty((B, Hkv, S, D), dtype=np.uint16)
     v = np.empty((B, Hkv, S, D), dtype=np.uint16)
-    for b in range(B):
-        for g in range(Hkv):
-            z = _normal_f32(rk, (S, D))
-            if w.drift_sd > 0.0:
-                steps = rdrift.standard_normal(size=(S, D)) * w.drift_sd
-                z = (z.astype(np.float64) + np.cumsum(steps, axis=0)).astype(np.float32)
-                del steps
-            if w.heavy_frac > 0.0:
-                n_heavy = int(round(w.heavy_frac * S))
-                pos = rheavy.choice(S, size=n_heavy, replace=False)
-                z[pos] *= np.float32(w.heavy_mult)
-            k[b, g] = f32_to_bf16_bits(z)
-            del z
-            v[b, g] = f32_to_bf16_bits(_normal_f32(rv, (S, D)))
+    n_rows = B * Hkv
+    ks, vs, ds, hs = (c.spawn(n_rows) for c in (children[1], children[2], children[4],
+                                                children[5]))
+
+    def make_row(i: int) -> None:
+        b, g = divmod(i, Hkv)
+        z = _normal_f32(np.random.Generator(np.random.PCG64(ks[i])), (S, D))
+        if w.drift_sd > 0.0:
+            steps = _normal_f32(np.random.Generator(np.random.PCG64(ds[i])), (S, D))
+            steps *= np.float32(w.drift_sd)
+            np.cumsum(steps, axis=0, out=steps)        # float32 random walk along S
+            z += steps
+            del steps
+        if w.heavy_frac > 0.0:
+            n_heavy = int(round(w.heavy_frac * S))
+            pos = np.random.Generator(np.random.PCG64(hs[i])).choice(S, size=n_heavy,
+                                                                      replace=False)
+            z[pos] *= np.float32(w.heavy_mult)
+        k[b, g] = f32_to_bf16_bits(z)
+        del z
+        v[b, g] = f32_to_bf16_bits(_normal_f32(np.random.Generator(np.random.PCG64(vs[i])),
+                                               (S, D)))
+
+    workers = max(1, min(n_rows, os.cpu_count() or 1, 8))
+    if workers == 1:
+        for i in range(n_rows):
+            make_row(i)
+    else:
+        with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(make_row, range(n_rows)))
 
     if w.n_needles > 0:
         qf = bf16_bits_to_f32(q_full).astype(np.float64)

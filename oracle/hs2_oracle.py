@@ -204,6 +204,10 @@ def sparse_step(q: np.ndarray, k: np.ndarray, v: np.ndarray, idx: np.ndarray,
             vv = widen_bf16(v[b, g])
             for t in range(T):
                 sel = np.asarray(idx[b, t, g, : int(n_sel[b, t, g])], dtype=np.int64)
+                if sel.size == 0:
+                    # reading: with nothing selected there is no softmax; the
+                    # sparse entry point defines such a row's output as zeros
+                    continue
                 for n in range(L):
                     qn = widen_bf16(q[n, b, t, g * G:(g + 1) * G])
                     out[n, b, t, g * G:(g + 1) * G] = sparse_attention_row(qn, kk, vv, sel, scale)

@@ -260,6 +260,22 @@ def pin_widening(orc, seed=10):
     np.testing.assert_array_equal(orc.widen_bf16(bits), ref)
 
 
+
+
+def pin_sparse_step_empty_rows(orc, seed=11):
+    """A row whose index list is empty gets zeros; the other rows are unaffected."""
+    r = _rng(seed)
+    bits = _bits(r.standard_normal((1, 1, 1, 8, 8)))
+    kv = _bits(r.standard_normal((1, 1, 10, 8)))
+    idx = np.array([[[[0, 3, 9, -1]]]])
+    out = orc.sparse_step(bits, kv, kv, idx, np.array([[[0]]]), scale=0.3)
+    assert np.all(out == 0.0)
+    out = orc.sparse_step(bits, kv, kv, idx, np.array([[[3]]]), scale=0.3)
+    ref = orc.sparse_attention_row(_f64(bits[0, 0, 0]), _f64(kv[0, 0]), _f64(kv[0, 0]),
+                                   np.array([0, 3, 9]), 0.3)
+    np.testing.assert_allclose(out[0, 0, 0], ref, rtol=1e-14)
+
+
 ALL_PINS = [
     pin_full_attention_vs_sdpa,
     pin_attention_closed_forms,
@@ -271,4 +287,5 @@ ALL_PINS = [
     pin_sparse_sliding_window,
     pin_sparse_permutation_invariance,
     pin_widening,
+    pin_sparse_step_empty_rows,
 ]
