@@ -114,7 +114,9 @@ int hs2_topk_select(const hs2_shape* shape, const float* scores, int32_t* idx, i
 /* Sparse attention of n_layers layers that reuse one KV cache and one index
  * list per row: for layer n, out^(n)_h = softmax_i(scale * <q^(n)_h, k_i>) . V_i
  * over i in idx[b][t][g][0..n_sel).  q [N][B][T][Hq][D], out [N][B][T][Hq][D];
- * idx / n_sel as written by hs2_topk_select (entries must be in [0, P_t]).
+ * idx / n_sel as written by hs2_topk_select (entries must be in [0, P_t];
+ * an entry outside [0, S) is clamped into it, so a malformed list gives wrong
+ * numbers for its row but never an out-of-bounds read).
  * Rows with n_sel = 0 get zero outputs.  News page, section
  * "两级KV共享：让模型少跑一半" (the sparse layers reuse the cache and the
  * selection). */

@@ -10,12 +10,11 @@
 //  * A row is (batch, KV head): the 8 query heads of the GQA group share one
 //    K/V stream.  The context is cut into splits; one work-group of 4 waves
 //    streams one split, each wave taking every 4th tile of 32 keys, so the
-//    work-group sweeps its split front to back.  Split partials (m, l, O) are
-//    merged by full_combine_kernel.
+//    work-group sweeps its split front to back.
 //  * S^T = K . Q^T on MFMA 16x16x32 bf16: K rows are the A operand (16 keys per
-//    MFMA, loaded straight from HBM with 16-byte loads), the group's queries
-//    padded to 16 heads are the B operand.  Half of the MFMA columns are
-//    padding; the kernel is bound by HBM bytes, not by MFMA issue.
+//    MFMA, loaded straight from HBM with 16-byte non-temporal loads), the
+//    group's queries padded to 16 heads are the B operand.  Half of the MFMA
+//    columns are padding; the kernel is bound by HBM bytes, not by MFMA issue.
 //  * O^T = V^T . P^T on MFMA: P^T comes out of the S^T accumulators already in
 //    the B-operand lane layout (head = lane % 16), so only V needs a transpose;
 //    it goes through a per-wave LDS tile (272-byte row pitch) and comes back
@@ -24,9 +23,14 @@
 //    every rescale factor is an exact power of two, and the normaliser l is
 //    accumulated in float64, so the only error left in log-sum-exp comes from
 //    the float32 logits themselves.
-//  * Every key's float32 base-2 logit (scale*log2(e)*<q_h,k_j>) of every head is
-//    written once (32 bytes per key row next to its 512 bytes of K/V); the
-//    selection turns them into importances once lse is known.
+//  * The only per-key output is, for every subtile of 16 keys and every head,
+//    the largest float32 base-2 logit (2 bytes per key row next to its 512
+//    bytes of K/V).  Once lse is known this bounds every key's importance from
+//    above, and the bound is attained by one of the subtile's own keys; the
+//    selection uses that to find the few subtiles that can hold selected keys.
+//    (Writing all logits, 32 bytes per key row, cost about 45% of the kernel's
+//    time on MI355X: the write stream slows the 2 GiB read stream far more than
+//    its byte count.)
 //  * The next tile's K/V loads are issued before the current tile is processed
 //    (two register buffers), so each wave keeps 16 KB of HBM reads in flight.
 
@@ -59,65 +63,59 @@ __device__ __forceinline__ void load_tile(KVTile& t, const u16* __restrict__ kr,
     key = key < key_last ? key : key_last;
     const u16* base = kr + key * kD + 8 * grp;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) t.ka[mt][c] = as_bf16x8(load_u32x4(base + 32 * c));
+    for (int c = 0; c < 4; ++c) t.ka[mt][c] = as_bf16x8(load_u32x4_nt(base + 32 * c));
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     int64_t key = t0 + grp + 4 * i;
     key = key < key_last ? key : key_last;
-    t.vv[i] = load_u32x4(vr + key * kD + 8 * col);
+    t.vv[i] = load_u32x4_nt(vr + key * kD + 8 * col);
   }
 }
 
-__device__ __forceinline__ float max8(const float* x) {
-  float a = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-  float b = fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7]));
-  return fmaxf(a, b);
-}
-
-__device__ __forceinline__ void process_tile(const KVTile& t, SoftmaxState& st,
-                                             const bf16x8 (&qb)[4], u16* __restrict__ vw,
-                                             float* __restrict__ lg, int64_t t0,
-                                             int64_t key_end, int col, int grp, float c2_hi,
-                                             float c2_lo) {
-  // ---- S^T = K Q^T for 32 keys
+// S^T for one tile: lane (col, grp) gets the base-2 logits of head col for keys
+// t0 + 16*mt + 4*grp + i in sv[4*mt + i] (-inf past key_end).
+__device__ __forceinline__ void tile_logits(const bf16x8 (&ka)[2][4], const bf16x8 (&qb)[4],
+                                            int64_t t0, int64_t key_end, int grp, float c2_hi,
+                                            float c2_lo, float (&sv)[8]) {
   f32x4 sacc[2];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
     sacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) sacc[mt] = mfma_16x16x32(t.ka[mt][c], qb[c], sacc[mt]);
+    for (int c = 0; c < 4; ++c) sacc[mt] = mfma_16x16x32(ka[mt][c], qb[c], sacc[mt]);
   }
-  // base-2 logits; the scale is applied as a two-term product so that its
-  // float32 rounding does not bias every logit of the row the same way
-  float sv[8];
+  // the scale is applied as a two-term product so that its float32 rounding
+  // does not bias every logit of the row the same way
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t key = t0 + 16 * mt + 4 * grp + i;
       const float a = sacc[mt][i];
-      const float x = fmaf(a, c2_hi, a * c2_lo);
-      sv[mt * 4 + i] = key < key_end ? x : -INFINITY;
+      sv[mt * 4 + i] = key < key_end ? fmaf(a, c2_hi, a * c2_lo) : -INFINITY;
     }
-  if (col < kG) {
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int64_t key0 = t0 + 16 * mt + 4 * grp;
-      if (key0 + 3 < key_end) {
-        *reinterpret_cast<f32x4*>(lg + key0) =
-            f32x4{sv[mt * 4], sv[mt * 4 + 1], sv[mt * 4 + 2], sv[mt * 4 + 3]};
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (key0 + i < key_end) lg[key0 + i] = sv[mt * 4 + i];
-      }
-    }
-  }
+}
+
+__device__ __forceinline__ void process_tile(const KVTile& t, SoftmaxState& st,
+                                             const bf16x8 (&qb)[4], u16* __restrict__ vw,
+                                             float* __restrict__ stmax_row, int64_t t0,
+                                             int64_t key_end, int col, int grp, float c2_hi,
+                                             float c2_lo) {
+  float sv[8];
+  tile_logits(t.ka, qb, t0, key_end, grp, c2_hi, c2_lo, sv);
+  // per-subtile (16 keys) maxima of each head: lanes of one head are col + 16*grp
+  float m0 = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+  float m1 = fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7]));
+  m0 = fmaxf(m0, __shfl_xor(m0, 16));
+  m1 = fmaxf(m1, __shfl_xor(m1, 16));
+  m0 = fmaxf(m0, __shfl_xor(m0, 32));
+  m1 = fmaxf(m1, __shfl_xor(m1, 32));
+  // subtile t0/16 + mt, head col: 64 contiguous bytes per tile (grp 0 and 1)
+  if (col < kG && grp < 2 && t0 + 16 * grp < key_end)
+    stmax_row[(t0 / 16 + grp) * kG + col] = grp == 0 ? m0 : m1;
   // ---- online softmax (per head = per lane % 16)
-  float tm = max8(sv);
-  tm = fmaxf(tm, __shfl_xor(tm, 16));
-  tm = fmaxf(tm, __shfl_xor(tm, 32));
+  const float tm = fmaxf(m0, m1);
   const float m_new = fmaxf(st.m, ceilf(tm));
   const float alpha = (st.m == -INFINITY) ? 0.f : ldexpf(1.f, static_cast<int>(st.m - m_new));
   float p[8];
@@ -128,7 +126,7 @@ __device__ __forceinline__ void process_tile(const KVTile& t, SoftmaxState& st,
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) st.o[nb] *= alpha;
   st.m = m_new;
-  // ---- V tile to LDS (natural layout), then V^T operands by column reads
+  // ---- V tile to LDS (natural layout), then V^T operands by transpose reads
 #pragma unroll
   for (int i = 0; i < 8; ++i)
     *reinterpret_cast<u32x4*>(vw + (grp + 4 * i) * kVPitch + 8 * col) = t.vv[i];
@@ -142,9 +140,17 @@ __device__ __forceinline__ void process_tile(const KVTile& t, SoftmaxState& st,
     st.o[nb] = mfma_16x16x32(lds_vt_operand(vw, kVPitch, nb, col, grp), pb, st.o[nb]);
 }
 
+__device__ __forceinline__ void load_q_operand(const u16* __restrict__ qr, int col, int grp,
+                                               bf16x8 (&qb)[4]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    qb[c] = col < kG ? as_bf16x8(load_u32x4(qr + col * kD + 32 * c + 8 * grp))
+                     : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+}
+
 __global__ __launch_bounds__(kWaves * 64, 2) void full_decode_split_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
-    float* __restrict__ logits, float* __restrict__ part_m, double* __restrict__ part_l,
+    float* __restrict__ stmax, float* __restrict__ part_m, double* __restrict__ part_l,
     float* __restrict__ part_o, int64_t S, int64_t Spad, int kps, int n_split, float c2_hi,
     float c2_lo) {
   // V tiles during the stream; reused for the cross-wave merge afterwards
@@ -160,17 +166,13 @@ __global__ __launch_bounds__(kWaves * 64, 2) void full_decode_split_kernel(
   const int s = blockIdx.x;
   const int64_t key_begin = static_cast<int64_t>(s) * kps;
   const int64_t key_end = min(S, key_begin + kps);
-  const u16* qr = q + static_cast<size_t>(r) * kG * kD;
   const u16* kr = k + static_cast<size_t>(r) * S * kD;
   const u16* vr = v + static_cast<size_t>(r) * S * kD;
-  float* lg = logits + (static_cast<size_t>(r) * kG + (col < kG ? col : 0)) * Spad;
+  float* stmax_row = stmax + static_cast<size_t>(r) * (Spad / 16) * kG;
   u16* vw = reinterpret_cast<u16*>(smem) + wave * kTile * kVPitch;
 
   bf16x8 qb[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-    qb[c] = col < kG ? as_bf16x8(load_u32x4(qr + col * kD + 32 * c + 8 * grp))
-                     : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+  load_q_operand(q + static_cast<size_t>(r) * kG * kD, col, grp, qb);
 
   SoftmaxState st;
 #pragma unroll
@@ -188,13 +190,13 @@ __global__ __launch_bounds__(kWaves * 64, 2) void full_decode_split_kernel(
       int64_t t1 = t0 + stride;
       bool more = t1 < key_end;
       if (more) load_tile(tb, kr, vr, t1, key_last, col, grp);
-      process_tile(ta, st, qb, vw, lg, t0, key_end, col, grp, c2_hi, c2_lo);
+      process_tile(ta, st, qb, vw, stmax_row, t0, key_end, col, grp, c2_hi, c2_lo);
       if (!more) break;
       t0 = t1;
       t1 = t0 + stride;
       more = t1 < key_end;
       if (more) load_tile(ta, kr, vr, t1, key_last, col, grp);
-      process_tile(tb, st, qb, vw, lg, t0, key_end, col, grp, c2_hi, c2_lo);
+      process_tile(tb, st, qb, vw, stmax_row, t0, key_end, col, grp, c2_hi, c2_lo);
       if (!more) break;
       t0 = t1;
     }
@@ -240,66 +242,164 @@ __global__ __launch_bounds__(kWaves * 64, 2) void full_decode_split_kernel(
   }
 }
 
-// One work-group per row: merge the split partials.
-__global__ __launch_bounds__(256) void full_combine_kernel(
+// Level 1 of the split merge: grid (groups, kG, R), work-group (gi, h, r)
+// merges the kCmbGroup splits of group gi for head h.  All of its loads are
+// issued in one round.  It also clears the row's selection state.
+__global__ __launch_bounds__(256) void full_merge_kernel(
     const float* __restrict__ part_m, const double* __restrict__ part_l,
-    const float* __restrict__ part_o, int n_split, u16* __restrict__ out,
-    float* __restrict__ lse_out, double* __restrict__ lse2, float* __restrict__ ytop,
-    uint32_t* __restrict__ hist, RowInfo* __restrict__ info) {
-  extern __shared__ float fac[];  // [n_split][kG]
-  __shared__ float sM[kG];
-  __shared__ double sL[kG];
-  const int r = blockIdx.x;
+    const float* __restrict__ part_o, int n_split, int n_groups, float* __restrict__ cmb_m,
+    double* __restrict__ cmb_l, float* __restrict__ cmb_o, uint32_t* __restrict__ hist,
+    RowInfo* __restrict__ info) {
+  __shared__ float sm[kCmbGroup];
+  __shared__ double sl[kCmbGroup];
+  __shared__ float half_o[kD];
+  const int gi = blockIdx.x, h = blockIdx.y, r = blockIdx.z;
   const int tid = threadIdx.x;
+  const int d = tid & 127, hf = tid >> 7;
+  const int s0 = gi * kCmbGroup;
+  const int ns = min(kCmbGroup, n_split - s0);
   const size_t rb = static_cast<size_t>(r) * n_split;
-  {
-    const int h = tid >> 5, j = tid & 31;  // 8 heads x 32 lanes
-    float M = -INFINITY;
-    for (int s = j; s < n_split; s += 32) M = fmaxf(M, part_m[(rb + s) * kG + h]);
+  if (tid < ns) {
+    sm[tid] = part_m[(rb + s0 + tid) * kG + h];
+    sl[tid] = part_l[(rb + s0 + tid) * kG + h];
+  }
+  float ov[kCmbGroup / 2];
+  const float* po = part_o + ((rb + s0) * kG + h) * kD + d;
 #pragma unroll
-    for (int off = 16; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 32));
-    double L = 0.0;
-    for (int s = j; s < n_split; s += 32) {
-      const float ms = part_m[(rb + s) * kG + h];
-      if (ms != -INFINITY) L += part_l[(rb + s) * kG + h] * ldexp(1.0, static_cast<int>(ms - M));
-    }
-#pragma unroll
-    for (int off = 16; off > 0; off >>= 1) L += __shfl_xor(L, off, 32);
-    if (j == 0) {
-      sM[h] = M;
-      sL[h] = L;
-    }
+  for (int i = 0; i < kCmbGroup / 2; ++i) {
+    const int s = hf + 2 * i;
+    ov[i] = s < ns ? po[static_cast<size_t>(s) * kG * kD] : 0.f;
   }
   __syncthreads();
-  for (int i = tid; i < n_split * kG; i += blockDim.x) {
-    const int s = i / kG, h = i % kG;
-    const float ms = part_m[(rb + s) * kG + h];
-    fac[i] = (ms == -INFINITY) ? 0.f
-                               : ldexpf(1.f, static_cast<int>(ms - sM[h])) /
-                                     static_cast<float>(sL[h]);
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, sm[s]);
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < kCmbGroup / 2; ++i) {
+    const int s = hf + 2 * i;
+    if (s < ns && sm[s] != -INFINITY) acc += ov[i] * ldexpf(1.f, static_cast<int>(sm[s] - M));
   }
+  if (hf == 1) half_o[d] = acc;
   __syncthreads();
-  for (int i = tid; i < kG * kD; i += blockDim.x) {
-    const int h = i >> 7;
-    float acc = 0.f;
-    for (int s = 0; s < n_split; ++s) acc += part_o[(rb + s) * kG * kD + i] * fac[s * kG + h];
-    out[static_cast<size_t>(r) * kG * kD + i] = f32_to_bf16_rne(acc);
-  }
-  if (tid < kG) {
-    const double l2 = static_cast<double>(sM[tid]) + log2(sL[tid]);
-    lse2[static_cast<size_t>(r) * kG + tid] = l2;
-    if (lse_out) lse_out[static_cast<size_t>(r) * kG + tid] = static_cast<float>(l2 * M_LN2);
-  }
+  const size_t cb = (static_cast<size_t>(r) * kG + h) * n_groups + gi;
+  if (hf == 0) cmb_o[cb * kD + d] = acc + half_o[d];
   if (tid == 0) {
-    float yt = -INFINITY;
-    for (int h = 0; h < kG; ++h)
-      yt = fmaxf(yt, static_cast<float>(static_cast<double>(sM[h]) -
-                                        (static_cast<double>(sM[h]) + log2(sL[h]))));
-    ytop[r] = yt;
+    double L = 0.0;
+    for (int s = 0; s < ns; ++s)
+      if (sm[s] != -INFINITY) L += sl[s] * ldexp(1.0, static_cast<int>(sm[s] - M));
+    cmb_m[cb] = M;
+    cmb_l[cb] = L;
   }
-  // fresh selection state for this row
-  for (int i = tid; i < kNB; i += blockDim.x) hist[static_cast<size_t>(r) * kNB + i] = 0u;
-  if (tid == 0) info[r] = RowInfo{0, 0, 0, 0, 0u, 0u, 0u, 0};
+  // fresh selection state for this row (group 0 of each head clears a share)
+  if (gi == 0) {
+    for (int i = tid; i < kNB / kG; i += 256)
+      hist[static_cast<size_t>(r) * kNB + h * (kNB / kG) + i] = 0u;
+    if (h == 0 && tid == 0) info[r] = RowInfo{0, 0, 0, 0, 0u, 0u, 0u, 0};
+  }
+}
+
+// Level 2: grid (kG, R): merge the group partials of one head in group order;
+// write the output row (bf16), lse (natural log), lse2 (float64, base 2) and
+// the row's bound on log2 importance for that head, max_j s2_j - lse2.
+__global__ __launch_bounds__(256) void full_finalize_kernel(
+    const float* __restrict__ cmb_m, const double* __restrict__ cmb_l,
+    const float* __restrict__ cmb_o, int n_groups, u16* __restrict__ out,
+    float* __restrict__ lse_out, double* __restrict__ lse2, float* __restrict__ ytop_h) {
+  __shared__ float sm[kCmbMaxGroups];
+  __shared__ double sl[kCmbMaxGroups];
+  __shared__ float half_o[kD];
+  const int h = blockIdx.x, r = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int d = tid & 127, hf = tid >> 7;
+  const size_t c0 = (static_cast<size_t>(r) * kG + h) * n_groups;
+  if (tid < n_groups) {
+    sm[tid] = cmb_m[c0 + tid];
+    sl[tid] = cmb_l[c0 + tid];
+  }
+  float o2[kCmbMaxGroups / 2];
+#pragma unroll
+  for (int i = 0; i < kCmbMaxGroups / 2; ++i) {
+    const int g2 = hf + 2 * i;
+    o2[i] = g2 < n_groups ? cmb_o[(c0 + g2) * kD + d] : 0.f;
+  }
+  __syncthreads();
+  float MM = -INFINITY;
+  for (int g2 = 0; g2 < n_groups; ++g2) MM = fmaxf(MM, sm[g2]);
+  double L = 0.0;
+  for (int g2 = 0; g2 < n_groups; ++g2)
+    if (sm[g2] != -INFINITY) L += sl[g2] * ldexp(1.0, static_cast<int>(sm[g2] - MM));
+  float o = 0.f;
+#pragma unroll
+  for (int i = 0; i < kCmbMaxGroups / 2; ++i) {
+    const int g2 = hf + 2 * i;
+    if (g2 < n_groups && sm[g2] != -INFINITY)
+      o += o2[i] * ldexpf(1.f, static_cast<int>(sm[g2] - MM));
+  }
+  if (hf == 1) half_o[d] = o;
+  __syncthreads();
+  if (hf == 0)
+    out[(static_cast<size_t>(r) * kG + h) * kD + d] =
+        f32_to_bf16_rne((o + half_o[d]) * static_cast<float>(1.0 / L));
+  if (tid == 0) {
+    const double l2 = static_cast<double>(MM) + log2(L);
+    lse2[static_cast<size_t>(r) * kG + h] = l2;
+    if (lse_out) lse_out[static_cast<size_t>(r) * kG + h] = static_cast<float>(l2 * M_LN2);
+    // every logit of this head is <= MM, so its base-2 log-probability is <= MM - lse2
+    ytop_h[static_cast<size_t>(r) * kG + h] = static_cast<float>(-log2(L));
+  }
+}
+
+// Optional per-key importance for the caller (the step itself never needs all
+// of them): recompute the logits tile by tile on MFMA and write
+// max_h 2^(s2_h - lse2_h); entries past P are 0.  Reads K once more.
+__global__ __launch_bounds__(256) void full_scores_kernel(
+    const u16* __restrict__ q, const u16* __restrict__ k, const double* __restrict__ lse2,
+    float* __restrict__ scores, int64_t S, int kps, float c2_hi, float c2_lo) {
+  __shared__ float l2f[kG];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int r = blockIdx.y;
+  const int64_t key_begin = static_cast<int64_t>(blockIdx.x) * kps;
+  const int64_t key_end = min(S, key_begin + kps);
+  if (threadIdx.x < kG)
+    l2f[threadIdx.x] = static_cast<float>(lse2[static_cast<size_t>(r) * kG + threadIdx.x]);
+  __syncthreads();
+  bf16x8 qb[4];
+  load_q_operand(q + static_cast<size_t>(r) * kG * kD, col, grp, qb);
+  const u16* kr = k + static_cast<size_t>(r) * S * kD;
+  float* sr = scores + static_cast<size_t>(r) * S;
+  for (int64_t t0 = key_begin + wave * kTile; t0 < key_end; t0 += 4 * kTile) {
+    bf16x8 ka[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      int64_t key = t0 + 16 * mt + col;
+      key = key < key_end - 1 ? key : key_end - 1;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        ka[mt][c] = as_bf16x8(load_u32x4(kr + key * kD + 8 * grp + 32 * c));
+    }
+    float sv[8];
+    tile_logits(ka, qb, t0, key_end, grp, c2_hi, c2_lo, sv);
+    // importance per key: max over the 8 real heads (lanes col 0..7 of a group)
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float yv = col < kG ? sv[e] - l2f[col] : -INFINITY;
+      yv = fmaxf(yv, __shfl_xor(yv, 1));
+      yv = fmaxf(yv, __shfl_xor(yv, 2));
+      yv = fmaxf(yv, __shfl_xor(yv, 4));
+      y[e] = yv;
+    }
+    if (col == 0) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t key = t0 + 16 * mt + 4 * grp + i;
+          if (key < key_end) sr[key] = exp2f(y[4 * mt + i]);
+        }
+    }
+  }
 }
 
 }  // namespace
@@ -312,7 +412,7 @@ hipError_t launch_full_decode_split(const Plan& p, const u16* q, const u16* k, c
   const float c2_lo = static_cast<float>(c2 - static_cast<double>(c2_hi));
   dim3 grid(p.n_split, p.R);
   hipLaunchKernelGGL(full_decode_split_kernel, grid, dim3(kWaves * 64), 0, st, q, k, v,
-                     reinterpret_cast<float*>(w + p.off_logits),
+                     reinterpret_cast<float*>(w + p.off_stmax),
                      reinterpret_cast<float*>(w + p.off_part_m),
                      reinterpret_cast<double*>(w + p.off_part_l),
                      reinterpret_cast<float*>(w + p.off_part_o), p.S, p.Spad, p.kps, p.n_split,
@@ -322,15 +422,35 @@ hipError_t launch_full_decode_split(const Plan& p, const u16* q, const u16* k, c
 
 hipError_t launch_full_combine(const Plan& p, u16* out, float* lse, void* ws, hipStream_t st) {
   char* w = static_cast<char*>(ws);
-  const size_t shm = static_cast<size_t>(p.n_split) * kG * sizeof(float);
-  hipLaunchKernelGGL(full_combine_kernel, dim3(p.R), dim3(256), shm, st,
+  hipLaunchKernelGGL(full_merge_kernel, dim3(p.cmb_groups, kG, p.R), dim3(256), 0, st,
                      reinterpret_cast<const float*>(w + p.off_part_m),
                      reinterpret_cast<const double*>(w + p.off_part_l),
-                     reinterpret_cast<const float*>(w + p.off_part_o), p.n_split, out, lse,
-                     reinterpret_cast<double*>(w + p.off_lse2),
-                     reinterpret_cast<float*>(w + p.off_ytop),
+                     reinterpret_cast<const float*>(w + p.off_part_o), p.n_split, p.cmb_groups,
+                     reinterpret_cast<float*>(w + p.off_cmb_m),
+                     reinterpret_cast<double*>(w + p.off_cmb_l),
+                     reinterpret_cast<float*>(w + p.off_cmb_o),
                      reinterpret_cast<uint32_t*>(w + p.off_hist),
                      reinterpret_cast<RowInfo*>(w + p.off_info));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(full_finalize_kernel, dim3(kG, p.R), dim3(256), 0, st,
+                     reinterpret_cast<const float*>(w + p.off_cmb_m),
+                     reinterpret_cast<const double*>(w + p.off_cmb_l),
+                     reinterpret_cast<const float*>(w + p.off_cmb_o), p.cmb_groups, out, lse,
+                     reinterpret_cast<double*>(w + p.off_lse2),
+                     reinterpret_cast<float*>(w + p.off_ytop));
+  return hipGetLastError();
+}
+
+hipError_t launch_full_scores(const Plan& p, const u16* q, const u16* k, float* scores,
+                              void* ws, hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  const double c2 = p.scale * 1.4426950408889634;
+  const float c2_hi = static_cast<float>(c2);
+  const float c2_lo = static_cast<float>(c2 - static_cast<double>(c2_hi));
+  hipLaunchKernelGGL(full_scores_kernel, dim3(p.n_split, p.R), dim3(256), 0, st, q, k,
+                     reinterpret_cast<const double*>(w + p.off_lse2), scores, p.S, p.kps, c2_hi,
+                     c2_lo);
   return hipGetLastError();
 }
 

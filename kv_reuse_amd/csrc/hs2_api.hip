@@ -55,17 +55,29 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
     const int64_t target = 1024;
     int64_t ns = ceil_div(target, R);
     ns = std::max<int64_t>(1, std::min<int64_t>(ns, ceil_div(q.S, 256)));
+    ns = std::min<int64_t>(ns, int64_t{kCmbGroup} * kCmbMaxGroups);
     int64_t kps = align_up(static_cast<size_t>(ceil_div(q.S, ns)), 128);
     q.kps = static_cast<int>(kps);
     q.n_split = static_cast<int>(ceil_div(q.S, kps));
+    q.cmb_groups = static_cast<int>(ceil_div(q.n_split, kCmbGroup));
   }
-  // selection: ~512 work-groups in total over the rows
+  // selection from given scores: ~256 work-groups over the rows, at most 16384
+  // keys per work-group (the compaction keeps 64 keys per thread in bit masks)
   {
-    int64_t chunk = align_up(static_cast<size_t>(ceil_div(q.S * R, 512)), 256);
-    chunk = std::max<int64_t>(chunk, 2048);
-    chunk = std::min<int64_t>(chunk, align_up(static_cast<size_t>(q.S), 256));
+    int64_t chunk = align_up(static_cast<size_t>(ceil_div(q.S * R, 256)), 2048);
+    chunk = std::max<int64_t>(chunk, 4096);
+    chunk = std::min<int64_t>(chunk, 16384);
     q.sel_chunk = static_cast<int>(chunk);
     q.sel_nchunk = static_cast<int>(ceil_div(q.S, chunk));
+  }
+  // fused selection: subtiles of 16 keys, ~256 work-groups, <= 8192 per group
+  const int64_t nst = q.Spad / 16;
+  {
+    int64_t chunk = align_up(static_cast<size_t>(ceil_div(nst * R, 256)), 256);
+    chunk = std::max<int64_t>(chunk, 256);
+    chunk = std::min<int64_t>(chunk, 8192);
+    q.st_chunk = static_cast<int>(chunk);
+    q.st_nchunk = static_cast<int>(ceil_div(nst, chunk));
   }
   // sparse: slices of 128 keys over work-groups when rows are few
   q.sp_nch = (R >= 256) ? 1 : static_cast<int>(ceil_div(q.cap, 128));
@@ -76,20 +88,31 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
     off = align_up(off + bytes, kAlign);
     return o;
   };
-  const size_t nsplit_rows = static_cast<size_t>(R) * q.n_split;
+  const size_t Rz = static_cast<size_t>(R);
+  const size_t nsplit_rows = Rz * q.n_split;
   const bool decode = q.T == 1;
   q.off_part_m = take(decode ? nsplit_rows * kG * sizeof(float) : 0);
   q.off_part_l = take(decode ? nsplit_rows * kG * sizeof(double) : 0);
   q.off_part_o = take(decode ? nsplit_rows * kG * kD * sizeof(float) : 0);
-  q.off_logits = take(decode ? static_cast<size_t>(R) * kG * q.Spad * sizeof(float) : 0);
-  q.off_lse2 = take(static_cast<size_t>(R) * kG * sizeof(double));
-  q.off_ytop = take(static_cast<size_t>(R) * sizeof(float));
-  q.off_ukey = take(static_cast<size_t>(R) * q.Spad * sizeof(uint32_t));
-  q.off_hist = take(static_cast<size_t>(R) * kNB * sizeof(uint32_t));
-  q.off_info = take(static_cast<size_t>(R) * sizeof(RowInfo));
-  q.off_cert = take(static_cast<size_t>(R) * align_up(static_cast<size_t>(q.k), 64) * sizeof(int32_t));
-  q.off_unc = take(static_cast<size_t>(R) * kUncCap * sizeof(int32_t));
-  const size_t sp_parts = q.sp_nch > 1 ? static_cast<size_t>(R) * q.sp_nch * n_layers * kG : 0;
+  q.off_stmax = take(decode ? Rz * nst * kG * sizeof(float) : 0);
+  const size_t cmb = decode ? Rz * kG * q.cmb_groups : 0;
+  q.off_cmb_m = take(cmb * sizeof(float));
+  q.off_cmb_l = take(cmb * sizeof(double));
+  q.off_cmb_o = take(cmb * kD * sizeof(float));
+  q.off_lse2 = take(Rz * kG * sizeof(double));
+  q.off_ytop = take(Rz * kG * sizeof(float));
+  q.off_hist = take(Rz * kNB * sizeof(uint32_t));
+  q.off_info = take(Rz * sizeof(RowInfo));
+  q.off_ukey = take(Rz * q.Spad * sizeof(uint32_t));
+  q.off_cert = take(Rz * align_up(static_cast<size_t>(q.k), 64) * sizeof(int32_t));
+  q.off_unc = take(Rz * kUncCap * sizeof(int32_t));
+  q.off_unck = take(Rz * kUncCap * sizeof(uint64_t));
+  const size_t fz = decode ? Rz * q.Spad : 0;
+  q.off_cand_y = take(fz * sizeof(float));
+  q.off_cand_idx = take(fz * sizeof(int32_t));
+  q.off_band_idx = take(fz * sizeof(int32_t));
+  q.off_band_key = take(fz * sizeof(uint64_t));
+  const size_t sp_parts = q.sp_nch > 1 ? Rz * q.sp_nch * n_layers * kG : 0;
   q.off_sp_m = take(sp_parts * sizeof(float));
   q.off_sp_l = take(sp_parts * sizeof(float));
   q.off_sp_o = take(sp_parts * kD * sizeof(float));
@@ -126,14 +149,6 @@ int run_full(const Plan& p, const u16* q, const u16* k, const u16* v, u16* out, 
   return HS2_OK;
 }
 
-int run_select_from_logits(const Plan& p, const u16* q, const u16* k, float* scores,
-                           int32_t* idx, int32_t* n_sel, void* ws, hipStream_t st) {
-  HS2_TRY(launch_select_hist(p, true, nullptr, scores, true, ws, st));
-  HS2_TRY(launch_select_compact(p, true, ws, st));
-  HS2_TRY(launch_select_finish(p, true, nullptr, q, k, idx, n_sel, ws, st));
-  return HS2_OK;
-}
-
 }  // namespace
 }  // namespace hs2
 
@@ -159,7 +174,7 @@ int hs2_full_attn_scores(const hs2_shape* shape, const hs2_bf16* q, const hs2_bf
   (void)hipGetLastError();
   const hipStream_t s = as_stream(stream);
   if ((st = run_full(p, q, k, v, out, lse, ws, s)) != HS2_OK) return st;
-  if (scores) HS2_TRY(launch_select_hist(p, true, nullptr, scores, false, ws, s));
+  if (scores) HS2_TRY(launch_full_scores(p, q, k, scores, ws, s));
   return HS2_OK;
 }
 
@@ -172,10 +187,7 @@ int hs2_topk_select(const hs2_shape* shape, const float* scores, int32_t* idx, i
   if ((st = check_ws(p, ws, ws_bytes)) != HS2_OK) return st;
   (void)hipGetLastError();
   const hipStream_t s = as_stream(stream);
-  HS2_TRY(launch_select_clear(p, ws, s));
-  HS2_TRY(launch_select_hist(p, false, scores, nullptr, true, ws, s));
-  HS2_TRY(launch_select_compact(p, false, ws, s));
-  HS2_TRY(launch_select_finish(p, false, scores, nullptr, nullptr, idx, n_sel, ws, s));
+  HS2_TRY(launch_scores_select(p, scores, idx, n_sel, ws, s));
   return HS2_OK;
 }
 
@@ -208,7 +220,8 @@ int hs2_cross_decoder_step(const hs2_shape* shape, int32_t n_sparse_layers,
   (void)hipGetLastError();
   const hipStream_t s = as_stream(stream);
   if ((st = run_full(p, q_full, k, v, out_full, lse, ws, s)) != HS2_OK) return st;
-  if ((st = run_select_from_logits(p, q_full, k, scores, idx, n_sel, ws, s)) != HS2_OK) return st;
+  if (scores) HS2_TRY(launch_full_scores(p, q_full, k, scores, ws, s));
+  HS2_TRY(launch_fused_select(p, q_full, k, idx, n_sel, ws, s));
   if (n_sparse_layers > 0)
     HS2_TRY(launch_sparse(p, q_sparse, k, v, idx, n_sel, out_sparse, ws, s));
   return HS2_OK;
@@ -246,7 +259,7 @@ int hs2_cross_decoder_step_timed(const hs2_shape* shape, int32_t n_sparse_layers
     if (rc == HS2_OK) rc = hip_status(hipEventRecord(ev[1], s));
     if (rc == HS2_OK) rc = hip_status(launch_full_combine(p, out_full, nullptr, ws, s));
     if (rc == HS2_OK) rc = hip_status(hipEventRecord(ev[2], s));
-    if (rc == HS2_OK) rc = run_select_from_logits(p, q_full, k, nullptr, idx, n_sel, ws, s);
+    if (rc == HS2_OK) rc = hip_status(launch_fused_select(p, q_full, k, idx, n_sel, ws, s));
     if (rc == HS2_OK) rc = hip_status(hipEventRecord(ev[3], s));
     if (rc == HS2_OK && n_sparse_layers > 0)
       rc = hip_status(launch_sparse(p, q_sparse, k, v, idx, n_sel, out_sparse, ws, s));

@@ -17,6 +17,8 @@ constexpr int kUncCap = 2048;    // near-threshold keys handled in LDS; more tak
 constexpr int kMaxSel = 4096;    // top_k + window limit (index list kept in LDS)
 constexpr int kSparseChunk = 128;  // selected keys per sparse work-group (4 waves x 32)
 constexpr float kYRange = 64.0f;   // log2 range below the row's top score that the bins span
+constexpr int kCmbGroup = 16;      // splits merged per work-group in level 1
+constexpr int kCmbMaxGroups = 64;  // level-1 groups merged in level 2
 
 typedef unsigned short u16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -43,12 +45,19 @@ struct Plan {
   int k, w, cap;             // cap = k + w (index list capacity per row)
   int n_layers;
   double scale;
-  // full attention (decode split kernel)
+  // full attention (decode split kernel) and the merge of its splits
   int n_split, kps;
-  size_t off_part_m, off_part_l, off_part_o, off_logits, off_lse2, off_ytop;
-  // selection
+  int cmb_groups;            // groups of 16 splits (level 1 of the merge)
+  size_t off_part_m, off_part_l, off_part_o, off_stmax, off_lse2, off_ytop;
+  size_t off_cmb_m, off_cmb_l, off_cmb_o;
+  // selection state shared by both selection paths
+  size_t off_hist, off_info;
+  // selection from given scores
   int sel_chunk, sel_nchunk;
-  size_t off_ukey, off_hist, off_info, off_cert, off_unc;
+  size_t off_ukey, off_cert, off_unc, off_unck;
+  // fused selection from the subtile maxima
+  int st_chunk, st_nchunk;
+  size_t off_cand_y, off_cand_idx, off_band_idx, off_band_key;
   // sparse
   int sp_nch;
   size_t off_sp_m, off_sp_l, off_sp_o;
@@ -56,26 +65,25 @@ struct Plan {
 };
 
 // ---------------------------------------------------------------- launchers
-// Each returns the hipError_t of its launch (hipGetLastError()).
+// Each returns the hipError_t of its launches (hipGetLastError()).
 
 // Full attention, decode (T == 1): split-context flash-decode writing per-split
-// partial (m, l, O) and the float32 base-2 logits of every key and head.
+// partial (m, l, O) and per-subtile (16 keys) maxima of every head's logits.
 hipError_t launch_full_decode_split(const Plan& p, const u16* q, const u16* k, const u16* v,
                                     void* ws, hipStream_t st);
-// Merge the splits: out (bf16), lse (nullable), lse2 (fp64, base 2) and the row's
-// top score bound; also clears this row's selection counters and histogram.
+// Merge the splits: out (bf16), lse (nullable), lse2 (fp64, base 2) and each
+// head's bound on log2 importance; also clears the rows' selection state.
 hipError_t launch_full_combine(const Plan& p, u16* out, float* lse, void* ws, hipStream_t st);
-
-// Selection.  from_logits: keys are ranked by importance computed from the
-// stored logits and lse2, then re-ranked in float64 near the threshold using
-// q and k.  Otherwise keys are the given float32 scores, compared exactly.
-hipError_t launch_select_clear(const Plan& p, void* ws, hipStream_t st);
-hipError_t launch_select_hist(const Plan& p, bool from_logits, const float* scores_in,
-                              float* scores_out, bool do_select, void* ws, hipStream_t st);
-hipError_t launch_select_compact(const Plan& p, bool from_logits, void* ws, hipStream_t st);
-hipError_t launch_select_finish(const Plan& p, bool from_logits, const float* scores_in,
-                                const u16* q, const u16* k, int32_t* idx, int32_t* n_sel,
-                                void* ws, hipStream_t st);
+// Per-key importance [R][S] (float32), recomputed from q, k and lse2.
+hipError_t launch_full_scores(const Plan& p, const u16* q, const u16* k, float* scores,
+                              void* ws, hipStream_t st);
+// Selection from given float32 scores, compared exactly.
+hipError_t launch_scores_select(const Plan& p, const float* scores, int32_t* idx,
+                                int32_t* n_sel, void* ws, hipStream_t st);
+// Selection of the fused step: candidate subtiles from the maxima, float32
+// rescoring on MFMA, float64 re-ranking near the threshold.
+hipError_t launch_fused_select(const Plan& p, const u16* q, const u16* k, int32_t* idx,
+                               int32_t* n_sel, void* ws, hipStream_t st);
 
 // Sparse layers (all n_layers fused: one gather of the selected K/V rows).
 hipError_t launch_sparse(const Plan& p, const u16* q, const u16* k, const u16* v,
@@ -102,6 +110,10 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 __device__ __forceinline__ u32x4 load_u32x4(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
+}
+// Streaming load: the data is read once, so it is marked non-temporal.
+__device__ __forceinline__ u32x4 load_u32x4_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 // Order-preserving maps from floats to unsigned integers (larger value -> larger key).
 __device__ __forceinline__ uint32_t ordered_u32(float f) {

@@ -76,8 +76,10 @@ __global__ __launch_bounds__(NCT * 64) void sparse_kernel(
     __syncthreads();
     for (int pc = tid; pc < kSub * 16; pc += blockDim.x) {
       const int key = pc >> 4, c16 = pc & 15;
+      // entries outside [0, S) (padding, or a malformed list) read row 0 / S-1
+      // instead of faulting; padding is masked out of the softmax below
       const int j = sidx[key];
-      const size_t jj = j < 0 ? 0 : static_cast<size_t>(j);
+      const size_t jj = j < 0 ? 0 : static_cast<size_t>(min(static_cast<int64_t>(j), S - 1));
       *reinterpret_cast<u32x4*>(klds + key * kPitch + 8 * c16) = load_u32x4(kr + jj * kD + 8 * c16);
       *reinterpret_cast<u32x4*>(vlds + key * kPitch + 8 * c16) = load_u32x4(vr + jj * kD + 8 * c16);
     }
@@ -146,33 +148,49 @@ __global__ __launch_bounds__(NCT * 64) void sparse_kernel(
   }
 }
 
-// grid (R, L): merge the slices of one row and layer.
+// grid (R, L): merge the slices of one row and layer.  The slices' maxima and
+// sums go through LDS first, so the O loads below are independent of each other.
 __global__ __launch_bounds__(256) void sparse_combine_kernel(
     const float* __restrict__ part_m, const float* __restrict__ part_l,
     const float* __restrict__ part_o, u16* __restrict__ out, int L, int nch,
     size_t layer_stride) {
+  extern __shared__ float fac[];   // [nch][kG]
+  __shared__ float inv_l[kG];
   const int r = blockIdx.x;
   const int layer = blockIdx.y;
-  for (int i = threadIdx.x; i < kG * kD; i += blockDim.x) {
-    const int h = i >> 7, d = i & 127;
-    float M = -INFINITY;
-    for (int c = 0; c < nch; ++c)
-      M = fmaxf(M, part_m[((static_cast<size_t>(r) * nch + c) * L + layer) * kG + h]);
-    float acc = 0.f, l = 0.f;
-    if (M != -INFINITY) {
-      for (int c = 0; c < nch; ++c) {
-        const size_t pb = ((static_cast<size_t>(r) * nch + c) * L + layer) * kG + h;
-        const float mc = part_m[pb];
-        if (mc == -INFINITY) continue;
-        const float f = __builtin_amdgcn_exp2f(mc - M);
-        l += part_l[pb] * f;
-        acc += part_o[pb * kD + d] * f;
-      }
-    }
-    const float res = l > 0.f ? acc / l : 0.f;
-    out[static_cast<size_t>(layer) * layer_stride + (static_cast<size_t>(r) * kG + h) * kD + d] =
-        f32_to_bf16_rne(res);
+  const int tid = threadIdx.x;
+  for (int i = tid; i < nch * kG; i += blockDim.x) {
+    const int c = i / kG, h = i % kG;
+    fac[i] = part_m[((static_cast<size_t>(r) * nch + c) * L + layer) * kG + h];
   }
+  __syncthreads();
+  if (tid < kG) {
+    float M = -INFINITY;
+    for (int c = 0; c < nch; ++c) M = fmaxf(M, fac[c * kG + tid]);
+    float l = 0.f;
+    for (int c = 0; c < nch; ++c) {
+      const float mc = fac[c * kG + tid];
+      const float f = (mc == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mc - M);
+      l += f * part_l[((static_cast<size_t>(r) * nch + c) * L + layer) * kG + tid];
+      fac[c * kG + tid] = f;
+    }
+    inv_l[tid] = l > 0.f ? 1.f / l : 0.f;
+  }
+  __syncthreads();
+  // one output per thread: blockIdx.z picks a quarter of the 8 x 128 outputs
+  const int i = blockIdx.z * 256 + tid;
+  const int h = i >> 7;
+  const float* po = part_o + ((static_cast<size_t>(r) * nch) * L + layer) * kG * kD + i;
+  const size_t cstride = static_cast<size_t>(L) * kG * kD;
+  float a0 = 0.f, a1 = 0.f;
+  int c = 0;
+  for (; c + 1 < nch; c += 2) {
+    a0 += fac[c * kG + h] * po[c * cstride];
+    a1 += fac[(c + 1) * kG + h] * po[(c + 1) * cstride];
+  }
+  if (c < nch) a0 += fac[c * kG + h] * po[c * cstride];
+  out[static_cast<size_t>(layer) * layer_stride + static_cast<size_t>(r) * kG * kD + i] =
+      f32_to_bf16_rne((a0 + a1) * inv_l[h]);
 }
 
 }  // namespace
@@ -208,7 +226,8 @@ hipError_t launch_sparse(const Plan& p, const u16* q, const u16* k, const u16* v
     if (e != hipSuccess) return e;
   }
   if (p.sp_nch > 1) {
-    hipLaunchKernelGGL(sparse_combine_kernel, dim3(p.R, p.n_layers), dim3(256), 0, st, pm, pl, po,
+    hipLaunchKernelGGL(sparse_combine_kernel, dim3(p.R, p.n_layers, 4), dim3(256),
+                       static_cast<size_t>(p.sp_nch) * kG * sizeof(float), st, pm, pl, po,
                        out, p.n_layers, p.sp_nch, layer_stride);
     return hipGetLastError();
   }
