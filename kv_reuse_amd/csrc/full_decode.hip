@@ -294,7 +294,7 @@ __global__ __launch_bounds__(256) void full_merge_kernel(
   if (gi == 0) {
     for (int i = tid; i < kNB / kG; i += 256)
       hist[static_cast<size_t>(r) * kNB + h * (kNB / kG) + i] = 0u;
-    if (h == 0 && tid == 0) info[r] = RowInfo{0, 0, 0, 0, 0u, 0u, 0u, 0};
+    if (h == 0 && tid == 0) info[r] = RowInfo{0u, 0u, 0u, 0u};
   }
 }
 

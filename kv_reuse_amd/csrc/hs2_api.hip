@@ -73,7 +73,7 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
   // fused selection: subtiles of 16 keys, ~256 work-groups, <= 8192 per group
   const int64_t nst = q.Spad / 16;
   {
-    int64_t chunk = align_up(static_cast<size_t>(ceil_div(nst * R, 256)), 256);
+    int64_t chunk = align_up(static_cast<size_t>(ceil_div(nst * R, 1024)), 256);
     chunk = std::max<int64_t>(chunk, 256);
     chunk = std::min<int64_t>(chunk, 8192);
     q.st_chunk = static_cast<int>(chunk);
@@ -108,10 +108,12 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
   q.off_unc = take(Rz * kUncCap * sizeof(int32_t));
   q.off_unck = take(Rz * kUncCap * sizeof(uint64_t));
   const size_t fz = decode ? Rz * q.Spad : 0;
-  q.off_cand_y = take(fz * sizeof(float));
+  q.off_hist_c = take(decode ? Rz * kNB * sizeof(uint32_t) : 0);
+  q.off_cand_y = take(fz * sizeof(double));
   q.off_cand_idx = take(fz * sizeof(int32_t));
   q.off_band_idx = take(fz * sizeof(int32_t));
   q.off_band_key = take(fz * sizeof(uint64_t));
+  q.off_sel_list = take(decode ? Rz * kMaxSel * sizeof(int32_t) : 0);
   const size_t sp_parts = q.sp_nch > 1 ? Rz * q.sp_nch * n_layers * kG : 0;
   q.off_sp_m = take(sp_parts * sizeof(float));
   q.off_sp_l = take(sp_parts * sizeof(float));

@@ -24,19 +24,16 @@ typedef unsigned short u16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
-// Per-row selection bookkeeping (lives in the workspace).
+// Per-row selection bookkeeping (lives in the workspace; zeroed each call).
 struct RowInfo {
-  int32_t bstar;       // histogram bin holding the k-th largest key
-  int32_t n_cert;      // candidates certainly selected (bins above the uncertain band)
-  int32_t n_unc;       // candidates in the uncertain band
-  int32_t mode;        // kModeNormal / kModeAll / kModeNone
-  uint32_t cert_count; // append counters (compaction)
-  uint32_t unc_count;
-  uint32_t arrive;     // work-groups of this row done with the histogram
-  int32_t band;        // 1 = uncertain band is bins [b*-1, b*+1]; 0 = bin b* only
+  uint32_t cert_count;  // entries appended to the row's first list
+  uint32_t unc_count;   // entries appended to the row's band list
+  uint32_t up_count;    // entries above the band appended to the selection
+  uint32_t pad;
 };
-enum { kModeNormal = 0, kModeAll = 1, kModeNone = 2 };
+constexpr int kBandRankMax = 4096;  // bands up to this size are ranked in parallel
 
 // Where each piece of the workspace sits, for one shape.
 struct Plan {
@@ -57,7 +54,7 @@ struct Plan {
   size_t off_ukey, off_cert, off_unc, off_unck;
   // fused selection from the subtile maxima
   int st_chunk, st_nchunk;
-  size_t off_cand_y, off_cand_idx, off_band_idx, off_band_key;
+  size_t off_hist_c, off_cand_y, off_cand_idx, off_band_idx, off_band_key, off_sel_list;
   // sparse
   int sp_nch;
   size_t off_sp_m, off_sp_l, off_sp_o;

@@ -30,6 +30,8 @@
 //                      float64 from the bf16 query and key, and the index list
 //                      (ascending) plus the window is written.
 
+#include <algorithm>
+
 #include "hs2_internal.h"
 
 namespace hs2 {
@@ -55,6 +57,11 @@ __device__ __forceinline__ uint32_t key_from_log2(float y, float ybase) {
   if (!(z > 0.f)) return 0u;
   if (z >= 4294967040.0f) return 0xFFFFFFFFu;
   return static_cast<uint32_t>(z);
+}
+
+// Histogram bin of a candidate's exact log2 importance (monotone in y).
+__device__ __forceinline__ int cand_bin(double y, float ybase) {
+  return static_cast<int>(key_from_log2(static_cast<float>(y), ybase) >> kBinShift);
 }
 
 // ---------------------------------------------------------------- helpers
@@ -163,32 +170,7 @@ struct Cand {
   int32_t pad;
 };
 __device__ __forceinline__ bool before(const Cand& a, const Cand& b) {
-  return a.key > b.key || (a.key == b.key && a.idx < b.idx);
-}
-
-// In-LDS bitonic sort of n (power of two) entries into "before" order.
-__device__ void bitonic_sort_cands(Cand* a, int n) {
-  for (int size = 2; size <= n; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < (n >> 1); i += blockDim.x) {
-        const int lo = 2 * stride * (i / stride) + (i % stride);
-        const int hi = lo + stride;
-        const bool up = (lo & size) == 0;
-        const Cand x = a[lo], y = a[hi];
-        if (before(y, x) == up) {
-          a[lo] = y;
-          a[hi] = x;
-        }
-      }
-      __syncthreads();
-    }
-  }
-}
-
-__device__ __forceinline__ int next_pow2(int n) {
-  int p = 1;
-  while (p < n) p <<= 1;
-  return p;
+  return (a.key > b.key) | ((a.key == b.key) & (a.idx < b.idx));
 }
 
 // Exact radix select over a band source: appends to sel[*s_count ...] the
@@ -198,6 +180,7 @@ template <typename Src>
 __device__ void radix_select_band(const Src& src, int64_t n, uint32_t take, int32_t* sel,
                                   uint32_t* s_count, uint32_t* h256, uint64_t* s_thr_hi,
                                   uint32_t* s_thr_lo, uint32_t* s_need) {
+  const uint32_t limit = *s_count + take;   // sel has room up to here
   uint64_t thr_hi = 0, mask_hi = 0;
   uint32_t thr_lo = 0, mask_lo = 0;
   uint32_t need = take;
@@ -245,26 +228,126 @@ __device__ void radix_select_band(const Src& src, int64_t n, uint32_t take, int3
     int32_t j;
     if (!src.get(i, vhi, j)) continue;
     const uint32_t vlo = ~static_cast<uint32_t>(j);
-    if (vhi > thr_hi || (vhi == thr_hi && vlo >= thr_lo)) sel[atomicAdd(s_count, 1u)] = j;
+    if (vhi > thr_hi || (vhi == thr_hi && vlo >= thr_lo)) {
+      const uint32_t slot = atomicAdd(s_count, 1u);
+      if (slot < limit) sel[slot] = j;
+    }
   }
   __syncthreads();
 }
 
-// The best `take` of a band of n entries into sel[*s_count ...]: a bitonic
-// sort in LDS when the band fits, the radix select otherwise.  keys/idx hold
-// the band (any memory); all threads call it.
+// ---------------------------------------------------------------- block sort
+// Bitonic sort of kRowThreads * E values held E per thread (thread t holds
+// elements E*t .. E*t+E-1), into `less` order.  Stages whose partners lie in
+// the same thread run in registers, those within a wave through lane
+// shuffles, the few across waves through the LDS buffer `xch` (N values).
+// All threads call it.
+__device__ __forceinline__ int32_t shfl_xor_val(int32_t v, int m) { return __shfl_xor(v, m); }
+__device__ __forceinline__ int32_t pick(bool c, int32_t a, int32_t b) { return c ? a : b; }
+__device__ __forceinline__ Cand pick(bool c, const Cand& a, const Cand& b) {
+  Cand r;
+  r.key = c ? a.key : b.key;
+  r.idx = c ? a.idx : b.idx;
+  r.pad = 0;
+  return r;
+}
+__device__ __forceinline__ Cand shfl_xor_val(const Cand& c, int m) {
+  const uint32_t lo = __shfl_xor(static_cast<uint32_t>(c.key), m);
+  const uint32_t hi = __shfl_xor(static_cast<uint32_t>(c.key >> 32), m);
+  return Cand{(static_cast<uint64_t>(hi) << 32) | lo, __shfl_xor(c.idx, m), 0};
+}
+
+// The values are distinct except for padding copies of one value, so "swap
+// iff the pair is out of order" needs one comparison and no branch.
+template <int E, int J, typename T, typename Less>
+__device__ __forceinline__ void bitonic_in_thread(T (&v)[E], int k, Less less) {
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int l = e ^ J;
+    if (l > e) {
+      const bool asc = ((E * static_cast<int>(threadIdx.x) + e) & k) == 0;
+      const bool sw = less(v[l], v[e]) == asc;
+      const T a = v[e], b = v[l];
+      v[e] = pick(sw, b, a);
+      v[l] = pick(sw, a, b);
+    }
+  }
+}
+
+// Sorts the first M = next_pow2(n) positions, which hold every real value
+// (positions >= n hold padding that sorts last).
+template <int E, typename T, typename Less>
+__device__ __forceinline__ void block_bitonic(T (&v)[E], T* xch, int n, Less less) {
+  static_assert(E == 4 || E == 8, "4 or 8 values per thread");
+  constexpr int N = kRowThreads * E;
+  int M = 2;
+  while (M < n && M < N) M <<= 1;
+  const int tid = threadIdx.x;
+#pragma unroll 1
+  for (int k = 2; k <= M; k <<= 1) {
+#pragma unroll 1
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j < E) {
+        if (j == 1) bitonic_in_thread<E, 1>(v, k, less);
+        else if (j == 2) bitonic_in_thread<E, 2>(v, k, less);
+        else bitonic_in_thread<E, E == 8 ? 4 : 2>(v, k, less);
+      } else {
+        const int tm = j / E;                  // partner thread = tid ^ tm
+        const bool asc = ((E * tid) & k) == 0;
+        const bool keep_min = ((tid & tm) == 0) == asc;
+        T o[E];
+        if (tm < 64) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) o[e] = shfl_xor_val(v[e], tm);
+        } else {
+          __syncthreads();
+#pragma unroll
+          for (int e = 0; e < E; ++e) xch[E * tid + e] = v[e];
+          __syncthreads();
+#pragma unroll
+          for (int e = 0; e < E; ++e) o[e] = xch[E * (tid ^ tm) + e];
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const bool take_o = less(o[e], v[e]) == keep_min;
+          v[e] = pick(take_o, o[e], v[e]);
+        }
+      }
+    }
+  }
+  __syncthreads();
+}
+
+struct CandBefore {
+  __device__ bool operator()(const Cand& a, const Cand& b) const { return before(a, b); }
+};
+struct IntLess {
+  __device__ bool operator()(int32_t a, int32_t b) const { return a < b; }
+};
+
+// The best `take` of a band of n entries into sel[*s_count ...], in order.  A
+// band that fits in LDS is sorted (key desc, index asc) in one block sort; a
+// larger one goes through the radix select.  keys/idx hold the band (any
+// memory); all threads call it.
 __device__ void take_best(const uint64_t* keys, const int32_t* idx, int64_t n, uint32_t take,
                           Cand* cands, int32_t* sel, uint32_t* s_count, uint32_t* h256,
                           uint64_t* s_thr_hi, uint32_t* s_thr_lo, uint32_t* s_need) {
   if (take == 0) return;
   if (n <= kUncCap) {
-    const int n2 = next_pow2(static_cast<int>(n));
-    for (int i = threadIdx.x; i < n2; i += blockDim.x)
-      cands[i] = i < n ? Cand{keys[i], idx[i], 0} : Cand{0ull, 0x7FFFFFFF, 0};
-    __syncthreads();
-    bitonic_sort_cands(cands, n2);
+    constexpr int E = kUncCap / kRowThreads;
+    Cand v[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int i = E * threadIdx.x + e;
+      v[e] = i < n ? Cand{keys[i], idx[i], 0} : Cand{0ull, 0x7FFFFFFF, 0};
+    }
     const uint32_t base = *s_count;
-    for (uint32_t i = threadIdx.x; i < take; i += blockDim.x) sel[base + i] = cands[i].idx;
+    block_bitonic<E>(v, cands, static_cast<int>(n), CandBefore{});
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const uint32_t i = E * threadIdx.x + e;
+      if (i < take) sel[base + i] = v[e].idx;
+    }
     __syncthreads();
     if (threadIdx.x == 0) *s_count = base + take;
     __syncthreads();
@@ -282,25 +365,34 @@ __device__ void take_best(const uint64_t* keys, const int32_t* idx, int64_t n, u
   radix_select_band(src, n, take, sel, s_count, h256, s_thr_hi, s_thr_lo, s_need);
 }
 
-// Write a row's output: the n_keep selected older keys of tmp sorted ascending
-// (into sel; values are distinct, each goes to its rank), then the window
-// [first, P], then -1 up to cap.  All threads call it.
-__device__ void emit_row(const int32_t* tmp, int32_t* sel, int n_keep, int64_t first, int P,
+template <int E>
+__device__ void sort_ascending(const int32_t* tmp, int32_t* xch, int n, int32_t* __restrict__ out) {
+  int32_t v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = E * threadIdx.x + e;
+    v[e] = i < n ? tmp[i] : 0x7FFFFFFF;
+  }
+  block_bitonic<E>(v, xch, n, IntLess{});
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = E * threadIdx.x + e;
+    if (i < n) out[i] = v[e];
+  }
+}
+
+// Write a row's output: the n_keep (<= kMaxSel) selected older keys of tmp in
+// ascending order, then the window [first, P], then -1 up to cap.  xch is LDS
+// room for kMaxSel values.  All threads call it.
+__device__ void emit_row(const int32_t* tmp, int32_t* xch, int n_keep, int64_t first, int P,
                          int32_t* __restrict__ out, int32_t* __restrict__ nsel_out, int cap) {
-  for (int i = threadIdx.x; i < n_keep; i += blockDim.x) {
-    const int32_t v = tmp[i];
-    int rank = 0;
-    for (int j = 0; j < n_keep; ++j) rank += tmp[j] < v;
-    sel[rank] = v;
+  if (n_keep > 0) {
+    if (n_keep <= 4 * kRowThreads) sort_ascending<4>(tmp, xch, n_keep, out);
+    else sort_ascending<kMaxSel / kRowThreads>(tmp, xch, n_keep, out);
   }
-  __syncthreads();
   const int n_total = n_keep + static_cast<int>(static_cast<int64_t>(P) - first + 1);
-  for (int i = threadIdx.x; i < cap; i += blockDim.x) {
-    int32_t val = -1;
-    if (i < n_keep) val = sel[i];
-    else if (i < n_total) val = static_cast<int32_t>(first + (i - n_keep));
-    out[i] = val;
-  }
+  for (int i = n_keep + threadIdx.x; i < cap; i += blockDim.x)
+    out[i] = i < n_total ? static_cast<int32_t>(first + (i - n_keep)) : -1;
   if (threadIdx.x == 0) *nsel_out = n_total;
 }
 
@@ -309,7 +401,7 @@ __device__ void emit_row(const int32_t* tmp, int32_t* sel, int n_keep, int64_t f
 __global__ void scores_clear_kernel(uint32_t* __restrict__ hist, RowInfo* __restrict__ info) {
   const int r = blockIdx.x;
   for (int i = threadIdx.x; i < kNB; i += blockDim.x) hist[static_cast<size_t>(r) * kNB + i] = 0u;
-  if (threadIdx.x == 0) info[r] = RowInfo{0, 0, 0, 0, 0u, 0u, 0u, 0};
+  if (threadIdx.x == 0) info[r] = RowInfo{0u, 0u, 0u, 0u};
 }
 
 __global__ __launch_bounds__(kHistThreads) void scores_hist_kernel(
@@ -373,7 +465,9 @@ __global__ __launch_bounds__(kThreads) void scores_compact_kernel(
               oc, ou);
   for (uint64_t m = mc; m; m &= m - 1) {
     const int i = __builtin_ctzll(m);
-    cert[static_cast<size_t>(r) * capk + oc++] = static_cast<int32_t>(j0 + tid + kThreads * i);
+    if (oc < static_cast<uint32_t>(capk))
+      cert[static_cast<size_t>(r) * capk + oc] = static_cast<int32_t>(j0 + tid + kThreads * i);
+    ++oc;
   }
   for (uint64_t m = mu; m; m &= m - 1) {
     const int i = __builtin_ctzll(m);
@@ -395,7 +489,7 @@ __global__ __launch_bounds__(kRowThreads) void scores_finish_kernel(
     int32_t* __restrict__ nsel_out, int64_t S, int64_t Spad, int T, int Hkv, int topk, int w,
     int capk, int cap) {
   __shared__ uint32_t lh[kNB];
-  __shared__ int32_t tmp[kMaxSel];
+  __shared__ __align__(16) int32_t tmp[kMaxSel + 4];
   __shared__ int32_t sel[kMaxSel];
   __shared__ Cand cands[kUncCap];
   __shared__ uint32_t h256[256];
@@ -424,7 +518,7 @@ __global__ __launch_bounds__(kRowThreads) void scores_finish_kernel(
         }
       }
       __syncthreads();
-      const int n_cert = static_cast<int>(s_above);
+      const int n_cert = min(static_cast<int>(s_above), topk);
       for (int i = tid; i < n_cert; i += kRowThreads) tmp[i] = cert[static_cast<size_t>(r) * capk + i];
       if (tid == 0) s_count = static_cast<uint32_t>(n_cert);
       __syncthreads();
@@ -482,8 +576,8 @@ __device__ __forceinline__ float subtile_ub(const float* __restrict__ stmax_row,
 // the window is always a candidate and is not counted here).
 __global__ __launch_bounds__(kThreads) void subtile_hist_kernel(
     const float* __restrict__ stmax, const double* __restrict__ lse2,
-    const float* __restrict__ ytop_h, uint32_t* __restrict__ hist, int64_t S, int64_t Spad,
-    int T, int Hkv, int topk, int w, int chunk) {
+    const float* __restrict__ ytop_h, uint32_t* __restrict__ hist, uint32_t* __restrict__ hist_c,
+    int64_t S, int64_t Spad, int T, int Hkv, int topk, int w, int chunk) {
   __shared__ uint32_t lh[kNB];
   __shared__ float lse2f[kG];
   __shared__ float s_ybase;
@@ -492,6 +586,9 @@ __global__ __launch_bounds__(kThreads) void subtile_hist_kernel(
   const int tid = threadIdx.x;
   const int64_t first = row_first(row_pos(r, T, Hkv, S), w);
   const int64_t n_counted = first / kSubKeys;
+  // the candidate histogram is filled by the next kernel
+  if (blockIdx.x == 0)
+    for (int i = tid; i < kNB; i += kThreads) hist_c[static_cast<size_t>(r) * kNB + i] = 0u;
   for (int i = tid; i < kNB; i += kThreads) lh[i] = 0u;
   if (tid < kG) lse2f[tid] = static_cast<float>(lse2[static_cast<size_t>(r) * kG + tid]);
   if (tid == 0) s_ybase = row_ybase(ytop_h, r);
@@ -500,19 +597,30 @@ __global__ __launch_bounds__(kThreads) void subtile_hist_kernel(
   const float* stmax_row = stmax + static_cast<size_t>(r) * (Spad / kSubKeys) * kG;
   const int64_t st0 = static_cast<int64_t>(blockIdx.x) * chunk;
   const int64_t st1 = min(n_counted, st0 + chunk);
-  for (int64_t st = st0 + tid; st < st1; st += kThreads)
-    atomicAdd(&lh[key_from_log2(subtile_ub(stmax_row, st, lse2f), ybase) >> kBinShift], 1u);
+  for (int64_t sb = st0 + tid; sb < st1; sb += 4 * kThreads) {
+    float ub[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t st = sb + u * kThreads;
+      ub[u] = st < st1 ? subtile_ub(stmax_row, st, lse2f) : -INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (sb + u * kThreads < st1)
+        atomicAdd(&lh[key_from_log2(ub[u], ybase) >> kBinShift], 1u);
+  }
   flush_hist(lh, hist + static_cast<size_t>(r) * kNB, static_cast<uint32_t>(topk), &s_lo);
 }
 
-// Candidate subtiles, then their keys' importances in float32 on MFMA: one wave
-// per candidate subtile, S^T = K . Q^T over its 16 keys.
+// Candidate subtiles, then their keys' importances in float64 on MFMA (one wave
+// per candidate subtile), appended to the row's candidate list, and their
+// histogram added to the row's candidate histogram hist_c.
 __global__ __launch_bounds__(kThreads) void subtile_score_kernel(
     const float* __restrict__ stmax, const double* __restrict__ lse2,
     const float* __restrict__ ytop_h, const uint32_t* __restrict__ hist,
-    RowInfo* __restrict__ info, const u16* __restrict__ q, const u16* __restrict__ k,
-    float* __restrict__ cand_y, int32_t* __restrict__ cand_idx, int64_t S, int64_t Spad,
-    int T, int Hkv, int topk, int w, int chunk, float c2_hi, float c2_lo) {
+    uint32_t* __restrict__ hist_c, RowInfo* __restrict__ info, const u16* __restrict__ q,
+    const u16* __restrict__ k, double* __restrict__ cand_y, int32_t* __restrict__ cand_idx,
+    int64_t S, int64_t Spad, int T, int Hkv, int topk, int w, int chunk, double c2) {
   __shared__ uint32_t lh[kNB];
   __shared__ int32_t s_list[kMaxSubChunk];
   __shared__ float lse2f[kG];
@@ -546,14 +654,22 @@ __global__ __launch_bounds__(kThreads) void subtile_score_kernel(
   const float* stmax_row = stmax + static_cast<size_t>(r) * (Spad / kSubKeys) * kG;
   // ---- phase 1: which subtiles of the chunk are candidates
   uint32_t mine = 0;
-  for (int i = 0; i < kMaxSubChunk / kThreads; ++i) {
-    const int64_t st = st0 + tid + static_cast<int64_t>(kThreads) * i;
-    if (st >= st1) break;
-    const bool cand =
-        all_mode || st >= n_counted ||
-        static_cast<int>(key_from_log2(subtile_ub(stmax_row, st, lse2f), ybase) >> kBinShift) >=
-            lo_bin;
-    if (cand) mine |= 1u << i;
+  for (int i0 = 0; i0 < kMaxSubChunk / kThreads; i0 += 4) {
+    if (st0 + tid + static_cast<int64_t>(kThreads) * i0 >= st1) break;
+    float ub[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t st = st0 + tid + static_cast<int64_t>(kThreads) * (i0 + u);
+      ub[u] = (st < min(st1, n_counted) && !all_mode) ? subtile_ub(stmax_row, st, lse2f) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t st = st0 + tid + static_cast<int64_t>(kThreads) * (i0 + u);
+      if (st >= st1) continue;
+      const bool cand = all_mode || st >= n_counted ||
+                        static_cast<int>(key_from_log2(ub[u], ybase) >> kBinShift) >= lo_bin;
+      if (cand) mine |= 1u << (i0 + u);
+    }
   }
   uint32_t o_list, o_dummy;
   reserve_two(__popc(mine), 0u, nullptr, nullptr, s_cnt, s_base, o_list, o_dummy);
@@ -565,171 +681,327 @@ __global__ __launch_bounds__(kThreads) void subtile_score_kernel(
     s_base[1] = n_local ? atomicAdd(&info[r].cert_count, n_local * kSubKeys) : 0u;
   __syncthreads();
   const uint32_t base = s_base[1];
-  // ---- phase 2: float32 importances of the candidates' keys
+  // ---- phase 2: float64 importances of the candidates' keys on MFMA.  A
+  // wave takes a subtile: D = K . Q^T over 16 keys x 16 (8 used) heads, the
+  // contraction split as dim = 32*(lane/16) + step, 32 steps of 4 dims.  The
+  // bf16 products are exact in float64.
+  for (int i = tid; i < kNB; i += kThreads) lh[i] = 0u;
   const int col = lane & 15, grp = lane >> 4;
-  bf16x8 qb[4];
+  double qd[32];
   {
-    const u16* qr = q + static_cast<size_t>(r) * kG * kD;
+    const u16* qr = q + static_cast<size_t>(r) * kG * kD + col * kD + 32 * grp;
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      qb[c] = col < kG ? as_bf16x8(load_u32x4(qr + col * kD + 32 * c + 8 * grp))
-                       : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+    for (int c = 0; c < 4; ++c) {
+      const u32x4 w4 = col < kG ? load_u32x4(qr + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t word = w4[t >> 1];
+        qd[8 * c + t] = static_cast<double>(
+            __uint_as_float((t & 1) ? (word & 0xFFFF0000u) : (word << 16)));
+      }
+    }
   }
+  const double l2 = col < kG ? lse2[static_cast<size_t>(r) * kG + col] : 0.0;
+  __syncthreads();
   const int b = r / (T * Hkv);
   const int g = r % Hkv;
   const u16* kr = k + (static_cast<size_t>(b) * Hkv + g) * static_cast<size_t>(S) * kD;
-  float* cy = cand_y + static_cast<size_t>(r) * Spad;
+  double* cy = cand_y + static_cast<size_t>(r) * Spad;
   int32_t* ci = cand_idx + static_cast<size_t>(r) * Spad;
+  auto load_sub = [&](uint32_t i, u32x4 (&ka)[4]) {
+    int64_t key = static_cast<int64_t>(s_list[i]) * kSubKeys + col;
+    key = key < S - 1 ? key : S - 1;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) ka[c] = load_u32x4(kr + key * kD + 32 * grp + 8 * c);
+  };
+  u32x4 ka_cur[4], ka_nxt[4];
+  if (static_cast<uint32_t>(wave) < n_local) load_sub(wave, ka_cur);
   for (uint32_t i = wave; i < n_local; i += kThreads / 64) {
     const int64_t key0 = static_cast<int64_t>(s_list[i]) * kSubKeys;
-    int64_t key = key0 + col;
-    key = key < S - 1 ? key : S - 1;
-    f32x4 acc{0.f, 0.f, 0.f, 0.f};
+    if (i + kThreads / 64 < n_local) load_sub(i + kThreads / 64, ka_nxt);
+    // four independent accumulation chains (one per 8-dim slice of the lane's
+    // 32 dims), summed at the end
+    f64x4 part[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      acc = mfma_16x16x32(as_bf16x8(load_u32x4(kr + key * kD + 32 * c + 8 * grp)), qb[c], acc);
-    float y[4];
+    for (int c = 0; c < 4; ++c) part[c] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t word = ka_cur[c][t >> 1];
+        const double kv = static_cast<double>(
+            __uint_as_float((t & 1) ? (word & 0xFFFF0000u) : (word << 16)));
+        part[c] = __builtin_amdgcn_mfma_f64_16x16x4f64(kv, qd[8 * c + t], part[c], 0, 0, 0);
+      }
+    }
+    const f64x4 acc = (part[0] + part[1]) + (part[2] + part[3]);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) ka_cur[c] = ka_nxt[c];
+    // register e holds key grp + 4e against head col
+    double y[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      float v = col < kG ? fmaf(acc[e], c2_hi, acc[e] * c2_lo) - lse2f[col] : -INFINITY;
-      v = fmaxf(v, __shfl_xor(v, 1));
-      v = fmaxf(v, __shfl_xor(v, 2));
-      v = fmaxf(v, __shfl_xor(v, 4));
+      double v = col < kG ? c2 * acc[e] - l2 : -INFINITY;
+      v = fmax(v, __shfl_xor(v, 1));
+      v = fmax(v, __shfl_xor(v, 2));
+      v = fmax(v, __shfl_xor(v, 4));
       y[e] = v;
     }
-    if (col == 0) {
-      const size_t pos = base + static_cast<size_t>(i) * kSubKeys + 4 * grp;
+    if (col < 4) {
+      const double ye = col == 0 ? y[0] : col == 1 ? y[1] : col == 2 ? y[2] : y[3];
+      const int kk = grp + 4 * col;
+      const int64_t j = key0 + kk;
+      const bool ok = j < first;
+      const size_t pos = base + static_cast<size_t>(i) * kSubKeys + kk;
+      cy[pos] = ok ? ye : -INFINITY;
+      ci[pos] = ok ? static_cast<int32_t>(j) : -1;
+      if (ok) atomicAdd(&lh[cand_bin(ye, ybase)], 1u);
+    }
+  }
+  __syncthreads();
+  flush_hist(lh, hist_c + static_cast<size_t>(r) * kNB, static_cast<uint32_t>(topk), &s_lo);
+}
+
+// ---- the row's exact top-k from its candidate list, over many work-groups:
+// split (above the k-th bin: selected; the k-th bin: band), rank the band,
+// rank the selection by index.
+
+constexpr int kSplitPerWG = 16 * kThreads;  // list entries per work-group round
+constexpr int kSplitMaxWG = 32;             // work-groups per row (grid-stride)
+
+// Entries in bins above the k-th bin b* of the row's candidate histogram are
+// appended to the selection list, entries in b* to the band list.  When the
+// histogram holds fewer than k entries every candidate is selected.
+__global__ __launch_bounds__(kThreads) void cand_split_kernel(
+    RowInfo* __restrict__ info, const uint32_t* __restrict__ hist_c,
+    const double* __restrict__ cand_y, const int32_t* __restrict__ cand_idx,
+    const float* __restrict__ ytop_h, int32_t* __restrict__ sel_list,
+    int32_t* __restrict__ band_idx, uint64_t* __restrict__ band_key, int64_t S, int64_t Spad,
+    int T, int Hkv, int topk, int w) {
+  __shared__ uint32_t lh[kNB];
+  __shared__ int s_b;
+  __shared__ float s_ybase;
+  __shared__ uint32_t s_cnt[2][16];
+  __shared__ uint32_t s_base[4];
+  const int r = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int64_t first = row_first(row_pos(r, T, Hkv, S), w);
+  if (topk <= 0 || first == 0) return;
+  const int64_t n_list = min(static_cast<int64_t>(info[r].cert_count), Spad);
+  if (static_cast<int64_t>(blockIdx.x) * kSplitPerWG >= n_list) return;
+  for (int i = tid; i < kNB; i += kThreads) lh[i] = hist_c[static_cast<size_t>(r) * kNB + i];
+  if (tid == 0) s_ybase = row_ybase(ytop_h, r);
+  __syncthreads();
+  if (tid < 64) {
+    const KthBin kb = kth_bin_wave(lh, static_cast<uint32_t>(topk));
+    if (tid == 0) s_b = kb.found ? kb.bstar : -1;
+  }
+  __syncthreads();
+  const int bstar = s_b;
+  const float ybase = s_ybase;
+  const double* cy = cand_y + static_cast<size_t>(r) * Spad;
+  const int32_t* ci = cand_idx + static_cast<size_t>(r) * Spad;
+  int32_t* sl = sel_list + static_cast<size_t>(r) * kMaxSel;
+  int32_t* gbi = band_idx + static_cast<size_t>(r) * Spad;
+  uint64_t* gbk = band_key + static_cast<size_t>(r) * Spad;
+  for (int64_t c0 = static_cast<int64_t>(blockIdx.x) * kSplitPerWG; c0 < n_list;
+       c0 += static_cast<int64_t>(gridDim.x) * kSplitPerWG) {
+    // the list holds whole subtiles: 16 consecutive entries per thread
+    const int64_t i0 = c0 + 16 * tid;
+    const bool live = i0 < n_list;
+    double yv[16];
+    int32_t cv[16];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t j = key0 + 4 * grp + e;
-        const bool ok = j < first;
-        cy[pos + e] = ok ? y[e] : -INFINITY;
-        ci[pos + e] = ok ? static_cast<int32_t>(j) : -1;
+    for (int u = 0; u < 4; ++u) {
+      const int4 c4 = live ? *reinterpret_cast<const int4*>(ci + i0 + 4 * u) : int4{-1, -1, -1, -1};
+      cv[4 * u] = c4.x;
+      cv[4 * u + 1] = c4.y;
+      cv[4 * u + 2] = c4.z;
+      cv[4 * u + 3] = c4.w;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const double2 y2 = live ? *reinterpret_cast<const double2*>(cy + i0 + 2 * u) : double2{0.0, 0.0};
+      yv[2 * u] = y2.x;
+      yv[2 * u + 1] = y2.y;
+    }
+    uint32_t mu = 0, ma = 0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int bn = cand_bin(yv[e], ybase);
+      const bool valid = cv[e] >= 0;
+      mu |= static_cast<uint32_t>(valid && bn > bstar) << e;
+      ma |= static_cast<uint32_t>(valid && bn == bstar) << e;
+    }
+    uint32_t ou, oa;
+    reserve_two(__popc(mu), __popc(ma), &info[r].up_count, &info[r].unc_count, s_cnt, s_base,
+                ou, oa);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      if ((mu >> e) & 1u) {
+        if (ou < static_cast<uint32_t>(kMaxSel)) sl[ou] = cv[e];
+        ++ou;
+      } else if ((ma >> e) & 1u) {
+        if (oa < static_cast<uint64_t>(Spad)) {
+          gbk[oa] = ordered_u64(yv[e]);
+          gbi[oa] = cv[e];
+        }
+        ++oa;
       }
     }
   }
 }
 
-// One work-group per row: exact top-k among the candidates, then emit.
-__global__ __launch_bounds__(kRowThreads) void row_select_kernel(
-    const RowInfo* __restrict__ info, const float* __restrict__ cand_y,
-    const int32_t* __restrict__ cand_idx, const float* __restrict__ ytop_h,
-    const double* __restrict__ lse2, const u16* __restrict__ q, const u16* __restrict__ k,
-    int32_t* __restrict__ band_idx, uint64_t* __restrict__ band_key,
-    int32_t* __restrict__ idx_out, int32_t* __restrict__ nsel_out, int64_t S, int64_t Spad,
-    int T, int Hkv, int topk, int w, int cap, double c2) {
-  __shared__ uint32_t lh[kNB];
-  __shared__ int32_t tmp[kMaxSel];
-  __shared__ int32_t sel[kMaxSel];
-  __shared__ Cand cands[kUncCap];
-  __shared__ double qd[kG * kD];
-  __shared__ double l2s[kG];
+// Sizes the rank kernels agree on: selected above the band, band size, and
+// how many band entries join the selection.
+struct SelCounts {
+  uint32_t n_up, n_band, take;
+};
+__device__ __forceinline__ SelCounts sel_counts(const RowInfo& inf, int topk) {
+  SelCounts c;
+  c.n_up = min(inf.up_count, static_cast<uint32_t>(topk));
+  c.n_band = inf.unc_count;
+  c.take = min(static_cast<uint32_t>(topk) - c.n_up, c.n_band);
+  return c;
+}
+
+// Rank of each band entry by (importance desc, index asc) among the row's band:
+// 64 entries per work-group (one per lane), the four waves each count over a
+// quarter of the band.  Entries of rank < take join the selection list at
+// n_up + rank.  A band above kBandRankMax entries is resolved by work-group 0
+// with the radix select.
+__global__ __launch_bounds__(kThreads) void band_rank_kernel(
+    const RowInfo* __restrict__ info, const int32_t* __restrict__ band_idx,
+    const uint64_t* __restrict__ band_key, int32_t* __restrict__ sel_list, int64_t S,
+    int64_t Spad, int T, int Hkv, int topk, int w) {
+  __shared__ uint32_t part[4][64];
   __shared__ uint32_t h256[256];
-  __shared__ uint32_t s_count, s_band, s_valid, s_tlo, s_need;
+  __shared__ uint32_t s_count, s_tlo, s_need;
   __shared__ uint64_t s_thi;
-  __shared__ int s_lo, s_hi;
-  __shared__ float s_ybase;
-  const int r = blockIdx.x;
+  const int r = blockIdx.y;
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t first = row_first(row_pos(r, T, Hkv, S), w);
+  if (topk <= 0 || first == 0) return;
+  const SelCounts c = sel_counts(info[r], topk);
+  if (c.take == 0) return;
+  const int32_t* bi = band_idx + static_cast<size_t>(r) * Spad;
+  const uint64_t* bk = band_key + static_cast<size_t>(r) * Spad;
+  int32_t* sl = sel_list + static_cast<size_t>(r) * kMaxSel;
+  if (c.n_band > static_cast<uint32_t>(kBandRankMax)) {
+    if (blockIdx.x != 0) return;
+    struct ListSrc {
+      const uint64_t* k;
+      const int32_t* x;
+      __device__ bool get(int64_t i, uint64_t& key, int32_t& j) const {
+        key = k[i];
+        j = x[i];
+        return true;
+      }
+    } src{bk, bi};
+    if (tid == 0) s_count = c.n_up;
+    __syncthreads();
+    radix_select_band(src, min(static_cast<int64_t>(c.n_band), Spad), c.take, sl, &s_count,
+                      h256, &s_thi, &s_tlo, &s_need);
+    return;
+  }
+  const uint32_t e0 = blockIdx.x * 64u;
+  if (e0 >= c.n_band) return;
+  const uint32_t e = e0 + lane;
+  const bool mine = e < c.n_band;
+  const Cand me = mine ? Cand{bk[e], bi[e], 0} : Cand{0ull, 0x7FFFFFFF, 0};
+  // quarters of whole 16-entry blocks; reads past the band stay inside the
+  // row's list (n_band <= Spad, both multiples of 64 after rounding) and are
+  // masked
+  const uint32_t q = ((c.n_band + 3u) / 4u + 15u) & ~15u;
+  const uint32_t f0 = wave * q, f1 = min(c.n_band, f0 + q);
+  uint32_t beat = 0;
+  for (uint32_t f = f0; f < f1; f += 16) {
+    uint64_t ok[16];
+    int32_t oi[16];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const ulonglong2 k2 = *reinterpret_cast<const ulonglong2*>(bk + f + 2 * u);
+      ok[2 * u] = k2.x;
+      ok[2 * u + 1] = k2.y;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int4 i4 = *reinterpret_cast<const int4*>(bi + f + 4 * u);
+      oi[4 * u] = i4.x;
+      oi[4 * u + 1] = i4.y;
+      oi[4 * u + 2] = i4.z;
+      oi[4 * u + 3] = i4.w;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      beat += static_cast<uint32_t>((f + u < f1) & before(Cand{ok[u], oi[u], 0}, me));
+  }
+  part[wave][lane] = beat;
+  __syncthreads();
+  if (wave == 0 && mine) {
+    const uint32_t rank = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
+    if (rank < c.take) sl[c.n_up + rank] = me.idx;
+  }
+}
+
+// The row's output: the selection in ascending index order (each entry goes to
+// its rank; 64 entries per work-group, four waves over quarters of the list),
+// then the window [first, P], then -1 up to cap, and the count.
+__global__ __launch_bounds__(kThreads) void emit_rank_kernel(
+    const RowInfo* __restrict__ info, const int32_t* __restrict__ sel_list,
+    int32_t* __restrict__ idx_out, int32_t* __restrict__ nsel_out, int64_t S, int T, int Hkv,
+    int topk, int w, int cap) {
+  __shared__ uint32_t part[4][64];
+  const int r = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int P = row_pos(r, T, Hkv, S);
   const int64_t first = row_first(P, w);
-  const int64_t n_list = min(static_cast<int64_t>(info[r].cert_count), Spad);
-  const float* cy = cand_y + static_cast<size_t>(r) * Spad;
-  const int32_t* ci = cand_idx + static_cast<size_t>(r) * Spad;
-  int n_keep = 0;
-  if (tid == 0) {
-    s_count = 0u;
-    s_band = 0u;
-    s_valid = 0u;
-    s_ybase = row_ybase(ytop_h, r);
-  }
-  for (int i = tid; i < kNB; i += kRowThreads) lh[i] = 0u;
-  __syncthreads();
+  uint32_t n_keep = 0;
   if (topk > 0 && first > 0) {
-    // ---- pass 1: histogram of the candidates' float32 importances
-    const float ybase = s_ybase;
-    uint32_t nv = 0;
-    for (int64_t i = tid; i < n_list; i += kRowThreads) {
-      if (ci[i] < 0) continue;
-      ++nv;
-      atomicAdd(&lh[key_from_log2(cy[i], ybase) >> kBinShift], 1u);
-    }
-    atomicAdd(&s_valid, nv);
-    __syncthreads();
-    const uint32_t n_valid = s_valid;
-    if (n_valid <= static_cast<uint32_t>(topk)) {
-      // every candidate key is kept
-      for (int64_t i = tid; i < n_list; i += kRowThreads)
-        if (ci[i] >= 0) tmp[atomicAdd(&s_count, 1u)] = ci[i];
-      __syncthreads();
-      n_keep = static_cast<int>(n_valid);
-    } else {
-      if (tid < 64) {
-        const KthBin kb = kth_bin_wave(lh, static_cast<uint32_t>(topk));
-        if (tid == 0) {
-          s_lo = max(0, kb.bstar - 1);
-          s_hi = min(kNB - 1, kb.bstar + 1);
-        }
-      }
-      // the query heads in float64, for the exact re-ranking of the band
-      const u16* qr = q + static_cast<size_t>(r) * kG * kD;
-      for (int i = tid; i < kG * kD; i += kRowThreads) qd[i] = static_cast<double>(bf16_bits_to_f32(qr[i]));
-      if (tid < kG) l2s[tid] = lse2[static_cast<size_t>(r) * kG + tid];
-      __syncthreads();
-      // ---- pass 2: bins above the band are selected; the band goes to the
-      // row's scratch list
-      const int lo = s_lo, hi = s_hi;
-      int32_t* bi = band_idx + static_cast<size_t>(r) * Spad;
-      uint64_t* bk = band_key + static_cast<size_t>(r) * Spad;
-      for (int64_t i = tid; i < n_list; i += kRowThreads) {
-        const int32_t j = ci[i];
-        if (j < 0) continue;
-        const int bn = static_cast<int>(key_from_log2(cy[i], ybase) >> kBinShift);
-        if (bn > hi) tmp[atomicAdd(&s_count, 1u)] = j;
-        else if (bn >= lo) bi[atomicAdd(&s_band, 1u)] = j;
-      }
-      __syncthreads();
-      const uint32_t n_band = s_band;
-      // exact importance of the band keys in float64 (bf16 products are exact)
-      const int b = r / (T * Hkv);
-      const int g = r % Hkv;
-      const u16* kr = k + (static_cast<size_t>(b) * Hkv + g) * static_cast<size_t>(S) * kD;
-      for (uint32_t i = tid; i < n_band; i += kRowThreads) {
-        const int32_t j = bi[i];
-        const u16* kj = kr + static_cast<size_t>(j) * kD;
-        u32x4 raw[16];
-#pragma unroll
-        for (int c = 0; c < 16; ++c) raw[c] = load_u32x4(kj + 8 * c);
-        double acc[kG];
-#pragma unroll
-        for (int h = 0; h < kG; ++h) acc[h] = 0.0;
-#pragma unroll
-        for (int c = 0; c < 16; ++c) {
-#pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            const uint32_t word = raw[c][t >> 1];
-            const double kv = static_cast<double>(
-                __uint_as_float((t & 1) ? (word & 0xFFFF0000u) : (word << 16)));
-#pragma unroll
-            for (int h = 0; h < kG; ++h) acc[h] = fma(qd[h * kD + 8 * c + t], kv, acc[h]);
-          }
-          // keep the scheduler from hoisting the next chunk's LDS reads of the
-          // query (it would run out of registers)
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        double y = -INFINITY;
-#pragma unroll
-        for (int h = 0; h < kG; ++h) y = fmax(y, c2 * acc[h] - l2s[h]);
-        bk[i] = ordered_u64(y);
-      }
-      __syncthreads();
-      const uint32_t take = static_cast<uint32_t>(topk) - s_count;
-      take_best(bk, bi, n_band, take, cands, tmp, &s_count, h256, &s_thi, &s_tlo, &s_need);
-      n_keep = topk;
-    }
+    const SelCounts c = sel_counts(info[r], topk);
+    n_keep = c.n_up + c.take;
   }
+  int32_t* out = idx_out + static_cast<size_t>(r) * cap;
+  if (blockIdx.x == 0) {
+    const int n_total = static_cast<int>(n_keep) + static_cast<int>(static_cast<int64_t>(P) - first + 1);
+    for (int i = static_cast<int>(n_keep) + tid; i < cap; i += kThreads)
+      out[i] = i < n_total ? static_cast<int32_t>(first + (i - static_cast<int>(n_keep))) : -1;
+    if (tid == 0) nsel_out[r] = n_total;
+  }
+  const uint32_t e0 = blockIdx.x * 64u;
+  if (e0 >= n_keep) return;
+  const int32_t* sl = sel_list + static_cast<size_t>(r) * kMaxSel;
+  const uint32_t e = e0 + lane;
+  const bool mine = e < n_keep;
+  const int32_t me = mine ? sl[e] : 0x7FFFFFFF;
+  // quarters of whole 16-entry blocks (reads stay inside the row's kMaxSel
+  // entries and are masked past n_keep)
+  const uint32_t q = ((n_keep + 3u) / 4u + 15u) & ~15u;
+  const uint32_t f0 = wave * q, f1 = min(n_keep, f0 + q);
+  uint32_t below = 0;
+  for (uint32_t f = f0; f < f1; f += 16) {
+    int32_t o[16];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int4 i4 = *reinterpret_cast<const int4*>(sl + f + 4 * u);
+      o[4 * u] = i4.x;
+      o[4 * u + 1] = i4.y;
+      o[4 * u + 2] = i4.z;
+      o[4 * u + 3] = i4.w;
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) below += static_cast<uint32_t>((f + u < f1) & (o[u] < me));
+  }
+  part[wave][lane] = below;
   __syncthreads();
-  emit_row(tmp, sel, n_keep, first, P, idx_out + static_cast<size_t>(r) * cap, nsel_out + r, cap);
+  if (wave == 0 && mine) {
+    const uint32_t rank = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
+    if (rank < n_keep) out[rank] = me;
+  }
 }
 
 }  // namespace
@@ -769,24 +1041,32 @@ hipError_t launch_fused_select(const Plan& p, const u16* q, const u16* k, int32_
   const double* lse2 = reinterpret_cast<const double*>(w + p.off_lse2);
   const float* ytop = reinterpret_cast<const float*>(w + p.off_ytop);
   uint32_t* hist = reinterpret_cast<uint32_t*>(w + p.off_hist);
+  uint32_t* hist_c = reinterpret_cast<uint32_t*>(w + p.off_hist_c);
   RowInfo* info = reinterpret_cast<RowInfo*>(w + p.off_info);
-  float* cand_y = reinterpret_cast<float*>(w + p.off_cand_y);
+  double* cand_y = reinterpret_cast<double*>(w + p.off_cand_y);
   int32_t* cand_idx = reinterpret_cast<int32_t*>(w + p.off_cand_idx);
   const double c2 = p.scale * 1.4426950408889634;  // scale * log2(e)
-  const float c2_hi = static_cast<float>(c2);
-  const float c2_lo = static_cast<float>(c2 - static_cast<double>(c2_hi));
   hipLaunchKernelGGL(subtile_hist_kernel, dim3(p.st_nchunk, p.R), dim3(kThreads), 0, st, stmax,
-                     lse2, ytop, hist, p.S, p.Spad, p.T, p.Hkv, p.k, p.w, p.st_chunk);
+                     lse2, ytop, hist, hist_c, p.S, p.Spad, p.T, p.Hkv, p.k, p.w, p.st_chunk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(subtile_score_kernel, dim3(p.st_nchunk, p.R), dim3(kThreads), 0, st, stmax,
-                     lse2, ytop, hist, info, q, k, cand_y, cand_idx, p.S, p.Spad, p.T, p.Hkv,
-                     p.k, p.w, p.st_chunk, c2_hi, c2_lo);
+                     lse2, ytop, hist, hist_c, info, q, k, cand_y, cand_idx, p.S, p.Spad, p.T,
+                     p.Hkv, p.k, p.w, p.st_chunk, c2);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(row_select_kernel, dim3(p.R), dim3(kRowThreads), 0, st, info, cand_y,
-                     cand_idx, ytop, lse2, q, k, reinterpret_cast<int32_t*>(w + p.off_band_idx),
-                     reinterpret_cast<uint64_t*>(w + p.off_band_key), idx, n_sel, p.S, p.Spad,
-                     p.T, p.Hkv, p.k, p.w, p.cap, c2);
+  const int64_t n_split = std::min<int64_t>((p.Spad + kSplitPerWG - 1) / kSplitPerWG, kSplitMaxWG);
+  int32_t* sel_list = reinterpret_cast<int32_t*>(w + p.off_sel_list);
+  int32_t* band_idx = reinterpret_cast<int32_t*>(w + p.off_band_idx);
+  uint64_t* band_key = reinterpret_cast<uint64_t*>(w + p.off_band_key);
+  hipLaunchKernelGGL(cand_split_kernel, dim3(static_cast<unsigned>(n_split), p.R), dim3(kThreads),
+                     0, st, info, hist_c, cand_y, cand_idx, ytop, sel_list, band_idx, band_key,
+                     p.S, p.Spad, p.T, p.Hkv, p.k, p.w);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(band_rank_kernel, dim3(kBandRankMax / 64, p.R), dim3(kThreads), 0, st, info,
+                     band_idx, band_key, sel_list, p.S, p.Spad, p.T, p.Hkv, p.k, p.w);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(emit_rank_kernel, dim3(kMaxSel / 64, p.R), dim3(kThreads), 0, st, info,
+                     sel_list, idx, n_sel, p.S, p.T, p.Hkv, p.k, p.w, p.cap);
   return hipGetLastError();
 }
 
