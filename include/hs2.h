@@ -128,9 +128,11 @@ int hs2_sparse_attn(const hs2_shape* shape, int32_t n_layers, const hs2_bf16* q,
 /* One Cross-Decoder group step: full attention with importance, selection,
  * then n_sparse_layers sparse layers — the same results as the three calls
  * above in sequence, except that the selection here ranks keys by importance
- * recomputed in float64 near the k-th threshold (so that keys are ordered by
+ * computed in float64 from exact bf16 products (so that keys are ordered by
  * their exact importance, not by its float32 rounding).  scores and lse are
- * nullable.  q_sparse / out_sparse may be NULL when n_sparse_layers = 0. */
+ * nullable.  q_sparse / out_sparse may be NULL when n_sparse_layers = 0.
+ * v1: decode only (n_q_tokens = 1); a prefill chunk returns
+ * HS2_ERR_UNSUPPORTED. */
 int hs2_cross_decoder_step(const hs2_shape* shape, int32_t n_sparse_layers,
                            const hs2_bf16* q_full, const hs2_bf16* q_sparse,
                            const hs2_bf16* k, const hs2_bf16* v, hs2_bf16* out_full,
