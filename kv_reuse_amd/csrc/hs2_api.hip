@@ -111,8 +111,12 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
   q.off_hist_c = take(decode ? Rz * kNB * sizeof(uint32_t) : 0);
   q.off_cand_y = take(fz * sizeof(double));
   q.off_cand_idx = take(fz * sizeof(int32_t));
-  q.off_band_idx = take(fz * sizeof(int32_t));
-  q.off_band_key = take(fz * sizeof(uint64_t));
+  // band lists: a whole row's worth in decode; in a prefill chunk (many rows)
+  // a bounded list per row
+  q.band_cap = decode ? q.Spad : std::min<int64_t>(q.Spad, kPrefillBandCap);
+  q.off_band_idx = take(Rz * q.band_cap * sizeof(int32_t));
+  q.off_band_key = take(Rz * q.band_cap * sizeof(uint64_t));
+  q.off_ybuf = take(decode ? 0 : Rz * q.Spad * sizeof(float));
   q.off_sel_list = take(decode ? Rz * kMaxSel * sizeof(int32_t) : 0);
   const size_t sp_parts = q.sp_nch > 1 ? Rz * q.sp_nch * n_layers * kG : 0;
   q.off_sp_m = take(sp_parts * sizeof(float));
@@ -172,9 +176,13 @@ int hs2_full_attn_scores(const hs2_shape* shape, const hs2_bf16* q, const hs2_bf
   if (st != HS2_OK) return st;
   if (!q || !k || !v || !out) return HS2_ERR_INVALID_ARG;
   if ((st = check_ws(p, ws, ws_bytes)) != HS2_OK) return st;
-  if (p.T != 1) return HS2_ERR_UNSUPPORTED;
   (void)hipGetLastError();
   const hipStream_t s = as_stream(stream);
+  if (p.T != 1) {
+    HS2_TRY(launch_full_prefill(p, q, k, v, out, lse, ws, s));
+    if (scores) HS2_TRY(launch_prefill_importance(p, q, k, false, scores, ws, s));
+    return HS2_OK;
+  }
   if ((st = run_full(p, q, k, v, out, lse, ws, s)) != HS2_OK) return st;
   if (scores) HS2_TRY(launch_full_scores(p, q, k, scores, ws, s));
   return HS2_OK;
@@ -218,9 +226,16 @@ int hs2_cross_decoder_step(const hs2_shape* shape, int32_t n_sparse_layers,
   if (!q_full || !k || !v || !out_full || !idx || !n_sel) return HS2_ERR_INVALID_ARG;
   if (n_sparse_layers > 0 && (!q_sparse || !out_sparse)) return HS2_ERR_INVALID_ARG;
   if ((st = check_ws(p, ws, ws_bytes)) != HS2_OK) return st;
-  if (p.T != 1) return HS2_ERR_UNSUPPORTED;
   (void)hipGetLastError();
   const hipStream_t s = as_stream(stream);
+  if (p.T != 1) {
+    HS2_TRY(launch_full_prefill(p, q_full, k, v, out_full, lse, ws, s));
+    HS2_TRY(launch_prefill_importance(p, q_full, k, true, scores, ws, s));
+    HS2_TRY(launch_prefill_select(p, q_full, k, idx, n_sel, ws, s));
+    if (n_sparse_layers > 0)
+      HS2_TRY(launch_sparse(p, q_sparse, k, v, idx, n_sel, out_sparse, ws, s));
+    return HS2_OK;
+  }
   if ((st = run_full(p, q_full, k, v, out_full, lse, ws, s)) != HS2_OK) return st;
   if (scores) HS2_TRY(launch_full_scores(p, q_full, k, scores, ws, s));
   HS2_TRY(launch_fused_select(p, q_full, k, idx, n_sel, ws, s));
@@ -241,7 +256,6 @@ int hs2_cross_decoder_step_timed(const hs2_shape* shape, int32_t n_sparse_layers
     return HS2_ERR_INVALID_ARG;
   if (n_sparse_layers > 0 && (!q_sparse || !out_sparse)) return HS2_ERR_INVALID_ARG;
   if ((st = check_ws(p, ws, ws_bytes)) != HS2_OK) return st;
-  if (p.T != 1) return HS2_ERR_UNSUPPORTED;
   (void)hipGetLastError();
   const hipStream_t s = as_stream(stream);
   hipEvent_t ev[5];
@@ -256,12 +270,18 @@ int hs2_cross_decoder_step_timed(const hs2_shape* shape, int32_t n_sparse_layers
   int rc = HS2_OK;
   for (int it = 0; it < iters && rc == HS2_OK; ++it) {
     float ms[4] = {0, 0, 0, 0};
+    const bool decode = p.T == 1;
     rc = hip_status(hipEventRecord(ev[0], s));
-    if (rc == HS2_OK) rc = hip_status(launch_full_decode_split(p, q_full, k, v, ws, s));
+    if (rc == HS2_OK)
+      rc = hip_status(decode ? launch_full_decode_split(p, q_full, k, v, ws, s)
+                             : launch_full_prefill(p, q_full, k, v, out_full, nullptr, ws, s));
     if (rc == HS2_OK) rc = hip_status(hipEventRecord(ev[1], s));
-    if (rc == HS2_OK) rc = hip_status(launch_full_combine(p, out_full, nullptr, ws, s));
+    if (rc == HS2_OK && decode) rc = hip_status(launch_full_combine(p, out_full, nullptr, ws, s));
     if (rc == HS2_OK) rc = hip_status(hipEventRecord(ev[2], s));
-    if (rc == HS2_OK) rc = hip_status(launch_fused_select(p, q_full, k, idx, n_sel, ws, s));
+    if (rc == HS2_OK)
+      rc = hip_status(decode ? launch_fused_select(p, q_full, k, idx, n_sel, ws, s)
+                             : launch_prefill_importance(p, q_full, k, true, nullptr, ws, s));
+    if (rc == HS2_OK && !decode) rc = hip_status(launch_prefill_select(p, q_full, k, idx, n_sel, ws, s));
     if (rc == HS2_OK) rc = hip_status(hipEventRecord(ev[3], s));
     if (rc == HS2_OK && n_sparse_layers > 0)
       rc = hip_status(launch_sparse(p, q_sparse, k, v, idx, n_sel, out_sparse, ws, s));

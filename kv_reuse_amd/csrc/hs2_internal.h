@@ -34,6 +34,7 @@ struct RowInfo {
   uint32_t pad;
 };
 constexpr int kBandRankMax = 4096;  // bands up to this size are ranked in parallel
+constexpr int64_t kPrefillBandCap = 8192;  // near-threshold keys listed per prefill row
 
 // Where each piece of the workspace sits, for one shape.
 struct Plan {
@@ -55,6 +56,9 @@ struct Plan {
   // fused selection from the subtile maxima
   int st_chunk, st_nchunk;
   size_t off_hist_c, off_cand_y, off_cand_idx, off_band_idx, off_band_key, off_sel_list;
+  // prefill chunk: per-row log2 importance of the older keys, band capacity per row
+  size_t off_ybuf;
+  int64_t band_cap;
   // sparse
   int sp_nch;
   size_t off_sp_m, off_sp_l, off_sp_o;
@@ -81,6 +85,18 @@ hipError_t launch_scores_select(const Plan& p, const float* scores, int32_t* idx
 // rescoring on MFMA, float64 re-ranking near the threshold.
 hipError_t launch_fused_select(const Plan& p, const u16* q, const u16* k, int32_t* idx,
                                int32_t* n_sel, void* ws, hipStream_t st);
+
+// Full attention over a prefill chunk (T > 1): causal flash attention writing
+// out, lse (nullable), lse2 and each head's bound on log2 importance.
+hipError_t launch_full_prefill(const Plan& p, const u16* q, const u16* k, const u16* v, u16* out,
+                               float* lse, void* ws, hipStream_t st);
+// Prefill chunk importance: for the selection (per-row y and histogram in the
+// workspace) and/or dense scores for the caller (nullable).
+hipError_t launch_prefill_importance(const Plan& p, const u16* q, const u16* k, bool for_select,
+                                     float* scores, void* ws, hipStream_t st);
+// Prefill chunk selection: one work-group per row.
+hipError_t launch_prefill_select(const Plan& p, const u16* q, const u16* k, int32_t* idx,
+                                 int32_t* n_sel, void* ws, hipStream_t st);
 
 // Sparse layers (all n_layers fused: one gather of the selected K/V rows).
 hipError_t launch_sparse(const Plan& p, const u16* q, const u16* k, const u16* v,
@@ -111,6 +127,16 @@ __device__ __forceinline__ u32x4 load_u32x4(const void* p) {
 // Streaming load: the data is read once, so it is marked non-temporal.
 __device__ __forceinline__ u32x4 load_u32x4_nt(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+// Fixed-point position of a log2 importance y within [ybase, ybase + kYRange)
+// as a 32-bit key (monotone in y, saturating at both ends); its top 11 bits
+// are the selection histogram bin (1/32 octave).  Every producer and consumer
+// of a histogram uses this one function.
+__device__ __forceinline__ uint32_t key_from_log2(float y, float ybase) {
+  const float z = (y - ybase) * 67108864.0f;  // 2^32 / kYRange
+  if (!(z > 0.f)) return 0u;
+  if (z >= 4294967040.0f) return 0xFFFFFFFFu;
+  return static_cast<uint32_t>(z);
 }
 // Order-preserving maps from floats to unsigned integers (larger value -> larger key).
 __device__ __forceinline__ uint32_t ordered_u32(float f) {

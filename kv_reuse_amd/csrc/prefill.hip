@@ -1,0 +1,423 @@
+// Full-attention layer of a Cross-Decoder group over a chunk of T > 1 query
+// tokens (prefill): causal attention of every chunk token over the shared KV
+// cache, then each (token, KV head) row's log2 importance of every older key.
+//
+// The group's full layer and its attention-derived selection: news page
+// "两天两连更：小米提前亮出V3底牌", section "两级KV共享：让模型少跑一半" (KV
+// Reuse), video page "小米 MiMo-V3 HySparse2 架构：读长文省一半", section
+// "HySparse2 的解法：两派都用，还改了流程".
+//
+// Design (gfx950):
+//  * A work-group takes 16 consecutive chunk tokens of one (batch, KV head);
+//    their 16 x 8 query heads are the 128 columns of S^T = K . Q^T.  Each of
+//    the 4 waves owns 4 tokens = two 16-column query blocks (2 tokens x 8 heads
+//    each), so no MFMA column is padding.
+//  * Keys come in tiles of 64, staged once in LDS for all four waves (K and V,
+//    272-byte row pitch); the next tile's global loads are in flight while the
+//    current one is processed.
+//  * S^T and O^T = V^T . P^T on MFMA 16x16x32 bf16; the P^T operand comes
+//    straight from the S^T accumulators and V^T from ds_read_b64_tr_b16, as in
+//    the decode kernel.  Online softmax in base 2 with an integer running
+//    max (exact power-of-two rescales, skipped when no column's max moved)
+//    and the normaliser accumulated in float64.
+//  * Causality: token t (position P_t = S - T + t) sees keys 0..P_t; only the
+//    last tiles of a work-group need the mask.
+//  * Work-groups are numbered so that each of the 8 XCDs gets a contiguous
+//    range of (batch, KV head, token block): the work-groups that share a KV
+//    head's K/V run on one XCD and share its L2.
+//  * The importance pass (second kernel) recomputes S^T with lse known and
+//    writes y = max_h(s2_h - lse2_h) per (row, older key) in float32, plus an
+//    exact per-row histogram kept in LDS (the work-group sees all of its rows'
+//    keys, so no atomics leave the work-group).
+
+#include "hs2_internal.h"
+
+namespace hs2 {
+namespace {
+
+constexpr int kPThreads = 256;
+constexpr int kPTok = 16;       // chunk tokens per work-group (attention)
+constexpr int kYTok = 8;        // chunk tokens per work-group (importance)
+constexpr int kPKeys = 64;      // keys per tile
+constexpr int kPPitch = 136;    // u16 per K/V row in LDS (272 bytes)
+
+__device__ __forceinline__ int xcd_linear(int id, int n) {
+  // hardware dispatch sends work-group id to XCD id % 8; renumber so that XCD x
+  // processes the contiguous range [x * n/8, (x+1) * n/8)
+  if (n % 8 != 0) return id;
+  return (id & 7) * (n >> 3) + (id >> 3);
+}
+
+// One 64-key tile of K (and optionally V) from global memory into registers:
+// thread t holds 64 bytes of key row t/4 (keys past `key_max` repeat it).
+struct TileRegs {
+  u32x4 k[4];
+  u32x4 v[4];
+};
+
+template <bool kWithV>
+__device__ __forceinline__ void tile_gload(TileRegs& r, const u16* __restrict__ kr,
+                                           const u16* __restrict__ vr, int64_t key0,
+                                           int64_t key_max) {
+  const int tid = threadIdx.x;
+  int64_t key = key0 + (tid >> 2);
+  key = key < key_max ? key : key_max;
+  const u16* ks = kr + key * kD + 32 * (tid & 3);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) r.k[c] = load_u32x4(ks + 8 * c);
+  if (kWithV) {
+    const u16* vs = vr + key * kD + 32 * (tid & 3);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) r.v[c] = load_u32x4(vs + 8 * c);
+  }
+}
+
+template <bool kWithV>
+__device__ __forceinline__ void tile_lstore(const TileRegs& r, u16* kt, u16* vt) {
+  const int tid = threadIdx.x;
+  u16* kd = kt + (tid >> 2) * kPPitch + 32 * (tid & 3);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(kd + 8 * c) = r.k[c];
+  if (kWithV) {
+    u16* vd = vt + (tid >> 2) * kPPitch + 32 * (tid & 3);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(vd + 8 * c) = r.v[c];
+  }
+}
+
+// K as the A operand of S^T for key subtile kt (16 keys) and dims 32c..32c+31.
+__device__ __forceinline__ bf16x8 lds_k_operand(const u16* kt, int sub, int c, int col, int grp) {
+  return as_bf16x8(*reinterpret_cast<const u32x4*>(kt + (16 * sub + col) * kPPitch + 32 * c + 8 * grp));
+}
+
+// Q^T as the B operand: column col of a query block = (token tok, head col & 7).
+__device__ __forceinline__ void load_q_block(const u16* __restrict__ qtok, int col, int grp,
+                                             bf16x8 (&qb)[4]) {
+  const u16* p = qtok + (col & 7) * kD + 8 * grp;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) qb[c] = as_bf16x8(load_u32x4(p + 32 * c));
+}
+
+// grid: B * Hkv * ceil(T / 16) work-groups of 256 threads.
+__global__ __launch_bounds__(kPThreads, 2) void full_prefill_kernel(
+    const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
+    u16* __restrict__ out, float* __restrict__ lse_out, double* __restrict__ lse2,
+    float* __restrict__ ytop_h, int64_t S, int T, int Hkv, int n_tblk, float c2_hi,
+    float c2_lo) {
+  __shared__ __align__(16) u16 kt[kPKeys * kPPitch];
+  __shared__ __align__(16) u16 vt[kPKeys * kPPitch];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int lin = xcd_linear(blockIdx.x, gridDim.x);
+  const int tb = lin % n_tblk;
+  const int bg = lin / n_tblk;
+  const int g = bg % Hkv, b = bg / Hkv;
+  const int Hq = Hkv * kG;
+  const u16* kr = k + static_cast<size_t>(bg) * S * kD;
+  const u16* vr = v + static_cast<size_t>(bg) * S * kD;
+  const int64_t pos0 = S - T;                      // position of chunk token 0
+  // this lane's two columns: query block qbk covers tokens 4*wave + 2*qbk + {0,1}
+  int64_t pcol[2];
+  bf16x8 qop[2][4];
+#pragma unroll
+  for (int qbk = 0; qbk < 2; ++qbk) {
+    int t = tb * kPTok + 4 * wave + 2 * qbk + (col >> 3);
+    t = t < T ? t : T - 1;                         // past the chunk: repeat the last token
+    pcol[qbk] = pos0 + t;
+    load_q_block(q + (static_cast<size_t>(b) * T + t) * Hq * kD + static_cast<size_t>(g) * kG * kD,
+                 col, grp, qop[qbk]);
+  }
+  const int t_last = min(T - 1, tb * kPTok + kPTok - 1);
+  const int64_t p_first = pos0 + tb * kPTok;       // smallest position in the work-group
+  const int64_t p_last = pos0 + t_last;
+  const int n_tiles = static_cast<int>((p_last + kPKeys) / kPKeys);
+
+  f32x4 o[2][8];
+#pragma unroll
+  for (int qbk = 0; qbk < 2; ++qbk)
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) o[qbk][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {-INFINITY, -INFINITY};
+  double l[2] = {0.0, 0.0};
+
+  TileRegs regs;
+  tile_gload<true>(regs, kr, vr, 0, p_last);
+  tile_lstore<true>(regs, kt, vt);
+  __syncthreads();
+  for (int it = 0; it < n_tiles; ++it) {
+    const int64_t key0 = static_cast<int64_t>(it) * kPKeys;
+    const bool more = it + 1 < n_tiles;
+    if (more) tile_gload<true>(regs, kr, vr, key0 + kPKeys, p_last);
+    // ---- S^T: 4 key subtiles x 2 query blocks
+    f32x4 sacc[2][4];
+#pragma unroll
+    for (int qbk = 0; qbk < 2; ++qbk)
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub) sacc[qbk][sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const bf16x8 a = lds_k_operand(kt, sub, c, col, grp);
+        sacc[0][sub] = mfma_16x16x32(a, qop[0][c], sacc[0][sub]);
+        sacc[1][sub] = mfma_16x16x32(a, qop[1][c], sacc[1][sub]);
+      }
+    const bool masked = key0 + kPKeys - 1 > p_first;
+    float p[2][4][4];
+#pragma unroll
+    for (int qbk = 0; qbk < 2; ++qbk) {
+      float sv[4][4];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a = sacc[qbk][sub][i];
+          float s = fmaf(a, c2_hi, a * c2_lo);
+          if (masked && key0 + 16 * sub + 4 * grp + i > pcol[qbk]) s = -INFINITY;
+          sv[sub][i] = s;
+          tmax = fmaxf(tmax, s);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      // key 0 is visible to every token, so the running max is finite from the
+      // first tile on
+      const float m_new = fmaxf(m[qbk], ceilf(tmax));
+      const float alpha = m[qbk] == -INFINITY ? 0.f : ldexpf(1.f, static_cast<int>(m[qbk] - m_new));
+      float ps = 0.f;
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[qbk][sub][i] = __builtin_amdgcn_exp2f(sv[sub][i] - m_new);
+          ps += p[qbk][sub][i];
+        }
+      l[qbk] = l[qbk] * static_cast<double>(alpha) + static_cast<double>(ps);
+      if (__ballot(alpha != 1.f) != 0) {
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) o[qbk][nb] *= alpha;
+      }
+      m[qbk] = m_new;
+    }
+    // ---- O^T += V^T . P^T over two k-steps of 32 keys
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      bf16x8 pb[2];
+#pragma unroll
+      for (int qbk = 0; qbk < 2; ++qbk) {
+        const u32x4 pp{pack_bf16x2(p[qbk][2 * ks][0], p[qbk][2 * ks][1]),
+                       pack_bf16x2(p[qbk][2 * ks][2], p[qbk][2 * ks][3]),
+                       pack_bf16x2(p[qbk][2 * ks + 1][0], p[qbk][2 * ks + 1][1]),
+                       pack_bf16x2(p[qbk][2 * ks + 1][2], p[qbk][2 * ks + 1][3])};
+        pb[qbk] = as_bf16x8(pp);
+      }
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const bf16x8 a = lds_vt_operand(vt + 32 * ks * kPPitch, kPPitch, nb, col, grp);
+        o[0][nb] = mfma_16x16x32(a, pb[0], o[0][nb]);
+        o[1][nb] = mfma_16x16x32(a, pb[1], o[1][nb]);
+      }
+    }
+    __syncthreads();               // every wave is done with this tile
+    if (more) {
+      tile_lstore<true>(regs, kt, vt);
+      __syncthreads();
+    }
+  }
+  // ---- epilogue: normalise, write out and the row statistics
+#pragma unroll
+  for (int qbk = 0; qbk < 2; ++qbk) {
+    double L = l[qbk];
+    L += __shfl_xor(L, 16);
+    L += __shfl_xor(L, 32);
+    const int t = tb * kPTok + 4 * wave + 2 * qbk + (col >> 3);
+    if (t >= T) continue;
+    const int h = col & 7;
+    const float inv = static_cast<float>(1.0 / L);
+    u16* orow = out + ((static_cast<size_t>(b) * T + t) * Hq + static_cast<size_t>(g) * kG + h) * kD;
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      const uint2 pk{pack_bf16x2(o[qbk][nb][0] * inv, o[qbk][nb][1] * inv),
+                     pack_bf16x2(o[qbk][nb][2] * inv, o[qbk][nb][3] * inv)};
+      *reinterpret_cast<uint2*>(orow + 16 * nb + 4 * grp) = pk;
+    }
+    if (grp == 0) {
+      const size_t row = (static_cast<size_t>(b) * T + t) * Hkv + g;
+      const double l2 = static_cast<double>(m[qbk]) + log2(L);
+      lse2[row * kG + h] = l2;
+      if (lse_out) lse_out[row * kG + h] = static_cast<float>(l2 * M_LN2);
+      ytop_h[row * kG + h] = static_cast<float>(-log2(L));
+    }
+  }
+}
+
+// Importance pass.  grid: B * Hkv * ceil(T / 8) work-groups of 256 threads; a
+// work-group takes 8 chunk tokens (one 16-column query block per wave).
+// Writes, for every row (b, t, g) it owns:
+//   y[row][j] = max_h(s2_h[j] - lse2_h) for older keys j < first_t (float32,
+//               when y is non-null), and its histogram hist[row][2048] over
+//               bins of 1/32 octave above the row's ybase (when hist is
+//               non-null; complete, plain stores);
+//   scores[row][j] = 2^y for all j <= P_t, 0 above (when scores is non-null).
+__global__ __launch_bounds__(kPThreads, 1) void prefill_importance_kernel(
+    const u16* __restrict__ q, const u16* __restrict__ k, const double* __restrict__ lse2,
+    const float* __restrict__ ytop_h, float* __restrict__ y, uint32_t* __restrict__ hist,
+    float* __restrict__ scores, int64_t S, int64_t Spad, int T, int Hkv, int w, int n_tblk,
+    float c2_hi, float c2_lo) {
+  __shared__ __align__(16) u16 kt[kPKeys * kPPitch];
+  __shared__ uint32_t lh[kYTok][kNB];
+  __shared__ float l2f[kYTok][kG];
+  __shared__ float s_ybase[kYTok];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int lin = xcd_linear(blockIdx.x, gridDim.x);
+  const int tb = lin % n_tblk;
+  const int bg = lin / n_tblk;
+  const int g = bg % Hkv, b = bg / Hkv;
+  const int Hq = Hkv * kG;
+  const u16* kr = k + static_cast<size_t>(bg) * S * kD;
+  const int64_t pos0 = S - T;
+  const bool want_hist = hist != nullptr;
+  if (want_hist)
+    for (int i = tid; i < kYTok * kNB; i += kPThreads) (&lh[0][0])[i] = 0u;
+  if (tid < kYTok * kG) {
+    const int j = tid / kG, h = tid % kG;
+    int t = tb * kYTok + j;
+    t = t < T ? t : T - 1;
+    const size_t row = (static_cast<size_t>(b) * T + t) * Hkv + g;
+    l2f[j][h] = static_cast<float>(lse2[row * kG + h]);
+    if (h == 0) {
+      float yt = -INFINITY;
+      for (int hh = 0; hh < kG; ++hh) yt = fmaxf(yt, ytop_h[row * kG + hh]);
+      s_ybase[j] = yt - kYRange;
+    }
+  }
+  // this lane's column: token 2*wave + (col >> 3), head col & 7
+  const int jloc = 2 * wave + (col >> 3);
+  int t = tb * kYTok + jloc;
+  const bool t_ok = t < T;
+  t = t_ok ? t : T - 1;
+  const int64_t P = pos0 + t;
+  const int64_t first = max(static_cast<int64_t>(0), P - w + 1);
+  const size_t row = (static_cast<size_t>(b) * T + t) * Hkv + g;
+  bf16x8 qop[4];
+  load_q_block(q + (static_cast<size_t>(b) * T + t) * Hq * kD + static_cast<size_t>(g) * kG * kD,
+               col, grp, qop);
+  const int t_last = min(T - 1, tb * kYTok + kYTok - 1);
+  const int64_t p_last = pos0 + t_last;
+  const int n_tiles = static_cast<int>((p_last + kPKeys) / kPKeys);
+  // this lane stores two of the 16 (subtile, i) values its half-wave shares
+  const int c8 = col & 7;
+  const int my_i = c8 & 3;
+  const int my_sub0 = 2 * (c8 >> 2);
+  float* yrow = y ? y + row * Spad : nullptr;
+  float* srow = scores ? scores + row * S : nullptr;
+
+  TileRegs regs;
+  tile_gload<false>(regs, kr, nullptr, 0, p_last);
+  tile_lstore<false>(regs, kt, nullptr);
+  __syncthreads();
+  const float ybase = s_ybase[jloc];
+  const float l2 = l2f[jloc][c8];
+  for (int it = 0; it < n_tiles; ++it) {
+    const int64_t key0 = static_cast<int64_t>(it) * kPKeys;
+    const bool more = it + 1 < n_tiles;
+    if (more) tile_gload<false>(regs, kr, nullptr, key0 + kPKeys, p_last);
+    f32x4 sacc[4];
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) {
+      sacc[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        sacc[sub] = mfma_16x16x32(lds_k_operand(kt, sub, c, col, grp), qop[c], sacc[sub]);
+    }
+    // y per (key, token): max over the token's 8 heads (lanes c8 = 0..7 of the
+    // half-wave); afterwards every lane of the half holds all 16 values
+    float yv[4][4];
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = sacc[sub][i];
+        float s = fmaf(a, c2_hi, a * c2_lo) - l2;
+        s = fmaxf(s, __shfl_xor(s, 1));
+        s = fmaxf(s, __shfl_xor(s, 2));
+        s = fmaxf(s, __shfl_xor(s, 4));
+        yv[sub][i] = s;
+      }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int sub = my_sub0 + u;
+      const float yy = sub == 0 ? yv[0][my_i] : sub == 1 ? yv[1][my_i] : sub == 2 ? yv[2][my_i] : yv[3][my_i];
+      const int64_t key = key0 + 16 * sub + 4 * grp + my_i;
+      if (!t_ok || key > P) continue;
+      if (srow) srow[key] = __builtin_amdgcn_exp2f(yy);
+      if (key < first) {
+        if (yrow) yrow[key] = yy;
+        if (want_hist) atomicAdd(&lh[jloc][key_from_log2(yy, ybase) >> kBinShift], 1u);
+      }
+    }
+    __syncthreads();
+    if (more) {
+      tile_lstore<false>(regs, kt, nullptr);
+      __syncthreads();
+    }
+  }
+  // scores past P_t are 0
+  if (scores) {
+    for (int j = 0; j < kYTok; ++j) {
+      const int tt = tb * kYTok + j;
+      if (tt >= T) break;
+      float* sr = scores + ((static_cast<size_t>(b) * T + tt) * Hkv + g) * S;
+      for (int64_t key = pos0 + tt + 1 + tid; key < S; key += kPThreads) sr[key] = 0.f;
+    }
+  }
+  if (want_hist) {
+    __syncthreads();
+    for (int i = tid; i < kYTok * kNB; i += kPThreads) {
+      const int j = i / kNB;
+      const int tt = tb * kYTok + j;
+      if (tt < T)
+        hist[((static_cast<size_t>(b) * T + tt) * Hkv + g) * kNB + (i % kNB)] = (&lh[0][0])[i];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_full_prefill(const Plan& p, const u16* q, const u16* k, const u16* v, u16* out,
+                               float* lse, void* ws, hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  const double c2 = p.scale * 1.4426950408889634;  // scale * log2(e)
+  const float c2_hi = static_cast<float>(c2);
+  const float c2_lo = static_cast<float>(c2 - static_cast<double>(c2_hi));
+  const int n_tblk = (p.T + kPTok - 1) / kPTok;
+  const int n_wg = p.B * p.Hkv * n_tblk;
+  hipLaunchKernelGGL(full_prefill_kernel, dim3(n_wg), dim3(kPThreads), 0, st, q, k, v, out, lse,
+                     reinterpret_cast<double*>(w + p.off_lse2),
+                     reinterpret_cast<float*>(w + p.off_ytop), p.S, p.T, p.Hkv, n_tblk, c2_hi,
+                     c2_lo);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_importance(const Plan& p, const u16* q, const u16* k, bool for_select,
+                                     float* scores, void* ws, hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  const double c2 = p.scale * 1.4426950408889634;
+  const float c2_hi = static_cast<float>(c2);
+  const float c2_lo = static_cast<float>(c2 - static_cast<double>(c2_hi));
+  const int n_tblk = (p.T + kYTok - 1) / kYTok;
+  const int n_wg = p.B * p.Hkv * n_tblk;
+  hipLaunchKernelGGL(prefill_importance_kernel, dim3(n_wg), dim3(kPThreads), 0, st, q, k,
+                     reinterpret_cast<const double*>(w + p.off_lse2),
+                     reinterpret_cast<const float*>(w + p.off_ytop),
+                     for_select ? reinterpret_cast<float*>(w + p.off_ybuf) : nullptr,
+                     for_select ? reinterpret_cast<uint32_t*>(w + p.off_hist) : nullptr, scores,
+                     p.S, p.Spad, p.T, p.Hkv, p.w, n_tblk, c2_hi, c2_lo);
+  return hipGetLastError();
+}
+
+}  // namespace hs2

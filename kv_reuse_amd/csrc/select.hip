@@ -52,12 +52,6 @@ __device__ __forceinline__ int64_t row_first(int P, int w) {
   return max(static_cast<int64_t>(0), static_cast<int64_t>(P) - w + 1);
 }
 
-__device__ __forceinline__ uint32_t key_from_log2(float y, float ybase) {
-  const float z = (y - ybase) * 67108864.0f;  // 2^32 / kYRange
-  if (!(z > 0.f)) return 0u;
-  if (z >= 4294967040.0f) return 0xFFFFFFFFu;
-  return static_cast<uint32_t>(z);
-}
 
 // Histogram bin of a candidate's exact log2 importance (monotone in y).
 __device__ __forceinline__ int cand_bin(double y, float ybase) {
@@ -1004,6 +998,190 @@ __global__ __launch_bounds__(kThreads) void emit_rank_kernel(
   }
 }
 
+// ================================================================ prefill chunk
+
+// One work-group per row (b, t, g) of a prefill chunk: the exact top-k of the
+// row's older keys from their float32 log2 importance y and the row's
+// complete histogram.  Bins above b*+1 are selected; keys in bins b*-1..b*+1
+// (the float32 error of y is far below a bin) get their importance recomputed
+// in float64 from exact bf16 products and are ranked (importance desc, index
+// asc).  A band larger than band_cap is ranked by its float32 y instead.
+__global__ __launch_bounds__(kRowThreads) void prefill_select_kernel(
+    const float* __restrict__ ybuf, const uint32_t* __restrict__ hist,
+    const float* __restrict__ ytop_h, const double* __restrict__ lse2, const u16* __restrict__ q,
+    const u16* __restrict__ k, int32_t* __restrict__ band_idx, uint64_t* __restrict__ band_key,
+    int64_t band_cap, int32_t* __restrict__ idx_out, int32_t* __restrict__ nsel_out, int64_t S,
+    int64_t Spad, int T, int Hkv, int topk, int w, int cap, double c2) {
+  __shared__ __align__(16) int32_t tmp[kMaxSel];
+  __shared__ __align__(16) uint32_t sel_lh[kMaxSel];   // histogram first, emit scratch last
+  __shared__ __align__(16) Cand cands[kUncCap];        // band (keys, indices), then sort scratch
+  __shared__ double qd[kG * kD];
+  __shared__ double l2s[kG];
+  __shared__ uint32_t h256[256];
+  __shared__ uint32_t s_count, s_tlo, s_need;
+  __shared__ uint64_t s_thi;
+  __shared__ int s_b, s_lo, s_hi;
+  __shared__ uint32_t s_nband;
+  __shared__ float s_ybase;
+  __shared__ uint32_t s_cnt[2][16];
+  __shared__ uint32_t s_base[4];
+  uint32_t* lh = sel_lh;
+  uint64_t* lband_k = reinterpret_cast<uint64_t*>(cands);
+  int32_t* lband_i = reinterpret_cast<int32_t*>(lband_k + kUncCap);
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int P = row_pos(r, T, Hkv, S);
+  const int64_t first = row_first(P, w);
+  int n_keep = 0;
+  if (topk > 0 && first > 0) {
+    for (int i = tid; i < kNB; i += kRowThreads) lh[i] = hist[static_cast<size_t>(r) * kNB + i];
+    if (tid == 0) s_ybase = row_ybase(ytop_h, r);
+    __syncthreads();
+    if (tid < 64) {
+      const KthBin kb = kth_bin_wave(lh, static_cast<uint32_t>(topk));
+      if (tid == 0) {
+        s_b = kb.found ? kb.bstar : -1;
+        if (kb.found) {
+          const int lo = max(0, kb.bstar - 1), hi = min(kNB - 1, kb.bstar + 1);
+          uint32_t nb = 0;
+          for (int bb = lo; bb <= hi; ++bb) nb += lh[bb];
+          s_lo = lo;
+          s_hi = hi;
+          s_nband = nb;
+        }
+      }
+    }
+    __syncthreads();
+    if (s_b < 0) {
+      // fewer older keys than top_k: all of them
+      n_keep = static_cast<int>(min(first, static_cast<int64_t>(kMaxSel)));
+      for (int i = tid; i < n_keep; i += kRowThreads) tmp[i] = i;
+    } else {
+      const int lo = s_lo, hi = s_hi;
+      const uint32_t n_band_h = s_nband;
+      const bool band_lds = n_band_h <= static_cast<uint32_t>(kUncCap);
+      const bool band_glob = !band_lds && n_band_h <= static_cast<uint64_t>(band_cap);
+      const float ybase = s_ybase;
+      const float* yr = ybuf + static_cast<size_t>(r) * Spad;
+      int32_t* gbi = band_idx + static_cast<size_t>(r) * band_cap;
+      uint64_t* gbk = band_key + static_cast<size_t>(r) * band_cap;
+      const u16* qr = q + static_cast<size_t>(r) * kG * kD;
+      for (int i = tid; i < kG * kD; i += kRowThreads) qd[i] = static_cast<double>(bf16_bits_to_f32(qr[i]));
+      if (tid < kG) l2s[tid] = lse2[static_cast<size_t>(r) * kG + tid];
+      // ---- one pass over y: above the band -> tmp, band -> band list
+      const int64_t rounds = (first + 16 * kRowThreads - 1) / (16 * kRowThreads);
+      uint32_t cu = 0, ca = 0;
+      for (int64_t rr = 0; rr < rounds; ++rr) {
+        const int64_t i0 = 16 * (static_cast<int64_t>(tid) + rr * kRowThreads);
+        float yv[16];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const f32x4 y4 = i0 + 4 * u < first ? *reinterpret_cast<const f32x4*>(yr + i0 + 4 * u)
+                                                : f32x4{0.f, 0.f, 0.f, 0.f};
+          yv[4 * u] = y4[0];
+          yv[4 * u + 1] = y4[1];
+          yv[4 * u + 2] = y4[2];
+          yv[4 * u + 3] = y4[3];
+        }
+        uint32_t mu = 0, ma = 0;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const bool valid = i0 + e < first;
+          const int bn = static_cast<int>(key_from_log2(yv[e], ybase) >> kBinShift);
+          mu |= static_cast<uint32_t>(valid && bn > hi) << e;
+          ma |= static_cast<uint32_t>(valid && bn >= lo && bn <= hi) << e;
+        }
+        uint32_t ou, oa;
+        reserve_two(__popc(mu), __popc(ma), nullptr, nullptr, s_cnt, s_base, ou, oa);
+        const uint32_t tu = s_base[2], ta = s_base[3];
+        ou += cu;
+        oa += ca;
+        cu += tu;
+        ca += ta;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int32_t j = static_cast<int32_t>(i0 + e);
+          if ((mu >> e) & 1u) {
+            if (ou < static_cast<uint32_t>(kMaxSel)) tmp[ou] = j;
+            ++ou;
+          } else if ((ma >> e) & 1u) {
+            if (band_lds) {
+              if (oa < static_cast<uint32_t>(kUncCap)) lband_i[oa] = j;
+            } else if (band_glob) {
+              if (oa < static_cast<uint64_t>(band_cap)) gbi[oa] = j;
+            }
+            ++oa;
+          }
+        }
+      }
+      __syncthreads();
+      const uint32_t n_up = min(cu, static_cast<uint32_t>(topk));
+      const uint32_t take = static_cast<uint32_t>(topk) - n_up;
+      if (tid == 0) s_count = n_up;
+      if (band_lds || band_glob) {
+        const uint32_t n_band = band_lds ? min(ca, static_cast<uint32_t>(kUncCap))
+                                         : static_cast<uint32_t>(min(static_cast<int64_t>(ca), band_cap));
+        // exact importance of the band keys in float64 (bf16 products are exact)
+        const int b = r / (T * Hkv);
+        const int g = r % Hkv;
+        const u16* kr = k + (static_cast<size_t>(b) * Hkv + g) * static_cast<size_t>(S) * kD;
+        for (uint32_t i = tid; i < n_band; i += kRowThreads) {
+          const int32_t j = band_lds ? lband_i[i] : gbi[i];
+          const u16* kj = kr + static_cast<size_t>(j) * kD;
+          u32x4 raw[16];
+#pragma unroll
+          for (int c = 0; c < 16; ++c) raw[c] = load_u32x4(kj + 8 * c);
+          double acc[kG];
+#pragma unroll
+          for (int h = 0; h < kG; ++h) acc[h] = 0.0;
+#pragma unroll
+          for (int c = 0; c < 16; ++c) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+              const uint32_t word = raw[c][t >> 1];
+              const double kv = static_cast<double>(
+                  __uint_as_float((t & 1) ? (word & 0xFFFF0000u) : (word << 16)));
+#pragma unroll
+              for (int h = 0; h < kG; ++h) acc[h] = fma(qd[h * kD + 8 * c + t], kv, acc[h]);
+            }
+            // keep the next chunk's LDS reads of the query from being hoisted
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          double yy = -INFINITY;
+#pragma unroll
+          for (int h = 0; h < kG; ++h) yy = fmax(yy, c2 * acc[h] - l2s[h]);
+          if (band_lds) lband_k[i] = ordered_u64(yy);
+          else gbk[i] = ordered_u64(yy);
+        }
+        __syncthreads();
+        take_best(band_lds ? lband_k : gbk, band_lds ? lband_i : gbi, n_band,
+                  min(take, n_band), cands, tmp, &s_count, h256, &s_thi, &s_tlo, &s_need);
+      } else {
+        // the band is too large to list: rank it by its float32 importance
+        __syncthreads();
+        struct ScanSrc {
+          const float* yr;
+          float ybase;
+          int lo, hi;
+          __device__ bool get(int64_t i, uint64_t& key, int32_t& j) const {
+            const float yy = yr[i];
+            const int bn = static_cast<int>(key_from_log2(yy, ybase) >> kBinShift);
+            if (bn < lo || bn > hi) return false;
+            key = static_cast<uint64_t>(ordered_u32(yy));
+            j = static_cast<int32_t>(i);
+            return true;
+          }
+        } src{yr, ybase, lo, hi};
+        radix_select_band(src, first, min(take, ca), tmp, &s_count, h256, &s_thi, &s_tlo, &s_need);
+      }
+      n_keep = static_cast<int>(min(s_count, static_cast<uint32_t>(topk)));
+    }
+  }
+  __syncthreads();
+  emit_row(tmp, reinterpret_cast<int32_t*>(sel_lh), n_keep, first, P,
+           idx_out + static_cast<size_t>(r) * cap, nsel_out + r, cap);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- launchers
@@ -1067,6 +1245,21 @@ hipError_t launch_fused_select(const Plan& p, const u16* q, const u16* k, int32_
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(emit_rank_kernel, dim3(kMaxSel / 64, p.R), dim3(kThreads), 0, st, info,
                      sel_list, idx, n_sel, p.S, p.T, p.Hkv, p.k, p.w, p.cap);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_select(const Plan& p, const u16* q, const u16* k, int32_t* idx,
+                                 int32_t* n_sel, void* ws, hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  const double c2 = p.scale * 1.4426950408889634;
+  hipLaunchKernelGGL(prefill_select_kernel, dim3(p.R), dim3(kRowThreads), 0, st,
+                     reinterpret_cast<const float*>(w + p.off_ybuf),
+                     reinterpret_cast<const uint32_t*>(w + p.off_hist),
+                     reinterpret_cast<const float*>(w + p.off_ytop),
+                     reinterpret_cast<const double*>(w + p.off_lse2), q, k,
+                     reinterpret_cast<int32_t*>(w + p.off_band_idx),
+                     reinterpret_cast<uint64_t*>(w + p.off_band_key), p.band_cap, idx, n_sel, p.S,
+                     p.Spad, p.T, p.Hkv, p.k, p.w, p.cap, c2);
   return hipGetLastError();
 }
 

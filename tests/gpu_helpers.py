@@ -92,11 +92,12 @@ def check_index_row(gi: np.ndarray, n: int, ref: dict, what: str, top_k: int, wi
     return len(sym)
 
 
-def compare_step(w: wl.Workload, x, res, check_scores=True):
-    """Compare a whole step's GPU results with the oracle; returns summary stats."""
+def compare_step(w: wl.Workload, x, res, check_scores=True, rows=None):
+    """Compare a whole step's GPU results with the oracle (on all rows, or on the
+    given (b, t, g) rows); returns summary stats."""
     ref = orc.cross_decoder_step(x["q_full"], x["k"], x["v"],
                                  x["q_sparse"] if w.n_sparse_layers else None,
-                                 top_k=w.top_k, window=w.window, scale=w.scale)
+                                 top_k=w.top_k, window=w.window, scale=w.scale, rows=rows)
     G = w.group
     stats = {"max_full": 0.0, "max_sparse": 0.0, "sym": 0}
     gpu_idx_oracle_sparse = []
@@ -122,6 +123,20 @@ def compare_step(w: wl.Workload, x, res, check_scores=True):
             gpu_idx_oracle_sparse.append((b, t, g))
     if w.n_sparse_layers and stats["sym"]:
         # the oracle's sparse layers on the GPU's own index lists
-        ref2 = orc.sparse_step(x["q_sparse"], x["k"], x["v"], res["idx"], res["n_sel"], scale=w.scale)
-        check_outputs(res["out_sparse"], ref2, "out_sparse on GPU indices")
+        if rows is None:
+            ref2 = orc.sparse_step(x["q_sparse"], x["k"], x["v"], res["idx"], res["n_sel"],
+                                   scale=w.scale)
+            check_outputs(res["out_sparse"], ref2, "out_sparse on GPU indices")
+        else:
+            for (b, t, g) in ref:
+                n = int(res["n_sel"][b, t, g])
+                sel = res["idx"][b, t, g, :n].astype(np.int64)
+                kk = orc.widen_bf16(x["k"][b, g])
+                vv = orc.widen_bf16(x["v"][b, g])
+                heads = slice(g * G, (g + 1) * G)
+                for n_l in range(w.n_sparse_layers):
+                    qn = orc.widen_bf16(x["q_sparse"][n_l, b, t, heads])
+                    check_outputs(res["out_sparse"][n_l, b, t, heads],
+                                  orc.sparse_attention_row(qn, kk, vv, sel, w.scale),
+                                  f"out_sparse[{n_l}]{(b, t, g)} on GPU indices")
     return stats
