@@ -22,11 +22,14 @@ import re
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "query tokens/s, full+sparse Cross-Decoder attn at 1M ctx; HBM TB/s vs peak"
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "full_decode_split_decode_1m_pmc.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "kv_reuse_amd", "csrc", f)
@@ -67,13 +70,26 @@ def algorithmic_full_layer_bytes(w) -> int:
     return kv + qo + 4 * rows * w.ctx_len
 
 
+def algorithmic_full_layer_flops(w) -> int:
+    """Causal attention: every query head attends to keys 0..P_t, 2*D flops for
+    the logit and 2*D for the value sum per key."""
+    pos = w.ctx_len - w.n_q_tokens + np.arange(w.n_q_tokens, dtype=np.int64)
+    return int(w.batch * w.n_q_heads * 4 * w.head_dim * int((pos + 1).sum()))
+
+
 def cpu_baseline(w, x, budget_s: float = 20.0):
-    """Time the CPU oracle (as it stands) on whole (batch, KV head) rows of the
-    same inputs until the budget is used; scale to query tokens per second."""
-    import numpy as np  # noqa: F401
+    """Time the CPU oracle (as it stands) on whole (batch, query token, KV head)
+    rows of the same inputs until the budget is used; scale to query tokens per
+    second."""
     from threadpoolctl import threadpool_info
     import oracle.hs2_oracle as orc
-    rows = [(b, 0, g) for b in range(w.batch) for g in range(w.n_kv_heads)]
+    rows = [(b, t, g) for t in range(w.n_q_tokens) for b in range(w.batch)
+            for g in range(w.n_kv_heads)]
+    if w.n_q_tokens > 1:
+        # a spread of query tokens across the chunk (all KV heads of each)
+        stride = max(1, w.n_q_tokens // 64)
+        rows = [(b, t, g) for t in range(0, w.n_q_tokens, stride) for b in range(w.batch)
+                for g in range(w.n_kv_heads)]
     done = 0
     t0 = time.perf_counter()
     for r in rows:
@@ -87,7 +103,7 @@ def cpu_baseline(w, x, budget_s: float = 20.0):
     threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
     return {"value": tokens / dt, "unit": "query tokens/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{done} of {len(rows)} (batch, KV head) rows of {w.name}: full float64 "
+            "sample": f"{done} (batch, query token, KV head) rows of {w.name}: full float64 "
                       f"attention over all {w.ctx_len} keys, group-max importance, full sort, "
                       f"{w.n_sparse_layers} sparse layers; {dt:.2f} s"}
 
@@ -108,7 +124,6 @@ def main():
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
     from kv_reuse_amd import hs2
     from kv_reuse_amd import workloads as wl
@@ -127,9 +142,6 @@ def main():
         log(f"[bench] calibration copy: {n} bytes read + {n} bytes written, 3 launches")
         del src, dst
     w = wl.WORKLOADS[args.workload]
-    if w.n_q_tokens != 1:
-        print("bench.py times the decode workloads", file=sys.stderr)
-        sys.exit(1)
     log(f"[bench] generating {w.name}")
     x = wl.generate(w)
     s = hs2.shape_of(w)
@@ -172,9 +184,21 @@ def main():
     phases = hs2.cross_decoder_step_timed(s, q, qs, k, v, out, outs, idx, nsel, ws,
                                           max(args.steps, 10))
     full_ms = phases[0]
-    algo = algorithmic_full_layer_bytes(w)
-    achieved = algo / (full_ms * 1e-3) / 1e9
-    traffic = measured_traffic(w.name)
+    if w.n_q_tokens == 1:
+        algo = algorithmic_full_layer_bytes(w)
+        achieved = algo / (full_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": measured_traffic(w.name), "kernel": "full_decode_split_kernel",
+                    "algorithmic_bytes": algo, "kernel_ms": round(full_ms, 5)}
+    else:
+        flops = algorithmic_full_layer_flops(w)
+        achieved = flops / (full_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1),
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                    "kernel": "full_prefill_kernel", "algorithmic_flops": flops,
+                    "kernel_ms": round(full_ms, 5)}
 
     rec = {
         "metric": METRIC,
@@ -192,10 +216,7 @@ def main():
         "config": {"workload": w.name, "batch": B, "n_q_tokens": T, "ctx_len": S,
                    "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": D, "top_k": w.top_k,
                    "window": w.window, "n_sparse_layers": L},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "full_decode_split_kernel",
-                     "algorithmic_bytes": algo, "kernel_ms": round(full_ms, 5)},
+        "roofline": roofline,
         "phases_ms": {"full_split": round(phases[0], 5), "full_combine": round(phases[1], 5),
                       "select": round(phases[2], 5), "sparse": round(phases[3], 5)},
         "wall_s_timed": round(wall, 4),

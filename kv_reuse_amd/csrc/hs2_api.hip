@@ -73,11 +73,18 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
   // fused selection: subtiles of 16 keys, ~256 work-groups, <= 8192 per group
   const int64_t nst = q.Spad / 16;
   {
-    int64_t chunk = align_up(static_cast<size_t>(ceil_div(nst * R, 1024)), 256);
-    chunk = std::max<int64_t>(chunk, 256);
-    chunk = std::min<int64_t>(chunk, 8192);
-    q.st_chunk = static_cast<int>(chunk);
-    q.st_nchunk = static_cast<int>(ceil_div(nst, chunk));
+    // bound histogram: about 256 work-groups
+    int64_t hc = align_up(static_cast<size_t>(ceil_div(nst * R, 256)), 256);
+    hc = std::min<int64_t>(std::max<int64_t>(hc, 256), 8192);
+    q.hs_chunk = static_cast<int>(hc);
+    q.hs_nchunk = static_cast<int>(ceil_div(nst, hc));
+    // candidate scoring: about 512 work-groups (all resident at once), whole
+    // rounds of kScoreRound subtiles, at most kMaxChunks chunks per row
+    int64_t sc = align_up(static_cast<size_t>(ceil_div(nst * R, 512)), kScoreRound);
+    sc = std::max<int64_t>(sc, kScoreRound);
+    sc = std::max<int64_t>(sc, static_cast<int64_t>(align_up(static_cast<size_t>(ceil_div(nst, kMaxChunks)), kScoreRound)));
+    q.sc_chunk = static_cast<int>(sc);
+    q.sc_nchunk = static_cast<int>(ceil_div(nst, sc));
   }
   // sparse: slices of 128 keys over work-groups when rows are few
   q.sp_nch = (R >= 256) ? 1 : static_cast<int>(ceil_div(q.cap, 128));
@@ -107,17 +114,17 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
   q.off_cert = take(Rz * align_up(static_cast<size_t>(q.k), 64) * sizeof(int32_t));
   q.off_unc = take(Rz * kUncCap * sizeof(int32_t));
   q.off_unck = take(Rz * kUncCap * sizeof(uint64_t));
-  const size_t fz = decode ? Rz * q.Spad : 0;
   q.off_hist_c = take(decode ? Rz * kNB * sizeof(uint32_t) : 0);
-  q.off_cand_y = take(fz * sizeof(double));
-  q.off_cand_idx = take(fz * sizeof(int32_t));
+  const size_t cz = decode ? Rz * static_cast<size_t>(q.sc_nchunk) * q.sc_chunk * 16 : 0;
+  q.off_cand_y = take(cz * sizeof(double));
+  q.off_cand_idx = take(cz * sizeof(int32_t));
+  q.off_cand_cnt = take(decode ? Rz * q.sc_nchunk * sizeof(uint32_t) : 0);
   // band lists: a whole row's worth in decode; in a prefill chunk (many rows)
   // a bounded list per row
-  q.band_cap = decode ? q.Spad : std::min<int64_t>(q.Spad, kPrefillBandCap);
+  q.band_cap = decode ? 0 : std::min<int64_t>(q.Spad, kPrefillBandCap);
   q.off_band_idx = take(Rz * q.band_cap * sizeof(int32_t));
   q.off_band_key = take(Rz * q.band_cap * sizeof(uint64_t));
   q.off_ybuf = take(decode ? 0 : Rz * q.Spad * sizeof(float));
-  q.off_sel_list = take(decode ? Rz * kMaxSel * sizeof(int32_t) : 0);
   const size_t sp_parts = q.sp_nch > 1 ? Rz * q.sp_nch * n_layers * kG : 0;
   q.off_sp_m = take(sp_parts * sizeof(float));
   q.off_sp_l = take(sp_parts * sizeof(float));

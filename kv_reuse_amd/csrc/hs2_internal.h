@@ -33,7 +33,8 @@ struct RowInfo {
   uint32_t up_count;    // entries above the band appended to the selection
   uint32_t pad;
 };
-constexpr int kBandRankMax = 4096;  // bands up to this size are ranked in parallel
+constexpr int kScoreRound = 256;   // subtiles scored per round of a work-group
+constexpr int kMaxChunks = 4096;   // candidate chunks per row
 constexpr int64_t kPrefillBandCap = 8192;  // near-threshold keys listed per prefill row
 
 // Where each piece of the workspace sits, for one shape.
@@ -54,8 +55,9 @@ struct Plan {
   int sel_chunk, sel_nchunk;
   size_t off_ukey, off_cert, off_unc, off_unck;
   // fused selection from the subtile maxima
-  int st_chunk, st_nchunk;
-  size_t off_hist_c, off_cand_y, off_cand_idx, off_band_idx, off_band_key, off_sel_list;
+  int hs_chunk, hs_nchunk;   // subtiles per work-group: bound histogram
+  int sc_chunk, sc_nchunk;   // subtiles per work-group: candidate scoring (<= kMaxChunks per row)
+  size_t off_hist_c, off_cand_y, off_cand_idx, off_cand_cnt, off_band_idx, off_band_key;
   // prefill chunk: per-row log2 importance of the older keys, band capacity per row
   size_t off_ybuf;
   int64_t band_cap;

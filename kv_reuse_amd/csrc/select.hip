@@ -41,7 +41,6 @@ constexpr int kThreads = 256;
 constexpr int kHistThreads = 512;
 constexpr int kRowThreads = 512;
 constexpr int kSubKeys = 16;        // keys per subtile (the full kernel's maxima)
-constexpr int kMaxSubChunk = 8192;  // subtiles per work-group (32 per thread)
 
 __device__ __forceinline__ int row_pos(int r, int T, int Hkv, int64_t S) {
   const int t = (r / Hkv) % T;
@@ -71,6 +70,7 @@ struct KthBin {
 };
 __device__ KthBin kth_bin_wave(const uint32_t* lh, uint32_t k) {
   const int lane = threadIdx.x & 63;
+  // level 1: lane l sums the 32 bins kNB-1-32l .. kNB-32-32l
   uint32_t lane_sum = 0;
   for (int i = 0; i < 32; ++i) lane_sum += lh[kNB - 1 - 32 * lane - i];
   uint32_t incl = lane_sum;
@@ -83,21 +83,21 @@ __device__ KthBin kth_bin_wave(const uint32_t* lh, uint32_t k) {
   const uint64_t hit = __ballot(incl >= k);
   if (!hit) return res;
   const int owner = __builtin_ctzll(hit);
-  int bs = 0;
-  uint32_t above = 0, at = 0;
-  if (lane == owner) {
-    above = incl - lane_sum;
-    bs = kNB - 1 - 32 * lane;
-    const int bs_end = bs - 31;
-    for (;; --bs) {
-      at = lh[bs];
-      if (above + at >= k || bs == bs_end) break;
-      above += at;
-    }
+  const uint32_t above0 = __shfl(incl - lane_sum, owner);
+  // level 2: lanes 0..31 take the owner's 32 bins from the top
+  const int bin = kNB - 1 - 32 * owner - (lane & 31);
+  const uint32_t c = lane < 32 ? lh[bin] : 0u;
+  uint32_t inc2 = c;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = __shfl_up(inc2, off);
+    if (lane >= off) inc2 += o;
   }
-  res.bstar = __shfl(bs, owner);
-  res.above = __shfl(above, owner);
-  res.at = __shfl(at, owner);
+  const uint64_t hit2 = __ballot(lane < 32 && above0 + inc2 >= k);
+  const int jj = __builtin_ctzll(hit2);   // the owner's group reaches k, so some lane hits
+  res.bstar = kNB - 1 - 32 * owner - jj;
+  res.above = above0 + __shfl(inc2 - c, jj);
+  res.at = __shfl(c, jj);
   res.found = true;
   return res;
 }
@@ -606,17 +606,29 @@ __global__ __launch_bounds__(kThreads) void subtile_hist_kernel(
   flush_hist(lh, hist + static_cast<size_t>(r) * kNB, static_cast<uint32_t>(topk), &s_lo);
 }
 
-// Candidate subtiles, then their keys' importances in float64 on MFMA (one wave
-// per candidate subtile), appended to the row's candidate list, and their
-// histogram added to the row's candidate histogram hist_c.
+// Candidate subtiles, then their keys' exact importance, in rounds of
+// kScoreRound subtiles:
+//  * a subtile is a candidate when its bound's bin is at least (k-th bound bin
+//    - 1): every key that can be selected lies in one;
+//  * a wave takes a candidate subtile and computes its 16 keys' importance in
+//    float64 on MFMA (D = K . Q^T, 16 keys x 16 heads of which 8 are used; the
+//    bf16 products are exact in float64), staged in LDS;
+//  * keys whose bin is below that same bound can never be selected and are
+//    dropped; the others are appended to the work-group's own region of the
+//    row's candidate list in ascending key order, and counted in the row's
+//    candidate histogram.  The region's length goes to cand_cnt.
+// The loads that do not depend on each other (histogram, first bounds, query
+// row) are issued together at the start.
 __global__ __launch_bounds__(kThreads) void subtile_score_kernel(
     const float* __restrict__ stmax, const double* __restrict__ lse2,
     const float* __restrict__ ytop_h, const uint32_t* __restrict__ hist,
-    uint32_t* __restrict__ hist_c, RowInfo* __restrict__ info, const u16* __restrict__ q,
-    const u16* __restrict__ k, double* __restrict__ cand_y, int32_t* __restrict__ cand_idx,
-    int64_t S, int64_t Spad, int T, int Hkv, int topk, int w, int chunk, double c2) {
+    uint32_t* __restrict__ hist_c, const u16* __restrict__ q, const u16* __restrict__ k,
+    double* __restrict__ cand_y, int32_t* __restrict__ cand_idx, uint32_t* __restrict__ cand_cnt,
+    int64_t S, int64_t Spad, int T, int Hkv, int topk, int w, int chunk, int n_chunks,
+    double c2) {
   __shared__ uint32_t lh[kNB];
-  __shared__ int32_t s_list[kMaxSubChunk];
+  __shared__ int32_t s_list[kScoreRound];
+  __shared__ double stage_y[kScoreRound * kSubKeys];
   __shared__ float lse2f[kG];
   __shared__ float s_ybase;
   __shared__ int s_lo;
@@ -625,18 +637,42 @@ __global__ __launch_bounds__(kThreads) void subtile_score_kernel(
   const int r = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
   const int64_t first = row_first(row_pos(r, T, Hkv, S), w);
-  if (topk <= 0 || first == 0) return;
   const int64_t n_counted = first / kSubKeys;
   const int64_t n_sub = (first + kSubKeys - 1) / kSubKeys;
   const int64_t st0 = static_cast<int64_t>(blockIdx.x) * chunk;
   const int64_t st1 = min(n_sub, st0 + chunk);
-  if (st0 >= st1) return;
+  uint32_t* cnt = cand_cnt + static_cast<size_t>(r) * n_chunks + blockIdx.x;
+  if (topk <= 0 || first == 0 || st0 >= st1) {
+    if (tid == 0) *cnt = 0u;
+    return;
+  }
   const bool all_mode = n_counted <= topk;
+  const float* stmax_row = stmax + static_cast<size_t>(r) * (Spad / kSubKeys) * kG;
+  // ---- the first loads, together: histogram, the first round's maxima, query
+  uint32_t hv[kNB / kThreads];
+#pragma unroll
+  for (int u = 0; u < kNB / kThreads; ++u)
+    hv[u] = all_mode ? 0u : hist[static_cast<size_t>(r) * kNB + tid + kThreads * u];
+  f32x4 mx[2];
+  {
+    const int64_t st = st0 + tid;
+    const bool ld = !all_mode && st < min(st1, n_counted);
+    mx[0] = ld ? *reinterpret_cast<const f32x4*>(stmax_row + st * kG) : f32x4{0.f, 0.f, 0.f, 0.f};
+    mx[1] = ld ? *reinterpret_cast<const f32x4*>(stmax_row + st * kG + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  u32x4 qraw[4];
+  {
+    const u16* qr = q + static_cast<size_t>(r) * kG * kD + (col & 7) * kD + 32 * grp;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qraw[c] = load_u32x4(qr + 8 * c);
+  }
+  const double l2 = col < kG ? lse2[static_cast<size_t>(r) * kG + col] : 0.0;
   if (tid < kG) lse2f[tid] = static_cast<float>(lse2[static_cast<size_t>(r) * kG + tid]);
   if (tid == 0) s_ybase = row_ybase(ytop_h, r);
-  if (!all_mode)
-    for (int i = tid; i < kNB; i += kThreads) lh[i] = hist[static_cast<size_t>(r) * kNB + i];
+#pragma unroll
+  for (int u = 0; u < kNB / kThreads; ++u) lh[tid + kThreads * u] = hv[u];
   __syncthreads();
   if (!all_mode && tid < 64) {
     const KthBin kb = kth_bin_wave(lh, static_cast<uint32_t>(topk));
@@ -645,357 +681,464 @@ __global__ __launch_bounds__(kThreads) void subtile_score_kernel(
   __syncthreads();
   const int lo_bin = all_mode ? 0 : s_lo;
   const float ybase = s_ybase;
-  const float* stmax_row = stmax + static_cast<size_t>(r) * (Spad / kSubKeys) * kG;
-  // ---- phase 1: which subtiles of the chunk are candidates
-  uint32_t mine = 0;
-  for (int i0 = 0; i0 < kMaxSubChunk / kThreads; i0 += 4) {
-    if (st0 + tid + static_cast<int64_t>(kThreads) * i0 >= st1) break;
-    float ub[4];
+  float l2v[kG];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t st = st0 + tid + static_cast<int64_t>(kThreads) * (i0 + u);
-      ub[u] = (st < min(st1, n_counted) && !all_mode) ? subtile_ub(stmax_row, st, lse2f) : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t st = st0 + tid + static_cast<int64_t>(kThreads) * (i0 + u);
-      if (st >= st1) continue;
-      const bool cand = all_mode || st >= n_counted ||
-                        static_cast<int>(key_from_log2(ub[u], ybase) >> kBinShift) >= lo_bin;
-      if (cand) mine |= 1u << (i0 + u);
-    }
-  }
-  uint32_t o_list, o_dummy;
-  reserve_two(__popc(mine), 0u, nullptr, nullptr, s_cnt, s_base, o_list, o_dummy);
-  const uint32_t n_local = s_base[2];
-  for (uint32_t m = mine; m; m &= m - 1)
-    s_list[o_list++] = static_cast<int32_t>(st0 + tid + kThreads * __builtin_ctz(m));
-  __syncthreads();
-  if (tid == 0)
-    s_base[1] = n_local ? atomicAdd(&info[r].cert_count, n_local * kSubKeys) : 0u;
-  __syncthreads();
-  const uint32_t base = s_base[1];
-  // ---- phase 2: float64 importances of the candidates' keys on MFMA.  A
-  // wave takes a subtile: D = K . Q^T over 16 keys x 16 (8 used) heads, the
-  // contraction split as dim = 32*(lane/16) + step, 32 steps of 4 dims.  The
-  // bf16 products are exact in float64.
-  for (int i = tid; i < kNB; i += kThreads) lh[i] = 0u;
-  const int col = lane & 15, grp = lane >> 4;
+  for (int h = 0; h < kG; ++h) l2v[h] = lse2f[h];
+  for (int i = tid; i < kNB; i += kThreads) lh[i] = 0u;   // now the candidate histogram
   double qd[32];
-  {
-    const u16* qr = q + static_cast<size_t>(r) * kG * kD + col * kD + 32 * grp;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const u32x4 w4 = col < kG ? load_u32x4(qr + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+  for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const uint32_t word = w4[t >> 1];
-        qd[8 * c + t] = static_cast<double>(
-            __uint_as_float((t & 1) ? (word & 0xFFFF0000u) : (word << 16)));
-      }
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t word = qraw[c][t >> 1];
+      const double qv = static_cast<double>(
+          __uint_as_float((t & 1) ? (word & 0xFFFF0000u) : (word << 16)));
+      qd[8 * c + t] = col < kG ? qv : 0.0;
     }
-  }
-  const double l2 = col < kG ? lse2[static_cast<size_t>(r) * kG + col] : 0.0;
-  __syncthreads();
   const int b = r / (T * Hkv);
   const int g = r % Hkv;
   const u16* kr = k + (static_cast<size_t>(b) * Hkv + g) * static_cast<size_t>(S) * kD;
-  double* cy = cand_y + static_cast<size_t>(r) * Spad;
-  int32_t* ci = cand_idx + static_cast<size_t>(r) * Spad;
-  auto load_sub = [&](uint32_t i, u32x4 (&ka)[4]) {
-    int64_t key = static_cast<int64_t>(s_list[i]) * kSubKeys + col;
-    key = key < S - 1 ? key : S - 1;
+  const size_t region = (static_cast<size_t>(r) * n_chunks + blockIdx.x) * static_cast<size_t>(chunk) * kSubKeys;
+  double* cy = cand_y + region;
+  int32_t* ci = cand_idx + region;
+  uint32_t written = 0;
+  for (int64_t sr0 = st0; sr0 < st1; sr0 += kScoreRound) {
+    // ---- which subtiles of the round are candidates (thread t: subtile sr0 + t)
+    const int64_t st = sr0 + tid;
+    if (sr0 != st0) {
+      const bool ld = !all_mode && st < min(st1, n_counted);
+      mx[0] = ld ? *reinterpret_cast<const f32x4*>(stmax_row + st * kG) : f32x4{0.f, 0.f, 0.f, 0.f};
+      mx[1] = ld ? *reinterpret_cast<const f32x4*>(stmax_row + st * kG + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    bool cand = false;
+    if (st < st1) {
+      float ub = mx[0][0] - l2v[0];
+      ub = fmaxf(ub, mx[0][1] - l2v[1]);
+      ub = fmaxf(ub, mx[0][2] - l2v[2]);
+      ub = fmaxf(ub, mx[0][3] - l2v[3]);
+      ub = fmaxf(ub, mx[1][0] - l2v[4]);
+      ub = fmaxf(ub, mx[1][1] - l2v[5]);
+      ub = fmaxf(ub, mx[1][2] - l2v[6]);
+      ub = fmaxf(ub, mx[1][3] - l2v[7]);
+      cand = all_mode || st >= n_counted ||
+             static_cast<int>(key_from_log2(ub, ybase) >> kBinShift) >= lo_bin;
+    }
+    uint32_t o_list, o_dummy;
+    reserve_two(cand ? 1u : 0u, 0u, nullptr, nullptr, s_cnt, s_base, o_list, o_dummy);
+    const uint32_t n_local = s_base[2];
+    if (cand) s_list[o_list] = static_cast<int32_t>(st);   // ascending: slots follow thread order
+    __syncthreads();
+    // ---- float64 importance of the candidates' keys, one subtile per wave
+    auto load_sub = [&](uint32_t i, u32x4 (&ka)[4]) {
+      int64_t key = static_cast<int64_t>(s_list[i]) * kSubKeys + col;
+      key = key < S - 1 ? key : S - 1;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) ka[c] = load_u32x4(kr + key * kD + 32 * grp + 8 * c);
-  };
-  u32x4 ka_cur[4], ka_nxt[4];
-  if (static_cast<uint32_t>(wave) < n_local) load_sub(wave, ka_cur);
-  for (uint32_t i = wave; i < n_local; i += kThreads / 64) {
-    const int64_t key0 = static_cast<int64_t>(s_list[i]) * kSubKeys;
-    if (i + kThreads / 64 < n_local) load_sub(i + kThreads / 64, ka_nxt);
-    // four independent accumulation chains (one per 8-dim slice of the lane's
-    // 32 dims), summed at the end
-    f64x4 part[4];
+      for (int c = 0; c < 4; ++c) ka[c] = load_u32x4(kr + key * kD + 32 * grp + 8 * c);
+    };
+    u32x4 ka_cur[4], ka_nxt[4];
+    if (static_cast<uint32_t>(wave) < n_local) load_sub(wave, ka_cur);
+    for (uint32_t i = wave; i < n_local; i += kThreads / 64) {
+      if (i + kThreads / 64 < n_local) load_sub(i + kThreads / 64, ka_nxt);
+      // four independent accumulation chains (one per 8-dim slice of the
+      // lane's 32 dims), summed at the end
+      f64x4 part[4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) part[c] = f64x4{0.0, 0.0, 0.0, 0.0};
+      for (int c = 0; c < 4; ++c) part[c] = f64x4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+      for (int t = 0; t < 8; ++t) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t word = ka_cur[c][t >> 1];
-        const double kv = static_cast<double>(
-            __uint_as_float((t & 1) ? (word & 0xFFFF0000u) : (word << 16)));
-        part[c] = __builtin_amdgcn_mfma_f64_16x16x4f64(kv, qd[8 * c + t], part[c], 0, 0, 0);
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t word = ka_cur[c][t >> 1];
+          const double kv = static_cast<double>(
+              __uint_as_float((t & 1) ? (word & 0xFFFF0000u) : (word << 16)));
+          part[c] = __builtin_amdgcn_mfma_f64_16x16x4f64(kv, qd[8 * c + t], part[c], 0, 0, 0);
+        }
+      }
+      const f64x4 acc = (part[0] + part[1]) + (part[2] + part[3]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) ka_cur[c] = ka_nxt[c];
+      // register e holds key grp + 4e against head col
+      double y[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        double v = col < kG ? c2 * acc[e] - l2 : -INFINITY;
+        v = fmax(v, __shfl_xor(v, 1));
+        v = fmax(v, __shfl_xor(v, 2));
+        v = fmax(v, __shfl_xor(v, 4));
+        y[e] = v;
+      }
+      if (col < 4)
+        stage_y[i * kSubKeys + grp + 4 * col] =
+            col == 0 ? y[0] : col == 1 ? y[1] : col == 2 ? y[2] : y[3];
+    }
+    __syncthreads();
+    // ---- keep the keys that can still be selected, in order (thread t: the
+    // 16 keys of the round's t-th candidate subtile)
+    uint32_t keep = 0;
+    int64_t key0 = 0;
+    if (static_cast<uint32_t>(tid) < n_local) {
+      key0 = static_cast<int64_t>(s_list[tid]) * kSubKeys;
+#pragma unroll
+      for (int e = 0; e < kSubKeys; ++e) {
+        const double yy = stage_y[tid * kSubKeys + e];
+        const bool ok = key0 + e < first && cand_bin(yy, ybase) >= lo_bin;
+        keep |= static_cast<uint32_t>(ok) << e;
       }
     }
-    const f64x4 acc = (part[0] + part[1]) + (part[2] + part[3]);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) ka_cur[c] = ka_nxt[c];
-    // register e holds key grp + 4e against head col
-    double y[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      double v = col < kG ? c2 * acc[e] - l2 : -INFINITY;
-      v = fmax(v, __shfl_xor(v, 1));
-      v = fmax(v, __shfl_xor(v, 2));
-      v = fmax(v, __shfl_xor(v, 4));
-      y[e] = v;
+    uint32_t o_keep;
+    reserve_two(__popc(keep), 0u, nullptr, nullptr, s_cnt, s_base, o_keep, o_dummy);
+    o_keep += written;
+    written += s_base[2];
+    for (uint32_t m = keep; m; m &= m - 1) {
+      const int e = __builtin_ctz(m);
+      const double yy = stage_y[tid * kSubKeys + e];
+      cy[o_keep] = yy;
+      ci[o_keep] = static_cast<int32_t>(key0 + e);
+      atomicAdd(&lh[cand_bin(yy, ybase)], 1u);
+      ++o_keep;
     }
-    if (col < 4) {
-      const double ye = col == 0 ? y[0] : col == 1 ? y[1] : col == 2 ? y[2] : y[3];
-      const int kk = grp + 4 * col;
-      const int64_t j = key0 + kk;
-      const bool ok = j < first;
-      const size_t pos = base + static_cast<size_t>(i) * kSubKeys + kk;
-      cy[pos] = ok ? ye : -INFINITY;
-      ci[pos] = ok ? static_cast<int32_t>(j) : -1;
-      if (ok) atomicAdd(&lh[cand_bin(ye, ybase)], 1u);
-    }
+    __syncthreads();   // s_list and stage_y are reused by the next round
   }
-  __syncthreads();
-  flush_hist(lh, hist_c + static_cast<size_t>(r) * kNB, static_cast<uint32_t>(topk), &s_lo);
+  for (int i = tid; i < kNB; i += kThreads)
+    if (lh[i]) atomicAdd(&hist_c[static_cast<size_t>(r) * kNB + i], lh[i]);
+  if (tid == 0) *cnt = written;
 }
 
-// ---- the row's exact top-k from its candidate list, over many work-groups:
-// split (above the k-th bin: selected; the k-th bin: band), rank the band,
-// rank the selection by index.
+__device__ __forceinline__ uint32_t wave_and(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v &= __shfl_xor(v, off);
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v |= __shfl_xor(v, off);
+  return v;
+}
 
-constexpr int kSplitPerWG = 16 * kThreads;  // list entries per work-group round
-constexpr int kSplitMaxWG = 32;             // work-groups per row (grid-stride)
+// ---- the row's exact top-k from its candidate list, one work-group per row.
+//
+// The list holds, in ascending key index, every key that can be selected with
+// its exact importance.  Bins above the k-th bin b* of the row's candidate
+// histogram are selected.  In b* (the band) a radix select over the 64-bit
+// importance finds the threshold T: entries above T are selected, and of the
+// entries equal to T the first ones in list order (the lowest indices) make up
+// the count.  One more pass writes the selected indices in list order, i.e.
+// ascending.  Each thread owns kPerThr consecutive list entries per sweep of
+// the list; the first sweep stays in registers.
 
-// Entries in bins above the k-th bin b* of the row's candidate histogram are
-// appended to the selection list, entries in b* to the band list.  When the
-// histogram holds fewer than k entries every candidate is selected.
-__global__ __launch_bounds__(kThreads) void cand_split_kernel(
-    RowInfo* __restrict__ info, const uint32_t* __restrict__ hist_c,
-    const double* __restrict__ cand_y, const int32_t* __restrict__ cand_idx,
-    const float* __restrict__ ytop_h, int32_t* __restrict__ sel_list,
-    int32_t* __restrict__ band_idx, uint64_t* __restrict__ band_key, int64_t S, int64_t Spad,
-    int T, int Hkv, int topk, int w) {
+constexpr int kSelThreads = 1024;
+constexpr int kPerThr = 8;
+constexpr int kSweep = kSelThreads * kPerThr;
+
+struct SelEntry {
+  double y[kPerThr];
+  int32_t j[kPerThr];
+  int n;   // entries held (0..kPerThr)
+};
+
+// Load list positions [p0, p0 + kPerThr) ∩ [0, n_total) into e.
+__device__ __forceinline__ void load_entries(SelEntry& e, const double* __restrict__ cy,
+                                             const int32_t* __restrict__ ci, const uint32_t* pre,
+                                             int n_chunks, size_t chunk_len, uint32_t p0,
+                                             uint32_t n_total) {
+  e.n = p0 < n_total ? static_cast<int>(min(static_cast<uint32_t>(kPerThr), n_total - p0)) : 0;
+  size_t at[kPerThr];
+  if (e.n > 0) {
+    int lo = 0, hi = n_chunks - 1;   // the chunk of p0: the largest c with pre[c] <= p0
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre[mid] <= p0) lo = mid;
+      else hi = mid - 1;
+    }
+    int c = lo;
+    uint32_t o = p0 - pre[c];
+#pragma unroll
+    for (int u = 0; u < kPerThr; ++u) {
+      if (u < e.n) {
+        while (o >= pre[c + 1] - pre[c]) {
+          ++c;
+          o = 0;
+        }
+        at[u] = static_cast<size_t>(c) * chunk_len + o;
+        ++o;
+      } else {
+        at[u] = u > 0 ? at[0] : 0;
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kPerThr; ++u) {
+    e.y[u] = u < e.n ? cy[at[u]] : -INFINITY;
+    e.j[u] = u < e.n ? ci[at[u]] : -1;
+  }
+}
+
+__global__ __launch_bounds__(kSelThreads) void row_select_kernel(
+    const uint32_t* __restrict__ hist_c, const double* __restrict__ cand_y,
+    const int32_t* __restrict__ cand_idx, const uint32_t* __restrict__ cand_cnt,
+    const float* __restrict__ ytop_h, int32_t* __restrict__ idx_out,
+    int32_t* __restrict__ nsel_out, int64_t S, int T, int Hkv, int topk, int w, int cap,
+    int chunk, int n_chunks) {
   __shared__ uint32_t lh[kNB];
+  __shared__ uint32_t pre[kMaxChunks + 1];
+  __shared__ uint32_t h256[256];
+  __shared__ uint32_t s_red[4];
+  __shared__ uint64_t s_hi;
+  __shared__ uint32_t s_need;
+  __shared__ int s_done;
   __shared__ int s_b;
+  __shared__ uint32_t s_above, s_at;
   __shared__ float s_ybase;
   __shared__ uint32_t s_cnt[2][16];
   __shared__ uint32_t s_base[4];
-  const int r = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int64_t first = row_first(row_pos(r, T, Hkv, S), w);
-  if (topk <= 0 || first == 0) return;
-  const int64_t n_list = min(static_cast<int64_t>(info[r].cert_count), Spad);
-  if (static_cast<int64_t>(blockIdx.x) * kSplitPerWG >= n_list) return;
-  for (int i = tid; i < kNB; i += kThreads) lh[i] = hist_c[static_cast<size_t>(r) * kNB + i];
-  if (tid == 0) s_ybase = row_ybase(ytop_h, r);
-  __syncthreads();
-  if (tid < 64) {
-    const KthBin kb = kth_bin_wave(lh, static_cast<uint32_t>(topk));
-    if (tid == 0) s_b = kb.found ? kb.bstar : -1;
-  }
-  __syncthreads();
-  const int bstar = s_b;
-  const float ybase = s_ybase;
-  const double* cy = cand_y + static_cast<size_t>(r) * Spad;
-  const int32_t* ci = cand_idx + static_cast<size_t>(r) * Spad;
-  int32_t* sl = sel_list + static_cast<size_t>(r) * kMaxSel;
-  int32_t* gbi = band_idx + static_cast<size_t>(r) * Spad;
-  uint64_t* gbk = band_key + static_cast<size_t>(r) * Spad;
-  for (int64_t c0 = static_cast<int64_t>(blockIdx.x) * kSplitPerWG; c0 < n_list;
-       c0 += static_cast<int64_t>(gridDim.x) * kSplitPerWG) {
-    // the list holds whole subtiles: 16 consecutive entries per thread
-    const int64_t i0 = c0 + 16 * tid;
-    const bool live = i0 < n_list;
-    double yv[16];
-    int32_t cv[16];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int4 c4 = live ? *reinterpret_cast<const int4*>(ci + i0 + 4 * u) : int4{-1, -1, -1, -1};
-      cv[4 * u] = c4.x;
-      cv[4 * u + 1] = c4.y;
-      cv[4 * u + 2] = c4.z;
-      cv[4 * u + 3] = c4.w;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const double2 y2 = live ? *reinterpret_cast<const double2*>(cy + i0 + 2 * u) : double2{0.0, 0.0};
-      yv[2 * u] = y2.x;
-      yv[2 * u + 1] = y2.y;
-    }
-    uint32_t mu = 0, ma = 0;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int bn = cand_bin(yv[e], ybase);
-      const bool valid = cv[e] >= 0;
-      mu |= static_cast<uint32_t>(valid && bn > bstar) << e;
-      ma |= static_cast<uint32_t>(valid && bn == bstar) << e;
-    }
-    uint32_t ou, oa;
-    reserve_two(__popc(mu), __popc(ma), &info[r].up_count, &info[r].unc_count, s_cnt, s_base,
-                ou, oa);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      if ((mu >> e) & 1u) {
-        if (ou < static_cast<uint32_t>(kMaxSel)) sl[ou] = cv[e];
-        ++ou;
-      } else if ((ma >> e) & 1u) {
-        if (oa < static_cast<uint64_t>(Spad)) {
-          gbk[oa] = ordered_u64(yv[e]);
-          gbi[oa] = cv[e];
-        }
-        ++oa;
-      }
-    }
-  }
-}
-
-// Sizes the rank kernels agree on: selected above the band, band size, and
-// how many band entries join the selection.
-struct SelCounts {
-  uint32_t n_up, n_band, take;
-};
-__device__ __forceinline__ SelCounts sel_counts(const RowInfo& inf, int topk) {
-  SelCounts c;
-  c.n_up = min(inf.up_count, static_cast<uint32_t>(topk));
-  c.n_band = inf.unc_count;
-  c.take = min(static_cast<uint32_t>(topk) - c.n_up, c.n_band);
-  return c;
-}
-
-// Rank of each band entry by (importance desc, index asc) among the row's band:
-// 64 entries per work-group (one per lane), the four waves each count over a
-// quarter of the band.  Entries of rank < take join the selection list at
-// n_up + rank.  A band above kBandRankMax entries is resolved by work-group 0
-// with the radix select.
-__global__ __launch_bounds__(kThreads) void band_rank_kernel(
-    const RowInfo* __restrict__ info, const int32_t* __restrict__ band_idx,
-    const uint64_t* __restrict__ band_key, int32_t* __restrict__ sel_list, int64_t S,
-    int64_t Spad, int T, int Hkv, int topk, int w) {
-  __shared__ uint32_t part[4][64];
-  __shared__ uint32_t h256[256];
-  __shared__ uint32_t s_count, s_tlo, s_need;
-  __shared__ uint64_t s_thi;
-  const int r = blockIdx.y;
+  const int r = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t first = row_first(row_pos(r, T, Hkv, S), w);
-  if (topk <= 0 || first == 0) return;
-  const SelCounts c = sel_counts(info[r], topk);
-  if (c.take == 0) return;
-  const int32_t* bi = band_idx + static_cast<size_t>(r) * Spad;
-  const uint64_t* bk = band_key + static_cast<size_t>(r) * Spad;
-  int32_t* sl = sel_list + static_cast<size_t>(r) * kMaxSel;
-  if (c.n_band > static_cast<uint32_t>(kBandRankMax)) {
-    if (blockIdx.x != 0) return;
-    struct ListSrc {
-      const uint64_t* k;
-      const int32_t* x;
-      __device__ bool get(int64_t i, uint64_t& key, int32_t& j) const {
-        key = k[i];
-        j = x[i];
-        return true;
-      }
-    } src{bk, bi};
-    if (tid == 0) s_count = c.n_up;
-    __syncthreads();
-    radix_select_band(src, min(static_cast<int64_t>(c.n_band), Spad), c.take, sl, &s_count,
-                      h256, &s_thi, &s_tlo, &s_need);
-    return;
-  }
-  const uint32_t e0 = blockIdx.x * 64u;
-  if (e0 >= c.n_band) return;
-  const uint32_t e = e0 + lane;
-  const bool mine = e < c.n_band;
-  const Cand me = mine ? Cand{bk[e], bi[e], 0} : Cand{0ull, 0x7FFFFFFF, 0};
-  // quarters of whole 16-entry blocks; reads past the band stay inside the
-  // row's list (n_band <= Spad, both multiples of 64 after rounding) and are
-  // masked
-  const uint32_t q = ((c.n_band + 3u) / 4u + 15u) & ~15u;
-  const uint32_t f0 = wave * q, f1 = min(c.n_band, f0 + q);
-  uint32_t beat = 0;
-  for (uint32_t f = f0; f < f1; f += 16) {
-    uint64_t ok[16];
-    int32_t oi[16];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const ulonglong2 k2 = *reinterpret_cast<const ulonglong2*>(bk + f + 2 * u);
-      ok[2 * u] = k2.x;
-      ok[2 * u + 1] = k2.y;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int4 i4 = *reinterpret_cast<const int4*>(bi + f + 4 * u);
-      oi[4 * u] = i4.x;
-      oi[4 * u + 1] = i4.y;
-      oi[4 * u + 2] = i4.z;
-      oi[4 * u + 3] = i4.w;
-    }
-#pragma unroll
-    for (int u = 0; u < 16; ++u)
-      beat += static_cast<uint32_t>((f + u < f1) & before(Cand{ok[u], oi[u], 0}, me));
-  }
-  part[wave][lane] = beat;
-  __syncthreads();
-  if (wave == 0 && mine) {
-    const uint32_t rank = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
-    if (rank < c.take) sl[c.n_up + rank] = me.idx;
-  }
-}
-
-// The row's output: the selection in ascending index order (each entry goes to
-// its rank; 64 entries per work-group, four waves over quarters of the list),
-// then the window [first, P], then -1 up to cap, and the count.
-__global__ __launch_bounds__(kThreads) void emit_rank_kernel(
-    const RowInfo* __restrict__ info, const int32_t* __restrict__ sel_list,
-    int32_t* __restrict__ idx_out, int32_t* __restrict__ nsel_out, int64_t S, int T, int Hkv,
-    int topk, int w, int cap) {
-  __shared__ uint32_t part[4][64];
-  const int r = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int P = row_pos(r, T, Hkv, S);
   const int64_t first = row_first(P, w);
+  int32_t* out = idx_out + static_cast<size_t>(r) * cap;
   uint32_t n_keep = 0;
   if (topk > 0 && first > 0) {
-    const SelCounts c = sel_counts(info[r], topk);
-    n_keep = c.n_up + c.take;
-  }
-  int32_t* out = idx_out + static_cast<size_t>(r) * cap;
-  if (blockIdx.x == 0) {
-    const int n_total = static_cast<int>(n_keep) + static_cast<int>(static_cast<int64_t>(P) - first + 1);
-    for (int i = static_cast<int>(n_keep) + tid; i < cap; i += kThreads)
-      out[i] = i < n_total ? static_cast<int32_t>(first + (i - static_cast<int>(n_keep))) : -1;
-    if (tid == 0) nsel_out[r] = n_total;
-  }
-  const uint32_t e0 = blockIdx.x * 64u;
-  if (e0 >= n_keep) return;
-  const int32_t* sl = sel_list + static_cast<size_t>(r) * kMaxSel;
-  const uint32_t e = e0 + lane;
-  const bool mine = e < n_keep;
-  const int32_t me = mine ? sl[e] : 0x7FFFFFFF;
-  // quarters of whole 16-entry blocks (reads stay inside the row's kMaxSel
-  // entries and are masked past n_keep)
-  const uint32_t q = ((n_keep + 3u) / 4u + 15u) & ~15u;
-  const uint32_t f0 = wave * q, f1 = min(n_keep, f0 + q);
-  uint32_t below = 0;
-  for (uint32_t f = f0; f < f1; f += 16) {
-    int32_t o[16];
+    // ---- histogram and chunk lengths (exclusive prefix in pre)
+    for (int i = tid; i < kNB; i += kSelThreads) lh[i] = hist_c[static_cast<size_t>(r) * kNB + i];
+    constexpr int kPer = kMaxChunks / kSelThreads;
+    uint32_t cl[kPer];
+    uint32_t mysum = 0;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int4 i4 = *reinterpret_cast<const int4*>(sl + f + 4 * u);
-      o[4 * u] = i4.x;
-      o[4 * u + 1] = i4.y;
-      o[4 * u + 2] = i4.z;
-      o[4 * u + 3] = i4.w;
+    for (int u = 0; u < kPer; ++u) {
+      const int c = kPer * tid + u;
+      cl[u] = c < n_chunks ? cand_cnt[static_cast<size_t>(r) * n_chunks + c] : 0u;
+      mysum += cl[u];
     }
+    if (tid == 0) s_ybase = row_ybase(ytop_h, r);
+    uint32_t off, dummy;
+    reserve_two(mysum, 0u, nullptr, nullptr, s_cnt, s_base, off, dummy);
 #pragma unroll
-    for (int u = 0; u < 16; ++u) below += static_cast<uint32_t>((f + u < f1) & (o[u] < me));
+    for (int u = 0; u < kPer; ++u) {
+      const int c = kPer * tid + u;
+      if (c < n_chunks) pre[c] = off;
+      off += cl[u];
+    }
+    if (tid == 0) pre[n_chunks] = s_base[2];
+    if (tid < 64) {
+      const KthBin kb = kth_bin_wave(lh, static_cast<uint32_t>(topk));
+      if (tid == 0) {
+        s_b = kb.found ? kb.bstar : -1;
+        s_above = kb.above;
+        s_at = kb.at;
+      }
+    }
+    __syncthreads();
+    const uint32_t n_total = pre[n_chunks];
+    const int bstar = s_b;
+    const float ybase = s_ybase;
+    const size_t chunk_len = static_cast<size_t>(chunk) * kSubKeys;
+    const size_t rbase = static_cast<size_t>(r) * n_chunks * chunk_len;
+    const double* cy = cand_y + rbase;
+    const int32_t* ci = cand_idx + rbase;
+    const int n_sweeps = static_cast<int>((n_total + kSweep - 1) / kSweep);
+    const bool all = bstar < 0;
+    const uint32_t take = all ? 0u : static_cast<uint32_t>(topk) - s_above;
+    const uint32_t n_band = all ? 0u : s_at;
+    SelEntry e0;
+    load_entries(e0, cy, ci, pre, n_chunks, chunk_len, kPerThr * tid, n_total);
+    // sweep sw of the list as registers
+    auto sweep = [&](int sw, SelEntry& e) {
+      if (sw == 0) e = e0;
+      else load_entries(e, cy, ci, pre, n_chunks, chunk_len, sw * kSweep + kPerThr * tid, n_total);
+    };
+    auto in_band = [&](const SelEntry& e, int u) {
+      return u < e.n && cand_bin(e.y[u], ybase) == bstar;
+    };
+    // ---- threshold T of the band's importance (radix over the 64-bit key)
+    uint64_t thr = 0;
+    uint32_t nd_t = 0;      // entries equal to T taken, in list order
+    bool incl = true;       // true: every band entry >= thr is taken
+    if (!all && take < n_band) {
+      uint64_t mask = 0;
+      uint32_t nd = take;
+      while (true) {
+        if (tid < 4) s_red[tid] = tid < 2 ? 0xFFFFFFFFu : 0u;
+        __syncthreads();
+        uint32_t a0 = ~0u, a1 = ~0u, o0 = 0u, o1 = 0u;
+        for (int sw = 0; sw < n_sweeps; ++sw) {
+          SelEntry e;
+          sweep(sw, e);
+#pragma unroll
+          for (int u = 0; u < kPerThr; ++u) {
+            if (!in_band(e, u)) continue;
+            const uint64_t kh = ordered_u64(e.y[u]);
+            if ((kh & mask) != thr) continue;
+            a0 &= static_cast<uint32_t>(kh >> 32);
+            a1 &= static_cast<uint32_t>(kh);
+            o0 |= static_cast<uint32_t>(kh >> 32);
+            o1 |= static_cast<uint32_t>(kh);
+          }
+        }
+        a0 = wave_and(a0);
+        a1 = wave_and(a1);
+        o0 = wave_or(o0);
+        o1 = wave_or(o1);
+        if (lane == 0) {
+          atomicAnd(&s_red[0], a0);
+          atomicAnd(&s_red[1], a1);
+          atomicOr(&s_red[2], o0);
+          atomicOr(&s_red[3], o1);
+        }
+        __syncthreads();
+        const uint64_t and_k = (static_cast<uint64_t>(s_red[0]) << 32) | s_red[1];
+        const uint64_t or_k = (static_cast<uint64_t>(s_red[2]) << 32) | s_red[3];
+        const uint64_t diff = and_k ^ or_k;
+        if (diff == 0) {
+          // every entry still in play has the same importance: T, taken in order
+          thr = and_k;
+          nd_t = nd;
+          incl = false;
+          break;
+        }
+        const int d = __clzll(static_cast<long long>(diff)) / 8;   // first digit that differs
+        mask = d == 0 ? 0ull : ~0ull << (64 - 8 * d);
+        thr = and_k & mask;
+        if (tid < 256) h256[tid] = 0u;
+        __syncthreads();
+        for (int sw = 0; sw < n_sweeps; ++sw) {
+          SelEntry e;
+          sweep(sw, e);
+#pragma unroll
+          for (int u = 0; u < kPerThr; ++u) {
+            bool act = false;
+            uint32_t dig = 0;
+            if (in_band(e, u)) {
+              const uint64_t kh = ordered_u64(e.y[u]);
+              act = (kh & mask) == thr;
+              dig = static_cast<uint32_t>(kh >> (56 - 8 * d)) & 255u;
+            }
+            const uint64_t m_act = __ballot(act);
+            if (m_act) {
+              const int leader = __builtin_ctzll(m_act);
+              const uint32_t d0 = __shfl(dig, leader);
+              if (__ballot(act && dig == d0) == m_act) {
+                if (lane == leader) atomicAdd(&h256[d0], static_cast<uint32_t>(__popcll(m_act)));
+              } else if (act) {
+                atomicAdd(&h256[dig], 1u);
+              }
+            }
+          }
+        }
+        __syncthreads();
+        if (tid < 64) {
+          // lane l holds bins 255-4l .. 252-4l; counts from the top
+          uint32_t c4[4];
+          uint32_t sum = 0;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            c4[u] = h256[255 - 4 * lane - u];
+            sum += c4[u];
+          }
+          uint32_t inc = sum;
+#pragma unroll
+          for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t v = __shfl_up(inc, o);
+            if (lane >= o) inc += v;
+          }
+          const uint64_t hit = __ballot(inc >= nd);
+          const int owner = hit ? __builtin_ctzll(hit) : 63;   // nd <= entries in play
+          if (lane == owner) {
+            uint32_t above = inc - sum;
+            int u = 0;
+            for (; u < 3; ++u) {
+              if (above + c4[u] >= nd) break;
+              above += c4[u];
+            }
+            const uint32_t left = nd - above;
+            s_need = left;
+            s_done = c4[u] == left;
+            s_hi = thr | (static_cast<uint64_t>(255 - 4 * lane - u) << (56 - 8 * d));
+          }
+        }
+        __syncthreads();
+        nd = s_need;
+        thr = s_hi;
+        mask |= 255ull << (56 - 8 * d);
+        if (s_done) break;   // every remaining entry of the bin is taken
+        __syncthreads();     // s_need / s_hi / s_done are rewritten next round
+      }
+    }
+    // ---- the selection in list order
+    auto pick = [&](const SelEntry& e, int u, uint32_t& sel, uint32_t& tie) {
+      sel = 0;
+      tie = 0;
+      if (u >= e.n) return;
+      if (all) {
+        sel = 1;
+        return;
+      }
+      const int bn = cand_bin(e.y[u], ybase);
+      if (bn != bstar) {
+        sel = bn > bstar;
+        return;
+      }
+      if (take >= n_band) {
+        sel = 1;
+        return;
+      }
+      const uint64_t kh = ordered_u64(e.y[u]);
+      if (kh > thr || (incl && kh == thr)) sel = 1;
+      else if (kh == thr) tie = 1;
+    };
+    uint32_t tie_seen = 0, written = 0;
+    for (int sw = 0; sw < n_sweeps; ++sw) {
+      SelEntry e;
+      sweep(sw, e);
+      uint32_t ns = 0, nt = 0;
+#pragma unroll
+      for (int u = 0; u < kPerThr; ++u) {
+        uint32_t sl, tl;
+        pick(e, u, sl, tl);
+        ns += sl;
+        nt += tl;
+      }
+      uint32_t o_tie, o_dummy;
+      reserve_two(nt, 0u, nullptr, nullptr, s_cnt, s_base, o_tie, o_dummy);
+      o_tie += tie_seen;
+      tie_seen += s_base[2];
+      // ties take the first nd_t in list order; count them into the selection
+      uint32_t keep_tie = 0;
+#pragma unroll
+      for (int u = 0; u < kPerThr; ++u) {
+        uint32_t sl, tl;
+        pick(e, u, sl, tl);
+        if (tl) {
+          keep_tie += o_tie < nd_t;
+          ++o_tie;
+        }
+      }
+      uint32_t o_out;
+      reserve_two(ns + keep_tie, 0u, nullptr, nullptr, s_cnt, s_base, o_out, o_dummy);
+      o_out += written;
+      written += s_base[2];
+      o_tie -= nt;   // rewind to this thread's first tie rank
+#pragma unroll
+      for (int u = 0; u < kPerThr; ++u) {
+        uint32_t sl, tl;
+        pick(e, u, sl, tl);
+        if (tl) {
+          sl = o_tie < nd_t;
+          ++o_tie;
+        }
+        if (sl) {
+          if (o_out < static_cast<uint32_t>(cap)) out[o_out] = e.j[u];
+          ++o_out;
+        }
+      }
+    }
+    n_keep = written;
   }
-  part[wave][lane] = below;
   __syncthreads();
-  if (wave == 0 && mine) {
-    const uint32_t rank = part[0][lane] + part[1][lane] + part[2][lane] + part[3][lane];
-    if (rank < n_keep) out[rank] = me;
-  }
+  const int n_total_sel = static_cast<int>(n_keep) + static_cast<int>(static_cast<int64_t>(P) - first + 1);
+  for (int i = static_cast<int>(n_keep) + tid; i < cap; i += kSelThreads)
+    out[i] = i < n_total_sel ? static_cast<int32_t>(first + (i - static_cast<int>(n_keep))) : -1;
+  if (tid == 0) nsel_out[r] = n_total_sel;
 }
 
 // ================================================================ prefill chunk
@@ -1220,31 +1363,21 @@ hipError_t launch_fused_select(const Plan& p, const u16* q, const u16* k, int32_
   const float* ytop = reinterpret_cast<const float*>(w + p.off_ytop);
   uint32_t* hist = reinterpret_cast<uint32_t*>(w + p.off_hist);
   uint32_t* hist_c = reinterpret_cast<uint32_t*>(w + p.off_hist_c);
-  RowInfo* info = reinterpret_cast<RowInfo*>(w + p.off_info);
   double* cand_y = reinterpret_cast<double*>(w + p.off_cand_y);
   int32_t* cand_idx = reinterpret_cast<int32_t*>(w + p.off_cand_idx);
+  uint32_t* cand_cnt = reinterpret_cast<uint32_t*>(w + p.off_cand_cnt);
   const double c2 = p.scale * 1.4426950408889634;  // scale * log2(e)
-  hipLaunchKernelGGL(subtile_hist_kernel, dim3(p.st_nchunk, p.R), dim3(kThreads), 0, st, stmax,
-                     lse2, ytop, hist, hist_c, p.S, p.Spad, p.T, p.Hkv, p.k, p.w, p.st_chunk);
+  hipLaunchKernelGGL(subtile_hist_kernel, dim3(p.hs_nchunk, p.R), dim3(kThreads), 0, st, stmax,
+                     lse2, ytop, hist, hist_c, p.S, p.Spad, p.T, p.Hkv, p.k, p.w, p.hs_chunk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(subtile_score_kernel, dim3(p.st_nchunk, p.R), dim3(kThreads), 0, st, stmax,
-                     lse2, ytop, hist, hist_c, info, q, k, cand_y, cand_idx, p.S, p.Spad, p.T,
-                     p.Hkv, p.k, p.w, p.st_chunk, c2);
+  hipLaunchKernelGGL(subtile_score_kernel, dim3(p.sc_nchunk, p.R), dim3(kThreads), 0, st, stmax,
+                     lse2, ytop, hist, hist_c, q, k, cand_y, cand_idx, cand_cnt, p.S, p.Spad, p.T,
+                     p.Hkv, p.k, p.w, p.sc_chunk, p.sc_nchunk, c2);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int64_t n_split = std::min<int64_t>((p.Spad + kSplitPerWG - 1) / kSplitPerWG, kSplitMaxWG);
-  int32_t* sel_list = reinterpret_cast<int32_t*>(w + p.off_sel_list);
-  int32_t* band_idx = reinterpret_cast<int32_t*>(w + p.off_band_idx);
-  uint64_t* band_key = reinterpret_cast<uint64_t*>(w + p.off_band_key);
-  hipLaunchKernelGGL(cand_split_kernel, dim3(static_cast<unsigned>(n_split), p.R), dim3(kThreads),
-                     0, st, info, hist_c, cand_y, cand_idx, ytop, sel_list, band_idx, band_key,
-                     p.S, p.Spad, p.T, p.Hkv, p.k, p.w);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(band_rank_kernel, dim3(kBandRankMax / 64, p.R), dim3(kThreads), 0, st, info,
-                     band_idx, band_key, sel_list, p.S, p.Spad, p.T, p.Hkv, p.k, p.w);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(emit_rank_kernel, dim3(kMaxSel / 64, p.R), dim3(kThreads), 0, st, info,
-                     sel_list, idx, n_sel, p.S, p.T, p.Hkv, p.k, p.w, p.cap);
+  hipLaunchKernelGGL(row_select_kernel, dim3(p.R), dim3(kSelThreads), 0, st, hist_c, cand_y,
+                     cand_idx, cand_cnt, ytop, idx, n_sel, p.S, p.T, p.Hkv, p.k, p.w, p.cap,
+                     p.sc_chunk, p.sc_nchunk);
   return hipGetLastError();
 }
 
