@@ -13,6 +13,8 @@ constexpr int kD = 128;          // head dim (v1)
 constexpr int kG = 8;            // query heads per KV head (v1)
 constexpr int kNB = 2048;        // selection histogram bins (top 11 bits of a 32-bit key)
 constexpr int kBinShift = 21;    // 32 - 11
+constexpr int kPNB = 512;        // prefill-chunk histogram bins (1/8 octave; top 9 bits)
+constexpr int kPBinShift = 23;   // 32 - 9
 constexpr int kUncCap = 2048;    // near-threshold keys handled in LDS; more take the slow path
 constexpr int kMaxSel = 4096;    // top_k + window limit (index list kept in LDS)
 constexpr int kSparseChunk = 128;  // selected keys per sparse work-group (4 waves x 32)

@@ -25,10 +25,10 @@
 //  * Work-groups are numbered so that each of the 8 XCDs gets a contiguous
 //    range of (batch, KV head, token block): the work-groups that share a KV
 //    head's K/V run on one XCD and share its L2.
-//  * The importance pass (second kernel) recomputes S^T with lse known and
-//    writes y = max_h(s2_h - lse2_h) per (row, older key) in float32, plus an
-//    exact per-row histogram kept in LDS (the work-group sees all of its rows'
-//    keys, so no atomics leave the work-group).
+//  * The importance pass (second kernel) recomputes the logits with lse known
+//    and writes y = max_h(s2_h - lse2_h) per (row, older key) in float32, plus
+//    an exact per-row histogram (1/8 octave bins) kept in LDS (the work-group
+//    sees all of its rows' keys, so no atomics leave the work-group).
 
 #include "hs2_internal.h"
 
@@ -37,7 +37,6 @@ namespace {
 
 constexpr int kPThreads = 256;
 constexpr int kPTok = 16;       // chunk tokens per work-group (attention)
-constexpr int kYTok = 8;        // chunk tokens per work-group (importance)
 constexpr int kPKeys = 64;      // keys per tile
 constexpr int kPPitch = 136;    // u16 per K/V row in LDS (272 bytes)
 
@@ -252,23 +251,26 @@ __global__ __launch_bounds__(kPThreads, 2) void full_prefill_kernel(
   }
 }
 
-// Importance pass.  grid: B * Hkv * ceil(T / 8) work-groups of 256 threads; a
-// work-group takes 8 chunk tokens (one 16-column query block per wave).
+// Importance pass.  grid: B * Hkv * ceil(T / 16) work-groups of 256 threads;
+// a work-group takes 16 chunk tokens, each wave two 16-row query blocks (2
+// tokens x 8 heads each), so every K tile staged in LDS serves 16 tokens.
+// Here the MFMA computes S = Q . K^T (query rows, key columns): a lane holds 4
+// heads of one token for one key, and the max over the token's 8 heads is 3
+// in-lane steps and one exchange with the partner lane.
 // Writes, for every row (b, t, g) it owns:
 //   y[row][j] = max_h(s2_h[j] - lse2_h) for older keys j < first_t (float32,
-//               when y is non-null), and its histogram hist[row][2048] over
-//               bins of 1/32 octave above the row's ybase (when hist is
+//               when y is non-null), and its histogram hist[row][kPNB] over
+//               bins of 1/8 octave above the row's ybase (when hist is
 //               non-null; complete, plain stores);
 //   scores[row][j] = 2^y for all j <= P_t, 0 above (when scores is non-null).
-__global__ __launch_bounds__(kPThreads, 1) void prefill_importance_kernel(
+__global__ __launch_bounds__(kPThreads, 2) void prefill_importance_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const double* __restrict__ lse2,
     const float* __restrict__ ytop_h, float* __restrict__ y, uint32_t* __restrict__ hist,
     float* __restrict__ scores, int64_t S, int64_t Spad, int T, int Hkv, int w, int n_tblk,
     float c2_hi, float c2_lo) {
   __shared__ __align__(16) u16 kt[kPKeys * kPPitch];
-  __shared__ uint32_t lh[kYTok][kNB];
-  __shared__ float l2f[kYTok][kG];
-  __shared__ float s_ybase[kYTok];
+  __shared__ uint32_t lh[kPTok][kPNB];
+  __shared__ float s_ybase[kPTok];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -282,82 +284,95 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_importance_kernel(
   const int64_t pos0 = S - T;
   const bool want_hist = hist != nullptr;
   if (want_hist)
-    for (int i = tid; i < kYTok * kNB; i += kPThreads) (&lh[0][0])[i] = 0u;
-  if (tid < kYTok * kG) {
-    const int j = tid / kG, h = tid % kG;
-    int t = tb * kYTok + j;
+    for (int i = tid; i < kPTok * kPNB; i += kPThreads) (&lh[0][0])[i] = 0u;
+  if (tid < kPTok) {
+    int t = tb * kPTok + tid;
     t = t < T ? t : T - 1;
     const size_t row = (static_cast<size_t>(b) * T + t) * Hkv + g;
-    l2f[j][h] = static_cast<float>(lse2[row * kG + h]);
-    if (h == 0) {
-      float yt = -INFINITY;
-      for (int hh = 0; hh < kG; ++hh) yt = fmaxf(yt, ytop_h[row * kG + hh]);
-      s_ybase[j] = yt - kYRange;
-    }
+    float yt = -INFINITY;
+    for (int hh = 0; hh < kG; ++hh) yt = fmaxf(yt, ytop_h[row * kG + hh]);
+    s_ybase[tid] = yt - kYRange;
   }
-  // this lane's column: token 2*wave + (col >> 3), head col & 7
-  const int jloc = 2 * wave + (col >> 3);
-  int t = tb * kYTok + jloc;
-  const bool t_ok = t < T;
-  t = t_ok ? t : T - 1;
-  const int64_t P = pos0 + t;
-  const int64_t first = max(static_cast<int64_t>(0), P - w + 1);
-  const size_t row = (static_cast<size_t>(b) * T + t) * Hkv + g;
-  bf16x8 qop[4];
-  load_q_block(q + (static_cast<size_t>(b) * T + t) * Hq * kD + static_cast<size_t>(g) * kG * kD,
-               col, grp, qop);
-  const int t_last = min(T - 1, tb * kYTok + kYTok - 1);
+  // block qbk of this wave: tokens 4*wave + 2*qbk + {0, 1}
+  bf16x8 qop[2][4];
+  int jloc[2];
+  bool t_ok[2];
+  int64_t P[2], first[2];
+  float l2r[2][4];
+  float* yrow[2];
+  float* srow[2];
+#pragma unroll
+  for (int qbk = 0; qbk < 2; ++qbk) {
+    // the A operand: query row col = (token .. + (col >> 3), head col & 7)
+    int tq = tb * kPTok + 4 * wave + 2 * qbk + (col >> 3);
+    tq = tq < T ? tq : T - 1;
+    load_q_block(q + (static_cast<size_t>(b) * T + tq) * Hq * kD + static_cast<size_t>(g) * kG * kD,
+                 col, grp, qop[qbk]);
+    // this lane's rows of S: 4*grp + i = (token .. + (grp >> 1), head 4*(grp & 1) + i)
+    jloc[qbk] = 4 * wave + 2 * qbk + (grp >> 1);
+    int t = tb * kPTok + jloc[qbk];
+    t_ok[qbk] = t < T;
+    t = t_ok[qbk] ? t : T - 1;
+    P[qbk] = pos0 + t;
+    first[qbk] = max(static_cast<int64_t>(0), P[qbk] - w + 1);
+    const size_t row = (static_cast<size_t>(b) * T + t) * Hkv + g;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) l2r[qbk][i] = static_cast<float>(lse2[row * kG + 4 * (grp & 1) + i]);
+    yrow[qbk] = y ? y + row * Spad : nullptr;
+    srow[qbk] = scores ? scores + row * S : nullptr;
+  }
+  const int t_last = min(T - 1, tb * kPTok + kPTok - 1);
   const int64_t p_last = pos0 + t_last;
   const int n_tiles = static_cast<int>((p_last + kPKeys) / kPKeys);
-  // this lane stores two of the 16 (subtile, i) values its half-wave shares
-  const int c8 = col & 7;
-  const int my_i = c8 & 3;
-  const int my_sub0 = 2 * (c8 >> 2);
-  float* yrow = y ? y + row * Spad : nullptr;
-  float* srow = scores ? scores + row * S : nullptr;
+  // after the head max a lane owns key subtiles 2*(grp & 1) and 2*(grp & 1) + 1
+  const int sub0 = 2 * (grp & 1);
 
   TileRegs regs;
   tile_gload<false>(regs, kr, nullptr, 0, p_last);
   tile_lstore<false>(regs, kt, nullptr);
   __syncthreads();
-  const float ybase = s_ybase[jloc];
-  const float l2 = l2f[jloc][c8];
+  const float ybase[2] = {s_ybase[jloc[0]], s_ybase[jloc[1]]};
   for (int it = 0; it < n_tiles; ++it) {
     const int64_t key0 = static_cast<int64_t>(it) * kPKeys;
     const bool more = it + 1 < n_tiles;
     if (more) tile_gload<false>(regs, kr, nullptr, key0 + kPKeys, p_last);
-    f32x4 sacc[4];
+    f32x4 sacc[2][4];
 #pragma unroll
     for (int sub = 0; sub < 4; ++sub) {
-      sacc[sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sacc[0][sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+      sacc[1][sub] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        sacc[sub] = mfma_16x16x32(lds_k_operand(kt, sub, c, col, grp), qop[c], sacc[sub]);
+      for (int c = 0; c < 4; ++c) {
+        const bf16x8 kb = lds_k_operand(kt, sub, c, col, grp);
+        sacc[0][sub] = mfma_16x16x32(qop[0][c], kb, sacc[0][sub]);
+        sacc[1][sub] = mfma_16x16x32(qop[1][c], kb, sacc[1][sub]);
+      }
     }
-    // y per (key, token): max over the token's 8 heads (lanes c8 = 0..7 of the
-    // half-wave); afterwards every lane of the half holds all 16 values
-    float yv[4][4];
 #pragma unroll
-    for (int sub = 0; sub < 4; ++sub)
+    for (int qbk = 0; qbk < 2; ++qbk) {
+      // y per (token, key): max over the 8 heads = 4 here x the partner lane
+      float yv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float a = sacc[sub][i];
-        float s = fmaf(a, c2_hi, a * c2_lo) - l2;
-        s = fmaxf(s, __shfl_xor(s, 1));
-        s = fmaxf(s, __shfl_xor(s, 2));
-        s = fmaxf(s, __shfl_xor(s, 4));
-        yv[sub][i] = s;
+      for (int sub = 0; sub < 4; ++sub) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float a = sacc[qbk][sub][i];
+          m = fmaxf(m, fmaf(a, c2_hi, a * c2_lo) - l2r[qbk][i]);
+        }
+        yv[sub] = fmaxf(m, __shfl_xor(m, 16));
       }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int sub = my_sub0 + u;
-      const float yy = sub == 0 ? yv[0][my_i] : sub == 1 ? yv[1][my_i] : sub == 2 ? yv[2][my_i] : yv[3][my_i];
-      const int64_t key = key0 + 16 * sub + 4 * grp + my_i;
-      if (!t_ok || key > P) continue;
-      if (srow) srow[key] = __builtin_amdgcn_exp2f(yy);
-      if (key < first) {
-        if (yrow) yrow[key] = yy;
-        if (want_hist) atomicAdd(&lh[jloc][key_from_log2(yy, ybase) >> kBinShift], 1u);
+      for (int u = 0; u < 2; ++u) {
+        const int sub = sub0 + u;
+        const float yy = sub == 0 ? yv[0] : sub == 1 ? yv[1] : sub == 2 ? yv[2] : yv[3];
+        const int64_t key = key0 + 16 * sub + col;
+        if (!t_ok[qbk] || key > P[qbk]) continue;
+        if (srow[qbk]) srow[qbk][key] = __builtin_amdgcn_exp2f(yy);
+        if (key < first[qbk]) {
+          if (yrow[qbk]) yrow[qbk][key] = yy;
+          if (want_hist) atomicAdd(&lh[jloc[qbk]][key_from_log2(yy, ybase[qbk]) >> kPBinShift], 1u);
+        }
       }
     }
     __syncthreads();
@@ -368,8 +383,8 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_importance_kernel(
   }
   // scores past P_t are 0
   if (scores) {
-    for (int j = 0; j < kYTok; ++j) {
-      const int tt = tb * kYTok + j;
+    for (int j = 0; j < kPTok; ++j) {
+      const int tt = tb * kPTok + j;
       if (tt >= T) break;
       float* sr = scores + ((static_cast<size_t>(b) * T + tt) * Hkv + g) * S;
       for (int64_t key = pos0 + tt + 1 + tid; key < S; key += kPThreads) sr[key] = 0.f;
@@ -377,11 +392,11 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_importance_kernel(
   }
   if (want_hist) {
     __syncthreads();
-    for (int i = tid; i < kYTok * kNB; i += kPThreads) {
-      const int j = i / kNB;
-      const int tt = tb * kYTok + j;
+    for (int i = tid; i < kPTok * kPNB; i += kPThreads) {
+      const int j = i / kPNB;
+      const int tt = tb * kPTok + j;
       if (tt < T)
-        hist[((static_cast<size_t>(b) * T + tt) * Hkv + g) * kNB + (i % kNB)] = (&lh[0][0])[i];
+        hist[((static_cast<size_t>(b) * T + tt) * Hkv + g) * kPNB + (i % kPNB)] = (&lh[0][0])[i];
     }
   }
 }
@@ -409,7 +424,7 @@ hipError_t launch_prefill_importance(const Plan& p, const u16* q, const u16* k, 
   const double c2 = p.scale * 1.4426950408889634;
   const float c2_hi = static_cast<float>(c2);
   const float c2_lo = static_cast<float>(c2 - static_cast<double>(c2_hi));
-  const int n_tblk = (p.T + kYTok - 1) / kYTok;
+  const int n_tblk = (p.T + kPTok - 1) / kPTok;
   const int n_wg = p.B * p.Hkv * n_tblk;
   hipLaunchKernelGGL(prefill_importance_kernel, dim3(n_wg), dim3(kPThreads), 0, st, q, k,
                      reinterpret_cast<const double*>(w + p.off_lse2),

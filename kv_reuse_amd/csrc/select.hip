@@ -68,11 +68,14 @@ struct KthBin {
   uint32_t at;
   bool found;
 };
-__device__ KthBin kth_bin_wave(const uint32_t* lh, uint32_t k) {
+template <int NB>
+__device__ KthBin kth_bin_wave_n(const uint32_t* lh, uint32_t k) {
+  constexpr int kPer = NB / 64;   // bins per lane at level 1
+  static_assert(kPer >= 1 && kPer <= 64, "64..4096 bins");
   const int lane = threadIdx.x & 63;
-  // level 1: lane l sums the 32 bins kNB-1-32l .. kNB-32-32l
+  // level 1: lane l sums the kPer bins NB-1-kPer*l .. NB-kPer-kPer*l
   uint32_t lane_sum = 0;
-  for (int i = 0; i < 32; ++i) lane_sum += lh[kNB - 1 - 32 * lane - i];
+  for (int i = 0; i < kPer; ++i) lane_sum += lh[NB - 1 - kPer * lane - i];
   uint32_t incl = lane_sum;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -84,22 +87,25 @@ __device__ KthBin kth_bin_wave(const uint32_t* lh, uint32_t k) {
   if (!hit) return res;
   const int owner = __builtin_ctzll(hit);
   const uint32_t above0 = __shfl(incl - lane_sum, owner);
-  // level 2: lanes 0..31 take the owner's 32 bins from the top
-  const int bin = kNB - 1 - 32 * owner - (lane & 31);
-  const uint32_t c = lane < 32 ? lh[bin] : 0u;
+  // level 2: lanes 0..kPer-1 take the owner's bins from the top
+  const int bin = NB - 1 - kPer * owner - (lane % kPer);
+  const uint32_t c = lane < kPer ? lh[bin] : 0u;
   uint32_t inc2 = c;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const uint32_t o = __shfl_up(inc2, off);
     if (lane >= off) inc2 += o;
   }
-  const uint64_t hit2 = __ballot(lane < 32 && above0 + inc2 >= k);
+  const uint64_t hit2 = __ballot(lane < kPer && above0 + inc2 >= k);
   const int jj = __builtin_ctzll(hit2);   // the owner's group reaches k, so some lane hits
-  res.bstar = kNB - 1 - 32 * owner - jj;
+  res.bstar = NB - 1 - kPer * owner - jj;
   res.above = above0 + __shfl(inc2 - c, jj);
   res.at = __shfl(c, jj);
   res.found = true;
   return res;
+}
+__device__ __forceinline__ KthBin kth_bin_wave(const uint32_t* lh, uint32_t k) {
+  return kth_bin_wave_n<kNB>(lh, k);
 }
 
 // Add a work-group's LDS histogram to the row histogram.  The row's k-th
@@ -1177,15 +1183,15 @@ __global__ __launch_bounds__(kRowThreads) void prefill_select_kernel(
   const int64_t first = row_first(P, w);
   int n_keep = 0;
   if (topk > 0 && first > 0) {
-    for (int i = tid; i < kNB; i += kRowThreads) lh[i] = hist[static_cast<size_t>(r) * kNB + i];
+    for (int i = tid; i < kPNB; i += kRowThreads) lh[i] = hist[static_cast<size_t>(r) * kPNB + i];
     if (tid == 0) s_ybase = row_ybase(ytop_h, r);
     __syncthreads();
     if (tid < 64) {
-      const KthBin kb = kth_bin_wave(lh, static_cast<uint32_t>(topk));
+      const KthBin kb = kth_bin_wave_n<kPNB>(lh, static_cast<uint32_t>(topk));
       if (tid == 0) {
         s_b = kb.found ? kb.bstar : -1;
         if (kb.found) {
-          const int lo = max(0, kb.bstar - 1), hi = min(kNB - 1, kb.bstar + 1);
+          const int lo = max(0, kb.bstar - 1), hi = min(kPNB - 1, kb.bstar + 1);
           uint32_t nb = 0;
           for (int bb = lo; bb <= hi; ++bb) nb += lh[bb];
           s_lo = lo;
@@ -1230,7 +1236,7 @@ __global__ __launch_bounds__(kRowThreads) void prefill_select_kernel(
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const bool valid = i0 + e < first;
-          const int bn = static_cast<int>(key_from_log2(yv[e], ybase) >> kBinShift);
+          const int bn = static_cast<int>(key_from_log2(yv[e], ybase) >> kPBinShift);
           mu |= static_cast<uint32_t>(valid && bn > hi) << e;
           ma |= static_cast<uint32_t>(valid && bn >= lo && bn <= hi) << e;
         }
@@ -1308,7 +1314,7 @@ __global__ __launch_bounds__(kRowThreads) void prefill_select_kernel(
           int lo, hi;
           __device__ bool get(int64_t i, uint64_t& key, int32_t& j) const {
             const float yy = yr[i];
-            const int bn = static_cast<int>(key_from_log2(yy, ybase) >> kBinShift);
+            const int bn = static_cast<int>(key_from_log2(yy, ybase) >> kPBinShift);
             if (bn < lo || bn > hi) return false;
             key = static_cast<uint64_t>(ordered_u32(yy));
             j = static_cast<int32_t>(i);
