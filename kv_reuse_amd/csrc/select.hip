@@ -1149,42 +1149,183 @@ __global__ __launch_bounds__(kSelThreads) void row_select_kernel(
 
 // ================================================================ prefill chunk
 
+// The threshold T of the best `need` of n 64-bit keys (larger is better): the
+// keys above T are taken, and of the keys equal to T the first nd_t in array
+// order (or, when incl, every key >= T).  MSB radix select in 8-bit digits:
+// each round first finds the highest bit where the keys still in play differ
+// (the bits they share are fixed at once, which skips exact ties), then takes
+// a 256-bin histogram of that digit; it stops as soon as every remaining key
+// of the chosen bin is needed.  keys: any memory, read several times.  All
+// threads call it (blockDim a multiple of 64, >= 256); 1 <= need <= n.
+struct KThr {
+  uint64_t thr;
+  uint32_t nd_t;
+  bool incl;
+};
+__device__ KThr key_threshold(const uint64_t* keys, uint32_t n, uint32_t need, uint32_t* h256,
+                              uint32_t* s_red, uint64_t* s_hi, uint32_t* s_need, int* s_done) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  uint64_t thr = 0, mask = 0;
+  uint32_t nd = need;
+  while (true) {
+    if (tid < 4) s_red[tid] = tid < 2 ? 0xFFFFFFFFu : 0u;
+    __syncthreads();
+    uint32_t a0 = ~0u, a1 = ~0u, o0 = 0u, o1 = 0u;
+    for (uint32_t base = 0; base < n; base += blockDim.x) {
+      const uint32_t i = base + tid;
+      if (i < n) {
+        const uint64_t kh = keys[i];
+        if ((kh & mask) == thr) {
+          a0 &= static_cast<uint32_t>(kh >> 32);
+          a1 &= static_cast<uint32_t>(kh);
+          o0 |= static_cast<uint32_t>(kh >> 32);
+          o1 |= static_cast<uint32_t>(kh);
+        }
+      }
+    }
+    a0 = wave_and(a0);
+    a1 = wave_and(a1);
+    o0 = wave_or(o0);
+    o1 = wave_or(o1);
+    if (lane == 0) {
+      atomicAnd(&s_red[0], a0);
+      atomicAnd(&s_red[1], a1);
+      atomicOr(&s_red[2], o0);
+      atomicOr(&s_red[3], o1);
+    }
+    __syncthreads();
+    const uint64_t and_k = (static_cast<uint64_t>(s_red[0]) << 32) | s_red[1];
+    const uint64_t or_k = (static_cast<uint64_t>(s_red[2]) << 32) | s_red[3];
+    const uint64_t diff = and_k ^ or_k;
+    if (diff == 0) {
+      __syncthreads();
+      return KThr{and_k, nd, false};   // all keys in play equal: take the first nd
+    }
+    const int d = __clzll(static_cast<long long>(diff)) / 8;
+    mask = d == 0 ? 0ull : ~0ull << (64 - 8 * d);
+    thr = and_k & mask;
+    if (tid < 256) h256[tid] = 0u;
+    __syncthreads();
+    for (uint32_t base = 0; base < n; base += blockDim.x) {
+      const uint32_t i = base + tid;
+      bool act = false;
+      uint32_t dig = 0;
+      if (i < n) {
+        const uint64_t kh = keys[i];
+        act = (kh & mask) == thr;
+        dig = static_cast<uint32_t>(kh >> (56 - 8 * d)) & 255u;
+      }
+      const uint64_t m_act = __ballot(act);
+      if (m_act) {
+        const int leader = __builtin_ctzll(m_act);
+        const uint32_t d0 = __shfl(dig, leader);
+        if (__ballot(act && dig == d0) == m_act) {
+          if (lane == leader) atomicAdd(&h256[d0], static_cast<uint32_t>(__popcll(m_act)));
+        } else if (act) {
+          atomicAdd(&h256[dig], 1u);
+        }
+      }
+    }
+    __syncthreads();
+    if (tid < 64) {
+      uint32_t c4[4];
+      uint32_t sum = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        c4[u] = h256[255 - 4 * lane - u];
+        sum += c4[u];
+      }
+      uint32_t inc = sum;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t v = __shfl_up(inc, o);
+        if (lane >= o) inc += v;
+      }
+      const uint64_t hit = __ballot(inc >= nd);
+      const int owner = hit ? __builtin_ctzll(hit) : 63;
+      if (lane == owner) {
+        uint32_t above = inc - sum;
+        int u = 0;
+        for (; u < 3; ++u) {
+          if (above + c4[u] >= nd) break;
+          above += c4[u];
+        }
+        const uint32_t left = nd - above;
+        *s_need = left;
+        *s_done = c4[u] == left;
+        *s_hi = thr | (static_cast<uint64_t>(255 - 4 * lane - u) << (56 - 8 * d));
+      }
+    }
+    __syncthreads();
+    nd = *s_need;
+    thr = *s_hi;
+    mask |= 255ull << (56 - 8 * d);
+    const bool done = *s_done != 0;
+    __syncthreads();
+    if (done) return KThr{thr, 0u, true};
+  }
+}
+
+// Number of entries of the ascending array a[0..n) that are < v.
+__device__ __forceinline__ uint32_t lower_bound_lds(const int32_t* a, uint32_t n, int32_t v) {
+  uint32_t lo = 0, hi = n;
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi) >> 1;
+    if (a[mid] < v) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
 // One work-group per row (b, t, g) of a prefill chunk: the exact top-k of the
 // row's older keys from their float32 log2 importance y and the row's
-// complete histogram.  Bins above b*+1 are selected; keys in bins b*-1..b*+1
-// (the float32 error of y is far below a bin) get their importance recomputed
-// in float64 from exact bf16 products and are ranked (importance desc, index
-// asc).  A band larger than band_cap is ranked by its float32 y instead.
-__global__ __launch_bounds__(kRowThreads) void prefill_select_kernel(
+// complete histogram (kPNB bins of 1/8 octave).
+//  * One pass over y in key order: bins above b*+1 go to the "up" list, bins
+//    b*-1..b*+1 (the float32 error of y is far below a bin) to the band list;
+//    both lists come out in ascending key order.
+//  * The band keys' importance is recomputed in float64 from exact bf16
+//    products; a radix threshold on it picks the band's share, ties going to
+//    the lower index (the band list is in index order).
+//  * The up list and the band winners, both ascending, are merged into the
+//    output by rank; then the window, the padding and the count.
+// A band larger than band_cap is ranked by its float32 y instead.
+__global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
     const float* __restrict__ ybuf, const uint32_t* __restrict__ hist,
     const float* __restrict__ ytop_h, const double* __restrict__ lse2, const u16* __restrict__ q,
     const u16* __restrict__ k, int32_t* __restrict__ band_idx, uint64_t* __restrict__ band_key,
     int64_t band_cap, int32_t* __restrict__ idx_out, int32_t* __restrict__ nsel_out, int64_t S,
     int64_t Spad, int T, int Hkv, int topk, int w, int cap, double c2) {
-  __shared__ __align__(16) int32_t tmp[kMaxSel];
-  __shared__ __align__(16) uint32_t sel_lh[kMaxSel];   // histogram first, emit scratch last
-  __shared__ __align__(16) Cand cands[kUncCap];        // band (keys, indices), then sort scratch
+  __shared__ __align__(16) int32_t up[kMaxSel];
+  __shared__ __align__(16) int32_t bw[kMaxSel];        // band winners; first the histogram
+  __shared__ __align__(16) uint64_t lbk[kUncCap];
+  __shared__ __align__(16) int32_t lbi[kUncCap];
   __shared__ double qd[kG * kD];
   __shared__ double l2s[kG];
   __shared__ uint32_t h256[256];
-  __shared__ uint32_t s_count, s_tlo, s_need;
+  __shared__ uint32_t s_red[4];
+  __shared__ uint64_t s_hi;
+  __shared__ uint32_t s_need, s_count, s_tlo;
   __shared__ uint64_t s_thi;
-  __shared__ int s_b, s_lo, s_hi;
+  __shared__ int s_done;
+  __shared__ int s_b, s_lo, s_hi2;
   __shared__ uint32_t s_nband;
   __shared__ float s_ybase;
   __shared__ uint32_t s_cnt[2][16];
   __shared__ uint32_t s_base[4];
-  uint32_t* lh = sel_lh;
-  uint64_t* lband_k = reinterpret_cast<uint64_t*>(cands);
-  int32_t* lband_i = reinterpret_cast<int32_t*>(lband_k + kUncCap);
+  uint32_t* lh = reinterpret_cast<uint32_t*>(bw);
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
   const int P = row_pos(r, T, Hkv, S);
   const int64_t first = row_first(P, w);
-  int n_keep = 0;
+  int32_t* out = idx_out + static_cast<size_t>(r) * cap;
+  uint32_t n_keep = 0;
   if (topk > 0 && first > 0) {
     for (int i = tid; i < kPNB; i += kRowThreads) lh[i] = hist[static_cast<size_t>(r) * kPNB + i];
     if (tid == 0) s_ybase = row_ybase(ytop_h, r);
+    const u16* qr = q + static_cast<size_t>(r) * kG * kD;
+    for (int i = tid; i < kG * kD; i += kRowThreads) qd[i] = static_cast<double>(bf16_bits_to_f32(qr[i]));
+    if (tid < kG) l2s[tid] = lse2[static_cast<size_t>(r) * kG + tid];
     __syncthreads();
     if (tid < 64) {
       const KthBin kb = kth_bin_wave_n<kPNB>(lh, static_cast<uint32_t>(topk));
@@ -1195,18 +1336,18 @@ __global__ __launch_bounds__(kRowThreads) void prefill_select_kernel(
           uint32_t nb = 0;
           for (int bb = lo; bb <= hi; ++bb) nb += lh[bb];
           s_lo = lo;
-          s_hi = hi;
+          s_hi2 = hi;
           s_nband = nb;
         }
       }
     }
     __syncthreads();
     if (s_b < 0) {
-      // fewer older keys than top_k: all of them
-      n_keep = static_cast<int>(min(first, static_cast<int64_t>(kMaxSel)));
-      for (int i = tid; i < n_keep; i += kRowThreads) tmp[i] = i;
+      // fewer older keys than top_k: all of them, in order
+      n_keep = static_cast<uint32_t>(min(first, static_cast<int64_t>(kMaxSel)));
+      for (uint32_t i = tid; i < n_keep; i += kRowThreads) out[i] = static_cast<int32_t>(i);
     } else {
-      const int lo = s_lo, hi = s_hi;
+      const int lo = s_lo, hi = s_hi2;
       const uint32_t n_band_h = s_nband;
       const bool band_lds = n_band_h <= static_cast<uint32_t>(kUncCap);
       const bool band_glob = !band_lds && n_band_h <= static_cast<uint64_t>(band_cap);
@@ -1214,100 +1355,139 @@ __global__ __launch_bounds__(kRowThreads) void prefill_select_kernel(
       const float* yr = ybuf + static_cast<size_t>(r) * Spad;
       int32_t* gbi = band_idx + static_cast<size_t>(r) * band_cap;
       uint64_t* gbk = band_key + static_cast<size_t>(r) * band_cap;
-      const u16* qr = q + static_cast<size_t>(r) * kG * kD;
-      for (int i = tid; i < kG * kD; i += kRowThreads) qd[i] = static_cast<double>(bf16_bits_to_f32(qr[i]));
-      if (tid < kG) l2s[tid] = lse2[static_cast<size_t>(r) * kG + tid];
-      // ---- one pass over y: above the band -> tmp, band -> band list
+      int32_t* bi = band_lds ? lbi : gbi;
+      uint64_t* bk = band_lds ? lbk : gbk;
+      // ---- one pass over y (16 entries per thread and round; the next
+      // round's loads are issued before this round is processed)
       const int64_t rounds = (first + 16 * kRowThreads - 1) / (16 * kRowThreads);
       uint32_t cu = 0, ca = 0;
+      f32x4 ycur[4], ynxt[4];
+      auto load_round = [&](int64_t rr, f32x4 (&yv)[4]) {
+        const int64_t i0 = 16 * (static_cast<int64_t>(tid) + rr * kRowThreads);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          yv[u] = i0 + 4 * u < first ? *reinterpret_cast<const f32x4*>(yr + i0 + 4 * u)
+                                     : f32x4{0.f, 0.f, 0.f, 0.f};
+      };
+      if (rounds > 0) load_round(0, ycur);
       for (int64_t rr = 0; rr < rounds; ++rr) {
         const int64_t i0 = 16 * (static_cast<int64_t>(tid) + rr * kRowThreads);
-        float yv[16];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const f32x4 y4 = i0 + 4 * u < first ? *reinterpret_cast<const f32x4*>(yr + i0 + 4 * u)
-                                                : f32x4{0.f, 0.f, 0.f, 0.f};
-          yv[4 * u] = y4[0];
-          yv[4 * u + 1] = y4[1];
-          yv[4 * u + 2] = y4[2];
-          yv[4 * u + 3] = y4[3];
-        }
+        if (rr + 1 < rounds) load_round(rr + 1, ynxt);
         uint32_t mu = 0, ma = 0;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const bool valid = i0 + e < first;
-          const int bn = static_cast<int>(key_from_log2(yv[e], ybase) >> kPBinShift);
+          const int bn = static_cast<int>(key_from_log2(ycur[e >> 2][e & 3], ybase) >> kPBinShift);
           mu |= static_cast<uint32_t>(valid && bn > hi) << e;
           ma |= static_cast<uint32_t>(valid && bn >= lo && bn <= hi) << e;
         }
         uint32_t ou, oa;
         reserve_two(__popc(mu), __popc(ma), nullptr, nullptr, s_cnt, s_base, ou, oa);
-        const uint32_t tu = s_base[2], ta = s_base[3];
         ou += cu;
         oa += ca;
-        cu += tu;
-        ca += ta;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int32_t j = static_cast<int32_t>(i0 + e);
-          if ((mu >> e) & 1u) {
-            if (ou < static_cast<uint32_t>(kMaxSel)) tmp[ou] = j;
-            ++ou;
-          } else if ((ma >> e) & 1u) {
-            if (band_lds) {
-              if (oa < static_cast<uint32_t>(kUncCap)) lband_i[oa] = j;
-            } else if (band_glob) {
-              if (oa < static_cast<uint64_t>(band_cap)) gbi[oa] = j;
-            }
+        cu += s_base[2];
+        ca += s_base[3];
+        for (uint32_t m = mu; m; m &= m - 1) {
+          if (ou < static_cast<uint32_t>(kMaxSel)) up[ou] = static_cast<int32_t>(i0 + __builtin_ctz(m));
+          ++ou;
+        }
+        if (band_lds || band_glob) {
+          const uint32_t lim = band_lds ? static_cast<uint32_t>(kUncCap) : static_cast<uint32_t>(band_cap);
+          for (uint32_t m = ma; m; m &= m - 1) {
+            if (oa < lim) bi[oa] = static_cast<int32_t>(i0 + __builtin_ctz(m));
             ++oa;
           }
         }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) ycur[u] = ynxt[u];
       }
       __syncthreads();
       const uint32_t n_up = min(cu, static_cast<uint32_t>(topk));
       const uint32_t take = static_cast<uint32_t>(topk) - n_up;
-      if (tid == 0) s_count = n_up;
+      uint32_t n_w = 0;
       if (band_lds || band_glob) {
-        const uint32_t n_band = band_lds ? min(ca, static_cast<uint32_t>(kUncCap))
-                                         : static_cast<uint32_t>(min(static_cast<int64_t>(ca), band_cap));
-        // exact importance of the band keys in float64 (bf16 products are exact)
+        const uint32_t n_band = min(ca, band_lds ? static_cast<uint32_t>(kUncCap)
+                                                 : static_cast<uint32_t>(band_cap));
+        // ---- exact importance of the band keys in float64 (bf16 products are exact)
         const int b = r / (T * Hkv);
         const int g = r % Hkv;
         const u16* kr = k + (static_cast<size_t>(b) * Hkv + g) * static_cast<size_t>(S) * kD;
         for (uint32_t i = tid; i < n_band; i += kRowThreads) {
-          const int32_t j = band_lds ? lband_i[i] : gbi[i];
-          const u16* kj = kr + static_cast<size_t>(j) * kD;
-          u32x4 raw[16];
-#pragma unroll
-          for (int c = 0; c < 16; ++c) raw[c] = load_u32x4(kj + 8 * c);
+          const u16* kj = kr + static_cast<size_t>(bi[i]) * kD;
           double acc[kG];
 #pragma unroll
           for (int h = 0; h < kG; ++h) acc[h] = 0.0;
+          for (int c4 = 0; c4 < 4; ++c4) {
+            u32x4 raw[4];
 #pragma unroll
-          for (int c = 0; c < 16; ++c) {
+            for (int c = 0; c < 4; ++c) raw[c] = load_u32x4(kj + 32 * c4 + 8 * c);
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-              const uint32_t word = raw[c][t >> 1];
-              const double kv = static_cast<double>(
-                  __uint_as_float((t & 1) ? (word & 0xFFFF0000u) : (word << 16)));
+            for (int c = 0; c < 4; ++c)
 #pragma unroll
-              for (int h = 0; h < kG; ++h) acc[h] = fma(qd[h * kD + 8 * c + t], kv, acc[h]);
-            }
-            // keep the next chunk's LDS reads of the query from being hoisted
-            __builtin_amdgcn_sched_barrier(0);
+              for (int t2 = 0; t2 < 8; ++t2) {
+                const uint32_t word = raw[c][t2 >> 1];
+                const double kv = static_cast<double>(
+                    __uint_as_float((t2 & 1) ? (word & 0xFFFF0000u) : (word << 16)));
+                const int dd = 32 * c4 + 8 * c + t2;
+#pragma unroll
+                for (int h = 0; h < kG; ++h) acc[h] = fma(qd[h * kD + dd], kv, acc[h]);
+              }
           }
           double yy = -INFINITY;
 #pragma unroll
           for (int h = 0; h < kG; ++h) yy = fmax(yy, c2 * acc[h] - l2s[h]);
-          if (band_lds) lband_k[i] = ordered_u64(yy);
-          else gbk[i] = ordered_u64(yy);
+          bk[i] = ordered_u64(yy);
         }
         __syncthreads();
-        take_best(band_lds ? lband_k : gbk, band_lds ? lband_i : gbi, n_band,
-                  min(take, n_band), cands, tmp, &s_count, h256, &s_thi, &s_tlo, &s_need);
-      } else {
+        // ---- the band's share: all of it, or the best `take` by threshold
+        KThr kt{0ull, 0u, true};
+        const bool by_thr = take < n_band;
+        if (by_thr && take > 0) kt = key_threshold(bk, n_band, take, h256, s_red, &s_hi, &s_need, &s_done);
+        // winners in band order (ascending index), ties: the first kt.nd_t
+        const uint32_t per = (n_band + kRowThreads - 1) / kRowThreads;
+        const uint32_t q0 = min(n_band, tid * per), q1 = min(n_band, q0 + per);
+        auto cls = [&](uint32_t i, uint32_t& win, uint32_t& tie) {
+          win = 0;
+          tie = 0;
+          if (!by_thr) {
+            win = 1;
+            return;
+          }
+          if (take == 0) return;
+          const uint64_t kh = bk[i];
+          if (kh > kt.thr || (kt.incl && kh == kt.thr)) win = 1;
+          else if (kh == kt.thr) tie = 1;
+        };
+        uint32_t nwin = 0, ntie = 0;
+        for (uint32_t i = q0; i < q1; ++i) {
+          uint32_t a, t2;
+          cls(i, a, t2);
+          nwin += a;
+          ntie += t2;
+        }
+        uint32_t o_tie, o_dummy;
+        reserve_two(ntie, 0u, nullptr, nullptr, s_cnt, s_base, o_tie, o_dummy);
+        uint32_t keep_tie = 0;
+        for (uint32_t i = q0, ot = o_tie; i < q1; ++i) {
+          uint32_t a, t2;
+          cls(i, a, t2);
+          if (t2) keep_tie += (ot++ < kt.nd_t);
+        }
+        uint32_t o_w;
+        reserve_two(nwin + keep_tie, 0u, nullptr, nullptr, s_cnt, s_base, o_w, o_dummy);
+        n_w = s_base[2];
+        for (uint32_t i = q0, ot = o_tie; i < q1; ++i) {
+          uint32_t a, t2;
+          cls(i, a, t2);
+          if (t2) a = (ot++ < kt.nd_t);
+          if (a) {
+            if (o_w < static_cast<uint32_t>(kMaxSel)) bw[o_w] = bi[i];
+            ++o_w;
+          }
+        }
+      } else if (take > 0) {
         // the band is too large to list: rank it by its float32 importance
-        __syncthreads();
+        // (unordered winners, then sorted)
         struct ScanSrc {
           const float* yr;
           float ybase;
@@ -1321,14 +1501,43 @@ __global__ __launch_bounds__(kRowThreads) void prefill_select_kernel(
             return true;
           }
         } src{yr, ybase, lo, hi};
-        radix_select_band(src, first, min(take, ca), tmp, &s_count, h256, &s_thi, &s_tlo, &s_need);
+        if (tid == 0) s_count = 0u;
+        __syncthreads();
+        radix_select_band(src, first, min(take, ca), bw, &s_count, h256, &s_thi, &s_tlo, &s_need);
+        n_w = min(s_count, static_cast<uint32_t>(kMaxSel));
+        int32_t v[kMaxSel / kRowThreads];
+#pragma unroll
+        for (int e = 0; e < kMaxSel / kRowThreads; ++e) {
+          const uint32_t ii = (kMaxSel / kRowThreads) * tid + e;
+          v[e] = ii < n_w ? bw[ii] : 0x7FFFFFFF;
+        }
+        __syncthreads();
+        block_bitonic<kMaxSel / kRowThreads>(v, bw, static_cast<int>(n_w), IntLess{});
+#pragma unroll
+        for (int e = 0; e < kMaxSel / kRowThreads; ++e) {
+          const uint32_t ii = (kMaxSel / kRowThreads) * tid + e;
+          if (ii < n_w) bw[ii] = v[e];
+        }
       }
-      n_keep = static_cast<int>(min(s_count, static_cast<uint32_t>(topk)));
+      __syncthreads();
+      // ---- merge the two ascending lists by rank
+      for (uint32_t i = tid; i < n_up; i += kRowThreads) {
+        const int32_t v = up[i];
+        const uint32_t rk = i + lower_bound_lds(bw, n_w, v);
+        if (rk < static_cast<uint32_t>(cap)) out[rk] = v;
+      }
+      for (uint32_t i = tid; i < n_w; i += kRowThreads) {
+        const int32_t v = bw[i];
+        const uint32_t rk = i + lower_bound_lds(up, n_up, v);
+        if (rk < static_cast<uint32_t>(cap)) out[rk] = v;
+      }
+      n_keep = n_up + n_w;
     }
   }
-  __syncthreads();
-  emit_row(tmp, reinterpret_cast<int32_t*>(sel_lh), n_keep, first, P,
-           idx_out + static_cast<size_t>(r) * cap, nsel_out + r, cap);
+  const int n_total = static_cast<int>(n_keep) + static_cast<int>(static_cast<int64_t>(P) - first + 1);
+  for (int i = static_cast<int>(n_keep) + tid; i < cap; i += kRowThreads)
+    out[i] = i < n_total ? static_cast<int32_t>(first + (i - static_cast<int>(n_keep))) : -1;
+  if (tid == 0) nsel_out[r] = n_total;
 }
 
 }  // namespace
