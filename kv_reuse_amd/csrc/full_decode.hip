@@ -242,110 +242,89 @@ __global__ __launch_bounds__(kWaves * 64, 2) void full_decode_split_kernel(
   }
 }
 
-// Level 1 of the split merge: grid (groups, kG, R), work-group (gi, h, r)
-// merges the kCmbGroup splits of group gi for head h.  All of its loads are
-// issued in one round.  It also clears the row's selection state.
-__global__ __launch_bounds__(256) void full_merge_kernel(
+// Merge of the splits, one work-group of 1024 threads per (head, row): the
+// maximum M of the split maxima, L = sum_s l_s 2^(m_s - M) in float64 (fixed
+// order), O = sum_s O_s 2^(m_s - M) / L (eight partial sums of 128 lanes,
+// then in order).  Writes the output row (bf16), lse (natural log, when
+// non-null), lse2 (float64, base 2) and the head's bound on log2 importance,
+// max_j s2_j - lse2 = -log2(L).  It also clears the row's selection state.
+constexpr int kCmbThreads = 1024;
+__global__ __launch_bounds__(kCmbThreads) void full_combine_kernel(
     const float* __restrict__ part_m, const double* __restrict__ part_l,
-    const float* __restrict__ part_o, int n_split, int n_groups, float* __restrict__ cmb_m,
-    double* __restrict__ cmb_l, float* __restrict__ cmb_o, uint32_t* __restrict__ hist,
-    RowInfo* __restrict__ info) {
-  __shared__ float sm[kCmbGroup];
-  __shared__ double sl[kCmbGroup];
-  __shared__ float half_o[kD];
-  const int gi = blockIdx.x, h = blockIdx.y, r = blockIdx.z;
-  const int tid = threadIdx.x;
-  const int d = tid & 127, hf = tid >> 7;
-  const int s0 = gi * kCmbGroup;
-  const int ns = min(kCmbGroup, n_split - s0);
-  const size_t rb = static_cast<size_t>(r) * n_split;
-  if (tid < ns) {
-    sm[tid] = part_m[(rb + s0 + tid) * kG + h];
-    sl[tid] = part_l[(rb + s0 + tid) * kG + h];
-  }
-  float ov[kCmbGroup / 2];
-  const float* po = part_o + ((rb + s0) * kG + h) * kD + d;
-#pragma unroll
-  for (int i = 0; i < kCmbGroup / 2; ++i) {
-    const int s = hf + 2 * i;
-    ov[i] = s < ns ? po[static_cast<size_t>(s) * kG * kD] : 0.f;
-  }
-  __syncthreads();
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, sm[s]);
-  float acc = 0.f;
-#pragma unroll
-  for (int i = 0; i < kCmbGroup / 2; ++i) {
-    const int s = hf + 2 * i;
-    if (s < ns && sm[s] != -INFINITY) acc += ov[i] * ldexpf(1.f, static_cast<int>(sm[s] - M));
-  }
-  if (hf == 1) half_o[d] = acc;
-  __syncthreads();
-  const size_t cb = (static_cast<size_t>(r) * kG + h) * n_groups + gi;
-  if (hf == 0) cmb_o[cb * kD + d] = acc + half_o[d];
-  if (tid == 0) {
-    double L = 0.0;
-    for (int s = 0; s < ns; ++s)
-      if (sm[s] != -INFINITY) L += sl[s] * ldexp(1.0, static_cast<int>(sm[s] - M));
-    cmb_m[cb] = M;
-    cmb_l[cb] = L;
-  }
-  // fresh selection state for this row (group 0 of each head clears a share)
-  if (gi == 0) {
-    for (int i = tid; i < kNB / kG; i += 256)
-      hist[static_cast<size_t>(r) * kNB + h * (kNB / kG) + i] = 0u;
-    if (h == 0 && tid == 0) info[r] = RowInfo{0u, 0u, 0u, 0u};
-  }
-}
-
-// Level 2: grid (kG, R): merge the group partials of one head in group order;
-// write the output row (bf16), lse (natural log), lse2 (float64, base 2) and
-// the row's bound on log2 importance for that head, max_j s2_j - lse2.
-__global__ __launch_bounds__(256) void full_finalize_kernel(
-    const float* __restrict__ cmb_m, const double* __restrict__ cmb_l,
-    const float* __restrict__ cmb_o, int n_groups, u16* __restrict__ out,
-    float* __restrict__ lse_out, double* __restrict__ lse2, float* __restrict__ ytop_h) {
-  __shared__ float sm[kCmbMaxGroups];
-  __shared__ double sl[kCmbMaxGroups];
-  __shared__ float half_o[kD];
+    const float* __restrict__ part_o, int n_split, u16* __restrict__ out,
+    float* __restrict__ lse_out, double* __restrict__ lse2, float* __restrict__ ytop_h,
+    uint32_t* __restrict__ hist, RowInfo* __restrict__ info) {
+  __shared__ float sm[kMaxSplits];
+  __shared__ float sf[kMaxSplits];      // 2^(m_s - M)
+  __shared__ double sl[kMaxSplits];
+  __shared__ float po[8][kD];
+  __shared__ float s_M;
+  __shared__ double s_L;
   const int h = blockIdx.x, r = blockIdx.y;
   const int tid = threadIdx.x;
-  const int d = tid & 127, hf = tid >> 7;
-  const size_t c0 = (static_cast<size_t>(r) * kG + h) * n_groups;
-  if (tid < n_groups) {
-    sm[tid] = cmb_m[c0 + tid];
-    sl[tid] = cmb_l[c0 + tid];
+  const int d = tid & (kD - 1), part = tid >> 7;
+  const size_t rb = static_cast<size_t>(r) * n_split;
+  for (int s2 = tid; s2 < n_split; s2 += kCmbThreads) {
+    sm[s2] = part_m[(rb + s2) * kG + h];
+    sl[s2] = part_l[(rb + s2) * kG + h];
   }
-  float o2[kCmbMaxGroups / 2];
+  // fresh selection state for this row (each head clears a share)
+  for (int i = tid; i < kNB / kG; i += kCmbThreads)
+    hist[static_cast<size_t>(r) * kNB + h * (kNB / kG) + i] = 0u;
+  if (h == 0 && tid == 0) info[r] = RowInfo{0u, 0u, 0u, 0u};
+  __syncthreads();
+  if (tid < 64) {
+    float M = -INFINITY;
+    for (int s2 = tid; s2 < n_split; s2 += 64) M = fmaxf(M, sm[s2]);
 #pragma unroll
-  for (int i = 0; i < kCmbMaxGroups / 2; ++i) {
-    const int g2 = hf + 2 * i;
-    o2[i] = g2 < n_groups ? cmb_o[(c0 + g2) * kD + d] : 0.f;
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    // L in a fixed order: lane-strided partial sums, then a fixed tree
+    double L = 0.0;
+    for (int s2 = tid; s2 < n_split; s2 += 64)
+      if (sm[s2] != -INFINITY) L += sl[s2] * ldexp(1.0, static_cast<int>(sm[s2] - M));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
+    if (tid == 0) {
+      s_M = M;
+      s_L = L;
+    }
   }
   __syncthreads();
-  float MM = -INFINITY;
-  for (int g2 = 0; g2 < n_groups; ++g2) MM = fmaxf(MM, sm[g2]);
-  double L = 0.0;
-  for (int g2 = 0; g2 < n_groups; ++g2)
-    if (sm[g2] != -INFINITY) L += sl[g2] * ldexp(1.0, static_cast<int>(sm[g2] - MM));
-  float o = 0.f;
-#pragma unroll
-  for (int i = 0; i < kCmbMaxGroups / 2; ++i) {
-    const int g2 = hf + 2 * i;
-    if (g2 < n_groups && sm[g2] != -INFINITY)
-      o += o2[i] * ldexpf(1.f, static_cast<int>(sm[g2] - MM));
-  }
-  if (hf == 1) half_o[d] = o;
+  const float M = s_M;
+  for (int s2 = tid; s2 < n_split; s2 += kCmbThreads)
+    sf[s2] = sm[s2] == -INFINITY ? 0.f : ldexpf(1.f, static_cast<int>(sm[s2] - M));
   __syncthreads();
-  if (hf == 0)
-    out[(static_cast<size_t>(r) * kG + h) * kD + d] =
-        f32_to_bf16_rne((o + half_o[d]) * static_cast<float>(1.0 / L));
-  if (tid == 0) {
-    const double l2 = static_cast<double>(MM) + log2(L);
-    lse2[static_cast<size_t>(r) * kG + h] = l2;
-    if (lse_out) lse_out[static_cast<size_t>(r) * kG + h] = static_cast<float>(l2 * M_LN2);
-    // every logit of this head is <= MM, so its base-2 log-probability is <= MM - lse2
-    ytop_h[static_cast<size_t>(r) * kG + h] = static_cast<float>(-log2(L));
+  // O: part p sums splits p, p + 8, ... (loads issued 8 at a time)
+  float acc = 0.f;
+  const float* po_base = part_o + (rb * kG + h) * kD + d;
+  for (int s0 = part; s0 < n_split; s0 += 8 * 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int s2 = s0 + 8 * u;
+      v[u] = s2 < n_split ? po_base[static_cast<size_t>(s2) * kG * kD] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int s2 = s0 + 8 * u;
+      if (s2 < n_split) acc += v[u] * sf[s2];
+    }
+  }
+  po[part][d] = acc;
+  __syncthreads();
+  if (part == 0) {
+    float o = 0.f;
+#pragma unroll
+    for (int p2 = 0; p2 < 8; ++p2) o += po[p2][d];
+    const double L = s_L;
+    out[(static_cast<size_t>(r) * kG + h) * kD + d] = f32_to_bf16_rne(o * static_cast<float>(1.0 / L));
+    if (d == 0) {
+      const double l2 = static_cast<double>(M) + log2(L);
+      lse2[static_cast<size_t>(r) * kG + h] = l2;
+      if (lse_out) lse_out[static_cast<size_t>(r) * kG + h] = static_cast<float>(l2 * M_LN2);
+      // every logit of this head is <= M, so its base-2 log-probability is <= M - lse2
+      ytop_h[static_cast<size_t>(r) * kG + h] = static_cast<float>(-log2(L));
+    }
   }
 }
 
@@ -422,23 +401,14 @@ hipError_t launch_full_decode_split(const Plan& p, const u16* q, const u16* k, c
 
 hipError_t launch_full_combine(const Plan& p, u16* out, float* lse, void* ws, hipStream_t st) {
   char* w = static_cast<char*>(ws);
-  hipLaunchKernelGGL(full_merge_kernel, dim3(p.cmb_groups, kG, p.R), dim3(256), 0, st,
+  hipLaunchKernelGGL(full_combine_kernel, dim3(kG, p.R), dim3(kCmbThreads), 0, st,
                      reinterpret_cast<const float*>(w + p.off_part_m),
                      reinterpret_cast<const double*>(w + p.off_part_l),
-                     reinterpret_cast<const float*>(w + p.off_part_o), p.n_split, p.cmb_groups,
-                     reinterpret_cast<float*>(w + p.off_cmb_m),
-                     reinterpret_cast<double*>(w + p.off_cmb_l),
-                     reinterpret_cast<float*>(w + p.off_cmb_o),
+                     reinterpret_cast<const float*>(w + p.off_part_o), p.n_split, out, lse,
+                     reinterpret_cast<double*>(w + p.off_lse2),
+                     reinterpret_cast<float*>(w + p.off_ytop),
                      reinterpret_cast<uint32_t*>(w + p.off_hist),
                      reinterpret_cast<RowInfo*>(w + p.off_info));
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(full_finalize_kernel, dim3(kG, p.R), dim3(256), 0, st,
-                     reinterpret_cast<const float*>(w + p.off_cmb_m),
-                     reinterpret_cast<const double*>(w + p.off_cmb_l),
-                     reinterpret_cast<const float*>(w + p.off_cmb_o), p.cmb_groups, out, lse,
-                     reinterpret_cast<double*>(w + p.off_lse2),
-                     reinterpret_cast<float*>(w + p.off_ytop));
   return hipGetLastError();
 }
 

@@ -55,11 +55,10 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
     const int64_t target = 1024;
     int64_t ns = ceil_div(target, R);
     ns = std::max<int64_t>(1, std::min<int64_t>(ns, ceil_div(q.S, 256)));
-    ns = std::min<int64_t>(ns, int64_t{kCmbGroup} * kCmbMaxGroups);
+    ns = std::min<int64_t>(ns, int64_t{kMaxSplits});
     int64_t kps = align_up(static_cast<size_t>(ceil_div(q.S, ns)), 128);
     q.kps = static_cast<int>(kps);
     q.n_split = static_cast<int>(ceil_div(q.S, kps));
-    q.cmb_groups = static_cast<int>(ceil_div(q.n_split, kCmbGroup));
   }
   // selection from given scores: ~256 work-groups over the rows, at most 16384
   // keys per work-group (the compaction keeps 64 keys per thread in bit masks)
@@ -102,10 +101,6 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
   q.off_part_l = take(decode ? nsplit_rows * kG * sizeof(double) : 0);
   q.off_part_o = take(decode ? nsplit_rows * kG * kD * sizeof(float) : 0);
   q.off_stmax = take(decode ? Rz * nst * kG * sizeof(float) : 0);
-  const size_t cmb = decode ? Rz * kG * q.cmb_groups : 0;
-  q.off_cmb_m = take(cmb * sizeof(float));
-  q.off_cmb_l = take(cmb * sizeof(double));
-  q.off_cmb_o = take(cmb * kD * sizeof(float));
   q.off_lse2 = take(Rz * kG * sizeof(double));
   q.off_ytop = take(Rz * kG * sizeof(float));
   q.off_hist = take(Rz * kNB * sizeof(uint32_t));

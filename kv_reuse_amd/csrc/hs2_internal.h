@@ -19,8 +19,7 @@ constexpr int kUncCap = 2048;    // near-threshold keys handled in LDS; more tak
 constexpr int kMaxSel = 4096;    // top_k + window limit (index list kept in LDS)
 constexpr int kSparseChunk = 128;  // selected keys per sparse work-group (4 waves x 32)
 constexpr float kYRange = 64.0f;   // log2 range below the row's top score that the bins span
-constexpr int kCmbGroup = 16;      // splits merged per work-group in level 1
-constexpr int kCmbMaxGroups = 64;  // level-1 groups merged in level 2
+constexpr int kMaxSplits = 1024;   // context splits per row (full layer, decode)
 
 typedef unsigned short u16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -48,9 +47,7 @@ struct Plan {
   double scale;
   // full attention (decode split kernel) and the merge of its splits
   int n_split, kps;
-  int cmb_groups;            // groups of 16 splits (level 1 of the merge)
   size_t off_part_m, off_part_l, off_part_o, off_stmax, off_lse2, off_ytop;
-  size_t off_cmb_m, off_cmb_l, off_cmb_o;
   // selection state shared by both selection paths
   size_t off_hist, off_info;
   // selection from given scores
@@ -112,14 +109,15 @@ hipError_t launch_sparse(const Plan& p, const u16* q, const u16* k, const u16* v
 __device__ __forceinline__ float bf16_bits_to_f32(u16 b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
+// float -> bfloat16, round to nearest even (gfx950 converts in hardware:
+// v_cvt_pk_bf16_f32)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u16 f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<u16>(u >> 16);
+  return __builtin_bit_cast(u16, static_cast<__bf16>(f));
 }
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16_rne(lo)) |
-         (static_cast<uint32_t>(f32_to_bf16_rne(hi)) << 16);
+  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 __device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);

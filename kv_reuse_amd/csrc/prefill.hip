@@ -89,6 +89,12 @@ __device__ __forceinline__ bf16x8 lds_k_operand(const u16* kt, int sub, int c, i
   return as_bf16x8(*reinterpret_cast<const u32x4*>(kt + (16 * sub + col) * kPPitch + 32 * c + 8 * grp));
 }
 
+// Make the compiler wait for a loaded operand here (an empty asm that reads
+// it), so that the load is not left outstanding into a loop.
+__device__ __forceinline__ void require_loaded(const bf16x8& x) {
+  asm volatile("" : : "v"(__builtin_bit_cast(u32x4, x)));
+}
+
 // Q^T as the B operand: column col of a query block = (token tok, head col & 7).
 __device__ __forceinline__ void load_q_block(const u16* __restrict__ qtok, int col, int grp,
                                              bf16x8 (&qb)[4]) {
@@ -143,6 +149,13 @@ __global__ __launch_bounds__(kPThreads, 2) void full_prefill_kernel(
   TileRegs regs;
   tile_gload<true>(regs, kr, vr, 0, p_last);
   tile_lstore<true>(regs, kt, vt);
+  // the query operands must have landed before the loop: inside it only the
+  // next tile's loads may be outstanding, or the first MFMAs of every tile
+  // would wait for them
+#pragma unroll
+  for (int qbk = 0; qbk < 2; ++qbk)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) require_loaded(qop[qbk][c]);
   __syncthreads();
   for (int it = 0; it < n_tiles; ++it) {
     const int64_t key0 = static_cast<int64_t>(it) * kPKeys;
@@ -162,22 +175,35 @@ __global__ __launch_bounds__(kPThreads, 2) void full_prefill_kernel(
         sacc[0][sub] = mfma_16x16x32(a, qop[0][c], sacc[0][sub]);
         sacc[1][sub] = mfma_16x16x32(a, qop[1][c], sacc[1][sub]);
       }
+    // only the last tiles of a work-group reach past some token's position
     const bool masked = key0 + kPKeys - 1 > p_first;
     float p[2][4][4];
 #pragma unroll
     for (int qbk = 0; qbk < 2; ++qbk) {
       float sv[4][4];
       float tmax = -INFINITY;
+      if (!masked) {
 #pragma unroll
-      for (int sub = 0; sub < 4; ++sub)
+        for (int sub = 0; sub < 4; ++sub)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float a = sacc[qbk][sub][i];
-          float s = fmaf(a, c2_hi, a * c2_lo);
-          if (masked && key0 + 16 * sub + 4 * grp + i > pcol[qbk]) s = -INFINITY;
-          sv[sub][i] = s;
-          tmax = fmaxf(tmax, s);
-        }
+          for (int i = 0; i < 4; ++i) {
+            const float a = sacc[qbk][sub][i];
+            sv[sub][i] = fmaf(a, c2_hi, a * c2_lo);
+            tmax = fmaxf(tmax, sv[sub][i]);
+          }
+      } else {
+        // key0 + off is visible to the column iff off <= P - key0
+        const int lim = static_cast<int>(min(static_cast<int64_t>(kPKeys), pcol[qbk] - key0));
+#pragma unroll
+        for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float a = sacc[qbk][sub][i];
+            const float s = fmaf(a, c2_hi, a * c2_lo);
+            sv[sub][i] = 16 * sub + 4 * grp + i <= lim ? s : -INFINITY;
+            tmax = fmaxf(tmax, sv[sub][i]);
+          }
+      }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
       // key 0 is visible to every token, so the running max is finite from the
@@ -330,6 +356,10 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_importance_kernel(
   TileRegs regs;
   tile_gload<false>(regs, kr, nullptr, 0, p_last);
   tile_lstore<false>(regs, kt, nullptr);
+#pragma unroll
+  for (int qbk = 0; qbk < 2; ++qbk)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) require_loaded(qop[qbk][c]);
   __syncthreads();
   const float ybase[2] = {s_ybase[jloc[0]], s_ybase[jloc[1]]};
   for (int it = 0; it < n_tiles; ++it) {

@@ -74,14 +74,36 @@ __global__ __launch_bounds__(NCT * 64) void sparse_kernel(
     for (int i = tid; i < kSub; i += blockDim.x)
       sidx[i] = i < n_here ? idx[static_cast<size_t>(r) * cap + sc + i] : -1;
     __syncthreads();
-    for (int pc = tid; pc < kSub * 16; pc += blockDim.x) {
-      const int key = pc >> 4, c16 = pc & 15;
-      // entries outside [0, S) (padding, or a malformed list) read row 0 / S-1
-      // instead of faulting; padding is masked out of the softmax below
-      const int j = sidx[key];
-      const size_t jj = j < 0 ? 0 : static_cast<size_t>(min(static_cast<int64_t>(j), S - 1));
-      *reinterpret_cast<u32x4*>(klds + key * kPitch + 8 * c16) = load_u32x4(kr + jj * kD + 8 * c16);
-      *reinterpret_cast<u32x4*>(vlds + key * kPitch + 8 * c16) = load_u32x4(vr + jj * kD + 8 * c16);
+    // every thread's 16-byte pieces of the sub-chunk, 8 (K, V) pairs at a
+    // time: all loads of a batch first, then its LDS stores, so a 256-thread
+    // work-group gathers the sub-chunk in one memory round trip
+    constexpr int kPieces = (kSub * 16 + NCT * 64 - 1) / (NCT * 64);
+    constexpr int kBatch = kPieces < 8 ? kPieces : 8;
+#pragma unroll
+    for (int u0 = 0; u0 < kPieces; u0 += kBatch) {
+      u32x4 kv_k[kBatch], kv_v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        // (pieces past the sub-chunk, when the thread count does not divide
+        // it, read piece 0 and are not stored)
+        const int pc0 = tid + (u0 + u) * NCT * 64;
+        const int pc = pc0 < kSub * 16 ? pc0 : 0;
+        const int key = pc >> 4, c16 = pc & 15;
+        // entries outside [0, S) (padding, or a malformed list) read row 0 /
+        // S-1 instead of faulting; padding is masked out of the softmax below
+        const int j = sidx[key];
+        const size_t jj = j < 0 ? 0 : static_cast<size_t>(min(static_cast<int64_t>(j), S - 1));
+        kv_k[u] = load_u32x4(kr + jj * kD + 8 * c16);
+        kv_v[u] = load_u32x4(vr + jj * kD + 8 * c16);
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int pc = tid + (u0 + u) * NCT * 64;
+        if (pc >= kSub * 16) continue;
+        const int key = pc >> 4, c16 = pc & 15;
+        *reinterpret_cast<u32x4*>(klds + key * kPitch + 8 * c16) = kv_k[u];
+        *reinterpret_cast<u32x4*>(vlds + key * kPitch + 8 * c16) = kv_v[u];
+      }
     }
     __syncthreads();
     for (int kb = 0; kb < n_here; kb += 32) {
