@@ -42,6 +42,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kTile = 32;       // keys per wave iteration
 constexpr int kVPitch = 136;    // u16 per V row in LDS: 272 bytes
+constexpr int kStageKeys = 4096;  // splits up to this many keys stage their maxima in LDS
 
 struct KVTile {
   bf16x8 ka[2][4];  // K as A operand: 2 sub-tiles of 16 keys x 4 chunks of 32 dims
@@ -99,9 +100,9 @@ __device__ __forceinline__ void tile_logits(const bf16x8 (&ka)[2][4], const bf16
 
 __device__ __forceinline__ void process_tile(const KVTile& t, SoftmaxState& st,
                                              const bf16x8 (&qb)[4], u16* __restrict__ vw,
-                                             float* __restrict__ stmax_row, int64_t t0,
-                                             int64_t key_end, int col, int grp, float c2_hi,
-                                             float c2_lo) {
+                                             float* __restrict__ stmax_row, int64_t st_base,
+                                             int64_t t0, int64_t key_end, int col, int grp,
+                                             float c2_hi, float c2_lo) {
   float sv[8];
   tile_logits(t.ka, qb, t0, key_end, grp, c2_hi, c2_lo, sv);
   // per-subtile (16 keys) maxima of each head: lanes of one head are col + 16*grp
@@ -111,9 +112,11 @@ __device__ __forceinline__ void process_tile(const KVTile& t, SoftmaxState& st,
   m1 = fmaxf(m1, __shfl_xor(m1, 16));
   m0 = fmaxf(m0, __shfl_xor(m0, 32));
   m1 = fmaxf(m1, __shfl_xor(m1, 32));
-  // subtile t0/16 + mt, head col: 64 contiguous bytes per tile (grp 0 and 1)
+  // subtile t0/16 + mt, head col: 64 contiguous bytes per tile (grp 0 and 1);
+  // stmax_row is either the row's global array or the work-group's LDS stage
+  // (then indexed from the split's first subtile)
   if (col < kG && grp < 2 && t0 + 16 * grp < key_end)
-    stmax_row[(t0 / 16 + grp) * kG + col] = grp == 0 ? m0 : m1;
+    stmax_row[(t0 / 16 + grp - st_base) * kG + col] = grp == 0 ? m0 : m1;
   // ---- online softmax (per head = per lane % 16)
   const float tm = fmaxf(m0, m1);
   const float m_new = fmaxf(st.m, ceilf(tm));
@@ -157,6 +160,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void full_decode_split_kernel(
   __shared__ __align__(16) unsigned char smem[kWaves * kTile * kVPitch * 2];
   __shared__ float sm_m[kWaves][kG];
   __shared__ double sm_l[kWaves][kG];
+  // the split's subtile maxima, written to HBM in one burst at the end (when
+  // the split is at most kStageKeys keys)
+  __shared__ __align__(16) float st_stage[kStageKeys / 16 * kG];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -169,6 +175,9 @@ __global__ __launch_bounds__(kWaves * 64, 2) void full_decode_split_kernel(
   const u16* kr = k + static_cast<size_t>(r) * S * kD;
   const u16* vr = v + static_cast<size_t>(r) * S * kD;
   float* stmax_row = stmax + static_cast<size_t>(r) * (Spad / 16) * kG;
+  const bool staged = kps <= kStageKeys;
+  float* st_dst = staged ? st_stage : stmax_row;
+  const int64_t st_base = staged ? key_begin / 16 : 0;
   u16* vw = reinterpret_cast<u16*>(smem) + wave * kTile * kVPitch;
 
   bf16x8 qb[4];
@@ -190,13 +199,13 @@ __global__ __launch_bounds__(kWaves * 64, 2) void full_decode_split_kernel(
       int64_t t1 = t0 + stride;
       bool more = t1 < key_end;
       if (more) load_tile(tb, kr, vr, t1, key_last, col, grp);
-      process_tile(ta, st, qb, vw, stmax_row, t0, key_end, col, grp, c2_hi, c2_lo);
+      process_tile(ta, st, qb, vw, st_dst, st_base, t0, key_end, col, grp, c2_hi, c2_lo);
       if (!more) break;
       t0 = t1;
       t1 = t0 + stride;
       more = t1 < key_end;
       if (more) load_tile(ta, kr, vr, t1, key_last, col, grp);
-      process_tile(tb, st, qb, vw, stmax_row, t0, key_end, col, grp, c2_hi, c2_lo);
+      process_tile(tb, st, qb, vw, st_dst, st_base, t0, key_end, col, grp, c2_hi, c2_lo);
       if (!more) break;
       t0 = t1;
     }
@@ -204,7 +213,14 @@ __global__ __launch_bounds__(kWaves * 64, 2) void full_decode_split_kernel(
   st.l += __shfl_xor(st.l, 16);
   st.l += __shfl_xor(st.l, 32);
 
-  __syncthreads();  // all waves done with their V tiles
+  __syncthreads();  // all waves done with their V tiles (and the stage)
+  if (staged) {
+    // subtiles [key_begin/16, ceil(key_end/16)) of this split, 16 bytes a thread
+    const int n4 = static_cast<int>((key_end - key_begin + 15) / 16) * kG / 4;
+    float* dst = stmax_row + (key_begin / 16) * kG;
+    for (int i = threadIdx.x; i < n4; i += blockDim.x)
+      *reinterpret_cast<f32x4*>(dst + 4 * i) = *reinterpret_cast<const f32x4*>(st_stage + 4 * i);
+  }
   float* sm_o = reinterpret_cast<float*>(smem);  // [kWaves][kG][kD]
   if (col < kG) {
     if (grp == 0) {
