@@ -42,7 +42,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kTile = 32;       // keys per wave iteration
 constexpr int kVPitch = 136;    // u16 per V row in LDS: 272 bytes
-constexpr int kStageKeys = 4096;  // splits up to this many keys stage their maxima in LDS
+constexpr int kStageKeys = 16384;  // splits up to this many keys stage their maxima in LDS
 
 struct KVTile {
   bf16x8 ka[2][4];  // K as A operand: 2 sub-tiles of 16 keys x 4 chunks of 32 dims

@@ -50,9 +50,11 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
   q.n_layers = n_layers;
   q.scale = sh->scale;
 
-  // full attention, decode: enough splits for ~4 work-groups per CU
+  // full attention, decode: about one work-group per compute unit, so that
+  // the stream runs in one round with no tail (the 256 CUs of an MI355X; a
+  // count that leaves some CUs a second work-group streams much slower)
   {
-    const int64_t target = 1024;
+    const int64_t target = kSplitTarget;
     int64_t ns = ceil_div(target, R);
     ns = std::max<int64_t>(1, std::min<int64_t>(ns, ceil_div(q.S, 256)));
     ns = std::min<int64_t>(ns, int64_t{kMaxSplits});

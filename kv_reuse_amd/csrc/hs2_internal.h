@@ -20,6 +20,7 @@ constexpr int kMaxSel = 4096;    // top_k + window limit (index list kept in LDS
 constexpr int kSparseChunk = 128;  // selected keys per sparse work-group (4 waves x 32)
 constexpr float kYRange = 64.0f;   // log2 range below the row's top score that the bins span
 constexpr int kMaxSplits = 1024;   // context splits per row (full layer, decode)
+constexpr int kSplitTarget = 256;  // decode full layer: work-groups over all rows (MI355X CUs)
 
 typedef unsigned short u16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
