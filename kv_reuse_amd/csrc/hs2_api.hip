@@ -79,9 +79,9 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
     hc = std::min<int64_t>(std::max<int64_t>(hc, 256), 8192);
     q.hs_chunk = static_cast<int>(hc);
     q.hs_nchunk = static_cast<int>(ceil_div(nst, hc));
-    // candidate scoring: about 512 work-groups (all resident at once), whole
-    // rounds of kScoreRound subtiles, at most kMaxChunks chunks per row
-    int64_t sc = align_up(static_cast<size_t>(ceil_div(nst * R, 512)), kScoreRound);
+    // candidate scoring: about 1024 work-groups (four per CU, all resident at
+    // once), whole rounds of kScoreRound subtiles, at most kMaxChunks per row
+    int64_t sc = align_up(static_cast<size_t>(ceil_div(nst * R, 1024)), kScoreRound);
     sc = std::max<int64_t>(sc, kScoreRound);
     sc = std::max<int64_t>(sc, static_cast<int64_t>(align_up(static_cast<size_t>(ceil_div(nst, kMaxChunks)), kScoreRound)));
     q.sc_chunk = static_cast<int>(sc);

@@ -618,14 +618,17 @@ __global__ __launch_bounds__(kThreads) void subtile_hist_kernel(
 //    - 1): every key that can be selected lies in one;
 //  * a wave takes a candidate subtile and computes its 16 keys' importance in
 //    float64 on MFMA (D = K . Q^T, 16 keys x 16 heads of which 8 are used; the
-//    bf16 products are exact in float64), staged in LDS;
+//    bf16 products are exact in float64), staged in LDS kStageSub subtiles at
+//    a time;
 //  * keys whose bin is below that same bound can never be selected and are
 //    dropped; the others are appended to the work-group's own region of the
 //    row's candidate list in ascending key order, and counted in the row's
 //    candidate histogram.  The region's length goes to cand_cnt.
-// The loads that do not depend on each other (histogram, first bounds, query
-// row) are issued together at the start.
-__global__ __launch_bounds__(kThreads) void subtile_score_kernel(
+// The query operand stays packed (bf16) in registers and is widened at each
+// step, so that four work-groups fit a CU and the whole grid is resident at
+// once.
+constexpr int kStageSub = 64;   // candidate subtiles staged per pass
+__global__ __launch_bounds__(kThreads, 4) void subtile_score_kernel(
     const float* __restrict__ stmax, const double* __restrict__ lse2,
     const float* __restrict__ ytop_h, const uint32_t* __restrict__ hist,
     uint32_t* __restrict__ hist_c, const u16* __restrict__ q, const u16* __restrict__ k,
@@ -634,7 +637,7 @@ __global__ __launch_bounds__(kThreads) void subtile_score_kernel(
     double c2) {
   __shared__ uint32_t lh[kNB];
   __shared__ int32_t s_list[kScoreRound];
-  __shared__ double stage_y[kScoreRound * kSubKeys];
+  __shared__ double stage_y[kStageSub * kSubKeys];
   __shared__ float lse2f[kG];
   __shared__ float s_ybase;
   __shared__ int s_lo;
@@ -668,11 +671,14 @@ __global__ __launch_bounds__(kThreads) void subtile_score_kernel(
     mx[0] = ld ? *reinterpret_cast<const f32x4*>(stmax_row + st * kG) : f32x4{0.f, 0.f, 0.f, 0.f};
     mx[1] = ld ? *reinterpret_cast<const f32x4*>(stmax_row + st * kG + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  // the B operand, packed bf16: head col (zero for the padding heads),
+  // dims 32*grp + 8c .. +8, widened exactly at each MFMA step
   u32x4 qraw[4];
   {
     const u16* qr = q + static_cast<size_t>(r) * kG * kD + (col & 7) * kD + 32 * grp;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) qraw[c] = load_u32x4(qr + 8 * c);
+    for (int c = 0; c < 4; ++c)
+      qraw[c] = col < kG ? load_u32x4(qr + 8 * c) : u32x4{0u, 0u, 0u, 0u};
   }
   const double l2 = col < kG ? lse2[static_cast<size_t>(r) * kG + col] : 0.0;
   if (tid < kG) lse2f[tid] = static_cast<float>(lse2[static_cast<size_t>(r) * kG + tid]);
@@ -691,16 +697,6 @@ __global__ __launch_bounds__(kThreads) void subtile_score_kernel(
 #pragma unroll
   for (int h = 0; h < kG; ++h) l2v[h] = lse2f[h];
   for (int i = tid; i < kNB; i += kThreads) lh[i] = 0u;   // now the candidate histogram
-  double qd[32];
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const uint32_t word = qraw[c][t >> 1];
-      const double qv = static_cast<double>(
-          __uint_as_float((t & 1) ? (word & 0xFFFF0000u) : (word << 16)));
-      qd[8 * c + t] = col < kG ? qv : 0.0;
-    }
   const int b = r / (T * Hkv);
   const int g = r % Hkv;
   const u16* kr = k + (static_cast<size_t>(b) * Hkv + g) * static_cast<size_t>(S) * kD;
@@ -734,76 +730,89 @@ __global__ __launch_bounds__(kThreads) void subtile_score_kernel(
     const uint32_t n_local = s_base[2];
     if (cand) s_list[o_list] = static_cast<int32_t>(st);   // ascending: slots follow thread order
     __syncthreads();
-    // ---- float64 importance of the candidates' keys, one subtile per wave
-    auto load_sub = [&](uint32_t i, u32x4 (&ka)[4]) {
-      int64_t key = static_cast<int64_t>(s_list[i]) * kSubKeys + col;
-      key = key < S - 1 ? key : S - 1;
+    for (uint32_t p0 = 0; p0 < n_local; p0 += kStageSub) {
+      const uint32_t np = min(static_cast<uint32_t>(kStageSub), n_local - p0);
+      // ---- float64 importance of the pass's candidates, one subtile per wave
+      auto load_sub = [&](uint32_t i, u32x4 (&ka)[4]) {
+        int64_t key = static_cast<int64_t>(s_list[p0 + i]) * kSubKeys + col;
+        key = key < S - 1 ? key : S - 1;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) ka[c] = load_u32x4(kr + key * kD + 32 * grp + 8 * c);
-    };
-    u32x4 ka_cur[4], ka_nxt[4];
-    if (static_cast<uint32_t>(wave) < n_local) load_sub(wave, ka_cur);
-    for (uint32_t i = wave; i < n_local; i += kThreads / 64) {
-      if (i + kThreads / 64 < n_local) load_sub(i + kThreads / 64, ka_nxt);
-      // four independent accumulation chains (one per 8-dim slice of the
-      // lane's 32 dims), summed at the end
-      f64x4 part[4];
+        for (int c = 0; c < 4; ++c) ka[c] = load_u32x4(kr + key * kD + 32 * grp + 8 * c);
+      };
+      u32x4 ka_cur[4], ka_nxt[4];
+      if (static_cast<uint32_t>(wave) < np) load_sub(wave, ka_cur);
+      for (uint32_t i = wave; i < np; i += kThreads / 64) {
+        if (i + kThreads / 64 < np) load_sub(i + kThreads / 64, ka_nxt);
+        // the widened query (32 doubles) must not be hoisted out of this loop
+        // and kept live: mark the packed operand as redefined here
 #pragma unroll
-      for (int c = 0; c < 4; ++c) part[c] = f64x4{0.0, 0.0, 0.0, 0.0};
+        for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(qraw[c]));
+        // four independent accumulation chains (one per 8-dim slice of the
+        // lane's 32 dims), summed at the end
+        f64x4 part[4];
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
+        for (int c = 0; c < 4; ++c) part[c] = f64x4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const uint32_t word = ka_cur[c][t >> 1];
-          const double kv = static_cast<double>(
-              __uint_as_float((t & 1) ? (word & 0xFFFF0000u) : (word << 16)));
-          part[c] = __builtin_amdgcn_mfma_f64_16x16x4f64(kv, qd[8 * c + t], part[c], 0, 0, 0);
+        for (int t = 0; t < 8; ++t) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const uint32_t word = ka_cur[c][t >> 1];
+            const double kv = static_cast<double>(
+                __uint_as_float((t & 1) ? (word & 0xFFFF0000u) : (word << 16)));
+            const uint32_t qw = qraw[c][t >> 1];
+            const double qv = static_cast<double>(
+                __uint_as_float((t & 1) ? (qw & 0xFFFF0000u) : (qw << 16)));
+            part[c] = __builtin_amdgcn_mfma_f64_16x16x4f64(kv, qv, part[c], 0, 0, 0);
+          }
+          // keep each step's operands short-lived (register pressure decides
+          // how many work-groups share a CU)
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        const f64x4 acc = (part[0] + part[1]) + (part[2] + part[3]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) ka_cur[c] = ka_nxt[c];
+        // register e holds key grp + 4e against head col
+        double y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          double v = col < kG ? c2 * acc[e] - l2 : -INFINITY;
+          v = fmax(v, __shfl_xor(v, 1));
+          v = fmax(v, __shfl_xor(v, 2));
+          v = fmax(v, __shfl_xor(v, 4));
+          y[e] = v;
+        }
+        if (col < 4)
+          stage_y[i * kSubKeys + grp + 4 * col] =
+              col == 0 ? y[0] : col == 1 ? y[1] : col == 2 ? y[2] : y[3];
+      }
+      __syncthreads();
+      // ---- keep the keys that can still be selected, in order (thread t:
+      // the 16 keys of the pass's t-th candidate subtile)
+      uint32_t keep = 0;
+      int64_t key0 = 0;
+      if (static_cast<uint32_t>(tid) < np) {
+        key0 = static_cast<int64_t>(s_list[p0 + tid]) * kSubKeys;
+#pragma unroll
+        for (int e = 0; e < kSubKeys; ++e) {
+          const double yy = stage_y[tid * kSubKeys + e];
+          const bool ok = key0 + e < first && cand_bin(yy, ybase) >= lo_bin;
+          keep |= static_cast<uint32_t>(ok) << e;
         }
       }
-      const f64x4 acc = (part[0] + part[1]) + (part[2] + part[3]);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) ka_cur[c] = ka_nxt[c];
-      // register e holds key grp + 4e against head col
-      double y[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        double v = col < kG ? c2 * acc[e] - l2 : -INFINITY;
-        v = fmax(v, __shfl_xor(v, 1));
-        v = fmax(v, __shfl_xor(v, 2));
-        v = fmax(v, __shfl_xor(v, 4));
-        y[e] = v;
-      }
-      if (col < 4)
-        stage_y[i * kSubKeys + grp + 4 * col] =
-            col == 0 ? y[0] : col == 1 ? y[1] : col == 2 ? y[2] : y[3];
-    }
-    __syncthreads();
-    // ---- keep the keys that can still be selected, in order (thread t: the
-    // 16 keys of the round's t-th candidate subtile)
-    uint32_t keep = 0;
-    int64_t key0 = 0;
-    if (static_cast<uint32_t>(tid) < n_local) {
-      key0 = static_cast<int64_t>(s_list[tid]) * kSubKeys;
-#pragma unroll
-      for (int e = 0; e < kSubKeys; ++e) {
+      uint32_t o_keep;
+      reserve_two(__popc(keep), 0u, nullptr, nullptr, s_cnt, s_base, o_keep, o_dummy);
+      o_keep += written;
+      written += s_base[2];
+      for (uint32_t m = keep; m; m &= m - 1) {
+        const int e = __builtin_ctz(m);
         const double yy = stage_y[tid * kSubKeys + e];
-        const bool ok = key0 + e < first && cand_bin(yy, ybase) >= lo_bin;
-        keep |= static_cast<uint32_t>(ok) << e;
+        cy[o_keep] = yy;
+        ci[o_keep] = static_cast<int32_t>(key0 + e);
+        atomicAdd(&lh[cand_bin(yy, ybase)], 1u);
+        ++o_keep;
       }
+      __syncthreads();   // stage_y is reused by the next pass
     }
-    uint32_t o_keep;
-    reserve_two(__popc(keep), 0u, nullptr, nullptr, s_cnt, s_base, o_keep, o_dummy);
-    o_keep += written;
-    written += s_base[2];
-    for (uint32_t m = keep; m; m &= m - 1) {
-      const int e = __builtin_ctz(m);
-      const double yy = stage_y[tid * kSubKeys + e];
-      cy[o_keep] = yy;
-      ci[o_keep] = static_cast<int32_t>(key0 + e);
-      atomicAdd(&lh[cand_bin(yy, ybase)], 1u);
-      ++o_keep;
-    }
-    __syncthreads();   // s_list and stage_y are reused by the next round
   }
   for (int i = tid; i < kNB; i += kThreads)
     if (lh[i]) atomicAdd(&hist_c[static_cast<size_t>(r) * kNB + i], lh[i]);
