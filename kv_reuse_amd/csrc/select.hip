@@ -842,7 +842,7 @@ __device__ __forceinline__ uint32_t wave_or(uint32_t v) {
 // the list; the first sweep stays in registers.
 
 constexpr int kSelThreads = 1024;
-constexpr int kPerThr = 8;
+constexpr int kPerThr = 2;
 constexpr int kSweep = kSelThreads * kPerThr;
 
 struct SelEntry {
@@ -1101,7 +1101,10 @@ __global__ __launch_bounds__(kSelThreads) void row_select_kernel(
       if (kh > thr || (incl && kh == thr)) sel = 1;
       else if (kh == thr) tie = 1;
     };
-    uint32_t tie_seen = 0, written = 0;
+    // output position of an entry = selected entries before it + kept ties
+    // before it, where the kept ties are the first nd_t ties: one block scan
+    // of both counts gives both prefixes
+    uint32_t sel_seen = 0, tie_seen = 0;
     for (int sw = 0; sw < n_sweeps; ++sw) {
       SelEntry e;
       sweep(sw, e);
@@ -1113,40 +1116,27 @@ __global__ __launch_bounds__(kSelThreads) void row_select_kernel(
         ns += sl;
         nt += tl;
       }
-      uint32_t o_tie, o_dummy;
-      reserve_two(nt, 0u, nullptr, nullptr, s_cnt, s_base, o_tie, o_dummy);
+      uint32_t o_sel, o_tie;
+      reserve_two(ns, nt, nullptr, nullptr, s_cnt, s_base, o_sel, o_tie);
+      o_sel += sel_seen;
       o_tie += tie_seen;
-      tie_seen += s_base[2];
-      // ties take the first nd_t in list order; count them into the selection
-      uint32_t keep_tie = 0;
+      sel_seen += s_base[2];
+      tie_seen += s_base[3];
 #pragma unroll
       for (int u = 0; u < kPerThr; ++u) {
         uint32_t sl, tl;
         pick(e, u, sl, tl);
-        if (tl) {
-          keep_tie += o_tie < nd_t;
-          ++o_tie;
-        }
-      }
-      uint32_t o_out;
-      reserve_two(ns + keep_tie, 0u, nullptr, nullptr, s_cnt, s_base, o_out, o_dummy);
-      o_out += written;
-      written += s_base[2];
-      o_tie -= nt;   // rewind to this thread's first tie rank
-#pragma unroll
-      for (int u = 0; u < kPerThr; ++u) {
-        uint32_t sl, tl;
-        pick(e, u, sl, tl);
-        if (tl) {
-          sl = o_tie < nd_t;
-          ++o_tie;
-        }
         if (sl) {
-          if (o_out < static_cast<uint32_t>(cap)) out[o_out] = e.j[u];
-          ++o_out;
+          const uint32_t at = o_sel + min(o_tie, nd_t);
+          if (at < static_cast<uint32_t>(cap)) out[at] = e.j[u];
+          ++o_sel;
+        } else if (tl) {
+          if (o_tie < nd_t && o_sel + o_tie < static_cast<uint32_t>(cap)) out[o_sel + o_tie] = e.j[u];
+          ++o_tie;
         }
       }
     }
+    const uint32_t written = sel_seen + min(tie_seen, nd_t);
     n_keep = written;
   }
   __syncthreads();
