@@ -36,7 +36,12 @@ namespace hs2 {
 namespace {
 
 constexpr int kPThreads = 256;
-constexpr int kPTok = 16;       // chunk tokens per work-group (attention)
+constexpr int kPTok = 16;       // chunk tokens per work-group (importance pass)
+// Attention: query blocks per wave.  Two keep the kernel at 244 VGPRs and two
+// work-groups per CU; three or four halve the LDS operand reads per MFMA but
+// drop to one wave per SIMD, and then measured 45-60% slower on the 4K-token
+// chunk over 128K keys.
+constexpr int kPrefillQB = 2;
 constexpr int kPKeys = 64;      // keys per tile
 constexpr int kPPitch = 136;    // u16 per K/V row in LDS (272 bytes)
 
@@ -103,8 +108,11 @@ __device__ __forceinline__ void load_q_block(const u16* __restrict__ qtok, int c
   for (int c = 0; c < 4; ++c) qb[c] = as_bf16x8(load_u32x4(p + 32 * c));
 }
 
-// grid: B * Hkv * ceil(T / 16) work-groups of 256 threads.
-__global__ __launch_bounds__(kPThreads, 2) void full_prefill_kernel(
+// grid: B * Hkv * ceil(T / (8 * QB)) work-groups of 256 threads; each wave
+// owns QB query blocks (2 QB tokens), so every K/V operand read from LDS
+// serves 16 QB query columns.
+template <int QB>
+__global__ __launch_bounds__(kPThreads, QB <= 2 ? 2 : 1) void full_prefill_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     u16* __restrict__ out, float* __restrict__ lse_out, double* __restrict__ lse2,
     float* __restrict__ ytop_h, int64_t S, int T, int Hkv, int n_tblk, float c2_hi,
@@ -122,29 +130,33 @@ __global__ __launch_bounds__(kPThreads, 2) void full_prefill_kernel(
   const u16* kr = k + static_cast<size_t>(bg) * S * kD;
   const u16* vr = v + static_cast<size_t>(bg) * S * kD;
   const int64_t pos0 = S - T;                      // position of chunk token 0
-  // this lane's two columns: query block qbk covers tokens 4*wave + 2*qbk + {0,1}
-  int64_t pcol[2];
-  bf16x8 qop[2][4];
+  constexpr int kTok = 8 * QB;                     // chunk tokens per work-group
+  // this lane's columns: query block qbk covers tokens 2*QB*wave + 2*qbk + {0,1}
+  int64_t pcol[QB];
+  bf16x8 qop[QB][4];
 #pragma unroll
-  for (int qbk = 0; qbk < 2; ++qbk) {
-    int t = tb * kPTok + 4 * wave + 2 * qbk + (col >> 3);
+  for (int qbk = 0; qbk < QB; ++qbk) {
+    int t = tb * kTok + 2 * QB * wave + 2 * qbk + (col >> 3);
     t = t < T ? t : T - 1;                         // past the chunk: repeat the last token
     pcol[qbk] = pos0 + t;
     load_q_block(q + (static_cast<size_t>(b) * T + t) * Hq * kD + static_cast<size_t>(g) * kG * kD,
                  col, grp, qop[qbk]);
   }
-  const int t_last = min(T - 1, tb * kPTok + kPTok - 1);
-  const int64_t p_first = pos0 + tb * kPTok;       // smallest position in the work-group
+  const int t_last = min(T - 1, tb * kTok + kTok - 1);
+  const int64_t p_first = pos0 + tb * kTok;        // smallest position in the work-group
   const int64_t p_last = pos0 + t_last;
   const int n_tiles = static_cast<int>((p_last + kPKeys) / kPKeys);
 
-  f32x4 o[2][8];
+  f32x4 o[QB][8];
+  float m[QB];
+  double l[QB];
 #pragma unroll
-  for (int qbk = 0; qbk < 2; ++qbk)
+  for (int qbk = 0; qbk < QB; ++qbk) {
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) o[qbk][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[2] = {-INFINITY, -INFINITY};
-  double l[2] = {0.0, 0.0};
+    m[qbk] = -INFINITY;
+    l[qbk] = 0.0;
+  }
 
   TileRegs regs;
   tile_gload<true>(regs, kr, vr, 0, p_last);
@@ -153,7 +165,7 @@ __global__ __launch_bounds__(kPThreads, 2) void full_prefill_kernel(
   // next tile's loads may be outstanding, or the first MFMAs of every tile
   // would wait for them
 #pragma unroll
-  for (int qbk = 0; qbk < 2; ++qbk)
+  for (int qbk = 0; qbk < QB; ++qbk)
 #pragma unroll
     for (int c = 0; c < 4; ++c) require_loaded(qop[qbk][c]);
   __syncthreads();
@@ -161,10 +173,10 @@ __global__ __launch_bounds__(kPThreads, 2) void full_prefill_kernel(
     const int64_t key0 = static_cast<int64_t>(it) * kPKeys;
     const bool more = it + 1 < n_tiles;
     if (more) tile_gload<true>(regs, kr, vr, key0 + kPKeys, p_last);
-    // ---- S^T: 4 key subtiles x 2 query blocks
-    f32x4 sacc[2][4];
+    // ---- S^T: 4 key subtiles x QB query blocks
+    f32x4 sacc[QB][4];
 #pragma unroll
-    for (int qbk = 0; qbk < 2; ++qbk)
+    for (int qbk = 0; qbk < QB; ++qbk)
 #pragma unroll
       for (int sub = 0; sub < 4; ++sub) sacc[qbk][sub] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -172,14 +184,15 @@ __global__ __launch_bounds__(kPThreads, 2) void full_prefill_kernel(
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const bf16x8 a = lds_k_operand(kt, sub, c, col, grp);
-        sacc[0][sub] = mfma_16x16x32(a, qop[0][c], sacc[0][sub]);
-        sacc[1][sub] = mfma_16x16x32(a, qop[1][c], sacc[1][sub]);
+#pragma unroll
+        for (int qbk = 0; qbk < QB; ++qbk)
+          sacc[qbk][sub] = mfma_16x16x32(a, qop[qbk][c], sacc[qbk][sub]);
       }
     // only the last tiles of a work-group reach past some token's position
     const bool masked = key0 + kPKeys - 1 > p_first;
-    float p[2][4][4];
+    float p[QB][4][4];
 #pragma unroll
-    for (int qbk = 0; qbk < 2; ++qbk) {
+    for (int qbk = 0; qbk < QB; ++qbk) {
       float sv[4][4];
       float tmax = -INFINITY;
       if (!masked) {
@@ -228,9 +241,9 @@ __global__ __launch_bounds__(kPThreads, 2) void full_prefill_kernel(
     // ---- O^T += V^T . P^T over two k-steps of 32 keys
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 pb[2];
+      bf16x8 pb[QB];
 #pragma unroll
-      for (int qbk = 0; qbk < 2; ++qbk) {
+      for (int qbk = 0; qbk < QB; ++qbk) {
         const u32x4 pp{pack_bf16x2(p[qbk][2 * ks][0], p[qbk][2 * ks][1]),
                        pack_bf16x2(p[qbk][2 * ks][2], p[qbk][2 * ks][3]),
                        pack_bf16x2(p[qbk][2 * ks + 1][0], p[qbk][2 * ks + 1][1]),
@@ -240,8 +253,8 @@ __global__ __launch_bounds__(kPThreads, 2) void full_prefill_kernel(
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) {
         const bf16x8 a = lds_vt_operand(vt + 32 * ks * kPPitch, kPPitch, nb, col, grp);
-        o[0][nb] = mfma_16x16x32(a, pb[0], o[0][nb]);
-        o[1][nb] = mfma_16x16x32(a, pb[1], o[1][nb]);
+#pragma unroll
+        for (int qbk = 0; qbk < QB; ++qbk) o[qbk][nb] = mfma_16x16x32(a, pb[qbk], o[qbk][nb]);
       }
     }
     __syncthreads();               // every wave is done with this tile
@@ -252,11 +265,11 @@ __global__ __launch_bounds__(kPThreads, 2) void full_prefill_kernel(
   }
   // ---- epilogue: normalise, write out and the row statistics
 #pragma unroll
-  for (int qbk = 0; qbk < 2; ++qbk) {
+  for (int qbk = 0; qbk < QB; ++qbk) {
     double L = l[qbk];
     L += __shfl_xor(L, 16);
     L += __shfl_xor(L, 32);
-    const int t = tb * kPTok + 4 * wave + 2 * qbk + (col >> 3);
+    const int t = tb * kTok + 2 * QB * wave + 2 * qbk + (col >> 3);
     if (t >= T) continue;
     const int h = col & 7;
     const float inv = static_cast<float>(1.0 / L);
@@ -439,10 +452,11 @@ hipError_t launch_full_prefill(const Plan& p, const u16* q, const u16* k, const 
   const double c2 = p.scale * 1.4426950408889634;  // scale * log2(e)
   const float c2_hi = static_cast<float>(c2);
   const float c2_lo = static_cast<float>(c2 - static_cast<double>(c2_hi));
-  const int n_tblk = (p.T + kPTok - 1) / kPTok;
+  constexpr int QB = kPrefillQB;
+  const int n_tblk = (p.T + 8 * QB - 1) / (8 * QB);
   const int n_wg = p.B * p.Hkv * n_tblk;
-  hipLaunchKernelGGL(full_prefill_kernel, dim3(n_wg), dim3(kPThreads), 0, st, q, k, v, out, lse,
-                     reinterpret_cast<double*>(w + p.off_lse2),
+  hipLaunchKernelGGL(full_prefill_kernel<QB>, dim3(n_wg), dim3(kPThreads), 0, st, q, k, v, out,
+                     lse, reinterpret_cast<double*>(w + p.off_lse2),
                      reinterpret_cast<float*>(w + p.off_ytop), p.S, p.T, p.Hkv, n_tblk, c2_hi,
                      c2_lo);
   return hipGetLastError();
