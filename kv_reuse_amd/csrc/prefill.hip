@@ -43,7 +43,12 @@ constexpr int kPTok = 16;       // chunk tokens per work-group (importance pass)
 // chunk over 128K keys.
 constexpr int kPrefillQB = 2;
 constexpr int kPKeys = 64;      // keys per tile
-constexpr int kPPitch = 136;    // u16 per K/V row in LDS (272 bytes)
+// LDS row pitches, in u16.  K rows advance by 4 banks (68 dwords), so the
+// 16-byte operand reads of 8 or 16 consecutive rows cover every bank once; V
+// rows advance by 8 banks (72 dwords), so the transposing 8-byte reads (4 rows
+// x 4 consecutive units per 16 lanes, 8 rows per 32) do.
+constexpr int kPPitch = 136;
+constexpr int kPVPitch = 144;
 
 __device__ __forceinline__ int xcd_linear(int id, int n) {
   // hardware dispatch sends work-group id to XCD id % 8; renumber so that XCD x
@@ -83,7 +88,7 @@ __device__ __forceinline__ void tile_lstore(const TileRegs& r, u16* kt, u16* vt)
 #pragma unroll
   for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(kd + 8 * c) = r.k[c];
   if (kWithV) {
-    u16* vd = vt + (tid >> 2) * kPPitch + 32 * (tid & 3);
+    u16* vd = vt + (tid >> 2) * kPVPitch + 32 * (tid & 3);
 #pragma unroll
     for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(vd + 8 * c) = r.v[c];
   }
@@ -118,7 +123,7 @@ __global__ __launch_bounds__(kPThreads, QB <= 2 ? 2 : 1) void full_prefill_kerne
     float* __restrict__ ytop_h, int64_t S, int T, int Hkv, int n_tblk, float c2_hi,
     float c2_lo) {
   __shared__ __align__(16) u16 kt[kPKeys * kPPitch];
-  __shared__ __align__(16) u16 vt[kPKeys * kPPitch];
+  __shared__ __align__(16) u16 vt[kPKeys * kPVPitch];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
@@ -190,37 +195,42 @@ __global__ __launch_bounds__(kPThreads, QB <= 2 ? 2 : 1) void full_prefill_kerne
       }
     // only the last tiles of a work-group reach past some token's position
     const bool masked = key0 + kPKeys - 1 > p_first;
+    // The running max is taken over the raw dot products (the scale is
+    // positive, and the rounded scaling is monotonic), and each exponent is
+    // a * c2 - m formed by two fmas: the product a * c2_hi and the shift by
+    // the integer m are exact inside the first, so only small values round.
     float p[QB][4][4];
 #pragma unroll
     for (int qbk = 0; qbk < QB; ++qbk) {
       float sv[4][4];
-      float tmax = -INFINITY;
+      float amax = -INFINITY;
       if (!masked) {
 #pragma unroll
         for (int sub = 0; sub < 4; ++sub)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float a = sacc[qbk][sub][i];
-            sv[sub][i] = fmaf(a, c2_hi, a * c2_lo);
-            tmax = fmaxf(tmax, sv[sub][i]);
+            sv[sub][i] = sacc[qbk][sub][i];
+            amax = fmaxf(amax, sv[sub][i]);
           }
       } else {
-        // key0 + off is visible to the column iff off <= P - key0
+        // key0 + off is visible to the column iff off <= P - key0; a hidden
+        // key gets a large finite negative product (not -inf, which the
+        // second fma would turn into NaN when c2_lo < 0), whose exponent
+        // underflows to 0
         const int lim = static_cast<int>(min(static_cast<int64_t>(kPKeys), pcol[qbk] - key0));
 #pragma unroll
         for (int sub = 0; sub < 4; ++sub)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float a = sacc[qbk][sub][i];
-            const float s = fmaf(a, c2_hi, a * c2_lo);
-            sv[sub][i] = 16 * sub + 4 * grp + i <= lim ? s : -INFINITY;
-            tmax = fmaxf(tmax, sv[sub][i]);
+            sv[sub][i] = 16 * sub + 4 * grp + i <= lim ? sacc[qbk][sub][i] : -1.0e30f;
+            amax = fmaxf(amax, sv[sub][i]);
           }
       }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      amax = fmaxf(amax, __shfl_xor(amax, 16));
+      amax = fmaxf(amax, __shfl_xor(amax, 32));
       // key 0 is visible to every token, so the running max is finite from the
       // first tile on
+      const float tmax = fmaf(amax, c2_hi, amax * c2_lo);
       const float m_new = fmaxf(m[qbk], ceilf(tmax));
       const float alpha = m[qbk] == -INFINITY ? 0.f : ldexpf(1.f, static_cast<int>(m[qbk] - m_new));
       float ps = 0.f;
@@ -228,7 +238,8 @@ __global__ __launch_bounds__(kPThreads, QB <= 2 ? 2 : 1) void full_prefill_kerne
       for (int sub = 0; sub < 4; ++sub)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[qbk][sub][i] = __builtin_amdgcn_exp2f(sv[sub][i] - m_new);
+          const float a = sv[sub][i];
+          p[qbk][sub][i] = __builtin_amdgcn_exp2f(fmaf(a, c2_lo, fmaf(a, c2_hi, -m_new)));
           ps += p[qbk][sub][i];
         }
       l[qbk] = l[qbk] * static_cast<double>(alpha) + static_cast<double>(ps);
@@ -252,7 +263,7 @@ __global__ __launch_bounds__(kPThreads, QB <= 2 ? 2 : 1) void full_prefill_kerne
       }
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) {
-        const bf16x8 a = lds_vt_operand(vt + 32 * ks * kPPitch, kPPitch, nb, col, grp);
+        const bf16x8 a = lds_vt_operand(vt + 32 * ks * kPVPitch, kPVPitch, nb, col, grp);
 #pragma unroll
         for (int qbk = 0; qbk < QB; ++qbk) o[qbk][nb] = mfma_16x16x32(a, pb[qbk], o[qbk][nb]);
       }
