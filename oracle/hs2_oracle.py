@@ -34,6 +34,17 @@ with query heads h in the GQA group {g*G, ..., g*G+G-1}:
      and global tokens share one KV cache):
          s'_h[i] = scale * <q^(n)_h, k_i>, i in idx;  O^(n)_h = softmax(s'_h) V[idx]
 
+Upstream of the path (the step just before the full layer):
+
+  0. KV Bridging (news page, section "两级KV共享：让模型少跑一半", item
+     "KV Bridging"): the Cross-Decoder's full-attention layer builds its K and
+     V from the Self-Decoder's hidden states.  Reading (the page gives no
+     formula): a plain linear projection per KV head, no bias, no
+     normalisation or position transform inside it,
+         K[b, g, t] = W_K[g] h[b, t],   V[b, g, t] = W_V[g] h[b, t],
+     written into the cache rows of the tokens' positions; one token at the
+     end of the cache is the decode-time append.
+
 Pins (tests/test_oracle_*.py, run with -m "not gpu"): agreement with
 torch.nn.functional.scaled_dot_product_attention in float64 on CPU and with
 scipy.special.logsumexp; closed forms (constant V, identical keys, one dominant
@@ -222,3 +233,37 @@ def topk_from_scores(scores: np.ndarray, pos: Sequence[int], top_k: int, window:
         idx, _, _ = select_tokens(scores[r, : p + 1], p, top_k, window)
         out.append(idx)
     return out
+
+
+# ---------------------------------------------------------------------------
+# step 0: KV Bridging (the cache rows the path reads)
+# ---------------------------------------------------------------------------
+
+def kv_bridge(hidden: np.ndarray, w_kv: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Cross-Decoder K and V of new tokens from their Self-Decoder hidden states
+    (news page, section "两级KV共享：让模型少跑一半", item "KV Bridging").
+
+    hidden [B][n][d_model] bf16 bits; w_kv [2][Hkv][D][d_model] bf16 bits (row
+    (0, g, d) is the weight vector of key feature d of KV head g, row (1, g, d)
+    that of value feature d).  Returns K_new, V_new [B][Hkv][n][D] float64:
+        K_new[b, g, t, d] = sum_m w_kv[0, g, d, m] * hidden[b, t, m]
+    and likewise V_new with w_kv[1].
+    """
+    h = widen_bf16(hidden)
+    wk = widen_bf16(w_kv[0])
+    wv = widen_bf16(w_kv[1])
+    k_new = np.einsum("gdm,btm->bgtd", wk, h)
+    v_new = np.einsum("gdm,btm->bgtd", wv, h)
+    return k_new, v_new
+
+
+def cache_append(k_cache: np.ndarray, v_cache: np.ndarray, k_new: np.ndarray,
+                 v_new: np.ndarray, pos0: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Write the new rows at positions pos0 .. pos0 + n - 1 of every KV head's
+    cache [B][Hkv][capacity][D]; every other row keeps its value."""
+    n = k_new.shape[2]
+    k_out = np.array(k_cache, dtype=np.float64, copy=True)
+    v_out = np.array(v_cache, dtype=np.float64, copy=True)
+    k_out[:, :, pos0:pos0 + n] = k_new
+    v_out[:, :, pos0:pos0 + n] = v_new
+    return k_out, v_out

@@ -276,6 +276,93 @@ def pin_sparse_step_empty_rows(orc, seed=11):
     np.testing.assert_allclose(out[0, 0, 0], ref, rtol=1e-14)
 
 
+def _bridge_inputs(rng, B, n, dm, Hkv, D):
+    hidden = _bits(rng.standard_normal((B, n, dm)))
+    w_kv = _bits(rng.standard_normal((2, Hkv, D, dm)) * 0.1)
+    return hidden, w_kv
+
+
+def pin_bridge_brute_force(orc, seed=12):
+    """KV Bridging against explicit loops over every output element (tiny sizes)."""
+    rng = _rng(seed)
+    B, n, dm, Hkv, D = 2, 3, 5, 2, 4
+    hidden, w_kv = _bridge_inputs(rng, B, n, dm, Hkv, D)
+    h, w = _f64(hidden), _f64(w_kv)
+    k_new, v_new = orc.kv_bridge(hidden, w_kv)
+    assert k_new.shape == (B, Hkv, n, D) and v_new.shape == (B, Hkv, n, D)
+    for b in range(B):
+        for g in range(Hkv):
+            for t in range(n):
+                for d in range(D):
+                    ek = sum(w[0, g, d, m] * h[b, t, m] for m in range(dm))
+                    ev = sum(w[1, g, d, m] * h[b, t, m] for m in range(dm))
+                    assert abs(k_new[b, g, t, d] - ek) <= 1e-12 * (1 + abs(ek))
+                    assert abs(v_new[b, g, t, d] - ev) <= 1e-12 * (1 + abs(ev))
+
+
+def pin_bridge_closed_forms(orc, seed=13):
+    """Identity weights copy the hidden state's slice of each head; a one-hot
+    hidden state picks one weight column; the projection is linear."""
+    rng = _rng(seed)
+    B, n, Hkv, D = 2, 3, 2, 8
+    dm = Hkv * D
+    hidden = _bits(rng.standard_normal((B, n, dm)))
+    eye = np.zeros((2, Hkv, D, dm), dtype=np.float32)
+    for g in range(Hkv):
+        for d in range(D):
+            eye[0, g, d, g * D + d] = 1.0
+            eye[1, g, d, (g * D + d + 1) % dm] = 1.0     # V: shifted by one feature
+    k_new, v_new = orc.kv_bridge(hidden, _bits(eye))
+    h = _f64(hidden)
+    for g in range(Hkv):
+        assert np.array_equal(k_new[:, g], h[:, :, g * D:(g + 1) * D])
+        assert np.array_equal(v_new[:, g], np.roll(h, -1, axis=2)[:, :, g * D:(g + 1) * D])
+    # one-hot hidden state e_m: K[b, g, t, d] = W_K[g, d, m]
+    w_kv = _bits(rng.standard_normal((2, Hkv, D, 6)))
+    m = 4
+    onehot = np.zeros((1, 1, 6), dtype=np.float32)
+    onehot[0, 0, m] = 1.0
+    k1, v1 = orc.kv_bridge(_bits(onehot), w_kv)
+    assert np.array_equal(k1[0, :, 0], _f64(w_kv[0])[:, :, m])
+    assert np.array_equal(v1[0, :, 0], _f64(w_kv[1])[:, :, m])
+    # linearity in the hidden state (values exact in bf16: small integers)
+    a = rng.integers(-3, 4, size=(2, 2, 6)).astype(np.float32)
+    c = rng.integers(-3, 4, size=(2, 2, 6)).astype(np.float32)
+    ka, va = orc.kv_bridge(_bits(a), w_kv)
+    kc, vc = orc.kv_bridge(_bits(c), w_kv)
+    ks, vs = orc.kv_bridge(_bits(2 * a + c), w_kv)
+    np.testing.assert_allclose(ks, 2 * ka + kc, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(vs, 2 * va + vc, rtol=0, atol=1e-12)
+
+
+def pin_cache_append(orc, seed=14):
+    """Appending writes exactly the new rows; appending tokens one at a time
+    equals projecting them together; the other rows are untouched."""
+    rng = _rng(seed)
+    B, n, dm, Hkv, D, cap, pos0 = 2, 4, 8, 2, 4, 12, 5
+    hidden, w_kv = _bridge_inputs(rng, B, n, dm, Hkv, D)
+    k0 = rng.standard_normal((B, Hkv, cap, D))
+    v0 = rng.standard_normal((B, Hkv, cap, D))
+    k_new, v_new = orc.kv_bridge(hidden, w_kv)
+    k1, v1 = orc.cache_append(k0, v0, k_new, v_new, pos0)
+    keep = np.ones(cap, dtype=bool)
+    keep[pos0:pos0 + n] = False
+    assert np.array_equal(k1[:, :, keep], k0[:, :, keep])
+    assert np.array_equal(v1[:, :, keep], v0[:, :, keep])
+    assert np.array_equal(k1[:, :, pos0:pos0 + n], k_new)
+    assert np.array_equal(v1[:, :, pos0:pos0 + n], v_new)
+    kk, vv = k0, v0
+    for t in range(n):
+        kt, vt = orc.kv_bridge(hidden[:, t:t + 1], w_kv)
+        kk, vv = orc.cache_append(kk, vv, kt, vt, pos0 + t)
+    np.testing.assert_allclose(kk, k1, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(vv, v1, rtol=0, atol=1e-12)
+    # the rows written hold the projection of their own token
+    h = _f64(hidden)
+    wk = _f64(w_kv[0])
+    np.testing.assert_allclose(k1[1, 1, pos0 + 2], wk[1] @ h[1, 2], rtol=1e-12, atol=1e-12)
+
+
 ALL_PINS = [
     pin_full_attention_vs_sdpa,
     pin_attention_closed_forms,
@@ -288,4 +375,7 @@ ALL_PINS = [
     pin_sparse_permutation_invariance,
     pin_widening,
     pin_sparse_step_empty_rows,
+    pin_bridge_brute_force,
+    pin_bridge_closed_forms,
+    pin_cache_append,
 ]

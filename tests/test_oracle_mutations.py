@@ -41,6 +41,16 @@ MUTANTS = [
     ("widen_shift", "<< np.uint32(16)", "<< np.uint32(15)"),
     ("keys_from_wrong_head", "kk = widen_bf16(k[b, g])", "kk = widen_bf16(k[b, (g + 1) % k.shape[1]])"),
     ("queries_wrong_group", "heads = slice(g * G, (g + 1) * G)", "heads = slice(0, G)"),
+    ("bridge_values_from_key_weights", "wv = widen_bf16(w_kv[1])", "wv = widen_bf16(w_kv[0])"),
+    ("bridge_batch_and_head_swapped", 'k_new = np.einsum("gdm,btm->bgtd", wk, h)',
+     'k_new = np.einsum("gdm,btm->gbtd", wk, h)'),
+    ("bridge_tokens_reversed", "h = widen_bf16(hidden)", "h = widen_bf16(hidden)[:, ::-1]"),
+    ("bridge_weight_transposed", 'v_new = np.einsum("gdm,btm->bgtd", wv, h)',
+     'v_new = np.einsum("gdm,btm->bgtd", wv[:, ::-1], h)'),
+    ("append_one_row_late", "k_out[:, :, pos0:pos0 + n] = k_new",
+     "k_out[:, :, pos0 + 1:pos0 + n + 1] = k_new[:, :, : k_out.shape[2] - pos0 - 1]"),
+    ("append_values_from_keys", "v_out[:, :, pos0:pos0 + n] = v_new",
+     "v_out[:, :, pos0:pos0 + n] = k_new"),
 ]
 
 
