@@ -32,7 +32,9 @@
  *     and sees keys 0..P_t (its own key included).  Decode is T = 1.
  *   - Layouts:  q, out            [B][T][Hq][D]
  *               q_sparse, out_sp  [N][B][T][Hq][D]
- *               k, v (KV cache)   [B][Hkv][S][D]   token-major per KV head
+ *               k, v (KV cache)   [B][Hkv][Sc][D]  token-major per KV head, Sc =
+ *                                                 kv_capacity (ctx_len when 0); rows
+ *                                                 S..Sc-1 are not read
  *               lse               [B][T][Hq]        natural log, float32
  *               scores            [B][T][Hkv][S]    float32, 0 past P_t
  *               idx               [B][T][Hkv][k+w]  int32, ascending, -1 past n_sel
@@ -74,7 +76,12 @@ typedef struct hs2_shape {
   int32_t top_k;      /* k: older tokens chosen per row (1024 in the pages' experiments) */
   int32_t window;     /* w: most recent tokens always kept (128 in the pages' experiments) */
   int32_t reserved;   /* must be 0 */
-} hs2_shape;          /* 48 bytes, no padding */
+  int64_t kv_capacity;/* token rows per KV head in k and v, i.e. the cache's row pitch:
+                         row j of head (b, g) starts at element ((b*Hkv + g)*kv_capacity + j)*D.
+                         0 means ctx_len; otherwise it must be >= ctx_len.  Rows ctx_len ..
+                         kv_capacity-1 are never read, so a cache allocated once for its
+                         final length serves every step as it grows (see hs2_kv_bridge). */
+} hs2_shape;          /* 56 bytes, no padding */
 
 enum {
   HS2_OK = 0,
@@ -93,7 +100,7 @@ size_t hs2_workspace_bytes(const hs2_shape* shape, int32_t n_sparse_layers);
  * For every (b, t, KV head g) and query head h of the group:
  *   s_h[j] = scale * <q_h, k_j> for j <= P_t,  out_h = softmax(s_h) . V,
  *   lse_h  = log sum_j exp(s_h[j]),  scores[j] = max_h softmax(s_h)[j].
- * q [B][T][Hq][D], k/v [B][Hkv][S][D] in; out [B][T][Hq][D] out.
+ * q [B][T][Hq][D], k/v [B][Hkv][Sc][D] in; out [B][T][Hq][D] out.
  * lse (nullable) [B][T][Hq]; scores (nullable) [B][T][Hkv][S] (0 past P_t).
  * This is the group's full-attention layer: news page, section
  * "两级KV共享：让模型少跑一半" (KV Reuse), and video page, section
@@ -131,8 +138,8 @@ int hs2_sparse_attn(const hs2_shape* shape, int32_t n_layers, const hs2_bf16* q,
  * computed in float64 from exact bf16 products (so that keys are ordered by
  * their exact importance, not by its float32 rounding).  scores and lse are
  * nullable.  q_sparse / out_sparse may be NULL when n_sparse_layers = 0.
- * v1: decode only (n_q_tokens = 1); a prefill chunk returns
- * HS2_ERR_UNSUPPORTED. */
+ * Both decode (n_q_tokens = 1) and a prefill chunk (n_q_tokens > 1, one
+ * selection per query token) are supported. */
 int hs2_cross_decoder_step(const hs2_shape* shape, int32_t n_sparse_layers,
                            const hs2_bf16* q_full, const hs2_bf16* q_sparse,
                            const hs2_bf16* k, const hs2_bf16* v, hs2_bf16* out_full,
@@ -150,6 +157,40 @@ int hs2_cross_decoder_step_timed(const hs2_shape* shape, int32_t n_sparse_layers
                                  hs2_bf16* out_sparse, int32_t* idx, int32_t* n_sel,
                                  void* ws, size_t ws_bytes, void* stream, int32_t iters,
                                  float* phase_ms /* [4] */);
+
+/* ---- KV Bridging: the cache rows themselves -------------------------------
+ * The Cross-Decoder's full-attention layer builds its K and V from the
+ * Self-Decoder's hidden states (news page, section
+ * "两级KV共享：让模型少跑一半", item "KV Bridging").  The page gives no formula;
+ * this call reads it as a plain linear projection per KV head (no bias, no
+ * normalisation or position transform inside it):
+ *   K[b][g][pos0 + t][d] = sum_m w_kv[0][g][d][m] * hidden[b][t][m]
+ *   V[b][g][pos0 + t][d] = sum_m w_kv[1][g][d][m] * hidden[b][t][m]
+ * accumulated in float32 and rounded to bf16 (nearest even).
+ *   hidden  [B][n][d_model]        bf16, the new tokens' hidden states
+ *   w_kv    [2][Hkv][D][d_model]   bf16, one weight row per output feature
+ *   k, v    [B][Hkv][kv_capacity][D] bf16 caches (the layout every call above
+ *           reads with kv_capacity as the row pitch); only rows pos0 .. pos0+n-1
+ *           of each head are written.
+ * n = 1 with pos0 = S - 1 is the decode-time append of the token that the
+ * next hs2_cross_decoder_step (ctx_len = S, same kv_capacity) attends from.
+ * No workspace.  Errors: null pointers, non-positive sizes, reserved != 0 or
+ * pos0 + n > kv_capacity give HS2_ERR_INVALID_ARG; head_dim != 128 or a
+ * d_model that is not a multiple of 64 give HS2_ERR_UNSUPPORTED.  k and v must
+ * not overlap hidden or w_kv. */
+typedef struct hs2_bridge_shape {
+  int64_t kv_capacity; /* token rows per KV head of k and v */
+  int64_t pos0;        /* cache position of the first new token */
+  int32_t batch;       /* B */
+  int32_t n_tokens;    /* n: new tokens per batch entry */
+  int32_t d_model;     /* hidden size of the Self-Decoder output */
+  int32_t n_kv_heads;  /* Hkv */
+  int32_t head_dim;    /* D */
+  int32_t reserved;    /* must be 0 */
+} hs2_bridge_shape;    /* 40 bytes, no padding */
+
+int hs2_kv_bridge(const hs2_bridge_shape* shape, const hs2_bf16* hidden, const hs2_bf16* w_kv,
+                  hs2_bf16* k, hs2_bf16* v, void* stream);
 
 /* Human-readable text for a status code (static storage). */
 const char* hs2_status_string(int status);

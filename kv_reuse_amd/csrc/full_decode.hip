@@ -155,7 +155,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void full_decode_split_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     float* __restrict__ stmax, float* __restrict__ part_m, double* __restrict__ part_l,
     float* __restrict__ part_o, int64_t S, int64_t Spad, int kps, int n_split, float c2_hi,
-    float c2_lo) {
+    float c2_lo, int64_t kvp) {
   // V tiles during the stream; reused for the cross-wave merge afterwards
   __shared__ __align__(16) unsigned char smem[kWaves * kTile * kVPitch * 2];
   __shared__ float sm_m[kWaves][kG];
@@ -172,8 +172,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void full_decode_split_kernel(
   const int s = blockIdx.x;
   const int64_t key_begin = static_cast<int64_t>(s) * kps;
   const int64_t key_end = min(S, key_begin + kps);
-  const u16* kr = k + static_cast<size_t>(r) * S * kD;
-  const u16* vr = v + static_cast<size_t>(r) * S * kD;
+  const u16* kr = k + static_cast<size_t>(r) * kvp * kD;
+  const u16* vr = v + static_cast<size_t>(r) * kvp * kD;
   float* stmax_row = stmax + static_cast<size_t>(r) * (Spad / 16) * kG;
   const bool staged = kps <= kStageKeys;
   float* st_dst = staged ? st_stage : stmax_row;
@@ -349,7 +349,7 @@ __global__ __launch_bounds__(kCmbThreads) void full_combine_kernel(
 // max_h 2^(s2_h - lse2_h); entries past P are 0.  Reads K once more.
 __global__ __launch_bounds__(256) void full_scores_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const double* __restrict__ lse2,
-    float* __restrict__ scores, int64_t S, int kps, float c2_hi, float c2_lo) {
+    float* __restrict__ scores, int64_t S, int kps, float c2_hi, float c2_lo, int64_t kvp) {
   __shared__ float l2f[kG];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
@@ -361,7 +361,7 @@ __global__ __launch_bounds__(256) void full_scores_kernel(
   __syncthreads();
   bf16x8 qb[4];
   load_q_operand(q + static_cast<size_t>(r) * kG * kD, col, grp, qb);
-  const u16* kr = k + static_cast<size_t>(r) * S * kD;
+  const u16* kr = k + static_cast<size_t>(r) * kvp * kD;
   float* sr = scores + static_cast<size_t>(r) * S;
   for (int64_t t0 = key_begin + wave * kTile; t0 < key_end; t0 += 4 * kTile) {
     bf16x8 ka[2][4];
@@ -411,7 +411,7 @@ hipError_t launch_full_decode_split(const Plan& p, const u16* q, const u16* k, c
                      reinterpret_cast<float*>(w + p.off_part_m),
                      reinterpret_cast<double*>(w + p.off_part_l),
                      reinterpret_cast<float*>(w + p.off_part_o), p.S, p.Spad, p.kps, p.n_split,
-                     c2_hi, c2_lo);
+                     c2_hi, c2_lo, p.kvp);
   return hipGetLastError();
 }
 
@@ -436,7 +436,7 @@ hipError_t launch_full_scores(const Plan& p, const u16* q, const u16* k, float* 
   const float c2_lo = static_cast<float>(c2 - static_cast<double>(c2_hi));
   hipLaunchKernelGGL(full_scores_kernel, dim3(p.n_split, p.R), dim3(256), 0, st, q, k,
                      reinterpret_cast<const double*>(w + p.off_lse2), scores, p.S, p.kps, c2_hi,
-                     c2_lo);
+                     c2_lo, p.kvp);
   return hipGetLastError();
 }
 

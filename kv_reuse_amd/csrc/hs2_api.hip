@@ -13,6 +13,9 @@
 namespace hs2 {
 namespace {
 
+static_assert(sizeof(hs2_shape) == 56, "hs2_shape layout is part of the ABI");
+static_assert(sizeof(hs2_bridge_shape) == 40, "hs2_bridge_shape layout is part of the ABI");
+
 thread_local int g_last_hip_error = 0;
 
 constexpr size_t kAlign = 256;
@@ -28,10 +31,12 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
     return HS2_ERR_INVALID_ARG;
   if (!(sh->scale > 0.0) || !isfinite(sh->scale)) return HS2_ERR_INVALID_ARG;
   if (sh->n_q_tokens > sh->ctx_len) return HS2_ERR_INVALID_ARG;
+  if (sh->kv_capacity != 0 && sh->kv_capacity < sh->ctx_len) return HS2_ERR_INVALID_ARG;
   if (sh->n_q_heads % sh->n_kv_heads != 0) return HS2_ERR_INVALID_ARG;
   if (static_cast<int64_t>(sh->top_k) + sh->window < 1) return HS2_ERR_INVALID_ARG;
   if (sh->head_dim != kD || sh->n_q_heads != kG * sh->n_kv_heads) return HS2_ERR_UNSUPPORTED;
   if (sh->ctx_len >= (int64_t{1} << 31)) return HS2_ERR_UNSUPPORTED;
+  if (sh->kv_capacity >= (int64_t{1} << 40)) return HS2_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(sh->top_k) + sh->window > kMaxSel) return HS2_ERR_UNSUPPORTED;
   const int64_t R = static_cast<int64_t>(sh->batch) * sh->n_q_tokens * sh->n_kv_heads;
   if (R > 65535) return HS2_ERR_UNSUPPORTED;
@@ -39,6 +44,7 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
   Plan q{};
   q.S = sh->ctx_len;
   q.Spad = static_cast<int64_t>(align_up(static_cast<size_t>(q.S), 64));
+  q.kvp = sh->kv_capacity != 0 ? sh->kv_capacity : q.S;
   q.B = sh->batch;
   q.T = sh->n_q_tokens;
   q.Hq = sh->n_q_heads;
@@ -301,6 +307,34 @@ int hs2_cross_decoder_step_timed(const hs2_shape* shape, int32_t n_sparse_layers
   for (int i = 0; i < 5; ++i) (void)hipEventDestroy(ev[i]);
   if (rc != HS2_OK) return rc;
   for (int i = 0; i < 4; ++i) phase_ms[i] = static_cast<float>(acc[i] / iters);
+  return HS2_OK;
+}
+
+int hs2_kv_bridge(const hs2_bridge_shape* shape, const hs2_bf16* hidden, const hs2_bf16* w_kv,
+                  hs2_bf16* k, hs2_bf16* v, void* stream) {
+  if (!shape || !hidden || !w_kv || !k || !v) return HS2_ERR_INVALID_ARG;
+  const hs2_bridge_shape& s = *shape;
+  if (s.batch < 1 || s.n_tokens < 1 || s.d_model < 1 || s.n_kv_heads < 1 || s.head_dim < 1 ||
+      s.kv_capacity < 1 || s.pos0 < 0 || s.reserved != 0)
+    return HS2_ERR_INVALID_ARG;
+  if (s.pos0 > s.kv_capacity - s.n_tokens) return HS2_ERR_INVALID_ARG;
+  if (s.head_dim != kD || s.d_model % 64 != 0) return HS2_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(s.batch) * s.n_tokens >= (int64_t{1} << 31) ||
+      s.kv_capacity >= (int64_t{1} << 40) || s.n_kv_heads > 4096)
+    return HS2_ERR_UNSUPPORTED;
+  BridgeArgs a{};
+  a.hidden = hidden;
+  a.w = w_kv;
+  a.k = k;
+  a.v = v;
+  a.kvp = s.kv_capacity;
+  a.pos0 = s.pos0;
+  a.M = s.batch * s.n_tokens;
+  a.n_tok = s.n_tokens;
+  a.dm = s.d_model;
+  a.Hkv = s.n_kv_heads;
+  (void)hipGetLastError();
+  HS2_TRY(launch_kv_bridge(a, as_stream(stream)));
   return HS2_OK;
 }
 

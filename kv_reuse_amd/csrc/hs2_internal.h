@@ -42,6 +42,7 @@ constexpr int64_t kPrefillBandCap = 8192;  // near-threshold keys listed per pre
 // Where each piece of the workspace sits, for one shape.
 struct Plan {
   int64_t S, Spad;
+  int64_t kvp;               // K/V row pitch in tokens (the cache's capacity per head)
   int B, T, Hq, Hkv, R;      // R = B*T*Hkv rows
   int k, w, cap;             // cap = k + w (index list capacity per row)
   int n_layers;
@@ -67,6 +68,17 @@ struct Plan {
   size_t total;
 };
 
+// KV Bridging: hidden [M][dm] (M = B * n_tok tokens) times W [2 Hkv D][dm]
+// into rows pos0 .. pos0 + n_tok - 1 of the caches k, v [B][Hkv][kvp][D].
+struct BridgeArgs {
+  const u16* hidden;
+  const u16* w;
+  u16* k;
+  u16* v;
+  int64_t kvp, pos0;
+  int M, n_tok, dm, Hkv;
+};
+
 // ---------------------------------------------------------------- launchers
 // Each returns the hipError_t of its launches (hipGetLastError()).
 
@@ -77,6 +89,8 @@ hipError_t launch_full_decode_split(const Plan& p, const u16* q, const u16* k, c
 // Merge the splits: out (bf16), lse (nullable), lse2 (fp64, base 2) and each
 // head's bound on log2 importance; also clears the rows' selection state.
 hipError_t launch_full_combine(const Plan& p, u16* out, float* lse, void* ws, hipStream_t st);
+// KV Bridging into the cache (no workspace).
+hipError_t launch_kv_bridge(const BridgeArgs& a, hipStream_t st);
 // Per-key importance [R][S] (float32), recomputed from q, k and lse2.
 hipError_t launch_full_scores(const Plan& p, const u16* q, const u16* k, float* scores,
                               void* ws, hipStream_t st);

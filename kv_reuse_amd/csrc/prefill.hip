@@ -121,7 +121,7 @@ __global__ __launch_bounds__(kPThreads, QB <= 2 ? 2 : 1) void full_prefill_kerne
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     u16* __restrict__ out, float* __restrict__ lse_out, double* __restrict__ lse2,
     float* __restrict__ ytop_h, int64_t S, int T, int Hkv, int n_tblk, float c2_hi,
-    float c2_lo) {
+    float c2_lo, int64_t kvp) {
   __shared__ __align__(16) u16 kt[kPKeys * kPPitch];
   __shared__ __align__(16) u16 vt[kPKeys * kPVPitch];
   const int lane = threadIdx.x & 63;
@@ -132,8 +132,8 @@ __global__ __launch_bounds__(kPThreads, QB <= 2 ? 2 : 1) void full_prefill_kerne
   const int bg = lin / n_tblk;
   const int g = bg % Hkv, b = bg / Hkv;
   const int Hq = Hkv * kG;
-  const u16* kr = k + static_cast<size_t>(bg) * S * kD;
-  const u16* vr = v + static_cast<size_t>(bg) * S * kD;
+  const u16* kr = k + static_cast<size_t>(bg) * kvp * kD;
+  const u16* vr = v + static_cast<size_t>(bg) * kvp * kD;
   const int64_t pos0 = S - T;                      // position of chunk token 0
   constexpr int kTok = 8 * QB;                     // chunk tokens per work-group
   // this lane's columns: query block qbk covers tokens 2*QB*wave + 2*qbk + {0,1}
@@ -317,7 +317,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_importance_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const double* __restrict__ lse2,
     const float* __restrict__ ytop_h, float* __restrict__ y, uint32_t* __restrict__ hist,
     float* __restrict__ scores, int64_t S, int64_t Spad, int T, int Hkv, int w, int n_tblk,
-    float c2_hi, float c2_lo) {
+    float c2_hi, float c2_lo, int64_t kvp) {
   __shared__ __align__(16) u16 kt[kPKeys * kPPitch];
   __shared__ uint32_t lh[kPTok][kPNB];
   __shared__ float s_ybase[kPTok];
@@ -330,7 +330,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_importance_kernel(
   const int bg = lin / n_tblk;
   const int g = bg % Hkv, b = bg / Hkv;
   const int Hq = Hkv * kG;
-  const u16* kr = k + static_cast<size_t>(bg) * S * kD;
+  const u16* kr = k + static_cast<size_t>(bg) * kvp * kD;
   const int64_t pos0 = S - T;
   const bool want_hist = hist != nullptr;
   if (want_hist)
@@ -469,7 +469,7 @@ hipError_t launch_full_prefill(const Plan& p, const u16* q, const u16* k, const 
   hipLaunchKernelGGL(full_prefill_kernel<QB>, dim3(n_wg), dim3(kPThreads), 0, st, q, k, v, out,
                      lse, reinterpret_cast<double*>(w + p.off_lse2),
                      reinterpret_cast<float*>(w + p.off_ytop), p.S, p.T, p.Hkv, n_tblk, c2_hi,
-                     c2_lo);
+                     c2_lo, p.kvp);
   return hipGetLastError();
 }
 
@@ -486,7 +486,7 @@ hipError_t launch_prefill_importance(const Plan& p, const u16* q, const u16* k, 
                      reinterpret_cast<const float*>(w + p.off_ytop),
                      for_select ? reinterpret_cast<float*>(w + p.off_ybuf) : nullptr,
                      for_select ? reinterpret_cast<uint32_t*>(w + p.off_hist) : nullptr, scores,
-                     p.S, p.Spad, p.T, p.Hkv, p.w, n_tblk, c2_hi, c2_lo);
+                     p.S, p.Spad, p.T, p.Hkv, p.w, n_tblk, c2_hi, c2_lo, p.kvp);
   return hipGetLastError();
 }
 

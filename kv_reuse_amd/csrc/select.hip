@@ -634,7 +634,7 @@ __global__ __launch_bounds__(kThreads, 4) void subtile_score_kernel(
     uint32_t* __restrict__ hist_c, const u16* __restrict__ q, const u16* __restrict__ k,
     double* __restrict__ cand_y, int32_t* __restrict__ cand_idx, uint32_t* __restrict__ cand_cnt,
     int64_t S, int64_t Spad, int T, int Hkv, int topk, int w, int chunk, int n_chunks,
-    double c2) {
+    double c2, int64_t kvp) {
   __shared__ uint32_t lh[kNB];
   __shared__ int32_t s_list[kScoreRound];
   __shared__ double stage_y[kStageSub * kSubKeys];
@@ -699,7 +699,7 @@ __global__ __launch_bounds__(kThreads, 4) void subtile_score_kernel(
   for (int i = tid; i < kNB; i += kThreads) lh[i] = 0u;   // now the candidate histogram
   const int b = r / (T * Hkv);
   const int g = r % Hkv;
-  const u16* kr = k + (static_cast<size_t>(b) * Hkv + g) * static_cast<size_t>(S) * kD;
+  const u16* kr = k + (static_cast<size_t>(b) * Hkv + g) * static_cast<size_t>(kvp) * kD;
   const size_t region = (static_cast<size_t>(r) * n_chunks + blockIdx.x) * static_cast<size_t>(chunk) * kSubKeys;
   double* cy = cand_y + region;
   int32_t* ci = cand_idx + region;
@@ -1294,7 +1294,7 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
     const float* __restrict__ ytop_h, const double* __restrict__ lse2, const u16* __restrict__ q,
     const u16* __restrict__ k, int32_t* __restrict__ band_idx, uint64_t* __restrict__ band_key,
     int64_t band_cap, int32_t* __restrict__ idx_out, int32_t* __restrict__ nsel_out, int64_t S,
-    int64_t Spad, int T, int Hkv, int topk, int w, int cap, double c2) {
+    int64_t Spad, int T, int Hkv, int topk, int w, int cap, double c2, int64_t kvp) {
   __shared__ __align__(16) int32_t up[kMaxSel];
   __shared__ __align__(16) int32_t bw[kMaxSel];        // band winners; first the histogram
   __shared__ __align__(16) uint64_t lbk[kUncCap];
@@ -1410,7 +1410,7 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
         // ---- exact importance of the band keys in float64 (bf16 products are exact)
         const int b = r / (T * Hkv);
         const int g = r % Hkv;
-        const u16* kr = k + (static_cast<size_t>(b) * Hkv + g) * static_cast<size_t>(S) * kD;
+        const u16* kr = k + (static_cast<size_t>(b) * Hkv + g) * static_cast<size_t>(kvp) * kD;
         for (uint32_t i = tid; i < n_band; i += kRowThreads) {
           const u16* kj = kr + static_cast<size_t>(bi[i]) * kD;
           double acc[kG];
@@ -1587,7 +1587,7 @@ hipError_t launch_fused_select(const Plan& p, const u16* q, const u16* k, int32_
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(subtile_score_kernel, dim3(p.sc_nchunk, p.R), dim3(kThreads), 0, st, stmax,
                      lse2, ytop, hist, hist_c, q, k, cand_y, cand_idx, cand_cnt, p.S, p.Spad, p.T,
-                     p.Hkv, p.k, p.w, p.sc_chunk, p.sc_nchunk, c2);
+                     p.Hkv, p.k, p.w, p.sc_chunk, p.sc_nchunk, c2, p.kvp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(row_select_kernel, dim3(p.R), dim3(kSelThreads), 0, st, hist_c, cand_y,
                      cand_idx, cand_cnt, ytop, idx, n_sel, p.S, p.T, p.Hkv, p.k, p.w, p.cap,
@@ -1606,7 +1606,7 @@ hipError_t launch_prefill_select(const Plan& p, const u16* q, const u16* k, int3
                      reinterpret_cast<const double*>(w + p.off_lse2), q, k,
                      reinterpret_cast<int32_t*>(w + p.off_band_idx),
                      reinterpret_cast<uint64_t*>(w + p.off_band_key), p.band_cap, idx, n_sel, p.S,
-                     p.Spad, p.T, p.Hkv, p.k, p.w, p.cap, c2);
+                     p.Spad, p.T, p.Hkv, p.k, p.w, p.cap, c2, p.kvp);
   return hipGetLastError();
 }
 

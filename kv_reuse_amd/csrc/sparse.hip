@@ -30,7 +30,7 @@ __global__ __launch_bounds__(NCT * 64) void sparse_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ n_sel, u16* __restrict__ out,
     float* __restrict__ part_m, float* __restrict__ part_l, float* __restrict__ part_o,
     int64_t S, int T, int Hkv, int L, int layer0, int cap, int nch, int keys_per_wg,
-    float c2_hi, float c2_lo, size_t layer_stride) {
+    float c2_hi, float c2_lo, size_t layer_stride, int64_t kvp) {
   __shared__ __align__(16) u16 klds[kSub * kPitch];
   __shared__ __align__(16) u16 vlds[kSub * kPitch];
   __shared__ int32_t sidx[kSub];
@@ -45,8 +45,8 @@ __global__ __launch_bounds__(NCT * 64) void sparse_kernel(
   const int b = r / (T * Hkv);
   const int g = r % Hkv;
   const size_t kvrow = static_cast<size_t>(b) * Hkv + g;
-  const u16* kr = k + kvrow * static_cast<size_t>(S) * kD;
-  const u16* vr = v + kvrow * static_cast<size_t>(S) * kD;
+  const u16* kr = k + kvrow * static_cast<size_t>(kvp) * kD;
+  const u16* vr = v + kvrow * static_cast<size_t>(kvp) * kD;
   const int ns = n_sel[r];
   const int pos_begin = ch * keys_per_wg;
   const int pos_end = min(ns, pos_begin + keys_per_wg);
@@ -236,7 +236,7 @@ hipError_t launch_sparse(const Plan& p, const u16* q, const u16* k, const u16* v
     auto go = [&](auto kern) {
       hipLaunchKernelGGL(kern, grid, dim3(nct * 64), 0, st, q, k, v, idx, n_sel, out, pm, pl, po,
                          p.S, p.T, p.Hkv, p.n_layers, layer0, p.cap, p.sp_nch, keys_per_wg, c2_hi,
-                         c2_lo, layer_stride);
+                         c2_lo, layer_stride, p.kvp);
     };
     switch (nct) {
       case 1: go(sparse_kernel<1>); break;

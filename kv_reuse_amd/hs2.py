@@ -26,8 +26,8 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 HS2_OK, HS2_ERR_INVALID_ARG, HS2_ERR_UNSUPPORTED, HS2_ERR_WORKSPACE, HS2_ERR_HIP = 0, -1, -2, -3, -4
 EXPORTED = ["hs2_workspace_bytes", "hs2_full_attn_scores", "hs2_topk_select", "hs2_sparse_attn",
-            "hs2_cross_decoder_step", "hs2_cross_decoder_step_timed", "hs2_status_string",
-            "hs2_last_hip_error"]
+            "hs2_cross_decoder_step", "hs2_cross_decoder_step_timed", "hs2_kv_bridge",
+            "hs2_status_string", "hs2_last_hip_error"]
 
 
 class Shape(ctypes.Structure):
@@ -35,7 +35,15 @@ class Shape(ctypes.Structure):
                 ("batch", ctypes.c_int32), ("n_q_tokens", ctypes.c_int32),
                 ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("top_k", ctypes.c_int32),
-                ("window", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("window", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("kv_capacity", ctypes.c_int64)]
+
+
+class BridgeShape(ctypes.Structure):
+    _fields_ = [("kv_capacity", ctypes.c_int64), ("pos0", ctypes.c_int64),
+                ("batch", ctypes.c_int32), ("n_tokens", ctypes.c_int32),
+                ("d_model", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -55,6 +63,8 @@ _lib.hs2_cross_decoder_step_timed.argtypes = [_SP, ctypes.c_int32, _P, _P, _P, _
                                               _P, _P, ctypes.c_size_t, _P, ctypes.c_int32,
                                               ctypes.POINTER(ctypes.c_float)]
 _lib.hs2_cross_decoder_step_timed.restype = ctypes.c_int
+_lib.hs2_kv_bridge.argtypes = [ctypes.POINTER(BridgeShape), _P, _P, _P, _P, _P]
+_lib.hs2_kv_bridge.restype = ctypes.c_int
 _lib.hs2_status_string.argtypes = [ctypes.c_int]
 _lib.hs2_status_string.restype = ctypes.c_char_p
 _lib.hs2_last_hip_error.argtypes = []
@@ -81,13 +91,14 @@ class ShapeArgs:
     top_k: int = 1024
     window: int = 128
     scale: Optional[float] = None
+    kv_capacity: int = 0      # token rows per KV head in k / v; 0 = ctx_len
 
     def c(self) -> Shape:
         scale = self.scale if self.scale is not None else 1.0 / math.sqrt(self.head_dim)
         return Shape(ctx_len=self.ctx_len, scale=scale, batch=self.batch,
                      n_q_tokens=self.n_q_tokens, n_q_heads=self.n_q_heads,
                      n_kv_heads=self.n_kv_heads, head_dim=self.head_dim, top_k=self.top_k,
-                     window=self.window, reserved=0)
+                     window=self.window, reserved=0, kv_capacity=self.kv_capacity)
 
     @property
     def rows(self) -> int:
@@ -96,6 +107,11 @@ class ShapeArgs:
     @property
     def cap(self) -> int:
         return self.top_k + self.window
+
+    @property
+    def kv_rows(self) -> int:
+        """Token rows per KV head of the k / v tensors."""
+        return self.kv_capacity or self.ctx_len
 
 
 def shape_of(workload) -> ShapeArgs:
@@ -148,8 +164,8 @@ def alloc_workspace(s: ShapeArgs, n_sparse_layers: int = 0, device="cuda") -> to
 def full_attn_scores(s: ShapeArgs, q, k, v, out, lse=None, scores=None, ws=None):
     B, T, Hq, Hkv, D, S = s.batch, s.n_q_tokens, s.n_q_heads, s.n_kv_heads, s.head_dim, s.ctx_len
     _check(q, "q", torch.bfloat16, (B, T, Hq, D))
-    _check(k, "k", torch.bfloat16, (B, Hkv, S, D))
-    _check(v, "v", torch.bfloat16, (B, Hkv, S, D))
+    _check(k, "k", torch.bfloat16, (B, Hkv, s.kv_rows, D))
+    _check(v, "v", torch.bfloat16, (B, Hkv, s.kv_rows, D))
     _check(out, "out", torch.bfloat16, (B, T, Hq, D))
     _check(lse, "lse", torch.float32, (B, T, Hq), allow_none=True)
     _check(scores, "scores", torch.float32, (B, T, Hkv, S), allow_none=True)
@@ -174,8 +190,8 @@ def sparse_attn(s: ShapeArgs, q, k, v, idx, n_sel, out, ws=None):
     B, T, Hq, Hkv, D, S = s.batch, s.n_q_tokens, s.n_q_heads, s.n_kv_heads, s.head_dim, s.ctx_len
     L = q.shape[0]
     _check(q, "q", torch.bfloat16, (L, B, T, Hq, D))
-    _check(k, "k", torch.bfloat16, (B, Hkv, S, D))
-    _check(v, "v", torch.bfloat16, (B, Hkv, S, D))
+    _check(k, "k", torch.bfloat16, (B, Hkv, s.kv_rows, D))
+    _check(v, "v", torch.bfloat16, (B, Hkv, s.kv_rows, D))
     _check(idx, "idx", torch.int32, (B, T, Hkv, s.cap))
     _check(n_sel, "n_sel", torch.int32, (B, T, Hkv))
     _check(out, "out", torch.bfloat16, (L, B, T, Hq, D))
@@ -190,8 +206,8 @@ def cross_decoder_step(s: ShapeArgs, q_full, q_sparse, k, v, out_full, out_spars
     B, T, Hq, Hkv, D, S = s.batch, s.n_q_tokens, s.n_q_heads, s.n_kv_heads, s.head_dim, s.ctx_len
     L = 0 if q_sparse is None else q_sparse.shape[0]
     _check(q_full, "q_full", torch.bfloat16, (B, T, Hq, D))
-    _check(k, "k", torch.bfloat16, (B, Hkv, S, D))
-    _check(v, "v", torch.bfloat16, (B, Hkv, S, D))
+    _check(k, "k", torch.bfloat16, (B, Hkv, s.kv_rows, D))
+    _check(v, "v", torch.bfloat16, (B, Hkv, s.kv_rows, D))
     _check(out_full, "out_full", torch.bfloat16, (B, T, Hq, D))
     if L:
         _check(q_sparse, "q_sparse", torch.bfloat16, (L, B, T, Hq, D))
@@ -221,3 +237,20 @@ def cross_decoder_step_timed(s: ShapeArgs, q_full, q_sparse, k, v, out_full, out
 def raw():
     """The ctypes library handle (for ABI tests)."""
     return _lib
+
+
+def kv_bridge(hidden, w_kv, k, v, pos0: int):
+    """KV Bridging into the cache: hidden [B][n][d_model] and w_kv
+    [2][Hkv][D][d_model] (bf16) write rows pos0 .. pos0 + n - 1 of every KV head
+    of the caches k, v [B][Hkv][capacity][D]."""
+    B, n, dm = hidden.shape
+    _, Hkv, D, _ = w_kv.shape
+    cap = k.shape[2]
+    _check(hidden, "hidden", torch.bfloat16, (B, n, dm))
+    _check(w_kv, "w_kv", torch.bfloat16, (2, Hkv, D, dm))
+    _check(k, "k", torch.bfloat16, (B, Hkv, cap, D))
+    _check(v, "v", torch.bfloat16, (B, Hkv, cap, D))
+    sh = BridgeShape(kv_capacity=cap, pos0=int(pos0), batch=B, n_tokens=n, d_model=dm,
+                     n_kv_heads=Hkv, head_dim=D, reserved=0)
+    _call("hs2_kv_bridge", _lib.hs2_kv_bridge(ctypes.byref(sh), _ptr(hidden), _ptr(w_kv), _ptr(k),
+                                              _ptr(v), _stream()))

@@ -227,3 +227,40 @@ def small(name: str = "small", *, batch=1, n_q_tokens=1, n_q_heads=8, n_kv_heads
                     n_sparse_layers=n_sparse_layers, top_k=top_k, window=window,
                     n_needles=n_needles, drift_sd=drift_sd, heavy_frac=heavy_frac,
                     config_id=config_id)
+
+
+# ---------------------------------------------------------------------------
+# KV Bridging inputs: Self-Decoder hidden states and projection weights
+# ---------------------------------------------------------------------------
+# The pages give no hidden size and no weights.  The synthetic ones: hidden
+# states N(0, 1); weights N(0, 1/d_model), so that every projected K/V entry is
+# about N(0, 1) like the cache entries of the workloads above.  Both are float32
+# draws rounded to bfloat16.  The bridge workloads use d_model = 4096.
+
+BRIDGE_D_MODEL = 4096
+
+
+def bridge_inputs(batch: int, n_tokens: int, d_model: int, n_kv_heads: int, head_dim: int = 128,
+                  seed: int = BASE_SEED + 50):
+    """(hidden [B][n][d_model], w_kv [2][Hkv][D][d_model]) as bf16 bit patterns
+    (numpy); streams spawned in the order hidden, w_kv."""
+    ss = np.random.SeedSequence(seed)
+    rh, rw = (np.random.default_rng(c) for c in ss.spawn(2))
+    hidden = f32_to_bf16_bits(_normal_f32(rh, (batch, n_tokens, d_model)))
+    w = _normal_f32(rw, (2, n_kv_heads, head_dim, d_model)) * np.float32(1.0 / np.sqrt(d_model))
+    return hidden, f32_to_bf16_bits(w.astype(np.float32))
+
+
+def bridge_inputs_device(batch: int, n_tokens: int, d_model: int, n_kv_heads: int,
+                         head_dim: int = 128, seed: int = BASE_SEED + 60):
+    """The same distributions drawn on the GPU with torch's seeded generator, for
+    sizes too large to draw on the host (a whole prompt's hidden states):
+    (hidden, w_kv) as torch.bfloat16 device tensors."""
+    import torch
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    hidden = torch.randn((batch, n_tokens, d_model), generator=g, device="cuda",
+                         dtype=torch.float32).to(torch.bfloat16)
+    w = torch.randn((2, n_kv_heads, head_dim, d_model), generator=g, device="cuda",
+                    dtype=torch.float32) * (1.0 / float(np.sqrt(d_model)))
+    return hidden, w.to(torch.bfloat16)

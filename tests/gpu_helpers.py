@@ -37,14 +37,27 @@ def host_f64(t: torch.Tensor) -> np.ndarray:
     return t.float().cpu().numpy().astype(np.float64)
 
 
-def run_step(w: wl.Workload, x, with_scores=True, with_lse=True):
+NAN_BF16 = 0x7FC0
+
+
+def cache_with_capacity(bits: np.ndarray, capacity: int) -> torch.Tensor:
+    """A [B][Hkv][capacity][D] device cache whose first S rows per head are the
+    given ones and whose spare rows hold NaN, so that any read of them shows."""
+    B, Hkv, S, D = bits.shape
+    full = np.full((B, Hkv, capacity, D), NAN_BF16, dtype=np.uint16)
+    full[:, :, :S] = bits
+    return dev(full)
+
+
+def run_step(w: wl.Workload, x, with_scores=True, with_lse=True, kv_capacity=0):
+    import dataclasses
     from kv_reuse_amd import hs2
-    s = hs2.shape_of(w)
+    s = dataclasses.replace(hs2.shape_of(w), kv_capacity=kv_capacity)
     B, T, Hq, Hkv, D, S, L = (w.batch, w.n_q_tokens, w.n_q_heads, w.n_kv_heads, w.head_dim,
                               w.ctx_len, w.n_sparse_layers)
     q = dev(x["q_full"])
-    k = dev(x["k"])
-    v = dev(x["v"])
+    k = cache_with_capacity(x["k"], kv_capacity) if kv_capacity else dev(x["k"])
+    v = cache_with_capacity(x["v"], kv_capacity) if kv_capacity else dev(x["v"])
     qs = dev(x["q_sparse"]) if L else None
     out = torch.empty((B, T, Hq, D), dtype=torch.bfloat16, device="cuda")
     outs = torch.empty((L, B, T, Hq, D), dtype=torch.bfloat16, device="cuda") if L else None

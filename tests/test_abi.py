@@ -1,6 +1,7 @@
 """C ABI of libhs2.so on the host: exported symbols, workspace sizing and argument
 validation.  Nothing here launches a kernel on a GPU."""
 import ctypes
+import dataclasses
 import os
 import re
 
@@ -21,7 +22,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 8
+    assert len(names) == 9
     lib = hs2.raw()
     for n in names:
         assert hasattr(lib, n), n
@@ -29,8 +30,9 @@ def test_every_declared_function_is_exported():
 
 
 def test_shape_struct_layout():
-    assert ctypes.sizeof(hs2.Shape) == 48
+    assert ctypes.sizeof(hs2.Shape) == 56
     assert hs2.Shape.scale.offset == 8 and hs2.Shape.batch.offset == 16
+    assert hs2.Shape.kv_capacity.offset == 48
 
 
 def good():
@@ -49,6 +51,8 @@ def test_workspace_bytes_valid_and_monotone():
     # the scores path (4 B) dominate; the K/V cache itself is 512 B per key and head
     n = hs2.workspace_bytes(big, 8)
     assert 18 * 4 * (1 << 20) <= n < 64 * 4 * (1 << 20)
+    # a cache allocated for a longer context does not change the workspace
+    assert hs2.workspace_bytes(dataclasses.replace(big, kv_capacity=(1 << 20) + 4096), 8) == n
 
 
 @pytest.mark.parametrize("field,value,code", [
@@ -65,6 +69,9 @@ def test_workspace_bytes_valid_and_monotone():
     ("scale", -1.0, hs2.HS2_ERR_INVALID_ARG),
     ("scale", float("nan"), hs2.HS2_ERR_INVALID_ARG),
     ("reserved", 7, hs2.HS2_ERR_INVALID_ARG),
+    ("kv_capacity", 4999, hs2.HS2_ERR_INVALID_ARG),   # smaller than ctx_len
+    ("kv_capacity", -1, hs2.HS2_ERR_INVALID_ARG),
+    ("kv_capacity", 1 << 40, hs2.HS2_ERR_UNSUPPORTED),
 ])
 def test_bad_shapes_rejected(field, value, code):
     c = good().c()
@@ -130,3 +137,40 @@ def test_valid_call_without_gpu_reports_hip_error():
     st = lib.hs2_topk_select(ctypes.byref(c), FAKE, FAKE, FAKE, ctypes.c_void_p(0x100000), need, None)
     assert st == hs2.HS2_ERR_HIP
     assert lib.hs2_last_hip_error() != 0
+
+
+def good_bridge():
+    return hs2.BridgeShape(kv_capacity=1000, pos0=990, batch=2, n_tokens=10, d_model=512,
+                           n_kv_heads=4, head_dim=128, reserved=0)
+
+
+def test_bridge_shape_struct_layout():
+    assert ctypes.sizeof(hs2.BridgeShape) == 40
+    assert hs2.BridgeShape.batch.offset == 16 and hs2.BridgeShape.reserved.offset == 36
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("pos0", 991, hs2.HS2_ERR_INVALID_ARG),           # rows past the capacity
+    ("pos0", -1, hs2.HS2_ERR_INVALID_ARG),
+    ("n_tokens", 0, hs2.HS2_ERR_INVALID_ARG),
+    ("batch", 0, hs2.HS2_ERR_INVALID_ARG),
+    ("kv_capacity", 0, hs2.HS2_ERR_INVALID_ARG),
+    ("reserved", 1, hs2.HS2_ERR_INVALID_ARG),
+    ("d_model", 0, hs2.HS2_ERR_INVALID_ARG),
+    ("d_model", 100, hs2.HS2_ERR_UNSUPPORTED),         # not a multiple of 64
+    ("head_dim", 64, hs2.HS2_ERR_UNSUPPORTED),
+])
+def test_bridge_bad_shapes_rejected(field, value, code):
+    c = good_bridge()
+    setattr(c, field, value)
+    assert hs2.raw().hs2_kv_bridge(ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, None) == code
+
+
+def test_bridge_null_pointers_rejected():
+    c = good_bridge()
+    lib = hs2.raw()
+    assert lib.hs2_kv_bridge(None, FAKE, FAKE, FAKE, FAKE, None) == hs2.HS2_ERR_INVALID_ARG
+    for i in range(4):
+        ptrs = [FAKE] * 4
+        ptrs[i] = None
+        assert lib.hs2_kv_bridge(ctypes.byref(c), *ptrs, None) == hs2.HS2_ERR_INVALID_ARG

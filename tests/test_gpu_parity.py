@@ -53,6 +53,28 @@ def test_step_small(hs2, name, kw):
     gh.log(f"  {st}")
 
 
+CAPACITY = [
+    # a cache allocated for more tokens than the context: the spare rows hold
+    # NaN and must never be read (decode, and a prefill chunk)
+    ("decode_1000_spare_77", dict(batch=2, n_q_heads=16, n_kv_heads=2, ctx_len=1000,
+                                  n_sparse_layers=2, top_k=64, window=16, n_needles=4,
+                                  config_id=19), 1077),
+    ("chunk_24_over_500_spare_500", dict(batch=1, n_q_tokens=24, n_q_heads=16, n_kv_heads=2,
+                                         ctx_len=500, n_sparse_layers=2, top_k=32, window=8,
+                                         n_needles=4, config_id=20), 1000),
+]
+
+
+@pytest.mark.parametrize("name,kw,cap", CAPACITY, ids=[s[0] for s in CAPACITY])
+def test_step_cache_with_spare_capacity(hs2, name, kw, cap):
+    w = wl.small(name=name, **kw)
+    x = wl.generate(w)
+    gh.log(f"[step] {name} S={w.ctx_len} T={w.n_q_tokens} capacity={cap}")
+    res = gh.run_step(w, x, kv_capacity=cap)
+    st = gh.compare_step(w, x, res)
+    gh.log(f"  {st}")
+
+
 def test_step_decode_2k_workload(hs2):
     w = wl.WORKLOADS["decode_2k_b4"]
     x = wl.generate(w)
