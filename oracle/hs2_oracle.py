@@ -28,6 +28,10 @@ with query heads h in the GQA group {g*G, ..., g*G+G-1}:
      kept; from the older tokens [0, P_t - w + 1) the `top_k` with the largest
      score are kept, ties going to the lower index.  Reading: when fewer than
      top_k older tokens exist, all of them are kept.
+     Variant (the previous generation's block-level selection, for the
+     comparison the same section draws): the older tokens are cut into aligned
+     blocks, a block's importance is the largest importance of its tokens, and
+     top_k // block whole blocks are kept, ties to the lower block index.
   4. each sparse layer n attends with its own queries q^(n) to the selected
      rows of the same K/V only, with one softmax over selected + window
      (the same section: the separate sliding-window branch is dropped and local
@@ -129,6 +133,38 @@ def select_tokens(score: np.ndarray, pos: int, top_k: int, window: int):
     return idx, tau, sigma
 
 
+def select_blocks(score: np.ndarray, pos: int, top_k: int, window: int, block: int):
+    """Block-level selection for one row: the previous generation's variant, in
+    which every pick is a whole run of consecutive tokens (news page, section
+    "Token级选择：精准定位大海里的那根针", which contrasts it with token-level
+    picks; the block explainer page names blocks of 64 or 128 tokens).
+
+    Readings (the pages give no formula): the window is forced as in the
+    token-level selection; the older tokens [0, first) are cut into aligned
+    blocks [c*block, (c+1)*block), the last one ending at `first`; a block's
+    importance is the largest importance of its tokens; the top_k // block
+    blocks with the largest importance are kept, ties to the lower block index
+    (all blocks when there are fewer).  With block = 1 this is select_tokens.
+    Returns (idx ascending int64, tau, sigma) with tau the importance of the
+    last block taken and sigma the largest importance of a block left out.
+    """
+    win, cand = window_and_candidates(pos, window)
+    first = cand.size
+    n_blocks = (first + block - 1) // block
+    bscore = np.array([score[c * block:min((c + 1) * block, first)].max()
+                       for c in range(n_blocks)])
+    blocks = np.arange(n_blocks, dtype=np.int64)
+    n_take = min(top_k // block, n_blocks)
+    order = np.lexsort((blocks, -bscore))
+    taken = blocks[order[:n_take]]
+    left = blocks[order[n_take:]]
+    toks = [np.arange(c * block, min((c + 1) * block, first), dtype=np.int64) for c in taken]
+    idx = np.sort(np.concatenate(toks + [win]))
+    tau = float(bscore[taken].min()) if taken.size else float("nan")
+    sigma = float(bscore[left].max()) if left.size else float("nan")
+    return idx, tau, sigma
+
+
 # ---------------------------------------------------------------------------
 # step 4: one sparse layer for one row
 # ---------------------------------------------------------------------------
@@ -152,13 +188,14 @@ def sparse_attention_row(q_g: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray
 def cross_decoder_step(q_full: np.ndarray, k: np.ndarray, v: np.ndarray,
                        q_sparse: Optional[np.ndarray], *, top_k: int, window: int,
                        scale: float, rows: Optional[Iterable[Tuple[int, int, int]]] = None,
-                       keep_scores: bool = True) -> Dict[str, object]:
+                       keep_scores: bool = True, block: int = 0) -> Dict[str, object]:
     """Run full attention -> importance -> selection -> N sparse layers.
 
     q_full   [B][T][Hq][D] bf16 bits
     k, v     [B][Hkv][S][D] bf16 bits
     q_sparse [N][B][T][Hq][D] bf16 bits, or None for no sparse layers
     rows     iterable of (b, t, g) to compute; None = all rows
+    block    0: token-level selection; > 0: block-level selection of that size
     Returns a dict keyed by (b, t, g) -> per-row results:
       out_full [G, D], lse [G], score [P_t+1] (if keep_scores), idx, tau,
       sigma, out_sparse [N, G, D].
@@ -184,7 +221,10 @@ def cross_decoder_step(q_full: np.ndarray, k: np.ndarray, v: np.ndarray,
             qg = widen_bf16(q_full[b, t, heads])
             out, lse, probs = full_attention_row(qg, kk[: pos + 1], vv[: pos + 1], scale)
             score = importance_scores(probs)
-            idx, tau, sigma = select_tokens(score, pos, top_k, window)
+            if block:
+                idx, tau, sigma = select_blocks(score, pos, top_k, window, block)
+            else:
+                idx, tau, sigma = select_tokens(score, pos, top_k, window)
             outs = np.zeros((N, G, D))
             for n in range(N):
                 qn = widen_bf16(q_sparse[n, b, t, heads])
@@ -225,12 +265,17 @@ def sparse_step(q: np.ndarray, k: np.ndarray, v: np.ndarray, idx: np.ndarray,
     return out
 
 
-def topk_from_scores(scores: np.ndarray, pos: Sequence[int], top_k: int, window: int):
-    """Selection alone, from given scores [R, S] (row r has context 0..pos[r])."""
+def topk_from_scores(scores: np.ndarray, pos: Sequence[int], top_k: int, window: int,
+                     block: int = 0):
+    """Selection alone, from given scores [R, S] (row r has context 0..pos[r]);
+    block > 0 selects whole blocks of that size."""
     out = []
     for r in range(scores.shape[0]):
         p = int(pos[r])
-        idx, _, _ = select_tokens(scores[r, : p + 1], p, top_k, window)
+        if block:
+            idx, _, _ = select_blocks(scores[r, : p + 1], p, top_k, window, block)
+        else:
+            idx, _, _ = select_tokens(scores[r, : p + 1], p, top_k, window)
         out.append(idx)
     return out
 

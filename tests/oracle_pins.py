@@ -189,6 +189,75 @@ def pin_selection_invariants(orc, seed=5):
     assert idx.tolist() == list(range(k)) + list(range(pos - w + 1, pos + 1))
 
 
+def _brute_force_blocks(score, pos, k, w, bs):
+    """Block selection by enumeration: block c = tokens [c*bs, min((c+1)*bs, first));
+    its value is the largest score in it (explicit loop); keep the size-m set of
+    blocks that beats every left-out block (larger value, or equal and lower index)."""
+    first = max(0, pos - w + 1)
+    nb = (first + bs - 1) // bs
+    val = []
+    for c in range(nb):
+        best = -np.inf
+        for j in range(c * bs, min((c + 1) * bs, first)):
+            if score[j] > best:
+                best = score[j]
+        val.append(best)
+    m = min(k // bs, nb)
+    winners = []
+    for sub in itertools.combinations(range(nb), m):
+        s = set(sub)
+        ok = all(val[i] > val[j] or (val[i] == val[j] and i < j)
+                 for i in s for j in range(nb) if j not in s)
+        if ok:
+            winners.append(s)
+    assert len(winners) == 1, "the definition must single out one set"
+    toks = set()
+    for c in winners[0]:
+        toks |= set(range(c * bs, min((c + 1) * bs, first)))
+    return sorted(toks | set(range(first, pos + 1))), val, winners[0]
+
+
+def pin_block_selection_brute_force(orc, seed=15, trials=80):
+    r = _rng(seed)
+    for _ in range(trials):
+        pos = int(r.integers(0, 30))
+        w = int(r.integers(0, 6))
+        bs = int(r.integers(2, 6))
+        k = bs * int(r.integers(0, 5)) + int(r.integers(0, bs))   # not always a multiple
+        score = r.integers(0, 4, size=pos + 1).astype(np.float64) / 8.0 + 1e-3
+        idx, tau, sigma = orc.select_blocks(score, pos, k, w, bs)
+        ref, val, won = _brute_force_blocks(score, pos, k, w, bs)
+        assert list(idx) == ref
+        if won:
+            assert tau == min(val[c] for c in won)
+        left = [c for c in range(len(val)) if c not in won]
+        if left:
+            assert sigma == max(val[c] for c in left)
+
+
+def pin_block_selection_special_cases(orc, seed=16):
+    """Blocks of one token are the token-level selection; equal scores keep the
+    lowest blocks; the selected older tokens are whole blocks."""
+    r = _rng(seed)
+    for pos, k, w in [(50, 10, 8), (7, 10, 8), (100, 0, 8), (30, 5, 0), (0, 4, 4)]:
+        score = r.random(pos + 1)
+        a = orc.select_blocks(score, pos, k, w, 1)
+        b = orc.select_tokens(score, pos, k, w)
+        assert a[0].tolist() == b[0].tolist()
+        np.testing.assert_equal(a[1:], b[1:])          # tau and sigma (nan when empty)
+    pos, k, w, bs = 70, 16, 6, 8
+    idx, _, _ = orc.select_blocks(np.full(pos + 1, 0.5), pos, k, w, bs)
+    assert idx.tolist() == list(range(16)) + list(range(65, 71))
+    score = r.random(pos + 1)
+    idx, tau, sigma = orc.select_blocks(score, pos, k, w, bs)
+    first = pos - w + 1
+    older = [i for i in idx.tolist() if i < first]
+    blocks = sorted(set(i // bs for i in older))
+    assert len(blocks) == k // bs
+    assert older == [j for c in blocks for j in range(c * bs, min((c + 1) * bs, first))]
+    assert tau >= sigma
+
+
 def pin_identical_keys_select_prefix(orc, seed=6):
     """All keys equal => all scores tie => idx = [0, k) followed by the window."""
     w = wl.small(batch=1, n_q_tokens=1, n_q_heads=4, n_kv_heads=1, head_dim=8, ctx_len=30,
@@ -378,4 +447,6 @@ ALL_PINS = [
     pin_bridge_brute_force,
     pin_bridge_closed_forms,
     pin_cache_append,
+    pin_block_selection_brute_force,
+    pin_block_selection_special_cases,
 ]

@@ -51,6 +51,17 @@ MUTANTS = [
      "k_out[:, :, pos0 + 1:pos0 + n + 1] = k_new[:, :, : k_out.shape[2] - pos0 - 1]"),
     ("append_values_from_keys", "v_out[:, :, pos0:pos0 + n] = v_new",
      "v_out[:, :, pos0:pos0 + n] = k_new"),
+    ("block_mean_not_max", "bscore = np.array([score[c * block:min((c + 1) * block, first)].max()",
+     "bscore = np.array([score[c * block:min((c + 1) * block, first)].mean()"),
+    ("block_ties_to_higher_index", "order = np.lexsort((blocks, -bscore))",
+     "order = np.lexsort((-blocks, -bscore))"),
+    ("block_last_partial_dropped", "n_blocks = (first + block - 1) // block",
+     "n_blocks = first // block"),
+    ("block_one_too_many", "n_take = min(top_k // block, n_blocks)",
+     "n_take = min(top_k // block + 1, n_blocks)"),
+    ("block_boundaries_shifted",
+     "toks = [np.arange(c * block, min((c + 1) * block, first), dtype=np.int64) for c in taken]",
+     "toks = [np.arange(c * block + 1, min((c + 1) * block + 1, first), dtype=np.int64) for c in taken]"),
 ]
 
 
