@@ -77,7 +77,7 @@ def algorithmic_full_layer_flops(w) -> int:
     return int(w.batch * w.n_q_heads * 4 * w.head_dim * int((pos + 1).sum()))
 
 
-def cpu_baseline(w, x, budget_s: float = 20.0):
+def cpu_baseline(w, x, budget_s: float = 20.0, block: int = 0):
     """Time the CPU oracle (as it stands) on whole (batch, query token, KV head)
     rows of the same inputs until the budget is used; scale to query tokens per
     second."""
@@ -94,7 +94,8 @@ def cpu_baseline(w, x, budget_s: float = 20.0):
     t0 = time.perf_counter()
     for r in rows:
         orc.cross_decoder_step(x["q_full"], x["k"], x["v"], x["q_sparse"], top_k=w.top_k,
-                               window=w.window, scale=w.scale, rows=[r], keep_scores=False)
+                               window=w.window, scale=w.scale, rows=[r], keep_scores=False,
+                               block=block)
         done += 1
         if time.perf_counter() - t0 > budget_s:
             break
@@ -108,6 +109,83 @@ def cpu_baseline(w, x, budget_s: float = 20.0):
                       f"{w.n_sparse_layers} sparse layers; {dt:.2f} s"}
 
 
+# KV Bridging workloads (the projection of Self-Decoder hidden states into the
+# cache): (batch, new tokens per batch entry, d_model, KV heads, cache capacity)
+BRIDGE_WORKLOADS = {
+    "bridge_prompt_128k": (1, 131072, 4096, 4, 131072),   # a whole 128K prompt
+    "bridge_append_b16": (16, 1, 4096, 4, 32768),         # decode-time append, batch 16
+}
+
+
+def bench_bridge(args, name):
+    """Time hs2_kv_bridge alone; one JSON line like the main benchmark's."""
+    import torch
+    from kv_reuse_amd import hs2
+    from kv_reuse_amd import workloads as wl
+
+    B, n, dm, Hkv, cap = BRIDGE_WORKLOADS[name]
+    D = 128
+    log(f"[bench] generating {name}")
+    hidden, w_kv = wl.bridge_inputs_device(B, n, dm, Hkv)
+    k = torch.empty((B, Hkv, cap, D), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty_like(k)
+    pos0 = cap - n
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        hs2.kv_bridge(hidden, w_kv, k, v, pos0)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        hs2.kv_bridge(hidden, w_kv, k, v, pos0)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    M = B * n
+    if M > 64:
+        flops = 2 * M * dm * 2 * Hkv * D
+        ach = flops / (ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "traffic": None, "kernel": "bridge_gemm_kernel", "algorithmic_flops": flops,
+                    "kernel_ms": round(ms, 5)}
+    else:
+        nbytes = 2 * Hkv * D * dm * 2 + M * dm * 2 + 2 * M * Hkv * D * 2
+        ach = nbytes / (ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                    "kernel": "bridge_small_kernel", "algorithmic_bytes": nbytes,
+                    "kernel_ms": round(ms, 5)}
+    rec = {"metric": "tokens/s projected into the Cross-Decoder KV cache (KV Bridging)",
+           "value": round(M / (ms * 1e-3), 2), "unit": "tokens/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic",
+           "config": {"workload": name, "batch": B, "n_tokens": n, "d_model": dm,
+                      "n_kv_heads": Hkv, "head_dim": D, "kv_capacity": cap},
+           "roofline": roofline, "wall_s_timed": round(wall, 4), "cpu_baseline": None}
+    if not args.no_cpu_baseline:
+        import oracle.hs2_oracle as orc
+        nt = min(M, 2048)
+        hb = hidden.reshape(M, dm)[:nt].view(torch.int16).cpu().numpy().view(np.uint16)
+        wb = w_kv.view(torch.int16).cpu().numpy().view(np.uint16)
+        reps = 0
+        t1 = time.perf_counter()
+        while reps == 0 or time.perf_counter() - t1 < 2.0:
+            orc.kv_bridge(hb.reshape(1, nt, dm), wb)
+            reps += 1
+        dt = time.perf_counter() - t1
+        # numpy's einsum contracts in its own single-threaded loops
+        rec["cpu_baseline"] = {"value": round(reps * nt / dt, 3), "unit": "tokens/s",
+                               "cores": 1, "kind": "oracle",
+                               "sample": f"{reps} x {nt} tokens of {name}: float64 projection "
+                                         f"into K and V of {Hkv} heads; {dt:.2f} s"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -115,6 +193,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_1m_b1_heavy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--select-block", type=int, default=0,
+                    help="time the block-level selection variant with this block size "
+                         "(0: the token-level selection of the method)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first run a plain device copy of this many MiB three times (the "
                          "reference kernel for scaling HBM byte counters)")
@@ -132,6 +213,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.workload in BRIDGE_WORKLOADS:
+        bench_bridge(args, args.workload)
+        return
     if args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -145,6 +229,9 @@ def main():
     log(f"[bench] generating {w.name}")
     x = wl.generate(w)
     s = hs2.shape_of(w)
+    if args.select_block:
+        import dataclasses
+        s = dataclasses.replace(s, select_block=args.select_block)
     B, T, Hq, Hkv, D, S, L = (w.batch, w.n_q_tokens, w.n_q_heads, w.n_kv_heads, w.head_dim,
                               w.ctx_len, w.n_sparse_layers)
 
@@ -215,7 +302,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": B, "n_q_tokens": T, "ctx_len": S,
                    "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": D, "top_k": w.top_k,
-                   "window": w.window, "n_sparse_layers": L},
+                   "window": w.window, "n_sparse_layers": L,
+                   "selection": (f"block_{args.select_block}" if args.select_block
+                                 else "token")},
         "roofline": roofline,
         "phases_ms": {"full_split": round(phases[0], 5), "full_combine": round(phases[1], 5),
                       "select": round(phases[2], 5), "sparse": round(phases[3], 5)},
@@ -223,7 +312,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
-        rec["cpu_baseline"] = cpu_baseline(w, x)
+        rec["cpu_baseline"] = cpu_baseline(w, x, block=args.select_block)
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec), flush=True)

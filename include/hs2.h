@@ -75,7 +75,15 @@ typedef struct hs2_shape {
   int32_t head_dim;   /* D */
   int32_t top_k;      /* k: older tokens chosen per row (1024 in the pages' experiments) */
   int32_t window;     /* w: most recent tokens always kept (128 in the pages' experiments) */
-  int32_t reserved;   /* must be 0 */
+  int32_t select_block;/* 0: token-level selection (this method).  A power of two in
+                         16..256: the previous generation's block-level variant, for
+                         comparison: the older tokens [0, P_t-w+1) are cut into aligned
+                         blocks of this many tokens (the last one ends at P_t-w+1), a
+                         block's importance is the largest importance of its tokens, and
+                         the top_k / select_block best blocks are kept, ties to the lower
+                         block; the window is kept as before.  Needs top_k to be a
+                         multiple of it and ceil(ctx_len / select_block) <= 16384; the
+                         fused step supports it in decode (n_q_tokens = 1) only. */
   int64_t kv_capacity;/* token rows per KV head in k and v, i.e. the cache's row pitch:
                          row j of head (b, g) starts at element ((b*Hkv + g)*kv_capacity + j)*D.
                          0 means ctx_len; otherwise it must be >= ctx_len.  Rows ctx_len ..

@@ -146,12 +146,13 @@ __global__ __launch_bounds__(kSmallWaves * 64) void bridge_small_kernel(BridgeAr
   const u16* hp = a.hidden + static_cast<size_t>(m) * a.dm + 8 * grp;
   const int nks = a.dm / 32;
   f32x4 acc{0.f, 0.f, 0.f, 0.f};
-  // wave w takes reduction steps w, w + 16, ...; four loads of each operand in
-  // flight per round
-  for (int s0 = wave; s0 < nks; s0 += 4 * kSmallWaves) {
-    u32x4 wv[4], hv[4];
+  // wave w takes reduction steps w, w + 16, ...; eight loads of each operand in
+  // flight per round (one round at d_model = 4096)
+  constexpr int kU = 8;
+  for (int s0 = wave; s0 < nks; s0 += kU * kSmallWaves) {
+    u32x4 wv[kU], hv[kU];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kU; ++u) {
       const int s = s0 + u * kSmallWaves;
       if (s < nks) {
         wv[u] = load_u32x4(wp + 32 * s);
@@ -159,7 +160,7 @@ __global__ __launch_bounds__(kSmallWaves * 64) void bridge_small_kernel(BridgeAr
       }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int u = 0; u < kU; ++u)
       if (s0 + u * kSmallWaves < nks) acc = mfma_16x16x32(as_bf16x8(wv[u]), as_bf16x8(hv[u]), acc);
   }
   red[wave][lane] = acc;

@@ -27,8 +27,14 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
   if (!sh || !p) return HS2_ERR_INVALID_ARG;
   if (sh->ctx_len < 1 || sh->batch < 1 || sh->n_q_tokens < 1 || sh->n_q_heads < 1 ||
       sh->n_kv_heads < 1 || sh->head_dim < 1 || sh->top_k < 0 || sh->window < 0 ||
-      n_layers < 0 || sh->reserved != 0)
+      n_layers < 0)
     return HS2_ERR_INVALID_ARG;
+  const int32_t bs = sh->select_block;
+  if (bs != 0) {
+    if (bs < 16 || bs > 256 || (bs & (bs - 1)) != 0 || sh->top_k % bs != 0)
+      return HS2_ERR_INVALID_ARG;
+    if ((sh->ctx_len + bs - 1) / bs > 16384) return HS2_ERR_UNSUPPORTED;
+  }
   if (!(sh->scale > 0.0) || !isfinite(sh->scale)) return HS2_ERR_INVALID_ARG;
   if (sh->n_q_tokens > sh->ctx_len) return HS2_ERR_INVALID_ARG;
   if (sh->kv_capacity != 0 && sh->kv_capacity < sh->ctx_len) return HS2_ERR_INVALID_ARG;
@@ -45,6 +51,7 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
   q.S = sh->ctx_len;
   q.Spad = static_cast<int64_t>(align_up(static_cast<size_t>(q.S), 64));
   q.kvp = sh->kv_capacity != 0 ? sh->kv_capacity : q.S;
+  q.bs = sh->select_block;
   q.B = sh->batch;
   q.T = sh->n_q_tokens;
   q.Hq = sh->n_q_heads;
@@ -237,6 +244,7 @@ int hs2_cross_decoder_step(const hs2_shape* shape, int32_t n_sparse_layers,
   if (st != HS2_OK) return st;
   if (!q_full || !k || !v || !out_full || !idx || !n_sel) return HS2_ERR_INVALID_ARG;
   if (n_sparse_layers > 0 && (!q_sparse || !out_sparse)) return HS2_ERR_INVALID_ARG;
+  if (p.T != 1 && p.bs != 0) return HS2_ERR_UNSUPPORTED;
   if ((st = check_ws(p, ws, ws_bytes)) != HS2_OK) return st;
   (void)hipGetLastError();
   const hipStream_t s = as_stream(stream);

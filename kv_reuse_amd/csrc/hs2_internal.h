@@ -43,6 +43,7 @@ constexpr int64_t kPrefillBandCap = 8192;  // near-threshold keys listed per pre
 struct Plan {
   int64_t S, Spad;
   int64_t kvp;               // K/V row pitch in tokens (the cache's capacity per head)
+  int bs;                    // block-level selection: block size (0 = token-level)
   int B, T, Hq, Hkv, R;      // R = B*T*Hkv rows
   int k, w, cap;             // cap = k + w (index list capacity per row)
   int n_layers;

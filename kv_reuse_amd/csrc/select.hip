@@ -1539,12 +1539,253 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
   if (tid == 0) nsel_out[r] = n_total;
 }
 
+// ================================================================ block-level selection
+//
+// The previous generation's variant (news page, section "Token级选择：精准定位
+// 大海里的那根针", which contrasts whole-block picks with token-level picks):
+// the older tokens [0, first) are cut into aligned blocks of bs tokens (the
+// last one ending at first), a block's importance is the largest importance of
+// its tokens, and the top_k / bs best blocks are kept, ties to the lower block
+// index; the window is forced as in the token-level selection.  Both kernels
+// below (fused, from the candidate lists, and from given scores) fill one
+// 64-bit key per block in LDS (0 = no key: below every real key), take the
+// threshold with the radix select of the token path, and emit.
+
+constexpr int kMaxBlocks = 16384;   // blocks per row held in LDS
+
+constexpr int kMaxSelBlocks = 256;  // top_k / block <= 4096 / 16
+
+// Select from the block keys (LDS, one per block, 0 = no key) and write the
+// row: the selected blocks' tokens in ascending order, the window, -1 padding,
+// and the count.  The keyed blocks are first compacted in place (block order
+// kept), so the radix select reads only them; the selected blocks' tokens are
+// then written by all threads at once.  All threads call it.
+__device__ __forceinline__ void emit_blocks(
+    uint64_t* bkey, int nblk, int bs, int64_t first, int P, int topk, int cap, int32_t* out,
+    int32_t* nsel_out, int r, uint32_t* sel_blk, uint32_t* sel_off, uint32_t* h256,
+    uint32_t* s_red, uint64_t* s_hi, uint32_t* s_need, int* s_done, uint32_t (*s_cnt)[16],
+    uint32_t* s_base) {
+  constexpr int kOwn = kMaxBlocks / kSelThreads;   // blocks owned per thread, at most
+  const int tid = threadIdx.x;
+  // thread t owns the consecutive blocks [t * per, (t + 1) * per)
+  const int per = (nblk + kSelThreads - 1) / kSelThreads;
+  const int c0 = min(nblk, tid * per), c1 = min(nblk, c0 + per);
+  uint32_t nzmask = 0;   // the owned blocks that have a key
+  {
+    uint64_t kr[kOwn];
+#pragma unroll
+    for (int u = 0; u < kOwn; ++u) {
+      kr[u] = c0 + u < c1 ? bkey[c0 + u] : 0ull;
+      nzmask |= (kr[u] != 0ull ? 1u : 0u) << u;
+    }
+    uint32_t p0, dummy;
+    reserve_two(__popc(nzmask), 0u, nullptr, nullptr, s_cnt, s_base, p0, dummy);  // reads done
+    uint32_t p = p0;
+#pragma unroll
+    for (int u = 0; u < kOwn; ++u)
+      if (kr[u] != 0ull) bkey[p++] = kr[u];
+  }
+  // after compaction the owned keyed blocks sit at pos0, pos0 + 1, ... in block order
+  uint32_t pos0, dummy;
+  reserve_two(__popc(nzmask), 0u, nullptr, nullptr, s_cnt, s_base, pos0, dummy);
+  const uint32_t n_nz = s_base[2];
+  const uint32_t need = min(static_cast<uint32_t>(topk / bs), n_nz);
+  const bool none = need == 0;
+  const bool all = !none && need >= n_nz;
+  KThr kt{0ull, 0u, true};
+  if (!none && !all) kt = key_threshold(bkey, n_nz, need, h256, s_red, s_hi, s_need, s_done);
+  // ties at the threshold go to the lowest blocks: rank them in block order
+  uint32_t n_tie = 0;
+  if (!none && !all && !kt.incl)
+    for (uint32_t i = 0; i < static_cast<uint32_t>(__popc(nzmask)); ++i)
+      n_tie += bkey[pos0 + i] == kt.thr ? 1u : 0u;
+  uint32_t tie0;
+  reserve_two(n_tie, 0u, nullptr, nullptr, s_cnt, s_base, tie0, dummy);
+  uint32_t selmask = 0, nsb = 0, ntok = 0;
+  {
+    uint32_t tr = tie0, i = 0;
+#pragma unroll
+    for (int u = 0; u < kOwn; ++u) {
+      if (!((nzmask >> u) & 1u)) continue;
+      const uint64_t key = bkey[pos0 + i++];
+      bool sel = false;
+      if (!none) {
+        if (all || key > kt.thr) sel = true;
+        else if (key == kt.thr) sel = kt.incl || tr++ < kt.nd_t;
+      }
+      if (sel) {
+        selmask |= 1u << u;
+        ++nsb;
+        ntok += static_cast<uint32_t>(
+            min(static_cast<int64_t>(bs), first - static_cast<int64_t>(c0 + u) * bs));
+      }
+    }
+  }
+  uint32_t sb, at;
+  reserve_two(nsb, ntok, nullptr, nullptr, s_cnt, s_base, sb, at);
+  const uint32_t n_sb = s_base[2], n_keep = s_base[3];
+  for (uint32_t m = selmask; m; m &= m - 1) {
+    const int u = __builtin_ctz(m);
+    sel_blk[sb] = static_cast<uint32_t>(c0 + u);
+    sel_off[sb] = at;
+    at += static_cast<uint32_t>(
+        min(static_cast<int64_t>(bs), first - static_cast<int64_t>(c0 + u) * bs));
+    ++sb;
+  }
+  if (tid == 0) sel_off[n_sb] = n_keep;
+  __syncthreads();
+  // the selected tokens, all threads: slot i lies in the last block whose offset is <= i
+  for (uint32_t i = tid; i < n_keep && i < static_cast<uint32_t>(cap); i += kSelThreads) {
+    uint32_t lo = 0, hi = n_sb - 1;
+    while (lo < hi) {
+      const uint32_t mid = (lo + hi + 1) >> 1;
+      if (sel_off[mid] <= i) lo = mid;
+      else hi = mid - 1;
+    }
+    out[i] = static_cast<int32_t>(sel_blk[lo] * static_cast<uint32_t>(bs) + (i - sel_off[lo]));
+  }
+  const int n_total =
+      static_cast<int>(n_keep) + static_cast<int>(static_cast<int64_t>(P) - first + 1);
+  for (int i = static_cast<int>(n_keep) + tid; i < cap; i += kSelThreads)
+    out[i] = i < n_total ? static_cast<int32_t>(first + (i - static_cast<int>(n_keep))) : -1;
+  if (tid == 0) nsel_out[r] = n_total;
+}
+
+// Fused decode: the candidate lists hold the exact float64 importance of every
+// key that can be the largest of a selectable block (such a block's best key
+// is among the best top_k keys, all of which the lists keep); a block's key is
+// the maximum over its listed keys.
+__global__ __launch_bounds__(kSelThreads) void block_row_select_kernel(
+    const double* __restrict__ cand_y, const int32_t* __restrict__ cand_idx,
+    const uint32_t* __restrict__ cand_cnt, int32_t* __restrict__ idx_out,
+    int32_t* __restrict__ nsel_out, int64_t S, int T, int Hkv, int topk, int w, int cap,
+    int chunk, int n_chunks, int bs) {
+  __shared__ uint64_t bkey[kMaxBlocks];
+  __shared__ uint32_t pre[kMaxChunks + 1];
+  __shared__ uint32_t sel_blk[kMaxSelBlocks];
+  __shared__ uint32_t sel_off[kMaxSelBlocks + 1];
+  __shared__ uint32_t h256[256];
+  __shared__ uint32_t s_red[4];
+  __shared__ uint64_t s_hi;
+  __shared__ uint32_t s_need;
+  __shared__ int s_done;
+  __shared__ uint32_t s_cnt[2][16];
+  __shared__ uint32_t s_base[4];
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int P = row_pos(r, T, Hkv, S);
+  const int64_t first = row_first(P, w);
+  const int nblk = static_cast<int>((first + bs - 1) / bs);
+  for (int c = tid; c < nblk; c += kSelThreads) bkey[c] = 0ull;
+  if (topk > 0 && first > 0) {
+    // chunk lengths, then their exclusive prefix in pre
+    constexpr int kPer = kMaxChunks / kSelThreads;
+    uint32_t cl[kPer];
+    uint32_t mysum = 0;
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int c = kPer * tid + u;
+      cl[u] = c < n_chunks ? cand_cnt[static_cast<size_t>(r) * n_chunks + c] : 0u;
+      mysum += cl[u];
+    }
+    uint32_t off, dummy;
+    reserve_two(mysum, 0u, nullptr, nullptr, s_cnt, s_base, off, dummy);
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int c = kPer * tid + u;
+      if (c < n_chunks) pre[c] = off;
+      off += cl[u];
+    }
+    if (tid == 0) pre[n_chunks] = s_base[2];
+    __syncthreads();
+    const uint32_t n_total = pre[n_chunks];
+    const size_t chunk_len = static_cast<size_t>(chunk) * kSubKeys;
+    const size_t rbase = static_cast<size_t>(r) * n_chunks * chunk_len;
+    // the entries spread evenly over the threads, four loads in flight each
+    constexpr int kU = 4;
+    for (uint32_t base = 0; base < n_total; base += kU * kSelThreads) {
+      double y[kU];
+      int32_t j[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const uint32_t i = base + u * kSelThreads + tid;
+        j[u] = -1;
+        if (i < n_total) {
+          int lo = 0, hi = n_chunks - 1;   // the chunk of entry i: largest c with pre[c] <= i
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (pre[mid] <= i) lo = mid;
+            else hi = mid - 1;
+          }
+          const size_t at = rbase + static_cast<size_t>(lo) * chunk_len + (i - pre[lo]);
+          y[u] = cand_y[at];
+          j[u] = cand_idx[at];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+        if (j[u] >= 0 && j[u] < first)
+          atomicMax(reinterpret_cast<unsigned long long*>(&bkey[j[u] / bs]),
+                    static_cast<unsigned long long>(ordered_u64(y[u])));
+    }
+  }
+  __syncthreads();
+  emit_blocks(bkey, nblk, bs, first, P, topk, cap, idx_out + static_cast<size_t>(r) * cap,
+              nsel_out, r, sel_blk, sel_off, h256, s_red, &s_hi, &s_need, &s_done, s_cnt,
+              s_base);
+}
+
+// From given scores [R][S] (compared exactly as given): a block's key is the
+// largest score of its older tokens.
+__global__ __launch_bounds__(kSelThreads) void block_scores_select_kernel(
+    const float* __restrict__ scores, int32_t* __restrict__ idx_out,
+    int32_t* __restrict__ nsel_out, int64_t S, int T, int Hkv, int topk, int w, int cap,
+    int bs) {
+  __shared__ uint64_t bkey[kMaxBlocks];
+  __shared__ uint32_t sel_blk[kMaxSelBlocks];
+  __shared__ uint32_t sel_off[kMaxSelBlocks + 1];
+  __shared__ uint32_t h256[256];
+  __shared__ uint32_t s_red[4];
+  __shared__ uint64_t s_hi;
+  __shared__ uint32_t s_need;
+  __shared__ int s_done;
+  __shared__ uint32_t s_cnt[2][16];
+  __shared__ uint32_t s_base[4];
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int P = row_pos(r, T, Hkv, S);
+  const int64_t first = row_first(P, w);
+  const int nblk = static_cast<int>((first + bs - 1) / bs);
+  const float* sr = scores + static_cast<size_t>(r) * S;
+  // each wave takes whole blocks: its lanes stride the block, then a wave max
+  for (int c = wave; c < nblk; c += kSelThreads / 64) {
+    const int64_t j0 = static_cast<int64_t>(c) * bs;
+    const int64_t j1 = min(first, j0 + bs);
+    uint32_t m = 0u;
+    for (int64_t j = j0 + lane; j < j1; j += 64) m = max(m, ordered_u32(sr[j]));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(m, off)));
+    // the low bit marks a real key, so that no block compares equal to "no key"
+    if (lane == 0) bkey[c] = (static_cast<uint64_t>(m) << 32) | 1ull;
+  }
+  __syncthreads();
+  emit_blocks(bkey, nblk, bs, first, P, topk, cap, idx_out + static_cast<size_t>(r) * cap,
+              nsel_out, r, sel_blk, sel_off, h256, s_red, &s_hi, &s_need, &s_done, s_cnt,
+              s_base);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- launchers
 
 hipError_t launch_scores_select(const Plan& p, const float* scores, int32_t* idx, int32_t* n_sel,
                                 void* ws, hipStream_t st) {
+  if (p.bs > 0) {
+    hipLaunchKernelGGL(block_scores_select_kernel, dim3(p.R), dim3(kSelThreads), 0, st, scores,
+                       idx, n_sel, p.S, p.T, p.Hkv, p.k, p.w, p.cap, p.bs);
+    return hipGetLastError();
+  }
   char* w = static_cast<char*>(ws);
   uint32_t* hist = reinterpret_cast<uint32_t*>(w + p.off_hist);
   RowInfo* info = reinterpret_cast<RowInfo*>(w + p.off_info);
@@ -1589,6 +1830,12 @@ hipError_t launch_fused_select(const Plan& p, const u16* q, const u16* k, int32_
                      lse2, ytop, hist, hist_c, q, k, cand_y, cand_idx, cand_cnt, p.S, p.Spad, p.T,
                      p.Hkv, p.k, p.w, p.sc_chunk, p.sc_nchunk, c2, p.kvp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (p.bs > 0) {
+    hipLaunchKernelGGL(block_row_select_kernel, dim3(p.R), dim3(kSelThreads), 0, st, cand_y,
+                       cand_idx, cand_cnt, idx, n_sel, p.S, p.T, p.Hkv, p.k, p.w, p.cap,
+                       p.sc_chunk, p.sc_nchunk, p.bs);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(row_select_kernel, dim3(p.R), dim3(kSelThreads), 0, st, hist_c, cand_y,
                      cand_idx, cand_cnt, ytop, idx, n_sel, p.S, p.T, p.Hkv, p.k, p.w, p.cap,
                      p.sc_chunk, p.sc_nchunk);

@@ -35,7 +35,7 @@ class Shape(ctypes.Structure):
                 ("batch", ctypes.c_int32), ("n_q_tokens", ctypes.c_int32),
                 ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("top_k", ctypes.c_int32),
-                ("window", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("select_block", ctypes.c_int32),
                 ("kv_capacity", ctypes.c_int64)]
 
 
@@ -92,13 +92,15 @@ class ShapeArgs:
     window: int = 128
     scale: Optional[float] = None
     kv_capacity: int = 0      # token rows per KV head in k / v; 0 = ctx_len
+    select_block: int = 0     # 0: token-level selection; else the block-level variant's block
 
     def c(self) -> Shape:
         scale = self.scale if self.scale is not None else 1.0 / math.sqrt(self.head_dim)
         return Shape(ctx_len=self.ctx_len, scale=scale, batch=self.batch,
                      n_q_tokens=self.n_q_tokens, n_q_heads=self.n_q_heads,
                      n_kv_heads=self.n_kv_heads, head_dim=self.head_dim, top_k=self.top_k,
-                     window=self.window, reserved=0, kv_capacity=self.kv_capacity)
+                     window=self.window, select_block=self.select_block,
+                     kv_capacity=self.kv_capacity)
 
     @property
     def rows(self) -> int:

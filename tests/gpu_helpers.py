@@ -49,10 +49,10 @@ def cache_with_capacity(bits: np.ndarray, capacity: int) -> torch.Tensor:
     return dev(full)
 
 
-def run_step(w: wl.Workload, x, with_scores=True, with_lse=True, kv_capacity=0):
+def run_step(w: wl.Workload, x, with_scores=True, with_lse=True, kv_capacity=0, block=0):
     import dataclasses
     from kv_reuse_amd import hs2
-    s = dataclasses.replace(hs2.shape_of(w), kv_capacity=kv_capacity)
+    s = dataclasses.replace(hs2.shape_of(w), kv_capacity=kv_capacity, select_block=block)
     B, T, Hq, Hkv, D, S, L = (w.batch, w.n_q_tokens, w.n_q_heads, w.n_kv_heads, w.head_dim,
                               w.ctx_len, w.n_sparse_layers)
     q = dev(x["q_full"])
@@ -105,12 +105,41 @@ def check_index_row(gi: np.ndarray, n: int, ref: dict, what: str, top_k: int, wi
     return len(sym)
 
 
-def compare_step(w: wl.Workload, x, res, check_scores=True, rows=None):
+def check_block_row(gi: np.ndarray, n: int, ref: dict, what: str, top_k: int, window: int,
+                    bs: int):
+    """Block-level selection: like check_index_row, with blocks in place of keys:
+    every block on which the GPU and the oracle differ has an importance (its
+    best key's) within 1e-6 (relative) of the oracle's block threshold tau."""
+    pos = ref["pos"]
+    row = gi[:n]
+    assert np.all(gi[n:] == -1), f"{what}: padding must be -1"
+    assert np.all(np.diff(row) > 0), f"{what}: indices must be strictly ascending"
+    assert n == ref["idx"].size, f"{what}: n_sel {n} vs oracle {ref['idx'].size}"
+    first = max(0, pos - window + 1)
+    assert set(range(first, pos + 1)) <= set(row.tolist()), f"{what}: window missing"
+    older = row[row < first]
+    blocks = sorted(set((older // bs).tolist()))
+    whole = [j for c in blocks for j in range(c * bs, min((c + 1) * bs, first))]
+    assert older.tolist() == whole, f"{what}: the selected older keys are not whole blocks"
+    ref_blocks = set((ref["idx"][ref["idx"] < first] // bs).tolist())
+    sym = set(blocks) ^ ref_blocks
+    if sym:
+        tau = ref["tau"]
+        sc = ref["score"]
+        bscore = {c: float(sc[c * bs:min((c + 1) * bs, first)].max()) for c in sym}
+        bad = [c for c in sym if abs(bscore[c] - tau) > BAND * tau]
+        assert not bad, (f"{what}: {len(bad)} blocks differ outside the 1e-6 band, e.g. "
+                         f"{[(c, bscore[c], tau) for c in bad[:3]]}")
+    return len(sym)
+
+
+def compare_step(w: wl.Workload, x, res, check_scores=True, rows=None, block=0):
     """Compare a whole step's GPU results with the oracle (on all rows, or on the
     given (b, t, g) rows); returns summary stats."""
     ref = orc.cross_decoder_step(x["q_full"], x["k"], x["v"],
                                  x["q_sparse"] if w.n_sparse_layers else None,
-                                 top_k=w.top_k, window=w.window, scale=w.scale, rows=rows)
+                                 top_k=w.top_k, window=w.window, scale=w.scale, rows=rows,
+                                 block=block)
     G = w.group
     stats = {"max_full": 0.0, "max_sparse": 0.0, "sym": 0}
     gpu_idx_oracle_sparse = []
@@ -121,8 +150,12 @@ def compare_step(w: wl.Workload, x, res, check_scores=True, rows=None):
         if "lse" in res:
             np.testing.assert_allclose(res["lse"][b, t, heads], rr["lse"], rtol=0, atol=2e-5)
         n = int(res["n_sel"][b, t, g])
-        stats["sym"] += check_index_row(res["idx"][b, t, g], n, rr, f"idx{(b, t, g)}",
-                                        w.top_k, w.window)
+        if block:
+            stats["sym"] += check_block_row(res["idx"][b, t, g], n, rr, f"idx{(b, t, g)}",
+                                            w.top_k, w.window, block)
+        else:
+            stats["sym"] += check_index_row(res["idx"][b, t, g], n, rr, f"idx{(b, t, g)}",
+                                            w.top_k, w.window)
         if check_scores and "scores" in res:
             pos = rr["pos"]
             gs = res["scores"][b, t, g]

@@ -68,7 +68,10 @@ def test_workspace_bytes_valid_and_monotone():
     ("batch", 0, hs2.HS2_ERR_INVALID_ARG),
     ("scale", -1.0, hs2.HS2_ERR_INVALID_ARG),
     ("scale", float("nan"), hs2.HS2_ERR_INVALID_ARG),
-    ("reserved", 7, hs2.HS2_ERR_INVALID_ARG),
+    ("select_block", 7, hs2.HS2_ERR_INVALID_ARG),       # not a power of two
+    ("select_block", 8, hs2.HS2_ERR_INVALID_ARG),       # below 16
+    ("select_block", 512, hs2.HS2_ERR_INVALID_ARG),     # above 256
+    ("select_block", 128, hs2.HS2_ERR_INVALID_ARG),     # top_k = 64 is not a multiple
     ("kv_capacity", 4999, hs2.HS2_ERR_INVALID_ARG),   # smaller than ctx_len
     ("kv_capacity", -1, hs2.HS2_ERR_INVALID_ARG),
     ("kv_capacity", 1 << 40, hs2.HS2_ERR_UNSUPPORTED),
@@ -174,3 +177,18 @@ def test_bridge_null_pointers_rejected():
         ptrs = [FAKE] * 4
         ptrs[i] = None
         assert lib.hs2_kv_bridge(ctypes.byref(c), *ptrs, None) == hs2.HS2_ERR_INVALID_ARG
+
+
+def test_block_selection_limits():
+    lib = hs2.raw()
+    c = good().c()
+    c.select_block = 32                      # top_k = 64: two blocks
+    assert lib.hs2_workspace_bytes(ctypes.byref(c), 2) > 0
+    c.ctx_len = 16384 * 32 + 1               # more than 16384 blocks
+    assert lib.hs2_workspace_bytes(ctypes.byref(c), 2) == 0
+    c = good().c()
+    c.select_block = 16
+    c.n_q_tokens = 4                         # the fused step: decode only
+    st = lib.hs2_cross_decoder_step(ctypes.byref(c), 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                    FAKE, None, None, FAKE, 1 << 40, None)
+    assert st == hs2.HS2_ERR_UNSUPPORTED
