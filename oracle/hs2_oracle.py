@@ -32,6 +32,12 @@ with query heads h in the GQA group {g*G, ..., g*G+G-1}:
      comparison the same section draws): the older tokens are cut into aligned
      blocks, a block's importance is the largest importance of its tokens, and
      top_k // block whole blocks are kept, ties to the lower block index.
+  4'. variant (the previous generation's sparse layer, the one the news page's
+     section "Token级选择" says was dropped together with its extra projections
+     and local cache): a sliding-window branch with the layer's own local K/V
+     for the w most recent positions, plus attention over the selected older
+     tokens of the shared cache, each with its own softmax; reading: the two
+     branch outputs are added (the pages give no gate).
   4. each sparse layer n attends with its own queries q^(n) to the selected
      rows of the same K/V only, with one softmax over selected + window
      (the same section: the separate sliding-window branch is dropped and local
@@ -312,3 +318,64 @@ def cache_append(k_cache: np.ndarray, v_cache: np.ndarray, k_new: np.ndarray,
     k_out[:, :, pos0:pos0 + n] = k_new
     v_out[:, :, pos0:pos0 + n] = v_new
     return k_out, v_out
+
+
+# ---------------------------------------------------------------------------
+# step 4': the separate sliding-window branch variant of a sparse layer
+# ---------------------------------------------------------------------------
+
+def attention_or_zero(q_g: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray,
+                      scale: float) -> np.ndarray:
+    """Softmax attention of the group's heads over the given rows; zeros when
+    there are no rows (an empty branch contributes nothing)."""
+    if k_rows.shape[0] == 0:
+        return np.zeros((q_g.shape[0], v_rows.shape[1]))
+    s = scale * (q_g @ k_rows.T)
+    s = s - s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    p = p / p.sum(axis=1, keepdims=True)
+    return p @ v_rows
+
+
+def sparse_swa_row(q_g: np.ndarray, k_rows: np.ndarray, v_rows: np.ndarray, sel: np.ndarray,
+                   kloc_rows: np.ndarray, vloc_rows: np.ndarray, scale: float) -> np.ndarray:
+    """One sparse layer with a separate sliding-window branch: attention over the
+    selected older rows of the shared cache plus attention over the layer's own
+    local rows of the window, each normalised on its own, summed."""
+    return (attention_or_zero(q_g, k_rows[sel], v_rows[sel], scale)
+            + attention_or_zero(q_g, kloc_rows, vloc_rows, scale))
+
+
+def sparse_swa_step(q: np.ndarray, k: np.ndarray, v: np.ndarray, idx: np.ndarray,
+                    n_sel: np.ndarray, k_loc: np.ndarray, v_loc: np.ndarray, *, scale: float,
+                    window: int) -> np.ndarray:
+    """The variant for every row and layer.
+
+    q [L][B][T][Hq][D], k / v [B][Hkv][S][D] (the shared cache), idx / n_sel as
+    the selection writes them (ascending, the window last: its entries are not
+    used here), k_loc / v_loc [L][B][Hkv][Lc][D] each layer's own local cache of
+    the last Lc = min(S, T + w - 1) positions (row i = position S - Lc + i).
+    Returns out [L][B][T][Hq][D] float64.
+    """
+    L, B, T, Hq, D = q.shape
+    _, Hkv, S, _ = k.shape
+    G = Hq // Hkv
+    Lc = k_loc.shape[3]
+    out = np.zeros((L, B, T, Hq, D))
+    for b in range(B):
+        for g in range(Hkv):
+            kk = widen_bf16(k[b, g])
+            vv = widen_bf16(v[b, g])
+            for t in range(T):
+                pos = S - T + t
+                first = max(0, pos - window + 1)
+                lst = np.asarray(idx[b, t, g, : int(n_sel[b, t, g])], dtype=np.int64)
+                sel = lst[lst < first]
+                rows = np.arange(first, pos + 1) - (S - Lc)
+                for n in range(L):
+                    qn = widen_bf16(q[n, b, t, g * G:(g + 1) * G])
+                    kl = widen_bf16(k_loc[n, b, g])[rows]
+                    vl = widen_bf16(v_loc[n, b, g])[rows]
+                    out[n, b, t, g * G:(g + 1) * G] = sparse_swa_row(qn, kk, vv, sel, kl, vl,
+                                                                      scale)
+    return out

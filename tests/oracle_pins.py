@@ -258,6 +258,70 @@ def pin_block_selection_special_cases(orc, seed=16):
     assert tau >= sigma
 
 
+def pin_swa_branch_vs_sdpa(orc, seed=17):
+    """The separate-window variant of a sparse layer is the sum of two softmax
+    attentions: checked against torch SDPA (float64) run on each branch's rows."""
+    r = _rng(seed)
+    G, D, S = 4, 16, 60
+    for n_sel, n_loc in [(10, 6), (0, 6), (10, 0), (1, 1)]:
+        q = r.standard_normal((G, D))
+        k = r.standard_normal((S, D))
+        v = r.standard_normal((S, D))
+        kl = r.standard_normal((n_loc, D))
+        vl = r.standard_normal((n_loc, D))
+        sel = np.sort(r.choice(S, size=n_sel, replace=False))
+        got = orc.sparse_swa_row(q, k, v, sel, kl, vl, 0.3)
+        ref = np.zeros((G, D))
+        if n_sel:
+            ref += _sdpa(q[:, None], np.broadcast_to(k[sel], (G, n_sel, D)).copy(),
+                         np.broadcast_to(v[sel], (G, n_sel, D)).copy(), 0.3)[:, 0]
+        if n_loc:
+            ref += _sdpa(q[:, None], np.broadcast_to(kl, (G, n_loc, D)).copy(),
+                         np.broadcast_to(vl, (G, n_loc, D)).copy(), 0.3)[:, 0]
+        np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+        perm = r.permutation(n_sel)
+        np.testing.assert_allclose(orc.sparse_swa_row(q, k, v, sel[perm], kl[::-1], vl[::-1], 0.3),
+                                   got, rtol=1e-12, atol=1e-12)
+
+
+def pin_swa_step_reads_the_window(orc, seed=18):
+    """The step's window branch reads exactly the local rows of positions
+    [P_t - w + 1, P_t], and the selected branch only the list's older entries:
+    with equal local keys the branch is the mean of the local values, which are
+    one-hot codes of their positions."""
+    r = _rng(seed)
+    L, B, T, Hkv, G, D, S, w = 2, 1, 3, 1, 8, 128, 50, 5
+    Lc = min(S, T + w - 1)
+    q = _bits(r.standard_normal((L, B, T, Hkv * G, D)))
+    k = _bits(r.standard_normal((B, Hkv, S, D)))
+    v = _bits(r.standard_normal((B, Hkv, S, D)))
+    k_loc = _bits(np.ones((L, B, Hkv, Lc, D)))
+    v_loc = np.zeros((L, B, Hkv, Lc, D), dtype=np.float32)
+    for i in range(Lc):
+        v_loc[:, :, :, i, (S - Lc + i) % D] = 1.0
+    v_loc = _bits(v_loc)
+    cap = 12
+    idx = np.full((B, T, Hkv, cap), -1, dtype=np.int32)
+    n_sel = np.zeros((B, T, Hkv), dtype=np.int32)
+    for t in range(T):
+        pos = S - T + t
+        lst = list(range(3 + t, 9 + t)) + list(range(pos - w + 1, pos + 1))
+        idx[0, t, 0, : len(lst)] = lst
+        n_sel[0, t, 0] = len(lst)
+    got = orc.sparse_swa_step(q, k, v, idx, n_sel, k_loc, v_loc, scale=0.1, window=w)
+    kk, vv = _f64(k[0, 0]), _f64(v[0, 0])
+    for t in range(T):
+        pos = S - T + t
+        sel = np.arange(3 + t, 9 + t)
+        for n in range(L):
+            qn = _f64(q[n, 0, t])
+            loc = np.zeros(D)
+            loc[[p % D for p in range(pos - w + 1, pos + 1)]] = 1.0 / w
+            ref = _sdpa(qn[:, None], np.broadcast_to(kk[sel], (G, sel.size, D)).copy(),
+                        np.broadcast_to(vv[sel], (G, sel.size, D)).copy(), 0.1)[:, 0] + loc
+            np.testing.assert_allclose(got[n, 0, t], ref, rtol=1e-12, atol=1e-12)
+
+
 def pin_identical_keys_select_prefix(orc, seed=6):
     """All keys equal => all scores tie => idx = [0, k) followed by the window."""
     w = wl.small(batch=1, n_q_tokens=1, n_q_heads=4, n_kv_heads=1, head_dim=8, ctx_len=30,
@@ -449,4 +513,6 @@ ALL_PINS = [
     pin_cache_append,
     pin_block_selection_brute_force,
     pin_block_selection_special_cases,
+    pin_swa_branch_vs_sdpa,
+    pin_swa_step_reads_the_window,
 ]

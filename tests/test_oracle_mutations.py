@@ -62,6 +62,14 @@ MUTANTS = [
     ("block_boundaries_shifted",
      "toks = [np.arange(c * block, min((c + 1) * block, first), dtype=np.int64) for c in taken]",
      "toks = [np.arange(c * block + 1, min((c + 1) * block + 1, first), dtype=np.int64) for c in taken]"),
+    ("swa_branch_dropped", "+ attention_or_zero(q_g, kloc_rows, vloc_rows, scale))",
+     "+ 0.0 * attention_or_zero(q_g, kloc_rows, vloc_rows, scale))"),
+    ("swa_keeps_window_entries", "sel = lst[lst < first]", "sel = lst"),
+    ("swa_local_rows_shifted", "rows = np.arange(first, pos + 1) - (S - Lc)",
+     "rows = np.arange(first, pos + 1) - (S - Lc) - 1"),
+    ("swa_local_from_shared_cache", "kl = widen_bf16(k_loc[n, b, g])[rows]", "kl = kk[first:pos + 1]"),
+    ("swa_branch_unnormalised", "    p = p / p.sum(axis=1, keepdims=True)\n    return p @ v_rows",
+     "    return p @ v_rows"),
 ]
 
 
