@@ -193,6 +193,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_1m_b1_heavy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--swa-branch", action="store_true",
+                    help="time the previous generation's sparse layers instead: a separate "
+                         "sliding-window branch over each layer's own local cache plus the "
+                         "selected older tokens")
     ap.add_argument("--select-block", type=int, default=0,
                     help="time the block-level selection variant with this block size "
                          "(0: the token-level selection of the method)")
@@ -246,8 +250,17 @@ def main():
     ws = hs2.alloc_workspace(s, L)
     torch.cuda.synchronize()
 
-    def step():
-        hs2.cross_decoder_step(s, q, qs, k, v, out, outs, idx, nsel, ws=ws)
+    if args.swa_branch:
+        Lc = hs2.local_rows(s)
+        kl_b, vl_b = wl.swa_local_cache(L, B, Hkv, Lc)
+        k_loc, v_loc = dev(kl_b), dev(vl_b)
+
+        def step():
+            hs2.cross_decoder_step(s, q, None, k, v, out, None, idx, nsel, ws=ws)
+            hs2.sparse_attn_swa(s, qs, k, v, idx, nsel, k_loc, v_loc, outs, ws=ws)
+    else:
+        def step():
+            hs2.cross_decoder_step(s, q, qs, k, v, out, outs, idx, nsel, ws=ws)
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -304,13 +317,14 @@ def main():
                    "n_q_heads": Hq, "n_kv_heads": Hkv, "head_dim": D, "top_k": w.top_k,
                    "window": w.window, "n_sparse_layers": L,
                    "selection": (f"block_{args.select_block}" if args.select_block
-                                 else "token")},
+                                 else "token"),
+                   "sparse_layers": "separate_window_branch" if args.swa_branch else "shared"},
         "roofline": roofline,
         "phases_ms": {"full_split": round(phases[0], 5), "full_combine": round(phases[1], 5),
                       "select": round(phases[2], 5), "sparse": round(phases[3], 5)},
         "wall_s_timed": round(wall, 4),
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.swa_branch:
         log("[bench] cpu baseline (oracle)")
         rec["cpu_baseline"] = cpu_baseline(w, x, block=args.select_block)
     else:

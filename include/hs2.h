@@ -140,6 +140,27 @@ int hs2_sparse_attn(const hs2_shape* shape, int32_t n_layers, const hs2_bf16* q,
                     const int32_t* n_sel, hs2_bf16* out, void* ws, size_t ws_bytes,
                     void* stream);
 
+/* The previous generation's sparse layer, for comparison: a separate sliding-
+ * window branch with the layer's own local K/V, next to attention over the
+ * selected older tokens of the shared cache (news page, section
+ * "Token级选择：精准定位大海里的那根针": HySparse2 drops this branch and its
+ * extra projections and local cache, and forces the window into the shared
+ * selection instead).  For layer n and head h of row (b, t, g):
+ *   out = softmax(scale q k_sel) . V_sel  +  softmax(scale q k_loc_win) . v_loc_win
+ * where sel = the entries of idx below P_t - w + 1 (the window entries that the
+ * selection appends to the list are not read), and win = the local rows of
+ * positions [max(0, P_t - w + 1), P_t].  Each branch has its own softmax; the
+ * pages give no gate, so the two outputs are added.  An empty branch adds 0.
+ *   k_loc, v_loc  [N][B][Hkv][Lc][D] bf16, Lc = min(S, T + w - 1): each layer's
+ *                 local cache of the positions S - Lc .. S - 1 (row i holds
+ *                 position S - Lc + i); with no rows (w = 0 in decode) they
+ *                 may be NULL
+ * Other arguments as in hs2_sparse_attn (k, v read with the kv_capacity pitch). */
+int hs2_sparse_attn_swa(const hs2_shape* shape, int32_t n_layers, const hs2_bf16* q,
+                        const hs2_bf16* k, const hs2_bf16* v, const int32_t* idx,
+                        const int32_t* n_sel, const hs2_bf16* k_loc, const hs2_bf16* v_loc,
+                        hs2_bf16* out, void* ws, size_t ws_bytes, void* stream);
+
 /* One Cross-Decoder group step: full attention with importance, selection,
  * then n_sparse_layers sparse layers — the same results as the three calls
  * above in sequence, except that the selection here ranks keys by importance

@@ -141,6 +141,7 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
   q.off_sp_m = take(sp_parts * sizeof(float));
   q.off_sp_l = take(sp_parts * sizeof(float));
   q.off_sp_o = take(sp_parts * kD * sizeof(float));
+  q.off_swa = take(Rz * static_cast<size_t>(n_layers) * kG * kD * sizeof(float));
   q.total = off;
   *p = q;
   return HS2_OK;
@@ -343,6 +344,25 @@ int hs2_kv_bridge(const hs2_bridge_shape* shape, const hs2_bf16* hidden, const h
   a.Hkv = s.n_kv_heads;
   (void)hipGetLastError();
   HS2_TRY(launch_kv_bridge(a, as_stream(stream)));
+  return HS2_OK;
+}
+
+int hs2_sparse_attn_swa(const hs2_shape* shape, int32_t n_layers, const hs2_bf16* q,
+                        const hs2_bf16* k, const hs2_bf16* v, const int32_t* idx,
+                        const int32_t* n_sel, const hs2_bf16* k_loc, const hs2_bf16* v_loc,
+                        hs2_bf16* out, void* ws, size_t ws_bytes, void* stream) {
+  Plan p;
+  int st = make_plan(shape, n_layers, &p);
+  if (st != HS2_OK) return st;
+  if (n_layers < 1 || !q || !k || !v || !idx || !n_sel || !out) return HS2_ERR_INVALID_ARG;
+  // the local caches have min(S, T + w - 1) rows: none (and may be NULL) when w = 0, T = 1
+  const bool has_local = std::min<int64_t>(p.S, static_cast<int64_t>(p.T) + p.w - 1) > 0;
+  if (has_local && (!k_loc || !v_loc)) return HS2_ERR_INVALID_ARG;
+  if ((st = check_ws(p, ws, ws_bytes)) != HS2_OK) return st;
+  (void)hipGetLastError();
+  static const hs2_bf16 kNoRows = 0;   // the window branch reads nothing when there are no rows
+  HS2_TRY(launch_sparse(p, q, k, v, idx, n_sel, out, ws, as_stream(stream),
+                        k_loc ? k_loc : &kNoRows, v_loc ? v_loc : &kNoRows));
   return HS2_OK;
 }
 

@@ -66,6 +66,7 @@ struct Plan {
   // sparse
   int sp_nch;
   size_t off_sp_m, off_sp_l, off_sp_o;
+  size_t off_swa;            // the window branch's outputs [L][R][G][D] float32
   size_t total;
 };
 
@@ -118,7 +119,7 @@ hipError_t launch_prefill_select(const Plan& p, const u16* q, const u16* k, int3
 // Sparse layers (all n_layers fused: one gather of the selected K/V rows).
 hipError_t launch_sparse(const Plan& p, const u16* q, const u16* k, const u16* v,
                          const int32_t* idx, const int32_t* n_sel, u16* out, void* ws,
-                         hipStream_t st);
+                         hipStream_t st, const u16* k_loc = nullptr, const u16* v_loc = nullptr);
 
 // ---------------------------------------------------------------- device helpers
 #ifdef __HIPCC__

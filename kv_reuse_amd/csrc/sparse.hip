@@ -16,6 +16,8 @@
 //    spread over work-groups, and a combine kernel merges the slices; a
 //    prefill chunk has enough rows to give each row one work-group.
 
+#include <algorithm>
+
 #include "hs2_internal.h"
 
 namespace hs2 {
@@ -30,7 +32,8 @@ __global__ __launch_bounds__(NCT * 64) void sparse_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ n_sel, u16* __restrict__ out,
     float* __restrict__ part_m, float* __restrict__ part_l, float* __restrict__ part_o,
     int64_t S, int T, int Hkv, int L, int layer0, int cap, int nch, int keys_per_wg,
-    float c2_hi, float c2_lo, size_t layer_stride, int64_t kvp) {
+    float c2_hi, float c2_lo, size_t layer_stride, int64_t kvp, int w_drop,
+    const float* __restrict__ swa_add) {
   __shared__ __align__(16) u16 klds[kSub * kPitch];
   __shared__ __align__(16) u16 vlds[kSub * kPitch];
   __shared__ int32_t sidx[kSub];
@@ -47,7 +50,14 @@ __global__ __launch_bounds__(NCT * 64) void sparse_kernel(
   const size_t kvrow = static_cast<size_t>(b) * Hkv + g;
   const u16* kr = k + kvrow * static_cast<size_t>(kvp) * kD;
   const u16* vr = v + kvrow * static_cast<size_t>(kvp) * kD;
-  const int ns = n_sel[r];
+  int ns = n_sel[r];
+  if (w_drop >= 0) {
+    // the separate-window variant: the window's entries (the last ones of the
+    // ascending list) are left to the window branch
+    const int64_t P = S - T + (r / Hkv) % T;
+    const int64_t nwin = P - max(static_cast<int64_t>(0), P - w_drop + 1) + 1;
+    ns = static_cast<int>(max(static_cast<int64_t>(0), ns - nwin));
+  }
   const int pos_begin = ch * keys_per_wg;
   const int pos_end = min(ns, pos_begin + keys_per_wg);
 
@@ -155,7 +165,14 @@ __global__ __launch_bounds__(NCT * 64) void sparse_kernel(
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) orow[16 * nb + 4 * grp + i] = f32_to_bf16_rne(o[nb][i] * inv);
+      for (int i = 0; i < 4; ++i) {
+        const int d = 16 * nb + 4 * grp + i;
+        // the window branch's output, [L][R][G][D] (grid.y = R)
+        const float add =
+            swa_add ? swa_add[((static_cast<size_t>(layer) * gridDim.y + r) * kG + head) * kD + d]
+                    : 0.f;
+        orow[d] = f32_to_bf16_rne(o[nb][i] * inv + add);
+      }
   } else {
     const size_t pb = ((static_cast<size_t>(r) * nch + ch) * L + layer) * kG + head;
     if (grp == 0) {
@@ -170,12 +187,113 @@ __global__ __launch_bounds__(NCT * 64) void sparse_kernel(
   }
 }
 
+// The separate sliding-window branch of the previous generation's sparse layer
+// (news page, section "Token级选择：精准定位大海里的那根针": the branch and its
+// local cache are what HySparse2 drops).  grid (R, L), one wave: layer n's own
+// local K/V rows of the window [P - w + 1, P] (the local cache holds positions
+// S - Lc .. S - 1), softmax over them, normalised output per head in float32
+// to swa_out [L][R][G][D], which the sparse kernel then adds to the selected
+// branch's output.  An empty window gives zeros.
+__global__ __launch_bounds__(64) void swa_branch_kernel(
+    const u16* __restrict__ q, const u16* __restrict__ k_loc, const u16* __restrict__ v_loc,
+    float* __restrict__ swa_out, int64_t S, int B, int T, int Hkv, int w, int64_t Lc,
+    float c2_hi, float c2_lo, size_t layer_stride) {
+  __shared__ __align__(16) u16 klds[32 * kPitch];
+  __shared__ __align__(16) u16 vlds[32 * kPitch];
+  const int r = blockIdx.x, n = blockIdx.y;
+  const int R = gridDim.x;
+  const int lane = threadIdx.x;
+  const int col = lane & 15, grp = lane >> 4;
+  const int b = r / (T * Hkv), t = (r / Hkv) % T, g = r % Hkv;
+  const int64_t P = S - T + t;
+  const int64_t first = max(static_cast<int64_t>(0), P - w + 1);
+  const int nk = static_cast<int>(P - first + 1);
+  const size_t cache = ((static_cast<size_t>(n) * B + b) * Hkv + g) * static_cast<size_t>(Lc);
+  const int64_t row0 = first - (S - Lc);
+  const u16* kl = k_loc + (cache + row0) * kD;
+  const u16* vl = v_loc + (cache + row0) * kD;
+  bf16x8 qb[4];
+  {
+    const u16* qr = q + static_cast<size_t>(n) * layer_stride +
+                    (static_cast<size_t>(r) * kG + (col & 7)) * kD;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      qb[c] = col < kG ? as_bf16x8(load_u32x4(qr + 32 * c + 8 * grp))
+                       : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+  }
+  f32x4 o[8];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  for (int kb = 0; kb < nk; kb += 32) {
+    const int n_here = min(32, nk - kb);
+    // 32 rows of K and V, 16 pieces of 16 bytes each: 8 pieces per lane (rows
+    // past the window repeat its last row and are masked below)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int pc = lane + 64 * u;
+      const int key = pc >> 4, c16 = pc & 15;
+      const size_t row = static_cast<size_t>(kb + min(key, n_here - 1));
+      *reinterpret_cast<u32x4*>(klds + key * kPitch + 8 * c16) = load_u32x4(kl + row * kD + 8 * c16);
+      *reinterpret_cast<u32x4*>(vlds + key * kPitch + 8 * c16) = load_u32x4(vl + row * kD + 8 * c16);
+    }
+    __syncthreads();
+    f32x4 sacc[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      sacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const u16* krow = klds + (16 * mt + col) * kPitch + 8 * grp;
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        sacc[mt] = mfma_16x16x32(as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 32 * c)),
+                                 qb[c], sacc[mt]);
+    }
+    float sv[8];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kk = 16 * mt + 4 * grp + i;
+        const float a = sacc[mt][i];
+        sv[mt * 4 + i] = kk < n_here ? fmaf(a, c2_hi, a * c2_lo) : -INFINITY;
+      }
+    float tm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                     fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+    tm = fmaxf(tm, __shfl_xor(tm, 16));
+    tm = fmaxf(tm, __shfl_xor(tm, 32));
+    const float m_new = fmaxf(m_run, tm);
+    const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    float p[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(sv[e] - m_new);
+    l_run = l_run * alpha + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
+    m_run = m_new;
+    const bf16x8 pb = as_bf16x8(u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                      pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])});
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      o[nb] *= alpha;
+      o[nb] = mfma_16x16x32(lds_vt_operand(vlds, kPitch, nb, col, grp), pb, o[nb]);
+    }
+    __syncthreads();   // the tile is consumed before the next one is staged
+  }
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (col >= kG) return;
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  float* dst = swa_out + ((static_cast<size_t>(n) * R + r) * kG + col) * kD;
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[16 * nb + 4 * grp + i] = o[nb][i] * inv;
+}
+
 // grid (R, L): merge the slices of one row and layer.  The slices' maxima and
 // sums go through LDS first, so the O loads below are independent of each other.
 __global__ __launch_bounds__(256) void sparse_combine_kernel(
     const float* __restrict__ part_m, const float* __restrict__ part_l,
     const float* __restrict__ part_o, u16* __restrict__ out, int L, int nch,
-    size_t layer_stride) {
+    size_t layer_stride, const float* __restrict__ swa_add) {
   extern __shared__ float fac[];   // [nch][kG]
   __shared__ float inv_l[kG];
   const int r = blockIdx.x;
@@ -212,14 +330,17 @@ __global__ __launch_bounds__(256) void sparse_combine_kernel(
   }
   if (c < nch) a0 += fac[c * kG + h] * po[c * cstride];
   out[static_cast<size_t>(layer) * layer_stride + static_cast<size_t>(r) * kG * kD + i] =
-      f32_to_bf16_rne((a0 + a1) * inv_l[h]);
+      f32_to_bf16_rne((a0 + a1) * inv_l[h] +
+                      (swa_add ? swa_add[(static_cast<size_t>(layer) * gridDim.x + r) * kG * kD + i]
+                               : 0.f));
 }
 
 }  // namespace
 
 hipError_t launch_sparse(const Plan& p, const u16* q, const u16* k, const u16* v,
                          const int32_t* idx, const int32_t* n_sel, u16* out, void* ws,
-                         hipStream_t st) {
+                         hipStream_t st, const u16* k_loc, const u16* v_loc) {
+  const bool swa = k_loc != nullptr;
   char* w = static_cast<char*>(ws);
   const double c2 = p.scale * 1.4426950408889634;
   const float c2_hi = static_cast<float>(c2);
@@ -229,6 +350,15 @@ hipError_t launch_sparse(const Plan& p, const u16* q, const u16* k, const u16* v
   float* pm = reinterpret_cast<float*>(w + p.off_sp_m);
   float* pl = reinterpret_cast<float*>(w + p.off_sp_l);
   float* po = reinterpret_cast<float*>(w + p.off_sp_o);
+  float* swa_out = swa ? reinterpret_cast<float*>(w + p.off_swa) : nullptr;
+  if (swa) {
+    const int64_t Lc = std::min<int64_t>(p.S, static_cast<int64_t>(p.T) + p.w - 1);
+    hipLaunchKernelGGL(swa_branch_kernel, dim3(p.R, p.n_layers), dim3(64), 0, st, q, k_loc,
+                       v_loc, swa_out, p.S, p.B, p.T, p.Hkv, p.w, Lc, c2_hi, c2_lo,
+                       layer_stride);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   for (int layer0 = 0; layer0 < p.n_layers; layer0 += 8) {
     const int nl = min(8, p.n_layers - layer0);
     const int nct = (nl + 1) / 2;
@@ -236,7 +366,7 @@ hipError_t launch_sparse(const Plan& p, const u16* q, const u16* k, const u16* v
     auto go = [&](auto kern) {
       hipLaunchKernelGGL(kern, grid, dim3(nct * 64), 0, st, q, k, v, idx, n_sel, out, pm, pl, po,
                          p.S, p.T, p.Hkv, p.n_layers, layer0, p.cap, p.sp_nch, keys_per_wg, c2_hi,
-                         c2_lo, layer_stride, p.kvp);
+                         c2_lo, layer_stride, p.kvp, swa ? p.w : -1, swa_out);
     };
     switch (nct) {
       case 1: go(sparse_kernel<1>); break;
@@ -250,7 +380,7 @@ hipError_t launch_sparse(const Plan& p, const u16* q, const u16* k, const u16* v
   if (p.sp_nch > 1) {
     hipLaunchKernelGGL(sparse_combine_kernel, dim3(p.R, p.n_layers, 4), dim3(256),
                        static_cast<size_t>(p.sp_nch) * kG * sizeof(float), st, pm, pl, po,
-                       out, p.n_layers, p.sp_nch, layer_stride);
+                       out, p.n_layers, p.sp_nch, layer_stride, swa_out);
     return hipGetLastError();
   }
   return hipSuccess;

@@ -27,6 +27,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 HS2_OK, HS2_ERR_INVALID_ARG, HS2_ERR_UNSUPPORTED, HS2_ERR_WORKSPACE, HS2_ERR_HIP = 0, -1, -2, -3, -4
 EXPORTED = ["hs2_workspace_bytes", "hs2_full_attn_scores", "hs2_topk_select", "hs2_sparse_attn",
             "hs2_cross_decoder_step", "hs2_cross_decoder_step_timed", "hs2_kv_bridge",
+            "hs2_sparse_attn_swa",
             "hs2_status_string", "hs2_last_hip_error"]
 
 
@@ -63,6 +64,9 @@ _lib.hs2_cross_decoder_step_timed.argtypes = [_SP, ctypes.c_int32, _P, _P, _P, _
                                               _P, _P, ctypes.c_size_t, _P, ctypes.c_int32,
                                               ctypes.POINTER(ctypes.c_float)]
 _lib.hs2_cross_decoder_step_timed.restype = ctypes.c_int
+_lib.hs2_sparse_attn_swa.argtypes = [_SP, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                     ctypes.c_size_t, _P]
+_lib.hs2_sparse_attn_swa.restype = ctypes.c_int
 _lib.hs2_kv_bridge.argtypes = [ctypes.POINTER(BridgeShape), _P, _P, _P, _P, _P]
 _lib.hs2_kv_bridge.restype = ctypes.c_int
 _lib.hs2_status_string.argtypes = [ctypes.c_int]
@@ -256,3 +260,27 @@ def kv_bridge(hidden, w_kv, k, v, pos0: int):
                      n_kv_heads=Hkv, head_dim=D, reserved=0)
     _call("hs2_kv_bridge", _lib.hs2_kv_bridge(ctypes.byref(sh), _ptr(hidden), _ptr(w_kv), _ptr(k),
                                               _ptr(v), _stream()))
+
+
+def local_rows(s: ShapeArgs) -> int:
+    """Rows of each layer's local window cache for the separate-window variant."""
+    return min(s.ctx_len, s.n_q_tokens + s.window - 1)
+
+
+def sparse_attn_swa(s: ShapeArgs, q, k, v, idx, n_sel, k_loc, v_loc, out, ws=None):
+    """The separate sliding-window branch variant of the sparse layers."""
+    B, T, Hq, Hkv, D = s.batch, s.n_q_tokens, s.n_q_heads, s.n_kv_heads, s.head_dim
+    L = q.shape[0]
+    Lc = local_rows(s)
+    _check(q, "q", torch.bfloat16, (L, B, T, Hq, D))
+    _check(k, "k", torch.bfloat16, (B, Hkv, s.kv_rows, D))
+    _check(v, "v", torch.bfloat16, (B, Hkv, s.kv_rows, D))
+    _check(idx, "idx", torch.int32, (B, T, Hkv, s.cap))
+    _check(n_sel, "n_sel", torch.int32, (B, T, Hkv))
+    _check(k_loc, "k_loc", torch.bfloat16, (L, B, Hkv, Lc, D))
+    _check(v_loc, "v_loc", torch.bfloat16, (L, B, Hkv, Lc, D))
+    _check(out, "out", torch.bfloat16, (L, B, T, Hq, D))
+    ws = alloc_workspace(s, L) if ws is None else ws
+    _call("hs2_sparse_attn_swa", _lib.hs2_sparse_attn_swa(
+        ctypes.byref(s.c()), L, _ptr(q), _ptr(k), _ptr(v), _ptr(idx), _ptr(n_sel), _ptr(k_loc),
+        _ptr(v_loc), _ptr(out), _ptr(ws), ws.numel(), _stream()))

@@ -264,3 +264,14 @@ def bridge_inputs_device(batch: int, n_tokens: int, d_model: int, n_kv_heads: in
     w = torch.randn((2, n_kv_heads, head_dim, d_model), generator=g, device="cuda",
                     dtype=torch.float32) * (1.0 / float(np.sqrt(d_model)))
     return hidden, w.to(torch.bfloat16)
+
+
+def swa_local_cache(n_layers: int, batch: int, n_kv_heads: int, rows: int, head_dim: int = 128,
+                    seed: int = BASE_SEED + 80):
+    """Each sparse layer's own local window cache for the separate-window
+    variant, (k_loc, v_loc) [L][B][Hkv][rows][D] bf16 bits, N(0, 1) entries like
+    the shared cache; streams spawned in the order k_loc, v_loc."""
+    ss = np.random.SeedSequence(seed)
+    rk, rv = (np.random.default_rng(c) for c in ss.spawn(2))
+    shape = (n_layers, batch, n_kv_heads, rows, head_dim)
+    return f32_to_bf16_bits(_normal_f32(rk, shape)), f32_to_bf16_bits(_normal_f32(rv, shape))
