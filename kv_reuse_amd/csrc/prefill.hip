@@ -348,7 +348,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_importance_kernel(
   int jloc[2];
   bool t_ok[2];
   int64_t P[2], first[2];
-  float l2r[2][4];
+  float nl2r[2][4];     // -lse2 of the lane's 4 heads
   float* yrow[2];
   float* srow[2];
 #pragma unroll
@@ -367,7 +367,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_importance_kernel(
     first[qbk] = max(static_cast<int64_t>(0), P[qbk] - w + 1);
     const size_t row = (static_cast<size_t>(b) * T + t) * Hkv + g;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) l2r[qbk][i] = static_cast<float>(lse2[row * kG + 4 * (grp & 1) + i]);
+    for (int i = 0; i < 4; ++i) nl2r[qbk][i] = -static_cast<float>(lse2[row * kG + 4 * (grp & 1) + i]);
     yrow[qbk] = y ? y + row * Spad : nullptr;
     srow[qbk] = scores ? scores + row * S : nullptr;
   }
@@ -404,16 +404,16 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_importance_kernel(
     }
 #pragma unroll
     for (int qbk = 0; qbk < 2; ++qbk) {
-      // y per (token, key): max over the 8 heads = 4 here x the partner lane
+      // y per (token, key): max over the 8 heads = 4 here x the partner lane.
+      // One fma per head: the scale's low part (a * c2_lo, below 1e-7 in log2
+      // units) is dropped; it is smaller than the float32 rounding of y, and
+      // the selection re-ranks every key near its threshold in float64
       float yv[4];
 #pragma unroll
       for (int sub = 0; sub < 4; ++sub) {
         float m = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float a = sacc[qbk][sub][i];
-          m = fmaxf(m, fmaf(a, c2_hi, a * c2_lo) - l2r[qbk][i]);
-        }
+        for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaf(sacc[qbk][sub][i], c2_hi, nl2r[qbk][i]));
         yv[sub] = fmaxf(m, __shfl_xor(m, 16));
       }
 #pragma unroll

@@ -393,7 +393,7 @@ __device__ void emit_row(const int32_t* tmp, int32_t* xch, int n_keep, int64_t f
   const int n_total = n_keep + static_cast<int>(static_cast<int64_t>(P) - first + 1);
   for (int i = n_keep + threadIdx.x; i < cap; i += blockDim.x)
     out[i] = i < n_total ? static_cast<int32_t>(first + (i - n_keep)) : -1;
-  if (threadIdx.x == 0) *nsel_out = n_total;
+  if (threadIdx.x == 0) *nsel_out = min(n_total, cap);
 }
 
 // ================================================================ path A
@@ -1137,13 +1137,13 @@ __global__ __launch_bounds__(kSelThreads) void row_select_kernel(
       }
     }
     const uint32_t written = sel_seen + min(tie_seen, nd_t);
-    n_keep = written;
+    n_keep = min(written, static_cast<uint32_t>(topk));
   }
   __syncthreads();
   const int n_total_sel = static_cast<int>(n_keep) + static_cast<int>(static_cast<int64_t>(P) - first + 1);
   for (int i = static_cast<int>(n_keep) + tid; i < cap; i += kSelThreads)
     out[i] = i < n_total_sel ? static_cast<int32_t>(first + (i - static_cast<int>(n_keep))) : -1;
-  if (tid == 0) nsel_out[r] = n_total_sel;
+  if (tid == 0) nsel_out[r] = min(n_total_sel, cap);
 }
 
 // ================================================================ prefill chunk
@@ -1343,7 +1343,7 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
     __syncthreads();
     if (s_b < 0) {
       // fewer older keys than top_k: all of them, in order
-      n_keep = static_cast<uint32_t>(min(first, static_cast<int64_t>(kMaxSel)));
+      n_keep = static_cast<uint32_t>(min(first, static_cast<int64_t>(topk)));
       for (uint32_t i = tid; i < n_keep; i += kRowThreads) out[i] = static_cast<int32_t>(i);
     } else {
       const int lo = s_lo, hi = s_hi2;
@@ -1530,13 +1530,13 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
         const uint32_t rk = i + lower_bound_lds(up, n_up, v);
         if (rk < static_cast<uint32_t>(cap)) out[rk] = v;
       }
-      n_keep = n_up + n_w;
+      n_keep = min(n_up + n_w, static_cast<uint32_t>(topk));
     }
   }
   const int n_total = static_cast<int>(n_keep) + static_cast<int>(static_cast<int64_t>(P) - first + 1);
   for (int i = static_cast<int>(n_keep) + tid; i < cap; i += kRowThreads)
     out[i] = i < n_total ? static_cast<int32_t>(first + (i - static_cast<int>(n_keep))) : -1;
-  if (tid == 0) nsel_out[r] = n_total;
+  if (tid == 0) nsel_out[r] = min(n_total, cap);
 }
 
 // ================================================================ block-level selection
@@ -1648,7 +1648,7 @@ __device__ __forceinline__ void emit_blocks(
       static_cast<int>(n_keep) + static_cast<int>(static_cast<int64_t>(P) - first + 1);
   for (int i = static_cast<int>(n_keep) + tid; i < cap; i += kSelThreads)
     out[i] = i < n_total ? static_cast<int32_t>(first + (i - static_cast<int>(n_keep))) : -1;
-  if (tid == 0) nsel_out[r] = n_total;
+  if (tid == 0) nsel_out[r] = min(n_total, cap);
 }
 
 // Fused decode: the candidate lists hold the exact float64 importance of every

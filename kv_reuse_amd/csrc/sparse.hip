@@ -50,7 +50,8 @@ __global__ __launch_bounds__(NCT * 64) void sparse_kernel(
   const size_t kvrow = static_cast<size_t>(b) * Hkv + g;
   const u16* kr = k + kvrow * static_cast<size_t>(kvp) * kD;
   const u16* vr = v + kvrow * static_cast<size_t>(kvp) * kD;
-  int ns = n_sel[r];
+  // a count beyond the list's capacity (a malformed list) reads no further than it
+  int ns = min(max(n_sel[r], 0), cap);
   if (w_drop >= 0) {
     // the separate-window variant: the window's entries (the last ones of the
     // ascending list) are left to the window branch

@@ -169,12 +169,14 @@ def test_sparse_attn_standalone(hs2):
         idx[b, t, g, : rr["idx"].size] = rr["idx"]
         ns[b, t, g] = rr["idx"].size
     ns[1, 0, 1] = 0                     # a row with nothing selected gets zeros
+    ns[1, 0, 0] = s.cap + 500           # a count past the list's capacity reads only the list
     out = torch.empty((5, w.batch, 1, w.n_q_heads, 128), dtype=torch.bfloat16, device="cuda")
     hs2.sparse_attn(s, gh.dev(x["q_sparse"]), gh.dev(x["k"]), gh.dev(x["v"]),
                     torch.from_numpy(idx).cuda(), torch.from_numpy(ns).cuda(), out)
     torch.cuda.synchronize()
     got = gh.host_f64(out)
-    want = orc.sparse_step(x["q_sparse"], x["k"], x["v"], idx, ns, scale=w.scale)
+    want = orc.sparse_step(x["q_sparse"], x["k"], x["v"], idx, np.minimum(ns, s.cap),
+                           scale=w.scale)
     gh.check_outputs(got, want, "sparse standalone")
     assert np.all(got[:, 1, 0, 8:16] == 0.0)
 
