@@ -134,7 +134,7 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
   q.band_cap = decode ? 0 : std::min<int64_t>(q.Spad, kPrefillBandCap);
   q.off_band_idx = take(Rz * q.band_cap * sizeof(int32_t));
   q.off_band_key = take(Rz * q.band_cap * sizeof(uint64_t));
-  // the float32 importance of a prefill chunk shares the key buffer of the
+  // the float16 importance of a prefill chunk shares the key buffer of the
   // selection from given scores: no call uses both
   q.off_ybuf = q.off_ukey;
   const size_t sp_parts = q.sp_nch > 1 ? Rz * q.sp_nch * n_layers * kG : 0;

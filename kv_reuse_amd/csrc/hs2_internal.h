@@ -26,6 +26,7 @@ typedef unsigned short u16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16;
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 // Per-row selection bookkeeping (lives in the workspace; zeroed each call).
@@ -60,7 +61,7 @@ struct Plan {
   int hs_chunk, hs_nchunk;   // subtiles per work-group: bound histogram
   int sc_chunk, sc_nchunk;   // subtiles per work-group: candidate scoring (<= kMaxChunks per row)
   size_t off_hist_c, off_cand_y, off_cand_idx, off_cand_cnt, off_band_idx, off_band_key;
-  // prefill chunk: per-row log2 importance of the older keys, band capacity per row
+  // prefill chunk: per-row log2 importance of the older keys (float16), band capacity per row
   size_t off_ybuf;
   int64_t band_cap;
   // sparse

@@ -315,7 +315,7 @@ __global__ __launch_bounds__(kPThreads, QB <= 2 ? 2 : 1) void full_prefill_kerne
 //   scores[row][j] = 2^y for all j <= P_t, 0 above (when scores is non-null).
 __global__ __launch_bounds__(kPThreads, 2) void prefill_importance_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const double* __restrict__ lse2,
-    const float* __restrict__ ytop_h, float* __restrict__ y, uint32_t* __restrict__ hist,
+    const float* __restrict__ ytop_h, f16* __restrict__ y, uint32_t* __restrict__ hist,
     float* __restrict__ scores, int64_t S, int64_t Spad, int T, int Hkv, int w, int n_tblk,
     float c2_hi, float c2_lo, int64_t kvp) {
   __shared__ __align__(16) u16 kt[kPKeys * kPPitch];
@@ -349,7 +349,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_importance_kernel(
   bool t_ok[2];
   int64_t P[2], first[2];
   float nl2r[2][4];     // -lse2 of the lane's 4 heads
-  float* yrow[2];
+  f16* yrow[2];
   float* srow[2];
 #pragma unroll
   for (int qbk = 0; qbk < 2; ++qbk) {
@@ -424,8 +424,13 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_importance_kernel(
         if (!t_ok[qbk] || key > P[qbk]) continue;
         if (srow[qbk]) srow[qbk][key] = __builtin_amdgcn_exp2f(yy);
         if (key < first[qbk]) {
-          if (yrow[qbk]) yrow[qbk][key] = yy;
-          if (want_hist) atomicAdd(&lh[jloc[qbk]][key_from_log2(yy, ybase[qbk]) >> kPBinShift], 1u);
+          // stored as float16 (error below 1/60 in log2 units over the range
+          // the histogram covers, an eighth of a bin); the histogram counts
+          // the stored value, which is what the selection reads
+          const f16 yh = static_cast<f16>(yy);
+          if (yrow[qbk]) yrow[qbk][key] = yh;
+          if (want_hist)
+            atomicAdd(&lh[jloc[qbk]][key_from_log2(static_cast<float>(yh), ybase[qbk]) >> kPBinShift], 1u);
         }
       }
     }
@@ -484,7 +489,7 @@ hipError_t launch_prefill_importance(const Plan& p, const u16* q, const u16* k, 
   hipLaunchKernelGGL(prefill_importance_kernel, dim3(n_wg), dim3(kPThreads), 0, st, q, k,
                      reinterpret_cast<const double*>(w + p.off_lse2),
                      reinterpret_cast<const float*>(w + p.off_ytop),
-                     for_select ? reinterpret_cast<float*>(w + p.off_ybuf) : nullptr,
+                     for_select ? reinterpret_cast<f16*>(w + p.off_ybuf) : nullptr,
                      for_select ? reinterpret_cast<uint32_t*>(w + p.off_hist) : nullptr, scores,
                      p.S, p.Spad, p.T, p.Hkv, p.w, n_tblk, c2_hi, c2_lo, p.kvp);
   return hipGetLastError();

@@ -1278,19 +1278,19 @@ __device__ __forceinline__ uint32_t lower_bound_lds(const int32_t* a, uint32_t n
 }
 
 // One work-group per row (b, t, g) of a prefill chunk: the exact top-k of the
-// row's older keys from their float32 log2 importance y and the row's
+// row's older keys from their log2 importance y (stored as float16) and the row's
 // complete histogram (kPNB bins of 1/8 octave).
 //  * One pass over y in key order: bins above b*+1 go to the "up" list, bins
-//    b*-1..b*+1 (the float32 error of y is far below a bin) to the band list;
+//    b*-1..b*+1 (the float16 error of y is below an eighth of a bin) to the band list;
 //    both lists come out in ascending key order.
 //  * The band keys' importance is recomputed in float64 from exact bf16
 //    products; a radix threshold on it picks the band's share, ties going to
 //    the lower index (the band list is in index order).
 //  * The up list and the band winners, both ascending, are merged into the
 //    output by rank; then the window, the padding and the count.
-// A band larger than band_cap is ranked by its float32 y instead.
+// A band larger than band_cap is ranked by its float16 y instead.
 __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
-    const float* __restrict__ ybuf, const uint32_t* __restrict__ hist,
+    const f16* __restrict__ ybuf, const uint32_t* __restrict__ hist,
     const float* __restrict__ ytop_h, const double* __restrict__ lse2, const u16* __restrict__ q,
     const u16* __restrict__ k, int32_t* __restrict__ band_idx, uint64_t* __restrict__ band_key,
     int64_t band_cap, int32_t* __restrict__ idx_out, int32_t* __restrict__ nsel_out, int64_t S,
@@ -1351,7 +1351,7 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
       const bool band_lds = n_band_h <= static_cast<uint32_t>(kUncCap);
       const bool band_glob = !band_lds && n_band_h <= static_cast<uint64_t>(band_cap);
       const float ybase = s_ybase;
-      const float* yr = ybuf + static_cast<size_t>(r) * Spad;
+      const f16* yr = ybuf + static_cast<size_t>(r) * Spad;
       int32_t* gbi = band_idx + static_cast<size_t>(r) * band_cap;
       uint64_t* gbk = band_key + static_cast<size_t>(r) * band_cap;
       int32_t* bi = band_lds ? lbi : gbi;
@@ -1360,13 +1360,19 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
       // round's loads are issued before this round is processed)
       const int64_t rounds = (first + 16 * kRowThreads - 1) / (16 * kRowThreads);
       uint32_t cu = 0, ca = 0;
-      f32x4 ycur[4], ynxt[4];
-      auto load_round = [&](int64_t rr, f32x4 (&yv)[4]) {
+      // 16 float16 values per thread and round, as two 16-byte loads
+      u32x4 ycur[2], ynxt[2];
+      auto load_round = [&](int64_t rr, u32x4 (&yv)[2]) {
         const int64_t i0 = 16 * (static_cast<int64_t>(tid) + rr * kRowThreads);
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          yv[u] = i0 + 4 * u < first ? *reinterpret_cast<const f32x4*>(yr + i0 + 4 * u)
-                                     : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < 2; ++u)
+          yv[u] = i0 + 8 * u < first ? *reinterpret_cast<const u32x4*>(yr + i0 + 8 * u)
+                                     : u32x4{0u, 0u, 0u, 0u};
+      };
+      auto y_at = [](const u32x4 (&yv)[2], int e) {
+        const uint32_t word = yv[e >> 3][(e >> 1) & 3];
+        const uint16_t bits = static_cast<uint16_t>((e & 1) ? (word >> 16) : (word & 0xFFFFu));
+        return static_cast<float>(__builtin_bit_cast(f16, bits));
       };
       if (rounds > 0) load_round(0, ycur);
       for (int64_t rr = 0; rr < rounds; ++rr) {
@@ -1376,7 +1382,7 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const bool valid = i0 + e < first;
-          const int bn = static_cast<int>(key_from_log2(ycur[e >> 2][e & 3], ybase) >> kPBinShift);
+          const int bn = static_cast<int>(key_from_log2(y_at(ycur, e), ybase) >> kPBinShift);
           mu |= static_cast<uint32_t>(valid && bn > hi) << e;
           ma |= static_cast<uint32_t>(valid && bn >= lo && bn <= hi) << e;
         }
@@ -1398,7 +1404,7 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
           }
         }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) ycur[u] = ynxt[u];
+        for (int u = 0; u < 2; ++u) ycur[u] = ynxt[u];
       }
       __syncthreads();
       const uint32_t n_up = min(cu, static_cast<uint32_t>(topk));
@@ -1485,14 +1491,14 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
           }
         }
       } else if (take > 0) {
-        // the band is too large to list: rank it by its float32 importance
+        // the band is too large to list: rank it by its float16 importance
         // (unordered winners, then sorted)
         struct ScanSrc {
-          const float* yr;
+          const f16* yr;
           float ybase;
           int lo, hi;
           __device__ bool get(int64_t i, uint64_t& key, int32_t& j) const {
-            const float yy = yr[i];
+            const float yy = static_cast<float>(yr[i]);
             const int bn = static_cast<int>(key_from_log2(yy, ybase) >> kPBinShift);
             if (bn < lo || bn > hi) return false;
             key = static_cast<uint64_t>(ordered_u32(yy));
@@ -1847,7 +1853,7 @@ hipError_t launch_prefill_select(const Plan& p, const u16* q, const u16* k, int3
   char* w = static_cast<char*>(ws);
   const double c2 = p.scale * 1.4426950408889634;
   hipLaunchKernelGGL(prefill_select_kernel, dim3(p.R), dim3(kRowThreads), 0, st,
-                     reinterpret_cast<const float*>(w + p.off_ybuf),
+                     reinterpret_cast<const f16*>(w + p.off_ybuf),
                      reinterpret_cast<const uint32_t*>(w + p.off_hist),
                      reinterpret_cast<const float*>(w + p.off_ytop),
                      reinterpret_cast<const double*>(w + p.off_lse2), q, k,
