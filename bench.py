@@ -193,6 +193,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode_1m_b1_heavy")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step in a HIP graph and time its replays (for the small, "
+                         "launch-bound workloads)")
     ap.add_argument("--swa-branch", action="store_true",
                     help="time the previous generation's sparse layers instead: a separate "
                          "sliding-window branch over each layer's own local cache plus the "
@@ -266,6 +269,25 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.graph:
+        # the library only enqueues kernels: the whole step captures into one graph
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+
+        def step():
+            graph.replay()
+
+        for _ in range(max(1, args.warmup)):
+            step()
+        torch.cuda.synchronize()
     log(f"[bench] timing {args.steps} steps")
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -278,6 +300,15 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = e0.elapsed_time(e1) / args.steps
+    # each step on its own, for the median and the minimum
+    per = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for a, b in per:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    each = sorted(a.elapsed_time(b) for a, b in per)
     tokens_per_s = B * T / (ms_step / 1e3)
 
     log("[bench] per-phase timing")
@@ -308,6 +339,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 5),
+        "ms_per_step_median": round(each[len(each) // 2], 5),
+        "ms_per_step_min": round(each[0], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -318,7 +351,8 @@ def main():
                    "window": w.window, "n_sparse_layers": L,
                    "selection": (f"block_{args.select_block}" if args.select_block
                                  else "token"),
-                   "sparse_layers": "separate_window_branch" if args.swa_branch else "shared"},
+                   "sparse_layers": "separate_window_branch" if args.swa_branch else "shared",
+                   "launch": "hip_graph" if args.graph else "stream"},
         "roofline": roofline,
         "phases_ms": {"full_split": round(phases[0], 5), "full_combine": round(phases[1], 5),
                       "select": round(phases[2], 5), "sparse": round(phases[3], 5)},

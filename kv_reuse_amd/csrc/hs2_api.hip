@@ -92,13 +92,20 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
     hc = std::min<int64_t>(std::max<int64_t>(hc, 256), 8192);
     q.hs_chunk = static_cast<int>(hc);
     q.hs_nchunk = static_cast<int>(ceil_div(nst, hc));
-    // candidate scoring: about 1024 work-groups (four per CU, all resident at
-    // once), whole rounds of kScoreRound subtiles, at most kMaxChunks per row
-    int64_t sc = align_up(static_cast<size_t>(ceil_div(nst * R, 1024)), kScoreRound);
-    sc = std::max<int64_t>(sc, kScoreRound);
-    sc = std::max<int64_t>(sc, static_cast<int64_t>(align_up(static_cast<size_t>(ceil_div(nst, kMaxChunks)), kScoreRound)));
-    q.sc_chunk = static_cast<int>(sc);
-    q.sc_nchunk = static_cast<int>(ceil_div(nst, sc));
+    // candidate-subtile lists: about 1024 work-groups, whole rounds of
+    // kScoreRound subtiles, at most kMaxChunks per row
+    int64_t cc = align_up(static_cast<size_t>(ceil_div(nst * R, 1024)), kScoreRound);
+    cc = std::max<int64_t>(cc, kScoreRound);
+    cc = std::max<int64_t>(cc, static_cast<int64_t>(align_up(static_cast<size_t>(ceil_div(nst, kMaxChunks)), kScoreRound)));
+    q.cc_chunk = static_cast<int>(cc);
+    q.cc_nchunk = static_cast<int>(ceil_div(nst, cc));
+    // scoring: about 1024 work-groups (four per CU, all resident at once), each
+    // taking an equal share of its row's candidate list, so that clustered
+    // candidates do not queue on a few work-groups
+    int64_t ns = std::min<int64_t>(ceil_div(1024, R), std::min<int64_t>(kMaxChunks, nst));
+    ns = std::max<int64_t>(ns, 1);
+    q.sc_nchunk = static_cast<int>(ns);
+    q.sc_chunk = static_cast<int>(ceil_div(nst, ns));   // list entries a region holds
   }
   // sparse: slices of 128 keys over work-groups when rows are few
   q.sp_nch = (R >= 256) ? 1 : static_cast<int>(ceil_div(q.cap, 128));
@@ -125,6 +132,9 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
   q.off_unc = take(Rz * kUncCap * sizeof(int32_t));
   q.off_unck = take(Rz * kUncCap * sizeof(uint64_t));
   q.off_hist_c = take(decode ? Rz * kNB * sizeof(uint32_t) : 0);
+  q.off_clist = take(decode ? Rz * q.cc_nchunk * static_cast<size_t>(q.cc_chunk) * sizeof(int32_t) : 0);
+  q.off_ccnt = take(decode ? Rz * q.cc_nchunk * sizeof(uint32_t) : 0);
+  q.off_lo = take(decode ? Rz * sizeof(int32_t) : 0);
   const size_t cz = decode ? Rz * static_cast<size_t>(q.sc_nchunk) * q.sc_chunk * 16 : 0;
   q.off_cand_y = take(cz * sizeof(double));
   q.off_cand_idx = take(cz * sizeof(int32_t));

@@ -59,7 +59,9 @@ struct Plan {
   size_t off_ukey, off_cert, off_unc, off_unck;
   // fused selection from the subtile maxima
   int hs_chunk, hs_nchunk;   // subtiles per work-group: bound histogram
-  int sc_chunk, sc_nchunk;   // subtiles per work-group: candidate scoring (<= kMaxChunks per row)
+  int cc_chunk, cc_nchunk;   // subtiles per work-group: the candidate-subtile lists
+  size_t off_clist, off_ccnt, off_lo;
+  int sc_chunk, sc_nchunk;   // scoring: list entries per work-group region, work-groups per row
   size_t off_hist_c, off_cand_y, off_cand_idx, off_cand_cnt, off_band_idx, off_band_key;
   // prefill chunk: per-row log2 importance of the older keys (float16), band capacity per row
   size_t off_ybuf;

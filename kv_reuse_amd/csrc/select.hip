@@ -612,32 +612,18 @@ __global__ __launch_bounds__(kThreads) void subtile_hist_kernel(
   flush_hist(lh, hist + static_cast<size_t>(r) * kNB, static_cast<uint32_t>(topk), &s_lo);
 }
 
-// Candidate subtiles, then their keys' exact importance, in rounds of
-// kScoreRound subtiles:
-//  * a subtile is a candidate when its bound's bin is at least (k-th bound bin
-//    - 1): every key that can be selected lies in one;
-//  * a wave takes a candidate subtile and computes its 16 keys' importance in
-//    float64 on MFMA (D = K . Q^T, 16 keys x 16 heads of which 8 are used; the
-//    bf16 products are exact in float64), staged in LDS kStageSub subtiles at
-//    a time;
-//  * keys whose bin is below that same bound can never be selected and are
-//    dropped; the others are appended to the work-group's own region of the
-//    row's candidate list in ascending key order, and counted in the row's
-//    candidate histogram.  The region's length goes to cand_cnt.
-// The query operand stays packed (bf16) in registers and is widened at each
-// step, so that four work-groups fit a CU and the whole grid is resident at
-// once.
-constexpr int kStageSub = 64;   // candidate subtiles staged per pass
-__global__ __launch_bounds__(kThreads, 4) void subtile_score_kernel(
+// The candidate subtiles of a row, in ascending order: a subtile is a
+// candidate when its bound's bin is at least (k-th bound bin - 1), since every
+// key that can be selected lies in one.  grid (cc chunks, R); each work-group
+// lists the candidates of its range of subtiles into its own region of the
+// row's list and counts them in ccnt.  Work-group 0 of a row also writes the
+// row's lower bin for the next kernel.
+__global__ __launch_bounds__(kThreads) void subtile_cand_kernel(
     const float* __restrict__ stmax, const double* __restrict__ lse2,
     const float* __restrict__ ytop_h, const uint32_t* __restrict__ hist,
-    uint32_t* __restrict__ hist_c, const u16* __restrict__ q, const u16* __restrict__ k,
-    double* __restrict__ cand_y, int32_t* __restrict__ cand_idx, uint32_t* __restrict__ cand_cnt,
-    int64_t S, int64_t Spad, int T, int Hkv, int topk, int w, int chunk, int n_chunks,
-    double c2, int64_t kvp) {
+    int32_t* __restrict__ clist, uint32_t* __restrict__ ccnt, int32_t* __restrict__ lo_out,
+    int64_t S, int64_t Spad, int T, int Hkv, int topk, int w, int chunk, int n_chunks) {
   __shared__ uint32_t lh[kNB];
-  __shared__ int32_t s_list[kScoreRound];
-  __shared__ double stage_y[kStageSub * kSubKeys];
   __shared__ float lse2f[kG];
   __shared__ float s_ybase;
   __shared__ int s_lo;
@@ -645,21 +631,19 @@ __global__ __launch_bounds__(kThreads, 4) void subtile_score_kernel(
   __shared__ uint32_t s_base[4];
   const int r = blockIdx.y;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 15, grp = lane >> 4;
   const int64_t first = row_first(row_pos(r, T, Hkv, S), w);
   const int64_t n_counted = first / kSubKeys;
   const int64_t n_sub = (first + kSubKeys - 1) / kSubKeys;
   const int64_t st0 = static_cast<int64_t>(blockIdx.x) * chunk;
   const int64_t st1 = min(n_sub, st0 + chunk);
-  uint32_t* cnt = cand_cnt + static_cast<size_t>(r) * n_chunks + blockIdx.x;
+  uint32_t* cnt = ccnt + static_cast<size_t>(r) * n_chunks + blockIdx.x;
   if (topk <= 0 || first == 0 || st0 >= st1) {
     if (tid == 0) *cnt = 0u;
     return;
   }
   const bool all_mode = n_counted <= topk;
   const float* stmax_row = stmax + static_cast<size_t>(r) * (Spad / kSubKeys) * kG;
-  // ---- the first loads, together: histogram, the first round's maxima, query
+  // ---- the first loads, together: histogram and the first round's maxima
   uint32_t hv[kNB / kThreads];
 #pragma unroll
   for (int u = 0; u < kNB / kThreads; ++u)
@@ -671,16 +655,6 @@ __global__ __launch_bounds__(kThreads, 4) void subtile_score_kernel(
     mx[0] = ld ? *reinterpret_cast<const f32x4*>(stmax_row + st * kG) : f32x4{0.f, 0.f, 0.f, 0.f};
     mx[1] = ld ? *reinterpret_cast<const f32x4*>(stmax_row + st * kG + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  // the B operand, packed bf16: head col (zero for the padding heads),
-  // dims 32*grp + 8c .. +8, widened exactly at each MFMA step
-  u32x4 qraw[4];
-  {
-    const u16* qr = q + static_cast<size_t>(r) * kG * kD + (col & 7) * kD + 32 * grp;
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      qraw[c] = col < kG ? load_u32x4(qr + 8 * c) : u32x4{0u, 0u, 0u, 0u};
-  }
-  const double l2 = col < kG ? lse2[static_cast<size_t>(r) * kG + col] : 0.0;
   if (tid < kG) lse2f[tid] = static_cast<float>(lse2[static_cast<size_t>(r) * kG + tid]);
   if (tid == 0) s_ybase = row_ybase(ytop_h, r);
 #pragma unroll
@@ -692,20 +666,14 @@ __global__ __launch_bounds__(kThreads, 4) void subtile_score_kernel(
   }
   __syncthreads();
   const int lo_bin = all_mode ? 0 : s_lo;
+  if (blockIdx.x == 0 && tid == 0) lo_out[r] = lo_bin;
   const float ybase = s_ybase;
   float l2v[kG];
 #pragma unroll
   for (int h = 0; h < kG; ++h) l2v[h] = lse2f[h];
-  for (int i = tid; i < kNB; i += kThreads) lh[i] = 0u;   // now the candidate histogram
-  const int b = r / (T * Hkv);
-  const int g = r % Hkv;
-  const u16* kr = k + (static_cast<size_t>(b) * Hkv + g) * static_cast<size_t>(kvp) * kD;
-  const size_t region = (static_cast<size_t>(r) * n_chunks + blockIdx.x) * static_cast<size_t>(chunk) * kSubKeys;
-  double* cy = cand_y + region;
-  int32_t* ci = cand_idx + region;
+  int32_t* out = clist + (static_cast<size_t>(r) * n_chunks + blockIdx.x) * chunk;
   uint32_t written = 0;
-  for (int64_t sr0 = st0; sr0 < st1; sr0 += kScoreRound) {
-    // ---- which subtiles of the round are candidates (thread t: subtile sr0 + t)
+  for (int64_t sr0 = st0; sr0 < st1; sr0 += kThreads) {
     const int64_t st = sr0 + tid;
     if (sr0 != st0) {
       const bool ld = !all_mode && st < min(st1, n_counted);
@@ -727,9 +695,112 @@ __global__ __launch_bounds__(kThreads, 4) void subtile_score_kernel(
     }
     uint32_t o_list, o_dummy;
     reserve_two(cand ? 1u : 0u, 0u, nullptr, nullptr, s_cnt, s_base, o_list, o_dummy);
-    const uint32_t n_local = s_base[2];
-    if (cand) s_list[o_list] = static_cast<int32_t>(st);   // ascending: slots follow thread order
+    if (cand) out[written + o_list] = static_cast<int32_t>(st);   // ascending: thread order
+    written += s_base[2];
+  }
+  if (tid == 0) *cnt = written;
+}
+
+// The exact importance of the candidates' keys.  grid (NS, R): work-group w of
+// a row takes the w-th equal share of the row's candidate list (the regions of
+// the list kernel in order), so clustered candidates spread over all NS
+// work-groups, in rounds of kScoreRound list entries:
+//  * a wave takes a candidate subtile and computes its 16 keys' importance in
+//    float64 on MFMA (D = K . Q^T, 16 keys x 16 heads of which 8 are used; the
+//    bf16 products are exact in float64), staged in LDS kStageSub subtiles at
+//    a time;
+//  * keys whose bin is below the row's lower bin can never be selected and
+//    are dropped; the others are appended to the work-group's own region of
+//    the row's candidate-key list in ascending key order, and counted in the
+//    row's candidate histogram.  The region's length goes to cand_cnt.
+// The query operand stays packed (bf16) in registers and is widened at each
+// step, so that four work-groups fit a CU and the whole grid is resident at
+// once.
+constexpr int kStageSub = 64;   // candidate subtiles staged per pass
+__global__ __launch_bounds__(kThreads, 4) void subtile_score_kernel(
+    const int32_t* __restrict__ lo_in, const int32_t* __restrict__ clist,
+    const uint32_t* __restrict__ ccnt, const double* __restrict__ lse2,
+    const float* __restrict__ ytop_h, uint32_t* __restrict__ hist_c, const u16* __restrict__ q,
+    const u16* __restrict__ k, double* __restrict__ cand_y, int32_t* __restrict__ cand_idx,
+    uint32_t* __restrict__ cand_cnt, int64_t S, int T, int Hkv, int topk, int w,
+    int cc_chunk, int cc_nchunk, int chunk, int n_chunks, double c2, int64_t kvp) {
+  __shared__ uint32_t lh[kNB];
+  __shared__ uint32_t pre[kMaxChunks + 1];
+  __shared__ int32_t s_list[kScoreRound];
+  __shared__ double stage_y[kStageSub * kSubKeys];
+  __shared__ float s_ybase;
+  __shared__ uint32_t s_cnt[2][16];
+  __shared__ uint32_t s_base[4];
+  const int r = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int64_t first = row_first(row_pos(r, T, Hkv, S), w);
+  uint32_t* cnt = cand_cnt + static_cast<size_t>(r) * n_chunks + blockIdx.x;
+  if (topk <= 0 || first == 0) {
+    if (tid == 0) *cnt = 0u;
+    return;
+  }
+  // ---- the row's list: region lengths, their exclusive prefix in pre
+  constexpr int kPer = kMaxChunks / kThreads;
+  uint32_t cl[kPer];
+  uint32_t mysum = 0;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int c = kPer * tid + u;
+    cl[u] = c < cc_nchunk ? ccnt[static_cast<size_t>(r) * cc_nchunk + c] : 0u;
+    mysum += cl[u];
+  }
+  // the B operand, packed bf16: head col (zero for the padding heads),
+  // dims 32*grp + 8c .. +8, widened exactly at each MFMA step
+  u32x4 qraw[4];
+  {
+    const u16* qr = q + static_cast<size_t>(r) * kG * kD + (col & 7) * kD + 32 * grp;
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      qraw[c] = col < kG ? load_u32x4(qr + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+  }
+  const double l2 = col < kG ? lse2[static_cast<size_t>(r) * kG + col] : 0.0;
+  const int lo_bin = lo_in[r];
+  if (tid == 0) s_ybase = row_ybase(ytop_h, r);
+  for (int i = tid; i < kNB; i += kThreads) lh[i] = 0u;   // the candidate histogram
+  uint32_t off, dummy;
+  reserve_two(mysum, 0u, nullptr, nullptr, s_cnt, s_base, off, dummy);
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int c = kPer * tid + u;
+    if (c < cc_nchunk) pre[c] = off;
+    off += cl[u];
+  }
+  if (tid == 0) pre[cc_nchunk] = s_base[2];
+  __syncthreads();
+  const uint32_t n_c = pre[cc_nchunk];
+  const uint32_t share = (n_c + n_chunks - 1) / n_chunks;
+  const uint32_t p_begin = min(n_c, share * blockIdx.x);
+  const uint32_t p_end = min(n_c, p_begin + share);
+  const float ybase = s_ybase;
+  const int b = r / (T * Hkv);
+  const int g = r % Hkv;
+  const u16* kr = k + (static_cast<size_t>(b) * Hkv + g) * static_cast<size_t>(kvp) * kD;
+  const size_t region = (static_cast<size_t>(r) * n_chunks + blockIdx.x) * static_cast<size_t>(chunk) * kSubKeys;
+  double* cy = cand_y + region;
+  int32_t* ci = cand_idx + region;
+  uint32_t written = 0;
+  for (uint32_t pr0 = p_begin; pr0 < p_end; pr0 += kScoreRound) {
+    const uint32_t n_local = min(static_cast<uint32_t>(kScoreRound), p_end - pr0);
+    // ---- this round's candidate subtiles (list entry -> region of the list kernel)
+    if (static_cast<uint32_t>(tid) < n_local) {
+      const uint32_t pos = pr0 + tid;
+      int lo = 0, hi = cc_nchunk - 1;   // the region of pos: largest c with pre[c] <= pos
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pre[mid] <= pos) lo = mid;
+        else hi = mid - 1;
+      }
+      s_list[tid] = clist[(static_cast<size_t>(r) * cc_nchunk + lo) * cc_chunk + (pos - pre[lo])];
+    }
     __syncthreads();
+    uint32_t o_dummy;
     for (uint32_t p0 = 0; p0 < n_local; p0 += kStageSub) {
       const uint32_t np = min(static_cast<uint32_t>(kStageSub), n_local - p0);
       // ---- float64 importance of the pass's candidates, one subtile per wave
@@ -1832,9 +1903,16 @@ hipError_t launch_fused_select(const Plan& p, const u16* q, const u16* k, int32_
                      lse2, ytop, hist, hist_c, p.S, p.Spad, p.T, p.Hkv, p.k, p.w, p.hs_chunk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(subtile_score_kernel, dim3(p.sc_nchunk, p.R), dim3(kThreads), 0, st, stmax,
-                     lse2, ytop, hist, hist_c, q, k, cand_y, cand_idx, cand_cnt, p.S, p.Spad, p.T,
-                     p.Hkv, p.k, p.w, p.sc_chunk, p.sc_nchunk, c2, p.kvp);
+  int32_t* clist = reinterpret_cast<int32_t*>(w + p.off_clist);
+  uint32_t* ccnt = reinterpret_cast<uint32_t*>(w + p.off_ccnt);
+  int32_t* lo = reinterpret_cast<int32_t*>(w + p.off_lo);
+  hipLaunchKernelGGL(subtile_cand_kernel, dim3(p.cc_nchunk, p.R), dim3(kThreads), 0, st, stmax,
+                     lse2, ytop, hist, clist, ccnt, lo, p.S, p.Spad, p.T, p.Hkv, p.k, p.w,
+                     p.cc_chunk, p.cc_nchunk);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(subtile_score_kernel, dim3(p.sc_nchunk, p.R), dim3(kThreads), 0, st, lo,
+                     clist, ccnt, lse2, ytop, hist_c, q, k, cand_y, cand_idx, cand_cnt, p.S, p.T,
+                     p.Hkv, p.k, p.w, p.cc_chunk, p.cc_nchunk, p.sc_chunk, p.sc_nchunk, c2, p.kvp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (p.bs > 0) {
     hipLaunchKernelGGL(block_row_select_kernel, dim3(p.R), dim3(kSelThreads), 0, st, cand_y,
