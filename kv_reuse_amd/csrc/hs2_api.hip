@@ -99,10 +99,10 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
     cc = std::max<int64_t>(cc, static_cast<int64_t>(align_up(static_cast<size_t>(ceil_div(nst, kMaxChunks)), kScoreRound)));
     q.cc_chunk = static_cast<int>(cc);
     q.cc_nchunk = static_cast<int>(ceil_div(nst, cc));
-    // scoring: about 1024 work-groups (four per CU, all resident at once), each
+    // scoring: about 768 work-groups (three per CU, all resident at once), each
     // taking an equal share of its row's candidate list, so that clustered
     // candidates do not queue on a few work-groups
-    int64_t ns = std::min<int64_t>(ceil_div(1024, R), std::min<int64_t>(kMaxChunks, nst));
+    int64_t ns = std::min<int64_t>(ceil_div(768, R), std::min<int64_t>(kMaxChunks, nst));
     ns = std::max<int64_t>(ns, 1);
     q.sc_nchunk = static_cast<int>(ns);
     q.sc_chunk = static_cast<int>(ceil_div(nst, ns));   // list entries a region holds

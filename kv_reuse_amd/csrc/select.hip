@@ -705,19 +705,20 @@ __global__ __launch_bounds__(kThreads) void subtile_cand_kernel(
 // a row takes the w-th equal share of the row's candidate list (the regions of
 // the list kernel in order), so clustered candidates spread over all NS
 // work-groups, in rounds of kScoreRound list entries:
-//  * a wave takes a candidate subtile and computes its 16 keys' importance in
-//    float64 on MFMA (D = K . Q^T, 16 keys x 16 heads of which 8 are used; the
-//    bf16 products are exact in float64), staged in LDS kStageSub subtiles at
-//    a time;
+//  * a wave takes a candidate subtile; its keys' importance (exact float64
+//    for every key that can be kept, see below) is staged in LDS kStageSub
+//    subtiles at a time;
 //  * keys whose bin is below the row's lower bin can never be selected and
 //    are dropped; the others are appended to the work-group's own region of
 //    the row's candidate-key list in ascending key order, and counted in the
 //    row's candidate histogram.  The region's length goes to cand_cnt.
-// The query operand stays packed (bf16) in registers and is widened at each
-// step, so that four work-groups fit a CU and the whole grid is resident at
-// once.
+// Each candidate subtile is first scored in float32 on the bf16 MFMA (16 keys
+// against the 8 heads); only its keys that may reach the lower bin (float
+// error is far below a bin) get the exact float64 importance, by plain fp64
+// fmas over lanes (head, 16 dims).  Three work-groups fit a CU, and the grid
+// is sized to be resident at once.
 constexpr int kStageSub = 64;   // candidate subtiles staged per pass
-__global__ __launch_bounds__(kThreads, 4) void subtile_score_kernel(
+__global__ __launch_bounds__(kThreads, 3) void subtile_score_kernel(
     const int32_t* __restrict__ lo_in, const int32_t* __restrict__ clist,
     const uint32_t* __restrict__ ccnt, const double* __restrict__ lse2,
     const float* __restrict__ ytop_h, uint32_t* __restrict__ hist_c, const u16* __restrict__ q,
@@ -760,7 +761,17 @@ __global__ __launch_bounds__(kThreads, 4) void subtile_score_kernel(
     for (int c = 0; c < 4; ++c)
       qraw[c] = col < kG ? load_u32x4(qr + 8 * c) : u32x4{0u, 0u, 0u, 0u};
   }
-  const double l2 = col < kG ? lse2[static_cast<size_t>(r) * kG + col] : 0.0;
+  // float32 scale and lse2 of head col for the filter; for the exact pass lane
+  // (h, j) keeps head h's query dims 16 j .. +16 widened to float64 and its lse2
+  const float c2f = static_cast<float>(c2);
+  const float l2f = col < kG ? static_cast<float>(lse2[static_cast<size_t>(r) * kG + col]) : 0.f;
+  const double l2h = lse2[static_cast<size_t>(r) * kG + (lane >> 3)];
+  u32x4 qh2[2];   // packed bf16, widened at each use
+  {
+    const u16* qh = q + (static_cast<size_t>(r) * kG + (lane >> 3)) * kD + 16 * (lane & 7);
+    qh2[0] = load_u32x4(qh);
+    qh2[1] = load_u32x4(qh + 8);
+  }
   const int lo_bin = lo_in[r];
   if (tid == 0) s_ybase = row_ybase(ytop_h, r);
   for (int i = tid; i < kNB; i += kThreads) lh[i] = 0u;   // the candidate histogram
@@ -814,47 +825,69 @@ __global__ __launch_bounds__(kThreads, 4) void subtile_score_kernel(
       if (static_cast<uint32_t>(wave) < np) load_sub(wave, ka_cur);
       for (uint32_t i = wave; i < np; i += kThreads / 64) {
         if (i + kThreads / 64 < np) load_sub(i + kThreads / 64, ka_nxt);
-        // the widened query (32 doubles) must not be hoisted out of this loop
-        // and kept live: mark the packed operand as redefined here
+        const int64_t key0 = static_cast<int64_t>(s_list[p0 + i]) * kSubKeys;
+        // ---- float32 importance of the 16 keys on the bf16 MFMA (S = K . Q^T,
+        // 16 keys x 16 heads of which 8 are used): lane (col, grp) gets keys
+        // 4 grp + e against head col
+        f32x4 sf = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(qraw[c]));
-        // four independent accumulation chains (one per 8-dim slice of the
-        // lane's 32 dims), summed at the end
-        f64x4 part[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) part[c] = f64x4{0.0, 0.0, 0.0, 0.0};
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const uint32_t word = ka_cur[c][t >> 1];
-            const double kv = static_cast<double>(
-                __uint_as_float((t & 1) ? (word & 0xFFFF0000u) : (word << 16)));
-            const uint32_t qw = qraw[c][t >> 1];
-            const double qv = static_cast<double>(
-                __uint_as_float((t & 1) ? (qw & 0xFFFF0000u) : (qw << 16)));
-            part[c] = __builtin_amdgcn_mfma_f64_16x16x4f64(kv, qv, part[c], 0, 0, 0);
-          }
-          // keep each step's operands short-lived (register pressure decides
-          // how many work-groups share a CU)
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        const f64x4 acc = (part[0] + part[1]) + (part[2] + part[3]);
+        for (int c = 0; c < 4; ++c) sf = mfma_16x16x32(as_bf16x8(ka_cur[c]), as_bf16x8(qraw[c]), sf);
 #pragma unroll
         for (int c = 0; c < 4; ++c) ka_cur[c] = ka_nxt[c];
-        // register e holds key grp + 4e against head col
-        double y[4];
+        uint32_t nib = 0;   // keys 4 grp + e that may reach the lower bin
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          double v = col < kG ? c2 * acc[e] - l2 : -INFINITY;
-          v = fmax(v, __shfl_xor(v, 1));
-          v = fmax(v, __shfl_xor(v, 2));
-          v = fmax(v, __shfl_xor(v, 4));
-          y[e] = v;
+          float v = col < kG ? fmaf(sf[e], c2f, -l2f) : -INFINITY;
+          v = fmaxf(v, __shfl_xor(v, 1));
+          v = fmaxf(v, __shfl_xor(v, 2));
+          v = fmaxf(v, __shfl_xor(v, 4));
+          // float error is far below a bin: a key one bin short can still make it
+          nib |= static_cast<uint32_t>(key0 + 4 * grp + e < first &&
+                                       cand_bin(static_cast<double>(v), ybase) >= lo_bin - 1) << e;
         }
-        if (col < 4)
-          stage_y[i * kSubKeys + grp + 4 * col] =
-              col == 0 ? y[0] : col == 1 ? y[1] : col == 2 ? y[2] : y[3];
+        const uint32_t promising = static_cast<uint32_t>(__shfl(nib, 0)) |
+                                   (static_cast<uint32_t>(__shfl(nib, 16)) << 4) |
+                                   (static_cast<uint32_t>(__shfl(nib, 32)) << 8) |
+                                   (static_cast<uint32_t>(__shfl(nib, 48)) << 12);
+        // ---- exact float64 importance of the promising keys only, two at a
+        // time: lane (h, j) = (lane >> 3, lane & 7) takes head h, dims 16 j .. +16
+        if (lane < kSubKeys) stage_y[i * kSubKeys + lane] = -INFINITY;
+        for (uint32_t m = promising; m; ) {
+          int ek[2];
+          u32x4 kv4[2][2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            ek[u] = m ? __builtin_ctz(m) : -1;
+            if (m) m &= m - 1;
+            const int64_t key = min(key0 + (ek[u] < 0 ? 0 : ek[u]), S - 1);
+            const u16* src = kr + key * kD + 16 * (lane & 7);
+            kv4[u][0] = load_u32x4(src);
+            kv4[u][1] = load_u32x4(src + 8);
+          }
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            if (ek[u] < 0) continue;
+            double acc = 0.0;
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+              const uint32_t word = kv4[u][t >> 3][(t >> 1) & 3];
+              const double kvd = static_cast<double>(
+                  __uint_as_float((t & 1) ? (word & 0xFFFF0000u) : (word << 16)));
+              const uint32_t qw = qh2[t >> 3][(t >> 1) & 3];
+              const double qvd = static_cast<double>(
+                  __uint_as_float((t & 1) ? (qw & 0xFFFF0000u) : (qw << 16)));
+              acc = fma(qvd, kvd, acc);
+            }
+            acc += __shfl_xor(acc, 1);
+            acc += __shfl_xor(acc, 2);
+            acc += __shfl_xor(acc, 4);
+            double yy = c2 * acc - l2h;
+            yy = fmax(yy, __shfl_xor(yy, 8));
+            yy = fmax(yy, __shfl_xor(yy, 16));
+            yy = fmax(yy, __shfl_xor(yy, 32));
+            if (lane == 0) stage_y[i * kSubKeys + ek[u]] = yy;
+          }
+        }
       }
       __syncthreads();
       // ---- keep the keys that can still be selected, in order (thread t:
