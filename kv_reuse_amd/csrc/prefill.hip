@@ -308,19 +308,14 @@ __global__ __launch_bounds__(kPThreads, QB <= 2 ? 2 : 1) void full_prefill_kerne
 // heads of one token for one key, and the max over the token's 8 heads is 3
 // in-lane steps and one exchange with the partner lane.
 // Writes, for every row (b, t, g) it owns:
-//   y[row][j] = max_h(s2_h[j] - lse2_h) for older keys j < first_t (float32,
-//               when y is non-null), and its histogram hist[row][kPNB] over
-//               bins of 1/8 octave above the row's ybase (when hist is
-//               non-null; complete, plain stores);
+//   y[row][j] = max_h(s2_h[j] - lse2_h) for older keys j < first_t (float16,
+//               when y is non-null);
 //   scores[row][j] = 2^y for all j <= P_t, 0 above (when scores is non-null).
 __global__ __launch_bounds__(kPThreads, 2) void prefill_importance_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const double* __restrict__ lse2,
-    const float* __restrict__ ytop_h, f16* __restrict__ y, uint32_t* __restrict__ hist,
-    float* __restrict__ scores, int64_t S, int64_t Spad, int T, int Hkv, int w, int n_tblk,
-    float c2_hi, float c2_lo, int64_t kvp) {
+    f16* __restrict__ y, float* __restrict__ scores, int64_t S, int64_t Spad, int T, int Hkv,
+    int w, int n_tblk, float c2_hi, float c2_lo, int64_t kvp) {
   __shared__ __align__(16) u16 kt[kPKeys * kPPitch];
-  __shared__ uint32_t lh[kPTok][kPNB];
-  __shared__ float s_ybase[kPTok];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -332,17 +327,6 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_importance_kernel(
   const int Hq = Hkv * kG;
   const u16* kr = k + static_cast<size_t>(bg) * kvp * kD;
   const int64_t pos0 = S - T;
-  const bool want_hist = hist != nullptr;
-  if (want_hist)
-    for (int i = tid; i < kPTok * kPNB; i += kPThreads) (&lh[0][0])[i] = 0u;
-  if (tid < kPTok) {
-    int t = tb * kPTok + tid;
-    t = t < T ? t : T - 1;
-    const size_t row = (static_cast<size_t>(b) * T + t) * Hkv + g;
-    float yt = -INFINITY;
-    for (int hh = 0; hh < kG; ++hh) yt = fmaxf(yt, ytop_h[row * kG + hh]);
-    s_ybase[tid] = yt - kYRange;
-  }
   // block qbk of this wave: tokens 4*wave + 2*qbk + {0, 1}
   bf16x8 qop[2][4];
   int jloc[2];
@@ -385,7 +369,6 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_importance_kernel(
 #pragma unroll
     for (int c = 0; c < 4; ++c) require_loaded(qop[qbk][c]);
   __syncthreads();
-  const float ybase[2] = {s_ybase[jloc[0]], s_ybase[jloc[1]]};
   for (int it = 0; it < n_tiles; ++it) {
     const int64_t key0 = static_cast<int64_t>(it) * kPKeys;
     const bool more = it + 1 < n_tiles;
@@ -423,15 +406,9 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_importance_kernel(
         const int64_t key = key0 + 16 * sub + col;
         if (!t_ok[qbk] || key > P[qbk]) continue;
         if (srow[qbk]) srow[qbk][key] = __builtin_amdgcn_exp2f(yy);
-        if (key < first[qbk]) {
-          // stored as float16 (error below 1/60 in log2 units over the range
-          // the histogram covers, an eighth of a bin); the histogram counts
-          // the stored value, which is what the selection reads
-          const f16 yh = static_cast<f16>(yy);
-          if (yrow[qbk]) yrow[qbk][key] = yh;
-          if (want_hist)
-            atomicAdd(&lh[jloc[qbk]][key_from_log2(static_cast<float>(yh), ybase[qbk]) >> kPBinShift], 1u);
-        }
+        // stored as float16: the error is below 1/60 in log2 units over the
+        // range the selection's histogram covers, an eighth of one of its bins
+        if (key < first[qbk] && yrow[qbk]) yrow[qbk][key] = static_cast<f16>(yy);
       }
     }
     __syncthreads();
@@ -447,15 +424,6 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_importance_kernel(
       if (tt >= T) break;
       float* sr = scores + ((static_cast<size_t>(b) * T + tt) * Hkv + g) * S;
       for (int64_t key = pos0 + tt + 1 + tid; key < S; key += kPThreads) sr[key] = 0.f;
-    }
-  }
-  if (want_hist) {
-    __syncthreads();
-    for (int i = tid; i < kPTok * kPNB; i += kPThreads) {
-      const int j = i / kPNB;
-      const int tt = tb * kPTok + j;
-      if (tt < T)
-        hist[((static_cast<size_t>(b) * T + tt) * Hkv + g) * kPNB + (i % kPNB)] = (&lh[0][0])[i];
     }
   }
 }
@@ -488,9 +456,7 @@ hipError_t launch_prefill_importance(const Plan& p, const u16* q, const u16* k, 
   const int n_wg = p.B * p.Hkv * n_tblk;
   hipLaunchKernelGGL(prefill_importance_kernel, dim3(n_wg), dim3(kPThreads), 0, st, q, k,
                      reinterpret_cast<const double*>(w + p.off_lse2),
-                     reinterpret_cast<const float*>(w + p.off_ytop),
-                     for_select ? reinterpret_cast<f16*>(w + p.off_ybuf) : nullptr,
-                     for_select ? reinterpret_cast<uint32_t*>(w + p.off_hist) : nullptr, scores,
+                     for_select ? reinterpret_cast<f16*>(w + p.off_ybuf) : nullptr, scores,
                      p.S, p.Spad, p.T, p.Hkv, p.w, n_tblk, c2_hi, c2_lo, p.kvp);
   return hipGetLastError();
 }

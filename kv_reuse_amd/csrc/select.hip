@@ -1370,6 +1370,13 @@ __device__ KThr key_threshold(const uint64_t* keys, uint32_t n, uint32_t need, u
   }
 }
 
+// Element e (0..15) of 16 float16 values held as two 16-byte words, widened.
+__device__ __forceinline__ float f16_at(const u32x4 (&v)[2], int e) {
+  const uint32_t word = v[e >> 3][(e >> 1) & 3];
+  const uint16_t bits = static_cast<uint16_t>((e & 1) ? (word >> 16) : (word & 0xFFFFu));
+  return static_cast<float>(__builtin_bit_cast(f16, bits));
+}
+
 // Number of entries of the ascending array a[0..n) that are < v.
 __device__ __forceinline__ uint32_t lower_bound_lds(const int32_t* a, uint32_t n, int32_t v) {
   uint32_t lo = 0, hi = n;
@@ -1382,9 +1389,10 @@ __device__ __forceinline__ uint32_t lower_bound_lds(const int32_t* a, uint32_t n
 }
 
 // One work-group per row (b, t, g) of a prefill chunk: the exact top-k of the
-// row's older keys from their log2 importance y (stored as float16) and the row's
-// complete histogram (kPNB bins of 1/8 octave).
-//  * One pass over y in key order: bins above b*+1 go to the "up" list, bins
+// row's older keys from their log2 importance y (stored as float16).
+//  * A first pass over y builds the row's histogram (kPNB bins of 1/8 octave
+//    above its ybase) and finds the bin b* of the k-th largest.
+//  * A second pass in key order: bins above b*+1 go to the "up" list, bins
 //    b*-1..b*+1 (the float16 error of y is below an eighth of a bin) to the band list;
 //    both lists come out in ascending key order.
 //  * The band keys' importance is recomputed in float64 from exact bf16
@@ -1394,8 +1402,7 @@ __device__ __forceinline__ uint32_t lower_bound_lds(const int32_t* a, uint32_t n
 //    output by rank; then the window, the padding and the count.
 // A band larger than band_cap is ranked by its float16 y instead.
 __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
-    const f16* __restrict__ ybuf, const uint32_t* __restrict__ hist,
-    const float* __restrict__ ytop_h, const double* __restrict__ lse2, const u16* __restrict__ q,
+    const f16* __restrict__ ybuf, const float* __restrict__ ytop_h, const double* __restrict__ lse2, const u16* __restrict__ q,
     const u16* __restrict__ k, int32_t* __restrict__ band_idx, uint64_t* __restrict__ band_key,
     int64_t band_cap, int32_t* __restrict__ idx_out, int32_t* __restrict__ nsel_out, int64_t S,
     int64_t Spad, int T, int Hkv, int topk, int w, int cap, double c2, int64_t kvp) {
@@ -1424,11 +1431,28 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
   int32_t* out = idx_out + static_cast<size_t>(r) * cap;
   uint32_t n_keep = 0;
   if (topk > 0 && first > 0) {
-    for (int i = tid; i < kPNB; i += kRowThreads) lh[i] = hist[static_cast<size_t>(r) * kPNB + i];
+    for (int i = tid; i < kPNB; i += kRowThreads) lh[i] = 0u;
     if (tid == 0) s_ybase = row_ybase(ytop_h, r);
     const u16* qr = q + static_cast<size_t>(r) * kG * kD;
     for (int i = tid; i < kG * kD; i += kRowThreads) qd[i] = static_cast<double>(bf16_bits_to_f32(qr[i]));
     if (tid < kG) l2s[tid] = lse2[static_cast<size_t>(r) * kG + tid];
+    __syncthreads();
+    // ---- the row's histogram of y (bins of 1/8 octave above ybase), from the
+    // same stored float16 values the classification below reads
+    {
+      const float yb = s_ybase;
+      const f16* yrh = ybuf + static_cast<size_t>(r) * Spad;
+      for (int64_t i0 = 16 * static_cast<int64_t>(tid); i0 < first; i0 += 16 * kRowThreads) {
+        u32x4 v[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          v[u] = i0 + 8 * u < first ? *reinterpret_cast<const u32x4*>(yrh + i0 + 8 * u)
+                                    : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (i0 + e < first) atomicAdd(&lh[key_from_log2(f16_at(v, e), yb) >> kPBinShift], 1u);
+      }
+    }
     __syncthreads();
     if (tid < 64) {
       const KthBin kb = kth_bin_wave_n<kPNB>(lh, static_cast<uint32_t>(topk));
@@ -1473,11 +1497,7 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
           yv[u] = i0 + 8 * u < first ? *reinterpret_cast<const u32x4*>(yr + i0 + 8 * u)
                                      : u32x4{0u, 0u, 0u, 0u};
       };
-      auto y_at = [](const u32x4 (&yv)[2], int e) {
-        const uint32_t word = yv[e >> 3][(e >> 1) & 3];
-        const uint16_t bits = static_cast<uint16_t>((e & 1) ? (word >> 16) : (word & 0xFFFFu));
-        return static_cast<float>(__builtin_bit_cast(f16, bits));
-      };
+
       if (rounds > 0) load_round(0, ycur);
       for (int64_t rr = 0; rr < rounds; ++rr) {
         const int64_t i0 = 16 * (static_cast<int64_t>(tid) + rr * kRowThreads);
@@ -1486,7 +1506,7 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const bool valid = i0 + e < first;
-          const int bn = static_cast<int>(key_from_log2(y_at(ycur, e), ybase) >> kPBinShift);
+          const int bn = static_cast<int>(key_from_log2(f16_at(ycur, e), ybase) >> kPBinShift);
           mu |= static_cast<uint32_t>(valid && bn > hi) << e;
           ma |= static_cast<uint32_t>(valid && bn >= lo && bn <= hi) << e;
         }
@@ -1965,7 +1985,6 @@ hipError_t launch_prefill_select(const Plan& p, const u16* q, const u16* k, int3
   const double c2 = p.scale * 1.4426950408889634;
   hipLaunchKernelGGL(prefill_select_kernel, dim3(p.R), dim3(kRowThreads), 0, st,
                      reinterpret_cast<const f16*>(w + p.off_ybuf),
-                     reinterpret_cast<const uint32_t*>(w + p.off_hist),
                      reinterpret_cast<const float*>(w + p.off_ytop),
                      reinterpret_cast<const double*>(w + p.off_lse2), q, k,
                      reinterpret_cast<int32_t*>(w + p.off_band_idx),
