@@ -36,12 +36,15 @@ namespace hs2 {
 namespace {
 
 constexpr int kPThreads = 256;
-constexpr int kPTok = 16;       // chunk tokens per work-group (importance pass)
 // Attention: query blocks per wave.  Two keep the kernel at 244 VGPRs and two
 // work-groups per CU; three or four halve the LDS operand reads per MFMA but
 // drop to one wave per SIMD, and then measured 45-60% slower on the 4K-token
 // chunk over 128K keys.
 constexpr int kPrefillQB = 2;
+// Importance pass: query blocks per wave.  Without an O accumulator four fit
+// (224 VGPRs, two waves per SIMD), so each K operand read from LDS serves 64
+// query columns; measured 4% faster than two on the 4096-token chunk.
+constexpr int kImportanceQB = 4;
 constexpr int kPKeys = 64;      // keys per tile
 // LDS row pitches, in u16.  K rows advance by 4 banks (68 dwords), so the
 // 16-byte operand reads of 8 or 16 consecutive rows cover every bank once; V
@@ -301,9 +304,10 @@ __global__ __launch_bounds__(kPThreads, QB <= 2 ? 2 : 1) void full_prefill_kerne
   }
 }
 
-// Importance pass.  grid: B * Hkv * ceil(T / 16) work-groups of 256 threads;
-// a work-group takes 16 chunk tokens, each wave two 16-row query blocks (2
-// tokens x 8 heads each), so every K tile staged in LDS serves 16 tokens.
+// Importance pass.  grid: B * Hkv * ceil(T / (8 QB)) work-groups of 256
+// threads; a work-group takes 8 QB chunk tokens, each wave QB 16-row query
+// blocks (2 tokens x 8 heads each), so every K tile staged in LDS serves 8 QB
+// tokens.
 // Here the MFMA computes S = Q . K^T (query rows, key columns): a lane holds 4
 // heads of one token for one key, and the max over the token's 8 heads is 3
 // in-lane steps and one exchange with the partner lane.
@@ -311,6 +315,7 @@ __global__ __launch_bounds__(kPThreads, QB <= 2 ? 2 : 1) void full_prefill_kerne
 //   y[row][j] = max_h(s2_h[j] - lse2_h) for older keys j < first_t (float16,
 //               when y is non-null);
 //   scores[row][j] = 2^y for all j <= P_t, 0 above (when scores is non-null).
+template <int QB>
 __global__ __launch_bounds__(kPThreads, 2) void prefill_importance_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const double* __restrict__ lse2,
     f16* __restrict__ y, float* __restrict__ scores, int64_t S, int64_t Spad, int T, int Hkv,
@@ -328,23 +333,24 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_importance_kernel(
   const u16* kr = k + static_cast<size_t>(bg) * kvp * kD;
   const int64_t pos0 = S - T;
   // block qbk of this wave: tokens 4*wave + 2*qbk + {0, 1}
-  bf16x8 qop[2][4];
-  int jloc[2];
-  bool t_ok[2];
-  int64_t P[2], first[2];
-  float nl2r[2][4];     // -lse2 of the lane's 4 heads
-  f16* yrow[2];
-  float* srow[2];
+  constexpr int kTok = 8 * QB;   // chunk tokens per work-group
+  bf16x8 qop[QB][4];
+  int jloc[QB];
+  bool t_ok[QB];
+  int64_t P[QB], first[QB];
+  float nl2r[QB][4];     // -lse2 of the lane's 4 heads
+  f16* yrow[QB];
+  float* srow[QB];
 #pragma unroll
-  for (int qbk = 0; qbk < 2; ++qbk) {
+  for (int qbk = 0; qbk < QB; ++qbk) {
     // the A operand: query row col = (token .. + (col >> 3), head col & 7)
-    int tq = tb * kPTok + 4 * wave + 2 * qbk + (col >> 3);
+    int tq = tb * kTok + 2 * QB * wave + 2 * qbk + (col >> 3);
     tq = tq < T ? tq : T - 1;
     load_q_block(q + (static_cast<size_t>(b) * T + tq) * Hq * kD + static_cast<size_t>(g) * kG * kD,
                  col, grp, qop[qbk]);
     // this lane's rows of S: 4*grp + i = (token .. + (grp >> 1), head 4*(grp & 1) + i)
-    jloc[qbk] = 4 * wave + 2 * qbk + (grp >> 1);
-    int t = tb * kPTok + jloc[qbk];
+    jloc[qbk] = 2 * QB * wave + 2 * qbk + (grp >> 1);
+    int t = tb * kTok + jloc[qbk];
     t_ok[qbk] = t < T;
     t = t_ok[qbk] ? t : T - 1;
     P[qbk] = pos0 + t;
@@ -355,7 +361,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_importance_kernel(
     yrow[qbk] = y ? y + row * Spad : nullptr;
     srow[qbk] = scores ? scores + row * S : nullptr;
   }
-  const int t_last = min(T - 1, tb * kPTok + kPTok - 1);
+  const int t_last = min(T - 1, tb * kTok + kTok - 1);
   const int64_t p_last = pos0 + t_last;
   const int n_tiles = static_cast<int>((p_last + kPKeys) / kPKeys);
   // after the head max a lane owns key subtiles 2*(grp & 1) and 2*(grp & 1) + 1
@@ -365,7 +371,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_importance_kernel(
   tile_gload<false>(regs, kr, nullptr, 0, p_last);
   tile_lstore<false>(regs, kt, nullptr);
 #pragma unroll
-  for (int qbk = 0; qbk < 2; ++qbk)
+  for (int qbk = 0; qbk < QB; ++qbk)
 #pragma unroll
     for (int c = 0; c < 4; ++c) require_loaded(qop[qbk][c]);
   __syncthreads();
@@ -373,20 +379,21 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_importance_kernel(
     const int64_t key0 = static_cast<int64_t>(it) * kPKeys;
     const bool more = it + 1 < n_tiles;
     if (more) tile_gload<false>(regs, kr, nullptr, key0 + kPKeys, p_last);
-    f32x4 sacc[2][4];
+    f32x4 sacc[QB][4];
 #pragma unroll
     for (int sub = 0; sub < 4; ++sub) {
-      sacc[0][sub] = f32x4{0.f, 0.f, 0.f, 0.f};
-      sacc[1][sub] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int qbk = 0; qbk < QB; ++qbk) sacc[qbk][sub] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const bf16x8 kb = lds_k_operand(kt, sub, c, col, grp);
-        sacc[0][sub] = mfma_16x16x32(qop[0][c], kb, sacc[0][sub]);
-        sacc[1][sub] = mfma_16x16x32(qop[1][c], kb, sacc[1][sub]);
+#pragma unroll
+        for (int qbk = 0; qbk < QB; ++qbk)
+          sacc[qbk][sub] = mfma_16x16x32(qop[qbk][c], kb, sacc[qbk][sub]);
       }
     }
 #pragma unroll
-    for (int qbk = 0; qbk < 2; ++qbk) {
+    for (int qbk = 0; qbk < QB; ++qbk) {
       // y per (token, key): max over the 8 heads = 4 here x the partner lane.
       // One fma per head: the scale's low part (a * c2_lo, below 1e-7 in log2
       // units) is dropped; it is smaller than the float32 rounding of y, and
@@ -419,8 +426,8 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_importance_kernel(
   }
   // scores past P_t are 0
   if (scores) {
-    for (int j = 0; j < kPTok; ++j) {
-      const int tt = tb * kPTok + j;
+    for (int j = 0; j < kTok; ++j) {
+      const int tt = tb * kTok + j;
       if (tt >= T) break;
       float* sr = scores + ((static_cast<size_t>(b) * T + tt) * Hkv + g) * S;
       for (int64_t key = pos0 + tt + 1 + tid; key < S; key += kPThreads) sr[key] = 0.f;
@@ -452,9 +459,10 @@ hipError_t launch_prefill_importance(const Plan& p, const u16* q, const u16* k, 
   const double c2 = p.scale * 1.4426950408889634;
   const float c2_hi = static_cast<float>(c2);
   const float c2_lo = static_cast<float>(c2 - static_cast<double>(c2_hi));
-  const int n_tblk = (p.T + kPTok - 1) / kPTok;
+  constexpr int QB = kImportanceQB;
+  const int n_tblk = (p.T + 8 * QB - 1) / (8 * QB);
   const int n_wg = p.B * p.Hkv * n_tblk;
-  hipLaunchKernelGGL(prefill_importance_kernel, dim3(n_wg), dim3(kPThreads), 0, st, q, k,
+  hipLaunchKernelGGL(prefill_importance_kernel<QB>, dim3(n_wg), dim3(kPThreads), 0, st, q, k,
                      reinterpret_cast<const double*>(w + p.off_lse2),
                      for_select ? reinterpret_cast<f16*>(w + p.off_ybuf) : nullptr, scores,
                      p.S, p.Spad, p.T, p.Hkv, p.w, n_tblk, c2_hi, c2_lo, p.kvp);
