@@ -19,6 +19,12 @@ constexpr int kUncCap = 2048;    // near-threshold keys handled in LDS; more tak
 constexpr int kMaxSel = 4096;    // top_k + window limit (index list kept in LDS)
 constexpr int kSparseChunk = 128;  // selected keys per sparse work-group (4 waves x 32)
 constexpr float kYRange = 64.0f;   // log2 range below the row's top score that the bins span
+constexpr int kYFixBits = 10;      // prefill importance: fixed point, 2^-10 log2 units per step
+// Prefill importance pass: query blocks per wave (8 chunk tokens each per
+// work-group).  Without an O accumulator four fit (two waves per SIMD), so
+// each K operand read from LDS serves 64 query columns; measured 4% faster
+// than two on the 4096-token chunk.
+constexpr int kImportanceQB = 4;
 constexpr int kMaxSplits = 1024;   // context splits per row (full layer, decode)
 constexpr int kSplitTarget = 256;  // decode full layer: work-groups over all rows (MI355X CUs)
 
@@ -65,6 +71,7 @@ struct Plan {
   size_t off_hist_c, off_cand_y, off_cand_idx, off_cand_cnt, off_band_idx, off_band_key;
   // prefill chunk: per-row log2 importance of the older keys (float16), band capacity per row
   size_t off_ybuf;
+  size_t off_kmax;           // prefill: largest |k| (bf16 bits) per (batch, KV head)
   int64_t band_cap;
   // sparse
   int sp_nch;

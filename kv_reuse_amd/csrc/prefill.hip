@@ -26,9 +26,10 @@
 //    range of (batch, KV head, token block): the work-groups that share a KV
 //    head's K/V run on one XCD and share its L2.
 //  * The importance pass (second kernel) recomputes the logits with lse known
-//    and writes y = max_h(s2_h - lse2_h) per (row, older key) in float32, plus
-//    an exact per-row histogram (1/8 octave bins) kept in LDS (the work-group
-//    sees all of its rows' keys, so no atomics leave the work-group).
+//    and writes y = max_h(s2_h - lse2_h) per (row, older key) as 16-bit fixed
+//    point over the 64 octaves below the row's top log-weight (2^-10 octave
+//    steps), and the largest |k| of each KV head, which bounds its float32
+//    error for the selection.
 
 #include "hs2_internal.h"
 
@@ -41,10 +42,6 @@ constexpr int kPThreads = 256;
 // drop to one wave per SIMD, and then measured 45-60% slower on the 4K-token
 // chunk over 128K keys.
 constexpr int kPrefillQB = 2;
-// Importance pass: query blocks per wave.  Without an O accumulator four fit
-// (224 VGPRs, two waves per SIMD), so each K operand read from LDS serves 64
-// query columns; measured 4% faster than two on the 4096-token chunk.
-constexpr int kImportanceQB = 4;
 constexpr int kPKeys = 64;      // keys per tile
 // LDS row pitches, in u16.  K rows advance by 4 banks (68 dwords), so the
 // 16-byte operand reads of 8 or 16 consecutive rows cover every bank once; V
@@ -95,6 +92,19 @@ __device__ __forceinline__ void tile_lstore(const TileRegs& r, u16* kt, u16* vt)
 #pragma unroll
     for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(vd + 8 * c) = r.v[c];
   }
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Running maximum of |k| over a staged K tile, on the bf16 bits: clearing the
+// sign bit leaves magnitudes whose bit patterns order like their values.
+__device__ __forceinline__ u16x2 abs_max_bf16(const TileRegs& r, u16x2 acc) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      acc = __builtin_elementwise_max(acc, __builtin_bit_cast(u16x2, r.k[c][e] & 0x7FFF7FFFu));
+  return acc;
 }
 
 // K as the A operand of S^T for key subtile kt (16 keys) and dims 32c..32c+31.
@@ -312,15 +322,23 @@ __global__ __launch_bounds__(kPThreads, QB <= 2 ? 2 : 1) void full_prefill_kerne
 // heads of one token for one key, and the max over the token's 8 heads is 3
 // in-lane steps and one exchange with the partner lane.
 // Writes, for every row (b, t, g) it owns:
-//   y[row][j] = max_h(s2_h[j] - lse2_h) for older keys j < first_t (float16,
-//               when y is non-null);
-//   scores[row][j] = 2^y for all j <= P_t, 0 above (when scores is non-null).
+//   y[row][j] = max_h(s2_h[j] - lse2_h) for older keys j < first_t, as
+//               round((y - ybase) 2^10) clamped to 0..65535, with ybase the
+//               row's top log-weight (over its 8 heads) minus 64 (when y is
+//               non-null);
+//   scores[row][j] = 2^y for all j <= P_t, 0 above (when scores is non-null);
+//   kmax[b][g][tb] = the largest |k| over this work-group's share of the KV
+//               head's keys 0..S-1 (bf16 bits; when kmax is non-null): whole
+//               key tile i belongs to token block i % n_tblk when that block
+//               reads all of it, else to the last block, which reads every key.
 template <int QB>
 __global__ __launch_bounds__(kPThreads, 2) void prefill_importance_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const double* __restrict__ lse2,
-    f16* __restrict__ y, float* __restrict__ scores, int64_t S, int64_t Spad, int T, int Hkv,
-    int w, int n_tblk, float c2_hi, float c2_lo, int64_t kvp) {
+    const float* __restrict__ ytop_h, u16* __restrict__ y, uint32_t* __restrict__ kmax,
+    float* __restrict__ scores, int64_t S, int64_t Spad, int T, int Hkv, int w, int n_tblk,
+    float c2_hi, float c2_lo, int64_t kvp) {
   __shared__ __align__(16) u16 kt[kPKeys * kPPitch];
+  __shared__ uint32_t s_kmax[kPThreads / 64];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -338,8 +356,11 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_importance_kernel(
   int jloc[QB];
   bool t_ok[QB];
   int64_t P[QB], first[QB];
-  float nl2r[QB][4];     // -lse2 of the lane's 4 heads
-  f16* yrow[QB];
+  // y in fixed-point steps plus 0.5 is s c2 2^10 + (0.5 - 2^10 (lse2_h + ybase)):
+  // one fma per head
+  float nl2r[QB][4];     // 0.5 - 2^10 (lse2_h + ybase) for the lane's 4 heads
+  float yb[QB];          // ybase - 2^-11: y = v 2^-10 + yb
+  u16* yrow[QB];
   float* srow[QB];
 #pragma unroll
   for (int qbk = 0; qbk < QB; ++qbk) {
@@ -356,8 +377,16 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_importance_kernel(
     P[qbk] = pos0 + t;
     first[qbk] = max(static_cast<int64_t>(0), P[qbk] - w + 1);
     const size_t row = (static_cast<size_t>(b) * T + t) * Hkv + g;
+    float yt = -INFINITY;
+    for (int h = 0; h < kG; ++h) yt = fmaxf(yt, ytop_h[row * kG + h]);
+    const float ybase = yt - kYRange;
+    // 2^10 ybase is exact, and so is its sum with 0.5 (|ybase| < 2^12)
+    const float yoff = 0.5f - ybase * static_cast<float>(1 << kYFixBits);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) nl2r[qbk][i] = -static_cast<float>(lse2[row * kG + 4 * (grp & 1) + i]);
+    for (int i = 0; i < 4; ++i)
+      nl2r[qbk][i] = fmaf(-static_cast<float>(lse2[row * kG + 4 * (grp & 1) + i]),
+                          static_cast<float>(1 << kYFixBits), yoff);
+    yb[qbk] = ybase - 1.0f / (2 << kYFixBits);
     yrow[qbk] = y ? y + row * Spad : nullptr;
     srow[qbk] = scores ? scores + row * S : nullptr;
   }
@@ -366,9 +395,19 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_importance_kernel(
   const int n_tiles = static_cast<int>((p_last + kPKeys) / kPKeys);
   // after the head max a lane owns key subtiles 2*(grp & 1) and 2*(grp & 1) + 1
   const int sub0 = 2 * (grp & 1);
+  const float c2s = c2_hi * static_cast<float>(1 << kYFixBits);   // exact
+  // this work-group's share of max |k|: whole tiles i with i % n_tblk == tb
+  // (or, when that block does not read all of tile i, the last block's)
+  auto owns_tile = [&](int i) {
+    const int o = i % n_tblk;
+    const int64_t o_last = pos0 + min(T - 1, o * kTok + kTok - 1);
+    return (static_cast<int64_t>(i + 1) * kPKeys <= o_last + 1 ? o : n_tblk - 1) == tb;
+  };
+  u16x2 kabs{0, 0};
 
   TileRegs regs;
   tile_gload<false>(regs, kr, nullptr, 0, p_last);
+  if (kmax && owns_tile(0)) kabs = abs_max_bf16(regs, kabs);
   tile_lstore<false>(regs, kt, nullptr);
 #pragma unroll
   for (int qbk = 0; qbk < QB; ++qbk)
@@ -394,16 +433,16 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_importance_kernel(
     }
 #pragma unroll
     for (int qbk = 0; qbk < QB; ++qbk) {
-      // y per (token, key): max over the 8 heads = 4 here x the partner lane.
-      // One fma per head: the scale's low part (a * c2_lo, below 1e-7 in log2
-      // units) is dropped; it is smaller than the float32 rounding of y, and
-      // the selection re-ranks every key near its threshold in float64
+      // y per (token, key), in fixed-point steps plus 0.5: max over the 8
+      // heads = 4 here x the partner lane.  One fma per head: the scale's low
+      // part (below 1e-7 of s c2) is dropped; the selection allows for it and
+      // re-ranks every key near its threshold in float64
       float yv[4];
 #pragma unroll
       for (int sub = 0; sub < 4; ++sub) {
         float m = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaf(sacc[qbk][sub][i], c2_hi, nl2r[qbk][i]));
+        for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaf(sacc[qbk][sub][i], c2s, nl2r[qbk][i]));
         yv[sub] = fmaxf(m, __shfl_xor(m, 16));
       }
 #pragma unroll
@@ -412,16 +451,31 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_importance_kernel(
         const float yy = sub == 0 ? yv[0] : sub == 1 ? yv[1] : sub == 2 ? yv[2] : yv[3];
         const int64_t key = key0 + 16 * sub + col;
         if (!t_ok[qbk] || key > P[qbk]) continue;
-        if (srow[qbk]) srow[qbk][key] = __builtin_amdgcn_exp2f(yy);
-        // stored as float16: the error is below 1/60 in log2 units over the
-        // range the selection's histogram covers, an eighth of one of its bins
-        if (key < first[qbk] && yrow[qbk]) yrow[qbk][key] = static_cast<f16>(yy);
+        if (srow[qbk])
+          srow[qbk][key] = __builtin_amdgcn_exp2f(fmaf(yy, 1.0f / (1 << kYFixBits), yb[qbk]));
+        if (key < first[qbk] && yrow[qbk]) {
+          // clamp to 0..65535, then truncate: rounds to nearest
+          const float z = __builtin_amdgcn_fmed3f(yy, 0.f, 65535.f);
+          yrow[qbk][key] = static_cast<u16>(static_cast<uint32_t>(z));
+        }
       }
     }
     __syncthreads();
     if (more) {
+      if (kmax && owns_tile(it + 1)) kabs = abs_max_bf16(regs, kabs);
       tile_lstore<false>(regs, kt, nullptr);
       __syncthreads();
+    }
+  }
+  if (kmax) {
+    uint32_t m = max(static_cast<uint32_t>(kabs[0]), static_cast<uint32_t>(kabs[1]));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(m, off)));
+    if (lane == 0) s_kmax[wave] = m;
+    __syncthreads();
+    if (tid == 0) {
+      for (int wv = 1; wv < kPThreads / 64; ++wv) m = max(m, s_kmax[wv]);
+      kmax[static_cast<size_t>(bg) * n_tblk + tb] = m;
     }
   }
   // scores past P_t are 0
@@ -464,7 +518,9 @@ hipError_t launch_prefill_importance(const Plan& p, const u16* q, const u16* k, 
   const int n_wg = p.B * p.Hkv * n_tblk;
   hipLaunchKernelGGL(prefill_importance_kernel<QB>, dim3(n_wg), dim3(kPThreads), 0, st, q, k,
                      reinterpret_cast<const double*>(w + p.off_lse2),
-                     for_select ? reinterpret_cast<f16*>(w + p.off_ybuf) : nullptr, scores,
+                     reinterpret_cast<const float*>(w + p.off_ytop),
+                     for_select ? reinterpret_cast<u16*>(w + p.off_ybuf) : nullptr,
+                     for_select ? reinterpret_cast<uint32_t*>(w + p.off_kmax) : nullptr, scores,
                      p.S, p.Spad, p.T, p.Hkv, p.w, n_tblk, c2_hi, c2_lo, p.kvp);
   return hipGetLastError();
 }

@@ -164,6 +164,45 @@ __device__ void reserve_two(uint32_t n0, uint32_t n1, uint32_t* ctr0, uint32_t* 
   o1 = s_base[1] + s_cnt[1][wave] + i1 - n1;
 }
 
+// Block-wide exclusive offsets of one or two per-thread counts with a single
+// barrier: each wave's totals go to its slots of buf, and every thread then
+// sums the slots before its wave.  Consecutive calls must alternate between
+// two buffers, so that a wave running ahead into the next call never
+// overwrites totals another wave is still reading.  NW = waves per block.
+template <int NW>
+__device__ __forceinline__ void block_offsets2(uint32_t n0, uint32_t n1, uint32_t (*buf)[NW],
+                                               uint32_t& o0, uint32_t& o1, uint32_t& t0,
+                                               uint32_t& t1) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t i0 = n0, i1 = n1;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t a = __shfl_up(i0, off), b = __shfl_up(i1, off);
+    if (lane >= off) {
+      i0 += a;
+      i1 += b;
+    }
+  }
+  if (lane == 63) {
+    buf[0][wave] = i0;
+    buf[1][wave] = i1;
+  }
+  __syncthreads();
+  uint32_t b0 = 0, b1 = 0, a0 = 0, a1 = 0;
+#pragma unroll
+  for (int wv = 0; wv < NW; ++wv) {
+    const uint32_t c0 = buf[0][wv], c1 = buf[1][wv];
+    a0 += c0;
+    a1 += c1;
+    b0 += wv < wave ? c0 : 0u;
+    b1 += wv < wave ? c1 : 0u;
+  }
+  o0 = b0 + i0 - n0;
+  o1 = b1 + i1 - n1;
+  t0 = a0;
+  t1 = a1;
+}
+
 struct Cand {
   uint64_t key;  // larger = better
   int32_t idx;   // ties: lower index first
@@ -1370,13 +1409,6 @@ __device__ KThr key_threshold(const uint64_t* keys, uint32_t n, uint32_t need, u
   }
 }
 
-// Element e (0..15) of 16 float16 values held as two 16-byte words, widened.
-__device__ __forceinline__ float f16_at(const u32x4 (&v)[2], int e) {
-  const uint32_t word = v[e >> 3][(e >> 1) & 3];
-  const uint16_t bits = static_cast<uint16_t>((e & 1) ? (word >> 16) : (word & 0xFFFFu));
-  return static_cast<float>(__builtin_bit_cast(f16, bits));
-}
-
 // Number of entries of the ascending array a[0..n) that are < v.
 __device__ __forceinline__ uint32_t lower_bound_lds(const int32_t* a, uint32_t n, int32_t v) {
   uint32_t lo = 0, hi = n;
@@ -1389,83 +1421,223 @@ __device__ __forceinline__ uint32_t lower_bound_lds(const int32_t* a, uint32_t n
 }
 
 // One work-group per row (b, t, g) of a prefill chunk: the exact top-k of the
-// row's older keys from their log2 importance y (stored as float16).
-//  * A first pass over y builds the row's histogram (kPNB bins of 1/8 octave
-//    above its ybase) and finds the bin b* of the k-th largest.
-//  * A second pass in key order: bins above b*+1 go to the "up" list, bins
-//    b*-1..b*+1 (the float16 error of y is below an eighth of a bin) to the band list;
-//    both lists come out in ascending key order.
-//  * The band keys' importance is recomputed in float64 from exact bf16
-//    products; a radix threshold on it picks the band's share, ties going to
-//    the lower index (the band list is in index order).
+// row's older keys from their stored log2 importance v (16-bit fixed point,
+// 2^-10 octave steps; bin = v >> 7 is an eighth of an octave).
+//  * One pass over v, in rounds of 16 values per thread, keeps the row's
+//    histogram of bins only at or above floor, the k-th largest bin of the
+//    values seen so far: a subset's k-th largest never exceeds the whole
+//    row's, so every bin at or above the row's k-th bin is counted exactly and
+//    most values cost no atomic.  The values within reach of the band (below)
+//    are listed in LDS (index and v), in key order.
+//  * The k-th bin b* of the finished histogram and a 128-bucket count of the
+//    listed values in b* give c, the k-th largest v exactly.
+//  * E bounds twice the difference between a stored v and the exact float64
+//    importance (the fixed-point rounding plus the float32 error of the
+//    importance pass, from the largest |k| of the head and the row's |q|).
+//    Keys with v > c + E are selected, keys with v < c - E are not, and the
+//    band [c - E, c + E] is re-ranked on its importance recomputed in float64
+//    from exact bf16 products: a radix threshold picks the band's share, ties
+//    going to the lower index (the band list is in index order).
 //  * The up list and the band winners, both ascending, are merged into the
 //    output by rank; then the window, the padding and the count.
-// A band larger than band_cap is ranked by its float16 y instead.
+// A list longer than LDS holds is replaced by a second pass over v, with the
+// band widened to [first value of b* - E, last value of b* + E]; a band larger
+// than band_cap is ranked by v itself.
+constexpr int kPList = 4 * kUncCap;   // listed values per row held in LDS
+constexpr int kPListPer = kPList / kRowThreads;
+constexpr int kVBinShift = 16 - 9;    // v >> 7: the kPNB = 512 bins
+static_assert(kPList % kRowThreads == 0, "list split evenly over the threads");
+static_assert(2 * kMaxSel >= kPList, "the list's values fit in the up list's space");
+static_assert(kPList >= 3 * kUncCap, "the band's keys and indices fit in the list's space");
+static_assert(kPNB == 1 << (16 - kVBinShift), "bins are the top bits of v");
+
+__device__ __forceinline__ uint32_t u16_at(const u32x4 (&v)[2], int e) {
+  const uint32_t word = v[e >> 3][(e >> 1) & 3];
+  return (e & 1) ? (word >> 16) : (word & 0xFFFFu);
+}
+
 __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
-    const f16* __restrict__ ybuf, const float* __restrict__ ytop_h, const double* __restrict__ lse2, const u16* __restrict__ q,
-    const u16* __restrict__ k, int32_t* __restrict__ band_idx, uint64_t* __restrict__ band_key,
-    int64_t band_cap, int32_t* __restrict__ idx_out, int32_t* __restrict__ nsel_out, int64_t S,
-    int64_t Spad, int T, int Hkv, int topk, int w, int cap, double c2, int64_t kvp) {
+    const u16* __restrict__ ybuf, const uint32_t* __restrict__ kmax, int n_ib,
+    const double* __restrict__ lse2,
+    const u16* __restrict__ q, const u16* __restrict__ k, int32_t* __restrict__ band_idx,
+    uint64_t* __restrict__ band_key, int64_t band_cap, int32_t* __restrict__ idx_out,
+    int32_t* __restrict__ nsel_out, int64_t S, int64_t Spad, int T, int Hkv, int topk, int w,
+    int cap, double c2, int64_t kvp) {
   __shared__ __align__(16) int32_t up[kMaxSel];
   __shared__ __align__(16) int32_t bw[kMaxSel];        // band winners; first the histogram
-  __shared__ __align__(16) uint64_t lbk[kUncCap];
-  __shared__ __align__(16) int32_t lbi[kUncCap];
+  // the list's indices; after the split, the band (keys, then indices); the
+  // list's values sit in the up list's space until the split
+  __shared__ __align__(16) uint32_t pool[kPList];
   __shared__ double qd[kG * kD];
   __shared__ double l2s[kG];
+  __shared__ float s_qn[2][kRowThreads / 64];
   __shared__ uint32_t h256[256];
   __shared__ uint32_t s_red[4];
   __shared__ uint64_t s_hi;
   __shared__ uint32_t s_need, s_count, s_tlo;
   __shared__ uint64_t s_thi;
   __shared__ int s_done;
-  __shared__ int s_b, s_lo, s_hi2;
-  __shared__ uint32_t s_nband;
-  __shared__ float s_ybase;
+  __shared__ int s_b, s_floor, s_c, s_E;
+  __shared__ uint32_t s_km;
+  __shared__ uint32_t s_off[2][2][kRowThreads / 64];
+  __shared__ uint32_t s_above;
   __shared__ uint32_t s_cnt[2][16];
   __shared__ uint32_t s_base[4];
   uint32_t* lh = reinterpret_cast<uint32_t*>(bw);
+  uint16_t* lval = reinterpret_cast<uint16_t*>(up);
+  int32_t* lidx = reinterpret_cast<int32_t*>(pool);
+  uint64_t* lbk = reinterpret_cast<uint64_t*>(pool);
+  int32_t* lbi = reinterpret_cast<int32_t*>(pool + 2 * kUncCap);
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int P = row_pos(r, T, Hkv, S);
   const int64_t first = row_first(P, w);
+  const int b = r / (T * Hkv);
+  const int g = r % Hkv;
   int32_t* out = idx_out + static_cast<size_t>(r) * cap;
   uint32_t n_keep = 0;
   if (topk > 0 && first > 0) {
     for (int i = tid; i < kPNB; i += kRowThreads) lh[i] = 0u;
-    if (tid == 0) s_ybase = row_ybase(ytop_h, r);
-    const u16* qr = q + static_cast<size_t>(r) * kG * kD;
-    for (int i = tid; i < kG * kD; i += kRowThreads) qd[i] = static_cast<double>(bf16_bits_to_f32(qr[i]));
-    if (tid < kG) l2s[tid] = lse2[static_cast<size_t>(r) * kG + tid];
+    if (tid == 0) {
+      s_floor = 0;
+      s_km = 0u;
+    }
     __syncthreads();
-    // ---- the row's histogram of y (bins of 1/8 octave above ybase), from the
-    // same stored float16 values the classification below reads
+    // the head's max |k|: the largest of the importance pass's block shares
     {
-      const float yb = s_ybase;
-      const f16* yrh = ybuf + static_cast<size_t>(r) * Spad;
-      for (int64_t i0 = 16 * static_cast<int64_t>(tid); i0 < first; i0 += 16 * kRowThreads) {
-        u32x4 v[2];
+      const uint32_t* kp = kmax + (static_cast<size_t>(b) * Hkv + g) * n_ib;
+      uint32_t m = 0u;
+      for (int i = tid; i < n_ib; i += kRowThreads) m = max(m, kp[i]);
 #pragma unroll
-        for (int u = 0; u < 2; ++u)
-          v[u] = i0 + 8 * u < first ? *reinterpret_cast<const u32x4*>(yrh + i0 + 8 * u)
-                                    : u32x4{0u, 0u, 0u, 0u};
+      for (int off = 32; off > 0; off >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(m, off)));
+      if (lane == 0 && m) atomicMax(&s_km, m);
+    }
+    const u16* qr = q + static_cast<size_t>(r) * kG * kD;
+    // q in float64, and each head's sum of |q| (thread t holds elements t and
+    // t + 512: heads wave / 2 and 4 + wave / 2)
+    {
+      float qa[2];
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (i0 + e < first) atomicAdd(&lh[key_from_log2(f16_at(v, e), yb) >> kPBinShift], 1u);
+      for (int u = 0; u < 2; ++u) {
+        const int i = tid + u * kRowThreads;
+        const float x = bf16_bits_to_f32(qr[i]);
+        qd[i] = static_cast<double>(x);
+        qa[u] = fabsf(x);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) qa[u] += __shfl_xor(qa[u], off);
+      if (lane == 0) {
+        s_qn[0][wave] = qa[0];
+        s_qn[1][wave] = qa[1];
       }
     }
+    if (tid < kG) l2s[tid] = lse2[static_cast<size_t>(r) * kG + tid];
+    __syncthreads();
+    if (tid == 0) {
+      // E: twice the largest |stored - exact| in steps of 2^-10 octave, plus
+      // one.  Storing costs at most 1.5 steps (rounding, and clamping at the
+      // top) and the float32 roundings of the per-head offset and of the fma
+      // that forms the step count (below 2^17 in magnitude near any
+      // threshold) 2^-6 steps each.  The float32 importance is off by at most
+      // 2^-24 (130 |s|max c2 + 2 |lse2|) octaves: the MFMA's 128 float32
+      // additions of exact bf16 products, the scale's dropped low part and
+      // the fma each cost 2^-24 of |s| c2 <= max|k| sum|q_h| c2; lse2's
+      // rounding to float32 costs 2^-24 |lse2|, counted twice.
+      double qn = 0.0, l2m = 0.0;
+      for (int h = 0; h < kG; ++h) {
+        const int wv = 2 * (h & 3);
+        const int u = h >> 2;
+        qn = fmax(qn, static_cast<double>(s_qn[u][wv]) + static_cast<double>(s_qn[u][wv + 1]));
+        l2m = fmax(l2m, fabs(l2s[h]));
+      }
+      const double km = static_cast<double>(bf16_bits_to_f32(static_cast<u16>(s_km)));
+      // sum|q| was taken in float32: allow 2^-20 relative for its rounding
+      const double d32 = 0x1p-24 * (130.0 * km * qn * (1.0 + 0x1p-20) * c2 + 2.0 * l2m);
+      const double steps = 1.5 + 0x1p-5 + d32 * static_cast<double>(1 << kYFixBits);
+      s_E = static_cast<int>(fmin(ceil(2.0 * steps) + 1.0, 65536.0));
+    }
+    __syncthreads();
+    const int E = s_E;
+    const u16* yr = ybuf + static_cast<size_t>(r) * Spad;
+    // 16 values per thread and round, as two 16-byte loads; the next round's
+    // loads are issued before this round is processed
+    const int64_t rounds = (first + 16 * kRowThreads - 1) / (16 * kRowThreads);
+    auto load_round = [&](int64_t rr, u32x4 (&yv)[2]) {
+      const int64_t i0 = 16 * (static_cast<int64_t>(tid) + rr * kRowThreads);
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        yv[u] = i0 + 8 * u < first ? *reinterpret_cast<const u32x4*>(yr + i0 + 8 * u)
+                                   : u32x4{0u, 0u, 0u, 0u};
+    };
+    // ---- the pass: histogram at or above floor, and the list of the values
+    // at or above (first value of floor) - E.  One barrier per round: the
+    // floor that wave 0 raises after it is read by the other waves whenever
+    // they get to it (a stale floor is still a valid one: it only lists and
+    // counts more).  The first round's values are counted before any are
+    // listed, so that its floor already applies to them.
+    uint32_t n_list = 0;
+    {
+      u32x4 ycur[2], ynxt[2];
+      if (rounds > 0) load_round(0, ycur);
+      for (int64_t rr = 0; rr < rounds; ++rr) {
+        const int64_t i0 = 16 * (static_cast<int64_t>(tid) + rr * kRowThreads);
+        if (rr + 1 < rounds) load_round(rr + 1, ynxt);
+        const int nv = static_cast<int>(min(static_cast<int64_t>(16), first - i0));
+        int fl = *static_cast<volatile int*>(&s_floor);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int bn = static_cast<int>(u16_at(ycur, e) >> kVBinShift);
+          if (e < nv && bn >= fl) atomicAdd(&lh[bn], 1u);
+        }
+        if (rr == 0) {
+          __syncthreads();
+          if (wave == 0) {
+            const KthBin kb = kth_bin_wave_n<kPNB>(lh, static_cast<uint32_t>(topk));
+            if (lane == 0 && kb.found) s_floor = kb.bstar;
+          }
+          __syncthreads();
+          fl = s_floor;
+        }
+        const int vmin = (fl << kVBinShift) - E;
+        uint32_t ml = 0;
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          ml |= static_cast<uint32_t>(e < nv && static_cast<int>(u16_at(ycur, e)) >= vmin) << e;
+        uint32_t ol, o_dummy, tot, t_dummy;
+        block_offsets2<kRowThreads / 64>(__popc(ml), 0u, s_off[rr & 1], ol, o_dummy, tot, t_dummy);
+        // the round's atomics are complete: raise the floor
+        if (wave == 0) {
+          const KthBin kb = kth_bin_wave_n<kPNB>(lh, static_cast<uint32_t>(topk));
+          if (lane == 0 && kb.found && kb.bstar > fl) atomicMax(&s_floor, kb.bstar);
+        }
+        ol += n_list;
+        n_list += tot;
+        if (ml) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            if (!((ml >> e) & 1u)) continue;
+            if (ol < static_cast<uint32_t>(kPList)) {
+              lidx[ol] = static_cast<int32_t>(i0 + e);
+              lval[ol] = static_cast<uint16_t>(u16_at(ycur, e));
+            }
+            ++ol;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) ycur[u] = ynxt[u];
+      }
+    }
+    const bool listed = n_list <= static_cast<uint32_t>(kPList);
+    if (tid < 128) h256[tid] = 0u;
     __syncthreads();
     if (tid < 64) {
       const KthBin kb = kth_bin_wave_n<kPNB>(lh, static_cast<uint32_t>(topk));
       if (tid == 0) {
         s_b = kb.found ? kb.bstar : -1;
-        if (kb.found) {
-          const int lo = max(0, kb.bstar - 1), hi = min(kPNB - 1, kb.bstar + 1);
-          uint32_t nb = 0;
-          for (int bb = lo; bb <= hi; ++bb) nb += lh[bb];
-          s_lo = lo;
-          s_hi2 = hi;
-          s_nband = nb;
-        }
+        s_above = kb.above;
       }
     }
     __syncthreads();
@@ -1474,61 +1646,100 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
       n_keep = static_cast<uint32_t>(min(first, static_cast<int64_t>(topk)));
       for (uint32_t i = tid; i < n_keep; i += kRowThreads) out[i] = static_cast<int32_t>(i);
     } else {
-      const int lo = s_lo, hi = s_hi2;
-      const uint32_t n_band_h = s_nband;
-      const bool band_lds = n_band_h <= static_cast<uint32_t>(kUncCap);
-      const bool band_glob = !band_lds && n_band_h <= static_cast<uint64_t>(band_cap);
-      const float ybase = s_ybase;
-      const f16* yr = ybuf + static_cast<size_t>(r) * Spad;
+      const int bstar = s_b;
+      int band_lo, band_hi;
+      if (listed) {
+        // ---- c: the k-th largest v, from the listed values in bin b*
+        for (uint32_t i = tid; i < n_list; i += kRowThreads) {
+          const uint32_t v = lval[i];
+          if (static_cast<int>(v >> kVBinShift) == bstar) atomicAdd(&h256[v & 127u], 1u);
+        }
+        __syncthreads();
+        if (tid < 64) {
+          const KthBin kc = kth_bin_wave_n<128>(h256, static_cast<uint32_t>(topk) - s_above);
+          if (tid == 0) s_c = (bstar << kVBinShift) | kc.bstar;
+        }
+        __syncthreads();
+        band_lo = max(0, s_c - E);
+        band_hi = min(65535, s_c + E);
+      } else {
+        band_lo = max(0, (bstar << kVBinShift) - E);
+        band_hi = min(65535, (bstar << kVBinShift) + 127 + E);
+      }
       int32_t* gbi = band_idx + static_cast<size_t>(r) * band_cap;
       uint64_t* gbk = band_key + static_cast<size_t>(r) * band_cap;
-      int32_t* bi = band_lds ? lbi : gbi;
-      uint64_t* bk = band_lds ? lbk : gbk;
-      // ---- one pass over y (16 entries per thread and round; the next
-      // round's loads are issued before this round is processed)
-      const int64_t rounds = (first + 16 * kRowThreads - 1) / (16 * kRowThreads);
+      bool band_lds = false, band_glob = false;
+      int32_t* bi = gbi;
+      uint64_t* bk = gbk;
       uint32_t cu = 0, ca = 0;
-      // 16 float16 values per thread and round, as two 16-byte loads
-      u32x4 ycur[2], ynxt[2];
-      auto load_round = [&](int64_t rr, u32x4 (&yv)[2]) {
-        const int64_t i0 = 16 * (static_cast<int64_t>(tid) + rr * kRowThreads);
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-          yv[u] = i0 + 8 * u < first ? *reinterpret_cast<const u32x4*>(yr + i0 + 8 * u)
-                                     : u32x4{0u, 0u, 0u, 0u};
-      };
-
-      if (rounds > 0) load_round(0, ycur);
-      for (int64_t rr = 0; rr < rounds; ++rr) {
-        const int64_t i0 = 16 * (static_cast<int64_t>(tid) + rr * kRowThreads);
-        if (rr + 1 < rounds) load_round(rr + 1, ynxt);
+      if (listed) {
+        // ---- split the list: each thread takes kPListPer consecutive
+        // entries into registers, so the band may overwrite the list
+        const uint32_t q0 = static_cast<uint32_t>(tid) * kPListPer;
+        int32_t li[kPListPer];
         uint32_t mu = 0, ma = 0;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const bool valid = i0 + e < first;
-          const int bn = static_cast<int>(key_from_log2(f16_at(ycur, e), ybase) >> kPBinShift);
-          mu |= static_cast<uint32_t>(valid && bn > hi) << e;
-          ma |= static_cast<uint32_t>(valid && bn >= lo && bn <= hi) << e;
+        for (int j = 0; j < kPListPer; ++j) {
+          const uint32_t i = q0 + j;
+          li[j] = 0;
+          if (i < n_list) {
+            li[j] = lidx[i];
+            const int v = lval[i];
+            mu |= static_cast<uint32_t>(v > band_hi) << j;
+            ma |= static_cast<uint32_t>(v >= band_lo && v <= band_hi) << j;
+          }
         }
         uint32_t ou, oa;
-        reserve_two(__popc(mu), __popc(ma), nullptr, nullptr, s_cnt, s_base, ou, oa);
-        ou += cu;
-        oa += ca;
-        cu += s_base[2];
-        ca += s_base[3];
-        for (uint32_t m = mu; m; m &= m - 1) {
-          if (ou < static_cast<uint32_t>(kMaxSel)) up[ou] = static_cast<int32_t>(i0 + __builtin_ctz(m));
-          ++ou;
-        }
-        if (band_lds || band_glob) {
-          const uint32_t lim = band_lds ? static_cast<uint32_t>(kUncCap) : static_cast<uint32_t>(band_cap);
-          for (uint32_t m = ma; m; m &= m - 1) {
-            if (oa < lim) bi[oa] = static_cast<int32_t>(i0 + __builtin_ctz(m));
+        block_offsets2<kRowThreads / 64>(__popc(mu), __popc(ma), s_off[0], ou, oa, cu, ca);
+        band_lds = ca <= static_cast<uint32_t>(kUncCap);
+        band_glob = !band_lds && ca <= static_cast<uint64_t>(band_cap);
+        bi = band_lds ? lbi : gbi;
+        bk = band_lds ? lbk : gbk;
+#pragma unroll
+        for (int j = 0; j < kPListPer; ++j) {
+          if ((mu >> j) & 1u) {
+            if (ou < static_cast<uint32_t>(kMaxSel)) up[ou] = li[j];
+            ++ou;
+          }
+          if ((ma >> j) & 1u) {
+            if (band_lds || band_glob) bi[oa] = li[j];
             ++oa;
           }
         }
+      } else {
+        // ---- the list overflowed: a second pass over v, in key order; the
+        // band goes to the global list (up to band_cap entries)
+        u32x4 ycur[2], ynxt[2];
+        if (rounds > 0) load_round(0, ycur);
+        for (int64_t rr = 0; rr < rounds; ++rr) {
+          const int64_t i0 = 16 * (static_cast<int64_t>(tid) + rr * kRowThreads);
+          if (rr + 1 < rounds) load_round(rr + 1, ynxt);
+          const int nv = static_cast<int>(min(static_cast<int64_t>(16), first - i0));
+          uint32_t mu = 0, ma = 0;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) ycur[u] = ynxt[u];
+          for (int e = 0; e < 16; ++e) {
+            const int v = static_cast<int>(u16_at(ycur, e));
+            mu |= static_cast<uint32_t>(e < nv && v > band_hi) << e;
+            ma |= static_cast<uint32_t>(e < nv && v >= band_lo && v <= band_hi) << e;
+          }
+          uint32_t ou, oa;
+          reserve_two(__popc(mu), __popc(ma), nullptr, nullptr, s_cnt, s_base, ou, oa);
+          ou += cu;
+          oa += ca;
+          cu += s_base[2];
+          ca += s_base[3];
+          for (uint32_t m = mu; m; m &= m - 1) {
+            if (ou < static_cast<uint32_t>(kMaxSel)) up[ou] = static_cast<int32_t>(i0 + __builtin_ctz(m));
+            ++ou;
+          }
+          for (uint32_t m = ma; m; m &= m - 1) {
+            if (oa < static_cast<uint64_t>(band_cap)) gbi[oa] = static_cast<int32_t>(i0 + __builtin_ctz(m));
+            ++oa;
+          }
+#pragma unroll
+          for (int u = 0; u < 2; ++u) ycur[u] = ynxt[u];
+        }
+        band_glob = ca <= static_cast<uint64_t>(band_cap);
       }
       __syncthreads();
       const uint32_t n_up = min(cu, static_cast<uint32_t>(topk));
@@ -1537,37 +1748,56 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
       if (band_lds || band_glob) {
         const uint32_t n_band = min(ca, band_lds ? static_cast<uint32_t>(kUncCap)
                                                  : static_cast<uint32_t>(band_cap));
-        // ---- exact importance of the band keys in float64 (bf16 products are exact)
-        const int b = r / (T * Hkv);
-        const int g = r % Hkv;
+        // ---- exact importance of the band keys in float64 (bf16 products are
+        // exact): 16 lanes per key, lane j of a group taking dims 8j..8j+7 of
+        // all 8 heads, then a sum over the group
         const u16* kr = k + (static_cast<size_t>(b) * Hkv + g) * static_cast<size_t>(kvp) * kD;
-        for (uint32_t i = tid; i < n_band; i += kRowThreads) {
-          const u16* kj = kr + static_cast<size_t>(bi[i]) * kD;
-          double acc[kG];
+        const int part = tid & 15;
+        for (uint32_t i = static_cast<uint32_t>(tid) >> 4; i < n_band; i += kRowThreads / 16) {
+          const u32x4 raw = load_u32x4(kr + static_cast<size_t>(bi[i]) * kD + 8 * part);
+          double kv[8];
 #pragma unroll
-          for (int h = 0; h < kG; ++h) acc[h] = 0.0;
-          for (int c4 = 0; c4 < 4; ++c4) {
-            u32x4 raw[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) raw[c] = load_u32x4(kj + 32 * c4 + 8 * c);
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-#pragma unroll
-              for (int t2 = 0; t2 < 8; ++t2) {
-                const uint32_t word = raw[c][t2 >> 1];
-                const double kv = static_cast<double>(
-                    __uint_as_float((t2 & 1) ? (word & 0xFFFF0000u) : (word << 16)));
-                const int dd = 32 * c4 + 8 * c + t2;
-#pragma unroll
-                for (int h = 0; h < kG; ++h) acc[h] = fma(qd[h * kD + dd], kv, acc[h]);
-              }
+          for (int t2 = 0; t2 < 8; ++t2) {
+            const uint32_t word = raw[t2 >> 1];
+            kv[t2] = static_cast<double>(__uint_as_float((t2 & 1) ? (word & 0xFFFF0000u) : (word << 16)));
           }
+          // one head at a time (a short live range), summed over the group:
+          // its 16 lanes share i, so the exchanges stay in the group
           double yy = -INFINITY;
+#pragma unroll 1
+          for (int h = 0; h < kG; ++h) {
+            const double* qh = qd + h * kD + 8 * part;
+            double acc = 0.0;
 #pragma unroll
-          for (int h = 0; h < kG; ++h) yy = fmax(yy, c2 * acc[h] - l2s[h]);
-          bk[i] = ordered_u64(yy);
+            for (int t2 = 0; t2 < 8; ++t2) acc = fma(qh[t2], kv[t2], acc);
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) acc += __shfl_xor(acc, off);
+            yy = fmax(yy, c2 * acc - l2s[h]);
+          }
+          if (part == 0) bk[i] = ordered_u64(yy);
         }
         __syncthreads();
+        if (n_band <= 64) {
+          // ---- a small band: wave 0 ranks it directly.  Lane i holds band
+          // entry i (index order); its rank counts the entries with a larger
+          // key, or an equal key and a lower index; the best `take` win
+          if (wave == 0) {
+            const bool have = static_cast<uint32_t>(lane) < n_band;
+            const uint64_t kh = have ? bk[lane] : 0ull;
+            uint32_t rank = 0;
+            for (int j = 0; j < static_cast<int>(n_band); ++j) {
+              const uint64_t kj = (static_cast<uint64_t>(static_cast<uint32_t>(__shfl(static_cast<int>(kh >> 32), j))) << 32) |
+                                  static_cast<uint32_t>(__shfl(static_cast<int>(kh & 0xFFFFFFFFull), j));
+              rank += (kj > kh || (kj == kh && j < lane)) ? 1u : 0u;
+            }
+            const bool win = have && rank < take;
+            const uint64_t bal = __ballot(win);
+            if (win) bw[__popcll(bal & ((1ull << lane) - 1ull))] = bi[lane];
+            if (lane == 0) s_count = static_cast<uint32_t>(__popcll(bal));
+          }
+          __syncthreads();
+          n_w = s_count;
+        } else {
         // ---- the band's share: all of it, or the best `take` by threshold
         KThr kt{0ull, 0u, true};
         const bool by_thr = take < n_band;
@@ -1614,22 +1844,21 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
             ++o_w;
           }
         }
+        }
       } else if (take > 0) {
         // the band is too large to list: rank it by its float16 importance
         // (unordered winners, then sorted)
         struct ScanSrc {
-          const f16* yr;
-          float ybase;
+          const u16* yr;
           int lo, hi;
           __device__ bool get(int64_t i, uint64_t& key, int32_t& j) const {
-            const float yy = static_cast<float>(yr[i]);
-            const int bn = static_cast<int>(key_from_log2(yy, ybase) >> kPBinShift);
-            if (bn < lo || bn > hi) return false;
-            key = static_cast<uint64_t>(ordered_u32(yy));
+            const int v = yr[i];
+            if (v < lo || v > hi) return false;
+            key = static_cast<uint64_t>(v);
             j = static_cast<int32_t>(i);
             return true;
           }
-        } src{yr, ybase, lo, hi};
+        } src{yr, band_lo, band_hi};
         if (tid == 0) s_count = 0u;
         __syncthreads();
         radix_select_band(src, first, min(take, ca), bw, &s_count, h256, &s_thi, &s_tlo, &s_need);
@@ -1984,8 +2213,9 @@ hipError_t launch_prefill_select(const Plan& p, const u16* q, const u16* k, int3
   char* w = static_cast<char*>(ws);
   const double c2 = p.scale * 1.4426950408889634;
   hipLaunchKernelGGL(prefill_select_kernel, dim3(p.R), dim3(kRowThreads), 0, st,
-                     reinterpret_cast<const f16*>(w + p.off_ybuf),
-                     reinterpret_cast<const float*>(w + p.off_ytop),
+                     reinterpret_cast<const u16*>(w + p.off_ybuf),
+                     reinterpret_cast<const uint32_t*>(w + p.off_kmax),
+                     (p.T + 8 * kImportanceQB - 1) / (8 * kImportanceQB),
                      reinterpret_cast<const double*>(w + p.off_lse2), q, k,
                      reinterpret_cast<int32_t*>(w + p.off_band_idx),
                      reinterpret_cast<uint64_t*>(w + p.off_band_key), p.band_cap, idx, n_sel, p.S,

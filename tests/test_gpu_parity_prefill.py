@@ -49,10 +49,15 @@ def test_prefill_small(hs2, name, kw):
     gh.log(f"  {st}")
 
 
-def test_prefill_identical_keys(hs2):
-    # every key the same: all importances of a row tie, the lowest indices win
-    w = wl.small(name="ties", batch=1, n_q_tokens=24, n_q_heads=8, n_kv_heads=1, ctx_len=900,
+@pytest.mark.parametrize("ctx,T", [(900, 24), (7000, 8), (9500, 6)],
+                         ids=["listed", "list_overflow_band_in_memory", "list_overflow_band_by_f16"])
+def test_prefill_identical_keys(hs2, ctx, T):
+    # every key the same: all importances of a row tie, the lowest indices win.
+    # Past 6144 older keys the tie overflows the selection's LDS list (a second
+    # pass over the importance); past 8192 the band is ranked by its float16 value.
+    w = wl.small(name="ties", batch=1, n_q_tokens=T, n_q_heads=8, n_kv_heads=1, ctx_len=ctx,
                  n_sparse_layers=1, top_k=50, window=10, config_id=36)
+    gh.log(f"[prefill] identical keys S={ctx} T={T}")
     x = wl.generate(w)
     x["k"][:] = x["k"][:, :, :1, :]
     res = gh.run_step(w, x)
