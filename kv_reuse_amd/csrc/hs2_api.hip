@@ -149,7 +149,7 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
   q.off_ybuf = q.off_ukey;
   // per (batch, KV head, importance token block): that block's share of max |k|
   q.off_kmax = take(decode ? 0 : static_cast<size_t>(q.B) * q.Hkv *
-                                      ceil_div(q.T, 8 * kImportanceQB) * sizeof(uint32_t));
+                                      ceil_div(q.T, kImportanceTok) * sizeof(uint32_t));
   const size_t sp_parts = q.sp_nch > 1 ? Rz * q.sp_nch * n_layers * kG : 0;
   q.off_sp_m = take(sp_parts * sizeof(float));
   q.off_sp_l = take(sp_parts * sizeof(float));

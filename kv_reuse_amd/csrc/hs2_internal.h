@@ -20,11 +20,7 @@ constexpr int kMaxSel = 4096;    // top_k + window limit (index list kept in LDS
 constexpr int kSparseChunk = 128;  // selected keys per sparse work-group (4 waves x 32)
 constexpr float kYRange = 64.0f;   // log2 range below the row's top score that the bins span
 constexpr int kYFixBits = 10;      // prefill importance: fixed point, 2^-10 log2 units per step
-// Prefill importance pass: query blocks per wave (8 chunk tokens each per
-// work-group).  Without an O accumulator four fit (two waves per SIMD), so
-// each K operand read from LDS serves 64 query columns; measured 4% faster
-// than two on the 4096-token chunk.
-constexpr int kImportanceQB = 4;
+constexpr int kImportanceTok = 64;  // prefill importance pass: chunk tokens per work-group
 constexpr int kMaxSplits = 1024;   // context splits per row (full layer, decode)
 constexpr int kSplitTarget = 256;  // decode full layer: work-groups over all rows (MI355X CUs)
 

@@ -31,6 +31,8 @@
 //    steps), and the largest |k| of each KV head, which bounds its float32
 //    error for the selection.
 
+#include <type_traits>
+
 #include "hs2_internal.h"
 
 namespace hs2 {
@@ -95,17 +97,6 @@ __device__ __forceinline__ void tile_lstore(const TileRegs& r, u16* kt, u16* vt)
 }
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-
-// Running maximum of |k| over a staged K tile, on the bf16 bits: clearing the
-// sign bit leaves magnitudes whose bit patterns order like their values.
-__device__ __forceinline__ u16x2 abs_max_bf16(const TileRegs& r, u16x2 acc) {
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      acc = __builtin_elementwise_max(acc, __builtin_bit_cast(u16x2, r.k[c][e] & 0x7FFF7FFFu));
-  return acc;
-}
 
 // K as the A operand of S^T for key subtile kt (16 keys) and dims 32c..32c+31.
 __device__ __forceinline__ bf16x8 lds_k_operand(const u16* kt, int sub, int c, int col, int grp) {
@@ -314,13 +305,19 @@ __global__ __launch_bounds__(kPThreads, QB <= 2 ? 2 : 1) void full_prefill_kerne
   }
 }
 
-// Importance pass.  grid: B * Hkv * ceil(T / (8 QB)) work-groups of 256
-// threads; a work-group takes 8 QB chunk tokens, each wave QB 16-row query
-// blocks (2 tokens x 8 heads each), so every K tile staged in LDS serves 8 QB
-// tokens.
+// Importance pass.  grid: B * Hkv * ceil(T / 64) work-groups of 8 waves; a
+// work-group takes 64 chunk tokens, each wave 4 query blocks (2 tokens x 8
+// heads each), so every K operand read from LDS serves 64 query rows.
 // Here the MFMA computes S = Q . K^T (query rows, key columns): a lane holds 4
 // heads of one token for one key, and the max over the token's 8 heads is 3
 // in-lane steps and one exchange with the partner lane.
+// The waves form two groups of four, one wave of each per SIMD, that take
+// turns: while one group runs a tile's MFMAs the other turns its previous
+// tile into importance values (VALU and stores), so the matrix cores stay
+// fed during the epilogue.  Group B runs one phase behind group A; a barrier
+// ends every phase.  K tiles (64 keys) are double-buffered in LDS; each wave
+// stages 8 rows of the next tile through registers, loading them in one
+// phase and writing them in the next.
 // Writes, for every row (b, t, g) it owns:
 //   y[row][j] = max_h(s2_h[j] - lse2_h) for older keys j < first_t, as
 //               round((y - ybase) 2^10) clamped to 0..65535, with ybase the
@@ -331,17 +328,48 @@ __global__ __launch_bounds__(kPThreads, QB <= 2 ? 2 : 1) void full_prefill_kerne
 //               head's keys 0..S-1 (bf16 bits; when kmax is non-null): whole
 //               key tile i belongs to token block i % n_tblk when that block
 //               reads all of it, else to the last block, which reads every key.
-template <int QB>
-__global__ __launch_bounds__(kPThreads, 2) void prefill_importance_kernel(
+constexpr int kIWaves = 8;
+constexpr int kIThreads = 64 * kIWaves;
+constexpr int kIQB = 4;                        // query blocks per wave
+static_assert(kIWaves * 2 * kIQB == kImportanceTok, "64 chunk tokens per work-group");
+
+// K tile in LDS as unpadded 256-byte rows, the 16-byte chunk c of row r at
+// slot c ^ (r & 15): the operand reads of 16 consecutive rows (one chunk each)
+// cover all banks once, and one LDS-direct load fills 4 whole rows.
+__device__ __forceinline__ bf16x8 lds_k_swizzled(const u16* kt, int sub, int c, int col, int grp) {
+  const int slot = (4 * c + grp) ^ col;
+  return as_bf16x8(*reinterpret_cast<const u32x4*>(kt + (16 * sub + col) * kD + 8 * slot));
+}
+
+__device__ __forceinline__ void wait_lgkm_all() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), other counters untouched
+}
+
+// A work-group barrier that waits for no memory operation: the importance
+// values' global stores stay in flight across it.  Whatever must be visible
+// past it is waited for explicitly (the tile's LDS writes), and the empty asm
+// statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void phase_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <bool kScores>
+__global__ __launch_bounds__(kIThreads, 1) void prefill_importance_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const double* __restrict__ lse2,
     const float* __restrict__ ytop_h, u16* __restrict__ y, uint32_t* __restrict__ kmax,
     float* __restrict__ scores, int64_t S, int64_t Spad, int T, int Hkv, int w, int n_tblk,
-    float c2_hi, float c2_lo, int64_t kvp) {
-  __shared__ __align__(16) u16 kt[kPKeys * kPPitch];
-  __shared__ uint32_t s_kmax[kPThreads / 64];
+    float c2_hi, int64_t kvp) {
+  __shared__ __align__(16) u16 kbuf[2][kPKeys * kD];
+  __shared__ uint32_t s_kmax[kIWaves];
+  constexpr int QB = kIQB;
+  constexpr int kTok = kImportanceTok;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  // waves w and w + 4 share a SIMD; the group is wave-uniform (read as such)
+  const bool group_b = __builtin_amdgcn_readfirstlane(wave) >= kIWaves / 2;
   const int col = lane & 15, grp = lane >> 4;
   const int lin = xcd_linear(blockIdx.x, gridDim.x);
   const int tb = lin % n_tblk;
@@ -350,10 +378,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_importance_kernel(
   const int Hq = Hkv * kG;
   const u16* kr = k + static_cast<size_t>(bg) * kvp * kD;
   const int64_t pos0 = S - T;
-  // block qbk of this wave: tokens 4*wave + 2*qbk + {0, 1}
-  constexpr int kTok = 8 * QB;   // chunk tokens per work-group
   bf16x8 qop[QB][4];
-  int jloc[QB];
   bool t_ok[QB];
   int64_t P[QB], first[QB];
   // y in fixed-point steps plus 0.5 is s c2 2^10 + (0.5 - 2^10 (lse2_h + ybase)):
@@ -370,8 +395,7 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_importance_kernel(
     load_q_block(q + (static_cast<size_t>(b) * T + tq) * Hq * kD + static_cast<size_t>(g) * kG * kD,
                  col, grp, qop[qbk]);
     // this lane's rows of S: 4*grp + i = (token .. + (grp >> 1), head 4*(grp & 1) + i)
-    jloc[qbk] = 2 * QB * wave + 2 * qbk + (grp >> 1);
-    int t = tb * kTok + jloc[qbk];
+    int t = tb * kTok + 2 * QB * wave + 2 * qbk + (grp >> 1);
     t_ok[qbk] = t < T;
     t = t_ok[qbk] ? t : T - 1;
     P[qbk] = pos0 + t;
@@ -405,32 +429,58 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_importance_kernel(
   };
   u16x2 kabs{0, 0};
 
-  TileRegs regs;
-  tile_gload<false>(regs, kr, nullptr, 0, p_last);
-  if (kmax && owns_tile(0)) kabs = abs_max_bf16(regs, kabs);
-  tile_lstore<false>(regs, kt, nullptr);
+  // this wave's 8 rows of a tile, staged through registers: lane l holds
+  // bytes 32 (l & 7) .. + 31 of row 8 wave + (l >> 3)
+  const int srow_ = 8 * wave + (lane >> 3);
+  const int sc0 = 2 * (lane & 7);
+  u32x4 stg[2];
+  auto stage_load = [&](int64_t key0) {
+    const int64_t key = min(key0 + srow_, p_last);
+    const u16* src = kr + key * kD + 8 * sc0;
+    stg[0] = load_u32x4(src);
+    stg[1] = load_u32x4(src + 8);
+  };
+  auto stage_store = [&](u16* kt, int tile) {
+    u16* dst = kt + srow_ * kD;
+    *reinterpret_cast<u32x4*>(dst + 8 * (sc0 ^ (srow_ & 15))) = stg[0];
+    *reinterpret_cast<u32x4*>(dst + 8 * ((sc0 + 1) ^ (srow_ & 15))) = stg[1];
+    if (kmax && tile < n_tiles && owns_tile(tile)) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          kabs = __builtin_elementwise_max(kabs, __builtin_bit_cast(u16x2, stg[u][e] & 0x7FFF7FFFu));
+    }
+  };
+
+  // prologue: tile 0 by every wave; group B loads its rows of tile 1 in the
+  // phase it spends behind group A
+  stage_load(0);
+  stage_store(kbuf[0], 0);
 #pragma unroll
   for (int qbk = 0; qbk < QB; ++qbk)
 #pragma unroll
     for (int c = 0; c < 4; ++c) require_loaded(qop[qbk][c]);
   __syncthreads();
-  for (int it = 0; it < n_tiles; ++it) {
-    const int64_t key0 = static_cast<int64_t>(it) * kPKeys;
-    const bool more = it + 1 < n_tiles;
-    if (more) tile_gload<false>(regs, kr, nullptr, key0 + kPKeys, p_last);
-    f32x4 sacc[QB][4];
+  // the tile loop, as a separate copy per group: each group's copy has only
+  // its own loads and stores in flight, so the compiler waits on exactly those
+  // a tile's MFMAs: S for this wave's 4 query blocks x 64 keys
+  auto mfma_phase = [&](const u16* kt, f32x4 (&sacc)[QB][4]) {
 #pragma unroll
     for (int sub = 0; sub < 4; ++sub) {
 #pragma unroll
       for (int qbk = 0; qbk < QB; ++qbk) sacc[qbk][sub] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const bf16x8 kb = lds_k_operand(kt, sub, c, col, grp);
+        const bf16x8 kb = lds_k_swizzled(kt, sub, c, col, grp);
 #pragma unroll
         for (int qbk = 0; qbk < QB; ++qbk)
           sacc[qbk][sub] = mfma_16x16x32(qop[qbk][c], kb, sacc[qbk][sub]);
       }
     }
+  };
+  // a tile's epilogue: importance values from S, and their stores
+  auto epilogue = [&](const f32x4 (&sacc)[QB][4], int64_t key0) {
 #pragma unroll
     for (int qbk = 0; qbk < QB; ++qbk) {
       // y per (token, key), in fixed-point steps plus 0.5: max over the 8
@@ -443,29 +493,72 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_importance_kernel(
         float m = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaf(sacc[qbk][sub][i], c2s, nl2r[qbk][i]));
-        yv[sub] = fmaxf(m, __shfl_xor(m, 16));
+        // the partner lane (lane ^ 16) holds the other 4 heads: one VALU
+        // row swap gives both lanes both halves
+        const auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m),
+                                                         false, false);
+        yv[sub] = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int sub = sub0 + u;
         const float yy = sub == 0 ? yv[0] : sub == 1 ? yv[1] : sub == 2 ? yv[2] : yv[3];
         const int64_t key = key0 + 16 * sub + col;
-        if (!t_ok[qbk] || key > P[qbk]) continue;
-        if (srow[qbk])
+        // clamp to 0..65535, then truncate: rounds to nearest
+        const u16 v = static_cast<u16>(static_cast<uint32_t>(__builtin_amdgcn_fmed3f(yy, 0.f, 65535.f)));
+        if constexpr (kScores) {
+          if (!t_ok[qbk] || key > P[qbk]) continue;
           srow[qbk][key] = __builtin_amdgcn_exp2f(fmaf(yy, 1.0f / (1 << kYFixBits), yb[qbk]));
-        if (key < first[qbk] && yrow[qbk]) {
-          // clamp to 0..65535, then truncate: rounds to nearest
-          const float z = __builtin_amdgcn_fmed3f(yy, 0.f, 65535.f);
-          yrow[qbk][key] = static_cast<u16>(static_cast<uint32_t>(z));
+          if (key < first[qbk] && yrow[qbk]) yrow[qbk][key] = v;
+        } else {
+          // every lane stores (a fixed count of stores per phase, so the
+          // tile loads can be waited for alone): keys at or past first_t
+          // land in the row's unread tail (key < Spad), and a block past
+          // the chunk's end repeats the last token, value for value
+          yrow[qbk][key] = v;
         }
       }
     }
-    __syncthreads();
-    if (more) {
-      if (kmax && owns_tile(it + 1)) kabs = abs_max_bf16(regs, kabs);
-      tile_lstore<false>(regs, kt, nullptr);
-      __syncthreads();
+  };
+  // The tile loops, one per group, each laid out so that a tile's staging
+  // loads and LDS writes fall in one loop iteration: the compiler then waits
+  // for the loads alone, not for the importance stores issued after them.
+  if (!group_b) {
+    // phases 2 it (MFMAs of tile it, loads of tile it + 1) and 2 it + 1
+    // (epilogue of tile it, LDS writes of tile it + 1)
+    for (int it = 0; it < n_tiles; ++it) {
+      const int64_t key0 = static_cast<int64_t>(it) * kPKeys;
+      f32x4 sacc[QB][4];
+      // past the last tile the rows repeat key p_last and the LDS writes land
+      // in a buffer nobody reads again: unconditional, so every load is
+      // waited for on every path
+      stage_load(key0 + kPKeys);
+      asm volatile("" ::: "memory");   // issue the loads before the phase's work
+      mfma_phase(kbuf[it & 1], sacc);
+      phase_barrier();
+      stage_store(kbuf[(it & 1) ^ 1], it + 1);
+      epilogue(sacc, key0);
+      wait_lgkm_all();
+      phase_barrier();
     }
+    phase_barrier();   // group B's last phase
+  } else {
+    // phases 2 it (epilogue of tile it - 1, loads of tile it + 1) and 2 it + 1
+    // (MFMAs of tile it, LDS writes of tile it + 1); the first of these phases
+    // has no epilogue and puts group B one phase behind group A
+    f32x4 sacc[QB][4];
+    for (int it = 0; it < n_tiles; ++it) {
+      const int64_t key0 = static_cast<int64_t>(it) * kPKeys;
+      stage_load(key0 + kPKeys);
+      if (it > 0) epilogue(sacc, key0 - kPKeys);
+      phase_barrier();
+      stage_store(kbuf[(it & 1) ^ 1], it + 1);
+      mfma_phase(kbuf[it & 1], sacc);
+      wait_lgkm_all();
+      phase_barrier();
+    }
+    epilogue(sacc, static_cast<int64_t>(n_tiles - 1) * kPKeys);
+    phase_barrier();
   }
   if (kmax) {
     uint32_t m = max(static_cast<uint32_t>(kabs[0]), static_cast<uint32_t>(kabs[1]));
@@ -474,17 +567,17 @@ __global__ __launch_bounds__(kPThreads, 2) void prefill_importance_kernel(
     if (lane == 0) s_kmax[wave] = m;
     __syncthreads();
     if (tid == 0) {
-      for (int wv = 1; wv < kPThreads / 64; ++wv) m = max(m, s_kmax[wv]);
+      for (int wv = 1; wv < kIWaves; ++wv) m = max(m, s_kmax[wv]);
       kmax[static_cast<size_t>(bg) * n_tblk + tb] = m;
     }
   }
   // scores past P_t are 0
-  if (scores) {
+  if (kScores) {
     for (int j = 0; j < kTok; ++j) {
       const int tt = tb * kTok + j;
       if (tt >= T) break;
       float* sr = scores + ((static_cast<size_t>(b) * T + tt) * Hkv + g) * S;
-      for (int64_t key = pos0 + tt + 1 + tid; key < S; key += kPThreads) sr[key] = 0.f;
+      for (int64_t key = pos0 + tt + 1 + tid; key < S; key += kIThreads) sr[key] = 0.f;
     }
   }
 }
@@ -512,16 +605,21 @@ hipError_t launch_prefill_importance(const Plan& p, const u16* q, const u16* k, 
   char* w = static_cast<char*>(ws);
   const double c2 = p.scale * 1.4426950408889634;
   const float c2_hi = static_cast<float>(c2);
-  const float c2_lo = static_cast<float>(c2 - static_cast<double>(c2_hi));
-  constexpr int QB = kImportanceQB;
-  const int n_tblk = (p.T + 8 * QB - 1) / (8 * QB);
+  const int n_tblk = (p.T + kImportanceTok - 1) / kImportanceTok;
   const int n_wg = p.B * p.Hkv * n_tblk;
-  hipLaunchKernelGGL(prefill_importance_kernel<QB>, dim3(n_wg), dim3(kPThreads), 0, st, q, k,
-                     reinterpret_cast<const double*>(w + p.off_lse2),
-                     reinterpret_cast<const float*>(w + p.off_ytop),
-                     for_select ? reinterpret_cast<u16*>(w + p.off_ybuf) : nullptr,
-                     for_select ? reinterpret_cast<uint32_t*>(w + p.off_kmax) : nullptr, scores,
-                     p.S, p.Spad, p.T, p.Hkv, p.w, n_tblk, c2_hi, c2_lo, p.kvp);
+  u16* y = for_select ? reinterpret_cast<u16*>(w + p.off_ybuf) : nullptr;
+  uint32_t* kmax = for_select ? reinterpret_cast<uint32_t*>(w + p.off_kmax) : nullptr;
+  if (!for_select && !scores) return hipSuccess;
+  if (scores)
+    hipLaunchKernelGGL(prefill_importance_kernel<true>, dim3(n_wg), dim3(kIThreads), 0, st, q, k,
+                       reinterpret_cast<const double*>(w + p.off_lse2),
+                       reinterpret_cast<const float*>(w + p.off_ytop), y, kmax, scores, p.S, p.Spad,
+                       p.T, p.Hkv, p.w, n_tblk, c2_hi, p.kvp);
+  else
+    hipLaunchKernelGGL(prefill_importance_kernel<false>, dim3(n_wg), dim3(kIThreads), 0, st, q, k,
+                       reinterpret_cast<const double*>(w + p.off_lse2),
+                       reinterpret_cast<const float*>(w + p.off_ytop), y, kmax, nullptr, p.S,
+                       p.Spad, p.T, p.Hkv, p.w, n_tblk, c2_hi, p.kvp);
   return hipGetLastError();
 }
 

@@ -2215,7 +2215,7 @@ hipError_t launch_prefill_select(const Plan& p, const u16* q, const u16* k, int3
   hipLaunchKernelGGL(prefill_select_kernel, dim3(p.R), dim3(kRowThreads), 0, st,
                      reinterpret_cast<const u16*>(w + p.off_ybuf),
                      reinterpret_cast<const uint32_t*>(w + p.off_kmax),
-                     (p.T + 8 * kImportanceQB - 1) / (8 * kImportanceQB),
+                     (p.T + kImportanceTok - 1) / kImportanceTok,
                      reinterpret_cast<const double*>(w + p.off_lse2), q, k,
                      reinterpret_cast<int32_t*>(w + p.off_band_idx),
                      reinterpret_cast<uint64_t*>(w + p.off_band_key), p.band_cap, idx, n_sel, p.S,
