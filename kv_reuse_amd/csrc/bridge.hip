@@ -11,11 +11,15 @@
 // along the reduction, so every MFMA operand is one 16-byte load per lane.
 //
 // Two kernels:
-//  * many tokens (a prefill chunk or a whole prompt): 128 tokens x 128
-//    features (one KV head's K or V) per work-group, 4 waves of 64 x 64, the
-//    reduction staged through LDS 64 deep with one barrier per stage; the
-//    work-groups of one token tile sit on one XCD so its L2 serves the tile's
-//    hidden rows to all 2 Hkv feature tiles;
+//  * many tokens (a prefill chunk or a whole prompt): 256 tokens x 256
+//    features (two heads' K or V) per work-group of 4 waves, each wave 128 x
+//    128 (its accumulators fill the accumulation registers, one wave per
+//    SIMD), so every operand read from LDS serves 8 MFMAs; the reduction is
+//    staged through LDS 32 deep, four stages in flight, by LDS-direct loads
+//    issued three stages ahead, and each stage's operands are read into
+//    registers while the previous stage's MFMAs run; the work-groups of one
+//    token tile sit on one XCD so its
+//    L2 serves the tile's hidden rows to all their feature tiles;
 //  * a few tokens (decode-time append, up to 64): the weights are the only
 //    real traffic, so each work-group takes 16 features x 16 tokens and its 16
 //    waves split the reduction, with operands loaded directly from global
@@ -26,11 +30,10 @@
 namespace hs2 {
 namespace {
 
-constexpr int kBM = 128;      // tokens per work-group (large kernel)
-constexpr int kBN = 128;      // features per work-group: one head's K or V
-constexpr int kBK = 64;       // reduction depth of one LDS stage
-constexpr int kBPitch = 72;   // u16 per LDS row: 36 dwords, so the 16-byte reads
-                              // of 8 or 16 consecutive rows cover every bank once
+constexpr int kBM = 256;      // tokens per work-group (large kernel)
+constexpr int kBN = 256;      // features per work-group: two heads' K or V
+constexpr int kBK = 32;       // reduction depth of one LDS stage (64-byte rows)
+constexpr int kBStages = 4;   // LDS stages in flight
 constexpr int kSmallWaves = 16;
 
 __device__ __forceinline__ int xcd_group(int id, int n) {
@@ -52,86 +55,123 @@ __device__ __forceinline__ void store4(const BridgeArgs& a, int f, int m, f32x4 
   *reinterpret_cast<uint2*>(dst) = pk;
 }
 
-// grid: 2 Hkv * ceil(M / 128) work-groups of 256 threads.
-__global__ __launch_bounds__(256, 2) void bridge_gemm_kernel(BridgeArgs a) {
-  __shared__ __align__(16) u16 wl[2][kBN * kBPitch];
-  __shared__ __align__(16) u16 hl[2][kBM * kBPitch];
+// LDS stage layout: 256 rows of 32 bf16 (64 bytes), the 16-byte chunk c of
+// row r at slot c ^ ((r >> 2) & 3): the operand reads of 16 consecutive rows
+// at one chunk then cover all banks once (four rows share a 256-byte bank
+// line, at different offsets; the swizzle separates rows 4 apart).
+__device__ __forceinline__ int bslot(int r, int c) { return c ^ ((r >> 2) & 3); }
+
+// grid: Hkv * ceil(M / 256) work-groups of 256 threads.
+__global__ __launch_bounds__(256, 1) void bridge_gemm_kernel(BridgeArgs a) {
+  __shared__ __align__(16) u16 wl[kBStages][kBN * kBK];
+  __shared__ __align__(16) u16 hl[kBStages][kBM * kBK];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
-  const int n_ft = 2 * a.Hkv;
+  const int n_ft = a.Hkv;                      // 2 Hkv D / 256
   const int lin = xcd_group(blockIdx.x, gridDim.x);
   const int ft = lin % n_ft;
   const int m0 = (lin / n_ft) * kBM;
   const int f0 = ft * kBN;
-  const int wm = wave & 1, wn = wave >> 1;  // the wave's 64 tokens and 64 features
+  const int wm = wave & 1, wn = wave >> 1;     // the wave's 128 tokens and 128 features
 
-  // staging: thread tid moves 16-byte chunk (tid & 7) of rows (tid >> 3) + 32 j
-  const int lr = tid >> 3, lc = tid & 7;
-  const u16* wsrc[4];
-  const u16* hsrc[4];
+  // One stage: 16 LDS-direct loads of 1 KB (16 rows each) per operand, 4 per
+  // wave and operand: lane l fills slot l & 3 of row 16 i + (l >> 2) with that
+  // row's chunk (l & 3) ^ swizzle.  Hidden rows past M repeat the last.  Each
+  // load is a scalar base (the work-group's first row at the stage's column)
+  // plus a fixed per-lane byte offset, its LDS address a scalar in m0.  Issued
+  // from inline assembly, so that the compiler, which cannot tell the stage
+  // buffers apart, does not wait for them before every LDS read; the waits
+  // are explicit (vector memory operations complete in order).
+  uint32_t w_off[4], h_off[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    wsrc[j] = a.w + static_cast<size_t>(f0 + lr + 32 * j) * a.dm + 8 * lc;
-    const int m = min(m0 + lr + 32 * j, a.M - 1);   // rows past the end repeat the last
-    hsrc[j] = a.hidden + static_cast<size_t>(m) * a.dm + 8 * lc;
+  for (int u = 0; u < 4; ++u) {
+    const int r = 64 * wave + 16 * u + (lane >> 2);
+    const int c = bslot(r, lane & 3);         // chunk for slot lane & 3 (an involution)
+    w_off[u] = static_cast<uint32_t>((static_cast<size_t>(r) * a.dm + 8 * c) * 2);
+    const int m = min(m0 + r, a.M - 1);
+    h_off[u] = static_cast<uint32_t>((static_cast<size_t>(m - m0) * a.dm + 8 * c) * 2);
   }
-  u32x4 wr[4], hr[4];
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      wr[j] = load_u32x4(wsrc[j] + kt * kBK);
-      hr[j] = load_u32x4(hsrc[j] + kt * kBK);
-    }
+  const u16* w_base = a.w + static_cast<size_t>(f0) * a.dm;
+  const u16* h_base = a.hidden + static_cast<size_t>(m0) * a.dm;
+  const uint32_t wl0 = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&wl[0][64 * wave * kBK])));
+  const uint32_t hl0 = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&hl[0][64 * wave * kBK])));
+  constexpr uint32_t kStageBytes = kBN * kBK * 2;
+  // load number i (0..7) of stage kt: rows 16 (i >> 1) .. of this wave's 64,
+  // of the weights (i even) or the hidden states (i odd)
+  auto dma_one = [&](int kt, int i) {
+    const uint32_t sb = (kt % kBStages) * kStageBytes + 16 * (i >> 1) * kBK * 2;
+    if (i & 1)
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :: "s"(hl0 + sb), "v"(h_off[i >> 1]), "s"(h_base + kt * kBK) : "memory", "m0");
+    else
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :: "s"(wl0 + sb), "v"(w_off[i >> 1]), "s"(w_base + kt * kBK) : "memory", "m0");
   };
-  auto lstore = [&](int buf) {
+  auto dma_stage = [&](int kt) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      *reinterpret_cast<u32x4*>(&wl[buf][(lr + 32 * j) * kBPitch + 8 * lc]) = wr[j];
-      *reinterpret_cast<u32x4*>(&hl[buf][(lr + 32 * j) * kBPitch + 8 * lc]) = hr[j];
+    for (int i = 0; i < 8; ++i) dma_one(kt, i);
+  };
+  // the wave's operands of one stage: 8 feature blocks and 8 token blocks
+  auto read_ops = [&](int kt, bf16x8 (&wa)[8], bf16x8 (&hb)[8]) {
+    const int buf = kt % kBStages;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rw = 128 * wn + 16 * i + col;
+      const int rh = 128 * wm + 16 * i + col;
+      wa[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(&wl[buf][rw * kBK + 8 * bslot(rw, grp)]));
+      hb[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(&hl[buf][rh * kBK + 8 * bslot(rh, grp)]));
     }
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[8][8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Stage kt + 3 is loaded at the start of stage kt (into the buffer of stage
+  // kt - 1, whose operands were read during stage kt - 2); stage kt + 1 must
+  // be in LDS by the end of stage kt - 1, since its operands are read while
+  // stage kt's MFMAs run (two register sets).
   const int nk = a.dm / kBK;
-  gload(0);
-  lstore(0);
+  dma_stage(0);
+  if (nk > 1) dma_stage(1);
+  if (nk > 2) dma_stage(2);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) gload(kt + 1);
+  bf16x8 wa[2][8], hb[2][8];
+  read_ops(0, wa[0], hb[0]);
+  for (int kt = 0; kt < nk; kt += 2) {
+    // two stages per trip (nk is even), so that the register sets are named
+    // statically
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 wa[4], hb[4];
+    for (int h = 0; h < 2; ++h) {
+      const int s = kt + h;
+      const bool more = s + 3 < nk;
+      if (more) dma_stage(s + 3);
+      read_ops(min(s + 1, nk - 1), wa[h ^ 1], hb[h ^ 1]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        wa[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(
-            &wl[buf][(64 * wn + 16 * i + col) * kBPitch + 32 * ks + 8 * grp]));
-        hb[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(
-            &hl[buf][(64 * wm + 16 * i + col) * kBPitch + 32 * ks + 8 * grp]));
-      }
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_16x16x32(wa[i], hb[j], acc[i][j]);
+        for (int j = 0; j < 8; ++j) acc[i][j] = mfma_16x16x32(wa[h][i], hb[h][j], acc[i][j]);
+      // stage s + 2 (read during stage s + 1): only stage s + 3's 8 loads,
+      // if issued, are newer
+      if (more) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
     }
-    // the other buffer was last read before the previous barrier
-    if (more) lstore(buf ^ 1);
-    __syncthreads();
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   // C[feature 4 grp + e][token col] of block (i, j)
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int m = m0 + 64 * wm + 16 * j + col;
+  for (int j = 0; j < 8; ++j) {
+    const int m = m0 + 128 * wm + 16 * j + col;
     if (m >= a.M) continue;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) store4(a, f0 + 64 * wn + 16 * i + 4 * grp, m, acc[i][j]);
+    for (int i = 0; i < 8; ++i) store4(a, f0 + 128 * wn + 16 * i + 4 * grp, m, acc[i][j]);
   }
 }
 
@@ -179,7 +219,7 @@ hipError_t launch_kv_bridge(const BridgeArgs& a, hipStream_t st) {
     dim3 grid(2 * a.Hkv * kD / 16, (a.M + 15) / 16);
     hipLaunchKernelGGL(bridge_small_kernel, grid, dim3(kSmallWaves * 64), 0, st, a);
   } else {
-    const int n_wg = 2 * a.Hkv * ((a.M + kBM - 1) / kBM);
+    const int n_wg = a.Hkv * ((a.M + kBM - 1) / kBM);
     hipLaunchKernelGGL(bridge_gemm_kernel, dim3(n_wg), dim3(256), 0, st, a);
   }
   return hipGetLastError();
