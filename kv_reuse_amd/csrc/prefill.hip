@@ -201,8 +201,11 @@ __global__ __launch_bounds__(kPThreads, QB <= 2 ? 2 : 1) void full_prefill_kerne
     const bool masked = key0 + kPKeys - 1 > p_first;
     // The running max is taken over the raw dot products (the scale is
     // positive, and the rounded scaling is monotonic), and each exponent is
-    // a * c2 - m formed by two fmas: the product a * c2_hi and the shift by
-    // the integer m are exact inside the first, so only small values round.
+    // a * c2_hi - m in one fma: the product and the shift by the integer m are
+    // exact inside it, so only the result rounds, and the scale's dropped low
+    // part (below 2^-24 of a * c2) moves a probability by under 2e-7 of
+    // itself, and lse2 by less: far inside the selection's tolerance (the
+    // importance pass and the float64 re-ranking share this lse2).
     float p[QB][4][4];
 #pragma unroll
     for (int qbk = 0; qbk < QB; ++qbk) {
@@ -218,8 +221,7 @@ __global__ __launch_bounds__(kPThreads, QB <= 2 ? 2 : 1) void full_prefill_kerne
           }
       } else {
         // key0 + off is visible to the column iff off <= P - key0; a hidden
-        // key gets a large finite negative product (not -inf, which the
-        // second fma would turn into NaN when c2_lo < 0), whose exponent
+        // key gets a large finite negative product, whose exponent
         // underflows to 0
         const int lim = static_cast<int>(min(static_cast<int64_t>(kPKeys), pcol[qbk] - key0));
 #pragma unroll
@@ -243,7 +245,7 @@ __global__ __launch_bounds__(kPThreads, QB <= 2 ? 2 : 1) void full_prefill_kerne
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float a = sv[sub][i];
-          p[qbk][sub][i] = __builtin_amdgcn_exp2f(fmaf(a, c2_lo, fmaf(a, c2_hi, -m_new)));
+          p[qbk][sub][i] = __builtin_amdgcn_exp2f(fmaf(a, c2_hi, -m_new));
           ps += p[qbk][sub][i];
         }
       l[qbk] = l[qbk] * static_cast<double>(alpha) + static_cast<double>(ps);
