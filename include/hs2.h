@@ -204,9 +204,10 @@ int hs2_cross_decoder_step_timed(const hs2_shape* shape, int32_t n_sparse_layers
  * n = 1 with pos0 = S - 1 is the decode-time append of the token that the
  * next hs2_cross_decoder_step (ctx_len = S, same kv_capacity) attends from.
  * No workspace.  Errors: null pointers, non-positive sizes, reserved != 0 or
- * pos0 + n > kv_capacity give HS2_ERR_INVALID_ARG; head_dim != 128 or a
- * d_model that is not a multiple of 64 give HS2_ERR_UNSUPPORTED.  k and v must
- * not overlap hidden or w_kv. */
+ * pos0 + n > kv_capacity give HS2_ERR_INVALID_ARG; head_dim != 128, a
+ * d_model that is not a multiple of 64 or above 2^20, more than 4096 KV heads
+ * or B * n >= 2^31 give HS2_ERR_UNSUPPORTED.  k and v must not overlap hidden
+ * or w_kv. */
 typedef struct hs2_bridge_shape {
   int64_t kv_capacity; /* token rows per KV head of k and v */
   int64_t pos0;        /* cache position of the first new token */

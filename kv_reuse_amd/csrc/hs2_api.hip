@@ -341,8 +341,9 @@ int hs2_kv_bridge(const hs2_bridge_shape* shape, const hs2_bf16* hidden, const h
     return HS2_ERR_INVALID_ARG;
   if (s.pos0 > s.kv_capacity - s.n_tokens) return HS2_ERR_INVALID_ARG;
   if (s.head_dim != kD || s.d_model % 64 != 0) return HS2_ERR_UNSUPPORTED;
+  // the many-token kernel addresses 256 rows of a tile with 32-bit byte offsets
   if (static_cast<int64_t>(s.batch) * s.n_tokens >= (int64_t{1} << 31) ||
-      s.kv_capacity >= (int64_t{1} << 40) || s.n_kv_heads > 4096)
+      s.kv_capacity >= (int64_t{1} << 40) || s.n_kv_heads > 4096 || s.d_model > (1 << 20))
     return HS2_ERR_UNSUPPORTED;
   BridgeArgs a{};
   a.hidden = hidden;

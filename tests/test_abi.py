@@ -161,6 +161,7 @@ def test_bridge_shape_struct_layout():
     ("reserved", 1, hs2.HS2_ERR_INVALID_ARG),
     ("d_model", 0, hs2.HS2_ERR_INVALID_ARG),
     ("d_model", 100, hs2.HS2_ERR_UNSUPPORTED),         # not a multiple of 64
+    ("d_model", (1 << 20) + 64, hs2.HS2_ERR_UNSUPPORTED),  # beyond the supported hidden size
     ("head_dim", 64, hs2.HS2_ERR_UNSUPPORTED),
 ])
 def test_bridge_bad_shapes_rejected(field, value, code):
