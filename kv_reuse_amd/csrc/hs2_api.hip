@@ -144,7 +144,7 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
   q.band_cap = decode ? 0 : std::min<int64_t>(q.Spad, kPrefillBandCap);
   q.off_band_idx = take(Rz * q.band_cap * sizeof(int32_t));
   q.off_band_key = take(Rz * q.band_cap * sizeof(uint64_t));
-  // the float16 importance of a prefill chunk shares the key buffer of the
+  // the fixed-point importance of a prefill chunk shares the key buffer of the
   // selection from given scores: no call uses both
   q.off_ybuf = q.off_ukey;
   // per (batch, KV head, importance token block): that block's share of max |k|

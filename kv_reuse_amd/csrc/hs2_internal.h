@@ -14,7 +14,6 @@ constexpr int kG = 8;            // query heads per KV head (v1)
 constexpr int kNB = 2048;        // selection histogram bins (top 11 bits of a 32-bit key)
 constexpr int kBinShift = 21;    // 32 - 11
 constexpr int kPNB = 512;        // prefill-chunk histogram bins (1/8 octave; top 9 bits)
-constexpr int kPBinShift = 23;   // 32 - 9
 constexpr int kUncCap = 2048;    // near-threshold keys handled in LDS; more take the slow path
 constexpr int kMaxSel = 4096;    // top_k + window limit (index list kept in LDS)
 constexpr int kSparseChunk = 128;  // selected keys per sparse work-group (4 waves x 32)
@@ -65,7 +64,7 @@ struct Plan {
   size_t off_clist, off_ccnt, off_lo;
   int sc_chunk, sc_nchunk;   // scoring: list entries per work-group region, work-groups per row
   size_t off_hist_c, off_cand_y, off_cand_idx, off_cand_cnt, off_band_idx, off_band_key;
-  // prefill chunk: per-row log2 importance of the older keys (float16), band capacity per row
+  // prefill chunk: per-row log2 importance of the older keys (16-bit fixed point), band capacity per row
   size_t off_ybuf;
   size_t off_kmax;           // prefill: largest |k| (bf16 bits) per (batch, KV head)
   int64_t band_cap;

@@ -1846,7 +1846,7 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
         }
         }
       } else if (take > 0) {
-        // the band is too large to list: rank it by its float16 importance
+        // the band is too large to list: rank it by its stored importance
         // (unordered winners, then sorted)
         struct ScanSrc {
           const u16* yr;
