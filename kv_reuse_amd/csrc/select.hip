@@ -1580,16 +1580,31 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
     // listed, so that its floor already applies to them.
     uint32_t n_list = 0;
     {
-      u32x4 ycur[2], ynxt[2];
-      if (rounds > 0) load_round(0, ycur);
-      for (int64_t rr = 0; rr < rounds; ++rr) {
-        const int64_t i0 = 16 * (static_cast<int64_t>(tid) + rr * kRowThreads);
-        if (rr + 1 < rounds) load_round(rr + 1, ynxt);
-        const int nv = static_cast<int>(min(static_cast<int64_t>(16), first - i0));
+      // 32 values per thread and round here (four 16-byte loads), so half as
+      // many rounds, and barriers, as the second pass below
+      constexpr int kV = 32;
+      const int64_t prounds = (first + kV * kRowThreads - 1) / (kV * kRowThreads);
+      auto load_pround = [&](int64_t rr, u32x4 (&yv)[4]) {
+        const int64_t i0 = kV * (static_cast<int64_t>(tid) + rr * kRowThreads);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          yv[u] = i0 + 8 * u < first ? *reinterpret_cast<const u32x4*>(yr + i0 + 8 * u)
+                                     : u32x4{0u, 0u, 0u, 0u};
+      };
+      auto val_at = [](const u32x4 (&yv)[4], int e) -> uint32_t {
+        const uint32_t word = yv[e >> 3][(e >> 1) & 3];
+        return (e & 1) ? (word >> 16) : (word & 0xFFFFu);
+      };
+      u32x4 ycur[4], ynxt[4];
+      if (prounds > 0) load_pround(0, ycur);
+      for (int64_t rr = 0; rr < prounds; ++rr) {
+        const int64_t i0 = kV * (static_cast<int64_t>(tid) + rr * kRowThreads);
+        if (rr + 1 < prounds) load_pround(rr + 1, ynxt);
+        const int nv = static_cast<int>(min(static_cast<int64_t>(kV), first - i0));
         int fl = *static_cast<volatile int*>(&s_floor);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int bn = static_cast<int>(u16_at(ycur, e) >> kVBinShift);
+        for (int e = 0; e < kV; ++e) {
+          const int bn = static_cast<int>(val_at(ycur, e) >> kVBinShift);
           if (e < nv && bn >= fl) atomicAdd(&lh[bn], 1u);
         }
         if (rr == 0) {
@@ -1604,8 +1619,8 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
         const int vmin = (fl << kVBinShift) - E;
         uint32_t ml = 0;
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-          ml |= static_cast<uint32_t>(e < nv && static_cast<int>(u16_at(ycur, e)) >= vmin) << e;
+        for (int e = 0; e < kV; ++e)
+          ml |= static_cast<uint32_t>(e < nv && static_cast<int>(val_at(ycur, e)) >= vmin) << e;
         uint32_t ol, o_dummy, tot, t_dummy;
         block_offsets2<kRowThreads / 64>(__popc(ml), 0u, s_off[rr & 1], ol, o_dummy, tot, t_dummy);
         // the round's atomics are complete: raise the floor
@@ -1617,17 +1632,17 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
         n_list += tot;
         if (ml) {
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
+          for (int e = 0; e < kV; ++e) {
             if (!((ml >> e) & 1u)) continue;
             if (ol < static_cast<uint32_t>(kPList)) {
               lidx[ol] = static_cast<int32_t>(i0 + e);
-              lval[ol] = static_cast<uint16_t>(u16_at(ycur, e));
+              lval[ol] = static_cast<uint16_t>(val_at(ycur, e));
             }
             ++ol;
           }
         }
 #pragma unroll
-        for (int u = 0; u < 2; ++u) ycur[u] = ynxt[u];
+        for (int u = 0; u < 4; ++u) ycur[u] = ynxt[u];
       }
     }
     const bool listed = n_list <= static_cast<uint32_t>(kPList);
