@@ -232,8 +232,15 @@ __global__ __launch_bounds__(kPThreads, QB <= 2 ? 2 : 1) void full_prefill_kerne
             amax = fmaxf(amax, sv[sub][i]);
           }
       }
-      amax = fmaxf(amax, __shfl_xor(amax, 16));
-      amax = fmaxf(amax, __shfl_xor(amax, 32));
+      // the column's other keys sit in lanes ^ 16 and ^ 32: VALU row swaps
+      {
+        const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(amax),
+                                                          __float_as_uint(amax), false, false);
+        amax = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+        const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(amax),
+                                                          __float_as_uint(amax), false, false);
+        amax = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+      }
       // key 0 is visible to every token, so the running max is finite from the
       // first tile on
       const float tmax = fmaf(amax, c2_hi, amax * c2_lo);
