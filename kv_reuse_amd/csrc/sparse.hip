@@ -7,7 +7,7 @@
 //  * One work-group serves one row (batch, query token, KV head) and a slice of
 //    its index list.  The slice's indices go to LDS; the work-group gathers the
 //    selected K and V rows (256 contiguous bytes each) into LDS once, in
-//    sub-chunks of 128 keys, and every layer of the launch reads them there:
+//    sub-chunks of 32 or 128 keys, and every layer of the launch reads them there:
 //    the N layers cost one gather, not N.
 //  * Wave c handles column tile c = two layers x 8 query heads (16 MFMA
 //    columns): S^T = K_sel . Q^T and O^T = V_sel^T . P^T on MFMA 16x16x32 bf16,
@@ -23,10 +23,16 @@
 namespace hs2 {
 namespace {
 
-constexpr int kSub = 128;     // keys gathered into LDS at a time
+// Keys gathered into LDS at a time (SUB).  With one work-group per row (a
+// prefill chunk) 32 keeps a work-group's LDS at 17 KB, so many work-groups per
+// CU hide each other's gather latency (measured on the 4096-token chunk: 128
+// keys 1.71 ms, 64 keys 1.26 ms, 32 keys 1.12 ms); a decode slice is one
+// 128-key sub-chunk (at 1M context 9.1 us against 11.5 us for 4 x 32).
+constexpr int kSubRows = 32;
+constexpr int kSubSlice = kSparseChunk;
 constexpr int kPitch = 136;   // u16 per LDS row (272 bytes)
 
-template <int NCT>
+template <int NCT, int kSub>
 __global__ __launch_bounds__(NCT * 64) void sparse_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ n_sel, u16* __restrict__ out,
@@ -347,7 +353,8 @@ hipError_t launch_sparse(const Plan& p, const u16* q, const u16* k, const u16* v
   const float c2_hi = static_cast<float>(c2);
   const float c2_lo = static_cast<float>(c2 - static_cast<double>(c2_hi));
   const size_t layer_stride = static_cast<size_t>(p.B) * p.T * p.Hq * kD;
-  const int keys_per_wg = p.sp_nch == 1 ? ((p.cap + kSub - 1) / kSub) * kSub : kSub;
+  // sliced (few rows): kSparseChunk keys per work-group, as the plan's slice count assumes
+  const int keys_per_wg = p.sp_nch == 1 ? ((p.cap + kSubRows - 1) / kSubRows) * kSubRows : kSparseChunk;
   float* pm = reinterpret_cast<float*>(w + p.off_sp_m);
   float* pl = reinterpret_cast<float*>(w + p.off_sp_l);
   float* po = reinterpret_cast<float*>(w + p.off_sp_o);
@@ -369,11 +376,20 @@ hipError_t launch_sparse(const Plan& p, const u16* q, const u16* k, const u16* v
                          p.S, p.T, p.Hkv, p.n_layers, layer0, p.cap, p.sp_nch, keys_per_wg, c2_hi,
                          c2_lo, layer_stride, p.kvp, swa ? p.w : -1, swa_out);
     };
-    switch (nct) {
-      case 1: go(sparse_kernel<1>); break;
-      case 2: go(sparse_kernel<2>); break;
-      case 3: go(sparse_kernel<3>); break;
-      default: go(sparse_kernel<4>); break;
+    if (p.sp_nch == 1) {
+      switch (nct) {
+        case 1: go(sparse_kernel<1, kSubRows>); break;
+        case 2: go(sparse_kernel<2, kSubRows>); break;
+        case 3: go(sparse_kernel<3, kSubRows>); break;
+        default: go(sparse_kernel<4, kSubRows>); break;
+      }
+    } else {
+      switch (nct) {
+        case 1: go(sparse_kernel<1, kSubSlice>); break;
+        case 2: go(sparse_kernel<2, kSubSlice>); break;
+        case 3: go(sparse_kernel<3, kSubSlice>); break;
+        default: go(sparse_kernel<4, kSubSlice>); break;
+      }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
