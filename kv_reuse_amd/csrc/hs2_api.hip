@@ -108,7 +108,7 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
     q.sc_chunk = static_cast<int>(ceil_div(nst, ns));   // list entries a region holds
   }
   // sparse: slices of 128 keys over work-groups when rows are few
-  q.sp_nch = (R >= 256) ? 1 : static_cast<int>(ceil_div(q.cap, 128));
+  q.sp_nch = (R >= 256) ? 1 : static_cast<int>(ceil_div(q.cap, kSparseChunk));
 
   size_t off = 0;
   auto take = [&](size_t bytes) {

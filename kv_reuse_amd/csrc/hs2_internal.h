@@ -16,7 +16,7 @@ constexpr int kBinShift = 21;    // 32 - 11
 constexpr int kPNB = 512;        // prefill-chunk histogram bins (1/8 octave; top 9 bits)
 constexpr int kUncCap = 2048;    // near-threshold keys handled in LDS; more take the slow path
 constexpr int kMaxSel = 4096;    // top_k + window limit (index list kept in LDS)
-constexpr int kSparseChunk = 128;  // selected keys per sparse work-group (4 waves x 32)
+constexpr int kSparseChunk = 128;  // selected keys per sparse work-group (a decode slice)
 constexpr float kYRange = 64.0f;   // log2 range below the row's top score that the bins span
 constexpr int kYFixBits = 10;      // prefill importance: fixed point, 2^-10 log2 units per step
 constexpr int kImportanceTok = 64;  // prefill importance pass: chunk tokens per work-group
