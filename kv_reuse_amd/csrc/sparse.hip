@@ -7,7 +7,7 @@
 //  * One work-group serves one row (batch, query token, KV head) and a slice of
 //    its index list.  The slice's indices go to LDS; the work-group gathers the
 //    selected K and V rows (256 contiguous bytes each) into LDS once, in
-//    sub-chunks of 32 or 128 keys, and every layer of the launch reads them there:
+//    sub-chunks of 32, 64 or 128 keys, and every layer of the launch reads them there:
 //    the N layers cost one gather, not N.
 //  * Wave c handles column tile c = two layers x 8 query heads (16 MFMA
 //    columns): S^T = K_sel . Q^T and O^T = V_sel^T . P^T on MFMA 16x16x32 bf16,
@@ -30,6 +30,11 @@ namespace {
 // 128-key sub-chunk (at 1M context 9.1 us against 11.5 us for 4 x 32).
 constexpr int kSubRows = 32;
 constexpr int kSubSlice = kSparseChunk;
+// slices beyond two 70 KB work-groups per CU (256 CUs) gather 64 keys at a time
+// instead, so all of them are resident at once (32K context x 64 rows: 19.5
+// against 15.3 us; with fewer slices the single 128-key sub-chunk is faster)
+constexpr int kSubSliceHalf = kSparseChunk / 2;
+constexpr int64_t kSliceWgOneRound = 512;
 constexpr int kPitch = 136;   // u16 per LDS row (272 bytes)
 
 template <int NCT, int kSub>
@@ -382,6 +387,13 @@ hipError_t launch_sparse(const Plan& p, const u16* q, const u16* k, const u16* v
         case 2: go(sparse_kernel<2, kSubRows>); break;
         case 3: go(sparse_kernel<3, kSubRows>); break;
         default: go(sparse_kernel<4, kSubRows>); break;
+      }
+    } else if (static_cast<int64_t>(p.R) * p.sp_nch > kSliceWgOneRound) {
+      switch (nct) {
+        case 1: go(sparse_kernel<1, kSubSliceHalf>); break;
+        case 2: go(sparse_kernel<2, kSubSliceHalf>); break;
+        case 3: go(sparse_kernel<3, kSubSliceHalf>); break;
+        default: go(sparse_kernel<4, kSubSliceHalf>); break;
       }
     } else {
       switch (nct) {
