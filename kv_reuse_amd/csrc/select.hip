@@ -768,6 +768,7 @@ __global__ __launch_bounds__(kThreads, 3) void subtile_score_kernel(
   __shared__ uint32_t pre[kMaxChunks + 1];
   __shared__ int32_t s_list[kScoreRound];
   __shared__ double stage_y[kStageSub * kSubKeys];
+  __shared__ u32x4 q_lds[2 * kG * kD / 8];   // 16 heads (8 real) x 128 dims, bf16
   __shared__ float s_ybase;
   __shared__ uint32_t s_cnt[2][16];
   __shared__ uint32_t s_base[4];
@@ -791,14 +792,13 @@ __global__ __launch_bounds__(kThreads, 3) void subtile_score_kernel(
     cl[u] = c < cc_nchunk ? ccnt[static_cast<size_t>(r) * cc_nchunk + c] : 0u;
     mysum += cl[u];
   }
-  // the B operand, packed bf16: head col (zero for the padding heads),
-  // dims 32*grp + 8c .. +8, widened exactly at each MFMA step
-  u32x4 qraw[4];
-  {
-    const u16* qr = q + static_cast<size_t>(r) * kG * kD + (col & 7) * kD + 32 * grp;
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-      qraw[c] = col < kG ? load_u32x4(qr + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+  // the B operand in LDS, packed bf16: head col (zero for the padding heads),
+  // dims 32*grp + 8c .. +8 (kept out of registers to leave room for a deeper
+  // prefetch of the candidates' K rows)
+  for (int i = tid; i < 2 * kG * kD / 8; i += kThreads) {
+    const int h = i / (kD / 8), d8 = i % (kD / 8);
+    q_lds[i] = h < kG ? load_u32x4(q + (static_cast<size_t>(r) * kG + h) * kD + 8 * d8)
+                      : u32x4{0u, 0u, 0u, 0u};
   }
   // float32 scale and lse2 of head col for the filter; for the exact pass lane
   // (h, j) keeps head h's query dims 16 j .. +16 widened to float64 and its lse2
@@ -860,19 +860,27 @@ __global__ __launch_bounds__(kThreads, 3) void subtile_score_kernel(
 #pragma unroll
         for (int c = 0; c < 4; ++c) ka[c] = load_u32x4(kr + key * kD + 32 * grp + 8 * c);
       };
-      u32x4 ka_cur[4], ka_nxt[4];
+      // two subtiles ahead per wave
+      constexpr uint32_t kW = kThreads / 64;
+      u32x4 ka_cur[4], ka_nxt[4], ka_nx2[4];
       if (static_cast<uint32_t>(wave) < np) load_sub(wave, ka_cur);
-      for (uint32_t i = wave; i < np; i += kThreads / 64) {
-        if (i + kThreads / 64 < np) load_sub(i + kThreads / 64, ka_nxt);
+      if (wave + kW < np) load_sub(wave + kW, ka_nxt);
+      for (uint32_t i = wave; i < np; i += kW) {
+        if (i + 2 * kW < np) load_sub(i + 2 * kW, ka_nx2);
         const int64_t key0 = static_cast<int64_t>(s_list[p0 + i]) * kSubKeys;
         // ---- float32 importance of the 16 keys on the bf16 MFMA (S = K . Q^T,
         // 16 keys x 16 heads of which 8 are used): lane (col, grp) gets keys
         // 4 grp + e against head col
         f32x4 sf = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) sf = mfma_16x16x32(as_bf16x8(ka_cur[c]), as_bf16x8(qraw[c]), sf);
+        for (int c = 0; c < 4; ++c)
+          sf = mfma_16x16x32(as_bf16x8(ka_cur[c]),
+                             as_bf16x8(q_lds[(col * kD + 32 * grp + 8 * c) / 8]), sf);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) ka_cur[c] = ka_nxt[c];
+        for (int c = 0; c < 4; ++c) {
+          ka_cur[c] = ka_nxt[c];
+          ka_nxt[c] = ka_nx2[c];
+        }
         uint32_t nib = 0;   // keys 4 grp + e that may reach the lower bin
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
