@@ -59,6 +59,101 @@ __device__ __forceinline__ int cand_bin(double y, float ybase) {
 
 // ---------------------------------------------------------------- helpers
 
+// Wave-wide scans and reductions on the VALU's cross-lane paths: DPP moves
+// inside each row of 16 lanes, row broadcasts (GFX9 DPP) or the gfx950 row
+// swaps across rows.  An LDS permute (ds_bpermute) costs a round trip through
+// the LDS pipeline per step; these do not, which matters in the one-work-group
+// per row kernels whose time is a chain of such steps.
+template <int kCtrl, int kRowMask = 0xF>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
+  // lanes whose source is outside the row, or whose row is masked off, read 0
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), kCtrl, kRowMask, 0xF, true));
+}
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += dpp_mov<0x111>(x);        // row_shr:1
+  x += dpp_mov<0x112>(x);        // row_shr:2
+  x += dpp_mov<0x114>(x);        // row_shr:4
+  x += dpp_mov<0x118>(x);        // row_shr:8: each row now holds its own prefix sums
+  x += dpp_mov<0x142, 0xA>(x);   // row_bcast:15 into rows 1 and 3
+  x += dpp_mov<0x143, 0xC>(x);   // row_bcast:31 into rows 2 and 3
+  return x;
+}
+// v combined over all 64 lanes, in every lane (op associative and commutative).
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_allreduce(uint32_t v, Op op) {
+  v = op(v, dpp_mov<0xB1>(v));    // quad_perm [1,0,3,2]: lane ^ 1
+  v = op(v, dpp_mov<0x4E>(v));    // quad_perm [2,3,0,1]: lane ^ 2
+  v = op(v, dpp_mov<0x141>(v));   // row_half_mirror: the other quad of the 8
+  v = op(v, dpp_mov<0x140>(v));   // row_mirror: the other half of the row
+  const auto r16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = op(r16[0], r16[1]);         // rows 0|1 and 2|3
+  const auto r32 = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return op(r32[0], r32[1]);      // rows 0-1 | 2-3
+}
+__device__ __forceinline__ uint32_t wave_and(uint32_t v) {
+  return wave_allreduce(v, [](uint32_t a, uint32_t b) { return a & b; });
+}
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+  return wave_allreduce(v, [](uint32_t a, uint32_t b) { return a | b; });
+}
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+  return wave_allreduce(v, [](uint32_t a, uint32_t b) { return max(a, b); });
+}
+// Lane `src`'s value (src the same in every lane).
+__device__ __forceinline__ uint32_t lane_value(uint32_t v, int src) {
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), src));
+}
+__device__ __forceinline__ uint64_t lane_value64(uint64_t v, int src) {
+  return (static_cast<uint64_t>(lane_value(static_cast<uint32_t>(v >> 32), src)) << 32) |
+         lane_value(static_cast<uint32_t>(v), src);
+}
+template <int kCtrl>
+__device__ __forceinline__ double dpp_mov_f64(double v) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  const uint64_t lo = dpp_mov<kCtrl>(static_cast<uint32_t>(u));
+  const uint64_t hi = dpp_mov<kCtrl>(static_cast<uint32_t>(u >> 32));
+  return __longlong_as_double(static_cast<long long>((hi << 32) | lo));
+}
+// The other rows' values through the gfx950 row swaps: the largest of a double
+// over lanes l, l ^ 16, l ^ 32, l ^ 48 (in every lane).
+__device__ __forceinline__ double max_over_rows_f64(double v) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  const auto l16 = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(u), static_cast<uint32_t>(u), false, false);
+  const auto h16 = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(u >> 32), static_cast<uint32_t>(u >> 32), false, false);
+  auto join = [](uint32_t hi, uint32_t lo) {
+    return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+  };
+  v = fmax(join(h16[0], l16[0]), join(h16[1], l16[1]));
+  const uint64_t w = static_cast<uint64_t>(__double_as_longlong(v));
+  const auto l32 = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(w), static_cast<uint32_t>(w), false, false);
+  const auto h32 = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(w >> 32), static_cast<uint32_t>(w >> 32), false, false);
+  return fmax(join(h32[0], l32[0]), join(h32[1], l32[1]));
+}
+// Sum over each group of 8 lanes (lane ^ 1, ^ 2, ^ 4 butterfly order), in
+// every lane of the group.
+__device__ __forceinline__ double oct_sum(double v) {
+  v += dpp_mov_f64<0xB1>(v);
+  v += dpp_mov_f64<0x4E>(v);
+  v += dpp_mov_f64<0x141>(v);
+  return v;
+}
+__device__ __forceinline__ float oct_max_f32(float v) {
+  v = fmaxf(v, __uint_as_float(dpp_mov<0xB1>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_mov<0x4E>(__float_as_uint(v))));
+  return fmaxf(v, __uint_as_float(dpp_mov<0x141>(__float_as_uint(v))));
+}
+// Sum over each row of 16 lanes, in every lane of the row: the pairing tree of
+// a lane ^ 1, ^ 2, ^ 4, ^ 8 butterfly, so every lane holds the same value.
+__device__ __forceinline__ double row16_sum(double v) {
+  v += dpp_mov_f64<0xB1>(v);    // lane ^ 1
+  v += dpp_mov_f64<0x4E>(v);    // lane ^ 2
+  v += dpp_mov_f64<0x141>(v);   // the other quad of the 8
+  v += dpp_mov_f64<0x140>(v);   // the other half of the row
+  return v;
+}
+
 // Run by the 64 lanes of one wave over an LDS histogram of kNB bins: the bin
 // where the count from the top first reaches k, the count strictly above it
 // and the count in it; found = false if the histogram holds fewer than k.
@@ -76,31 +171,21 @@ __device__ KthBin kth_bin_wave_n(const uint32_t* lh, uint32_t k) {
   // level 1: lane l sums the kPer bins NB-1-kPer*l .. NB-kPer-kPer*l
   uint32_t lane_sum = 0;
   for (int i = 0; i < kPer; ++i) lane_sum += lh[NB - 1 - kPer * lane - i];
-  uint32_t incl = lane_sum;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t o = __shfl_up(incl, off);
-    if (lane >= off) incl += o;
-  }
-  KthBin res{0, __shfl(incl, 63), 0u, false};
+  const uint32_t incl = wave_incl_scan(lane_sum);
+  KthBin res{0, lane_value(incl, 63), 0u, false};
   const uint64_t hit = __ballot(incl >= k);
   if (!hit) return res;
   const int owner = __builtin_ctzll(hit);
-  const uint32_t above0 = __shfl(incl - lane_sum, owner);
+  const uint32_t above0 = lane_value(incl - lane_sum, owner);
   // level 2: lanes 0..kPer-1 take the owner's bins from the top
   const int bin = NB - 1 - kPer * owner - (lane % kPer);
   const uint32_t c = lane < kPer ? lh[bin] : 0u;
-  uint32_t inc2 = c;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t o = __shfl_up(inc2, off);
-    if (lane >= off) inc2 += o;
-  }
+  const uint32_t inc2 = wave_incl_scan(c);
   const uint64_t hit2 = __ballot(lane < kPer && above0 + inc2 >= k);
   const int jj = __builtin_ctzll(hit2);   // the owner's group reaches k, so some lane hits
   res.bstar = NB - 1 - kPer * owner - jj;
-  res.above = above0 + __shfl(inc2 - c, jj);
-  res.at = __shfl(c, jj);
+  res.above = above0 + lane_value(inc2 - c, jj);
+  res.at = lane_value(c, jj);
   res.found = true;
   return res;
 }
@@ -131,33 +216,27 @@ __device__ void reserve_two(uint32_t n0, uint32_t n1, uint32_t* ctr0, uint32_t* 
                             uint32_t& o1) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nwaves = blockDim.x >> 6;
-  uint32_t i0 = n0, i1 = n1;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t a = __shfl_up(i0, off), b = __shfl_up(i1, off);
-    if (lane >= off) {
-      i0 += a;
-      i1 += b;
-    }
-  }
+  const uint32_t i0 = wave_incl_scan(n0), i1 = wave_incl_scan(n1);
   if (lane == 63) {
     s_cnt[0][wave] = i0;
     s_cnt[1][wave] = i1;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t t0 = 0, t1 = 0;
-    for (int wv = 0; wv < nwaves; ++wv) {
-      const uint32_t a = s_cnt[0][wv], b = s_cnt[1][wv];
-      s_cnt[0][wv] = t0;
-      s_cnt[1][wv] = t1;
-      t0 += a;
-      t1 += b;
+  if (wave == 0) {
+    // the waves' totals (at most 16) scanned by lanes 0 .. nwaves-1
+    const uint32_t c0 = lane < nwaves ? s_cnt[0][lane] : 0u;
+    const uint32_t c1 = lane < nwaves ? s_cnt[1][lane] : 0u;
+    const uint32_t x0 = wave_incl_scan(c0), x1 = wave_incl_scan(c1);
+    if (lane < nwaves) {
+      s_cnt[0][lane] = x0 - c0;
+      s_cnt[1][lane] = x1 - c1;
     }
-    s_base[0] = (t0 && ctr0) ? atomicAdd(ctr0, t0) : 0u;
-    s_base[1] = (t1 && ctr1) ? atomicAdd(ctr1, t1) : 0u;
-    s_base[2] = t0;
-    s_base[3] = t1;
+    if (lane == nwaves - 1) {
+      s_base[0] = (x0 && ctr0) ? atomicAdd(ctr0, x0) : 0u;
+      s_base[1] = (x1 && ctr1) ? atomicAdd(ctr1, x1) : 0u;
+      s_base[2] = x0;
+      s_base[3] = x1;
+    }
   }
   __syncthreads();
   o0 = s_base[0] + s_cnt[0][wave] + i0 - n0;
@@ -174,15 +253,7 @@ __device__ __forceinline__ void block_offsets2(uint32_t n0, uint32_t n1, uint32_
                                                uint32_t& o0, uint32_t& o1, uint32_t& t0,
                                                uint32_t& t1) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t i0 = n0, i1 = n1;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t a = __shfl_up(i0, off), b = __shfl_up(i1, off);
-    if (lane >= off) {
-      i0 += a;
-      i1 += b;
-    }
-  }
+  const uint32_t i0 = wave_incl_scan(n0), i1 = wave_incl_scan(n1);
   if (lane == 63) {
     buf[0][wave] = i0;
     buf[1][wave] = i1;
@@ -885,17 +956,13 @@ __global__ __launch_bounds__(kThreads, 3) void subtile_score_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float v = col < kG ? fmaf(sf[e], c2f, -l2f) : -INFINITY;
-          v = fmaxf(v, __shfl_xor(v, 1));
-          v = fmaxf(v, __shfl_xor(v, 2));
-          v = fmaxf(v, __shfl_xor(v, 4));
+          v = oct_max_f32(v);   // heads 0..7 of the row
           // float error is far below a bin: a key one bin short can still make it
           nib |= static_cast<uint32_t>(key0 + 4 * grp + e < first &&
                                        cand_bin(static_cast<double>(v), ybase) >= lo_bin - 1) << e;
         }
-        const uint32_t promising = static_cast<uint32_t>(__shfl(nib, 0)) |
-                                   (static_cast<uint32_t>(__shfl(nib, 16)) << 4) |
-                                   (static_cast<uint32_t>(__shfl(nib, 32)) << 8) |
-                                   (static_cast<uint32_t>(__shfl(nib, 48)) << 12);
+        const uint32_t promising = lane_value(nib, 0) | (lane_value(nib, 16) << 4) |
+                                   (lane_value(nib, 32) << 8) | (lane_value(nib, 48) << 12);
         // ---- exact float64 importance of the promising keys only, two at a
         // time: lane (h, j) = (lane >> 3, lane & 7) takes head h, dims 16 j .. +16
         if (lane < kSubKeys) stage_y[i * kSubKeys + lane] = -INFINITY;
@@ -925,13 +992,10 @@ __global__ __launch_bounds__(kThreads, 3) void subtile_score_kernel(
                   __uint_as_float((t & 1) ? (qw & 0xFFFF0000u) : (qw << 16)));
               acc = fma(qvd, kvd, acc);
             }
-            acc += __shfl_xor(acc, 1);
-            acc += __shfl_xor(acc, 2);
-            acc += __shfl_xor(acc, 4);
+            acc = oct_sum(acc);
             double yy = c2 * acc - l2h;
-            yy = fmax(yy, __shfl_xor(yy, 8));
-            yy = fmax(yy, __shfl_xor(yy, 16));
-            yy = fmax(yy, __shfl_xor(yy, 32));
+            yy = fmax(yy, dpp_mov_f64<0x140>(yy));   // the row's other head
+            yy = max_over_rows_f64(yy);
             if (lane == 0) stage_y[i * kSubKeys + ek[u]] = yy;
           }
         }
@@ -970,16 +1034,6 @@ __global__ __launch_bounds__(kThreads, 3) void subtile_score_kernel(
   if (tid == 0) *cnt = written;
 }
 
-__device__ __forceinline__ uint32_t wave_and(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v &= __shfl_xor(v, off);
-  return v;
-}
-__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v |= __shfl_xor(v, off);
-  return v;
-}
 
 // ---- the row's exact top-k from its candidate list, one work-group per row.
 //
@@ -995,6 +1049,8 @@ __device__ __forceinline__ uint32_t wave_or(uint32_t v) {
 constexpr int kSelThreads = 1024;
 constexpr int kPerThr = 2;
 constexpr int kSweep = kSelThreads * kPerThr;
+static_assert(kNB % kSelThreads == 0, "whole histogram rows per thread");
+constexpr int kSmallBand = 64;   // bands up to this size are ranked by one wave
 
 struct SelEntry {
   double y[kPerThr];
@@ -1057,6 +1113,9 @@ __global__ __launch_bounds__(kSelThreads) void row_select_kernel(
   __shared__ float s_ybase;
   __shared__ uint32_t s_cnt[2][16];
   __shared__ uint32_t s_base[4];
+  __shared__ uint64_t s_bkey[kSmallBand];
+  __shared__ uint32_t s_bpos[kSmallBand];
+  __shared__ uint32_t s_nb;
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1065,8 +1124,12 @@ __global__ __launch_bounds__(kSelThreads) void row_select_kernel(
   int32_t* out = idx_out + static_cast<size_t>(r) * cap;
   uint32_t n_keep = 0;
   if (topk > 0 && first > 0) {
-    // ---- histogram and chunk lengths (exclusive prefix in pre)
-    for (int i = tid; i < kNB; i += kSelThreads) lh[i] = hist_c[static_cast<size_t>(r) * kNB + i];
+    // ---- histogram and chunk lengths (exclusive prefix in pre); all of the
+    // loads are issued before the first wait
+    constexpr int kHv = kNB / kSelThreads;
+    uint32_t hv[kHv];
+#pragma unroll
+    for (int u = 0; u < kHv; ++u) hv[u] = hist_c[static_cast<size_t>(r) * kNB + tid + u * kSelThreads];
     constexpr int kPer = kMaxChunks / kSelThreads;
     uint32_t cl[kPer];
     uint32_t mysum = 0;
@@ -1077,6 +1140,8 @@ __global__ __launch_bounds__(kSelThreads) void row_select_kernel(
       mysum += cl[u];
     }
     if (tid == 0) s_ybase = row_ybase(ytop_h, r);
+#pragma unroll
+    for (int u = 0; u < kHv; ++u) lh[tid + u * kSelThreads] = hv[u];
     uint32_t off, dummy;
     reserve_two(mysum, 0u, nullptr, nullptr, s_cnt, s_base, off, dummy);
 #pragma unroll
@@ -1086,6 +1151,10 @@ __global__ __launch_bounds__(kSelThreads) void row_select_kernel(
       off += cl[u];
     }
     if (tid == 0) pre[n_chunks] = s_base[2];
+    // the band's first radix round starts from cleared reductions
+    if (tid < 4) s_red[tid] = tid < 2 ? 0xFFFFFFFFu : 0u;
+    if (tid < 256) h256[tid] = 0u;
+    if (tid == 0) s_nb = 0u;
     if (tid < 64) {
       const KthBin kb = kth_bin_wave(lh, static_cast<uint32_t>(topk));
       if (tid == 0) {
@@ -1120,12 +1189,57 @@ __global__ __launch_bounds__(kSelThreads) void row_select_kernel(
     uint64_t thr = 0;
     uint32_t nd_t = 0;      // entries equal to T taken, in list order
     bool incl = true;       // true: every band entry >= thr is taken
-    if (!all && take < n_band) {
+    if (!all && take < n_band && n_band <= kSmallBand) {
+      // ---- a small band: its entries (key, list position) go to LDS and
+      // wave 0 ranks them directly, larger key first and then lower position;
+      // the best `take` are selected.  T is the key of the last one taken and
+      // nd_t the taken entries equal to T, which are the first ties in list
+      // order because the rank orders ties by position.
+      for (int sw = 0; sw < n_sweeps; ++sw) {
+        SelEntry e;
+        sweep(sw, e);
+#pragma unroll
+        for (int u = 0; u < kPerThr; ++u) {
+          if (!in_band(e, u)) continue;
+          const uint32_t slot = atomicAdd(&s_nb, 1u);   // < n_band: the band's own count
+          if (slot < static_cast<uint32_t>(kSmallBand)) {
+            s_bkey[slot] = ordered_u64(e.y[u]);
+            s_bpos[slot] = static_cast<uint32_t>(sw * kSweep + kPerThr * tid + u);
+          }
+        }
+      }
+      __syncthreads();
+      if (tid < 64) {
+        const bool have = static_cast<uint32_t>(lane) < n_band;
+        const uint64_t kh = have ? s_bkey[lane] : 0ull;
+        const uint32_t ph = have ? s_bpos[lane] : ~0u;
+        uint32_t rank = 0;
+        for (int j = 0; j < static_cast<int>(n_band); ++j) {
+          const uint64_t kj = lane_value64(kh, j);
+          const uint32_t pj = lane_value(ph, j);
+          rank += (kj > kh || (kj == kh && pj < ph)) ? 1u : 0u;
+        }
+        const uint64_t last = __ballot(have && rank == take - 1);
+        const uint64_t t_key = lane_value64(kh, last ? __builtin_ctzll(last) : 0);
+        const uint64_t eq = __ballot(have && rank < take && kh == t_key);
+        if (lane == 0) {
+          s_hi = t_key;
+          s_need = static_cast<uint32_t>(__popcll(eq));
+        }
+      }
+      __syncthreads();
+      thr = s_hi;
+      nd_t = s_need;
+      incl = false;
+    } else if (!all && take < n_band) {
+      // Each round: AND/OR of the keys in play -> barrier -> histogram of the
+      // first digit where they differ -> barrier -> wave 0 picks the digit and
+      // clears s_red / h256 for the next round -> barrier.  Every thread reads
+      // s_red between the first two barriers and the round's result after the
+      // third, so those single buffers are never rewritten while being read.
       uint64_t mask = 0;
       uint32_t nd = take;
       while (true) {
-        if (tid < 4) s_red[tid] = tid < 2 ? 0xFFFFFFFFu : 0u;
-        __syncthreads();
         uint32_t a0 = ~0u, a1 = ~0u, o0 = 0u, o1 = 0u;
         for (int sw = 0; sw < n_sweeps; ++sw) {
           SelEntry e;
@@ -1165,8 +1279,6 @@ __global__ __launch_bounds__(kSelThreads) void row_select_kernel(
         const int d = __clzll(static_cast<long long>(diff)) / 8;   // first digit that differs
         mask = d == 0 ? 0ull : ~0ull << (64 - 8 * d);
         thr = and_k & mask;
-        if (tid < 256) h256[tid] = 0u;
-        __syncthreads();
         for (int sw = 0; sw < n_sweeps; ++sw) {
           SelEntry e;
           sweep(sw, e);
@@ -1182,7 +1294,7 @@ __global__ __launch_bounds__(kSelThreads) void row_select_kernel(
             const uint64_t m_act = __ballot(act);
             if (m_act) {
               const int leader = __builtin_ctzll(m_act);
-              const uint32_t d0 = __shfl(dig, leader);
+              const uint32_t d0 = lane_value(dig, leader);
               if (__ballot(act && dig == d0) == m_act) {
                 if (lane == leader) atomicAdd(&h256[d0], static_cast<uint32_t>(__popcll(m_act)));
               } else if (act) {
@@ -1201,12 +1313,7 @@ __global__ __launch_bounds__(kSelThreads) void row_select_kernel(
             c4[u] = h256[255 - 4 * lane - u];
             sum += c4[u];
           }
-          uint32_t inc = sum;
-#pragma unroll
-          for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t v = __shfl_up(inc, o);
-            if (lane >= o) inc += v;
-          }
+          const uint32_t inc = wave_incl_scan(sum);
           const uint64_t hit = __ballot(inc >= nd);
           const int owner = hit ? __builtin_ctzll(hit) : 63;   // nd <= entries in play
           if (lane == owner) {
@@ -1221,13 +1328,17 @@ __global__ __launch_bounds__(kSelThreads) void row_select_kernel(
             s_done = c4[u] == left;
             s_hi = thr | (static_cast<uint64_t>(255 - 4 * lane - u) << (56 - 8 * d));
           }
+          // the next round's reductions start from cleared buffers (this
+          // lane's reads of h256 above come first)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) h256[255 - 4 * lane - u] = 0u;
+          if (lane < 4) s_red[lane] = lane < 2 ? 0xFFFFFFFFu : 0u;
         }
         __syncthreads();
         nd = s_need;
         thr = s_hi;
         mask |= 255ull << (56 - 8 * d);
         if (s_done) break;   // every remaining entry of the bin is taken
-        __syncthreads();     // s_need / s_hi / s_done are rewritten next round
       }
     }
     // ---- the selection in list order
@@ -1369,7 +1480,7 @@ __device__ KThr key_threshold(const uint64_t* keys, uint32_t n, uint32_t need, u
       const uint64_t m_act = __ballot(act);
       if (m_act) {
         const int leader = __builtin_ctzll(m_act);
-        const uint32_t d0 = __shfl(dig, leader);
+        const uint32_t d0 = lane_value(dig, leader);
         if (__ballot(act && dig == d0) == m_act) {
           if (lane == leader) atomicAdd(&h256[d0], static_cast<uint32_t>(__popcll(m_act)));
         } else if (act) {
@@ -1386,12 +1497,7 @@ __device__ KThr key_threshold(const uint64_t* keys, uint32_t n, uint32_t need, u
         c4[u] = h256[255 - 4 * lane - u];
         sum += c4[u];
       }
-      uint32_t inc = sum;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t v = __shfl_up(inc, o);
-        if (lane >= o) inc += v;
-      }
+      const uint32_t inc = wave_incl_scan(sum);
       const uint64_t hit = __ballot(inc >= nd);
       const int owner = hit ? __builtin_ctzll(hit) : 63;
       if (lane == owner) {
@@ -1517,8 +1623,7 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
       const uint32_t* kp = kmax + (static_cast<size_t>(b) * Hkv + g) * n_ib;
       uint32_t m = 0u;
       for (int i = tid; i < n_ib; i += kRowThreads) m = max(m, kp[i]);
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(m, off)));
+      m = wave_umax(m);
       if (lane == 0 && m) atomicMax(&s_km, m);
     }
     const u16* qr = q + static_cast<size_t>(r) * kG * kD;
@@ -1793,8 +1898,7 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
             double acc = 0.0;
 #pragma unroll
             for (int t2 = 0; t2 < 8; ++t2) acc = fma(qh[t2], kv[t2], acc);
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) acc += __shfl_xor(acc, off);
+            acc = row16_sum(acc);
             yy = fmax(yy, c2 * acc - l2s[h]);
           }
           if (part == 0) bk[i] = ordered_u64(yy);
@@ -1809,8 +1913,7 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
             const uint64_t kh = have ? bk[lane] : 0ull;
             uint32_t rank = 0;
             for (int j = 0; j < static_cast<int>(n_band); ++j) {
-              const uint64_t kj = (static_cast<uint64_t>(static_cast<uint32_t>(__shfl(static_cast<int>(kh >> 32), j))) << 32) |
-                                  static_cast<uint32_t>(__shfl(static_cast<int>(kh & 0xFFFFFFFFull), j));
+              const uint64_t kj = lane_value64(kh, j);
               rank += (kj > kh || (kj == kh && j < lane)) ? 1u : 0u;
             }
             const bool win = have && rank < take;

@@ -119,6 +119,22 @@ def test_identical_keys_take_lowest_indices(hs2):
     assert res["idx"][0, 0, 0, :116].tolist() == list(range(100)) + list(range(5984, 6000))
 
 
+def test_small_band_ties_take_lowest_indices(hs2):
+    """40 identical keys scoring far above the rest, top_k 16: the bin of the
+    k-th key holds just those 40 ties (a band small enough for the one-wave
+    rank), so the 16 lowest of their positions win."""
+    w = wl.small(batch=1, n_q_heads=8, n_kv_heads=1, ctx_len=2000, n_sparse_layers=1, top_k=16,
+                 window=16, config_id=25)
+    x = wl.generate(w)
+    qf = wl.bf16_bits_to_f32(x["q_full"])
+    vec = wl.f32_to_bf16_bits((4.0 * qf[0, 0, :, :].mean(axis=0)).astype(np.float32))
+    pos = np.sort(np.random.default_rng(2025).choice(1984, 40, replace=False))
+    x["k"][0, 0, pos, :] = vec[None, :]
+    res = gh.run_step(w, x)
+    gh.compare_step(w, x, res)
+    assert res["idx"][0, 0, 0, :32].tolist() == pos[:16].tolist() + list(range(1984, 2000))
+
+
 def test_deterministic_across_runs(hs2):
     w = wl.small(batch=2, n_q_heads=16, n_kv_heads=2, ctx_len=3333, n_sparse_layers=3,
                  top_k=256, window=64, n_needles=8, config_id=24)
