@@ -139,11 +139,6 @@ __device__ __forceinline__ double oct_sum(double v) {
   v += dpp_mov_f64<0x141>(v);
   return v;
 }
-__device__ __forceinline__ float oct_max_f32(float v) {
-  v = fmaxf(v, __uint_as_float(dpp_mov<0xB1>(__float_as_uint(v))));
-  v = fmaxf(v, __uint_as_float(dpp_mov<0x4E>(__float_as_uint(v))));
-  return fmaxf(v, __uint_as_float(dpp_mov<0x141>(__float_as_uint(v))));
-}
 // Sum over each row of 16 lanes, in every lane of the row: the pairing tree of
 // a lane ^ 1, ^ 2, ^ 4, ^ 8 butterfly, so every lane holds the same value.
 __device__ __forceinline__ double row16_sum(double v) {
@@ -825,9 +820,12 @@ __global__ __launch_bounds__(kThreads) void subtile_cand_kernel(
 // Each candidate subtile is first scored in float32 on the bf16 MFMA (16 keys
 // against the 8 heads); only its keys that may reach the lower bin (float
 // error is far below a bin) get the exact float64 importance, by plain fp64
-// fmas over lanes (head, 16 dims).  Three work-groups fit a CU, and the grid
-// is sized to be resident at once.
-constexpr int kStageSub = 64;   // candidate subtiles staged per pass
+// fmas over lanes (head, 16 dims).  Those keys' rows come from the MFMA
+// operand registers through a small per-wave LDS slot, not from memory again,
+// so the exact pass adds no memory round trip to the wave's chain.  Three
+// work-groups fit a CU, and the grid is sized to be resident at once.
+constexpr int kStageSub = 128;  // candidate subtiles staged per pass
+static_assert(kStageSub / (kThreads / 64) <= 64, "a wave's subtiles of a pass fit one per lane");
 __global__ __launch_bounds__(kThreads, 3) void subtile_score_kernel(
     const int32_t* __restrict__ lo_in, const int32_t* __restrict__ clist,
     const uint32_t* __restrict__ ccnt, const double* __restrict__ lse2,
@@ -840,12 +838,14 @@ __global__ __launch_bounds__(kThreads, 3) void subtile_score_kernel(
   __shared__ int32_t s_list[kScoreRound];
   __shared__ double stage_y[kStageSub * kSubKeys];
   __shared__ u32x4 q_lds[2 * kG * kD / 8];   // 16 heads (8 real) x 128 dims, bf16
+  __shared__ u32x4 k_slot[kThreads / 64][2][kD / 8];   // per wave: two key rows, bf16
   __shared__ float s_ybase;
   __shared__ uint32_t s_cnt[2][16];
   __shared__ uint32_t s_base[4];
   const int r = blockIdx.y;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // wave index in a scalar register: the per-wave loops below are uniform
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const int64_t first = row_first(row_pos(r, T, Hkv, S), w);
   uint32_t* cnt = cand_cnt + static_cast<size_t>(r) * n_chunks + blockIdx.x;
@@ -871,10 +871,14 @@ __global__ __launch_bounds__(kThreads, 3) void subtile_score_kernel(
     q_lds[i] = h < kG ? load_u32x4(q + (static_cast<size_t>(r) * kG + h) * kD + 8 * d8)
                       : u32x4{0u, 0u, 0u, 0u};
   }
-  // float32 scale and lse2 of head col for the filter; for the exact pass lane
-  // (h, j) keeps head h's query dims 16 j .. +16 widened to float64 and its lse2
+  // float32 scale and the lse2 of heads 4 grp .. 4 grp + 3 for the filter; for
+  // the exact pass lane (h, j) keeps head h's query dims 16 j .. +16 widened to
+  // float64 and its lse2
   const float c2f = static_cast<float>(c2);
-  const float l2f = col < kG ? static_cast<float>(lse2[static_cast<size_t>(r) * kG + col]) : 0.f;
+  float l2f[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    l2f[i] = 4 * grp + i < kG ? static_cast<float>(lse2[static_cast<size_t>(r) * kG + 4 * grp + i]) : 0.f;
   const double l2h = lse2[static_cast<size_t>(r) * kG + (lane >> 3)];
   u32x4 qh2[2];   // packed bf16, widened at each use
   {
@@ -900,6 +904,19 @@ __global__ __launch_bounds__(kThreads, 3) void subtile_score_kernel(
   const uint32_t p_begin = min(n_c, share * blockIdx.x);
   const uint32_t p_end = min(n_c, p_begin + share);
   const float ybase = s_ybase;
+  // The float32 filter as one compare per head on the raw MFMA logit: a key
+  // may reach the lower bin only if, for some head h, s2_h c2 - lse2_h is at
+  // least the bottom of the bin below it (one bin of margin for the float
+  // error), i.e. s2_h >= t_h = (that bound + lse2_h) / c2.  Lane (col, grp)
+  // holds heads 4 grp .. 4 grp + 3 of key col; the padding heads never pass.
+  float t4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    t4[i] = 4 * grp + i >= kG ? INFINITY
+            : lo_bin - 1 <= 0 ? -INFINITY
+                              : (ybase + static_cast<float>(lo_bin - 1) * (kYRange / kNB) + l2f[i]) / c2f;
+  // lane (col, grp)'s part of a subtile: key col, dims 32 grp .. 32 grp + 31
+  const uint32_t lane_off = static_cast<uint32_t>(col * kD + 32 * grp);
   const int b = r / (T * Hkv);
   const int g = r % Hkv;
   const u16* kr = k + (static_cast<size_t>(b) * Hkv + g) * static_cast<size_t>(kvp) * kD;
@@ -925,59 +942,68 @@ __global__ __launch_bounds__(kThreads, 3) void subtile_score_kernel(
     for (uint32_t p0 = 0; p0 < n_local; p0 += kStageSub) {
       const uint32_t np = min(static_cast<uint32_t>(kStageSub), n_local - p0);
       // ---- float64 importance of the pass's candidates, one subtile per wave
-      auto load_sub = [&](uint32_t i, u32x4 (&ka)[4]) {
-        int64_t key = static_cast<int64_t>(s_list[p0 + i]) * kSubKeys + col;
-        key = key < S - 1 ? key : S - 1;
+      // subtile st's K rows (uniform base, fixed lane offsets); a subtile that
+      // runs past the cache's rows reads the last row instead
+      auto load_sub = [&](int32_t st, u32x4 (&ka)[4]) {
+        const int64_t key0 = static_cast<int64_t>(st) * kSubKeys;
+        if (key0 + kSubKeys <= kvp) {
+          const u16* base = kr + key0 * kD;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) ka[c] = load_u32x4(kr + key * kD + 32 * grp + 8 * c);
+          for (int c = 0; c < 4; ++c) ka[c] = load_u32x4(base + lane_off + 8 * c);
+        } else {
+          const int64_t key = min(key0 + col, kvp - 1);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) ka[c] = load_u32x4(kr + key * kD + 32 * grp + 8 * c);
+        }
       };
-      // two subtiles ahead per wave
+      // Three register buffers per wave, used in turn, so that two subtiles
+      // are always in flight behind the one being scored.  The loads are
+      // unconditional (past the wave's last subtile they repeat it) and no
+      // buffer is copied, so each wait is for the oldest buffer only.
       constexpr uint32_t kW = kThreads / 64;
-      u32x4 ka_cur[4], ka_nxt[4], ka_nx2[4];
-      if (static_cast<uint32_t>(wave) < np) load_sub(wave, ka_cur);
-      if (wave + kW < np) load_sub(wave + kW, ka_nxt);
-      for (uint32_t i = wave; i < np; i += kW) {
-        if (i + 2 * kW < np) load_sub(i + 2 * kW, ka_nx2);
-        const int64_t key0 = static_cast<int64_t>(s_list[p0 + i]) * kSubKeys;
-        // ---- float32 importance of the 16 keys on the bf16 MFMA (S = K . Q^T,
-        // 16 keys x 16 heads of which 8 are used): lane (col, grp) gets keys
-        // 4 grp + e against head col
+      // pass entry i (this wave's entries i = wave + kW t) is subtile st
+      auto score_sub = [&](uint32_t i, int32_t st, const u32x4 (&ka)[4]) {
+        const int64_t key0 = static_cast<int64_t>(st) * kSubKeys;
+        // ---- float32 logits of the 16 keys on the bf16 MFMA (Q . K^T, 16
+        // heads of which 8 are used x 16 keys): lane (col, grp) gets heads
+        // 4 grp + e against key col
         f32x4 sf = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          sf = mfma_16x16x32(as_bf16x8(ka_cur[c]),
-                             as_bf16x8(q_lds[(col * kD + 32 * grp + 8 * c) / 8]), sf);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          ka_cur[c] = ka_nxt[c];
-          ka_nxt[c] = ka_nx2[c];
-        }
-        uint32_t nib = 0;   // keys 4 grp + e that may reach the lower bin
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float v = col < kG ? fmaf(sf[e], c2f, -l2f) : -INFINITY;
-          v = oct_max_f32(v);   // heads 0..7 of the row
-          // float error is far below a bin: a key one bin short can still make it
-          nib |= static_cast<uint32_t>(key0 + 4 * grp + e < first &&
-                                       cand_bin(static_cast<double>(v), ybase) >= lo_bin - 1) << e;
-        }
-        const uint32_t promising = lane_value(nib, 0) | (lane_value(nib, 16) << 4) |
-                                   (lane_value(nib, 32) << 8) | (lane_value(nib, 48) << 12);
+          sf = mfma_16x16x32(as_bf16x8(q_lds[(col * kD + 32 * grp + 8 * c) / 8]),
+                             as_bf16x8(ka[c]), sf);
+        // keys that may reach the lower bin: key col passes in lane col
+        // (heads 0..3) or lane 16 + col (heads 4..7)
+        const uint64_t hit = __ballot(sf[0] >= t4[0] || sf[1] >= t4[1] || sf[2] >= t4[2] ||
+                                      sf[3] >= t4[3]);
+        uint32_t promising = static_cast<uint32_t>(hit | (hit >> 16)) & 0xFFFFu;
+        // only keys before `first` are candidates
+        const int64_t room = first - key0;
+        if (room < kSubKeys) promising &= room <= 0 ? 0u : (1u << room) - 1u;
         // ---- exact float64 importance of the promising keys only, two at a
-        // time: lane (h, j) = (lane >> 3, lane & 7) takes head h, dims 16 j .. +16
+        // time: lane (h, j) = (lane >> 3, lane & 7) takes head h, dims 16 j .. +16.
+        // Key e's row sits in the MFMA operand of lanes (col = e, grp = 0..3),
+        // 32 dims each; those lanes copy it to the wave's LDS slot.
         if (lane < kSubKeys) stage_y[i * kSubKeys + lane] = -INFINITY;
         for (uint32_t m = promising; m; ) {
           int ek[2];
-          u32x4 kv4[2][2];
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             ek[u] = m ? __builtin_ctz(m) : -1;
             if (m) m &= m - 1;
-            const int64_t key = min(key0 + (ek[u] < 0 ? 0 : ek[u]), S - 1);
-            const u16* src = kr + key * kD + 16 * (lane & 7);
-            kv4[u][0] = load_u32x4(src);
-            kv4[u][1] = load_u32x4(src + 8);
+            if (col == ek[u]) {
+#pragma unroll
+              for (int c = 0; c < 4; ++c) k_slot[wave][u][4 * grp + c] = ka[c];
+            }
           }
+          lds_fence_wave();   // the slot's writes land before any lane reads them
+          u32x4 kv4[2][2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            kv4[u][0] = k_slot[wave][u][2 * (lane & 7)];
+            kv4[u][1] = k_slot[wave][u][2 * (lane & 7) + 1];
+          }
+          lds_fence_wave();   // and are read before the next pair overwrites them
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             if (ek[u] < 0) continue;
@@ -999,7 +1025,38 @@ __global__ __launch_bounds__(kThreads, 3) void subtile_score_kernel(
             if (lane == 0) stage_y[i * kSubKeys + ek[u]] = yy;
           }
         }
+      };
+      // (the scheduling barriers keep the loads in program order: the oldest
+      // buffer is the one scored next).  The wave's subtile numbers for the
+      // pass sit one per lane, read out with a scalar lane read.
+      if (static_cast<uint32_t>(wave) < np) {
+        const uint32_t n_w = (np - 1 - wave) / kW + 1;   // <= kStageSub / kW <= 64
+        const int32_t my_sub = static_cast<uint32_t>(lane) < n_w ? s_list[p0 + wave + kW * lane] : 0;
+        auto sub_at = [&](uint32_t t) {
+          return static_cast<int32_t>(lane_value(static_cast<uint32_t>(my_sub), static_cast<int>(min(t, n_w - 1))));
+        };
+        u32x4 kb0[4], kb1[4], kb2[4];
+        load_sub(sub_at(0), kb0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_sub(sub_at(1), kb1);
+        __builtin_amdgcn_sched_barrier(0);
+        // (no early exit from the trip: an exit path that leaves a buffer in
+        // flight would make every trip wait for it)
+        for (uint32_t t = 0; t < n_w; t += 3) {
+          load_sub(sub_at(t + 2), kb2);
+          __builtin_amdgcn_sched_barrier(0);
+          score_sub(wave + kW * t, sub_at(t), kb0);
+          load_sub(sub_at(t + 3), kb0);
+          __builtin_amdgcn_sched_barrier(0);
+          if (t + 1 < n_w) score_sub(wave + kW * (t + 1), sub_at(t + 1), kb1);
+          load_sub(sub_at(t + 4), kb1);
+          __builtin_amdgcn_sched_barrier(0);
+          if (t + 2 < n_w) score_sub(wave + kW * (t + 2), sub_at(t + 2), kb2);
+        }
       }
+      // the prefetches past the end are never used: drain them here, once,
+      // so that no wait for them lands inside the next pass's loop
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
       __syncthreads();
       // ---- keep the keys that can still be selected, in order (thread t:
       // the 16 keys of the pass's t-th candidate subtile)
