@@ -1212,6 +1212,16 @@ __global__ __launch_bounds__(kSelThreads) void row_select_kernel(
     if (tid < 4) s_red[tid] = tid < 2 ? 0xFFFFFFFFu : 0u;
     if (tid < 256) h256[tid] = 0u;
     if (tid == 0) s_nb = 0u;
+    __syncthreads();
+    // the list's first sweep is loaded while wave 0 finds the k-th bin
+    const uint32_t n_total = pre[n_chunks];
+    const size_t chunk_len = static_cast<size_t>(chunk) * kSubKeys;
+    const size_t rbase = static_cast<size_t>(r) * n_chunks * chunk_len;
+    const double* cy = cand_y + rbase;
+    const int32_t* ci = cand_idx + rbase;
+    const int n_sweeps = static_cast<int>((n_total + kSweep - 1) / kSweep);
+    SelEntry e0;
+    load_entries(e0, cy, ci, pre, n_chunks, chunk_len, kPerThr * tid, n_total);
     if (tid < 64) {
       const KthBin kb = kth_bin_wave(lh, static_cast<uint32_t>(topk));
       if (tid == 0) {
@@ -1221,19 +1231,11 @@ __global__ __launch_bounds__(kSelThreads) void row_select_kernel(
       }
     }
     __syncthreads();
-    const uint32_t n_total = pre[n_chunks];
     const int bstar = s_b;
     const float ybase = s_ybase;
-    const size_t chunk_len = static_cast<size_t>(chunk) * kSubKeys;
-    const size_t rbase = static_cast<size_t>(r) * n_chunks * chunk_len;
-    const double* cy = cand_y + rbase;
-    const int32_t* ci = cand_idx + rbase;
-    const int n_sweeps = static_cast<int>((n_total + kSweep - 1) / kSweep);
     const bool all = bstar < 0;
     const uint32_t take = all ? 0u : static_cast<uint32_t>(topk) - s_above;
     const uint32_t n_band = all ? 0u : s_at;
-    SelEntry e0;
-    load_entries(e0, cy, ci, pre, n_chunks, chunk_len, kPerThr * tid, n_total);
     // sweep sw of the list as registers
     auto sweep = [&](int sw, SelEntry& e) {
       if (sw == 0) e = e0;
@@ -1458,7 +1460,9 @@ __global__ __launch_bounds__(kSelThreads) void row_select_kernel(
     const uint32_t written = sel_seen + min(tie_seen, nd_t);
     n_keep = min(written, static_cast<uint32_t>(topk));
   }
-  __syncthreads();
+  // no barrier: the selection filled positions [0, n_keep) (exactly top-k of
+  // them, or the whole list when it is shorter), the tail below starts at
+  // n_keep, and n_keep is the same in every thread
   const int n_total_sel = static_cast<int>(n_keep) + static_cast<int>(static_cast<int64_t>(P) - first + 1);
   for (int i = static_cast<int>(n_keep) + tid; i < cap; i += kSelThreads)
     out[i] = i < n_total_sel ? static_cast<int32_t>(first + (i - static_cast<int>(n_keep))) : -1;
