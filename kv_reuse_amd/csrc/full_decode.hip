@@ -108,17 +108,22 @@ __device__ __forceinline__ void process_tile(const KVTile& t, SoftmaxState& st,
   // per-subtile (16 keys) maxima of each head: lanes of one head are col + 16*grp
   float m0 = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
   float m1 = fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7]));
-  m0 = fmaxf(m0, __shfl_xor(m0, 16));
-  m1 = fmaxf(m1, __shfl_xor(m1, 16));
-  m0 = fmaxf(m0, __shfl_xor(m0, 32));
-  m1 = fmaxf(m1, __shfl_xor(m1, 32));
+  // one row swap serves both: rows 0 and 2 pair m0 across rows 0|1 and 2|3,
+  // rows 1 and 3 pair m1; the second swap then joins 0-1 with 2-3, leaving
+  // m0's subtile maximum in rows 0 and 2 and m1's in rows 1 and 3
+  float mx;
+  {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(m0), __float_as_uint(m1), false, false);
+    mx = max_xor32(fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1])));
+  }
   // subtile t0/16 + mt, head col: 64 contiguous bytes per tile (grp 0 and 1);
   // stmax_row is either the row's global array or the work-group's LDS stage
   // (then indexed from the split's first subtile)
   if (col < kG && grp < 2 && t0 + 16 * grp < key_end)
-    stmax_row[(t0 / 16 + grp - st_base) * kG + col] = grp == 0 ? m0 : m1;
-  // ---- online softmax (per head = per lane % 16)
-  const float tm = fmaxf(m0, m1);
+    stmax_row[(t0 / 16 + grp - st_base) * kG + col] = mx;   // row grp: subtile grp
+  // ---- online softmax (per head = per lane % 16); the tile's maximum joins
+  // the two subtiles' (rows 0|1 and 2|3)
+  const float tm = max_xor16(mx);
   const float m_new = fmaxf(st.m, ceilf(tm));
   const float alpha = (st.m == -INFINITY) ? 0.f : ldexpf(1.f, static_cast<int>(st.m - m_new));
   float p[8];
@@ -210,8 +215,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void full_decode_split_kernel(
       t0 = t1;
     }
   }
-  st.l += __shfl_xor(st.l, 16);
-  st.l += __shfl_xor(st.l, 32);
+  st.l = sum_rows(st.l);
 
   __syncthreads();  // all waves done with their V tiles (and the stage)
   if (staged) {
@@ -292,14 +296,22 @@ __global__ __launch_bounds__(kCmbThreads) void full_combine_kernel(
   if (tid < 64) {
     float M = -INFINITY;
     for (int s2 = tid; s2 < n_split; s2 += 64) M = fmaxf(M, sm[s2]);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    // L in a fixed order: lane-strided partial sums, then a fixed tree
+    M = max_xor32(max_xor16(M));
+    M = fmaxf(M, dpp_f32<0x128>(M));   // row_ror:8, the other half of the row
+    M = fmaxf(M, dpp_f32<0x141>(M));   // row_half_mirror, the other quad of 8
+    M = fmaxf(M, dpp_f32<0x4E>(M));    // lane ^ 2
+    M = fmaxf(M, dpp_f32<0xB1>(M));    // lane ^ 1
+    // L in a fixed order: lane-strided partial sums, then the tree of a lane
+    // ^ 32, ^ 16, ^ 8, ^ 4, ^ 2, ^ 1 butterfly.  After the ^ 8 step the row
+    // repeats with period 8, so a rotation by 4 within the row reads lane ^ 4.
     double L = 0.0;
     for (int s2 = tid; s2 < n_split; s2 += 64)
       if (sm[s2] != -INFINITY) L += sl[s2] * ldexp(1.0, static_cast<int>(sm[s2] - M));
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
+    L = sum_rows_f64(L);
+    L += dpp_f64<0x128>(L);   // row_ror:8: lane ^ 8
+    L += dpp_f64<0x124>(L);   // row_ror:4: lane ^ 4 (period 8)
+    L += dpp_f64<0x4E>(L);    // lane ^ 2
+    L += dpp_f64<0xB1>(L);    // lane ^ 1
     if (tid == 0) {
       s_M = M;
       s_L = L;

@@ -192,6 +192,56 @@ __device__ __forceinline__ bf16x8 lds_vt_operand(const u16* tile, int pitch, int
   const uint2 b = lds_read_tr16_b64(p0 + 16 * pitch);
   return as_bf16x8(u32x4{a.x, a.y, b.x, b.y});
 }
+// Cross-row steps on the gfx950 row swaps (VALU, no LDS round trip).  With
+// both operands v, v_permlane16_swap leaves rows (0, 0, 2, 2) of v in the
+// first result and rows (1, 1, 3, 3) in the second, and v_permlane32_swap
+// leaves rows (0, 1, 0, 1) and (2, 3, 2, 3): combining the two results pairs
+// lane l with l ^ 16, or with l ^ 32.
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// v + v[l ^ 16], then + v[l ^ 32]: each step adds the same two values in
+// every lane of a pair (addition is commutative), as a lane-xor butterfly does.
+__device__ __forceinline__ float sum_rows(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+// DPP moves within rows of 16 lanes (every source lane valid for the
+// controls used: quad_perm, row_ror, row mirrors).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kCtrl, 0xF, 0xF, true));
+}
+template <int kCtrl>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const long long u = __double_as_longlong(v);
+  const uint32_t lo = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(u)), kCtrl, 0xF, 0xF, true));
+  const uint32_t hi = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(u >> 32)), kCtrl, 0xF, 0xF, true));
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+// v + v[l ^ 32] then + v[l ^ 16] for a double (the butterfly's first two steps).
+__device__ __forceinline__ double sum_rows_f64(double v) {
+  auto join = [](uint32_t hi, uint32_t lo) {
+    return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+  };
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  const auto l32 = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(u), static_cast<uint32_t>(u), false, false);
+  const auto h32 = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(u >> 32), static_cast<uint32_t>(u >> 32), false, false);
+  v = join(h32[0], l32[0]) + join(h32[1], l32[1]);
+  const uint64_t w = static_cast<uint64_t>(__double_as_longlong(v));
+  const auto l16 = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(w), static_cast<uint32_t>(w), false, false);
+  const auto h16 = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(w >> 32), static_cast<uint32_t>(w >> 32), false, false);
+  return join(h16[0], l16[0]) + join(h16[1], l16[1]);
+}
 // Wait until this wave's outstanding LDS operations are done, and keep the
 // compiler from moving memory accesses across this point.
 __device__ __forceinline__ void lds_fence_wave() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }

@@ -150,8 +150,7 @@ __global__ __launch_bounds__(NCT * 64) void sparse_kernel(
         }
       float tm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                        fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-      tm = fmaxf(tm, __shfl_xor(tm, 16));
-      tm = fmaxf(tm, __shfl_xor(tm, 32));
+      tm = max_xor32(max_xor16(tm));
       const float m_new = fmaxf(m_run, tm);
       const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
       float p[8];
@@ -168,8 +167,7 @@ __global__ __launch_bounds__(NCT * 64) void sparse_kernel(
       }
     }
   }
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = sum_rows(l_run);
   if (!col_ok) return;
   if (nch == 1) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
@@ -271,8 +269,7 @@ __global__ __launch_bounds__(64) void swa_branch_kernel(
       }
     float tm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
                      fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-    tm = fmaxf(tm, __shfl_xor(tm, 16));
-    tm = fmaxf(tm, __shfl_xor(tm, 32));
+    tm = max_xor32(max_xor16(tm));
     const float m_new = fmaxf(m_run, tm);
     const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
     float p[8];
@@ -289,8 +286,7 @@ __global__ __launch_bounds__(64) void swa_branch_kernel(
     }
     __syncthreads();   // the tile is consumed before the next one is staged
   }
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = sum_rows(l_run);
   if (col >= kG) return;
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
   float* dst = swa_out + ((static_cast<size_t>(n) * R + r) * kG + col) * kD;
