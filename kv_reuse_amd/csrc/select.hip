@@ -1992,40 +1992,32 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
         // winners in band order (ascending index), ties: the first kt.nd_t
         const uint32_t per = (n_band + kRowThreads - 1) / kRowThreads;
         const uint32_t q0 = min(n_band, tid * per), q1 = min(n_band, q0 + per);
-        auto cls = [&](uint32_t i, uint32_t& win, uint32_t& tie) {
-          win = 0;
-          tie = 0;
-          if (!by_thr) {
-            win = 1;
-            return;
-          }
-          if (take == 0) return;
+        // class of band entry i: 1 a winner, 2 a tie at the threshold, 0 out
+        auto cls = [&](uint32_t i) -> uint32_t {
+          if (!by_thr) return 1u;
+          if (take == 0) return 0u;
           const uint64_t kh = bk[i];
-          if (kh > kt.thr || (kt.incl && kh == kt.thr)) win = 1;
-          else if (kh == kt.thr) tie = 1;
+          if (kh > kt.thr || (kt.incl && kh == kt.thr)) return 1u;
+          return kh == kt.thr ? 2u : 0u;
         };
         uint32_t nwin = 0, ntie = 0;
         for (uint32_t i = q0; i < q1; ++i) {
-          uint32_t a, t2;
-          cls(i, a, t2);
-          nwin += a;
-          ntie += t2;
+          const uint32_t c = cls(i);
+          nwin += c == 1u;
+          ntie += c == 2u;
         }
         uint32_t o_tie, o_dummy;
         reserve_two(ntie, 0u, nullptr, nullptr, s_cnt, s_base, o_tie, o_dummy);
         uint32_t keep_tie = 0;
-        for (uint32_t i = q0, ot = o_tie; i < q1; ++i) {
-          uint32_t a, t2;
-          cls(i, a, t2);
-          if (t2) keep_tie += (ot++ < kt.nd_t);
-        }
+        for (uint32_t i = q0, ot = o_tie; i < q1; ++i)
+          if (cls(i) == 2u) keep_tie += (ot++ < kt.nd_t);
         uint32_t o_w;
         reserve_two(nwin + keep_tie, 0u, nullptr, nullptr, s_cnt, s_base, o_w, o_dummy);
         n_w = s_base[2];
         for (uint32_t i = q0, ot = o_tie; i < q1; ++i) {
-          uint32_t a, t2;
-          cls(i, a, t2);
-          if (t2) a = (ot++ < kt.nd_t);
+          const uint32_t c = cls(i);
+          bool a = c == 1u;
+          if (c == 2u) a = (ot++ < kt.nd_t);
           if (a) {
             if (o_w < static_cast<uint32_t>(kMaxSel)) bw[o_w] = bi[i];
             ++o_w;
