@@ -135,6 +135,24 @@ def test_small_band_ties_take_lowest_indices(hs2):
     assert res["idx"][0, 0, 0, :32].tolist() == pos[:16].tolist() + list(range(1984, 2000))
 
 
+def test_large_band_distinct_keys(hs2):
+    """200 keys near one needle vector (distinct, within about one bin of each
+    other) far above the rest, top_k 100: the bin of the k-th key holds more
+    than 64 distinct entries, so the radix threshold (not the one-wave rank)
+    decides, over digits that really differ."""
+    w = wl.small(batch=1, n_q_heads=8, n_kv_heads=1, ctx_len=6000, n_sparse_layers=1, top_k=100,
+                 window=16, config_id=26)
+    x = wl.generate(w)
+    qf = wl.bf16_bits_to_f32(x["q_full"])
+    rng = np.random.default_rng(2026)
+    base = 4.0 * qf[0, 0, :, :].mean(axis=0)
+    pos = np.sort(rng.choice(5984, 200, replace=False))
+    noise = rng.standard_normal((200, 128)).astype(np.float32) * 0.003
+    x["k"][0, 0, pos, :] = wl.f32_to_bf16_bits((base[None, :] + noise).astype(np.float32))
+    res = gh.run_step(w, x)
+    gh.compare_step(w, x, res)
+
+
 def test_deterministic_across_runs(hs2):
     w = wl.small(batch=2, n_q_heads=16, n_kv_heads=2, ctx_len=3333, n_sparse_layers=3,
                  top_k=256, window=64, n_needles=8, config_id=24)
