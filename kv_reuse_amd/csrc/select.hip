@@ -863,9 +863,8 @@ __global__ __launch_bounds__(kThreads, 3) void subtile_score_kernel(
     cl[u] = c < cc_nchunk ? ccnt[static_cast<size_t>(r) * cc_nchunk + c] : 0u;
     mysum += cl[u];
   }
-  // the B operand in LDS, packed bf16: head col (zero for the padding heads),
-  // dims 32*grp + 8c .. +8 (kept out of registers to leave room for a deeper
-  // prefetch of the candidates' K rows)
+  // the query operand staged in LDS, packed bf16: lane (col, grp) of MFMA c
+  // takes head col (zero for the padding heads), dims 32*grp + 8c .. +8
   for (int i = tid; i < 2 * kG * kD / 8; i += kThreads) {
     const int h = i / (kD / 8), d8 = i % (kD / 8);
     q_lds[i] = h < kG ? load_u32x4(q + (static_cast<size_t>(r) * kG + h) * kD + 8 * d8)
@@ -956,6 +955,10 @@ __global__ __launch_bounds__(kThreads, 3) void subtile_score_kernel(
           for (int c = 0; c < 4; ++c) ka[c] = load_u32x4(kr + key * kD + 32 * grp + 8 * c);
         }
       };
+      // the A operand (the query heads) in registers for the whole pass
+      u32x4 qa[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qa[c] = q_lds[(col * kD + 32 * grp + 8 * c) / 8];
       // Three register buffers per wave, used in turn, so that two subtiles
       // are always in flight behind the one being scored.  The loads are
       // unconditional (past the wave's last subtile they repeat it) and no
@@ -970,7 +973,7 @@ __global__ __launch_bounds__(kThreads, 3) void subtile_score_kernel(
         f32x4 sf = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          sf = mfma_16x16x32(as_bf16x8(q_lds[(col * kD + 32 * grp + 8 * c) / 8]),
+          sf = mfma_16x16x32(as_bf16x8(qa[c]),
                              as_bf16x8(ka[c]), sf);
         // keys that may reach the lower bin: key col passes in lane col
         // (heads 0..3) or lane 16 + col (heads 4..7)
