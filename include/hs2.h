@@ -89,7 +89,12 @@ typedef struct hs2_shape {
                          0 means ctx_len; otherwise it must be >= ctx_len.  Rows ctx_len ..
                          kv_capacity-1 are never read, so a cache allocated once for its
                          final length serves every step as it grows (see hs2_kv_bridge). */
-} hs2_shape;          /* 56 bytes, no padding */
+  int32_t decode_splits;/* 0: the library's plan.  Otherwise the number of context splits
+                         per row of the decode full layer (clamped to 1 .. min(1024,
+                         ceil(ctx_len / 128))), e.g. to check that the results do not
+                         depend on the plan.  Ignored for a prefill chunk. */
+  int32_t reserved;   /* must be 0 */
+} hs2_shape;          /* 64 bytes, no padding */
 
 enum {
   HS2_OK = 0,
@@ -221,6 +226,28 @@ typedef struct hs2_bridge_shape {
 
 int hs2_kv_bridge(const hs2_bridge_shape* shape, const hs2_bf16* hidden, const hs2_bf16* w_kv,
                   hs2_bf16* k, hs2_bf16* v, void* stream);
+
+/* ---- Introspection (tests and diagnostics) ---------------------------------
+ * Where a named piece of the state that a step leaves in its workspace sits,
+ * for this shape and number of sparse layers: *offset (bytes from the start of
+ * ws) and *bytes.  The regions:
+ *   HS2_WS_LSE2  float64 [B][T][Hq]: each query head's base-2 log-normaliser,
+ *                log2 sum_j 2^(c2 s_j) with c2 = scale * log2(e) (the natural-log
+ *                lse divided by ln 2), as the selection ranks keys with it.
+ *                Valid after hs2_full_attn_scores or hs2_cross_decoder_step.
+ *   HS2_WS_REFINE uint32 [B*T*Hkv rows][4]: the refinement of that normaliser
+ *                over the keys that carry weight (see hs2_cross_decoder_step):
+ *                [0] dominant units summed again (decode: 16-key subtiles,
+ *                prefill chunk: keys), [1] decode subtiles whose recomputed
+ *                float32 maximum differed from the full layer's (expected 0),
+ *                [2] prefill dominant keys beyond the per-row list capacity
+ *                (not summed again; expected 0), [3] reserved.  Valid after
+ *                hs2_cross_decoder_step (and, in decode, hs2_full_attn_scores).
+ * Returns HS2_OK; HS2_ERR_INVALID_ARG for a null pointer or an unknown region;
+ * the status of hs2_workspace_bytes' checks for an invalid shape. */
+enum { HS2_WS_LSE2 = 1, HS2_WS_REFINE = 2 };
+int hs2_workspace_region(const hs2_shape* shape, int32_t n_sparse_layers, int32_t region,
+                         size_t* offset, size_t* bytes);
 
 /* Human-readable text for a status code (static storage). */
 const char* hs2_status_string(int status);

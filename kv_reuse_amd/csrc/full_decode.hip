@@ -43,6 +43,7 @@ constexpr int kWaves = 4;
 constexpr int kTile = 32;       // keys per wave iteration
 constexpr int kVPitch = 136;    // u16 per V row in LDS: 272 bytes
 constexpr int kStageKeys = 16384;  // splits up to this many keys stage their maxima in LDS
+constexpr int kSubTileKeys = 16;   // keys per stored maximum
 
 struct KVTile {
   bf16x8 ka[2][4];  // K as A operand: 2 sub-tiles of 16 keys x 4 chunks of 32 dims
@@ -215,7 +216,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void full_decode_split_kernel(
       t0 = t1;
     }
   }
-  st.l = sum_rows(st.l);
+  st.l = sum_rows_f64(st.l);
 
   __syncthreads();  // all waves done with their V tiles (and the stage)
   if (staged) {
@@ -356,56 +357,240 @@ __global__ __launch_bounds__(kCmbThreads) void full_combine_kernel(
   }
 }
 
-// Optional per-key importance for the caller (the step itself never needs all
-// of them): recompute the logits tile by tile on MFMA and write
-// max_h 2^(s2_h - lse2_h); entries past P are 0.  Reads K once more.
-__global__ __launch_bounds__(256) void full_scores_kernel(
-    const u16* __restrict__ q, const u16* __restrict__ k, const double* __restrict__ lse2,
-    float* __restrict__ scores, int64_t S, int kps, float c2_hi, float c2_lo, int64_t kvp) {
-  __shared__ float l2f[kG];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int col = lane & 15, grp = lane >> 4;
-  const int r = blockIdx.y;
-  const int64_t key_begin = static_cast<int64_t>(blockIdx.x) * kps;
-  const int64_t key_end = min(S, key_begin + kps);
-  if (threadIdx.x < kG)
-    l2f[threadIdx.x] = static_cast<float>(lse2[static_cast<size_t>(r) * kG + threadIdx.x]);
-  __syncthreads();
-  bf16x8 qb[4];
-  load_q_operand(q + static_cast<size_t>(r) * kG * kD, col, grp, qb);
-  const u16* kr = k + static_cast<size_t>(r) * kvp * kD;
-  float* sr = scores + static_cast<size_t>(r) * S;
-  for (int64_t t0 = key_begin + wave * kTile; t0 < key_end; t0 += 4 * kTile) {
-    bf16x8 ka[2][4];
+// ---------------------------------------------------------------- refinement of lse2
+//
+// lse2 above comes from float32 logits.  The bf16 MFMA's chained float32
+// accumulation errs by up to a few units of 2^-24 sum_d |q_d k_d| per logit,
+// and even a correctly rounded float32 logit of a large key is off by up to
+// 2^-25 |s|.  A key that carries a large share of a head's softmax passes its
+// logit error into lse2 at that share, and the selection's float64 ranking
+// would shift every importance of that head by it.  So the keys that carry
+// weight are summed again: for every subtile whose stored maximum reaches
+// 2^kDomLog2 of some head's normaliser, each of its keys' terms 2^(sv - lse2),
+// sv the very float32 logit the split kernel exponentiated, is replaced by
+// 2^(y - lse2), y the float64 logit of exact bf16 products.  sv is recomputed
+// by the split kernel's own MFMA sequence on the same operands, which gives
+// the same bits (the MFMA result of an element does not depend on where in the
+// tile it sits); the subtile maximum the split kernel stored is checked
+// against it, and a mismatch is counted.  What remains is the weighted mean of
+// the other keys' logit errors, each such key below 2^kDomLog2 of the total, in
+// which independent errors average out, and the float32 exponentials and
+// partial sums of the kept terms (a few units of 2^-24 of each).
+
+constexpr int kRefThreads = 256;
+constexpr int kRefWaves = kRefThreads / 64;
+
+// bf16 bits of a 16-byte group, element t, widened to float64 (exact)
+__device__ __forceinline__ double bf16_word_f64(const u32x4& raw, int t) {
+  const uint32_t word = raw[t >> 1];
+  return static_cast<double>(__uint_as_float((t & 1) ? (word & 0xFFFF0000u) : (word << 16)));
+}
+
+// float64 dot product of a query row (float64, LDS) and a bf16 key row (LDS):
+// the bf16 products are exact in float64
+__device__ __forceinline__ double dot_f64(const double* __restrict__ qh, const u16* __restrict__ krow) {
+  double dot = 0.0;
+#pragma unroll 4
+  for (int d8 = 0; d8 < kD / 8; ++d8) {
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(krow + 8 * d8);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      int64_t key = t0 + 16 * mt + col;
-      key = key < key_end - 1 ? key : key_end - 1;
+    for (int t = 0; t < 8; ++t) dot = fma(qh[8 * d8 + t], bf16_word_f64(raw, t), dot);
+  }
+  return dot;
+}
+
+// grid (ref chunks, R): work-group c of row r takes subtiles [c chunk, (c+1) chunk)
+// of the row's ceil(S/16), and writes its partial sums to part[r][c].
+__global__ __launch_bounds__(kRefThreads) void lse_refine_kernel(
+    const u16* __restrict__ q, const u16* __restrict__ k, const float* __restrict__ stmax,
+    const double* __restrict__ lse2, RefinePart* __restrict__ part, int64_t S, int64_t Spad,
+    int chunk, int n_chunks, float c2_hi, float c2_lo, double c2, int64_t kvp) {
+  __shared__ int32_t s_list[kRefThreads];
+  __shared__ uint32_t s_wcnt[kRefWaves];
+  __shared__ double s_q[kG * kD];                                  // the group's queries
+  __shared__ __align__(16) u16 s_k[kRefWaves][kSubTileKeys * kD];  // a wave's subtile of K rows
+  __shared__ float s_sv[kRefWaves][kSubTileKeys * kG];             // its float32 logits [key][head]
+  __shared__ double s_acc[kRefWaves][kG];
+  __shared__ uint32_t s_bad[kRefWaves];
+  const int r = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int64_t nst = (S + kSubTileKeys - 1) / kSubTileKeys;
+  const int64_t st0 = static_cast<int64_t>(blockIdx.x) * chunk;
+  const int64_t st1 = min(nst, st0 + chunk);
+  const u16* qr = q + static_cast<size_t>(r) * kG * kD;
+  const u16* kr = k + static_cast<size_t>(r) * kvp * kD;
+  const float* stmax_row = stmax + static_cast<size_t>(r) * (Spad / kSubTileKeys) * kG;
+  for (int i = tid; i < kG * kD; i += kRefThreads) s_q[i] = static_cast<double>(bf16_bits_to_f32(qr[i]));
+  // a subtile is dominant when its maximum for some head h reaches lse2_h + kDomLog2
+  float thr[kG];
+#pragma unroll
+  for (int h = 0; h < kG; ++h) thr[h] = static_cast<float>(lse2[static_cast<size_t>(r) * kG + h]) + kDomLog2;
+  // this lane's (key, head) pairs of a subtile: keys (lane >> 3) and 8 + (lane >> 3), head lane & 7
+  const int h_l = lane & 7;
+  const double l2h = lse2[static_cast<size_t>(r) * kG + h_l];
+  bf16x8 qb[4];
+  load_q_operand(qr, col, grp, qb);
+  double corr = 0.0;
+  uint32_t n_dom = 0, n_bad = 0;
+  __syncthreads();
+  for (int64_t sr0 = st0; sr0 < st1; sr0 += kRefThreads) {
+    const int64_t st = sr0 + tid;
+    bool dom = false;
+    if (st < st1) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(stmax_row + st * kG);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(stmax_row + st * kG + 4);
+      dom = a[0] >= thr[0] || a[1] >= thr[1] || a[2] >= thr[2] || a[3] >= thr[3] ||
+            b[0] >= thr[4] || b[1] >= thr[5] || b[2] >= thr[6] || b[3] >= thr[7];
+    }
+    // the round's dominant subtiles, ascending
+    const uint64_t bal = __ballot(dom);
+    if (lane == 0) s_wcnt[wave] = static_cast<uint32_t>(__popcll(bal));
+    __syncthreads();
+    uint32_t off = 0, tot = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < kRefWaves; ++w2) {
+      off += w2 < wave ? s_wcnt[w2] : 0u;
+      tot += s_wcnt[w2];
+    }
+    if (dom) s_list[off + __popcll(bal & ((1ull << lane) - 1ull))] = static_cast<int32_t>(st);
+    __syncthreads();
+    n_dom += tot;
+    for (uint32_t i = wave; i < tot; i += kRefWaves) {
+      const int32_t sti = s_list[i];
+      const int64_t key0 = static_cast<int64_t>(sti) * kSubTileKeys;
+      // the split kernel's operands and MFMA sequence for this subtile
+      bf16x8 ka[4];
+      {
+        const int64_t key = min(key0 + col, S - 1);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) ka[c] = as_bf16x8(load_u32x4(kr + key * kD + 8 * grp + 32 * c));
+      }
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc = mfma_16x16x32(ka[c], qb[c], acc);
+      float mx = -INFINITY;
+      float sv[4];
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const float a = acc[i4];
+        sv[i4] = key0 + 4 * grp + i4 < S ? fmaf(a, c2_hi, a * c2_lo) : -INFINITY;
+        mx = fmaxf(mx, sv[i4]);
+      }
+      mx = max_xor32(max_xor16(mx));
+      if (col < kG && grp == 0 && mx != stmax_row[static_cast<int64_t>(sti) * kG + col]) ++n_bad;
+      // the K rows and the logits, staged for the float64 pass
 #pragma unroll
       for (int c = 0; c < 4; ++c)
-        ka[mt][c] = as_bf16x8(load_u32x4(kr + key * kD + 8 * grp + 32 * c));
-    }
-    float sv[8];
-    tile_logits(ka, qb, t0, key_end, grp, c2_hi, c2_lo, sv);
-    // importance per key: max over the 8 real heads (lanes col 0..7 of a group)
-    float y[8];
+        *reinterpret_cast<bf16x8*>(s_k[wave] + col * kD + 32 * c + 8 * grp) = ka[c];
+      if (col < kG) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float yv = col < kG ? sv[e] - l2f[col] : -INFINITY;
-      yv = fmaxf(yv, __shfl_xor(yv, 1));
-      yv = fmaxf(yv, __shfl_xor(yv, 2));
-      yv = fmaxf(yv, __shfl_xor(yv, 4));
-      y[e] = yv;
-    }
-    if (col == 0) {
+        for (int i4 = 0; i4 < 4; ++i4) s_sv[wave][(4 * grp + i4) * kG + col] = sv[i4];
+      }
+      lds_fence_wave();
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t key = t0 + 16 * mt + 4 * grp + i;
-          if (key < key_end) sr[key] = exp2f(y[4 * mt + i]);
-        }
+      for (int u = 0; u < 2; ++u) {
+        const int e = (lane >> 3) + 8 * u;
+        const double dot = dot_f64(s_q + h_l * kD, s_k[wave] + e * kD);
+        if (key0 + e < S)
+          corr += exp2(c2 * dot - l2h) - exp2(static_cast<double>(s_sv[wave][e * kG + h_l]) - l2h);
+      }
+      lds_fence_wave();   // the stage is read before the next subtile overwrites it
     }
+    __syncthreads();      // s_list is rewritten by the next round
+  }
+  // per head: the lanes l with l & 7 = h, paired as a lane ^ 8, ^ 32, ^ 16 butterfly
+  corr += dpp_f64<0x128>(corr);   // row_ror:8, i.e. lane ^ 8 within the row of 16
+  corr = sum_rows_f64(corr);
+  n_bad = static_cast<uint32_t>(__popcll(__ballot(n_bad != 0)));   // lanes with a mismatch
+  if (lane < kG) s_acc[wave][lane] = corr;
+  if (lane == 0) s_bad[wave] = n_bad;
+  __syncthreads();
+  if (tid < kG) {
+    double c = 0.0;
+#pragma unroll
+    for (int w2 = 0; w2 < kRefWaves; ++w2) c += s_acc[w2][tid];
+    RefinePart* pr = part + static_cast<size_t>(r) * n_chunks + blockIdx.x;
+    pr->corr[tid] = c;
+    if (tid == 0) {
+      uint32_t nb = 0;
+#pragma unroll
+      for (int w2 = 0; w2 < kRefWaves; ++w2) nb += s_bad[w2];
+      pr->n_dom = n_dom;
+      pr->n_bad = nb;
+      pr->pad0 = 0u;
+      pr->pad1 = 0u;
+    }
+  }
+}
+
+// One wave per row: the chunks' partial sums in order, then lse2 += log2(1 +
+// sum), the natural-log lse for the caller and the head's importance bound.
+__global__ __launch_bounds__(64) void lse_finalize_kernel(
+    const RefinePart* __restrict__ part, int n_chunks, double* __restrict__ lse2,
+    float* __restrict__ lse_out, float* __restrict__ ytop_h, RefineStat* __restrict__ stat) {
+  const int r = blockIdx.x, lane = threadIdx.x;
+  const RefinePart* pr = part + static_cast<size_t>(r) * n_chunks;
+  if (lane < kG) {
+    double c = 0.0;
+    for (int i = 0; i < n_chunks; ++i) c += pr[i].corr[lane];
+    const double d = log1p(c) * M_LOG2E;
+    const size_t o = static_cast<size_t>(r) * kG + lane;
+    const double l2 = lse2[o] + d;
+    lse2[o] = l2;
+    if (lse_out) lse_out[o] = static_cast<float>(l2 * M_LN2);
+    ytop_h[o] = static_cast<float>(static_cast<double>(ytop_h[o]) - d);
+  }
+  if (lane == 0) {
+    uint32_t nd = 0, nb = 0;
+    for (int i = 0; i < n_chunks; ++i) {
+      nd += pr[i].n_dom;
+      nb += pr[i].n_bad;
+    }
+    stat[r] = RefineStat{nd, nb, 0u, 0u};
+  }
+}
+
+// Optional per-key importance for the caller (the step itself never needs all
+// of them): every key's importance max_h 2^(y_h - lse2_h), y the float64 logit
+// of exact bf16 products; one wave per subtile of 16 keys, lane (key, head)
+// pairs as in the refinement.  grid (splits, R) over the split kernel's key
+// ranges (multiples of 16 keys).
+__global__ __launch_bounds__(kRefThreads) void full_scores_kernel(
+    const u16* __restrict__ q, const u16* __restrict__ k, const double* __restrict__ lse2,
+    float* __restrict__ scores, int64_t S, int kps, double c2, int64_t kvp) {
+  __shared__ double s_q[kG * kD];
+  __shared__ __align__(16) u16 s_k[kRefWaves][kSubTileKeys * kD];
+  const int r = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int64_t key_begin = static_cast<int64_t>(blockIdx.x) * kps;
+  const int64_t key_end = min(S, key_begin + kps);
+  const u16* qr = q + static_cast<size_t>(r) * kG * kD;
+  const u16* kr = k + static_cast<size_t>(r) * kvp * kD;
+  float* sr = scores + static_cast<size_t>(r) * S;
+  for (int i = tid; i < kG * kD; i += kRefThreads) s_q[i] = static_cast<double>(bf16_bits_to_f32(qr[i]));
+  const int h_l = lane & 7;
+  const double l2h = lse2[static_cast<size_t>(r) * kG + h_l];
+  __syncthreads();
+  for (int64_t key0 = key_begin + kSubTileKeys * wave; key0 < key_end; key0 += kSubTileKeys * kRefWaves) {
+    const int64_t key = min(key0 + col, key_end - 1);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      *reinterpret_cast<u32x4*>(s_k[wave] + col * kD + 32 * c + 8 * grp) =
+          load_u32x4(kr + key * kD + 32 * c + 8 * grp);
+    lds_fence_wave();
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = (lane >> 3) + 8 * u;
+      double y = c2 * dot_f64(s_q + h_l * kD, s_k[wave] + e * kD) - l2h;
+      // the largest over the 8 heads: lanes 8 (lane >> 3) .. + 7
+      y = fmax(y, dpp_f64<0xB1>(y));    // lane ^ 1
+      y = fmax(y, dpp_f64<0x4E>(y));    // lane ^ 2
+      y = fmax(y, dpp_f64<0x141>(y));   // the other quad of the 8
+      if (h_l == 0 && key0 + e < key_end) sr[key0 + e] = static_cast<float>(exp2(y));
+    }
+    lds_fence_wave();
   }
 }
 
@@ -440,15 +625,32 @@ hipError_t launch_full_combine(const Plan& p, u16* out, float* lse, void* ws, hi
   return hipGetLastError();
 }
 
-hipError_t launch_full_scores(const Plan& p, const u16* q, const u16* k, float* scores,
-                              void* ws, hipStream_t st) {
+hipError_t launch_lse_refine(const Plan& p, const u16* q, const u16* k, float* lse, void* ws,
+                             hipStream_t st) {
   char* w = static_cast<char*>(ws);
   const double c2 = p.scale * 1.4426950408889634;
   const float c2_hi = static_cast<float>(c2);
   const float c2_lo = static_cast<float>(c2 - static_cast<double>(c2_hi));
-  hipLaunchKernelGGL(full_scores_kernel, dim3(p.n_split, p.R), dim3(256), 0, st, q, k,
-                     reinterpret_cast<const double*>(w + p.off_lse2), scores, p.S, p.kps, c2_hi,
-                     c2_lo, p.kvp);
+  hipLaunchKernelGGL(lse_refine_kernel, dim3(p.ref_nchunk, p.R), dim3(kRefThreads), 0, st, q, k,
+                     reinterpret_cast<const float*>(w + p.off_stmax),
+                     reinterpret_cast<const double*>(w + p.off_lse2),
+                     reinterpret_cast<RefinePart*>(w + p.off_ref_part), p.S, p.Spad, p.ref_chunk,
+                     p.ref_nchunk, c2_hi, c2_lo, c2, p.kvp);
+  hipLaunchKernelGGL(lse_finalize_kernel, dim3(p.R), dim3(64), 0, st,
+                     reinterpret_cast<const RefinePart*>(w + p.off_ref_part), p.ref_nchunk,
+                     reinterpret_cast<double*>(w + p.off_lse2), lse,
+                     reinterpret_cast<float*>(w + p.off_ytop),
+                     reinterpret_cast<RefineStat*>(w + p.off_ref_stat));
+  return hipGetLastError();
+}
+
+hipError_t launch_full_scores(const Plan& p, const u16* q, const u16* k, float* scores,
+                              void* ws, hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  const double c2 = p.scale * 1.4426950408889634;
+  hipLaunchKernelGGL(full_scores_kernel, dim3(p.n_split, p.R), dim3(kRefThreads), 0, st, q, k,
+                     reinterpret_cast<const double*>(w + p.off_lse2), scores, p.S, p.kps, c2,
+                     p.kvp);
   return hipGetLastError();
 }
 

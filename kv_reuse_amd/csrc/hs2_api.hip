@@ -7,19 +7,43 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "hs2_internal.h"
 
 namespace hs2 {
 namespace {
 
-static_assert(sizeof(hs2_shape) == 56, "hs2_shape layout is part of the ABI");
+static_assert(sizeof(hs2_shape) == 64, "hs2_shape layout is part of the ABI");
 static_assert(sizeof(hs2_bridge_shape) == 40, "hs2_bridge_shape layout is part of the ABI");
 
 thread_local int g_last_hip_error = 0;
 
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Compute units of the current device, read once per device (the decode full
+// layer is planned as one work-group per compute unit).  Without a device to
+// ask (a host-only process sizing a workspace) the MI355X's 256 are assumed.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return kDefaultCUs;
+  }
+  const int cached = g_cu_count[dev].load(std::memory_order_relaxed);
+  if (cached > 0) return cached;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    n = kDefaultCUs;
+  }
+  g_cu_count[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Validate a shape and lay out the workspace.  Returns HS2_OK or an error code.
@@ -27,7 +51,7 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
   if (!sh || !p) return HS2_ERR_INVALID_ARG;
   if (sh->ctx_len < 1 || sh->batch < 1 || sh->n_q_tokens < 1 || sh->n_q_heads < 1 ||
       sh->n_kv_heads < 1 || sh->head_dim < 1 || sh->top_k < 0 || sh->window < 0 ||
-      n_layers < 0)
+      n_layers < 0 || sh->decode_splits < 0 || sh->reserved != 0)
     return HS2_ERR_INVALID_ARG;
   const int32_t bs = sh->select_block;
   if (bs != 0) {
@@ -61,15 +85,18 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
   q.w = sh->window;
   q.cap = sh->top_k + sh->window;
   q.n_layers = n_layers;
+  q.n_cu = device_cu_count();
   q.scale = sh->scale;
 
   // full attention, decode: about one work-group per compute unit, so that
-  // the stream runs in one round with no tail (the 256 CUs of an MI355X; a
-  // count that leaves some CUs a second work-group streams much slower)
+  // the stream runs in one round with no tail (a count that leaves some CUs a
+  // second work-group streams much slower)
   {
-    const int64_t target = kSplitTarget;
+    const int64_t target = q.n_cu;
     int64_t ns = ceil_div(target, R);
     ns = std::max<int64_t>(1, std::min<int64_t>(ns, ceil_div(q.S, 256)));
+    if (sh->decode_splits > 0)   // the caller's split count
+      ns = std::max<int64_t>(1, std::min<int64_t>(sh->decode_splits, ceil_div(q.S, 128)));
     ns = std::min<int64_t>(ns, int64_t{kMaxSplits});
     int64_t kps = align_up(static_cast<size_t>(ceil_div(q.S, ns)), 128);
     q.kps = static_cast<int>(kps);
@@ -99,13 +126,22 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
     cc = std::max<int64_t>(cc, static_cast<int64_t>(align_up(static_cast<size_t>(ceil_div(nst, kMaxChunks)), kScoreRound)));
     q.cc_chunk = static_cast<int>(cc);
     q.cc_nchunk = static_cast<int>(ceil_div(nst, cc));
-    // scoring: about 768 work-groups (three per CU, all resident at once), each
+    // scoring: three work-groups per compute unit (all resident at once), each
     // taking an equal share of its row's candidate list, so that clustered
     // candidates do not queue on a few work-groups
-    int64_t ns = std::min<int64_t>(ceil_div(768, R), std::min<int64_t>(kMaxChunks, nst));
+    int64_t ns = std::min<int64_t>(ceil_div(3 * q.n_cu, R), std::min<int64_t>(kMaxChunks, nst));
     ns = std::max<int64_t>(ns, 1);
     q.sc_nchunk = static_cast<int>(ns);
     q.sc_chunk = static_cast<int>(ceil_div(nst, ns));   // list entries a region holds
+  }
+  // refinement of lse2 (decode): subtile chunks of at least 16, about 256
+  // work-groups over all rows
+  {
+    const int64_t nst_all = ceil_div(q.S, 16);
+    int64_t rc = align_up(static_cast<size_t>(ceil_div(nst_all * R, 256)), 16);
+    rc = std::max<int64_t>(rc, 16);
+    q.ref_chunk = static_cast<int>(rc);
+    q.ref_nchunk = static_cast<int>(ceil_div(nst_all, rc));
   }
   // sparse: slices of 128 keys over work-groups when rows are few
   q.sp_nch = (R >= 256) ? 1 : static_cast<int>(ceil_div(q.cap, kSparseChunk));
@@ -150,6 +186,10 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
   // per (batch, KV head, importance token block): that block's share of max |k|
   q.off_kmax = take(decode ? 0 : static_cast<size_t>(q.B) * q.Hkv *
                                       ceil_div(q.T, kImportanceTok) * sizeof(uint32_t));
+  q.off_ref_part = take(decode ? Rz * q.ref_nchunk * sizeof(RefinePart) : 0);
+  q.off_ref_stat = take(Rz * sizeof(RefineStat));
+  q.off_dom_cnt = take(decode ? 0 : Rz * sizeof(uint32_t));
+  q.off_dom_list = take(decode ? 0 : Rz * kDomCap * sizeof(int32_t));
   const size_t sp_parts = q.sp_nch > 1 ? Rz * q.sp_nch * n_layers * kG : 0;
   q.off_sp_m = take(sp_parts * sizeof(float));
   q.off_sp_l = take(sp_parts * sizeof(float));
@@ -185,6 +225,7 @@ int run_full(const Plan& p, const u16* q, const u16* k, const u16* v, u16* out, 
              void* ws, hipStream_t st) {
   HS2_TRY(launch_full_decode_split(p, q, k, v, ws, st));
   HS2_TRY(launch_full_combine(p, out, lse, ws, st));
+  HS2_TRY(launch_lse_refine(p, q, k, lse, ws, st));
   return HS2_OK;
 }
 
@@ -213,7 +254,7 @@ int hs2_full_attn_scores(const hs2_shape* shape, const hs2_bf16* q, const hs2_bf
   const hipStream_t s = as_stream(stream);
   if (p.T != 1) {
     HS2_TRY(launch_full_prefill(p, q, k, v, out, lse, ws, s));
-    if (scores) HS2_TRY(launch_prefill_importance(p, q, k, false, scores, ws, s));
+    if (scores) HS2_TRY(launch_prefill_scores(p, q, k, scores, s));
     return HS2_OK;
   }
   if ((st = run_full(p, q, k, v, out, lse, ws, s)) != HS2_OK) return st;
@@ -264,8 +305,9 @@ int hs2_cross_decoder_step(const hs2_shape* shape, int32_t n_sparse_layers,
   const hipStream_t s = as_stream(stream);
   if (p.T != 1) {
     HS2_TRY(launch_full_prefill(p, q_full, k, v, out_full, lse, ws, s));
-    HS2_TRY(launch_prefill_importance(p, q_full, k, true, scores, ws, s));
-    HS2_TRY(launch_prefill_select(p, q_full, k, idx, n_sel, ws, s));
+    HS2_TRY(launch_prefill_importance(p, q_full, k, ws, s));
+    HS2_TRY(launch_prefill_select(p, q_full, k, idx, n_sel, lse, ws, s));
+    if (scores) HS2_TRY(launch_prefill_scores(p, q_full, k, scores, s));
     if (n_sparse_layers > 0)
       HS2_TRY(launch_sparse(p, q_sparse, k, v, idx, n_sel, out_sparse, ws, s));
     return HS2_OK;
@@ -289,6 +331,7 @@ int hs2_cross_decoder_step_timed(const hs2_shape* shape, int32_t n_sparse_layers
   if (!q_full || !k || !v || !out_full || !idx || !n_sel || !phase_ms || iters < 1)
     return HS2_ERR_INVALID_ARG;
   if (n_sparse_layers > 0 && (!q_sparse || !out_sparse)) return HS2_ERR_INVALID_ARG;
+  if (p.T != 1 && p.bs != 0) return HS2_ERR_UNSUPPORTED;
   if ((st = check_ws(p, ws, ws_bytes)) != HS2_OK) return st;
   (void)hipGetLastError();
   const hipStream_t s = as_stream(stream);
@@ -311,11 +354,13 @@ int hs2_cross_decoder_step_timed(const hs2_shape* shape, int32_t n_sparse_layers
                              : launch_full_prefill(p, q_full, k, v, out_full, nullptr, ws, s));
     if (rc == HS2_OK) rc = hip_status(hipEventRecord(ev[1], s));
     if (rc == HS2_OK && decode) rc = hip_status(launch_full_combine(p, out_full, nullptr, ws, s));
+    if (rc == HS2_OK && decode) rc = hip_status(launch_lse_refine(p, q_full, k, nullptr, ws, s));
     if (rc == HS2_OK) rc = hip_status(hipEventRecord(ev[2], s));
     if (rc == HS2_OK)
       rc = hip_status(decode ? launch_fused_select(p, q_full, k, idx, n_sel, ws, s)
-                             : launch_prefill_importance(p, q_full, k, true, nullptr, ws, s));
-    if (rc == HS2_OK && !decode) rc = hip_status(launch_prefill_select(p, q_full, k, idx, n_sel, ws, s));
+                             : launch_prefill_importance(p, q_full, k, ws, s));
+    if (rc == HS2_OK && !decode)
+      rc = hip_status(launch_prefill_select(p, q_full, k, idx, n_sel, nullptr, ws, s));
     if (rc == HS2_OK) rc = hip_status(hipEventRecord(ev[3], s));
     if (rc == HS2_OK && n_sparse_layers > 0)
       rc = hip_status(launch_sparse(p, q_sparse, k, v, idx, n_sel, out_sparse, ws, s));
@@ -378,6 +423,26 @@ int hs2_sparse_attn_swa(const hs2_shape* shape, int32_t n_layers, const hs2_bf16
   HS2_TRY(launch_sparse(p, q, k, v, idx, n_sel, out, ws, as_stream(stream),
                         k_loc ? k_loc : &kNoRows, v_loc ? v_loc : &kNoRows));
   return HS2_OK;
+}
+
+int hs2_workspace_region(const hs2_shape* shape, int32_t n_sparse_layers, int32_t region,
+                         size_t* offset, size_t* bytes) {
+  Plan p;
+  const int st = make_plan(shape, n_sparse_layers, &p);
+  if (st != HS2_OK) return st;
+  if (!offset || !bytes) return HS2_ERR_INVALID_ARG;
+  switch (region) {
+    case HS2_WS_LSE2:
+      *offset = p.off_lse2;
+      *bytes = static_cast<size_t>(p.R) * kG * sizeof(double);
+      return HS2_OK;
+    case HS2_WS_REFINE:
+      *offset = p.off_ref_stat;
+      *bytes = static_cast<size_t>(p.R) * sizeof(RefineStat);
+      return HS2_OK;
+    default:
+      return HS2_ERR_INVALID_ARG;
+  }
 }
 
 const char* hs2_status_string(int status) {

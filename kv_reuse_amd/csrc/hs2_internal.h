@@ -21,7 +21,16 @@ constexpr float kYRange = 64.0f;   // log2 range below the row's top score that 
 constexpr int kYFixBits = 10;      // prefill importance: fixed point, 2^-10 log2 units per step
 constexpr int kImportanceTok = 64;  // prefill importance pass: chunk tokens per work-group
 constexpr int kMaxSplits = 1024;   // context splits per row (full layer, decode)
-constexpr int kSplitTarget = 256;  // decode full layer: work-groups over all rows (MI355X CUs)
+constexpr int kDefaultCUs = 256;   // compute units assumed when no device can be queried
+// Refinement of the log-normaliser: a key is dominant for head h when its
+// probability under h is at least 2^kDomLog2 (decode, by 16-key subtiles) or
+// 2^kDomLog2Chunk (prefill chunk, by keys); such keys' terms are summed again
+// from exact float64 logits.  A head has at most 2^8 keys of weight 2^-8 or
+// more, so a prefill row has at most 8 * 2^8 dominant keys: the list capacity
+// covers them with room for float32 rounding at the cut.
+constexpr float kDomLog2 = -12.0f;
+constexpr float kDomLog2Chunk = -8.0f;
+constexpr int kDomCap = 2304;      // dominant keys listed per prefill row
 
 typedef unsigned short u16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -37,6 +46,19 @@ struct RowInfo {
   uint32_t up_count;    // entries above the band appended to the selection
   uint32_t pad;
 };
+// Per-(row, chunk) result of the decode refinement: each head's relative
+// change of its softmax denominator, the dominant subtiles seen and the
+// subtiles whose recomputed float32 maximum differed from the stored one.
+struct RefinePart {
+  double corr[8];
+  uint32_t n_dom, n_bad, pad0, pad1;
+};
+// Per-row statistics of the refinement (HS2_WS_REFINE): dominant units (decode:
+// subtiles, prefill: keys), float32 replica mismatches (decode), dominant keys
+// beyond the list capacity (prefill), reserved.
+struct RefineStat {
+  uint32_t n_dom, n_bad, n_over, pad;
+};
 constexpr int kScoreRound = 256;   // subtiles scored per round of a work-group
 constexpr int kMaxChunks = 4096;   // candidate chunks per row
 constexpr int64_t kPrefillBandCap = 8192;  // near-threshold keys listed per prefill row
@@ -49,6 +71,7 @@ struct Plan {
   int B, T, Hq, Hkv, R;      // R = B*T*Hkv rows
   int k, w, cap;             // cap = k + w (index list capacity per row)
   int n_layers;
+  int n_cu;                  // compute units of the current device (work-group targets)
   double scale;
   // full attention (decode split kernel) and the merge of its splits
   int n_split, kps;
@@ -64,6 +87,10 @@ struct Plan {
   size_t off_clist, off_ccnt, off_lo;
   int sc_chunk, sc_nchunk;   // scoring: list entries per work-group region, work-groups per row
   size_t off_hist_c, off_cand_y, off_cand_idx, off_cand_cnt, off_band_idx, off_band_key;
+  // refinement of lse2 over the dominant keys: decode per-(row, chunk) partial
+  // sums (RefinePart); prefill per-row dominant-key lists; per-row statistics
+  int ref_chunk, ref_nchunk;
+  size_t off_ref_part, off_ref_stat, off_dom_cnt, off_dom_list;
   // prefill chunk: per-row log2 importance of the older keys (16-bit fixed point), band capacity per row
   size_t off_ybuf;
   size_t off_kmax;           // prefill: largest |k| (bf16 bits) per (batch, KV head)
@@ -101,6 +128,10 @@ hipError_t launch_kv_bridge(const BridgeArgs& a, hipStream_t st);
 // Per-key importance [R][S] (float32), recomputed from q, k and lse2.
 hipError_t launch_full_scores(const Plan& p, const u16* q, const u16* k, float* scores,
                               void* ws, hipStream_t st);
+// Refinement of lse2 over the dominant keys (decode): partial sums per chunk,
+// then the per-row update of lse2, lse (nullable) and the importance bound.
+hipError_t launch_lse_refine(const Plan& p, const u16* q, const u16* k, float* lse, void* ws,
+                             hipStream_t st);
 // Selection from given float32 scores, compared exactly.
 hipError_t launch_scores_select(const Plan& p, const float* scores, int32_t* idx,
                                 int32_t* n_sel, void* ws, hipStream_t st);
@@ -113,13 +144,18 @@ hipError_t launch_fused_select(const Plan& p, const u16* q, const u16* k, int32_
 // out, lse (nullable), lse2 and each head's bound on log2 importance.
 hipError_t launch_full_prefill(const Plan& p, const u16* q, const u16* k, const u16* v, u16* out,
                                float* lse, void* ws, hipStream_t st);
-// Prefill chunk importance: for the selection (per-row y and histogram in the
-// workspace) and/or dense scores for the caller (nullable).
-hipError_t launch_prefill_importance(const Plan& p, const u16* q, const u16* k, bool for_select,
-                                     float* scores, void* ws, hipStream_t st);
-// Prefill chunk selection: one work-group per row.
+// Prefill chunk importance for the selection: per-row fixed-point y, each KV
+// head's largest |k| and each row's dominant keys, in the workspace.
+hipError_t launch_prefill_importance(const Plan& p, const u16* q, const u16* k, void* ws,
+                                     hipStream_t st);
+// Dense importance [R][S] of a prefill chunk for the caller, from float64
+// logits and an exactly recomputed normaliser (no workspace).
+hipError_t launch_prefill_scores(const Plan& p, const u16* q, const u16* k, float* scores,
+                                 hipStream_t st);
+// Prefill chunk selection: one work-group per row.  It first refines lse2
+// over the row's dominant keys (and writes lse, when non-null, from it).
 hipError_t launch_prefill_select(const Plan& p, const u16* q, const u16* k, int32_t* idx,
-                                 int32_t* n_sel, void* ws, hipStream_t st);
+                                 int32_t* n_sel, float* lse, void* ws, hipStream_t st);
 
 // Sparse layers (all n_layers fused: one gather of the selected K/V rows).
 hipError_t launch_sparse(const Plan& p, const u16* q, const u16* k, const u16* v,

@@ -332,7 +332,6 @@ __global__ __launch_bounds__(kPThreads, QB <= 2 ? 2 : 1) void full_prefill_kerne
 //               round((y - ybase) 2^10) clamped to 0..65535, with ybase the
 //               row's top log-weight (over its 8 heads) minus 64 (when y is
 //               non-null);
-//   scores[row][j] = 2^y for all j <= P_t, 0 above (when scores is non-null);
 //   kmax[b][g][tb] = the largest |k| over this work-group's share of the KV
 //               head's keys 0..S-1 (bf16 bits; when kmax is non-null): whole
 //               key tile i belongs to token block i % n_tblk when that block
@@ -364,14 +363,14 @@ __device__ __forceinline__ void phase_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <bool kScores>
 __global__ __launch_bounds__(kIThreads, 1) void prefill_importance_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const double* __restrict__ lse2,
     const float* __restrict__ ytop_h, u16* __restrict__ y, uint32_t* __restrict__ kmax,
-    float* __restrict__ scores, int64_t S, int64_t Spad, int T, int Hkv, int w, int n_tblk,
-    float c2_hi, int64_t kvp) {
+    uint32_t* __restrict__ dom_cnt, int32_t* __restrict__ dom_list,
+    int64_t S, int64_t Spad, int T, int Hkv, int w, int n_tblk, float c2_hi, int64_t kvp) {
   __shared__ __align__(16) u16 kbuf[2][kPKeys * kD];
   __shared__ uint32_t s_kmax[kIWaves];
+  __shared__ uint32_t s_dom[kImportanceTok];   // dominant keys found per token of the block
   constexpr int QB = kIQB;
   constexpr int kTok = kImportanceTok;
   const int tid = threadIdx.x;
@@ -393,9 +392,10 @@ __global__ __launch_bounds__(kIThreads, 1) void prefill_importance_kernel(
   // y in fixed-point steps plus 0.5 is s c2 2^10 + (0.5 - 2^10 (lse2_h + ybase)):
   // one fma per head
   float nl2r[QB][4];     // 0.5 - 2^10 (lse2_h + ybase) for the lane's 4 heads
-  float yb[QB];          // ybase - 2^-11: y = v 2^-10 + yb
+  float ydom[QB];        // the fixed-point value (plus 0.5) of y = kDomLog2
+  int tloc[QB];          // the lane's token within the block
+  size_t rowi[QB];
   u16* yrow[QB];
-  float* srow[QB];
 #pragma unroll
   for (int qbk = 0; qbk < QB; ++qbk) {
     // the A operand: query row col = (token .. + (col >> 3), head col & 7)
@@ -419,9 +419,10 @@ __global__ __launch_bounds__(kIThreads, 1) void prefill_importance_kernel(
     for (int i = 0; i < 4; ++i)
       nl2r[qbk][i] = fmaf(-static_cast<float>(lse2[row * kG + 4 * (grp & 1) + i]),
                           static_cast<float>(1 << kYFixBits), yoff);
-    yb[qbk] = ybase - 1.0f / (2 << kYFixBits);
+    ydom[qbk] = (kDomLog2Chunk - ybase) * static_cast<float>(1 << kYFixBits) + 0.5f;
+    tloc[qbk] = t - tb * kTok;
+    rowi[qbk] = row;
     yrow[qbk] = y ? y + row * Spad : nullptr;
-    srow[qbk] = scores ? scores + row * S : nullptr;
   }
   const int t_last = min(T - 1, tb * kTok + kTok - 1);
   const int64_t p_last = pos0 + t_last;
@@ -462,6 +463,7 @@ __global__ __launch_bounds__(kIThreads, 1) void prefill_importance_kernel(
     }
   };
 
+  if (tid < kTok) s_dom[tid] = 0u;
   // prologue: tile 0 by every wave; group B loads its rows of tile 1 in the
   // phase it spends behind group A
   stage_load(0);
@@ -515,16 +517,18 @@ __global__ __launch_bounds__(kIThreads, 1) void prefill_importance_kernel(
         const int64_t key = key0 + 16 * sub + col;
         // clamp to 0..65535, then truncate: rounds to nearest
         const u16 v = static_cast<u16>(static_cast<uint32_t>(__builtin_amdgcn_fmed3f(yy, 0.f, 65535.f)));
-        if constexpr (kScores) {
-          if (!t_ok[qbk] || key > P[qbk]) continue;
-          srow[qbk][key] = __builtin_amdgcn_exp2f(fmaf(yy, 1.0f / (1 << kYFixBits), yb[qbk]));
-          if (key < first[qbk] && yrow[qbk]) yrow[qbk][key] = v;
-        } else {
-          // every lane stores (a fixed count of stores per phase, so the
-          // tile loads can be waited for alone): keys at or past first_t
-          // land in the row's unread tail (key < Spad), and a block past
-          // the chunk's end repeats the last token, value for value
-          yrow[qbk][key] = v;
+        // every lane stores (a fixed count of stores per phase, so the
+        // tile loads can be waited for alone): keys at or past first_t
+        // land in the row's unread tail (key < Spad), and a block past
+        // the chunk's end repeats the last token, value for value
+        yrow[qbk][key] = v;
+        // a key that some head weights by 2^kDomLog2Chunk or more (window keys
+        // included): listed for the refinement of lse2 (rare; the block's
+        // token counters are in LDS)
+        if (dom_list && t_ok[qbk] && key <= P[qbk] && yy >= ydom[qbk]) {
+          const uint32_t slot = atomicAdd(&s_dom[tloc[qbk]], 1u);
+          if (slot < static_cast<uint32_t>(kDomCap))
+            dom_list[rowi[qbk] * kDomCap + slot] = static_cast<int32_t>(key);
         }
       }
     }
@@ -569,6 +573,12 @@ __global__ __launch_bounds__(kIThreads, 1) void prefill_importance_kernel(
     epilogue(sacc, static_cast<int64_t>(n_tiles - 1) * kPKeys);
     phase_barrier();
   }
+  if (dom_cnt) {
+    __syncthreads();   // every listing is done
+    const int tt = tb * kTok + tid;
+    if (tid < kTok && tt < T)
+      dom_cnt[(static_cast<size_t>(b) * T + tt) * Hkv + g] = s_dom[tid];
+  }
   if (kmax) {
     uint32_t m = max(static_cast<uint32_t>(kabs[0]), static_cast<uint32_t>(kabs[1]));
 #pragma unroll
@@ -580,15 +590,119 @@ __global__ __launch_bounds__(kIThreads, 1) void prefill_importance_kernel(
       kmax[static_cast<size_t>(bg) * n_tblk + tb] = m;
     }
   }
-  // scores past P_t are 0
-  if (kScores) {
-    for (int j = 0; j < kTok; ++j) {
-      const int tt = tb * kTok + j;
-      if (tt >= T) break;
-      float* sr = scores + ((static_cast<size_t>(b) * T + tt) * Hkv + g) * S;
-      for (int64_t key = pos0 + tt + 1 + tid; key < S; key += kIThreads) sr[key] = 0.f;
+}
+
+// Dense importance of a chunk for the caller (an optional output: the step
+// itself never needs it), exactly: one work-group per row (b, t, g), the
+// logits of keys 0..P_t in float64 from exact bf16 products, a first pass for
+// each head's log-normaliser (an online max and sum in float64, combined in a
+// fixed order), a second for max_h 2^(y_h - lse2_h); keys past P_t get 0.
+constexpr int kXThreads = 256;
+constexpr int kXWaves = kXThreads / 64;
+
+__device__ __forceinline__ double dot_row_f64(const double* __restrict__ qh, const u16* __restrict__ krow) {
+  double dot = 0.0;
+#pragma unroll 4
+  for (int d8 = 0; d8 < kD / 8; ++d8) {
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(krow + 8 * d8);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t word = raw[t >> 1];
+      dot = fma(qh[8 * d8 + t],
+                static_cast<double>(__uint_as_float((t & 1) ? (word & 0xFFFF0000u) : (word << 16))), dot);
     }
   }
+  return dot;
+}
+
+__global__ __launch_bounds__(kXThreads) void prefill_scores_kernel(
+    const u16* __restrict__ q, const u16* __restrict__ k, float* __restrict__ scores, int64_t S,
+    int T, int Hkv, double c2, int64_t kvp) {
+  __shared__ double s_q[kG * kD];
+  __shared__ __align__(16) u16 s_k[kXWaves][16 * kD];
+  __shared__ double s_m[kXWaves][kG], s_l[kXWaves][kG];
+  __shared__ double s_l2[kG];
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int t = (r / Hkv) % T, g = r % Hkv, b = r / (T * Hkv);
+  const int64_t P = S - T + t;
+  const u16* qr = q + static_cast<size_t>(r) * kG * kD;
+  const u16* kr = k + (static_cast<size_t>(b) * Hkv + g) * static_cast<size_t>(kvp) * kD;
+  float* sr = scores + static_cast<size_t>(r) * S;
+  for (int i = tid; i < kG * kD; i += kXThreads) s_q[i] = static_cast<double>(bf16_bits_to_f32(qr[i]));
+  __syncthreads();
+  // lane (key e = (lane >> 3) + 8 u, head h = lane & 7) of each 16-key subtile
+  const int h_l = lane & 7;
+  const double* qh = s_q + h_l * kD;
+  auto stage = [&](int64_t key0) {
+    const int64_t key = min(key0 + col, P);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      *reinterpret_cast<u32x4*>(s_k[wave] + col * kD + 32 * c + 8 * grp) =
+          load_u32x4(kr + key * kD + 32 * c + 8 * grp);
+    lds_fence_wave();
+  };
+  double m = -INFINITY, l = 0.0;
+  for (int64_t key0 = 16 * wave; key0 <= P; key0 += 16 * kXWaves) {
+    stage(key0);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = (lane >> 3) + 8 * u;
+      if (key0 + e > P) continue;
+      const double y = c2 * dot_row_f64(qh, s_k[wave] + e * kD);
+      if (y > m) {
+        l = l * exp2(m - y) + 1.0;
+        m = y;
+      } else {
+        l += exp2(y - m);
+      }
+    }
+    lds_fence_wave();
+  }
+  // each head over the lanes l with l & 7 = h (lane ^ 8, ^ 16, ^ 32), then the waves
+  auto merge = [](double& m1, double& l1, double m2, double l2) {
+    const double mm = fmax(m1, m2);
+    if (mm == -INFINITY) return;
+    l1 = (m1 == -INFINITY ? 0.0 : l1 * exp2(m1 - mm)) + (m2 == -INFINITY ? 0.0 : l2 * exp2(m2 - mm));
+    m1 = mm;
+  };
+  {
+    double m2 = dpp_f64<0x128>(m), l2 = dpp_f64<0x128>(l);   // lane ^ 8
+    merge(m, l, m2, l2);
+    m2 = __shfl_xor(m, 16);
+    l2 = __shfl_xor(l, 16);
+    merge(m, l, m2, l2);
+    m2 = __shfl_xor(m, 32);
+    l2 = __shfl_xor(l, 32);
+    merge(m, l, m2, l2);
+  }
+  if (lane < kG) {
+    s_m[wave][lane] = m;
+    s_l[wave][lane] = l;
+  }
+  __syncthreads();
+  if (tid < kG) {
+    double mm = s_m[0][tid], ll = s_l[0][tid];
+    for (int w2 = 1; w2 < kXWaves; ++w2) merge(mm, ll, s_m[w2][tid], s_l[w2][tid]);
+    s_l2[tid] = mm + log2(ll);
+  }
+  __syncthreads();
+  const double l2h = s_l2[h_l];
+  for (int64_t key0 = 16 * wave; key0 <= P; key0 += 16 * kXWaves) {
+    stage(key0);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = (lane >> 3) + 8 * u;
+      double y = c2 * dot_row_f64(qh, s_k[wave] + e * kD) - l2h;
+      y = fmax(y, dpp_f64<0xB1>(y));    // lane ^ 1
+      y = fmax(y, dpp_f64<0x4E>(y));    // lane ^ 2
+      y = fmax(y, dpp_f64<0x141>(y));   // the other quad of the 8
+      if (h_l == 0 && key0 + e <= P) sr[key0 + e] = static_cast<float>(exp2(y));
+    }
+    lds_fence_wave();
+  }
+  for (int64_t key = P + 1 + tid; key < S; key += kXThreads) sr[key] = 0.f;
 }
 
 }  // namespace
@@ -609,26 +723,29 @@ hipError_t launch_full_prefill(const Plan& p, const u16* q, const u16* k, const 
   return hipGetLastError();
 }
 
-hipError_t launch_prefill_importance(const Plan& p, const u16* q, const u16* k, bool for_select,
-                                     float* scores, void* ws, hipStream_t st) {
+hipError_t launch_prefill_importance(const Plan& p, const u16* q, const u16* k, void* ws,
+                                     hipStream_t st) {
   char* w = static_cast<char*>(ws);
   const double c2 = p.scale * 1.4426950408889634;
   const float c2_hi = static_cast<float>(c2);
   const int n_tblk = (p.T + kImportanceTok - 1) / kImportanceTok;
   const int n_wg = p.B * p.Hkv * n_tblk;
-  u16* y = for_select ? reinterpret_cast<u16*>(w + p.off_ybuf) : nullptr;
-  uint32_t* kmax = for_select ? reinterpret_cast<uint32_t*>(w + p.off_kmax) : nullptr;
-  if (!for_select && !scores) return hipSuccess;
-  if (scores)
-    hipLaunchKernelGGL(prefill_importance_kernel<true>, dim3(n_wg), dim3(kIThreads), 0, st, q, k,
-                       reinterpret_cast<const double*>(w + p.off_lse2),
-                       reinterpret_cast<const float*>(w + p.off_ytop), y, kmax, scores, p.S, p.Spad,
-                       p.T, p.Hkv, p.w, n_tblk, c2_hi, p.kvp);
-  else
-    hipLaunchKernelGGL(prefill_importance_kernel<false>, dim3(n_wg), dim3(kIThreads), 0, st, q, k,
-                       reinterpret_cast<const double*>(w + p.off_lse2),
-                       reinterpret_cast<const float*>(w + p.off_ytop), y, kmax, nullptr, p.S,
-                       p.Spad, p.T, p.Hkv, p.w, n_tblk, c2_hi, p.kvp);
+  hipLaunchKernelGGL(prefill_importance_kernel, dim3(n_wg), dim3(kIThreads), 0, st, q, k,
+                     reinterpret_cast<const double*>(w + p.off_lse2),
+                     reinterpret_cast<const float*>(w + p.off_ytop),
+                     reinterpret_cast<u16*>(w + p.off_ybuf),
+                     reinterpret_cast<uint32_t*>(w + p.off_kmax),
+                     reinterpret_cast<uint32_t*>(w + p.off_dom_cnt),
+                     reinterpret_cast<int32_t*>(w + p.off_dom_list), p.S, p.Spad, p.T, p.Hkv, p.w,
+                     n_tblk, c2_hi, p.kvp);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_scores(const Plan& p, const u16* q, const u16* k, float* scores,
+                                 hipStream_t st) {
+  const double c2 = p.scale * 1.4426950408889634;
+  hipLaunchKernelGGL(prefill_scores_kernel, dim3(p.R), dim3(kXThreads), 0, st, q, k, scores, p.S,
+                     p.T, p.Hkv, c2, p.kvp);
   return hipGetLastError();
 }
 

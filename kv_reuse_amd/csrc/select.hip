@@ -1636,11 +1636,12 @@ __device__ __forceinline__ uint32_t u16_at(const u32x4 (&v)[2], int e) {
 
 __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
     const u16* __restrict__ ybuf, const uint32_t* __restrict__ kmax, int n_ib,
-    const double* __restrict__ lse2,
+    double* __restrict__ lse2, float* __restrict__ lse_out, const uint32_t* __restrict__ dom_cnt,
+    const int32_t* __restrict__ dom_list, RefineStat* __restrict__ stat,
     const u16* __restrict__ q, const u16* __restrict__ k, int32_t* __restrict__ band_idx,
     uint64_t* __restrict__ band_key, int64_t band_cap, int32_t* __restrict__ idx_out,
     int32_t* __restrict__ nsel_out, int64_t S, int64_t Spad, int T, int Hkv, int topk, int w,
-    int cap, double c2, int64_t kvp) {
+    int cap, double c2, float c2_hi, int64_t kvp) {
   __shared__ __align__(16) int32_t up[kMaxSel];
   __shared__ __align__(16) int32_t bw[kMaxSel];        // band winners; first the histogram
   // the list's indices; after the split, the band (keys, then indices); the
@@ -1648,6 +1649,7 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
   __shared__ __align__(16) uint32_t pool[kPList];
   __shared__ double qd[kG * kD];
   __shared__ double l2s[kG];
+  __shared__ double s_dl2[kG];
   __shared__ float s_qn[2][kRowThreads / 64];
   __shared__ uint32_t h256[256];
   __shared__ uint32_t s_red[4];
@@ -1674,6 +1676,104 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
   const int b = r / (T * Hkv);
   const int g = r % Hkv;
   int32_t* out = idx_out + static_cast<size_t>(r) * cap;
+  const u16* qr = q + static_cast<size_t>(r) * kG * kD;
+  const u16* kr = k + (static_cast<size_t>(b) * Hkv + g) * static_cast<size_t>(kvp) * kD;
+  // ---- refinement of lse2 over the row's dominant keys (listed by the
+  // importance pass: some head gives them at least 2^kDomLog2Chunk of its
+  // weight).  The attention kernel summed 2^(a c2_hi - m) for each key, a the
+  // float32 MFMA logit; each listed key's term is replaced by the one of its
+  // float64 logit from exact bf16 products.  a is recomputed by the attention
+  // kernel's MFMA sequence on the same operands (same bits wherever the
+  // element sits in the tile).  The other keys, each below 2^kDomLog2Chunk of
+  // the total, keep their float32 terms: their independent logit errors
+  // average out in the weighted sum.
+  {
+    constexpr int kE = kMaxSel / kRowThreads;            // sort slots per thread
+    static_assert(kDomCap <= kMaxSel, "the list sorts in one block sort");
+    for (int i = tid; i < kG * kD; i += kRowThreads)
+      qd[i] = static_cast<double>(bf16_bits_to_f32(qr[i]));
+    const uint32_t n_raw = dom_cnt[r];
+    const uint32_t n_dom = min(n_raw, static_cast<uint32_t>(kDomCap));
+    int32_t* dk = up;                                     // the list, ascending
+    double* gsum = reinterpret_cast<double*>(pool);       // [group of 16 keys][kG]
+    if (tid < kG) l2s[tid] = lse2[static_cast<size_t>(r) * kG + tid];
+    // ascending key order (the keys are distinct), so the sums below have a
+    // fixed order
+    {
+      int32_t v[kE];
+#pragma unroll
+      for (int e = 0; e < kE; ++e) {
+        const uint32_t ii = static_cast<uint32_t>(kE * tid + e);
+        v[e] = ii < n_dom ? dom_list[static_cast<size_t>(r) * kDomCap + ii] : 0x7FFFFFFF;
+      }
+      if (n_dom > 1) block_bitonic<kE>(v, bw, static_cast<int>(n_dom), IntLess{});
+#pragma unroll
+      for (int e = 0; e < kE; ++e) {
+        const uint32_t ii = static_cast<uint32_t>(kE * tid + e);
+        if (ii < n_dom) dk[ii] = v[e];
+      }
+    }
+    __syncthreads();
+    const int col = lane & 15, grp = lane >> 4;
+    const uint32_t n_grp = (n_dom + 15) / 16;
+    for (uint32_t gi = wave; gi < n_grp; gi += kRowThreads / 64) {
+      // 16 keys as the A operand rows, the 8 heads as B columns (8 .. 15 zero)
+      const int32_t key = dk[min(16 * gi + col, n_dom - 1)];
+      bf16x8 ka[4], qb[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        ka[c] = as_bf16x8(load_u32x4(kr + static_cast<size_t>(key) * kD + 32 * c + 8 * grp));
+        qb[c] = col < kG ? as_bf16x8(load_u32x4(qr + col * kD + 32 * c + 8 * grp))
+                         : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+      }
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc = mfma_16x16x32(ka[c], qb[c], acc);
+      // lane (head col, grp) holds keys 16 gi + 4 grp + i: its four terms in
+      // key order, then the group's sum over grp in a fixed pairing
+      double part = 0.0;
+      if (col < kG) {
+        const double l2h = l2s[col];
+        const double* qh = qd + col * kD;
+#pragma unroll 1
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t e = 16 * gi + 4 * grp + i;
+          if (e >= n_dom) break;
+          const u16* krow = kr + static_cast<size_t>(dk[e]) * kD;
+          double dot = 0.0;
+#pragma unroll 2
+          for (int d8 = 0; d8 < kD / 8; ++d8) {
+            const u32x4 raw = load_u32x4(krow + 8 * d8);
+#pragma unroll
+            for (int t2 = 0; t2 < 8; ++t2) {
+              const uint32_t word = raw[t2 >> 1];
+              dot = fma(qh[8 * d8 + t2],
+                        static_cast<double>(__uint_as_float((t2 & 1) ? (word & 0xFFFF0000u) : (word << 16))),
+                        dot);
+            }
+          }
+          const double a2 = static_cast<double>(acc[i]) * static_cast<double>(c2_hi);   // exact
+          part += exp2(c2 * dot - l2h) - exp2(a2 - l2h);
+        }
+      }
+      part += __shfl_xor(part, 16);
+      part += __shfl_xor(part, 32);
+      if (grp == 0 && col < kG) gsum[gi * kG + col] = part;
+    }
+    __syncthreads();
+    if (tid < kG) {
+      double c = 0.0;
+      for (uint32_t gi = 0; gi < n_grp; ++gi) c += gsum[gi * kG + tid];
+      const double d = log1p(c) * M_LOG2E;
+      const double l2 = l2s[tid] + d;
+      l2s[tid] = l2;
+      s_dl2[tid] = d;
+      lse2[static_cast<size_t>(r) * kG + tid] = l2;
+      if (lse_out) lse_out[static_cast<size_t>(r) * kG + tid] = static_cast<float>(l2 * M_LN2);
+    }
+    if (tid == 0) stat[r] = RefineStat{n_dom, 0u, n_raw - n_dom, 0u};
+    __syncthreads();
+  }
   uint32_t n_keep = 0;
   if (topk > 0 && first > 0) {
     for (int i = tid; i < kPNB; i += kRowThreads) lh[i] = 0u;
@@ -1690,17 +1790,14 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
       m = wave_umax(m);
       if (lane == 0 && m) atomicMax(&s_km, m);
     }
-    const u16* qr = q + static_cast<size_t>(r) * kG * kD;
-    // q in float64, and each head's sum of |q| (thread t holds elements t and
-    // t + 512: heads wave / 2 and 4 + wave / 2)
+    // each head's sum of |q| (thread t holds elements t and t + 512: heads
+    // wave / 2 and 4 + wave / 2)
     {
       float qa[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int i = tid + u * kRowThreads;
-        const float x = bf16_bits_to_f32(qr[i]);
-        qd[i] = static_cast<double>(x);
-        qa[u] = fabsf(x);
+        qa[u] = fabsf(bf16_bits_to_f32(qr[i]));
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u)
@@ -1711,7 +1808,6 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
         s_qn[1][wave] = qa[1];
       }
     }
-    if (tid < kG) l2s[tid] = lse2[static_cast<size_t>(r) * kG + tid];
     __syncthreads();
     if (tid == 0) {
       // E: twice the largest |stored - exact| in steps of 2^-10 octave, plus
@@ -1723,16 +1819,20 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
       // additions of exact bf16 products, the scale's dropped low part and
       // the fma each cost 2^-24 of |s| c2 <= max|k| sum|q_h| c2; lse2's
       // rounding to float32 costs 2^-24 |lse2|, counted twice.
-      double qn = 0.0, l2m = 0.0;
+      double qn = 0.0, l2m = 0.0, dl2 = 0.0;
       for (int h = 0; h < kG; ++h) {
         const int wv = 2 * (h & 3);
         const int u = h >> 2;
         qn = fmax(qn, static_cast<double>(s_qn[u][wv]) + static_cast<double>(s_qn[u][wv + 1]));
         l2m = fmax(l2m, fabs(l2s[h]));
+        dl2 = fmax(dl2, fabs(s_dl2[h]));
       }
       const double km = static_cast<double>(bf16_bits_to_f32(static_cast<u16>(s_km)));
-      // sum|q| was taken in float32: allow 2^-20 relative for its rounding
-      const double d32 = 0x1p-24 * (130.0 * km * qn * (1.0 + 0x1p-20) * c2 + 2.0 * l2m);
+      // sum|q| was taken in float32: allow 2^-20 relative for its rounding.
+      // The stored values were formed with lse2 before its refinement: the
+      // refinement's change dl2 adds to their error against the exact
+      // importance ranked here.
+      const double d32 = 0x1p-24 * (130.0 * km * qn * (1.0 + 0x1p-20) * c2 + 2.0 * l2m) + dl2;
       const double steps = 1.5 + 0x1p-5 + d32 * static_cast<double>(1 << kYFixBits);
       s_E = static_cast<int>(fmin(ceil(2.0 * steps) + 1.0, 65536.0));
     }
@@ -1943,7 +2043,6 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
         // ---- exact importance of the band keys in float64 (bf16 products are
         // exact): 16 lanes per key, lane j of a group taking dims 8j..8j+7 of
         // all 8 heads, then a sum over the group
-        const u16* kr = k + (static_cast<size_t>(b) * Hkv + g) * static_cast<size_t>(kvp) * kD;
         const int part = tid & 15;
         for (uint32_t i = static_cast<uint32_t>(tid) >> 4; i < n_band; i += kRowThreads / 16) {
           const u32x4 raw = load_u32x4(kr + static_cast<size_t>(bi[i]) * kD + 8 * part);
@@ -2391,17 +2490,21 @@ hipError_t launch_fused_select(const Plan& p, const u16* q, const u16* k, int32_
 }
 
 hipError_t launch_prefill_select(const Plan& p, const u16* q, const u16* k, int32_t* idx,
-                                 int32_t* n_sel, void* ws, hipStream_t st) {
+                                 int32_t* n_sel, float* lse, void* ws, hipStream_t st) {
   char* w = static_cast<char*>(ws);
   const double c2 = p.scale * 1.4426950408889634;
+  const float c2_hi = static_cast<float>(c2);
   hipLaunchKernelGGL(prefill_select_kernel, dim3(p.R), dim3(kRowThreads), 0, st,
                      reinterpret_cast<const u16*>(w + p.off_ybuf),
                      reinterpret_cast<const uint32_t*>(w + p.off_kmax),
                      (p.T + kImportanceTok - 1) / kImportanceTok,
-                     reinterpret_cast<const double*>(w + p.off_lse2), q, k,
+                     reinterpret_cast<double*>(w + p.off_lse2), lse,
+                     reinterpret_cast<const uint32_t*>(w + p.off_dom_cnt),
+                     reinterpret_cast<const int32_t*>(w + p.off_dom_list),
+                     reinterpret_cast<RefineStat*>(w + p.off_ref_stat), q, k,
                      reinterpret_cast<int32_t*>(w + p.off_band_idx),
                      reinterpret_cast<uint64_t*>(w + p.off_band_key), p.band_cap, idx, n_sel, p.S,
-                     p.Spad, p.T, p.Hkv, p.k, p.w, p.cap, c2, p.kvp);
+                     p.Spad, p.T, p.Hkv, p.k, p.w, p.cap, c2, c2_hi, p.kvp);
   return hipGetLastError();
 }
 

@@ -27,7 +27,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 HS2_OK, HS2_ERR_INVALID_ARG, HS2_ERR_UNSUPPORTED, HS2_ERR_WORKSPACE, HS2_ERR_HIP = 0, -1, -2, -3, -4
 EXPORTED = ["hs2_workspace_bytes", "hs2_full_attn_scores", "hs2_topk_select", "hs2_sparse_attn",
             "hs2_cross_decoder_step", "hs2_cross_decoder_step_timed", "hs2_kv_bridge",
-            "hs2_sparse_attn_swa",
+            "hs2_sparse_attn_swa", "hs2_workspace_region",
             "hs2_status_string", "hs2_last_hip_error"]
 
 
@@ -37,7 +37,8 @@ class Shape(ctypes.Structure):
                 ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("select_block", ctypes.c_int32),
-                ("kv_capacity", ctypes.c_int64)]
+                ("kv_capacity", ctypes.c_int64), ("decode_splits", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class BridgeShape(ctypes.Structure):
@@ -69,6 +70,10 @@ _lib.hs2_sparse_attn_swa.argtypes = [_SP, ctypes.c_int32, _P, _P, _P, _P, _P, _P
 _lib.hs2_sparse_attn_swa.restype = ctypes.c_int
 _lib.hs2_kv_bridge.argtypes = [ctypes.POINTER(BridgeShape), _P, _P, _P, _P, _P]
 _lib.hs2_kv_bridge.restype = ctypes.c_int
+_lib.hs2_workspace_region.argtypes = [_SP, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.POINTER(ctypes.c_size_t),
+                                      ctypes.POINTER(ctypes.c_size_t)]
+_lib.hs2_workspace_region.restype = ctypes.c_int
 _lib.hs2_status_string.argtypes = [ctypes.c_int]
 _lib.hs2_status_string.restype = ctypes.c_char_p
 _lib.hs2_last_hip_error.argtypes = []
@@ -97,6 +102,7 @@ class ShapeArgs:
     scale: Optional[float] = None
     kv_capacity: int = 0      # token rows per KV head in k / v; 0 = ctx_len
     select_block: int = 0     # 0: token-level selection; else the block-level variant's block
+    decode_splits: int = 0    # 0: the library's plan; else context splits per decode row
 
     def c(self) -> Shape:
         scale = self.scale if self.scale is not None else 1.0 / math.sqrt(self.head_dim)
@@ -104,7 +110,7 @@ class ShapeArgs:
                      n_q_tokens=self.n_q_tokens, n_q_heads=self.n_q_heads,
                      n_kv_heads=self.n_kv_heads, head_dim=self.head_dim, top_k=self.top_k,
                      window=self.window, select_block=self.select_block,
-                     kv_capacity=self.kv_capacity)
+                     kv_capacity=self.kv_capacity, decode_splits=self.decode_splits, reserved=0)
 
     @property
     def rows(self) -> int:
@@ -165,6 +171,32 @@ def alloc_workspace(s: ShapeArgs, n_sparse_layers: int = 0, device="cuda") -> to
     if n == 0:
         raise HS2Error("hs2_workspace_bytes", HS2_ERR_UNSUPPORTED)
     return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+HS2_WS_LSE2 = 1
+HS2_WS_REFINE = 2
+
+
+def workspace_region(s: ShapeArgs, n_sparse_layers: int, region: int):
+    """(offset, bytes) of a named region of the workspace (hs2_workspace_region)."""
+    off, nb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _call("hs2_workspace_region", _lib.hs2_workspace_region(
+        ctypes.byref(s.c()), int(n_sparse_layers), int(region), ctypes.byref(off),
+        ctypes.byref(nb)))
+    return int(off.value), int(nb.value)
+
+
+def workspace_lse2(s: ShapeArgs, n_sparse_layers: int, ws: torch.Tensor) -> torch.Tensor:
+    """The base-2 log-normalisers [B][T][Hq] (float64) that a step left in ws."""
+    off, nb = workspace_region(s, n_sparse_layers, HS2_WS_LSE2)
+    return ws[off:off + nb].view(torch.float64).view(s.batch, s.n_q_tokens, s.n_q_heads)
+
+
+def workspace_refine_stats(s: ShapeArgs, n_sparse_layers: int, ws: torch.Tensor) -> torch.Tensor:
+    """Per-row statistics of the normaliser's refinement [rows][4] (uint32 as
+    int32): dominant units, float32 replica mismatches, list overflow, 0."""
+    off, nb = workspace_region(s, n_sparse_layers, HS2_WS_REFINE)
+    return ws[off:off + nb].view(torch.int32).view(s.rows, 4)
 
 
 def full_attn_scores(s: ShapeArgs, q, k, v, out, lse=None, scores=None, ws=None):

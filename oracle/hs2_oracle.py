@@ -67,7 +67,7 @@ example with numbers, so there is no golden value from the pages themselves.
 """
 from __future__ import annotations
 
-from typing import Dict, Iterable, Optional, Sequence, Tuple
+from typing import Dict, Iterable, Optional, Tuple
 
 import numpy as np
 
@@ -268,21 +268,6 @@ def sparse_step(q: np.ndarray, k: np.ndarray, v: np.ndarray, idx: np.ndarray,
                 for n in range(L):
                     qn = widen_bf16(q[n, b, t, g * G:(g + 1) * G])
                     out[n, b, t, g * G:(g + 1) * G] = sparse_attention_row(qn, kk, vv, sel, scale)
-    return out
-
-
-def topk_from_scores(scores: np.ndarray, pos: Sequence[int], top_k: int, window: int,
-                     block: int = 0):
-    """Selection alone, from given scores [R, S] (row r has context 0..pos[r]);
-    block > 0 selects whole blocks of that size."""
-    out = []
-    for r in range(scores.shape[0]):
-        p = int(pos[r])
-        if block:
-            idx, _, _ = select_blocks(scores[r, : p + 1], p, top_k, window, block)
-        else:
-            idx, _, _ = select_tokens(scores[r, : p + 1], p, top_k, window)
-        out.append(idx)
     return out
 
 

@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 11
     lib = hs2.raw()
     for n in names:
         assert hasattr(lib, n), n
@@ -30,9 +30,9 @@ def test_every_declared_function_is_exported():
 
 
 def test_shape_struct_layout():
-    assert ctypes.sizeof(hs2.Shape) == 56
+    assert ctypes.sizeof(hs2.Shape) == 64
     assert hs2.Shape.scale.offset == 8 and hs2.Shape.batch.offset == 16
-    assert hs2.Shape.kv_capacity.offset == 48
+    assert hs2.Shape.kv_capacity.offset == 48 and hs2.Shape.decode_splits.offset == 56
 
 
 def good():
@@ -75,6 +75,8 @@ def test_workspace_bytes_valid_and_monotone():
     ("kv_capacity", 4999, hs2.HS2_ERR_INVALID_ARG),   # smaller than ctx_len
     ("kv_capacity", -1, hs2.HS2_ERR_INVALID_ARG),
     ("kv_capacity", 1 << 40, hs2.HS2_ERR_UNSUPPORTED),
+    ("decode_splits", -1, hs2.HS2_ERR_INVALID_ARG),
+    ("reserved", 1, hs2.HS2_ERR_INVALID_ARG),
 ])
 def test_bad_shapes_rejected(field, value, code):
     c = good().c()
@@ -115,12 +117,54 @@ def test_null_pointers_and_workspace_errors():
                                             FAKE, FAKE, FAKE, need, None, 0, ms) == E
 
 
-def test_prefill_chunk_full_layer_reported_unsupported_or_accepted():
+@pytest.mark.parametrize("T", [1, 4])
+def test_workspace_regions(T):
+    """The introspection regions lie inside the workspace, 256-byte aligned,
+    with the documented sizes; unknown regions and null pointers are rejected."""
+    s = dataclasses.replace(good(), n_q_tokens=T)
+    total = hs2.workspace_bytes(s, 2)
+    rows = s.batch * T * s.n_kv_heads
+    for region, size in ((hs2.HS2_WS_LSE2, rows * 8 * 8), (hs2.HS2_WS_REFINE, rows * 16)):
+        off, nb = hs2.workspace_region(s, 2, region)
+        assert nb == size and off % 256 == 0 and off + nb <= total
+    lib = hs2.raw()
+    o, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    c = s.c()
+    assert lib.hs2_workspace_region(ctypes.byref(c), 2, 99, ctypes.byref(o), ctypes.byref(b)) == \
+        hs2.HS2_ERR_INVALID_ARG
+    assert lib.hs2_workspace_region(ctypes.byref(c), 2, hs2.HS2_WS_LSE2, None, ctypes.byref(b)) == \
+        hs2.HS2_ERR_INVALID_ARG
+    c.batch = 0
+    assert lib.hs2_workspace_region(ctypes.byref(c), 2, hs2.HS2_WS_LSE2, ctypes.byref(o),
+                                    ctypes.byref(b)) == hs2.HS2_ERR_INVALID_ARG
+
+
+def test_decode_split_override_changes_the_plan():
+    """A caller's split count changes the decode plan (and so the workspace of
+    the per-split partial results); it is clamped to the context's 128-key
+    splits; a prefill chunk ignores it."""
+    base = hs2.ShapeArgs(batch=1, n_q_tokens=1, n_q_heads=8, n_kv_heads=1, head_dim=128,
+                         ctx_len=100000, top_k=64, window=16)
+    sizes = {n: hs2.workspace_bytes(dataclasses.replace(base, decode_splits=n), 0)
+             for n in (1, 7, 300, 100000)}
+    assert sizes[1] < sizes[7] < sizes[300] <= sizes[100000]
+    assert sizes[100000] == hs2.workspace_bytes(dataclasses.replace(base, decode_splits=782), 0)
+    chunk = dataclasses.replace(base, n_q_tokens=4)
+    assert hs2.workspace_bytes(dataclasses.replace(chunk, decode_splits=3), 0) == \
+        hs2.workspace_bytes(chunk, 0)
+
+
+def test_timed_step_rejects_block_selection_on_a_chunk():
+    """Block-level selection inside a prefill chunk's fused step is refused by
+    the timed entry point exactly as by the step itself."""
     lib = hs2.raw()
     c = good().c()
+    c.select_block = 16
     c.n_q_tokens = 4
-    need = lib.hs2_workspace_bytes(ctypes.byref(c), 0)
-    assert need > 0
+    ms = (ctypes.c_float * 4)()
+    st = lib.hs2_cross_decoder_step_timed(ctypes.byref(c), 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                          FAKE, FAKE, FAKE, 1 << 40, None, 1, ms)
+    assert st == hs2.HS2_ERR_UNSUPPORTED
 
 
 def test_status_strings():

@@ -115,7 +115,7 @@ def test_identical_keys_take_lowest_indices(hs2):
     x = wl.generate(w)
     x["k"][:] = x["k"][:, :, :1, :]
     res = gh.run_step(w, x)
-    gh.compare_step(w, x, res)
+    gh.compare_step(w, x, res, check_lse2=False)
     assert res["idx"][0, 0, 0, :116].tolist() == list(range(100)) + list(range(5984, 6000))
 
 
@@ -154,14 +154,39 @@ def test_large_band_distinct_keys(hs2):
 
 
 def test_deterministic_across_runs(hs2):
+    """Ten runs of one plan: every output bit for bit the same."""
     w = wl.small(batch=2, n_q_heads=16, n_kv_heads=2, ctx_len=3333, n_sparse_layers=3,
                  top_k=256, window=64, n_needles=8, config_id=24)
     x = wl.generate(w)
     a = gh.run_step(w, x)
-    for _ in range(3):
+    for _ in range(9):
         b = gh.run_step(w, x)
         for key in a:
             np.testing.assert_array_equal(a[key], b[key])
+
+
+def test_results_do_not_depend_on_the_split_plan(hs2):
+    """Decode with the library's plan and three caller split counts (1, 7 and
+    33 context splits per row): the index lists are bit-identical (the
+    selection ranks float64 importances of exact products), every output is
+    within the parity tolerance of the oracle, and each plan repeats bit for
+    bit.  The outputs themselves differ in their last bits between plans: the
+    splits' partial sums are added in a different order."""
+    w = wl.small(batch=2, n_q_heads=16, n_kv_heads=2, ctx_len=5000, n_sparse_layers=3,
+                 top_k=256, window=64, n_needles=8, config_id=27)
+    x = wl.generate(w)
+    runs = {}
+    for n in (0, 1, 7, 33):
+        gh.log(f"[plan] decode_splits={n}")
+        a = gh.run_step(w, x, decode_splits=n)
+        b = gh.run_step(w, x, decode_splits=n)
+        for key in a:
+            np.testing.assert_array_equal(a[key], b[key])
+        gh.compare_step(w, x, a)
+        runs[n] = a
+    for n in (1, 7, 33):
+        np.testing.assert_array_equal(runs[n]["idx"], runs[0]["idx"])
+        np.testing.assert_array_equal(runs[n]["n_sel"], runs[0]["n_sel"])
 
 
 def test_topk_select_from_given_scores(hs2):
@@ -231,4 +256,4 @@ def test_full_attn_scores_standalone(hs2):
         gh.check_outputs(gh.host_f64(out)[b, t, 8 * g:8 * g + 8], rr["out_full"], "out")
         np.testing.assert_allclose(lse.cpu().numpy()[b, t, 8 * g:8 * g + 8], rr["lse"], atol=2e-5)
         np.testing.assert_allclose(sc.cpu().numpy()[b, t, g].astype(np.float64), rr["score"],
-                                   rtol=5e-5)
+                                   rtol=gh.SCORES_RTOL_DECODE, atol=1e-30)

@@ -61,7 +61,7 @@ def test_prefill_identical_keys(hs2, ctx, T):
     x = wl.generate(w)
     x["k"][:] = x["k"][:, :, :1, :]
     res = gh.run_step(w, x)
-    gh.compare_step(w, x, res)
+    gh.compare_step(w, x, res, check_lse2=False)
     for t in range(w.n_q_tokens):
         first = w.ctx_len - w.n_q_tokens + t - w.window + 1
         row = res["idx"][0, t, 0, : res["n_sel"][0, t, 0]]
@@ -91,7 +91,8 @@ def test_prefill_full_attn_scores_standalone(hs2):
         gh.check_outputs(o[b, t, heads], rr["out_full"], f"out{(b, t, g)}")
         np.testing.assert_allclose(l[b, t, heads], rr["lse"], rtol=0, atol=2e-5)
         pos = rr["pos"]
-        np.testing.assert_allclose(scn[b, t, g, : pos + 1], rr["score"], rtol=5e-5, atol=1e-30)
+        np.testing.assert_allclose(scn[b, t, g, : pos + 1], rr["score"],
+                                   rtol=gh.SCORES_RTOL_PREFILL, atol=1e-30)
         assert np.all(scn[b, t, g, pos + 1:] == 0.0)
 
 
@@ -101,12 +102,13 @@ def test_prefill_4k_over_128k_sampled_rows(hs2):
     x = wl.generate(w)
     gh.log("[prefill] prefill_4k_over_128k: GPU step")
     res = gh.run_step(w, x, with_scores=False)
-    rng = np.random.default_rng(5)
-    ts = sorted({0, 1, 15, 16, 2047, 4095} | set(rng.integers(0, w.n_q_tokens, 10).tolist()))
-    rows = [(0, t, int(rng.integers(0, w.n_kv_heads))) for t in ts] + [(0, 4095, g) for g in range(4)]
+    # every row: count, order, window and padding (structure only)
+    gh.check_index_rows_all(res["idx"], res["n_sel"], w)
+    # against the oracle: every 16th query token (and the chunk's first and last
+    # few) on all four KV heads, about 1,030 rows
+    ts = sorted(set(range(0, w.n_q_tokens, 16)) | {1, 15, 2047, 4094, 4095})
+    rows = [(0, t, g) for t in ts for g in range(w.n_kv_heads)]
     gh.log(f"[prefill] oracle on {len(rows)} rows")
     st = gh.compare_step(w, x, res, rows=rows)
     gh.log(f"  {st}")
-    # every row: n_sel = k + w and the window present (cheap checks on all 16384 rows)
-    n = res["n_sel"]
-    assert np.all(n == w.top_k + w.window)
+    assert len(rows) >= 1024
