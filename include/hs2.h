@@ -234,7 +234,8 @@ int hs2_kv_bridge(const hs2_bridge_shape* shape, const hs2_bf16* hidden, const h
  *   HS2_WS_LSE2  float64 [B][T][Hq]: each query head's base-2 log-normaliser,
  *                log2 sum_j 2^(c2 s_j) with c2 = scale * log2(e) (the natural-log
  *                lse divided by ln 2), as the selection ranks keys with it.
- *                Valid after hs2_full_attn_scores or hs2_cross_decoder_step.
+ *                Valid after hs2_cross_decoder_step, and in decode after
+ *                hs2_full_attn_scores.
  *   HS2_WS_REFINE uint32 [B*T*Hkv rows][4]: the refinement of that normaliser
  *                over the keys that carry weight (see hs2_cross_decoder_step):
  *                [0] dominant units summed again (decode: 16-key subtiles,
@@ -248,6 +249,20 @@ int hs2_kv_bridge(const hs2_bridge_shape* shape, const hs2_bf16* hidden, const h
 enum { HS2_WS_LSE2 = 1, HS2_WS_REFINE = 2 };
 int hs2_workspace_region(const hs2_shape* shape, int32_t n_sparse_layers, int32_t region,
                          size_t* offset, size_t* bytes);
+
+/* ---- Measurement: the device's streaming-read ceiling -----------------------
+ * Reads every 16-byte unit of buf (device memory, 16-byte aligned, `bytes`
+ * long; only whole 16-byte units are read) once per pass with non-temporal
+ * loads, iters passes back to back on `stream`, then synchronises the stream
+ * and writes the average milliseconds per pass to *ms_out: bytes / ms is the
+ * bandwidth a plain stream reaches, the measured ceiling next to the HBM
+ * datasheet peak for the full layer's streaming read.  buf is only read; *sink
+ * (device memory, one uint32) is written only if the XOR of everything read
+ * equals one fixed constant, which keeps the loads from being optimised away.
+ * Not for the serving loop.  Errors: HS2_ERR_INVALID_ARG for null pointers,
+ * bytes < 16, iters < 1 or a misaligned buf; HS2_ERR_HIP. */
+int hs2_stream_read_ms(const void* buf, size_t bytes, uint32_t* sink, int32_t iters, void* stream,
+                       float* ms_out);
 
 /* Human-readable text for a status code (static storage). */
 const char* hs2_status_string(int status);

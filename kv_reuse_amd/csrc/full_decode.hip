@@ -34,6 +34,8 @@
 //  * The next tile's K/V loads are issued before the current tile is processed
 //    (two register buffers), so each wave keeps 16 KB of HBM reads in flight.
 
+#include <algorithm>
+
 #include "hs2_internal.h"
 
 namespace hs2 {
@@ -364,17 +366,19 @@ __global__ __launch_bounds__(kCmbThreads) void full_combine_kernel(
 // and even a correctly rounded float32 logit of a large key is off by up to
 // 2^-25 |s|.  A key that carries a large share of a head's softmax passes its
 // logit error into lse2 at that share, and the selection's float64 ranking
-// would shift every importance of that head by it.  So the keys that carry
-// weight are summed again: for every subtile whose stored maximum reaches
-// 2^kDomLog2 of some head's normaliser, each of its keys' terms 2^(sv - lse2),
-// sv the very float32 logit the split kernel exponentiated, is replaced by
-// 2^(y - lse2), y the float64 logit of exact bf16 products.  sv is recomputed
-// by the split kernel's own MFMA sequence on the same operands, which gives
-// the same bits (the MFMA result of an element does not depend on where in the
-// tile it sits); the subtile maximum the split kernel stored is checked
-// against it, and a mismatch is counted.  What remains is the weighted mean of
-// the other keys' logit errors, each such key below 2^kDomLog2 of the total, in
-// which independent errors average out, and the float32 exponentials and
+// would shift every importance of that head by it.  So the (key, head) terms
+// that carry weight are summed again: in every subtile whose stored maximum
+// reaches 2^kDomLog2 of some head's normaliser, each pair whose term
+// 2^(sv - lse2) reaches it, sv the very float32 logit the split kernel
+// exponentiated, gets the term 2^(y - lse2) instead, y the float64 logit of
+// exact bf16 products.  sv is recomputed by the split kernel's own MFMA
+// sequence on the same operands, which gives the same bits (the MFMA result of
+// an element does not depend on where in the tile it sits); the subtile
+// maximum the split kernel stored is checked against it, and a mismatch is
+// counted.  The change of a term is 2^(sv - lse2) (e^d - 1), d = (y - sv) ln 2
+// below 1e-4 in size, taken as d + d^2 / 2.  What remains is the weighted mean
+// of the other terms' logit errors, each term below 2^kDomLog2 of the total,
+// in which independent errors average out, and the float32 exponentials and
 // partial sums of the kept terms (a few units of 2^-24 of each).
 
 constexpr int kRefThreads = 256;
@@ -386,86 +390,149 @@ __device__ __forceinline__ double bf16_word_f64(const u32x4& raw, int t) {
   return static_cast<double>(__uint_as_float((t & 1) ? (word & 0xFFFF0000u) : (word << 16)));
 }
 
-// float64 dot product of a query row (float64, LDS) and a bf16 key row (LDS):
-// the bf16 products are exact in float64
-__device__ __forceinline__ double dot_f64(const double* __restrict__ qh, const u16* __restrict__ krow) {
-  double dot = 0.0;
-#pragma unroll 4
-  for (int d8 = 0; d8 < kD / 8; ++d8) {
-    const u32x4 raw = *reinterpret_cast<const u32x4*>(krow + 8 * d8);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) dot = fma(qh[8 * d8 + t], bf16_word_f64(raw, t), dot);
-  }
-  return dot;
+// Sum over each group of 8 lanes, in every lane of the group (the pairing of a
+// lane ^ 1, ^ 2, ^ 4 butterfly).
+__device__ __forceinline__ double group8_sum(double v) {
+  v += dpp_f64<0xB1>(v);    // lane ^ 1
+  v += dpp_f64<0x4E>(v);    // lane ^ 2
+  v += dpp_f64<0x141>(v);   // the other quad of the 8
+  return v;
 }
 
-// grid (ref chunks, R): work-group c of row r takes subtiles [c chunk, (c+1) chunk)
-// of the row's ceil(S/16), and writes its partial sums to part[r][c].
+// The float64 logit (unscaled dot product) of a bf16 key row and a query row,
+// by the 8 lanes of a group: lane j takes dims 16 j .. 16 j + 15 (q_part its
+// 16 query values, krow the key row in LDS), then the group's sum.
+__device__ __forceinline__ double dot_group8(const double (&q_part)[16], const u16* __restrict__ krow,
+                                             int j) {
+  const u32x4 r0 = *reinterpret_cast<const u32x4*>(krow + 16 * j);
+  const u32x4 r1 = *reinterpret_cast<const u32x4*>(krow + 16 * j + 8);
+  double acc = 0.0;
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc = fma(q_part[t], bf16_word_f64(r0, t), acc);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc = fma(q_part[8 + t], bf16_word_f64(r1, t), acc);
+  return group8_sum(acc);
+}
+
+// grid (n_wg, R): work-group w of row r takes the w-th equal share of the row's
+// dominant subtiles: the ones the selection's candidate kernel listed (their
+// bound reaches the row's cut), region by region in ascending order, then
+// every subtile reaching into the window (which that kernel does not see); a
+// wave takes one subtile at a time.  Each work-group writes its partial sums
+// to part[r][w].
 __global__ __launch_bounds__(kRefThreads) void lse_refine_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const float* __restrict__ stmax,
-    const double* __restrict__ lse2, RefinePart* __restrict__ part, int64_t S, int64_t Spad,
-    int chunk, int n_chunks, float c2_hi, float c2_lo, double c2, int64_t kvp) {
-  __shared__ int32_t s_list[kRefThreads];
-  __shared__ uint32_t s_wcnt[kRefWaves];
-  __shared__ double s_q[kG * kD];                                  // the group's queries
+    const double* __restrict__ lse2, const float* __restrict__ cut_row,
+    const int32_t* __restrict__ dsub, const uint32_t* __restrict__ dsub_cnt,
+    RefinePart* __restrict__ part, int64_t S, int64_t Spad, int w, int cc_chunk, int cc_nchunk,
+    int n_wg, float c2_hi, float c2_lo, double c2, int64_t kvp) {
+  __shared__ uint32_t pre[kMaxChunks + 1];
+  __shared__ int32_t s_ids[kRefThreads];
+  __shared__ uint32_t s_wsum[kRefWaves];
   __shared__ __align__(16) u16 s_k[kRefWaves][kSubTileKeys * kD];  // a wave's subtile of K rows
   __shared__ float s_sv[kRefWaves][kSubTileKeys * kG];             // its float32 logits [key][head]
   __shared__ double s_acc[kRefWaves][kG];
   __shared__ uint32_t s_bad[kRefWaves];
+  __shared__ float s_cut;
   const int r = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
+  const int h_l = lane >> 3, j = lane & 7;
+  const int64_t first = max(static_cast<int64_t>(0), S - w);
+  const int64_t n_sub = (first + kSubTileKeys - 1) / kSubTileKeys;
   const int64_t nst = (S + kSubTileKeys - 1) / kSubTileKeys;
-  const int64_t st0 = static_cast<int64_t>(blockIdx.x) * chunk;
-  const int64_t st1 = min(nst, st0 + chunk);
   const u16* qr = q + static_cast<size_t>(r) * kG * kD;
   const u16* kr = k + static_cast<size_t>(r) * kvp * kD;
   const float* stmax_row = stmax + static_cast<size_t>(r) * (Spad / kSubTileKeys) * kG;
-  for (int i = tid; i < kG * kD; i += kRefThreads) s_q[i] = static_cast<double>(bf16_bits_to_f32(qr[i]));
-  // a subtile is dominant when its maximum for some head h reaches lse2_h + kDomLog2
-  float thr[kG];
+  // ---- the row's list: region lengths and their exclusive prefix
+  constexpr int kPer = kMaxChunks / kRefThreads;
+  uint32_t cl[kPer];
+  uint32_t mysum = 0;
 #pragma unroll
-  for (int h = 0; h < kG; ++h) thr[h] = static_cast<float>(lse2[static_cast<size_t>(r) * kG + h]) + kDomLog2;
-  // this lane's (key, head) pairs of a subtile: keys (lane >> 3) and 8 + (lane >> 3), head lane & 7
-  const int h_l = lane & 7;
+  for (int u = 0; u < kPer; ++u) {
+    const int c = kPer * tid + u;
+    cl[u] = c < cc_nchunk ? dsub_cnt[static_cast<size_t>(r) * cc_nchunk + c] : 0u;
+    mysum += cl[u];
+  }
+  uint32_t incl = mysum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) s_wsum[wave] = incl;
+  if (tid == 0) s_cut = cut_row[r];
+  __syncthreads();
+  uint32_t base = incl - mysum;
+  for (int w2 = 0; w2 < wave; ++w2) base += s_wsum[w2];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int c = kPer * tid + u;
+    if (c < cc_nchunk) pre[c] = base;
+    base += cl[u];
+  }
+  if (tid == kRefThreads - 1) pre[cc_nchunk] = base;
+  __syncthreads();
+  const uint32_t n_listed = pre[cc_nchunk];
+  const uint32_t n_total = n_listed + static_cast<uint32_t>(nst - n_sub);
+  const uint32_t share = (n_total + n_wg - 1) / n_wg;
+  const uint32_t e0 = min(n_total, share * blockIdx.x);
+  const uint32_t e1 = min(n_total, e0 + share);
+  const float cut = s_cut;
+  // lane (head h_l, dims 16 j ..): the query part in float64; lane (col, grp)
+  // of the MFMA layout: the threshold of head col
+  double q_part[16];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) q_part[t] = static_cast<double>(bf16_bits_to_f32(qr[h_l * kD + 16 * j + t]));
   const double l2h = lse2[static_cast<size_t>(r) * kG + h_l];
+  const float thr_h = static_cast<float>(l2h) + cut;
+  const float thr_c = col < kG ? static_cast<float>(lse2[static_cast<size_t>(r) * kG + col]) + cut
+                               : INFINITY;
   bf16x8 qb[4];
   load_q_operand(qr, col, grp, qb);
-  double corr = 0.0;
-  uint32_t n_dom = 0, n_bad = 0;
-  __syncthreads();
-  for (int64_t sr0 = st0; sr0 < st1; sr0 += kRefThreads) {
-    const int64_t st = sr0 + tid;
-    bool dom = false;
-    if (st < st1) {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(stmax_row + st * kG);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(stmax_row + st * kG + 4);
-      dom = a[0] >= thr[0] || a[1] >= thr[1] || a[2] >= thr[2] || a[3] >= thr[3] ||
-            b[0] >= thr[4] || b[1] >= thr[5] || b[2] >= thr[6] || b[3] >= thr[7];
-    }
-    // the round's dominant subtiles, ascending
-    const uint64_t bal = __ballot(dom);
-    if (lane == 0) s_wcnt[wave] = static_cast<uint32_t>(__popcll(bal));
-    __syncthreads();
-    uint32_t off = 0, tot = 0;
+  double corr = 0.0;   // lanes j = 0: head h_l's sum, subtile by subtile in list order
+  uint32_t n_bad = 0;
+  // the split kernel's K operand of a subtile (rows past S repeat the last) and,
+  // in lanes (col < 8, grp 0), its stored maximum for head col
+  auto load_sub = [&](int64_t sti, bf16x8 (&ka)[4], float& smax) {
+    const int64_t key = min(sti * kSubTileKeys + col, S - 1);
 #pragma unroll
-    for (int w2 = 0; w2 < kRefWaves; ++w2) {
-      off += w2 < wave ? s_wcnt[w2] : 0u;
-      tot += s_wcnt[w2];
-    }
-    if (dom) s_list[off + __popcll(bal & ((1ull << lane) - 1ull))] = static_cast<int32_t>(st);
-    __syncthreads();
-    n_dom += tot;
-    for (uint32_t i = wave; i < tot; i += kRefWaves) {
-      const int32_t sti = s_list[i];
-      const int64_t key0 = static_cast<int64_t>(sti) * kSubTileKeys;
-      // the split kernel's operands and MFMA sequence for this subtile
-      bf16x8 ka[4];
-      {
-        const int64_t key = min(key0 + col, S - 1);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) ka[c] = as_bf16x8(load_u32x4(kr + key * kD + 8 * grp + 32 * c));
+    for (int c = 0; c < 4; ++c) ka[c] = as_bf16x8(load_u32x4(kr + key * kD + 8 * grp + 32 * c));
+    smax = col < kG && grp == 0 ? stmax_row[sti * kG + col] : 0.f;
+  };
+  for (uint32_t b0 = e0; b0 < e1; b0 += kRefThreads) {
+    // this round's subtiles, one list entry per thread (the regions of the
+    // candidate kernel in order, then the window's subtiles)
+    const uint32_t nb = min(static_cast<uint32_t>(kRefThreads), e1 - b0);
+    __syncthreads();   // the previous round's ids are read
+    if (static_cast<uint32_t>(tid) < nb) {
+      const uint32_t e = b0 + tid;
+      if (e < n_listed) {
+        int lo = 0, hi = cc_nchunk - 1;   // the region of e: the largest c with pre[c] <= e
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (pre[mid] <= e) lo = mid;
+          else hi = mid - 1;
+        }
+        s_ids[tid] = dsub[(static_cast<size_t>(r) * cc_nchunk + lo) * cc_chunk + (e - pre[lo])];
+      } else {
+        s_ids[tid] = static_cast<int32_t>(n_sub + (e - n_listed));
       }
+    }
+    __syncthreads();
+    // one subtile ahead: its K rows and maxima load while the current one is processed
+    bf16x8 ka_next[4];
+    float smax_next = 0.f;
+    if (static_cast<uint32_t>(wave) < nb) load_sub(s_ids[wave], ka_next, smax_next);
+    for (uint32_t i = wave; i < nb; i += kRefWaves) {
+      const int64_t sti = s_ids[i];
+      bf16x8 ka[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) ka[c] = ka_next[c];
+      const float smax = smax_next;
+      if (i + kRefWaves < nb) load_sub(s_ids[i + kRefWaves], ka_next, smax_next);
+      const int64_t key0 = sti * kSubTileKeys;
+      // the split kernel's MFMA sequence for this subtile
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 4; ++c) acc = mfma_16x16x32(ka[c], qb[c], acc);
@@ -478,45 +545,53 @@ __global__ __launch_bounds__(kRefThreads) void lse_refine_kernel(
         mx = fmaxf(mx, sv[i4]);
       }
       mx = max_xor32(max_xor16(mx));
-      if (col < kG && grp == 0 && mx != stmax_row[static_cast<int64_t>(sti) * kG + col]) ++n_bad;
-      // the K rows and the logits, staged for the float64 pass
+      if (col < kG && grp == 0 && mx != smax) ++n_bad;
+      // the K rows and the logits, staged for the float64 pass; the keys with a
+      // dominant pair
 #pragma unroll
       for (int c = 0; c < 4; ++c)
         *reinterpret_cast<bf16x8*>(s_k[wave] + col * kD + 32 * c + 8 * grp) = ka[c];
-      if (col < kG) {
+      uint32_t keys = 0;
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) s_sv[wave][(4 * grp + i4) * kG + col] = sv[i4];
+      for (int i4 = 0; i4 < 4; ++i4) {
+        if (col < kG) s_sv[wave][(4 * grp + i4) * kG + col] = sv[i4];
+        const uint64_t pb = __ballot(col < kG && sv[i4] >= thr_c);
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          keys |= (((pb >> (16 * g4)) & 0xFFull) != 0 ? 1u : 0u) << (4 * g4 + i4);
       }
       lds_fence_wave();
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int e = (lane >> 3) + 8 * u;
-        const double dot = dot_f64(s_q + h_l * kD, s_k[wave] + e * kD);
-        if (key0 + e < S)
-          corr += exp2(c2 * dot - l2h) - exp2(static_cast<double>(s_sv[wave][e * kG + h_l]) - l2h);
+      for (uint32_t m = keys; m; m &= m - 1) {
+        const int ek = __builtin_ctz(m);
+        const double dot = dot_group8(q_part, s_k[wave] + ek * kD, j);
+        if (j == 0) {
+          const float svf = s_sv[wave][ek * kG + h_l];
+          if (svf >= thr_h) {
+            const double svd = static_cast<double>(svf);
+            const double dd = (c2 * dot - svd) * M_LN2;
+            const float pw = __builtin_amdgcn_exp2f(static_cast<float>(svd - l2h));
+            corr += static_cast<double>(pw) * (dd + 0.5 * dd * dd);
+          }
+        }
       }
       lds_fence_wave();   // the stage is read before the next subtile overwrites it
     }
-    __syncthreads();      // s_list is rewritten by the next round
   }
-  // per head: the lanes l with l & 7 = h, paired as a lane ^ 8, ^ 32, ^ 16 butterfly
-  corr += dpp_f64<0x128>(corr);   // row_ror:8, i.e. lane ^ 8 within the row of 16
-  corr = sum_rows_f64(corr);
   n_bad = static_cast<uint32_t>(__popcll(__ballot(n_bad != 0)));   // lanes with a mismatch
-  if (lane < kG) s_acc[wave][lane] = corr;
+  if (j == 0) s_acc[wave][h_l] = corr;
   if (lane == 0) s_bad[wave] = n_bad;
   __syncthreads();
   if (tid < kG) {
     double c = 0.0;
 #pragma unroll
     for (int w2 = 0; w2 < kRefWaves; ++w2) c += s_acc[w2][tid];
-    RefinePart* pr = part + static_cast<size_t>(r) * n_chunks + blockIdx.x;
+    RefinePart* pr = part + static_cast<size_t>(r) * n_wg + blockIdx.x;
     pr->corr[tid] = c;
     if (tid == 0) {
       uint32_t nb = 0;
 #pragma unroll
       for (int w2 = 0; w2 < kRefWaves; ++w2) nb += s_bad[w2];
-      pr->n_dom = n_dom;
+      pr->n_dom = e1 - e0;
       pr->n_bad = nb;
       pr->pad0 = 0u;
       pr->pad1 = 0u;
@@ -524,55 +599,75 @@ __global__ __launch_bounds__(kRefThreads) void lse_refine_kernel(
   }
 }
 
-// One wave per row: the chunks' partial sums in order, then lse2 += log2(1 +
-// sum), the natural-log lse for the caller and the head's importance bound.
-__global__ __launch_bounds__(64) void lse_finalize_kernel(
-    const RefinePart* __restrict__ part, int n_chunks, double* __restrict__ lse2,
-    float* __restrict__ lse_out, float* __restrict__ ytop_h, RefineStat* __restrict__ stat) {
-  const int r = blockIdx.x, lane = threadIdx.x;
-  const RefinePart* pr = part + static_cast<size_t>(r) * n_chunks;
-  if (lane < kG) {
-    double c = 0.0;
-    for (int i = 0; i < n_chunks; ++i) c += pr[i].corr[lane];
-    const double d = log1p(c) * M_LOG2E;
-    const size_t o = static_cast<size_t>(r) * kG + lane;
-    const double l2 = lse2[o] + d;
-    lse2[o] = l2;
-    if (lse_out) lse_out[o] = static_cast<float>(l2 * M_LN2);
-    ytop_h[o] = static_cast<float>(static_cast<double>(ytop_h[o]) - d);
-  }
+// One work-group of 8 waves per row, wave h for head h: the refined lse2 =
+// lse2 + log2(1 + the head's partial sums) into lse2r, the natural-log lse for
+// the caller, and the row's statistics.  (The heads' importance bounds keep
+// the value they had: the selection's histograms are placed by them, and a
+// bound off by the refinement's size stays a bound within a bin.)
+__global__ __launch_bounds__(kG * 64) void lse_finalize_kernel(
+    const RefinePart* __restrict__ part, int n_parts, const double* __restrict__ lse2,
+    double* __restrict__ lse2r, float* __restrict__ lse_out, RefineStat* __restrict__ stat) {
+  const int r = blockIdx.x, lane = threadIdx.x & 63, h = threadIdx.x >> 6;
+  const RefinePart* pr = part + static_cast<size_t>(r) * n_parts;
+  const double c = refine_head_sum(pr, n_parts, h);
   if (lane == 0) {
+    const size_t o = static_cast<size_t>(r) * kG + h;
+    const double l2 = lse2[o] + log1p(c) * M_LOG2E;
+    lse2r[o] = l2;
+    if (lse_out) lse_out[o] = static_cast<float>(l2 * M_LN2);
+  }
+  if (h == 0) {
     uint32_t nd = 0, nb = 0;
-    for (int i = 0; i < n_chunks; ++i) {
+    for (int i = lane; i < n_parts; i += 64) {
       nd += pr[i].n_dom;
       nb += pr[i].n_bad;
     }
-    stat[r] = RefineStat{nd, nb, 0u, 0u};
+    for (int off = 32; off > 0; off >>= 1) {
+      nd += __shfl_xor(nd, off);
+      nb += __shfl_xor(nb, off);
+    }
+    if (lane == 0) stat[r] = RefineStat{nd, nb, 0u, 0u};
   }
+}
+
+// The largest of a double over lanes l, l ^ 8, l ^ 16, ..., l ^ 56 (in every lane).
+__device__ __forceinline__ double max_over_groups8(double v) {
+  v = fmax(v, dpp_f64<0x128>(v));   // row_ror:8, i.e. lane ^ 8 within the row of 16
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  auto join = [](uint32_t hi, uint32_t lo) {
+    return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+  };
+  const auto l16 = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(u), static_cast<uint32_t>(u), false, false);
+  const auto h16 = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(u >> 32), static_cast<uint32_t>(u >> 32), false, false);
+  v = fmax(join(h16[0], l16[0]), join(h16[1], l16[1]));
+  const uint64_t w = static_cast<uint64_t>(__double_as_longlong(v));
+  const auto l32 = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(w), static_cast<uint32_t>(w), false, false);
+  const auto h32 = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(w >> 32), static_cast<uint32_t>(w >> 32), false, false);
+  return fmax(join(h32[0], l32[0]), join(h32[1], l32[1]));
 }
 
 // Optional per-key importance for the caller (the step itself never needs all
 // of them): every key's importance max_h 2^(y_h - lse2_h), y the float64 logit
-// of exact bf16 products; one wave per subtile of 16 keys, lane (key, head)
-// pairs as in the refinement.  grid (splits, R) over the split kernel's key
-// ranges (multiples of 16 keys).
+// of exact bf16 products; one wave per subtile of 16 keys, lane (head h = lane
+// >> 3, dims 16 (lane & 7) ..) as in the refinement.  grid (splits, R) over
+// the split kernel's key ranges (multiples of 16 keys).
 __global__ __launch_bounds__(kRefThreads) void full_scores_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const double* __restrict__ lse2,
     float* __restrict__ scores, int64_t S, int kps, double c2, int64_t kvp) {
-  __shared__ double s_q[kG * kD];
   __shared__ __align__(16) u16 s_k[kRefWaves][kSubTileKeys * kD];
   const int r = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
+  const int h = lane >> 3, j = lane & 7;
   const int64_t key_begin = static_cast<int64_t>(blockIdx.x) * kps;
   const int64_t key_end = min(S, key_begin + kps);
   const u16* qr = q + static_cast<size_t>(r) * kG * kD;
   const u16* kr = k + static_cast<size_t>(r) * kvp * kD;
   float* sr = scores + static_cast<size_t>(r) * S;
-  for (int i = tid; i < kG * kD; i += kRefThreads) s_q[i] = static_cast<double>(bf16_bits_to_f32(qr[i]));
-  const int h_l = lane & 7;
-  const double l2h = lse2[static_cast<size_t>(r) * kG + h_l];
-  __syncthreads();
+  double q_part[16];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) q_part[t] = static_cast<double>(bf16_bits_to_f32(qr[h * kD + 16 * j + t]));
+  const double l2h = lse2[static_cast<size_t>(r) * kG + h];
   for (int64_t key0 = key_begin + kSubTileKeys * wave; key0 < key_end; key0 += kSubTileKeys * kRefWaves) {
     const int64_t key = min(key0 + col, key_end - 1);
 #pragma unroll
@@ -580,15 +675,9 @@ __global__ __launch_bounds__(kRefThreads) void full_scores_kernel(
       *reinterpret_cast<u32x4*>(s_k[wave] + col * kD + 32 * c + 8 * grp) =
           load_u32x4(kr + key * kD + 32 * c + 8 * grp);
     lds_fence_wave();
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int e = (lane >> 3) + 8 * u;
-      double y = c2 * dot_f64(s_q + h_l * kD, s_k[wave] + e * kD) - l2h;
-      // the largest over the 8 heads: lanes 8 (lane >> 3) .. + 7
-      y = fmax(y, dpp_f64<0xB1>(y));    // lane ^ 1
-      y = fmax(y, dpp_f64<0x4E>(y));    // lane ^ 2
-      y = fmax(y, dpp_f64<0x141>(y));   // the other quad of the 8
-      if (h_l == 0 && key0 + e < key_end) sr[key0 + e] = static_cast<float>(exp2(y));
+    for (int e = 0; e < kSubTileKeys; ++e) {
+      const double y = max_over_groups8(c2 * dot_group8(q_part, s_k[wave] + e * kD, j) - l2h);
+      if (lane == 0 && key0 + e < key_end) sr[key0 + e] = static_cast<float>(exp2(y));
     }
     lds_fence_wave();
   }
@@ -625,21 +714,28 @@ hipError_t launch_full_combine(const Plan& p, u16* out, float* lse, void* ws, hi
   return hipGetLastError();
 }
 
-hipError_t launch_lse_refine(const Plan& p, const u16* q, const u16* k, float* lse, void* ws,
-                             hipStream_t st) {
+hipError_t launch_lse_refine(const Plan& p, const u16* q, const u16* k, void* ws, hipStream_t st) {
   char* w = static_cast<char*>(ws);
   const double c2 = p.scale * 1.4426950408889634;
   const float c2_hi = static_cast<float>(c2);
   const float c2_lo = static_cast<float>(c2 - static_cast<double>(c2_hi));
-  hipLaunchKernelGGL(lse_refine_kernel, dim3(p.ref_nchunk, p.R), dim3(kRefThreads), 0, st, q, k,
+  hipLaunchKernelGGL(lse_refine_kernel, dim3(p.ref_nwg, p.R), dim3(kRefThreads), 0, st, q, k,
                      reinterpret_cast<const float*>(w + p.off_stmax),
                      reinterpret_cast<const double*>(w + p.off_lse2),
-                     reinterpret_cast<RefinePart*>(w + p.off_ref_part), p.S, p.Spad, p.ref_chunk,
-                     p.ref_nchunk, c2_hi, c2_lo, c2, p.kvp);
-  hipLaunchKernelGGL(lse_finalize_kernel, dim3(p.R), dim3(64), 0, st,
-                     reinterpret_cast<const RefinePart*>(w + p.off_ref_part), p.ref_nchunk,
-                     reinterpret_cast<double*>(w + p.off_lse2), lse,
-                     reinterpret_cast<float*>(w + p.off_ytop),
+                     reinterpret_cast<const float*>(w + p.off_cut),
+                     reinterpret_cast<const int32_t*>(w + p.off_dsub),
+                     reinterpret_cast<const uint32_t*>(w + p.off_dsub_cnt),
+                     reinterpret_cast<RefinePart*>(w + p.off_ref_part), p.S, p.Spad, p.w,
+                     p.cc_chunk, p.cc_nchunk, p.ref_nwg, c2_hi, c2_lo, c2, p.kvp);
+  return hipGetLastError();
+}
+
+hipError_t launch_lse_finalize(const Plan& p, float* lse, void* ws, hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  hipLaunchKernelGGL(lse_finalize_kernel, dim3(p.R), dim3(kG * 64), 0, st,
+                     reinterpret_cast<const RefinePart*>(w + p.off_ref_part), p.ref_nwg,
+                     reinterpret_cast<const double*>(w + p.off_lse2),
+                     reinterpret_cast<double*>(w + p.off_lse2r), lse,
                      reinterpret_cast<RefineStat*>(w + p.off_ref_stat));
   return hipGetLastError();
 }
@@ -649,7 +745,7 @@ hipError_t launch_full_scores(const Plan& p, const u16* q, const u16* k, float* 
   char* w = static_cast<char*>(ws);
   const double c2 = p.scale * 1.4426950408889634;
   hipLaunchKernelGGL(full_scores_kernel, dim3(p.n_split, p.R), dim3(kRefThreads), 0, st, q, k,
-                     reinterpret_cast<const double*>(w + p.off_lse2), scores, p.S, p.kps, c2,
+                     reinterpret_cast<const double*>(w + p.off_lse2r), scores, p.S, p.kps, c2,
                      p.kvp);
   return hipGetLastError();
 }

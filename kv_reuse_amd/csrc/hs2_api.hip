@@ -134,15 +134,10 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
     q.sc_nchunk = static_cast<int>(ns);
     q.sc_chunk = static_cast<int>(ceil_div(nst, ns));   // list entries a region holds
   }
-  // refinement of lse2 (decode): subtile chunks of at least 16, about 256
-  // work-groups over all rows
-  {
-    const int64_t nst_all = ceil_div(q.S, 16);
-    int64_t rc = align_up(static_cast<size_t>(ceil_div(nst_all * R, 256)), 16);
-    rc = std::max<int64_t>(rc, 16);
-    q.ref_chunk = static_cast<int>(rc);
-    q.ref_nchunk = static_cast<int>(ceil_div(nst_all, rc));
-  }
+  // refinement of lse2 (decode): about two work-groups per compute unit over
+  // all rows (all resident at once), each taking an equal share of its row's
+  // dominant subtiles
+  q.ref_nwg = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(ceil_div(2 * q.n_cu, R), 1024)));
   // sparse: slices of 128 keys over work-groups when rows are few
   q.sp_nch = (R >= 256) ? 1 : static_cast<int>(ceil_div(q.cap, kSparseChunk));
 
@@ -186,9 +181,12 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
   // per (batch, KV head, importance token block): that block's share of max |k|
   q.off_kmax = take(decode ? 0 : static_cast<size_t>(q.B) * q.Hkv *
                                       ceil_div(q.T, kImportanceTok) * sizeof(uint32_t));
-  q.off_ref_part = take(decode ? Rz * q.ref_nchunk * sizeof(RefinePart) : 0);
+  q.off_ref_part = take(decode ? Rz * q.ref_nwg * sizeof(RefinePart) : 0);
+  q.off_dsub = take(decode ? Rz * q.cc_nchunk * static_cast<size_t>(q.cc_chunk) * sizeof(int32_t) : 0);
+  q.off_dsub_cnt = take(decode ? Rz * q.cc_nchunk * sizeof(uint32_t) : 0);
+  q.off_cut = take(decode ? Rz * sizeof(float) : 0);
+  q.off_lse2r = take(Rz * kG * sizeof(double));
   q.off_ref_stat = take(Rz * sizeof(RefineStat));
-  q.off_dom_cnt = take(decode ? 0 : Rz * sizeof(uint32_t));
   q.off_dom_list = take(decode ? 0 : Rz * kDomCap * sizeof(int32_t));
   const size_t sp_parts = q.sp_nch > 1 ? Rz * q.sp_nch * n_layers * kG : 0;
   q.off_sp_m = take(sp_parts * sizeof(float));
@@ -213,6 +211,12 @@ int hip_status(hipError_t e) {
   return HS2_ERR_HIP;
 }
 
+}  // namespace
+
+int record_hip_error(hipError_t e) { return hip_status(e); }
+
+namespace {
+
 #define HS2_TRY(expr)                        \
   do {                                       \
     const int st_ = hip_status((expr));      \
@@ -225,7 +229,6 @@ int run_full(const Plan& p, const u16* q, const u16* k, const u16* v, u16* out, 
              void* ws, hipStream_t st) {
   HS2_TRY(launch_full_decode_split(p, q, k, v, ws, st));
   HS2_TRY(launch_full_combine(p, out, lse, ws, st));
-  HS2_TRY(launch_lse_refine(p, q, k, lse, ws, st));
   return HS2_OK;
 }
 
@@ -258,6 +261,13 @@ int hs2_full_attn_scores(const hs2_shape* shape, const hs2_bf16* q, const hs2_bf
     return HS2_OK;
   }
   if ((st = run_full(p, q, k, v, out, lse, ws, s)) != HS2_OK) return st;
+  // the refined normaliser (lse and the scores): the selection's subtile-bound
+  // histogram places the refinement's cut and its candidate kernel lists the
+  // dominant subtiles
+  HS2_TRY(launch_subtile_hist(p, ws, s));
+  HS2_TRY(launch_subtile_cand(p, ws, s));
+  HS2_TRY(launch_lse_refine(p, q, k, ws, s));
+  HS2_TRY(launch_lse_finalize(p, lse, ws, s));
   if (scores) HS2_TRY(launch_full_scores(p, q, k, scores, ws, s));
   return HS2_OK;
 }
@@ -313,8 +323,8 @@ int hs2_cross_decoder_step(const hs2_shape* shape, int32_t n_sparse_layers,
     return HS2_OK;
   }
   if ((st = run_full(p, q_full, k, v, out_full, lse, ws, s)) != HS2_OK) return st;
+  HS2_TRY(launch_fused_select(p, q_full, k, idx, n_sel, lse, ws, s));
   if (scores) HS2_TRY(launch_full_scores(p, q_full, k, scores, ws, s));
-  HS2_TRY(launch_fused_select(p, q_full, k, idx, n_sel, ws, s));
   if (n_sparse_layers > 0)
     HS2_TRY(launch_sparse(p, q_sparse, k, v, idx, n_sel, out_sparse, ws, s));
   return HS2_OK;
@@ -354,10 +364,9 @@ int hs2_cross_decoder_step_timed(const hs2_shape* shape, int32_t n_sparse_layers
                              : launch_full_prefill(p, q_full, k, v, out_full, nullptr, ws, s));
     if (rc == HS2_OK) rc = hip_status(hipEventRecord(ev[1], s));
     if (rc == HS2_OK && decode) rc = hip_status(launch_full_combine(p, out_full, nullptr, ws, s));
-    if (rc == HS2_OK && decode) rc = hip_status(launch_lse_refine(p, q_full, k, nullptr, ws, s));
     if (rc == HS2_OK) rc = hip_status(hipEventRecord(ev[2], s));
     if (rc == HS2_OK)
-      rc = hip_status(decode ? launch_fused_select(p, q_full, k, idx, n_sel, ws, s)
+      rc = hip_status(decode ? launch_fused_select(p, q_full, k, idx, n_sel, nullptr, ws, s)
                              : launch_prefill_importance(p, q_full, k, ws, s));
     if (rc == HS2_OK && !decode)
       rc = hip_status(launch_prefill_select(p, q_full, k, idx, n_sel, nullptr, ws, s));
@@ -419,9 +428,8 @@ int hs2_sparse_attn_swa(const hs2_shape* shape, int32_t n_layers, const hs2_bf16
   if (has_local && (!k_loc || !v_loc)) return HS2_ERR_INVALID_ARG;
   if ((st = check_ws(p, ws, ws_bytes)) != HS2_OK) return st;
   (void)hipGetLastError();
-  static const hs2_bf16 kNoRows = 0;   // the window branch reads nothing when there are no rows
-  HS2_TRY(launch_sparse(p, q, k, v, idx, n_sel, out, ws, as_stream(stream),
-                        k_loc ? k_loc : &kNoRows, v_loc ? v_loc : &kNoRows));
+  // (with no local rows the caches may be NULL: the window branch then reads nothing)
+  HS2_TRY(launch_sparse(p, q, k, v, idx, n_sel, out, ws, as_stream(stream), true, k_loc, v_loc));
   return HS2_OK;
 }
 
@@ -433,7 +441,7 @@ int hs2_workspace_region(const hs2_shape* shape, int32_t n_sparse_layers, int32_
   if (!offset || !bytes) return HS2_ERR_INVALID_ARG;
   switch (region) {
     case HS2_WS_LSE2:
-      *offset = p.off_lse2;
+      *offset = p.off_lse2r;
       *bytes = static_cast<size_t>(p.R) * kG * sizeof(double);
       return HS2_OK;
     case HS2_WS_REFINE:

@@ -23,14 +23,18 @@ constexpr int kImportanceTok = 64;  // prefill importance pass: chunk tokens per
 constexpr int kMaxSplits = 1024;   // context splits per row (full layer, decode)
 constexpr int kDefaultCUs = 256;   // compute units assumed when no device can be queried
 // Refinement of the log-normaliser: a key is dominant for head h when its
-// probability under h is at least 2^kDomLog2 (decode, by 16-key subtiles) or
-// 2^kDomLog2Chunk (prefill chunk, by keys); such keys' terms are summed again
-// from exact float64 logits.  A head has at most 2^8 keys of weight 2^-8 or
-// more, so a prefill row has at most 8 * 2^8 dominant keys: the list capacity
-// covers them with room for float32 rounding at the cut.
-constexpr float kDomLog2 = -12.0f;
-constexpr float kDomLog2Chunk = -8.0f;
+// probability under h is at least 2^kDomLog2; such (key, head) terms are
+// summed again from exact float64 logits.  A head has at most 2^8 keys of
+// weight 2^-8 or more, so a prefill row has at most 8 * 2^8 dominant keys: the
+// list capacity covers them with room for float32 rounding at the cut.
+constexpr float kDomLog2 = -8.0f;
+// Decode refines further down, to 2^kDomFloorLog2, as far as a per-row budget
+// of subtiles allows (the heaviest first).
+constexpr float kDomFloorLog2 = -14.0f;
 constexpr int kDomCap = 2304;      // dominant keys listed per prefill row
+// A prefill chunk's selection bands its stored importance allowing for a
+// refinement of lse2 of up to this many octaves (the change is checked).
+constexpr double kDl2Allow = 0x1p-12;
 
 typedef unsigned short u16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -89,8 +93,11 @@ struct Plan {
   size_t off_hist_c, off_cand_y, off_cand_idx, off_cand_cnt, off_band_idx, off_band_key;
   // refinement of lse2 over the dominant keys: decode per-(row, chunk) partial
   // sums (RefinePart); prefill per-row dominant-key lists; per-row statistics
-  int ref_chunk, ref_nchunk;
-  size_t off_ref_part, off_ref_stat, off_dom_cnt, off_dom_list;
+  int ref_nwg;                // decode: refinement work-groups per row
+  size_t off_ref_part, off_ref_stat, off_dom_list;
+  size_t off_dsub, off_dsub_cnt;   // decode: dominant subtiles per (row, candidate chunk)
+  size_t off_cut;            // decode: each row's refinement cut (float, log2 probability)
+  size_t off_lse2r;          // the refined lse2 (float64 [R][8]) the selection ranks with
   // prefill chunk: per-row log2 importance of the older keys (16-bit fixed point), band capacity per row
   size_t off_ybuf;
   size_t off_kmax;           // prefill: largest |k| (bf16 bits) per (batch, KV head)
@@ -113,6 +120,10 @@ struct BridgeArgs {
   int M, n_tok, dm, Hkv;
 };
 
+// Keep e as the calling thread's last HIP error (hs2_last_hip_error) and
+// return HS2_ERR_HIP (or HS2_OK for hipSuccess).
+int record_hip_error(hipError_t e);
+
 // ---------------------------------------------------------------- launchers
 // Each returns the hipError_t of its launches (hipGetLastError()).
 
@@ -128,17 +139,24 @@ hipError_t launch_kv_bridge(const BridgeArgs& a, hipStream_t st);
 // Per-key importance [R][S] (float32), recomputed from q, k and lse2.
 hipError_t launch_full_scores(const Plan& p, const u16* q, const u16* k, float* scores,
                               void* ws, hipStream_t st);
-// Refinement of lse2 over the dominant keys (decode): partial sums per chunk,
-// then the per-row update of lse2, lse (nullable) and the importance bound.
-hipError_t launch_lse_refine(const Plan& p, const u16* q, const u16* k, float* lse, void* ws,
-                             hipStream_t st);
+// Refinement of lse2 over the dominant keys (decode), after the subtile-bound
+// histogram: partial sums per chunk, then the per-row update of lse2 and lse
+// (nullable).
+hipError_t launch_lse_refine(const Plan& p, const u16* q, const u16* k, void* ws, hipStream_t st);
+// The refined lse2 (and lse, nullable) from the refinement's partial sums; the
+// fused selection does the same inside its scoring kernel instead.
+hipError_t launch_lse_finalize(const Plan& p, float* lse, void* ws, hipStream_t st);
+// The first two kernels of the fused decode selection: the subtile-bound
+// histogram, then the candidate subtiles (and the refinement's dominant ones).
+hipError_t launch_subtile_hist(const Plan& p, void* ws, hipStream_t st);
+hipError_t launch_subtile_cand(const Plan& p, void* ws, hipStream_t st);
 // Selection from given float32 scores, compared exactly.
 hipError_t launch_scores_select(const Plan& p, const float* scores, int32_t* idx,
                                 int32_t* n_sel, void* ws, hipStream_t st);
 // Selection of the fused step: candidate subtiles from the maxima, float32
 // rescoring on MFMA, float64 re-ranking near the threshold.
 hipError_t launch_fused_select(const Plan& p, const u16* q, const u16* k, int32_t* idx,
-                               int32_t* n_sel, void* ws, hipStream_t st);
+                               int32_t* n_sel, float* lse, void* ws, hipStream_t st);
 
 // Full attention over a prefill chunk (T > 1): causal flash attention writing
 // out, lse (nullable), lse2 and each head's bound on log2 importance.
@@ -158,9 +176,13 @@ hipError_t launch_prefill_select(const Plan& p, const u16* q, const u16* k, int3
                                  int32_t* n_sel, float* lse, void* ws, hipStream_t st);
 
 // Sparse layers (all n_layers fused: one gather of the selected K/V rows).
+// With window_branch, the previous generation's layer: the selected older
+// tokens plus a separate branch over each layer's local window cache (k_loc,
+// v_loc; NULL when the cache has no rows).
 hipError_t launch_sparse(const Plan& p, const u16* q, const u16* k, const u16* v,
                          const int32_t* idx, const int32_t* n_sel, u16* out, void* ws,
-                         hipStream_t st, const u16* k_loc = nullptr, const u16* v_loc = nullptr);
+                         hipStream_t st, bool window_branch = false, const u16* k_loc = nullptr,
+                         const u16* v_loc = nullptr);
 
 // ---------------------------------------------------------------- device helpers
 #ifdef __HIPCC__
@@ -278,6 +300,68 @@ __device__ __forceinline__ double sum_rows_f64(double v) {
   const auto h16 = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(w >> 32), static_cast<uint32_t>(w >> 32), false, false);
   return join(h16[0], l16[0]) + join(h16[1], l16[1]);
 }
+// The refinement's cut for a decode row, by one wave (the value in every lane):
+// the lowest whole bin of the row's histogram of subtile bounds (kNB bins of
+// kYRange / kNB octave from ybase) down to which at most `budget` subtiles
+// lie, clamped to [kDomFloorLog2, kDomLog2], as a log2 probability.  The
+// selection's candidate kernel (which lists the dominant subtiles) and the
+// refinement (which tests their pairs) both call it on the same histogram.
+__device__ __forceinline__ float refine_cut_wave(const uint32_t* hist_row, float ybase,
+                                                 uint32_t budget) {
+  const int lane = threadIdx.x & 63;
+  constexpr float kBinW = kYRange / kNB;
+  constexpr int kPer = kNB / 64;
+  const int floor_bin = max(0, min(kNB, static_cast<int>(ceilf((kDomFloorLog2 - ybase) / kBinW))));
+  const int cap_bin = max(0, min(kNB, static_cast<int>(ceilf((kDomLog2 - ybase) / kBinW))));
+  // lane l holds bins kNB-1-kPer*l .. kNB-kPer-kPer*l (the top bins in lane 0)
+  uint32_t lsum = 0;
+  for (int i = 0; i < kPer; ++i) lsum += hist_row[kNB - 1 - kPer * lane - i];
+  uint32_t incl = lsum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  const uint64_t over = __ballot(incl > budget);
+  int b_cut = 0;   // the lowest bin whose count from the top stays within the budget
+  if (over) {
+    // the owner lane's bins, top down, one per lane, and their running count
+    const int owner = __builtin_ctzll(over);
+    const uint32_t above = __shfl(incl - lsum, owner);
+    const int top = kNB - 1 - kPer * owner;
+    const uint32_t cb = lane < kPer ? hist_row[top - lane] : 0u;
+    uint32_t run = cb;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t o = __shfl_up(run, off);
+      if (lane >= off) run += o;
+    }
+    const uint64_t hit = __ballot(lane < kPer && above + run > budget);
+    b_cut = top - __builtin_ctzll(hit) + 1;   // the owner's bins reach past the budget
+  }
+  const int bin = max(min(b_cut, cap_bin), floor_bin);
+  return ybase + static_cast<float>(bin) * kBinW;
+}
+// Sum of head h's refinement partials of one row (n_parts of them), by one
+// wave, in every lane: lane l adds partials l, l + 64, ... in order, then the
+// fixed pairing of a lane-xor butterfly.
+__device__ __forceinline__ double refine_head_sum(const RefinePart* __restrict__ pr, int n_parts,
+                                                  int h) {
+  const int lane = threadIdx.x & 63;
+  double c = 0.0;
+  for (int i = lane; i < n_parts; i += 64) c += pr[i].corr[h];
+  c += dpp_f64<0xB1>(c);     // lane ^ 1
+  c += dpp_f64<0x4E>(c);     // lane ^ 2
+  c += dpp_f64<0x141>(c);    // the other quad of the 8
+  c += dpp_f64<0x128>(c);    // lane ^ 8 within the row of 16
+  return sum_rows_f64(c);    // ^ 32, then ^ 16
+}
+// The refinement's budget of subtiles per decode row: a twentieth of them, at least 64.
+__host__ __device__ __forceinline__ uint32_t refine_budget(int64_t S) {
+  const int64_t n = (S + 15) / 16 / 20;
+  return static_cast<uint32_t>(n > 64 ? n : 64);
+}
+
 // Wait until this wave's outstanding LDS operations are done, and keep the
 // compiler from moving memory accesses across this point.
 __device__ __forceinline__ void lds_fence_wave() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }

@@ -366,11 +366,9 @@ __device__ __forceinline__ void phase_barrier() {
 __global__ __launch_bounds__(kIThreads, 1) void prefill_importance_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const double* __restrict__ lse2,
     const float* __restrict__ ytop_h, u16* __restrict__ y, uint32_t* __restrict__ kmax,
-    uint32_t* __restrict__ dom_cnt, int32_t* __restrict__ dom_list,
     int64_t S, int64_t Spad, int T, int Hkv, int w, int n_tblk, float c2_hi, int64_t kvp) {
   __shared__ __align__(16) u16 kbuf[2][kPKeys * kD];
   __shared__ uint32_t s_kmax[kIWaves];
-  __shared__ uint32_t s_dom[kImportanceTok];   // dominant keys found per token of the block
   constexpr int QB = kIQB;
   constexpr int kTok = kImportanceTok;
   const int tid = threadIdx.x;
@@ -392,9 +390,6 @@ __global__ __launch_bounds__(kIThreads, 1) void prefill_importance_kernel(
   // y in fixed-point steps plus 0.5 is s c2 2^10 + (0.5 - 2^10 (lse2_h + ybase)):
   // one fma per head
   float nl2r[QB][4];     // 0.5 - 2^10 (lse2_h + ybase) for the lane's 4 heads
-  float ydom[QB];        // the fixed-point value (plus 0.5) of y = kDomLog2
-  int tloc[QB];          // the lane's token within the block
-  size_t rowi[QB];
   u16* yrow[QB];
 #pragma unroll
   for (int qbk = 0; qbk < QB; ++qbk) {
@@ -419,9 +414,6 @@ __global__ __launch_bounds__(kIThreads, 1) void prefill_importance_kernel(
     for (int i = 0; i < 4; ++i)
       nl2r[qbk][i] = fmaf(-static_cast<float>(lse2[row * kG + 4 * (grp & 1) + i]),
                           static_cast<float>(1 << kYFixBits), yoff);
-    ydom[qbk] = (kDomLog2Chunk - ybase) * static_cast<float>(1 << kYFixBits) + 0.5f;
-    tloc[qbk] = t - tb * kTok;
-    rowi[qbk] = row;
     yrow[qbk] = y ? y + row * Spad : nullptr;
   }
   const int t_last = min(T - 1, tb * kTok + kTok - 1);
@@ -463,7 +455,6 @@ __global__ __launch_bounds__(kIThreads, 1) void prefill_importance_kernel(
     }
   };
 
-  if (tid < kTok) s_dom[tid] = 0u;
   // prologue: tile 0 by every wave; group B loads its rows of tile 1 in the
   // phase it spends behind group A
   stage_load(0);
@@ -522,14 +513,6 @@ __global__ __launch_bounds__(kIThreads, 1) void prefill_importance_kernel(
         // land in the row's unread tail (key < Spad), and a block past
         // the chunk's end repeats the last token, value for value
         yrow[qbk][key] = v;
-        // a key that some head weights by 2^kDomLog2Chunk or more (window keys
-        // included): listed for the refinement of lse2 (rare; the block's
-        // token counters are in LDS)
-        if (dom_list && t_ok[qbk] && key <= P[qbk] && yy >= ydom[qbk]) {
-          const uint32_t slot = atomicAdd(&s_dom[tloc[qbk]], 1u);
-          if (slot < static_cast<uint32_t>(kDomCap))
-            dom_list[rowi[qbk] * kDomCap + slot] = static_cast<int32_t>(key);
-        }
       }
     }
   };
@@ -572,12 +555,6 @@ __global__ __launch_bounds__(kIThreads, 1) void prefill_importance_kernel(
     }
     epilogue(sacc, static_cast<int64_t>(n_tiles - 1) * kPKeys);
     phase_barrier();
-  }
-  if (dom_cnt) {
-    __syncthreads();   // every listing is done
-    const int tt = tb * kTok + tid;
-    if (tid < kTok && tt < T)
-      dom_cnt[(static_cast<size_t>(b) * T + tt) * Hkv + g] = s_dom[tid];
   }
   if (kmax) {
     uint32_t m = max(static_cast<uint32_t>(kabs[0]), static_cast<uint32_t>(kabs[1]));
@@ -734,9 +711,7 @@ hipError_t launch_prefill_importance(const Plan& p, const u16* q, const u16* k, 
                      reinterpret_cast<const double*>(w + p.off_lse2),
                      reinterpret_cast<const float*>(w + p.off_ytop),
                      reinterpret_cast<u16*>(w + p.off_ybuf),
-                     reinterpret_cast<uint32_t*>(w + p.off_kmax),
-                     reinterpret_cast<uint32_t*>(w + p.off_dom_cnt),
-                     reinterpret_cast<int32_t*>(w + p.off_dom_list), p.S, p.Spad, p.T, p.Hkv, p.w,
+                     reinterpret_cast<uint32_t*>(w + p.off_kmax), p.S, p.Spad, p.T, p.Hkv, p.w,
                      n_tblk, c2_hi, p.kvp);
   return hipGetLastError();
 }

@@ -722,18 +722,23 @@ __global__ __launch_bounds__(kThreads) void subtile_hist_kernel(
 // key that can be selected lies in one.  grid (cc chunks, R); each work-group
 // lists the candidates of its range of subtiles into its own region of the
 // row's list and counts them in ccnt.  Work-group 0 of a row also writes the
-// row's lower bin for the next kernel.
+// row's lower bin for the next kernel.  The same pass lists, in dlist / dcnt,
+// the subtiles whose bound reaches the refinement's cut (refine_cut_wave): the
+// ones the refinement of lse2 sums again.
 __global__ __launch_bounds__(kThreads) void subtile_cand_kernel(
     const float* __restrict__ stmax, const double* __restrict__ lse2,
     const float* __restrict__ ytop_h, const uint32_t* __restrict__ hist,
     int32_t* __restrict__ clist, uint32_t* __restrict__ ccnt, int32_t* __restrict__ lo_out,
-    int64_t S, int64_t Spad, int T, int Hkv, int topk, int w, int chunk, int n_chunks) {
+    int32_t* __restrict__ dlist, uint32_t* __restrict__ dcnt, float* __restrict__ cut_out,
+    uint32_t budget, int64_t S, int64_t Spad, int T, int Hkv, int topk, int w, int chunk,
+    int n_chunks) {
   __shared__ uint32_t lh[kNB];
   __shared__ float lse2f[kG];
   __shared__ float s_ybase;
   __shared__ int s_lo;
   __shared__ uint32_t s_cnt[2][16];
   __shared__ uint32_t s_base[4];
+  __shared__ float s_cut;
   const int r = blockIdx.y;
   const int tid = threadIdx.x;
   const int64_t first = row_first(row_pos(r, T, Hkv, S), w);
@@ -742,8 +747,15 @@ __global__ __launch_bounds__(kThreads) void subtile_cand_kernel(
   const int64_t st0 = static_cast<int64_t>(blockIdx.x) * chunk;
   const int64_t st1 = min(n_sub, st0 + chunk);
   uint32_t* cnt = ccnt + static_cast<size_t>(r) * n_chunks + blockIdx.x;
+  uint32_t* dct = dcnt + static_cast<size_t>(r) * n_chunks + blockIdx.x;
   if (topk <= 0 || first == 0 || st0 >= st1) {
-    if (tid == 0) *cnt = 0u;
+    if (tid == 0) {
+      *cnt = 0u;
+      *dct = 0u;
+      // rows without candidates: the refinement takes the window's subtiles
+      // down to the lowest cut
+      if (blockIdx.x == 0 && (topk <= 0 || first == 0)) cut_out[r] = kDomFloorLog2;
+    }
     return;
   }
   const bool all_mode = n_counted <= topk;
@@ -752,11 +764,11 @@ __global__ __launch_bounds__(kThreads) void subtile_cand_kernel(
   uint32_t hv[kNB / kThreads];
 #pragma unroll
   for (int u = 0; u < kNB / kThreads; ++u)
-    hv[u] = all_mode ? 0u : hist[static_cast<size_t>(r) * kNB + tid + kThreads * u];
+    hv[u] = hist[static_cast<size_t>(r) * kNB + tid + kThreads * u];
   f32x4 mx[2];
   {
     const int64_t st = st0 + tid;
-    const bool ld = !all_mode && st < min(st1, n_counted);
+    const bool ld = st < st1;
     mx[0] = ld ? *reinterpret_cast<const f32x4*>(stmax_row + st * kG) : f32x4{0.f, 0.f, 0.f, 0.f};
     mx[1] = ld ? *reinterpret_cast<const f32x4*>(stmax_row + st * kG + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -765,27 +777,37 @@ __global__ __launch_bounds__(kThreads) void subtile_cand_kernel(
 #pragma unroll
   for (int u = 0; u < kNB / kThreads; ++u) lh[tid + kThreads * u] = hv[u];
   __syncthreads();
-  if (!all_mode && tid < 64) {
-    const KthBin kb = kth_bin_wave(lh, static_cast<uint32_t>(topk));
-    if (tid == 0) s_lo = max(0, kb.bstar - 1);
+  if (tid < 64) {
+    if (!all_mode) {
+      const KthBin kb = kth_bin_wave(lh, static_cast<uint32_t>(topk));
+      if (tid == 0) s_lo = max(0, kb.bstar - 1);
+    }
+  } else if (tid < 128) {   // the second wave, meanwhile
+    const float cut = refine_cut_wave(lh, s_ybase, budget);
+    if (tid == 64) s_cut = cut;
   }
   __syncthreads();
   const int lo_bin = all_mode ? 0 : s_lo;
-  if (blockIdx.x == 0 && tid == 0) lo_out[r] = lo_bin;
+  if (blockIdx.x == 0 && tid == 0) {
+    lo_out[r] = lo_bin;
+    cut_out[r] = s_cut;
+  }
   const float ybase = s_ybase;
+  const float cut = s_cut;
   float l2v[kG];
 #pragma unroll
   for (int h = 0; h < kG; ++h) l2v[h] = lse2f[h];
   int32_t* out = clist + (static_cast<size_t>(r) * n_chunks + blockIdx.x) * chunk;
-  uint32_t written = 0;
+  int32_t* dout = dlist + (static_cast<size_t>(r) * n_chunks + blockIdx.x) * chunk;
+  uint32_t written = 0, dwritten = 0;
   for (int64_t sr0 = st0; sr0 < st1; sr0 += kThreads) {
     const int64_t st = sr0 + tid;
     if (sr0 != st0) {
-      const bool ld = !all_mode && st < min(st1, n_counted);
+      const bool ld = st < st1;
       mx[0] = ld ? *reinterpret_cast<const f32x4*>(stmax_row + st * kG) : f32x4{0.f, 0.f, 0.f, 0.f};
       mx[1] = ld ? *reinterpret_cast<const f32x4*>(stmax_row + st * kG + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    bool cand = false;
+    bool cand = false, dom = false;
     if (st < st1) {
       float ub = mx[0][0] - l2v[0];
       ub = fmaxf(ub, mx[0][1] - l2v[1]);
@@ -797,13 +819,19 @@ __global__ __launch_bounds__(kThreads) void subtile_cand_kernel(
       ub = fmaxf(ub, mx[1][3] - l2v[7]);
       cand = all_mode || st >= n_counted ||
              static_cast<int>(key_from_log2(ub, ybase) >> kBinShift) >= lo_bin;
+      dom = ub >= cut;
     }
-    uint32_t o_list, o_dummy;
-    reserve_two(cand ? 1u : 0u, 0u, nullptr, nullptr, s_cnt, s_base, o_list, o_dummy);
+    uint32_t o_list, o_dom;
+    reserve_two(cand ? 1u : 0u, dom ? 1u : 0u, nullptr, nullptr, s_cnt, s_base, o_list, o_dom);
     if (cand) out[written + o_list] = static_cast<int32_t>(st);   // ascending: thread order
+    if (dom) dout[dwritten + o_dom] = static_cast<int32_t>(st);
     written += s_base[2];
+    dwritten += s_base[3];
   }
-  if (tid == 0) *cnt = written;
+  if (tid == 0) {
+    *cnt = written;
+    *dct = dwritten;
+  }
 }
 
 // The exact importance of the candidates' keys.  grid (NS, R): work-group w of
@@ -829,6 +857,8 @@ static_assert(kStageSub / (kThreads / 64) <= 64, "a wave's subtiles of a pass fi
 __global__ __launch_bounds__(kThreads, 3) void subtile_score_kernel(
     const int32_t* __restrict__ lo_in, const int32_t* __restrict__ clist,
     const uint32_t* __restrict__ ccnt, const double* __restrict__ lse2,
+    const RefinePart* __restrict__ ref_part, int ref_nparts, double* __restrict__ lse2r,
+    float* __restrict__ lse_out, RefineStat* __restrict__ ref_stat,
     const float* __restrict__ ytop_h, uint32_t* __restrict__ hist_c, const u16* __restrict__ q,
     const u16* __restrict__ k, double* __restrict__ cand_y, int32_t* __restrict__ cand_idx,
     uint32_t* __restrict__ cand_cnt, int64_t S, int T, int Hkv, int topk, int w,
@@ -842,6 +872,7 @@ __global__ __launch_bounds__(kThreads, 3) void subtile_score_kernel(
   __shared__ float s_ybase;
   __shared__ uint32_t s_cnt[2][16];
   __shared__ uint32_t s_base[4];
+  __shared__ double s_l2[kG];
   const int r = blockIdx.y;
   const int tid = threadIdx.x;
   // wave index in a scalar register: the per-wave loops below are uniform
@@ -849,6 +880,34 @@ __global__ __launch_bounds__(kThreads, 3) void subtile_score_kernel(
   const int col = lane & 15, grp = lane >> 4;
   const int64_t first = row_first(row_pos(r, T, Hkv, S), w);
   uint32_t* cnt = cand_cnt + static_cast<size_t>(r) * n_chunks + blockIdx.x;
+  // The refined lse2 that the keys are ranked with: lse2 + log2(1 + the
+  // refinement's partial sums), in every work-group of the row (the same
+  // arithmetic as the refinement's own finishing kernel); work-group 0 also
+  // writes it, lse for the caller and the row's refinement statistics.
+  {
+    const RefinePart* pr = ref_part + static_cast<size_t>(r) * ref_nparts;
+    for (int h = wave; h < kG; h += kThreads / 64) {
+      const double c = refine_head_sum(pr, ref_nparts, h);
+      if (lane == 0) s_l2[h] = lse2[static_cast<size_t>(r) * kG + h] + log1p(c) * M_LOG2E;
+    }
+    if (blockIdx.x == 0 && wave == 0) {
+      uint32_t nd = 0, nb = 0;
+      for (int i = lane; i < ref_nparts; i += 64) {
+        nd += pr[i].n_dom;
+        nb += pr[i].n_bad;
+      }
+      for (int off = 32; off > 0; off >>= 1) {
+        nd += __shfl_xor(nd, off);
+        nb += __shfl_xor(nb, off);
+      }
+      if (lane == 0) ref_stat[r] = RefineStat{nd, nb, 0u, 0u};
+    }
+    __syncthreads();
+    if (blockIdx.x == 0 && tid < kG) {
+      lse2r[static_cast<size_t>(r) * kG + tid] = s_l2[tid];
+      if (lse_out) lse_out[static_cast<size_t>(r) * kG + tid] = static_cast<float>(s_l2[tid] * M_LN2);
+    }
+  }
   if (topk <= 0 || first == 0) {
     if (tid == 0) *cnt = 0u;
     return;
@@ -876,9 +935,8 @@ __global__ __launch_bounds__(kThreads, 3) void subtile_score_kernel(
   const float c2f = static_cast<float>(c2);
   float l2f[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    l2f[i] = 4 * grp + i < kG ? static_cast<float>(lse2[static_cast<size_t>(r) * kG + 4 * grp + i]) : 0.f;
-  const double l2h = lse2[static_cast<size_t>(r) * kG + (lane >> 3)];
+  for (int i = 0; i < 4; ++i) l2f[i] = 4 * grp + i < kG ? static_cast<float>(s_l2[4 * grp + i]) : 0.f;
+  const double l2h = s_l2[lane >> 3];
   u32x4 qh2[2];   // packed bf16, widened at each use
   {
     const u16* qh = q + (static_cast<size_t>(r) * kG + (lane >> 3)) * kD + 16 * (lane & 7);
@@ -1636,8 +1694,8 @@ __device__ __forceinline__ uint32_t u16_at(const u32x4 (&v)[2], int e) {
 
 __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
     const u16* __restrict__ ybuf, const uint32_t* __restrict__ kmax, int n_ib,
-    double* __restrict__ lse2, float* __restrict__ lse_out, const uint32_t* __restrict__ dom_cnt,
-    const int32_t* __restrict__ dom_list, RefineStat* __restrict__ stat,
+    const double* __restrict__ lse2, double* __restrict__ lse2r, float* __restrict__ lse_out,
+    const float* __restrict__ ytop_h, int32_t* __restrict__ dom_list, RefineStat* __restrict__ stat,
     const u16* __restrict__ q, const u16* __restrict__ k, int32_t* __restrict__ band_idx,
     uint64_t* __restrict__ band_key, int64_t band_cap, int32_t* __restrict__ idx_out,
     int32_t* __restrict__ nsel_out, int64_t S, int64_t Spad, int T, int Hkv, int topk, int w,
@@ -1650,6 +1708,8 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
   __shared__ double qd[kG * kD];
   __shared__ double l2s[kG];
   __shared__ double s_dl2[kG];
+  __shared__ unsigned long long s_corr[kG];   // each head's refinement, fixed point 2^-60
+  __shared__ uint32_t s_ndom;
   __shared__ float s_qn[2][kRowThreads / 64];
   __shared__ uint32_t h256[256];
   __shared__ uint32_t s_red[4];
@@ -1678,47 +1738,53 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
   int32_t* out = idx_out + static_cast<size_t>(r) * cap;
   const u16* qr = q + static_cast<size_t>(r) * kG * kD;
   const u16* kr = k + (static_cast<size_t>(b) * Hkv + g) * static_cast<size_t>(kvp) * kD;
-  // ---- refinement of lse2 over the row's dominant keys (listed by the
-  // importance pass: some head gives them at least 2^kDomLog2Chunk of its
-  // weight).  The attention kernel summed 2^(a c2_hi - m) for each key, a the
-  // float32 MFMA logit; each listed key's term is replaced by the one of its
-  // float64 logit from exact bf16 products.  a is recomputed by the attention
-  // kernel's MFMA sequence on the same operands (same bits wherever the
-  // element sits in the tile).  The other keys, each below 2^kDomLog2Chunk of
-  // the total, keep their float32 terms: their independent logit errors
-  // average out in the weighted sum.
+  const u16* yr = ybuf + static_cast<size_t>(r) * Spad;
+  // ---- refinement of lse2 over the row's dominant keys: those that some head
+  // gives 2^kDomLog2 of its weight or more, found from the stored importance
+  // (the pass below lists the older ones, refine_row the window's).  The
+  // attention kernel summed 2^(a c2_hi - m) for each key, a the float32 MFMA
+  // logit; each listed key's term is replaced by the one of its float64 logit
+  // from exact bf16 products.  a is recomputed by the attention kernel's MFMA
+  // sequence on the same operands (same bits wherever the element sits in the
+  // tile).  The other keys, each below 2^kDomLog2 of the total, keep their
+  // float32 terms: their independent logit errors average out in the
+  // weighted sum.  The terms are summed as 64-bit fixed point (2^-60), so the
+  // sum does not depend on the order the keys were listed in.  The stored
+  // values were formed with the unrefined lse2, so the selection's band
+  // allows for a change of up to kDl2Allow octave; a larger change is counted
+  // in the row's statistics.
+  for (int i = tid; i < kG * kD; i += kRowThreads)
+    qd[i] = static_cast<double>(bf16_bits_to_f32(qr[i]));
+  if (tid < kG) {
+    l2s[tid] = lse2[static_cast<size_t>(r) * kG + tid];
+    s_corr[tid] = 0ull;
+  }
+  if (tid == 0) s_ndom = 0u;
+  // the stored value of importance 2^kDomLog2 (as the importance pass stores:
+  // 2^10 steps per octave above the row's top log-weight minus 64)
+  int vdom;
   {
-    constexpr int kE = kMaxSel / kRowThreads;            // sort slots per thread
-    static_assert(kDomCap <= kMaxSel, "the list sorts in one block sort");
-    for (int i = tid; i < kG * kD; i += kRowThreads)
-      qd[i] = static_cast<double>(bf16_bits_to_f32(qr[i]));
-    const uint32_t n_raw = dom_cnt[r];
-    const uint32_t n_dom = min(n_raw, static_cast<uint32_t>(kDomCap));
-    int32_t* dk = up;                                     // the list, ascending
-    double* gsum = reinterpret_cast<double*>(pool);       // [group of 16 keys][kG]
-    if (tid < kG) l2s[tid] = lse2[static_cast<size_t>(r) * kG + tid];
-    // ascending key order (the keys are distinct), so the sums below have a
-    // fixed order
-    {
-      int32_t v[kE];
-#pragma unroll
-      for (int e = 0; e < kE; ++e) {
-        const uint32_t ii = static_cast<uint32_t>(kE * tid + e);
-        v[e] = ii < n_dom ? dom_list[static_cast<size_t>(r) * kDomCap + ii] : 0x7FFFFFFF;
-      }
-      if (n_dom > 1) block_bitonic<kE>(v, bw, static_cast<int>(n_dom), IntLess{});
-#pragma unroll
-      for (int e = 0; e < kE; ++e) {
-        const uint32_t ii = static_cast<uint32_t>(kE * tid + e);
-        if (ii < n_dom) dk[ii] = v[e];
-      }
-    }
+    float yt = -INFINITY;
+    for (int h = 0; h < kG; ++h) yt = fmaxf(yt, ytop_h[static_cast<size_t>(r) * kG + h]);
+    const float vd = (kDomLog2 - (yt - kYRange)) * static_cast<float>(1 << kYFixBits);
+    vdom = static_cast<int>(fminf(fmaxf(floorf(vd), 0.f), 65536.f));
+  }
+  int32_t* dlr = dom_list + static_cast<size_t>(r) * kDomCap;
+  auto list_dom = [&](int64_t key) {
+    const uint32_t slot = atomicAdd(&s_ndom, 1u);
+    if (slot < static_cast<uint32_t>(kDomCap)) dlr[slot] = static_cast<int32_t>(key);
+  };
+  auto refine_row = [&]() {
+    // the window's dominant keys
+    for (int64_t j = first + tid; j <= P; j += kRowThreads)
+      if (static_cast<int>(yr[j]) >= vdom) list_dom(j);
     __syncthreads();
+    const uint32_t n_raw = s_ndom;
+    const uint32_t n_dom = min(n_raw, static_cast<uint32_t>(kDomCap));
     const int col = lane & 15, grp = lane >> 4;
-    const uint32_t n_grp = (n_dom + 15) / 16;
-    for (uint32_t gi = wave; gi < n_grp; gi += kRowThreads / 64) {
+    for (uint32_t gi = wave; 16 * gi < n_dom; gi += kRowThreads / 64) {
       // 16 keys as the A operand rows, the 8 heads as B columns (8 .. 15 zero)
-      const int32_t key = dk[min(16 * gi + col, n_dom - 1)];
+      const int32_t key = dlr[min(16 * gi + col, n_dom - 1)];
       bf16x8 ka[4], qb[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -1729,9 +1795,7 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int c = 0; c < 4; ++c) acc = mfma_16x16x32(ka[c], qb[c], acc);
-      // lane (head col, grp) holds keys 16 gi + 4 grp + i: its four terms in
-      // key order, then the group's sum over grp in a fixed pairing
-      double part = 0.0;
+      // lane (head col, grp) holds keys 16 gi + 4 grp + i
       if (col < kG) {
         const double l2h = l2s[col];
         const double* qh = qd + col * kD;
@@ -1739,7 +1803,7 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
         for (int i = 0; i < 4; ++i) {
           const uint32_t e = 16 * gi + 4 * grp + i;
           if (e >= n_dom) break;
-          const u16* krow = kr + static_cast<size_t>(dk[e]) * kD;
+          const u16* krow = kr + static_cast<size_t>(dlr[e]) * kD;
           double dot = 0.0;
 #pragma unroll 2
           for (int d8 = 0; d8 < kD / 8; ++d8) {
@@ -1752,28 +1816,33 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
                         dot);
             }
           }
+          // the term's change 2^(y - lse2) - 2^(a2 - lse2) = p (e^d - 1), d = (y - a2) ln 2,
+          // p = 2^(a2 - lse2); |d| is below 1e-4, so d + d^2 / 2 leaves 2e-13 of p
           const double a2 = static_cast<double>(acc[i]) * static_cast<double>(c2_hi);   // exact
-          part += exp2(c2 * dot - l2h) - exp2(a2 - l2h);
+          const double dd = (c2 * dot - a2) * M_LN2;
+          const float pw = __builtin_amdgcn_exp2f(static_cast<float>(a2 - l2h));
+          const double term = static_cast<double>(pw) * (dd + 0.5 * dd * dd);
+          atomicAdd(&s_corr[col], static_cast<unsigned long long>(llrint(term * 0x1p60)));
         }
       }
-      part += __shfl_xor(part, 16);
-      part += __shfl_xor(part, 32);
-      if (grp == 0 && col < kG) gsum[gi * kG + col] = part;
     }
     __syncthreads();
     if (tid < kG) {
-      double c = 0.0;
-      for (uint32_t gi = 0; gi < n_grp; ++gi) c += gsum[gi * kG + tid];
+      const double c = static_cast<double>(static_cast<long long>(s_corr[tid])) * 0x1p-60;
       const double d = log1p(c) * M_LOG2E;
       const double l2 = l2s[tid] + d;
       l2s[tid] = l2;
       s_dl2[tid] = d;
-      lse2[static_cast<size_t>(r) * kG + tid] = l2;
+      lse2r[static_cast<size_t>(r) * kG + tid] = l2;
       if (lse_out) lse_out[static_cast<size_t>(r) * kG + tid] = static_cast<float>(l2 * M_LN2);
     }
-    if (tid == 0) stat[r] = RefineStat{n_dom, 0u, n_raw - n_dom, 0u};
     __syncthreads();
-  }
+    if (tid == 0) {
+      uint32_t big = 0;
+      for (int h = 0; h < kG; ++h) big += fabs(s_dl2[h]) > kDl2Allow ? 1u : 0u;
+      stat[r] = RefineStat{n_dom, big, n_raw - n_dom, 0u};
+    }
+  };
   uint32_t n_keep = 0;
   if (topk > 0 && first > 0) {
     for (int i = tid; i < kPNB; i += kRowThreads) lh[i] = 0u;
@@ -1819,26 +1888,24 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
       // additions of exact bf16 products, the scale's dropped low part and
       // the fma each cost 2^-24 of |s| c2 <= max|k| sum|q_h| c2; lse2's
       // rounding to float32 costs 2^-24 |lse2|, counted twice.
-      double qn = 0.0, l2m = 0.0, dl2 = 0.0;
+      double qn = 0.0, l2m = 0.0;
       for (int h = 0; h < kG; ++h) {
         const int wv = 2 * (h & 3);
         const int u = h >> 2;
         qn = fmax(qn, static_cast<double>(s_qn[u][wv]) + static_cast<double>(s_qn[u][wv + 1]));
         l2m = fmax(l2m, fabs(l2s[h]));
-        dl2 = fmax(dl2, fabs(s_dl2[h]));
       }
       const double km = static_cast<double>(bf16_bits_to_f32(static_cast<u16>(s_km)));
       // sum|q| was taken in float32: allow 2^-20 relative for its rounding.
-      // The stored values were formed with lse2 before its refinement: the
-      // refinement's change dl2 adds to their error against the exact
-      // importance ranked here.
-      const double d32 = 0x1p-24 * (130.0 * km * qn * (1.0 + 0x1p-20) * c2 + 2.0 * l2m) + dl2;
+      // The stored values were formed with lse2 before its refinement (after
+      // the pass): its change, at most kDl2Allow (checked), adds to their
+      // error against the exact importance ranked here.
+      const double d32 = 0x1p-24 * (130.0 * km * qn * (1.0 + 0x1p-20) * c2 + 2.0 * l2m) + kDl2Allow;
       const double steps = 1.5 + 0x1p-5 + d32 * static_cast<double>(1 << kYFixBits);
       s_E = static_cast<int>(fmin(ceil(2.0 * steps) + 1.0, 65536.0));
     }
     __syncthreads();
     const int E = s_E;
-    const u16* yr = ybuf + static_cast<size_t>(r) * Spad;
     // 16 values per thread and round, as two 16-byte loads; the next round's
     // loads are issued before this round is processed
     const int64_t rounds = (first + 16 * kRowThreads - 1) / (16 * kRowThreads);
@@ -1894,10 +1961,14 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
           fl = s_floor;
         }
         const int vmin = (fl << kVBinShift) - E;
-        uint32_t ml = 0;
+        uint32_t ml = 0, md = 0;
 #pragma unroll
-        for (int e = 0; e < kV; ++e)
-          ml |= static_cast<uint32_t>(e < nv && static_cast<int>(val_at(ycur, e)) >= vmin) << e;
+        for (int e = 0; e < kV; ++e) {
+          const int v = static_cast<int>(val_at(ycur, e));
+          ml |= static_cast<uint32_t>(e < nv && v >= vmin) << e;
+          md |= static_cast<uint32_t>(e < nv && v >= vdom) << e;
+        }
+        for (uint32_t m = md; m; m &= m - 1) list_dom(i0 + __builtin_ctz(m));   // rare
         uint32_t ol, o_dummy, tot, t_dummy;
         block_offsets2<kRowThreads / 64>(__popc(ml), 0u, s_off[rr & 1], ol, o_dummy, tot, t_dummy);
         // the round's atomics are complete: raise the floor
@@ -1922,6 +1993,7 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
         for (int u = 0; u < 4; ++u) ycur[u] = ynxt[u];
       }
     }
+    refine_row();   // (l2s refined before the band is ranked with it)
     const bool listed = n_list <= static_cast<uint32_t>(kPList);
     if (tid < 128) h256[tid] = 0u;
     __syncthreads();
@@ -2172,6 +2244,9 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
       }
       n_keep = min(n_up + n_w, static_cast<uint32_t>(topk));
     }
+  } else {
+    __syncthreads();
+    refine_row();
   }
   const int n_total = static_cast<int>(n_keep) + static_cast<int>(static_cast<int64_t>(P) - first + 1);
   for (int i = static_cast<int>(n_keep) + tid; i < cap; i += kRowThreads)
@@ -2450,8 +2525,37 @@ hipError_t launch_scores_select(const Plan& p, const float* scores, int32_t* idx
   return hipGetLastError();
 }
 
+hipError_t launch_subtile_hist(const Plan& p, void* ws, hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  hipLaunchKernelGGL(subtile_hist_kernel, dim3(p.hs_nchunk, p.R), dim3(kThreads), 0, st,
+                     reinterpret_cast<const float*>(w + p.off_stmax),
+                     reinterpret_cast<const double*>(w + p.off_lse2),
+                     reinterpret_cast<const float*>(w + p.off_ytop),
+                     reinterpret_cast<uint32_t*>(w + p.off_hist),
+                     reinterpret_cast<uint32_t*>(w + p.off_hist_c), p.S, p.Spad, p.T, p.Hkv, p.k,
+                     p.w, p.hs_chunk);
+  return hipGetLastError();
+}
+
+hipError_t launch_subtile_cand(const Plan& p, void* ws, hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  hipLaunchKernelGGL(subtile_cand_kernel, dim3(p.cc_nchunk, p.R), dim3(kThreads), 0, st,
+                     reinterpret_cast<const float*>(w + p.off_stmax),
+                     reinterpret_cast<const double*>(w + p.off_lse2),
+                     reinterpret_cast<const float*>(w + p.off_ytop),
+                     reinterpret_cast<const uint32_t*>(w + p.off_hist),
+                     reinterpret_cast<int32_t*>(w + p.off_clist),
+                     reinterpret_cast<uint32_t*>(w + p.off_ccnt),
+                     reinterpret_cast<int32_t*>(w + p.off_lo),
+                     reinterpret_cast<int32_t*>(w + p.off_dsub),
+                     reinterpret_cast<uint32_t*>(w + p.off_dsub_cnt),
+                     reinterpret_cast<float*>(w + p.off_cut), refine_budget(p.S), p.S, p.Spad,
+                     p.T, p.Hkv, p.k, p.w, p.cc_chunk, p.cc_nchunk);
+  return hipGetLastError();
+}
+
 hipError_t launch_fused_select(const Plan& p, const u16* q, const u16* k, int32_t* idx,
-                               int32_t* n_sel, void* ws, hipStream_t st) {
+                               int32_t* n_sel, float* lse, void* ws, hipStream_t st) {
   char* w = static_cast<char*>(ws);
   const float* stmax = reinterpret_cast<const float*>(w + p.off_stmax);
   const double* lse2 = reinterpret_cast<const double*>(w + p.off_lse2);
@@ -2462,20 +2566,21 @@ hipError_t launch_fused_select(const Plan& p, const u16* q, const u16* k, int32_
   int32_t* cand_idx = reinterpret_cast<int32_t*>(w + p.off_cand_idx);
   uint32_t* cand_cnt = reinterpret_cast<uint32_t*>(w + p.off_cand_cnt);
   const double c2 = p.scale * 1.4426950408889634;  // scale * log2(e)
-  hipLaunchKernelGGL(subtile_hist_kernel, dim3(p.hs_nchunk, p.R), dim3(kThreads), 0, st, stmax,
-                     lse2, ytop, hist, hist_c, p.S, p.Spad, p.T, p.Hkv, p.k, p.w, p.hs_chunk);
-  hipError_t e = hipGetLastError();
+  // the subtile-bound histogram, the candidate (and dominant) subtiles, then
+  // the refinement of lse2 before anything ranks keys with it
+  hipError_t e = launch_subtile_hist(p, ws, st);
   if (e != hipSuccess) return e;
+  if ((e = launch_subtile_cand(p, ws, st)) != hipSuccess) return e;
+  if ((e = launch_lse_refine(p, q, k, ws, st)) != hipSuccess) return e;
   int32_t* clist = reinterpret_cast<int32_t*>(w + p.off_clist);
   uint32_t* ccnt = reinterpret_cast<uint32_t*>(w + p.off_ccnt);
   int32_t* lo = reinterpret_cast<int32_t*>(w + p.off_lo);
-  hipLaunchKernelGGL(subtile_cand_kernel, dim3(p.cc_nchunk, p.R), dim3(kThreads), 0, st, stmax,
-                     lse2, ytop, hist, clist, ccnt, lo, p.S, p.Spad, p.T, p.Hkv, p.k, p.w,
-                     p.cc_chunk, p.cc_nchunk);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(subtile_score_kernel, dim3(p.sc_nchunk, p.R), dim3(kThreads), 0, st, lo,
-                     clist, ccnt, lse2, ytop, hist_c, q, k, cand_y, cand_idx, cand_cnt, p.S, p.T,
-                     p.Hkv, p.k, p.w, p.cc_chunk, p.cc_nchunk, p.sc_chunk, p.sc_nchunk, c2, p.kvp);
+                     clist, ccnt, lse2, reinterpret_cast<const RefinePart*>(w + p.off_ref_part),
+                     p.ref_nwg, reinterpret_cast<double*>(w + p.off_lse2r), lse,
+                     reinterpret_cast<RefineStat*>(w + p.off_ref_stat), ytop, hist_c, q, k,
+                     cand_y, cand_idx, cand_cnt, p.S, p.T, p.Hkv, p.k, p.w, p.cc_chunk,
+                     p.cc_nchunk, p.sc_chunk, p.sc_nchunk, c2, p.kvp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (p.bs > 0) {
     hipLaunchKernelGGL(block_row_select_kernel, dim3(p.R), dim3(kSelThreads), 0, st, cand_y,
@@ -2498,9 +2603,10 @@ hipError_t launch_prefill_select(const Plan& p, const u16* q, const u16* k, int3
                      reinterpret_cast<const u16*>(w + p.off_ybuf),
                      reinterpret_cast<const uint32_t*>(w + p.off_kmax),
                      (p.T + kImportanceTok - 1) / kImportanceTok,
-                     reinterpret_cast<double*>(w + p.off_lse2), lse,
-                     reinterpret_cast<const uint32_t*>(w + p.off_dom_cnt),
-                     reinterpret_cast<const int32_t*>(w + p.off_dom_list),
+                     reinterpret_cast<const double*>(w + p.off_lse2),
+                     reinterpret_cast<double*>(w + p.off_lse2r), lse,
+                     reinterpret_cast<const float*>(w + p.off_ytop),
+                     reinterpret_cast<int32_t*>(w + p.off_dom_list),
                      reinterpret_cast<RefineStat*>(w + p.off_ref_stat), q, k,
                      reinterpret_cast<int32_t*>(w + p.off_band_idx),
                      reinterpret_cast<uint64_t*>(w + p.off_band_key), p.band_cap, idx, n_sel, p.S,

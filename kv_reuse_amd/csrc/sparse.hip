@@ -220,8 +220,10 @@ __global__ __launch_bounds__(64) void swa_branch_kernel(
   const int nk = static_cast<int>(P - first + 1);
   const size_t cache = ((static_cast<size_t>(n) * B + b) * Hkv + g) * static_cast<size_t>(Lc);
   const int64_t row0 = first - (S - Lc);
-  const u16* kl = k_loc + (cache + row0) * kD;
-  const u16* vl = v_loc + (cache + row0) * kD;
+  // no window rows (the caches may then be NULL): the branch adds zeros
+  const bool any = nk > 0 && k_loc != nullptr && v_loc != nullptr;
+  const u16* kl = any ? k_loc + (cache + row0) * kD : nullptr;
+  const u16* vl = any ? v_loc + (cache + row0) * kD : nullptr;
   bf16x8 qb[4];
   {
     const u16* qr = q + static_cast<size_t>(n) * layer_stride +
@@ -235,7 +237,7 @@ __global__ __launch_bounds__(64) void swa_branch_kernel(
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
-  for (int kb = 0; kb < nk; kb += 32) {
+  for (int kb = 0; any && kb < nk; kb += 32) {
     const int n_here = min(32, nk - kb);
     // 32 rows of K and V, 16 pieces of 16 bytes each: 8 pieces per lane (rows
     // past the window repeat its last row and are masked below)
@@ -347,8 +349,9 @@ __global__ __launch_bounds__(256) void sparse_combine_kernel(
 
 hipError_t launch_sparse(const Plan& p, const u16* q, const u16* k, const u16* v,
                          const int32_t* idx, const int32_t* n_sel, u16* out, void* ws,
-                         hipStream_t st, const u16* k_loc, const u16* v_loc) {
-  const bool swa = k_loc != nullptr;
+                         hipStream_t st, bool window_branch, const u16* k_loc,
+                         const u16* v_loc) {
+  const bool swa = window_branch;
   char* w = static_cast<char*>(ws);
   const double c2 = p.scale * 1.4426950408889634;
   const float c2_hi = static_cast<float>(c2);

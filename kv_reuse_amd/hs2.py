@@ -27,7 +27,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 HS2_OK, HS2_ERR_INVALID_ARG, HS2_ERR_UNSUPPORTED, HS2_ERR_WORKSPACE, HS2_ERR_HIP = 0, -1, -2, -3, -4
 EXPORTED = ["hs2_workspace_bytes", "hs2_full_attn_scores", "hs2_topk_select", "hs2_sparse_attn",
             "hs2_cross_decoder_step", "hs2_cross_decoder_step_timed", "hs2_kv_bridge",
-            "hs2_sparse_attn_swa", "hs2_workspace_region",
+            "hs2_sparse_attn_swa", "hs2_workspace_region", "hs2_stream_read_ms",
             "hs2_status_string", "hs2_last_hip_error"]
 
 
@@ -74,6 +74,9 @@ _lib.hs2_workspace_region.argtypes = [_SP, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.POINTER(ctypes.c_size_t),
                                       ctypes.POINTER(ctypes.c_size_t)]
 _lib.hs2_workspace_region.restype = ctypes.c_int
+_lib.hs2_stream_read_ms.argtypes = [_P, ctypes.c_size_t, _P, ctypes.c_int32, _P,
+                                    ctypes.POINTER(ctypes.c_float)]
+_lib.hs2_stream_read_ms.restype = ctypes.c_int
 _lib.hs2_status_string.argtypes = [ctypes.c_int]
 _lib.hs2_status_string.restype = ctypes.c_char_p
 _lib.hs2_last_hip_error.argtypes = []
@@ -272,6 +275,19 @@ def cross_decoder_step_timed(s: ShapeArgs, q_full, q_sparse, k, v, out_full, out
     return [float(x) for x in ms]
 
 
+def stream_read_ms(buf: torch.Tensor, iters: int) -> float:
+    """Average milliseconds per non-temporal streaming read of the whole of buf
+    (a contiguous device tensor); synchronises the current stream."""
+    if buf.device.type != "cuda" or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    ms = ctypes.c_float(0.0)
+    _call("hs2_stream_read_ms", _lib.hs2_stream_read_ms(
+        _ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), int(iters), _stream(),
+        ctypes.byref(ms)))
+    return float(ms.value)
+
+
 def raw():
     """The ctypes library handle (for ABI tests)."""
     return _lib
@@ -309,8 +325,9 @@ def sparse_attn_swa(s: ShapeArgs, q, k, v, idx, n_sel, k_loc, v_loc, out, ws=Non
     _check(v, "v", torch.bfloat16, (B, Hkv, s.kv_rows, D))
     _check(idx, "idx", torch.int32, (B, T, Hkv, s.cap))
     _check(n_sel, "n_sel", torch.int32, (B, T, Hkv))
-    _check(k_loc, "k_loc", torch.bfloat16, (L, B, Hkv, Lc, D))
-    _check(v_loc, "v_loc", torch.bfloat16, (L, B, Hkv, Lc, D))
+    # with no local rows (w = 0 in decode) the caches may be None
+    _check(k_loc, "k_loc", torch.bfloat16, (L, B, Hkv, Lc, D), allow_none=Lc == 0)
+    _check(v_loc, "v_loc", torch.bfloat16, (L, B, Hkv, Lc, D), allow_none=Lc == 0)
     _check(out, "out", torch.bfloat16, (L, B, T, Hq, D))
     ws = alloc_workspace(s, L) if ws is None else ws
     _call("hs2_sparse_attn_swa", _lib.hs2_sparse_attn_swa(

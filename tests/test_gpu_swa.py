@@ -56,9 +56,11 @@ def test_swa_variant(hs2, name, kw):
     if B > 1:
         ns[1, 0, 0] = 0            # nothing selected: only the window branch remains
     out = torch.empty((L, B, T, w.n_q_heads, 128), dtype=torch.bfloat16, device="cuda")
+    # with no local rows the caches are passed as NULL
+    kl = gh.dev(k_loc) if Lc else None
+    vl = gh.dev(v_loc) if Lc else None
     hs2.sparse_attn_swa(s, gh.dev(x["q_sparse"]), gh.dev(x["k"]), gh.dev(x["v"]),
-                        torch.from_numpy(idx).cuda(), torch.from_numpy(ns).cuda(),
-                        gh.dev(k_loc), gh.dev(v_loc), out)
+                        torch.from_numpy(idx).cuda(), torch.from_numpy(ns).cuda(), kl, vl, out)
     torch.cuda.synchronize()
     want = orc.sparse_swa_step(x["q_sparse"], x["k"], x["v"], idx, ns, k_loc, v_loc,
                                scale=w.scale, window=w.window)
