@@ -159,6 +159,12 @@ __device__ __forceinline__ void load_q_operand(const u16* __restrict__ qr, int c
                      : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
 }
 
+// kStaged: the split is at most kStageKeys keys and its subtile maxima go to
+// LDS first.  A template parameter rather than a run-time choice, so that the
+// maxima's stores are LDS stores: a vector-memory store among the stream's
+// loads makes the compiler wait for every load in flight (the counter no
+// longer drains in order), which serialises the prefetch with the tile.
+template <bool kStaged>
 __global__ __launch_bounds__(kWaves * 64, 2) void full_decode_split_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     float* __restrict__ stmax, float* __restrict__ part_m, double* __restrict__ part_l,
@@ -183,7 +189,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void full_decode_split_kernel(
   const u16* kr = k + static_cast<size_t>(r) * kvp * kD;
   const u16* vr = v + static_cast<size_t>(r) * kvp * kD;
   float* stmax_row = stmax + static_cast<size_t>(r) * (Spad / 16) * kG;
-  const bool staged = kps <= kStageKeys;
+  constexpr bool staged = kStaged;
   float* st_dst = staged ? st_stage : stmax_row;
   const int64_t st_base = staged ? key_begin / 16 : 0;
   u16* vw = reinterpret_cast<u16*>(smem) + wave * kTile * kVPitch;
@@ -203,16 +209,21 @@ __global__ __launch_bounds__(kWaves * 64, 2) void full_decode_split_kernel(
   if (t0 < key_end) {
     KVTile ta, tb;
     load_tile(ta, kr, vr, t0, key_last, col, grp);
+    // The next tile is loaded whether or not it exists: past the split every
+    // key clamps to key_last, so the wave reads that one row (512 bytes), and
+    // with no branch around the loads the compiler does not wait for them
+    // before the current tile's MFMAs (it does at the join of a conditional
+    // prefetch).
     while (true) {
       int64_t t1 = t0 + stride;
       bool more = t1 < key_end;
-      if (more) load_tile(tb, kr, vr, t1, key_last, col, grp);
+      load_tile(tb, kr, vr, t1, key_last, col, grp);
       process_tile(ta, st, qb, vw, st_dst, st_base, t0, key_end, col, grp, c2_hi, c2_lo);
       if (!more) break;
       t0 = t1;
       t1 = t0 + stride;
       more = t1 < key_end;
-      if (more) load_tile(ta, kr, vr, t1, key_last, col, grp);
+      load_tile(ta, kr, vr, t1, key_last, col, grp);
       process_tile(tb, st, qb, vw, st_dst, st_base, t0, key_end, col, grp, c2_hi, c2_lo);
       if (!more) break;
       t0 = t1;
@@ -692,7 +703,8 @@ hipError_t launch_full_decode_split(const Plan& p, const u16* q, const u16* k, c
   const float c2_hi = static_cast<float>(c2);
   const float c2_lo = static_cast<float>(c2 - static_cast<double>(c2_hi));
   dim3 grid(p.n_split, p.R);
-  hipLaunchKernelGGL(full_decode_split_kernel, grid, dim3(kWaves * 64), 0, st, q, k, v,
+  auto kern = p.kps <= kStageKeys ? full_decode_split_kernel<true> : full_decode_split_kernel<false>;
+  hipLaunchKernelGGL(kern, grid, dim3(kWaves * 64), 0, st, q, k, v,
                      reinterpret_cast<float*>(w + p.off_stmax),
                      reinterpret_cast<float*>(w + p.off_part_m),
                      reinterpret_cast<double*>(w + p.off_part_l),

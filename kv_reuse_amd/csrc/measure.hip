@@ -30,6 +30,9 @@ __global__ __launch_bounds__(kSThreads) void stream_read_kernel(const u32x4* __r
     u32x4 v[kSUnroll];
 #pragma unroll
     for (int u = 0; u < kSUnroll; ++u) v[u] = __builtin_nontemporal_load(p + i + u * kSThreads);
+    // every load of the batch is issued before the first is waited on (left to
+    // itself the scheduler pulls the first XOR up between the loads)
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < kSUnroll; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
