@@ -101,7 +101,9 @@ enum {
   HS2_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, bad workspace alignment */
   HS2_ERR_UNSUPPORTED = -2, /* a valid shape this build does not implement */
   HS2_ERR_WORKSPACE = -3,   /* ws_bytes smaller than hs2_workspace_bytes() */
-  HS2_ERR_HIP = -4          /* a HIP runtime call or kernel launch failed */
+  HS2_ERR_HIP = -4,         /* a HIP runtime call or kernel launch failed */
+  HS2_ERR_SCRATCH = -5      /* the shape needs more than the static scratch (see
+                               hs2_cross_decoder_step_static) */
 };
 
 /* Bytes of workspace any call below needs for this shape and number of sparse
@@ -179,6 +181,28 @@ int hs2_cross_decoder_step(const hs2_shape* shape, int32_t n_sparse_layers,
                            const hs2_bf16* k, const hs2_bf16* v, hs2_bf16* out_full,
                            hs2_bf16* out_sparse, int32_t* idx, int32_t* n_sel, float* lse,
                            float* scores, void* ws, size_t ws_bytes, void* stream);
+
+/* The step above for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments and results, minus the workspace, which here is a buffer
+ * of HS2_STATIC_SCRATCH_BYTES that the library holds in device memory on
+ * every GPU it runs on, until the process ends.  The call allocates nothing.
+ * Its first call on a device looks up that device's buffer (with the device
+ * current, as for every call), so make one call before a graph capture.
+ *   - Shapes whose hs2_workspace_bytes exceeds HS2_STATIC_SCRATCH_BYTES get
+ *     HS2_ERR_SCRATCH, before anything is enqueued (the decode workloads up to
+ *     1M keys over B * n_kv_heads = 4 rows, or 256K keys over 16 rows, fit).
+ *   - Every call on a GPU shares that GPU's buffer, whose contents are those
+ *     of the last call: calls that may overlap on one GPU (other streams,
+ *     other threads) race and must be ordered by the caller.
+ *   - hs2_workspace_region's regions are not reachable for this buffer.
+ * Other errors as hs2_cross_decoder_step. */
+#define HS2_STATIC_SCRATCH_BYTES ((size_t)96 << 20)
+int hs2_cross_decoder_step_static(const hs2_shape* shape, int32_t n_sparse_layers,
+                                  const hs2_bf16* q_full, const hs2_bf16* q_sparse,
+                                  const hs2_bf16* k, const hs2_bf16* v, hs2_bf16* out_full,
+                                  hs2_bf16* out_sparse, int32_t* idx, int32_t* n_sel,
+                                  float* lse, float* scores, void* stream);
 
 /* The step above, with HIP events recorded on `stream` between its phases,
  * for measurement: phase_ms[0] = full-attention split kernel, [1] = combine,

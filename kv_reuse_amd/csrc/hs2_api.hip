@@ -2,12 +2,15 @@
 // workspace plan, and the launch sequence of each entry point.  Nothing here
 // allocates, frees or synchronises, except the measurement entry point
 // hs2_cross_decoder_step_timed, which synchronises its stream at the end.
+// hs2_cross_decoder_step_static runs on a device buffer the library holds
+// (a file-scope device array, below), not on a caller's workspace.
 
 #include <math.h>
 #include <string.h>
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "hs2_internal.h"
 
@@ -299,20 +302,28 @@ int hs2_sparse_attn(const hs2_shape* shape, int32_t n_layers, const hs2_bf16* q,
   return HS2_OK;
 }
 
-int hs2_cross_decoder_step(const hs2_shape* shape, int32_t n_sparse_layers,
-                           const hs2_bf16* q_full, const hs2_bf16* q_sparse, const hs2_bf16* k,
-                           const hs2_bf16* v, hs2_bf16* out_full, hs2_bf16* out_sparse,
-                           int32_t* idx, int32_t* n_sel, float* lse, float* scores, void* ws,
-                           size_t ws_bytes, void* stream) {
-  Plan p;
-  int st = make_plan(shape, n_sparse_layers, &p);
-  if (st != HS2_OK) return st;
+}  // extern "C"
+
+namespace hs2 {
+namespace {
+
+// the argument checks of a step, before any workspace is looked at
+int check_step_args(const Plan& p, int32_t n_sparse_layers, const hs2_bf16* q_full,
+                    const hs2_bf16* q_sparse, const hs2_bf16* k, const hs2_bf16* v,
+                    const hs2_bf16* out_full, const hs2_bf16* out_sparse, const int32_t* idx,
+                    const int32_t* n_sel) {
   if (!q_full || !k || !v || !out_full || !idx || !n_sel) return HS2_ERR_INVALID_ARG;
   if (n_sparse_layers > 0 && (!q_sparse || !out_sparse)) return HS2_ERR_INVALID_ARG;
   if (p.T != 1 && p.bs != 0) return HS2_ERR_UNSUPPORTED;
-  if ((st = check_ws(p, ws, ws_bytes)) != HS2_OK) return st;
-  (void)hipGetLastError();
-  const hipStream_t s = as_stream(stream);
+  return HS2_OK;
+}
+
+// one step's launches on a checked plan and workspace
+int run_step(const Plan& p, int32_t n_sparse_layers, const hs2_bf16* q_full,
+             const hs2_bf16* q_sparse, const hs2_bf16* k, const hs2_bf16* v, hs2_bf16* out_full,
+             hs2_bf16* out_sparse, int32_t* idx, int32_t* n_sel, float* lse, float* scores,
+             void* ws, hipStream_t s) {
+  int st;
   if (p.T != 1) {
     HS2_TRY(launch_full_prefill(p, q_full, k, v, out_full, lse, ws, s));
     HS2_TRY(launch_prefill_importance(p, q_full, k, ws, s));
@@ -328,6 +339,88 @@ int hs2_cross_decoder_step(const hs2_shape* shape, int32_t n_sparse_layers,
   if (n_sparse_layers > 0)
     HS2_TRY(launch_sparse(p, q_sparse, k, v, idx, n_sel, out_sparse, ws, s));
   return HS2_OK;
+}
+
+// ---- the library-held workspace of hs2_cross_decoder_step_static
+//
+// One buffer per GPU: a file-scope device array, so that it exists on every
+// device the library's code object is loaded on.  Host code never passes the
+// array's name to a kernel (on the host it names a stand-in, not device
+// memory): each device's address is looked up once, with that device current,
+// and kept in g_scratch_dev[device].
+static __device__ __align__(256) unsigned char scratch[HS2_STATIC_SCRATCH_BYTES];
+
+std::atomic<void*> g_scratch_dev[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's scratch address, looked up on its first use; nullptr
+// with *err set when the lookup fails.
+void* scratch_of_current_device(int* err) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *err = hip_status(e);
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = HS2_ERR_UNSUPPORTED;
+    return nullptr;
+  }
+  void* ptr = g_scratch_dev[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ptr = g_scratch_dev[dev].load(std::memory_order_relaxed);
+  if (ptr) return ptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !ptr) {
+    *err = hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol);
+    return nullptr;
+  }
+  g_scratch_dev[dev].store(ptr, std::memory_order_release);
+  return ptr;
+}
+
+}  // namespace
+}  // namespace hs2
+
+extern "C" {
+
+int hs2_cross_decoder_step(const hs2_shape* shape, int32_t n_sparse_layers,
+                           const hs2_bf16* q_full, const hs2_bf16* q_sparse, const hs2_bf16* k,
+                           const hs2_bf16* v, hs2_bf16* out_full, hs2_bf16* out_sparse,
+                           int32_t* idx, int32_t* n_sel, float* lse, float* scores, void* ws,
+                           size_t ws_bytes, void* stream) {
+  Plan p;
+  int st = make_plan(shape, n_sparse_layers, &p);
+  if (st != HS2_OK) return st;
+  if ((st = check_step_args(p, n_sparse_layers, q_full, q_sparse, k, v, out_full, out_sparse,
+                            idx, n_sel)) != HS2_OK)
+    return st;
+  if ((st = check_ws(p, ws, ws_bytes)) != HS2_OK) return st;
+  (void)hipGetLastError();
+  return run_step(p, n_sparse_layers, q_full, q_sparse, k, v, out_full, out_sparse, idx, n_sel,
+                  lse, scores, ws, as_stream(stream));
+}
+
+int hs2_cross_decoder_step_static(const hs2_shape* shape, int32_t n_sparse_layers,
+                                  const hs2_bf16* q_full, const hs2_bf16* q_sparse,
+                                  const hs2_bf16* k, const hs2_bf16* v, hs2_bf16* out_full,
+                                  hs2_bf16* out_sparse, int32_t* idx, int32_t* n_sel,
+                                  float* lse, float* scores, void* stream) {
+  Plan p;
+  int st = make_plan(shape, n_sparse_layers, &p);
+  if (st != HS2_OK) return st;
+  if ((st = check_step_args(p, n_sparse_layers, q_full, q_sparse, k, v, out_full, out_sparse,
+                            idx, n_sel)) != HS2_OK)
+    return st;
+  if (p.total > HS2_STATIC_SCRATCH_BYTES) return HS2_ERR_SCRATCH;
+  (void)hipGetLastError();
+  void* ws = scratch_of_current_device(&st);
+  if (!ws) return st;
+  // the step's kernels clear every counter and histogram they accumulate into,
+  // so the previous call's contents need no clearing here
+  return run_step(p, n_sparse_layers, q_full, q_sparse, k, v, out_full, out_sparse, idx, n_sel,
+                  lse, scores, ws, as_stream(stream));
 }
 
 int hs2_cross_decoder_step_timed(const hs2_shape* shape, int32_t n_sparse_layers,
@@ -460,6 +553,7 @@ const char* hs2_status_string(int status) {
     case HS2_ERR_UNSUPPORTED: return "unsupported shape";
     case HS2_ERR_WORKSPACE: return "workspace too small";
     case HS2_ERR_HIP: return "HIP runtime error";
+    case HS2_ERR_SCRATCH: return "shape needs more than the static scratch buffer";
     default: return "unknown status";
   }
 }

@@ -25,10 +25,12 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 HS2_OK, HS2_ERR_INVALID_ARG, HS2_ERR_UNSUPPORTED, HS2_ERR_WORKSPACE, HS2_ERR_HIP = 0, -1, -2, -3, -4
+HS2_ERR_SCRATCH = -5
+HS2_STATIC_SCRATCH_BYTES = 96 << 20   # the library-held buffer of cross_decoder_step_static
 EXPORTED = ["hs2_workspace_bytes", "hs2_full_attn_scores", "hs2_topk_select", "hs2_sparse_attn",
             "hs2_cross_decoder_step", "hs2_cross_decoder_step_timed", "hs2_kv_bridge",
             "hs2_sparse_attn_swa", "hs2_workspace_region", "hs2_stream_read_ms",
-            "hs2_status_string", "hs2_last_hip_error"]
+            "hs2_status_string", "hs2_last_hip_error", "hs2_cross_decoder_step_static"]
 
 
 class Shape(ctypes.Structure):
@@ -77,6 +79,9 @@ _lib.hs2_workspace_region.restype = ctypes.c_int
 _lib.hs2_stream_read_ms.argtypes = [_P, ctypes.c_size_t, _P, ctypes.c_int32, _P,
                                     ctypes.POINTER(ctypes.c_float)]
 _lib.hs2_stream_read_ms.restype = ctypes.c_int
+# q_full, q_sparse, k, v, out_full, out_sparse, idx, n_sel, lse, scores, stream
+_lib.hs2_cross_decoder_step_static.argtypes = [_SP, ctypes.c_int32] + [_P] * 11
+_lib.hs2_cross_decoder_step_static.restype = ctypes.c_int
 _lib.hs2_status_string.argtypes = [ctypes.c_int]
 _lib.hs2_status_string.restype = ctypes.c_char_p
 _lib.hs2_last_hip_error.argtypes = []
@@ -262,6 +267,29 @@ def cross_decoder_step(s: ShapeArgs, q_full, q_sparse, k, v, out_full, out_spars
         ctypes.byref(s.c()), L, _ptr(q_full), _ptr(q_sparse), _ptr(k), _ptr(v), _ptr(out_full),
         _ptr(out_sparse), _ptr(idx), _ptr(n_sel), _ptr(lse), _ptr(scores), _ptr(ws), ws.numel(),
         _stream()))
+
+
+def cross_decoder_step_static(s: ShapeArgs, q_full, q_sparse, k, v, out_full, out_sparse, idx,
+                              n_sel, lse=None, scores=None):
+    """cross_decoder_step on the library-held device buffer: no workspace, no
+    allocation (hs2_cross_decoder_step_static).  Calls that overlap on one GPU
+    share that buffer and race."""
+    B, T, Hq, Hkv, D, S = s.batch, s.n_q_tokens, s.n_q_heads, s.n_kv_heads, s.head_dim, s.ctx_len
+    L = 0 if q_sparse is None else q_sparse.shape[0]
+    _check(q_full, "q_full", torch.bfloat16, (B, T, Hq, D))
+    _check(k, "k", torch.bfloat16, (B, Hkv, s.kv_rows, D))
+    _check(v, "v", torch.bfloat16, (B, Hkv, s.kv_rows, D))
+    _check(out_full, "out_full", torch.bfloat16, (B, T, Hq, D))
+    if L:
+        _check(q_sparse, "q_sparse", torch.bfloat16, (L, B, T, Hq, D))
+        _check(out_sparse, "out_sparse", torch.bfloat16, (L, B, T, Hq, D))
+    _check(idx, "idx", torch.int32, (B, T, Hkv, s.cap))
+    _check(n_sel, "n_sel", torch.int32, (B, T, Hkv))
+    _check(lse, "lse", torch.float32, (B, T, Hq), allow_none=True)
+    _check(scores, "scores", torch.float32, (B, T, Hkv, S), allow_none=True)
+    _call("hs2_cross_decoder_step_static", _lib.hs2_cross_decoder_step_static(
+        ctypes.byref(s.c()), L, _ptr(q_full), _ptr(q_sparse), _ptr(k), _ptr(v), _ptr(out_full),
+        _ptr(out_sparse), _ptr(idx), _ptr(n_sel), _ptr(lse), _ptr(scores), _stream()))
 
 
 def cross_decoder_step_timed(s: ShapeArgs, q_full, q_sparse, k, v, out_full, out_sparse, idx,

@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     lib = hs2.raw()
     for n in names:
         assert hasattr(lib, n), n
@@ -237,3 +237,23 @@ def test_block_selection_limits():
     st = lib.hs2_cross_decoder_step(ctypes.byref(c), 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                     FAKE, None, None, FAKE, 1 << 40, None)
     assert st == hs2.HS2_ERR_UNSUPPORTED
+
+
+def test_static_step_rejects_shapes_beyond_its_scratch():
+    """A shape whose workspace exceeds the library-held buffer gets
+    HS2_ERR_SCRATCH before anything touches a device; one that fits passes the
+    size check (and then fails on a null pointer, still before any device call)."""
+    lib = hs2.raw()
+    big = hs2.ShapeArgs(batch=4, n_q_tokens=1, n_q_heads=32, n_kv_heads=4, head_dim=128,
+                        ctx_len=1 << 20)
+    assert hs2.workspace_bytes(big, 8) > hs2.HS2_STATIC_SCRATCH_BYTES
+    args = [FAKE] * 8 + [None, None, None]
+    st = lib.hs2_cross_decoder_step_static(ctypes.byref(big.c()), 8, *args)
+    assert st == hs2.HS2_ERR_SCRATCH
+    assert "static scratch" in lib.hs2_status_string(st).decode()
+    small = hs2.ShapeArgs(batch=1, n_q_tokens=1, n_q_heads=8, n_kv_heads=1, head_dim=128,
+                          ctx_len=4096)
+    assert hs2.workspace_bytes(small, 1) <= hs2.HS2_STATIC_SCRATCH_BYTES
+    st = lib.hs2_cross_decoder_step_static(ctypes.byref(small.c()), 1, FAKE, None, *([FAKE] * 6),
+                                           None, None, None)
+    assert st == hs2.HS2_ERR_INVALID_ARG     # q_sparse is NULL with one sparse layer
