@@ -39,18 +39,8 @@ namespace hs2 {
 namespace {
 
 constexpr int kPThreads = 256;
-// Attention: query blocks per wave.  Two keep the kernel at 244 VGPRs and two
-// work-groups per CU; three or four halve the LDS operand reads per MFMA but
-// drop to one wave per SIMD, and then measured 45-60% slower on the 4K-token
-// chunk over 128K keys.
-constexpr int kPrefillQB = 2;
+constexpr int kAttnQC = 1;   // attention: 32-column blocks per wave
 constexpr int kPKeys = 64;      // keys per tile
-// LDS row pitches, in u16.  K rows advance by 4 banks (68 dwords), so the
-// 16-byte operand reads of 8 or 16 consecutive rows cover every bank once; V
-// rows advance by 8 banks (72 dwords), so the transposing 8-byte reads (4 rows
-// x 4 consecutive units per 16 lanes, 8 rows per 32) do.
-constexpr int kPPitch = 136;
-constexpr int kPVPitch = 144;
 
 __device__ __forceinline__ int xcd_linear(int id, int n) {
   // hardware dispatch sends work-group id to XCD id % 8; renumber so that XCD x
@@ -59,49 +49,7 @@ __device__ __forceinline__ int xcd_linear(int id, int n) {
   return (id & 7) * (n >> 3) + (id >> 3);
 }
 
-// One 64-key tile of K (and optionally V) from global memory into registers:
-// thread t holds 64 bytes of key row t/4 (keys past `key_max` repeat it).
-struct TileRegs {
-  u32x4 k[4];
-  u32x4 v[4];
-};
-
-template <bool kWithV>
-__device__ __forceinline__ void tile_gload(TileRegs& r, const u16* __restrict__ kr,
-                                           const u16* __restrict__ vr, int64_t key0,
-                                           int64_t key_max) {
-  const int tid = threadIdx.x;
-  int64_t key = key0 + (tid >> 2);
-  key = key < key_max ? key : key_max;
-  const u16* ks = kr + key * kD + 32 * (tid & 3);
-#pragma unroll
-  for (int c = 0; c < 4; ++c) r.k[c] = load_u32x4(ks + 8 * c);
-  if (kWithV) {
-    const u16* vs = vr + key * kD + 32 * (tid & 3);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) r.v[c] = load_u32x4(vs + 8 * c);
-  }
-}
-
-template <bool kWithV>
-__device__ __forceinline__ void tile_lstore(const TileRegs& r, u16* kt, u16* vt) {
-  const int tid = threadIdx.x;
-  u16* kd = kt + (tid >> 2) * kPPitch + 32 * (tid & 3);
-#pragma unroll
-  for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(kd + 8 * c) = r.k[c];
-  if (kWithV) {
-    u16* vd = vt + (tid >> 2) * kPVPitch + 32 * (tid & 3);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(vd + 8 * c) = r.v[c];
-  }
-}
-
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-
-// K as the A operand of S^T for key subtile kt (16 keys) and dims 32c..32c+31.
-__device__ __forceinline__ bf16x8 lds_k_operand(const u16* kt, int sub, int c, int col, int grp) {
-  return as_bf16x8(*reinterpret_cast<const u32x4*>(kt + (16 * sub + col) * kPPitch + 32 * c + 8 * grp));
-}
 
 // Make the compiler wait for a loaded operand here (an empty asm that reads
 // it), so that the load is not left outstanding into a loop.
@@ -117,20 +65,61 @@ __device__ __forceinline__ void load_q_block(const u16* __restrict__ qtok, int c
   for (int c = 0; c < 4; ++c) qb[c] = as_bf16x8(load_u32x4(p + 32 * c));
 }
 
-// grid: B * Hkv * ceil(T / (8 * QB)) work-groups of 256 threads; each wave
-// owns QB query blocks (2 QB tokens), so every K/V operand read from LDS
-// serves 16 QB query columns.
-template <int QB>
-__global__ __launch_bounds__(kPThreads, QB <= 2 ? 2 : 1) void full_prefill_kernel(
+// ---- attention kernel
+//
+// grid: B * Hkv * ceil(T / 16) work-groups of 256 threads.  A work-group takes
+// 16 consecutive chunk tokens of one (batch, KV head); each wave owns 4 of
+// them, whose 4 x 8 query heads are the 32 columns of its S^T = K Q^T and
+// O^T = V^T P^T, both on the 32x32x16 bf16 MFMA (which leaves the VALU more
+// room beside each MFMA than the 16x16x32 form at the same rate).
+//
+// Lane l holds column n = l & 31 (token 4 wave + n / 8, head n % 8) and, of a
+// 32-row accumulator block, rows 8 (r / 4) + 4 (l >> 5) + r % 4 in register r.
+// A 64-key tile's logits are two such blocks (keys 32 kb + row).  The P^T
+// operand of a 16-key step s is the 8 registers 8 (s & 1) .. of block s / 2,
+// as bf16: its k-index 8 (l >> 5) + j is key 16 s + 8 (j / 4) + 4 (l >> 5) +
+// j % 4, and V^T's operand takes the same key order (two transposing reads
+// of 4 rows each).
+//
+// Software pipeline: step i turns tile i's logits S_i (computed in step
+// i - 1) into probabilities while the MFMAs of tile i + 1's logits run, then
+// adds V_i^T P_i to O.  So the wave's own VALU work (the softmax) sits
+// between independent MFMAs instead of after them.  K and V tiles are
+// double-buffered in LDS and filled by LDS-direct loads (16 bytes a lane) one
+// step ahead, with one barrier per step.  Rows are 256 bytes, their 16-byte
+// chunks XOR-swizzled so that both operand reads are bank-conflict-free: K's
+// chunk c of row r sits at slot c ^ (r & 15) (the 16 rows of one K read hit 16
+// different slots), V's at c ^ 4 (r & 3) (the 4 rows x 4 chunks x 2 halves
+// that 32 lanes of a transposing read address hit 32 different 8-byte places).
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+// an LDS-direct load's destination: the wave-uniform start of its 1 KB
+__device__ __forceinline__ lds_void_ptr lds_ptr(u16* tile, int byte_off) {
+  return (lds_void_ptr)((__attribute__((address_space(3))) char*)tile + byte_off);
+}
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// QC column blocks of 32 per wave: every K and V^T operand read from LDS
+// then feeds QC MFMAs (LDS instruction issue, not bytes, is what bounds the
+// operand reads: a transposing 8-byte read costs about as much as a 16-byte
+// one).  QC = 2 needs more than 256 registers (O in accumulation registers),
+// so one wave per SIMD; QC = 1 runs two.
+template <int QC>
+__global__ __launch_bounds__(kPThreads, QC == 1 ? 2 : 1) void full_prefill_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     u16* __restrict__ out, float* __restrict__ lse_out, double* __restrict__ lse2,
     float* __restrict__ ytop_h, int64_t S, int T, int Hkv, int n_tblk, float c2_hi,
     float c2_lo, int64_t kvp) {
-  __shared__ __align__(16) u16 kt[kPKeys * kPPitch];
-  __shared__ __align__(16) u16 vt[kPKeys * kPVPitch];
+  constexpr int kTok = 16 * QC;   // chunk tokens per work-group
+  __shared__ __align__(16) u16 kb0[kPKeys * kD];
+  __shared__ __align__(16) u16 kb1[kPKeys * kD];
+  __shared__ __align__(16) u16 vb0[kPKeys * kD];
+  __shared__ __align__(16) u16 vb1[kPKeys * kD];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int col = lane & 15, grp = lane >> 4;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int n = lane & 31, hf = lane >> 5;
   const int lin = xcd_linear(blockIdx.x, gridDim.x);
   const int tb = lin % n_tblk;
   const int bg = lin / n_tblk;
@@ -138,175 +127,326 @@ __global__ __launch_bounds__(kPThreads, QB <= 2 ? 2 : 1) void full_prefill_kerne
   const int Hq = Hkv * kG;
   const u16* kr = k + static_cast<size_t>(bg) * kvp * kD;
   const u16* vr = v + static_cast<size_t>(bg) * kvp * kD;
-  const int64_t pos0 = S - T;                      // position of chunk token 0
-  constexpr int kTok = 8 * QB;                     // chunk tokens per work-group
-  // this lane's columns: query block qbk covers tokens 2*QB*wave + 2*qbk + {0,1}
-  int64_t pcol[QB];
-  bf16x8 qop[QB][4];
+  // positions fit in 32 bits (the context is below 2^31 keys)
+  const int pos0 = static_cast<int>(S) - T;        // position of chunk token 0
+  // column block cb of this wave: tokens 4 (QC wave + cb) .. + 3 of the group
+  int t_col[QC], pcol[QC];
+  // Q^T as the B operand: k-step ks holds dims 16 ks + 8 hf .. + 7 of column n
+  bf16x8 qop[QC][8];
 #pragma unroll
-  for (int qbk = 0; qbk < QB; ++qbk) {
-    int t = tb * kTok + 2 * QB * wave + 2 * qbk + (col >> 3);
-    t = t < T ? t : T - 1;                         // past the chunk: repeat the last token
-    pcol[qbk] = pos0 + t;
-    load_q_block(q + (static_cast<size_t>(b) * T + t) * Hq * kD + static_cast<size_t>(g) * kG * kD,
-                 col, grp, qop[qbk]);
+  for (int cb = 0; cb < QC; ++cb) {
+    t_col[cb] = tb * kTok + 4 * (QC * wave + cb) + (n >> 3);
+    const int t_q = t_col[cb] < T ? t_col[cb] : T - 1;   // past the chunk: repeat the last token
+    pcol[cb] = pos0 + t_q;
+    const u16* qp = q + (static_cast<size_t>(b) * T + t_q) * Hq * kD +
+                    (static_cast<size_t>(g) * kG + (n & 7)) * kD + 8 * hf;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qop[cb][ks] = as_bf16x8(load_u32x4(qp + 16 * ks));
   }
   const int t_last = min(T - 1, tb * kTok + kTok - 1);
-  const int64_t p_first = pos0 + tb * kTok;        // smallest position in the work-group
-  const int64_t p_last = pos0 + t_last;
-  const int n_tiles = static_cast<int>((p_last + kPKeys) / kPKeys);
+  const int p_first = pos0 + tb * kTok;            // smallest position in the work-group
+  const int p_last = pos0 + t_last;
+  const int n_tiles = (p_last + kPKeys) / kPKeys;
 
-  f32x4 o[QB][8];
-  float m[QB];
-  double l[QB];
+  // fills: wave w writes rows 16w .. 16w + 15 of a tile, 4 rows (1 KB) per
+  // load, lane l at row r = 16w + 4j + (l >> 4), slot l & 15.  The source
+  // chunk's byte offset in its 4 rows is f0 ^ (64 j) for K (swizzle r & 15 =
+  // 4 j + (l >> 4)) and f0 for V (swizzle 4 (r & 3) = 4 (l >> 4)), f0 that of
+  // j = 0.  A tile is filled from key kf = min(key0, p_last - 63), so that
+  // every row it reads is a key at most p_last: the last tile of a
+  // work-group then starts delta = key0 - kf rows early, and its softmax hides
+  // those rows (their keys were the previous tile's).  With fewer than 64 keys
+  // in all (a single tile) rows past p_last repeat it instead.
+  const uint32_t fk0 = (lane >> 4) * 256u + 16u * ((lane & 15) ^ (lane >> 4));
+  const uint32_t fv0 = (lane >> 4) * 256u + 16u * ((lane & 15) ^ (4 * (lane >> 4)));
+  auto fill_base = [&](int key0) { return p_last >= kPKeys - 1 ? min(key0, p_last - (kPKeys - 1)) : 0; };
+  auto fill_one = [&](const u16* src_head, u16* dst, int key0, uint32_t f0, bool is_v) {
+    const int kf = fill_base(key0);
+    const char* src = reinterpret_cast<const char*>(src_head + static_cast<size_t>(kf) * kD) +
+                      (16 * wave_u) * 256;
 #pragma unroll
-  for (int qbk = 0; qbk < QB; ++qbk) {
+    for (int j = 0; j < 4; ++j) {
+      uint32_t off = (is_v ? f0 : f0 ^ (64u * j)) + 1024u * j;
+      // kept a 32-bit value here (not a hoisted 64-bit one), so that the load
+      // takes the scalar base + 32-bit vector offset form
+      asm volatile("" : "+v"(off));
+      __builtin_amdgcn_global_load_lds(src + off, lds_ptr(dst, (16 * wave_u + 4 * j) * 256), 16, 0, 0);
+    }
+  };
+  // the one-tile case with fewer than 64 keys: rows past p_last repeat it
+  auto fill_short = [&](const u16* src_head, u16* dst, uint32_t f0, bool is_v) {
+    const char* src = reinterpret_cast<const char*>(src_head);
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) o[qbk][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m[qbk] = -INFINITY;
-    l[qbk] = 0.0;
+    for (int j = 0; j < 4; ++j) {
+      const int r = 16 * wave_u + 4 * j + (lane >> 4);
+      const uint32_t off = static_cast<uint32_t>(min(r, p_last)) * 256u + ((is_v ? f0 : f0 ^ (64u * j)) & 255u);
+      __builtin_amdgcn_global_load_lds(src + off, lds_ptr(dst, (16 * wave_u + 4 * j) * 256), 16, 0, 0);
+    }
+  };
+  auto fill_k = [&](u16* dst, int key0) { fill_one(kr, dst, key0, fk0, false); };
+  auto fill_v = [&](u16* dst, int key0) { fill_one(vr, dst, key0, fv0, true); };
+
+  // operand reads, as byte offsets in a tile.  K's A operand of key block kb,
+  // k-step ks: row 32 kb + n, chunk 2 ks + hf, at kbase ^ 32 ks (+ 8192 kb),
+  // kbase = 256 n + 16 (hf ^ (n & 15)).  V^T's A operand of dim block db,
+  // key step s: lane i = l & 15 of 16-lane group (l >> 4) reads 8 bytes of
+  // row 16 s + 4 hf + (i >> 2) (+ 8 for the second read), chunk 4 db +
+  // 2 ((l >> 4) & 1) + ((i & 3) >> 1), half i & 1: at vbase ^ 64 db
+  // (+ 4096 s, + 2048), vbase = 256 (4 hf + (i >> 2)) + 64 (i >> 2) +
+  // 16 (2 ((l >> 4) & 1) + ((i & 3) >> 1)) + 8 (i & 1).  The XORs are redone
+  // in every step (a few VALU) rather than held in registers.
+  const uint32_t kbase0 = 256u * n + 16u * (hf ^ (n & 15));
+  const uint32_t li = lane & 15;
+  const uint32_t vbase0 = 256u * (4 * hf + (li >> 2)) + 64u * (li >> 2) +
+                          16u * (2 * ((lane >> 4) & 1) + ((li & 3) >> 1)) + 8u * (li & 1);
+  uint32_t kbase = kbase0, vbase = vbase0;
+  auto k_operand = [&](const u16* kt, int kb, int ks) {
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(kt) + 8192 * kb +
+                                                     (kbase ^ (32u * ks))));
+  };
+  auto vt_operand = [&](const u16* vt, int db, int st) {
+    const char* p0 = reinterpret_cast<const char*>(vt) + 4096 * st + (vbase ^ (64u * db));
+    const uint2 lo = lds_read_tr16_b64(reinterpret_cast<const u16*>(p0));
+    const uint2 hi = lds_read_tr16_b64(reinterpret_cast<const u16*>(p0 + 2048));
+    return as_bf16x8(u32x4{lo.x, lo.y, hi.x, hi.y});
+  };
+  auto logits = [&](const u16* kt, f32x16 (&sacc)[QC][2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int cb = 0; cb < QC; ++cb) sacc[cb][kb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 a = k_operand(kt, kb, ks);
+#pragma unroll
+        for (int cb = 0; cb < QC; ++cb) sacc[cb][kb] = mfma_32x32x16(a, qop[cb][ks], sacc[cb][kb]);
+      }
+    }
+  };
+
+  f32x16 o[QC][4];
+  float m[QC];
+  double l[QC];
+#pragma unroll
+  for (int cb = 0; cb < QC; ++cb) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) o[cb][db] = f32x16{};
+    m[cb] = -INFINITY;
+    l[cb] = 0.0;
   }
 
-  TileRegs regs;
-  tile_gload<true>(regs, kr, vr, 0, p_last);
-  tile_lstore<true>(regs, kt, vt);
-  // the query operands must have landed before the loop: inside it only the
-  // next tile's loads may be outstanding, or the first MFMAs of every tile
-  // would wait for them
+  // The online softmax of a tile in two parts: tile_max takes the tile's
+  // maximum and moves the running max m to m_new (alpha = 2^(m - m_new) is
+  // the rescale of O and l it implies); tile_exp then turns the logits into
+  // probabilities at m_new, their bf16 P^T operands (4 key steps) and l.  The
+  // max is taken over the raw dot products (the scale is positive, and the
+  // rounded scaling is monotonic), and each exponent is a * c2_hi - m in one
+  // fma: the product and the shift by the integer m are exact inside it, so
+  // only the result rounds, and the scale's dropped low part (below 2^-24 of
+  // a * c2) moves a probability by under 2e-7 of itself, and lse2 by less:
+  // far inside the selection's tolerance (the importance pass and the float64
+  // re-ranking share this lse2).  kMasked: the tile reaches past some
+  // column's position, or starts early (the last tile of a work-group, whose
+  // first key0 - kf rows belong to the previous tile); otherwise no branch,
+  // so that the work can be interleaved with MFMAs.
+  auto masked_logits = [&](const f32x16 (&sacc)[2], int key0, int pc, float (&sv)[2][16]) {
+    // row off (key kf + off) is new and visible to the column iff
+    // key0 - kf <= off <= P - kf; a hidden key gets a large finite negative
+    // product, whose exponent underflows to 0
+    const int kf = fill_base(key0);
+    const int lo = key0 - kf;
+    const int lim = min(kPKeys, pc - kf);
 #pragma unroll
-  for (int qbk = 0; qbk < QB; ++qbk)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) require_loaded(qop[qbk][c]);
-  __syncthreads();
-  for (int it = 0; it < n_tiles; ++it) {
-    const int64_t key0 = static_cast<int64_t>(it) * kPKeys;
-    const bool more = it + 1 < n_tiles;
-    if (more) tile_gload<true>(regs, kr, vr, key0 + kPKeys, p_last);
-    // ---- S^T: 4 key subtiles x QB query blocks
-    f32x4 sacc[QB][4];
-#pragma unroll
-    for (int qbk = 0; qbk < QB; ++qbk)
-#pragma unroll
-      for (int sub = 0; sub < 4; ++sub) sacc[qbk][sub] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int sub = 0; sub < 4; ++sub)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const bf16x8 a = lds_k_operand(kt, sub, c, col, grp);
-#pragma unroll
-        for (int qbk = 0; qbk < QB; ++qbk)
-          sacc[qbk][sub] = mfma_16x16x32(a, qop[qbk][c], sacc[qbk][sub]);
+      for (int r = 0; r < 16; ++r) {
+        const int off = 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+        sv[kb][r] = off <= lim && off >= lo ? sacc[kb][r] : -1.0e30f;
       }
-    // only the last tiles of a work-group reach past some token's position
-    const bool masked = key0 + kPKeys - 1 > p_first;
-    // The running max is taken over the raw dot products (the scale is
-    // positive, and the rounded scaling is monotonic), and each exponent is
-    // a * c2_hi - m in one fma: the product and the shift by the integer m are
-    // exact inside it, so only the result rounds, and the scale's dropped low
-    // part (below 2^-24 of a * c2) moves a probability by under 2e-7 of
-    // itself, and lse2 by less: far inside the selection's tolerance (the
-    // importance pass and the float64 re-ranking share this lse2).
-    float p[QB][4][4];
+  };
+  auto tile_max = [&](const f32x16 (&sacc)[QC][2], int key0, float (&alpha)[QC], auto masked_tag) {
+    constexpr bool kMasked = decltype(masked_tag)::value;
 #pragma unroll
-    for (int qbk = 0; qbk < QB; ++qbk) {
-      float sv[4][4];
-      float amax = -INFINITY;
-      if (!masked) {
-#pragma unroll
-        for (int sub = 0; sub < 4; ++sub)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            sv[sub][i] = sacc[qbk][sub][i];
-            amax = fmaxf(amax, sv[sub][i]);
-          }
+    for (int cb = 0; cb < QC; ++cb) {
+      float sv[2][16];
+      if (kMasked) {
+        masked_logits(sacc[cb], key0, pcol[cb], sv);
       } else {
-        // key0 + off is visible to the column iff off <= P - key0; a hidden
-        // key gets a large finite negative product, whose exponent
-        // underflows to 0
-        const int lim = static_cast<int>(min(static_cast<int64_t>(kPKeys), pcol[qbk] - key0));
 #pragma unroll
-        for (int sub = 0; sub < 4; ++sub)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            sv[sub][i] = 16 * sub + 4 * grp + i <= lim ? sacc[qbk][sub][i] : -1.0e30f;
-            amax = fmaxf(amax, sv[sub][i]);
-          }
+          for (int r = 0; r < 16; ++r) sv[kb][r] = sacc[cb][kb][r];
       }
-      // the column's other keys sit in lanes ^ 16 and ^ 32: VALU row swaps
-      {
-        const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(amax),
-                                                          __float_as_uint(amax), false, false);
-        amax = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
-        const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(amax),
-                                                          __float_as_uint(amax), false, false);
-        amax = fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
-      }
-      // key 0 is visible to every token, so the running max is finite from the
-      // first tile on
+      float mx[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        mx[u] = fmaxf(fmaxf(sv[u >> 2][4 * (u & 3)], sv[u >> 2][4 * (u & 3) + 1]),
+                      fmaxf(sv[u >> 2][4 * (u & 3) + 2], sv[u >> 2][4 * (u & 3) + 3]));
+      float amax = fmaxf(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])),
+                         fmaxf(fmaxf(mx[4], mx[5]), fmaxf(mx[6], mx[7])));
+      // the column's other 32 keys sit in lane ^ 32: one VALU row swap
+      amax = max_xor32(amax);
+      // key 0 is visible to every token, so the running max is finite from
+      // the first tile on
       const float tmax = fmaf(amax, c2_hi, amax * c2_lo);
-      const float m_new = fmaxf(m[qbk], ceilf(tmax));
-      const float alpha = m[qbk] == -INFINITY ? 0.f : ldexpf(1.f, static_cast<int>(m[qbk] - m_new));
-      float ps = 0.f;
-#pragma unroll
-      for (int sub = 0; sub < 4; ++sub)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float a = sv[sub][i];
-          p[qbk][sub][i] = __builtin_amdgcn_exp2f(fmaf(a, c2_hi, -m_new));
-          ps += p[qbk][sub][i];
-        }
-      l[qbk] = l[qbk] * static_cast<double>(alpha) + static_cast<double>(ps);
-      if (__ballot(alpha != 1.f) != 0) {
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) o[qbk][nb] *= alpha;
-      }
-      m[qbk] = m_new;
+      const float m_new = fmaxf(m[cb], ceilf(tmax));
+      alpha[cb] = m[cb] == -INFINITY ? 0.f : ldexpf(1.f, static_cast<int>(m[cb] - m_new));
+      m[cb] = m_new;
     }
-    // ---- O^T += V^T . P^T over two k-steps of 32 keys
+  };
+  auto tile_exp = [&](const f32x16 (&sacc)[QC][2], int key0, const float (&alpha)[QC],
+                      bf16x8 (&pb)[QC][4], auto masked_tag) {
+    constexpr bool kMasked = decltype(masked_tag)::value;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8 pb[QB];
+    for (int cb = 0; cb < QC; ++cb) {
+      float sv[2][16];
+      if (kMasked) {
+        masked_logits(sacc[cb], key0, pcol[cb], sv);
+      } else {
 #pragma unroll
-      for (int qbk = 0; qbk < QB; ++qbk) {
-        const u32x4 pp{pack_bf16x2(p[qbk][2 * ks][0], p[qbk][2 * ks][1]),
-                       pack_bf16x2(p[qbk][2 * ks][2], p[qbk][2 * ks][3]),
-                       pack_bf16x2(p[qbk][2 * ks + 1][0], p[qbk][2 * ks + 1][1]),
-                       pack_bf16x2(p[qbk][2 * ks + 1][2], p[qbk][2 * ks + 1][3])};
-        pb[qbk] = as_bf16x8(pp);
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sv[kb][r] = sacc[cb][kb][r];
       }
+      float p[2][16];
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        const bf16x8 a = lds_vt_operand(vt + 32 * ks * kPVPitch, kPVPitch, nb, col, grp);
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int qbk = 0; qbk < QB; ++qbk) o[qbk][nb] = mfma_16x16x32(a, pb[qbk], o[qbk][nb]);
+        for (int r = 0; r < 16; ++r) p[kb][r] = __builtin_amdgcn_exp2f(fmaf(sv[kb][r], c2_hi, -m[cb]));
+      // the tile's sum as a tree (short dependency chains)
+      float ps8[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        ps8[u] = (p[u >> 2][4 * (u & 3)] + p[u >> 2][4 * (u & 3) + 1]) +
+                 (p[u >> 2][4 * (u & 3) + 2] + p[u >> 2][4 * (u & 3) + 3]);
+      const float ps = ((ps8[0] + ps8[1]) + (ps8[2] + ps8[3])) + ((ps8[4] + ps8[5]) + (ps8[6] + ps8[7]));
+      l[cb] = l[cb] * static_cast<double>(alpha[cb]) + static_cast<double>(ps);
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const float* q8 = &p[st >> 1][8 * (st & 1)];
+        const u32x4 pp{pack_bf16x2(q8[0], q8[1]), pack_bf16x2(q8[2], q8[3]), pack_bf16x2(q8[4], q8[5]),
+                       pack_bf16x2(q8[6], q8[7])};
+        pb[cb][st] = as_bf16x8(pp);
       }
     }
-    __syncthreads();               // every wave is done with this tile
-    if (more) {
-      tile_lstore<true>(regs, kt, vt);
-      __syncthreads();
+  };
+  auto rescale = [&](const float (&alpha)[QC]) {
+#pragma unroll
+    for (int cb = 0; cb < QC; ++cb)
+      if (__ballot(alpha[cb] != 1.f) != 0) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[cb][db] *= alpha[cb];
+      }
+  };
+  auto accumulate = [&](const u16* vt, const bf16x8 (&pb)[QC][4]) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const bf16x8 a = vt_operand(vt, db, st);
+#pragma unroll
+        for (int cb = 0; cb < QC; ++cb) o[cb][db] = mfma_32x32x16(a, pb[cb][st], o[cb][db]);
+      }
+  };
+  auto wait_fills = [] {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's tile loads landed
+  };
+
+  // tiles 0 .. n_full - 1 are visible to every column and start at key0; the
+  // last one or two tiles of a work-group take the masked path
+  const int n_full = min((p_first + 1) / kPKeys, n_tiles - 1);
+  using Full = std::integral_constant<bool, false>;
+  using Masked = std::integral_constant<bool, true>;
+
+  // prologue: K_0, V_0 and K_1 in LDS, S_0 computed
+  if (p_last >= kPKeys - 1) {
+    fill_k(kb0, 0);
+    fill_v(vb0, 0);
+  } else {
+    fill_short(kr, kb0, fk0, false);
+    fill_short(vr, vb0, fv0, true);
+  }
+  if (n_tiles > 1) fill_k(kb1, kPKeys);
+  // the query operands and the first fills must have landed before the loop
+#pragma unroll
+  for (int cb = 0; cb < QC; ++cb)
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) require_loaded(qop[cb][ks]);
+  wait_fills();
+  __syncthreads();
+  f32x16 sa[QC][2], sbk[QC][2];
+  logits(kb0, sa);
+
+  // Step i: fills of K_{i+2} and V_{i+1} (into the buffers that tile i - 1's
+  // reads are done with: the barrier before them); the logits of tile i + 1
+  // from K_{i+1} beside tile i's softmax; O rescaled; O += V_i^T P_i; then
+  // wait for the fills.  Even steps hold K_{i+1} in kb1, V_i in vb0, S_i in
+  // sa; odd steps the other buffers.
+  bf16x8 pb[QC][4];
+  float alpha[QC];
+  auto step = [&](int i, auto odd_tag) {
+    constexpr bool kOdd = decltype(odd_tag)::value;
+    u16* k_next = kOdd ? kb0 : kb1;
+    u16* k_fill = kOdd ? kb1 : kb0;
+    u16* v_cur = kOdd ? vb1 : vb0;
+    u16* v_fill = kOdd ? vb0 : vb1;
+    f32x16 (&s_cur)[QC][2] = kOdd ? sbk : sa;
+    f32x16 (&s_next)[QC][2] = kOdd ? sa : sbk;
+    const int key0 = i * kPKeys;
+    // the operand bases, re-derived here so that their XORs stay in the step
+    kbase = kbase0;
+    vbase = vbase0;
+    asm volatile("" : "+v"(kbase), "+v"(vbase));
+    __syncthreads();
+    if (i + 2 < n_tiles) fill_k(k_fill, key0 + 2 * kPKeys);
+    if (i + 1 < n_tiles) fill_v(v_fill, key0 + kPKeys);
+    if (i < n_full) {
+      // the next tile's operand reads and MFMAs and this tile's softmax in
+      // one basic block, for the scheduler to interleave
+      logits(k_next, s_next);
+      tile_max(s_cur, key0, alpha, Full{});
+      tile_exp(s_cur, key0, alpha, pb, Full{});
+    } else {
+      if (i + 1 < n_tiles) logits(k_next, s_next);
+      tile_max(s_cur, key0, alpha, Masked{});
+      tile_exp(s_cur, key0, alpha, pb, Masked{});
     }
+    rescale(alpha);
+    // the MFMA phase at raised wave priority: the arbiter then prefers this
+    // wave's MFMAs over the other wave's softmax on the SIMD (measured 4%
+    // faster on the 4K-token chunk over 128K keys)
+    __builtin_amdgcn_s_setprio(1);
+    accumulate(v_cur, pb);
+    __builtin_amdgcn_s_setprio(0);
+    wait_fills();
+  };
+  using Even = std::integral_constant<bool, false>;
+  using Odd = std::integral_constant<bool, true>;
+  for (int i = 0; i < n_tiles; i += 2) {
+    step(i, Even{});
+    if (i + 1 >= n_tiles) break;
+    step(i + 1, Odd{});
   }
   // ---- epilogue: normalise, write out and the row statistics
 #pragma unroll
-  for (int qbk = 0; qbk < QB; ++qbk) {
-    double L = l[qbk];
-    L += __shfl_xor(L, 16);
+  for (int cb = 0; cb < QC; ++cb) {
+    double L = l[cb];
     L += __shfl_xor(L, 32);
-    const int t = tb * kTok + 2 * QB * wave + 2 * qbk + (col >> 3);
-    if (t >= T) continue;
-    const int h = col & 7;
+    if (t_col[cb] >= T) continue;
+    const int h = n & 7;
     const float inv = static_cast<float>(1.0 / L);
-    u16* orow = out + ((static_cast<size_t>(b) * T + t) * Hq + static_cast<size_t>(g) * kG + h) * kD;
+    u16* orow = out + ((static_cast<size_t>(b) * T + t_col[cb]) * Hq + static_cast<size_t>(g) * kG + h) * kD;
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      const uint2 pk{pack_bf16x2(o[qbk][nb][0] * inv, o[qbk][nb][1] * inv),
-                     pack_bf16x2(o[qbk][nb][2] * inv, o[qbk][nb][3] * inv)};
-      *reinterpret_cast<uint2*>(orow + 16 * nb + 4 * grp) = pk;
-    }
-    if (grp == 0) {
-      const size_t row = (static_cast<size_t>(b) * T + t) * Hkv + g;
-      const double l2 = static_cast<double>(m[qbk]) + log2(L);
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint2 pk{pack_bf16x2(o[cb][db][4 * j] * inv, o[cb][db][4 * j + 1] * inv),
+                       pack_bf16x2(o[cb][db][4 * j + 2] * inv, o[cb][db][4 * j + 3] * inv)};
+        *reinterpret_cast<uint2*>(orow + 32 * db + 8 * j + 4 * hf) = pk;
+      }
+    if (hf == 0) {
+      const size_t row = (static_cast<size_t>(b) * T + t_col[cb]) * Hkv + g;
+      const double l2 = static_cast<double>(m[cb]) + log2(L);
       lse2[row * kG + h] = l2;
       if (lse_out) lse_out[row * kG + h] = static_cast<float>(l2 * M_LN2);
       ytop_h[row * kG + h] = static_cast<float>(-log2(L));
@@ -690,10 +830,10 @@ hipError_t launch_full_prefill(const Plan& p, const u16* q, const u16* k, const 
   const double c2 = p.scale * 1.4426950408889634;  // scale * log2(e)
   const float c2_hi = static_cast<float>(c2);
   const float c2_lo = static_cast<float>(c2 - static_cast<double>(c2_hi));
-  constexpr int QB = kPrefillQB;
-  const int n_tblk = (p.T + 8 * QB - 1) / (8 * QB);
+  constexpr int QC = kAttnQC;
+  const int n_tblk = (p.T + 16 * QC - 1) / (16 * QC);
   const int n_wg = p.B * p.Hkv * n_tblk;
-  hipLaunchKernelGGL(full_prefill_kernel<QB>, dim3(n_wg), dim3(kPThreads), 0, st, q, k, v, out,
+  hipLaunchKernelGGL(full_prefill_kernel<QC>, dim3(n_wg), dim3(kPThreads), 0, st, q, k, v, out,
                      lse, reinterpret_cast<double*>(w + p.off_lse2),
                      reinterpret_cast<float*>(w + p.off_ytop), p.S, p.T, p.Hkv, n_tblk, c2_hi,
                      c2_lo, p.kvp);
