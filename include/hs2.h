@@ -82,8 +82,9 @@ typedef struct hs2_shape {
                          block's importance is the largest importance of its tokens, and
                          the top_k / select_block best blocks are kept, ties to the lower
                          block; the window is kept as before.  Needs top_k to be a
-                         multiple of it and ceil(ctx_len / select_block) <= 16384; the
-                         fused step supports it in decode (n_q_tokens = 1) only. */
+                         multiple of it and ceil(ctx_len / select_block) <= 16384.  A
+                         row's last block ends at the window, so a row that takes it holds
+                         fewer than top_k older tokens. */
   int64_t kv_capacity;/* token rows per KV head in k and v, i.e. the cache's row pitch:
                          row j of head (b, g) starts at element ((b*Hkv + g)*kv_capacity + j)*D.
                          0 means ctx_len; otherwise it must be >= ctx_len.  Rows ctx_len ..

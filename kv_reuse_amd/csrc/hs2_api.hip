@@ -174,8 +174,10 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
   q.off_cand_idx = take(cz * sizeof(int32_t));
   q.off_cand_cnt = take(decode ? Rz * q.sc_nchunk * sizeof(uint32_t) : 0);
   // band lists: a whole row's worth in decode; in a prefill chunk (many rows)
-  // a bounded list per row
+  // a bounded list per row, but one entry per block for block selection, so
+  // that any band of blocks is ranked exactly
   q.band_cap = decode ? 0 : std::min<int64_t>(q.Spad, kPrefillBandCap);
+  if (!decode && q.bs > 0) q.band_cap = std::max<int64_t>(q.band_cap, ceil_div(q.S, q.bs));
   q.off_band_idx = take(Rz * q.band_cap * sizeof(int32_t));
   q.off_band_key = take(Rz * q.band_cap * sizeof(uint64_t));
   // the fixed-point importance of a prefill chunk shares the key buffer of the
@@ -314,7 +316,6 @@ int check_step_args(const Plan& p, int32_t n_sparse_layers, const hs2_bf16* q_fu
                     const int32_t* n_sel) {
   if (!q_full || !k || !v || !out_full || !idx || !n_sel) return HS2_ERR_INVALID_ARG;
   if (n_sparse_layers > 0 && (!q_sparse || !out_sparse)) return HS2_ERR_INVALID_ARG;
-  if (p.T != 1 && p.bs != 0) return HS2_ERR_UNSUPPORTED;
   return HS2_OK;
 }
 
@@ -434,7 +435,6 @@ int hs2_cross_decoder_step_timed(const hs2_shape* shape, int32_t n_sparse_layers
   if (!q_full || !k || !v || !out_full || !idx || !n_sel || !phase_ms || iters < 1)
     return HS2_ERR_INVALID_ARG;
   if (n_sparse_layers > 0 && (!q_sparse || !out_sparse)) return HS2_ERR_INVALID_ARG;
-  if (p.T != 1 && p.bs != 0) return HS2_ERR_UNSUPPORTED;
   if ((st = check_ws(p, ws, ws_bytes)) != HS2_OK) return st;
   (void)hipGetLastError();
   const hipStream_t s = as_stream(stream);

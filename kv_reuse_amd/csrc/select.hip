@@ -1656,6 +1656,78 @@ __device__ __forceinline__ uint32_t lower_bound_lds(const int32_t* a, uint32_t n
   return lo;
 }
 
+// Rank a band of n_band keyed entries (bk[i] the key, bi[i] its payload, the
+// entries in ascending payload order) and write the payloads of the best
+// `take`, ascending, to win (at most win_cap of them); ties go to the earlier
+// entry.  Returns how many won.  The band is only read.  All kRowThreads
+// threads call it.
+__device__ uint32_t rank_band(const uint64_t* bk, const int32_t* bi, uint32_t n_band,
+                              uint32_t take, int32_t* win, uint32_t win_cap, uint32_t* s_count,
+                              uint32_t* h256, uint32_t* s_red, uint64_t* s_hi, uint32_t* s_need,
+                              int* s_done, uint32_t (*s_cnt)[16], uint32_t* s_base) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  if (n_band <= 64) {
+    // a small band: wave 0 ranks it directly.  Lane i holds entry i; its rank
+    // counts the entries with a larger key, or an equal key and a lower
+    // position; the best `take` win
+    if (wave == 0) {
+      const bool have = static_cast<uint32_t>(lane) < n_band;
+      const uint64_t kh = have ? bk[lane] : 0ull;
+      uint32_t rank = 0;
+      for (int j = 0; j < static_cast<int>(n_band); ++j) {
+        const uint64_t kj = lane_value64(kh, j);
+        rank += (kj > kh || (kj == kh && j < lane)) ? 1u : 0u;
+      }
+      const bool won = have && rank < take;
+      const uint64_t bal = __ballot(won);
+      if (won) win[__popcll(bal & ((1ull << lane) - 1ull))] = bi[lane];
+      if (lane == 0) *s_count = static_cast<uint32_t>(__popcll(bal));
+    }
+    __syncthreads();
+    return *s_count;
+  }
+  // the band's share: all of it, or the best `take` by threshold
+  KThr kt{0ull, 0u, true};
+  const bool by_thr = take < n_band;
+  if (by_thr && take > 0) kt = key_threshold(bk, n_band, take, h256, s_red, s_hi, s_need, s_done);
+  // winners in band order, ties: the first kt.nd_t
+  const uint32_t per = (n_band + kRowThreads - 1) / kRowThreads;
+  const uint32_t q0 = min(n_band, tid * per), q1 = min(n_band, q0 + per);
+  // class of entry i: 1 a winner, 2 a tie at the threshold, 0 out
+  auto cls = [&](uint32_t i) -> uint32_t {
+    if (!by_thr) return 1u;
+    if (take == 0) return 0u;
+    const uint64_t kh = bk[i];
+    if (kh > kt.thr || (kt.incl && kh == kt.thr)) return 1u;
+    return kh == kt.thr ? 2u : 0u;
+  };
+  uint32_t nwin = 0, ntie = 0;
+  for (uint32_t i = q0; i < q1; ++i) {
+    const uint32_t c = cls(i);
+    nwin += c == 1u;
+    ntie += c == 2u;
+  }
+  uint32_t o_tie, o_dummy;
+  reserve_two(ntie, 0u, nullptr, nullptr, s_cnt, s_base, o_tie, o_dummy);
+  uint32_t keep_tie = 0;
+  for (uint32_t i = q0, ot = o_tie; i < q1; ++i)
+    if (cls(i) == 2u) keep_tie += (ot++ < kt.nd_t);
+  uint32_t o_w;
+  reserve_two(nwin + keep_tie, 0u, nullptr, nullptr, s_cnt, s_base, o_w, o_dummy);
+  const uint32_t n_w = s_base[2];
+  for (uint32_t i = q0, ot = o_tie; i < q1; ++i) {
+    const uint32_t c = cls(i);
+    bool a = c == 1u;
+    if (c == 2u) a = (ot++ < kt.nd_t);
+    if (a) {
+      if (o_w < win_cap) win[o_w] = bi[i];
+      ++o_w;
+    }
+  }
+  return n_w;
+}
+
 // One work-group per row (b, t, g) of a prefill chunk: the exact top-k of the
 // row's older keys from their stored log2 importance v (16-bit fixed point,
 // 2^-10 octave steps; bin = v >> 7 is an eighth of an octave).
@@ -1679,6 +1751,15 @@ __device__ __forceinline__ uint32_t lower_bound_lds(const int32_t* a, uint32_t n
 // A list longer than LDS holds is replaced by a second pass over v, with the
 // band widened to [first value of b* - E, last value of b* + E]; a band larger
 // than band_cap is ranked by v itself.
+// Block-level selection (kBlocks, blocks of bs tokens) takes the same steps on
+// the blocks' values, each the largest stored value of its tokens: one pass
+// writes them (and their histogram) to LDS, c is the n_take-th largest, blocks
+// above c + E are taken, and each band block's exact importance is the largest
+// float64 importance of its tokens stored at or above (its value) - E, the only
+// ones that can hold it.  The band is ranked exactly whatever its size (the
+// plan gives every row a band list of one entry per block).
+constexpr int kMaxBlocks = 16384;   // blocks per row (block-level selection)
+constexpr int kMaxSelBlocks = kMaxSel / 16;   // blocks taken per row: top_k / block, block >= 16
 constexpr int kPList = 4 * kUncCap;   // listed values per row held in LDS
 constexpr int kPListPer = kPList / kRowThreads;
 constexpr int kVBinShift = 16 - 9;    // v >> 7: the kPNB = 512 bins
@@ -1692,6 +1773,7 @@ __device__ __forceinline__ uint32_t u16_at(const u32x4 (&v)[2], int e) {
   return (e & 1) ? (word >> 16) : (word & 0xFFFFu);
 }
 
+template <bool kBlocks>
 __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
     const u16* __restrict__ ybuf, const uint32_t* __restrict__ kmax, int n_ib,
     const double* __restrict__ lse2, double* __restrict__ lse2r, float* __restrict__ lse_out,
@@ -1699,7 +1781,9 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, int32_t* __restrict__ band_idx,
     uint64_t* __restrict__ band_key, int64_t band_cap, int32_t* __restrict__ idx_out,
     int32_t* __restrict__ nsel_out, int64_t S, int64_t Spad, int T, int Hkv, int topk, int w,
-    int cap, double c2, float c2_hi, int64_t kvp) {
+    int cap, int bs, double c2, float c2_hi, int64_t kvp) {
+  static_assert(kMaxBlocks * sizeof(uint16_t) <= kPList * sizeof(uint32_t), "block maxima fit the list");
+  static_assert(3 * (kMaxSel / 4) + 2 * kMaxSelBlocks <= kMaxSel, "block lists fit bw");
   __shared__ __align__(16) int32_t up[kMaxSel];
   __shared__ __align__(16) int32_t bw[kMaxSel];        // band winners; first the histogram
   // the list's indices; after the split, the band (keys, then indices); the
@@ -1760,6 +1844,31 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
     s_corr[tid] = 0ull;
   }
   if (tid == 0) s_ndom = 0u;
+  // A key's importance in float64 (bf16 products are exact), the largest over
+  // the heads of c2 q_h.k - lse2_h: 16 lanes per key, lane `part` of a group
+  // taking dims 8 part .. 8 part + 7 of all the heads, then a sum over the
+  // group (its 16 lanes must share the key).  Every lane returns the value.
+  auto exact_importance = [&](int64_t key, int part) -> double {
+    const u32x4 raw = load_u32x4(kr + static_cast<size_t>(key) * kD + 8 * part);
+    double kv[8];
+#pragma unroll
+    for (int t2 = 0; t2 < 8; ++t2) {
+      const uint32_t word = raw[t2 >> 1];
+      kv[t2] = static_cast<double>(__uint_as_float((t2 & 1) ? (word & 0xFFFF0000u) : (word << 16)));
+    }
+    // one head at a time (a short live range)
+    double yy = -INFINITY;
+#pragma unroll 1
+    for (int h = 0; h < kG; ++h) {
+      const double* qh = qd + h * kD + 8 * part;
+      double acc = 0.0;
+#pragma unroll
+      for (int t2 = 0; t2 < 8; ++t2) acc = fma(qh[t2], kv[t2], acc);
+      acc = row16_sum(acc);
+      yy = fmax(yy, c2 * acc - l2s[h]);
+    }
+    return yy;
+  };
   // the stored value of importance 2^kDomLog2 (as the importance pass stores:
   // 2^10 steps per octave above the row's top log-weight minus 64)
   int vdom;
@@ -1906,343 +2015,463 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
     }
     __syncthreads();
     const int E = s_E;
-    // 16 values per thread and round, as two 16-byte loads; the next round's
-    // loads are issued before this round is processed
-    const int64_t rounds = (first + 16 * kRowThreads - 1) / (16 * kRowThreads);
-    auto load_round = [&](int64_t rr, u32x4 (&yv)[2]) {
-      const int64_t i0 = 16 * (static_cast<int64_t>(tid) + rr * kRowThreads);
+    if (kBlocks) {
+      // ---- block-level selection.  A block's stored value (the largest
+      // stored value of its tokens) is within the same bound of its exact
+      // importance (the largest float64 importance of its tokens) as a
+      // token's, so the band argument carries over to blocks unchanged: with
+      // c the n_take-th largest block value, blocks above c + E are taken,
+      // blocks below c - E are not, and the band's blocks are ranked on their
+      // exact importance.  Of a band block only the tokens stored at or above
+      // (block value) - E can hold its exact maximum.
+      uint16_t* bmx = reinterpret_cast<uint16_t*>(pool);   // a value per block
+      const int nblk = static_cast<int>((first + bs - 1) / bs);
+      const int bs_log2 = __builtin_ctz(static_cast<unsigned>(bs));
+      const int n_take = min(topk >> bs_log2, nblk);
+      {
+        // the pass: 32 values per thread and round (an aligned run inside one
+        // block when bs >= 32, two blocks' runs when bs = 16), block maxima
+        // over bs / 32 neighbouring lanes, their histogram, and the older
+        // dominant keys for the refinement
+        constexpr int kV = 32;
+        const int lpb = bs / kV;   // lanes per block (0: bs = 16)
+        const int64_t prounds = (first + kV * kRowThreads - 1) / (kV * kRowThreads);
+        auto load_pround = [&](int64_t rr, u32x4 (&yv)[4]) {
+          const int64_t i0 = kV * (static_cast<int64_t>(tid) + rr * kRowThreads);
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-        yv[u] = i0 + 8 * u < first ? *reinterpret_cast<const u32x4*>(yr + i0 + 8 * u)
-                                   : u32x4{0u, 0u, 0u, 0u};
-    };
-    // ---- the pass: histogram at or above floor, and the list of the values
-    // at or above (first value of floor) - E.  One barrier per round: the
-    // floor that wave 0 raises after it is read by the other waves whenever
-    // they get to it (a stale floor is still a valid one: it only lists and
-    // counts more).  The first round's values are counted before any are
-    // listed, so that its floor already applies to them.
-    uint32_t n_list = 0;
-    {
-      // 32 values per thread and round here (four 16-byte loads), so half as
-      // many rounds, and barriers, as the second pass below
-      constexpr int kV = 32;
-      const int64_t prounds = (first + kV * kRowThreads - 1) / (kV * kRowThreads);
-      auto load_pround = [&](int64_t rr, u32x4 (&yv)[4]) {
-        const int64_t i0 = kV * (static_cast<int64_t>(tid) + rr * kRowThreads);
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          yv[u] = i0 + 8 * u < first ? *reinterpret_cast<const u32x4*>(yr + i0 + 8 * u)
-                                     : u32x4{0u, 0u, 0u, 0u};
-      };
-      auto val_at = [](const u32x4 (&yv)[4], int e) -> uint32_t {
-        const uint32_t word = yv[e >> 3][(e >> 1) & 3];
-        return (e & 1) ? (word >> 16) : (word & 0xFFFFu);
-      };
-      u32x4 ycur[4], ynxt[4];
-      if (prounds > 0) load_pround(0, ycur);
-      for (int64_t rr = 0; rr < prounds; ++rr) {
-        const int64_t i0 = kV * (static_cast<int64_t>(tid) + rr * kRowThreads);
-        if (rr + 1 < prounds) load_pround(rr + 1, ynxt);
-        const int nv = static_cast<int>(min(static_cast<int64_t>(kV), first - i0));
-        int fl = *static_cast<volatile int*>(&s_floor);
-#pragma unroll
-        for (int e = 0; e < kV; ++e) {
-          const int bn = static_cast<int>(val_at(ycur, e) >> kVBinShift);
-          if (e < nv && bn >= fl) atomicAdd(&lh[bn], 1u);
-        }
-        if (rr == 0) {
-          __syncthreads();
-          if (wave == 0) {
-            const KthBin kb = kth_bin_wave_n<kPNB>(lh, static_cast<uint32_t>(topk));
-            if (lane == 0 && kb.found) s_floor = kb.bstar;
-          }
-          __syncthreads();
-          fl = s_floor;
-        }
-        const int vmin = (fl << kVBinShift) - E;
-        uint32_t ml = 0, md = 0;
-#pragma unroll
-        for (int e = 0; e < kV; ++e) {
-          const int v = static_cast<int>(val_at(ycur, e));
-          ml |= static_cast<uint32_t>(e < nv && v >= vmin) << e;
-          md |= static_cast<uint32_t>(e < nv && v >= vdom) << e;
-        }
-        for (uint32_t m = md; m; m &= m - 1) list_dom(i0 + __builtin_ctz(m));   // rare
-        uint32_t ol, o_dummy, tot, t_dummy;
-        block_offsets2<kRowThreads / 64>(__popc(ml), 0u, s_off[rr & 1], ol, o_dummy, tot, t_dummy);
-        // the round's atomics are complete: raise the floor
-        if (wave == 0) {
-          const KthBin kb = kth_bin_wave_n<kPNB>(lh, static_cast<uint32_t>(topk));
-          if (lane == 0 && kb.found && kb.bstar > fl) atomicMax(&s_floor, kb.bstar);
-        }
-        ol += n_list;
-        n_list += tot;
-        if (ml) {
+          for (int u = 0; u < 4; ++u)
+            yv[u] = i0 + 8 * u < first ? *reinterpret_cast<const u32x4*>(yr + i0 + 8 * u)
+                                       : u32x4{0u, 0u, 0u, 0u};
+        };
+        u32x4 ycur[4], ynxt[4];
+        if (prounds > 0) load_pround(0, ycur);
+        for (int64_t rr = 0; rr < prounds; ++rr) {
+          const int64_t i0 = kV * (static_cast<int64_t>(tid) + rr * kRowThreads);
+          if (rr + 1 < prounds) load_pround(rr + 1, ynxt);
+          const int nv = static_cast<int>(max(static_cast<int64_t>(0), min(static_cast<int64_t>(kV), first - i0)));
+          uint32_t m0 = 0, m1 = 0, md = 0;
 #pragma unroll
           for (int e = 0; e < kV; ++e) {
-            if (!((ml >> e) & 1u)) continue;
-            if (ol < static_cast<uint32_t>(kPList)) {
-              lidx[ol] = static_cast<int32_t>(i0 + e);
-              lval[ol] = static_cast<uint16_t>(val_at(ycur, e));
+            const uint32_t word = ycur[e >> 3][(e >> 1) & 3];
+            const uint32_t v = e < nv ? ((e & 1) ? (word >> 16) : (word & 0xFFFFu)) : 0u;
+            if (e < 16) m0 = max(m0, v);
+            else m1 = max(m1, v);
+            md |= static_cast<uint32_t>(e < nv && static_cast<int>(v) >= vdom) << e;
+          }
+          for (uint32_t m = md; m; m &= m - 1) list_dom(i0 + __builtin_ctz(m));   // rare
+          if (lpb == 0) {
+            if (nv > 0) {
+              bmx[i0 >> 4] = static_cast<uint16_t>(m0);
+              atomicAdd(&lh[m0 >> kVBinShift], 1u);
             }
-            ++ol;
+            if (nv > 16) {
+              bmx[(i0 >> 4) + 1] = static_cast<uint16_t>(m1);
+              atomicAdd(&lh[m1 >> kVBinShift], 1u);
+            }
+          } else {
+            uint32_t m = max(m0, m1);
+            for (int off = 1; off < lpb; off <<= 1)
+              m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), off)));
+            // the block's first lane: its run starts the block
+            if ((lane & (lpb - 1)) == 0 && nv > 0) {
+              bmx[i0 >> bs_log2] = static_cast<uint16_t>(m);
+              atomicAdd(&lh[m >> kVBinShift], 1u);
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) ycur[u] = ynxt[u];
+        }
+      }
+      refine_row();   // (l2s refined before the band is ranked with it)
+      // LDS use from here: bw holds the band's keys (u64, at most kBandBlk),
+      // its block indices, the band winners and the merged selection; up the
+      // blocks taken outright
+      constexpr int kBandBlk = kMaxSel / 4;   // band blocks held in LDS
+      uint64_t* lbk_b = reinterpret_cast<uint64_t*>(bw);
+      int32_t* lbi_b = bw + 2 * kBandBlk;
+      int32_t* bwin = bw + 3 * kBandBlk;
+      int32_t* sel = bw + 3 * kBandBlk + kMaxSelBlocks;
+      if (n_take == nblk) {
+        // every block: the selection is [0, first)
+        for (int64_t i = tid; i < first; i += kRowThreads) out[i] = static_cast<int32_t>(i);
+        n_keep = static_cast<uint32_t>(first);
+      } else {
+        if (tid < 128) h256[tid] = 0u;
+        __syncthreads();
+        if (tid < 64) {
+          const KthBin kb = kth_bin_wave_n<kPNB>(lh, static_cast<uint32_t>(n_take));
+          if (tid == 0) {
+            s_b = kb.bstar;   // found: n_take < nblk, the number of values counted
+            s_above = kb.above;
           }
         }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) ycur[u] = ynxt[u];
-      }
-    }
-    refine_row();   // (l2s refined before the band is ranked with it)
-    const bool listed = n_list <= static_cast<uint32_t>(kPList);
-    if (tid < 128) h256[tid] = 0u;
-    __syncthreads();
-    if (tid < 64) {
-      const KthBin kb = kth_bin_wave_n<kPNB>(lh, static_cast<uint32_t>(topk));
-      if (tid == 0) {
-        s_b = kb.found ? kb.bstar : -1;
-        s_above = kb.above;
-      }
-    }
-    __syncthreads();
-    if (s_b < 0) {
-      // fewer older keys than top_k: all of them, in order
-      n_keep = static_cast<uint32_t>(min(first, static_cast<int64_t>(topk)));
-      for (uint32_t i = tid; i < n_keep; i += kRowThreads) out[i] = static_cast<int32_t>(i);
-    } else {
-      const int bstar = s_b;
-      int band_lo, band_hi;
-      if (listed) {
-        // ---- c: the k-th largest v, from the listed values in bin b*
-        for (uint32_t i = tid; i < n_list; i += kRowThreads) {
-          const uint32_t v = lval[i];
+        __syncthreads();
+        const int bstar = s_b;
+        for (int c = tid; c < nblk; c += kRowThreads) {
+          const uint32_t v = bmx[c];
           if (static_cast<int>(v >> kVBinShift) == bstar) atomicAdd(&h256[v & 127u], 1u);
         }
         __syncthreads();
         if (tid < 64) {
-          const KthBin kc = kth_bin_wave_n<128>(h256, static_cast<uint32_t>(topk) - s_above);
+          const KthBin kc = kth_bin_wave_n<128>(h256, static_cast<uint32_t>(n_take) - s_above);
           if (tid == 0) s_c = (bstar << kVBinShift) | kc.bstar;
         }
         __syncthreads();
-        band_lo = max(0, s_c - E);
-        band_hi = min(65535, s_c + E);
-      } else {
-        band_lo = max(0, (bstar << kVBinShift) - E);
-        band_hi = min(65535, (bstar << kVBinShift) + 127 + E);
-      }
-      int32_t* gbi = band_idx + static_cast<size_t>(r) * band_cap;
-      uint64_t* gbk = band_key + static_cast<size_t>(r) * band_cap;
-      bool band_lds = false, band_glob = false;
-      int32_t* bi = gbi;
-      uint64_t* bk = gbk;
-      uint32_t cu = 0, ca = 0;
-      if (listed) {
-        // ---- split the list: each thread takes kPListPer consecutive
-        // entries into registers, so the band may overwrite the list
-        const uint32_t q0 = static_cast<uint32_t>(tid) * kPListPer;
-        int32_t li[kPListPer];
+        const int band_lo = max(0, s_c - E);
+        const int band_hi = min(65535, s_c + E);
+        // thread t classifies the blocks [t per, (t + 1) per), per <= 32
+        const int per = (nblk + kRowThreads - 1) / kRowThreads;
+        const int c0 = min(nblk, tid * per), c1 = min(nblk, c0 + per);
         uint32_t mu = 0, ma = 0;
-#pragma unroll
-        for (int j = 0; j < kPListPer; ++j) {
-          const uint32_t i = q0 + j;
-          li[j] = 0;
-          if (i < n_list) {
-            li[j] = lidx[i];
-            const int v = lval[i];
-            mu |= static_cast<uint32_t>(v > band_hi) << j;
-            ma |= static_cast<uint32_t>(v >= band_lo && v <= band_hi) << j;
-          }
+        for (int j = 0; j < c1 - c0; ++j) {
+          const int v = bmx[c0 + j];
+          mu |= static_cast<uint32_t>(v > band_hi) << j;
+          ma |= static_cast<uint32_t>(v >= band_lo && v <= band_hi) << j;
         }
-        uint32_t ou, oa;
+        uint32_t ou, oa, cu, ca;
         block_offsets2<kRowThreads / 64>(__popc(mu), __popc(ma), s_off[0], ou, oa, cu, ca);
-        band_lds = ca <= static_cast<uint32_t>(kUncCap);
-        band_glob = !band_lds && ca <= static_cast<uint64_t>(band_cap);
-        bi = band_lds ? lbi : gbi;
-        bk = band_lds ? lbk : gbk;
-#pragma unroll
-        for (int j = 0; j < kPListPer; ++j) {
-          if ((mu >> j) & 1u) {
-            if (ou < static_cast<uint32_t>(kMaxSel)) up[ou] = li[j];
-            ++ou;
-          }
-          if ((ma >> j) & 1u) {
-            if (band_lds || band_glob) bi[oa] = li[j];
-            ++oa;
-          }
+        // the band fits LDS or the row's global band list (the plan gives
+        // block selection a list of at least one entry per block)
+        const bool band_lds = ca <= static_cast<uint32_t>(kBandBlk);
+        int32_t* bi = band_lds ? lbi_b : band_idx + static_cast<size_t>(r) * band_cap;
+        uint64_t* bk = band_lds ? lbk_b : band_key + static_cast<size_t>(r) * band_cap;
+        const uint32_t bcap = band_lds ? static_cast<uint32_t>(kBandBlk)
+                                       : static_cast<uint32_t>(min(band_cap, static_cast<int64_t>(nblk)));
+        for (uint32_t m = mu; m; m &= m - 1) {
+          if (ou < static_cast<uint32_t>(kMaxSelBlocks)) up[ou] = c0 + __builtin_ctz(m);
+          ++ou;
         }
-      } else {
-        // ---- the list overflowed: a second pass over v, in key order; the
-        // band goes to the global list (up to band_cap entries)
-        u32x4 ycur[2], ynxt[2];
-        if (rounds > 0) load_round(0, ycur);
-        for (int64_t rr = 0; rr < rounds; ++rr) {
-          const int64_t i0 = 16 * (static_cast<int64_t>(tid) + rr * kRowThreads);
-          if (rr + 1 < rounds) load_round(rr + 1, ynxt);
-          const int nv = static_cast<int>(min(static_cast<int64_t>(16), first - i0));
-          uint32_t mu = 0, ma = 0;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int v = static_cast<int>(u16_at(ycur, e));
-            mu |= static_cast<uint32_t>(e < nv && v > band_hi) << e;
-            ma |= static_cast<uint32_t>(e < nv && v >= band_lo && v <= band_hi) << e;
-          }
-          uint32_t ou, oa;
-          reserve_two(__popc(mu), __popc(ma), nullptr, nullptr, s_cnt, s_base, ou, oa);
-          ou += cu;
-          oa += ca;
-          cu += s_base[2];
-          ca += s_base[3];
-          for (uint32_t m = mu; m; m &= m - 1) {
-            if (ou < static_cast<uint32_t>(kMaxSel)) up[ou] = static_cast<int32_t>(i0 + __builtin_ctz(m));
-            ++ou;
-          }
-          for (uint32_t m = ma; m; m &= m - 1) {
-            if (oa < static_cast<uint64_t>(band_cap)) gbi[oa] = static_cast<int32_t>(i0 + __builtin_ctz(m));
-            ++oa;
-          }
-#pragma unroll
-          for (int u = 0; u < 2; ++u) ycur[u] = ynxt[u];
-        }
-        band_glob = ca <= static_cast<uint64_t>(band_cap);
-      }
-      __syncthreads();
-      const uint32_t n_up = min(cu, static_cast<uint32_t>(topk));
-      const uint32_t take = static_cast<uint32_t>(topk) - n_up;
-      uint32_t n_w = 0;
-      if (band_lds || band_glob) {
-        const uint32_t n_band = min(ca, band_lds ? static_cast<uint32_t>(kUncCap)
-                                                 : static_cast<uint32_t>(band_cap));
-        // ---- exact importance of the band keys in float64 (bf16 products are
-        // exact): 16 lanes per key, lane j of a group taking dims 8j..8j+7 of
-        // all 8 heads, then a sum over the group
-        const int part = tid & 15;
-        for (uint32_t i = static_cast<uint32_t>(tid) >> 4; i < n_band; i += kRowThreads / 16) {
-          const u32x4 raw = load_u32x4(kr + static_cast<size_t>(bi[i]) * kD + 8 * part);
-          double kv[8];
-#pragma unroll
-          for (int t2 = 0; t2 < 8; ++t2) {
-            const uint32_t word = raw[t2 >> 1];
-            kv[t2] = static_cast<double>(__uint_as_float((t2 & 1) ? (word & 0xFFFF0000u) : (word << 16)));
-          }
-          // one head at a time (a short live range), summed over the group:
-          // its 16 lanes share i, so the exchanges stay in the group
-          double yy = -INFINITY;
-#pragma unroll 1
-          for (int h = 0; h < kG; ++h) {
-            const double* qh = qd + h * kD + 8 * part;
-            double acc = 0.0;
-#pragma unroll
-            for (int t2 = 0; t2 < 8; ++t2) acc = fma(qh[t2], kv[t2], acc);
-            acc = row16_sum(acc);
-            yy = fmax(yy, c2 * acc - l2s[h]);
-          }
-          if (part == 0) bk[i] = ordered_u64(yy);
+        for (uint32_t m = ma; m; m &= m - 1) {
+          if (oa < bcap) bi[oa] = c0 + __builtin_ctz(m);
+          ++oa;
         }
         __syncthreads();
-        if (n_band <= 64) {
-          // ---- a small band: wave 0 ranks it directly.  Lane i holds band
-          // entry i (index order); its rank counts the entries with a larger
-          // key, or an equal key and a lower index; the best `take` win
-          if (wave == 0) {
-            const bool have = static_cast<uint32_t>(lane) < n_band;
-            const uint64_t kh = have ? bk[lane] : 0ull;
-            uint32_t rank = 0;
-            for (int j = 0; j < static_cast<int>(n_band); ++j) {
-              const uint64_t kj = lane_value64(kh, j);
-              rank += (kj > kh || (kj == kh && j < lane)) ? 1u : 0u;
+        const uint32_t n_up = min(cu, static_cast<uint32_t>(n_take));
+        const uint32_t take = static_cast<uint32_t>(n_take) - n_up;
+        const uint32_t n_band = min(ca, bcap);
+        // ---- each band block's exact importance, a wave per block: its
+        // tokens stored at or above (block value) - E, four at a time (16
+        // lanes each), the largest key over the wave
+        const int part = lane & 15, grp = lane >> 4;
+        for (uint32_t i = wave; i < n_band; i += kRowThreads / 64) {
+          const int blk = bi[i];
+          const int64_t j0 = static_cast<int64_t>(blk) << bs_log2;
+          const int64_t j1 = min(first, j0 + bs);
+          const int thr = static_cast<int>(bmx[blk]) - E;
+          uint64_t best = 0ull;
+          for (int64_t jb = j0; jb < j1; jb += 64) {
+            const int64_t j = jb + lane;
+            uint64_t m = __ballot(j < j1 && static_cast<int>(yr[min(j, j1 - 1)]) >= thr);
+            while (m) {
+              uint64_t mg = m;   // this group's candidate: the grp-th of m
+              for (int s = 0; s < grp; ++s) mg &= mg - 1;
+              const int64_t key = jb + __builtin_ctzll(mg ? mg : m);
+              const double yy = exact_importance(key, part);
+              if (mg) best = max(best, ordered_u64(yy));
+#pragma unroll
+              for (int s = 0; s < 4; ++s) m &= m - 1;
             }
-            const bool win = have && rank < take;
-            const uint64_t bal = __ballot(win);
-            if (win) bw[__popcll(bal & ((1ull << lane) - 1ull))] = bi[lane];
-            if (lane == 0) s_count = static_cast<uint32_t>(__popcll(bal));
+          }
+#pragma unroll
+          for (int off = 32; off > 0; off >>= 1) {
+            const uint64_t o = (static_cast<uint64_t>(static_cast<uint32_t>(
+                                    __shfl_xor(static_cast<int>(best >> 32), off))) << 32) |
+                               static_cast<uint32_t>(__shfl_xor(static_cast<int>(best), off));
+            best = max(best, o);
+          }
+          if (lane == 0) bk[i] = best;
+        }
+        __syncthreads();
+        const uint32_t n_w = rank_band(bk, bi, n_band, take, bwin, kMaxSelBlocks, &s_count, h256,
+                                       s_red, &s_hi, &s_need, &s_done, s_cnt, s_base);
+        __syncthreads();
+        // ---- merge the two ascending block lists by rank
+        for (uint32_t i = tid; i < n_up; i += kRowThreads) {
+          const int32_t v = up[i];
+          const uint32_t rk = i + lower_bound_lds(bwin, n_w, v);
+          if (rk < static_cast<uint32_t>(kMaxSelBlocks)) sel[rk] = v;
+        }
+        for (uint32_t i = tid; i < n_w; i += kRowThreads) {
+          const int32_t v = bwin[i];
+          const uint32_t rk = i + lower_bound_lds(up, n_up, v);
+          if (rk < static_cast<uint32_t>(kMaxSelBlocks)) sel[rk] = v;
+        }
+        const uint32_t n_sb = min(n_up + n_w, static_cast<uint32_t>(n_take));
+        __syncthreads();
+        // the selected blocks' tokens in ascending order: every block but the
+        // row's last is whole, and the last, if taken, comes last
+        const uint32_t n_tok = n_sb << bs_log2;
+        for (uint32_t i = tid; i < n_tok; i += kRowThreads) {
+          const int64_t j = (static_cast<int64_t>(sel[i >> bs_log2]) << bs_log2) + (i & (bs - 1));
+          if (j < first) out[i] = static_cast<int32_t>(j);
+        }
+        if (n_sb > 0 && sel[n_sb - 1] == nblk - 1) {
+          n_keep = n_tok - static_cast<uint32_t>((static_cast<int64_t>(nblk) << bs_log2) - first);
+        } else {
+          n_keep = n_tok;
+        }
+      }
+    } else {
+      // 16 values per thread and round, as two 16-byte loads; the next round's
+      // loads are issued before this round is processed
+      const int64_t rounds = (first + 16 * kRowThreads - 1) / (16 * kRowThreads);
+      auto load_round = [&](int64_t rr, u32x4 (&yv)[2]) {
+        const int64_t i0 = 16 * (static_cast<int64_t>(tid) + rr * kRowThreads);
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+          yv[u] = i0 + 8 * u < first ? *reinterpret_cast<const u32x4*>(yr + i0 + 8 * u)
+                                     : u32x4{0u, 0u, 0u, 0u};
+      };
+      // ---- the pass: histogram at or above floor, and the list of the values
+      // at or above (first value of floor) - E.  One barrier per round: the
+      // floor that wave 0 raises after it is read by the other waves whenever
+      // they get to it (a stale floor is still a valid one: it only lists and
+      // counts more).  The first round's values are counted before any are
+      // listed, so that its floor already applies to them.
+      uint32_t n_list = 0;
+      {
+        // 32 values per thread and round here (four 16-byte loads), so half as
+        // many rounds, and barriers, as the second pass below
+        constexpr int kV = 32;
+        const int64_t prounds = (first + kV * kRowThreads - 1) / (kV * kRowThreads);
+        auto load_pround = [&](int64_t rr, u32x4 (&yv)[4]) {
+          const int64_t i0 = kV * (static_cast<int64_t>(tid) + rr * kRowThreads);
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            yv[u] = i0 + 8 * u < first ? *reinterpret_cast<const u32x4*>(yr + i0 + 8 * u)
+                                       : u32x4{0u, 0u, 0u, 0u};
+        };
+        auto val_at = [](const u32x4 (&yv)[4], int e) -> uint32_t {
+          const uint32_t word = yv[e >> 3][(e >> 1) & 3];
+          return (e & 1) ? (word >> 16) : (word & 0xFFFFu);
+        };
+        u32x4 ycur[4], ynxt[4];
+        if (prounds > 0) load_pround(0, ycur);
+        for (int64_t rr = 0; rr < prounds; ++rr) {
+          const int64_t i0 = kV * (static_cast<int64_t>(tid) + rr * kRowThreads);
+          if (rr + 1 < prounds) load_pround(rr + 1, ynxt);
+          const int nv = static_cast<int>(min(static_cast<int64_t>(kV), first - i0));
+          int fl = *static_cast<volatile int*>(&s_floor);
+#pragma unroll
+          for (int e = 0; e < kV; ++e) {
+            const int bn = static_cast<int>(val_at(ycur, e) >> kVBinShift);
+            if (e < nv && bn >= fl) atomicAdd(&lh[bn], 1u);
+          }
+          if (rr == 0) {
+            __syncthreads();
+            if (wave == 0) {
+              const KthBin kb = kth_bin_wave_n<kPNB>(lh, static_cast<uint32_t>(topk));
+              if (lane == 0 && kb.found) s_floor = kb.bstar;
+            }
+            __syncthreads();
+            fl = s_floor;
+          }
+          const int vmin = (fl << kVBinShift) - E;
+          uint32_t ml = 0, md = 0;
+#pragma unroll
+          for (int e = 0; e < kV; ++e) {
+            const int v = static_cast<int>(val_at(ycur, e));
+            ml |= static_cast<uint32_t>(e < nv && v >= vmin) << e;
+            md |= static_cast<uint32_t>(e < nv && v >= vdom) << e;
+          }
+          for (uint32_t m = md; m; m &= m - 1) list_dom(i0 + __builtin_ctz(m));   // rare
+          uint32_t ol, o_dummy, tot, t_dummy;
+          block_offsets2<kRowThreads / 64>(__popc(ml), 0u, s_off[rr & 1], ol, o_dummy, tot, t_dummy);
+          // the round's atomics are complete: raise the floor
+          if (wave == 0) {
+            const KthBin kb = kth_bin_wave_n<kPNB>(lh, static_cast<uint32_t>(topk));
+            if (lane == 0 && kb.found && kb.bstar > fl) atomicMax(&s_floor, kb.bstar);
+          }
+          ol += n_list;
+          n_list += tot;
+          if (ml) {
+#pragma unroll
+            for (int e = 0; e < kV; ++e) {
+              if (!((ml >> e) & 1u)) continue;
+              if (ol < static_cast<uint32_t>(kPList)) {
+                lidx[ol] = static_cast<int32_t>(i0 + e);
+                lval[ol] = static_cast<uint16_t>(val_at(ycur, e));
+              }
+              ++ol;
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) ycur[u] = ynxt[u];
+        }
+      }
+      refine_row();   // (l2s refined before the band is ranked with it)
+      const bool listed = n_list <= static_cast<uint32_t>(kPList);
+      if (tid < 128) h256[tid] = 0u;
+      __syncthreads();
+      if (tid < 64) {
+        const KthBin kb = kth_bin_wave_n<kPNB>(lh, static_cast<uint32_t>(topk));
+        if (tid == 0) {
+          s_b = kb.found ? kb.bstar : -1;
+          s_above = kb.above;
+        }
+      }
+      __syncthreads();
+      if (s_b < 0) {
+        // fewer older keys than top_k: all of them, in order
+        n_keep = static_cast<uint32_t>(min(first, static_cast<int64_t>(topk)));
+        for (uint32_t i = tid; i < n_keep; i += kRowThreads) out[i] = static_cast<int32_t>(i);
+      } else {
+        const int bstar = s_b;
+        int band_lo, band_hi;
+        if (listed) {
+          // ---- c: the k-th largest v, from the listed values in bin b*
+          for (uint32_t i = tid; i < n_list; i += kRowThreads) {
+            const uint32_t v = lval[i];
+            if (static_cast<int>(v >> kVBinShift) == bstar) atomicAdd(&h256[v & 127u], 1u);
           }
           __syncthreads();
-          n_w = s_count;
+          if (tid < 64) {
+            const KthBin kc = kth_bin_wave_n<128>(h256, static_cast<uint32_t>(topk) - s_above);
+            if (tid == 0) s_c = (bstar << kVBinShift) | kc.bstar;
+          }
+          __syncthreads();
+          band_lo = max(0, s_c - E);
+          band_hi = min(65535, s_c + E);
         } else {
-        // ---- the band's share: all of it, or the best `take` by threshold
-        KThr kt{0ull, 0u, true};
-        const bool by_thr = take < n_band;
-        if (by_thr && take > 0) kt = key_threshold(bk, n_band, take, h256, s_red, &s_hi, &s_need, &s_done);
-        // winners in band order (ascending index), ties: the first kt.nd_t
-        const uint32_t per = (n_band + kRowThreads - 1) / kRowThreads;
-        const uint32_t q0 = min(n_band, tid * per), q1 = min(n_band, q0 + per);
-        // class of band entry i: 1 a winner, 2 a tie at the threshold, 0 out
-        auto cls = [&](uint32_t i) -> uint32_t {
-          if (!by_thr) return 1u;
-          if (take == 0) return 0u;
-          const uint64_t kh = bk[i];
-          if (kh > kt.thr || (kt.incl && kh == kt.thr)) return 1u;
-          return kh == kt.thr ? 2u : 0u;
-        };
-        uint32_t nwin = 0, ntie = 0;
-        for (uint32_t i = q0; i < q1; ++i) {
-          const uint32_t c = cls(i);
-          nwin += c == 1u;
-          ntie += c == 2u;
+          band_lo = max(0, (bstar << kVBinShift) - E);
+          band_hi = min(65535, (bstar << kVBinShift) + 127 + E);
         }
-        uint32_t o_tie, o_dummy;
-        reserve_two(ntie, 0u, nullptr, nullptr, s_cnt, s_base, o_tie, o_dummy);
-        uint32_t keep_tie = 0;
-        for (uint32_t i = q0, ot = o_tie; i < q1; ++i)
-          if (cls(i) == 2u) keep_tie += (ot++ < kt.nd_t);
-        uint32_t o_w;
-        reserve_two(nwin + keep_tie, 0u, nullptr, nullptr, s_cnt, s_base, o_w, o_dummy);
-        n_w = s_base[2];
-        for (uint32_t i = q0, ot = o_tie; i < q1; ++i) {
-          const uint32_t c = cls(i);
-          bool a = c == 1u;
-          if (c == 2u) a = (ot++ < kt.nd_t);
-          if (a) {
-            if (o_w < static_cast<uint32_t>(kMaxSel)) bw[o_w] = bi[i];
-            ++o_w;
+        int32_t* gbi = band_idx + static_cast<size_t>(r) * band_cap;
+        uint64_t* gbk = band_key + static_cast<size_t>(r) * band_cap;
+        bool band_lds = false, band_glob = false;
+        int32_t* bi = gbi;
+        uint64_t* bk = gbk;
+        uint32_t cu = 0, ca = 0;
+        if (listed) {
+          // ---- split the list: each thread takes kPListPer consecutive
+          // entries into registers, so the band may overwrite the list
+          const uint32_t q0 = static_cast<uint32_t>(tid) * kPListPer;
+          int32_t li[kPListPer];
+          uint32_t mu = 0, ma = 0;
+#pragma unroll
+          for (int j = 0; j < kPListPer; ++j) {
+            const uint32_t i = q0 + j;
+            li[j] = 0;
+            if (i < n_list) {
+              li[j] = lidx[i];
+              const int v = lval[i];
+              mu |= static_cast<uint32_t>(v > band_hi) << j;
+              ma |= static_cast<uint32_t>(v >= band_lo && v <= band_hi) << j;
+            }
+          }
+          uint32_t ou, oa;
+          block_offsets2<kRowThreads / 64>(__popc(mu), __popc(ma), s_off[0], ou, oa, cu, ca);
+          band_lds = ca <= static_cast<uint32_t>(kUncCap);
+          band_glob = !band_lds && ca <= static_cast<uint64_t>(band_cap);
+          bi = band_lds ? lbi : gbi;
+          bk = band_lds ? lbk : gbk;
+#pragma unroll
+          for (int j = 0; j < kPListPer; ++j) {
+            if ((mu >> j) & 1u) {
+              if (ou < static_cast<uint32_t>(kMaxSel)) up[ou] = li[j];
+              ++ou;
+            }
+            if ((ma >> j) & 1u) {
+              if (band_lds || band_glob) bi[oa] = li[j];
+              ++oa;
+            }
+          }
+        } else {
+          // ---- the list overflowed: a second pass over v, in key order; the
+          // band goes to the global list (up to band_cap entries)
+          u32x4 ycur[2], ynxt[2];
+          if (rounds > 0) load_round(0, ycur);
+          for (int64_t rr = 0; rr < rounds; ++rr) {
+            const int64_t i0 = 16 * (static_cast<int64_t>(tid) + rr * kRowThreads);
+            if (rr + 1 < rounds) load_round(rr + 1, ynxt);
+            const int nv = static_cast<int>(min(static_cast<int64_t>(16), first - i0));
+            uint32_t mu = 0, ma = 0;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int v = static_cast<int>(u16_at(ycur, e));
+              mu |= static_cast<uint32_t>(e < nv && v > band_hi) << e;
+              ma |= static_cast<uint32_t>(e < nv && v >= band_lo && v <= band_hi) << e;
+            }
+            uint32_t ou, oa;
+            reserve_two(__popc(mu), __popc(ma), nullptr, nullptr, s_cnt, s_base, ou, oa);
+            ou += cu;
+            oa += ca;
+            cu += s_base[2];
+            ca += s_base[3];
+            for (uint32_t m = mu; m; m &= m - 1) {
+              if (ou < static_cast<uint32_t>(kMaxSel)) up[ou] = static_cast<int32_t>(i0 + __builtin_ctz(m));
+              ++ou;
+            }
+            for (uint32_t m = ma; m; m &= m - 1) {
+              if (oa < static_cast<uint64_t>(band_cap)) gbi[oa] = static_cast<int32_t>(i0 + __builtin_ctz(m));
+              ++oa;
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) ycur[u] = ynxt[u];
+          }
+          band_glob = ca <= static_cast<uint64_t>(band_cap);
+        }
+        __syncthreads();
+        const uint32_t n_up = min(cu, static_cast<uint32_t>(topk));
+        const uint32_t take = static_cast<uint32_t>(topk) - n_up;
+        uint32_t n_w = 0;
+        if (band_lds || band_glob) {
+          const uint32_t n_band = min(ca, band_lds ? static_cast<uint32_t>(kUncCap)
+                                                   : static_cast<uint32_t>(band_cap));
+          // ---- exact importance of the band keys
+          for (uint32_t i = static_cast<uint32_t>(tid) >> 4; i < n_band; i += kRowThreads / 16) {
+            const double yy = exact_importance(bi[i], tid & 15);
+            if ((tid & 15) == 0) bk[i] = ordered_u64(yy);
+          }
+          __syncthreads();
+          n_w = rank_band(bk, bi, n_band, take, bw, kMaxSel, &s_count, h256, s_red, &s_hi,
+                          &s_need, &s_done, s_cnt, s_base);
+        } else if (take > 0) {
+          // the band is too large to list: rank it by its stored importance
+          // (unordered winners, then sorted)
+          struct ScanSrc {
+            const u16* yr;
+            int lo, hi;
+            __device__ bool get(int64_t i, uint64_t& key, int32_t& j) const {
+              const int v = yr[i];
+              if (v < lo || v > hi) return false;
+              key = static_cast<uint64_t>(v);
+              j = static_cast<int32_t>(i);
+              return true;
+            }
+          } src{yr, band_lo, band_hi};
+          if (tid == 0) s_count = 0u;
+          __syncthreads();
+          radix_select_band(src, first, min(take, ca), bw, &s_count, h256, &s_thi, &s_tlo, &s_need);
+          n_w = min(s_count, static_cast<uint32_t>(kMaxSel));
+          int32_t v[kMaxSel / kRowThreads];
+#pragma unroll
+          for (int e = 0; e < kMaxSel / kRowThreads; ++e) {
+            const uint32_t ii = (kMaxSel / kRowThreads) * tid + e;
+            v[e] = ii < n_w ? bw[ii] : 0x7FFFFFFF;
+          }
+          __syncthreads();
+          block_bitonic<kMaxSel / kRowThreads>(v, bw, static_cast<int>(n_w), IntLess{});
+#pragma unroll
+          for (int e = 0; e < kMaxSel / kRowThreads; ++e) {
+            const uint32_t ii = (kMaxSel / kRowThreads) * tid + e;
+            if (ii < n_w) bw[ii] = v[e];
           }
         }
-        }
-      } else if (take > 0) {
-        // the band is too large to list: rank it by its stored importance
-        // (unordered winners, then sorted)
-        struct ScanSrc {
-          const u16* yr;
-          int lo, hi;
-          __device__ bool get(int64_t i, uint64_t& key, int32_t& j) const {
-            const int v = yr[i];
-            if (v < lo || v > hi) return false;
-            key = static_cast<uint64_t>(v);
-            j = static_cast<int32_t>(i);
-            return true;
-          }
-        } src{yr, band_lo, band_hi};
-        if (tid == 0) s_count = 0u;
         __syncthreads();
-        radix_select_band(src, first, min(take, ca), bw, &s_count, h256, &s_thi, &s_tlo, &s_need);
-        n_w = min(s_count, static_cast<uint32_t>(kMaxSel));
-        int32_t v[kMaxSel / kRowThreads];
-#pragma unroll
-        for (int e = 0; e < kMaxSel / kRowThreads; ++e) {
-          const uint32_t ii = (kMaxSel / kRowThreads) * tid + e;
-          v[e] = ii < n_w ? bw[ii] : 0x7FFFFFFF;
+        // ---- merge the two ascending lists by rank
+        for (uint32_t i = tid; i < n_up; i += kRowThreads) {
+          const int32_t v = up[i];
+          const uint32_t rk = i + lower_bound_lds(bw, n_w, v);
+          if (rk < static_cast<uint32_t>(cap)) out[rk] = v;
         }
-        __syncthreads();
-        block_bitonic<kMaxSel / kRowThreads>(v, bw, static_cast<int>(n_w), IntLess{});
-#pragma unroll
-        for (int e = 0; e < kMaxSel / kRowThreads; ++e) {
-          const uint32_t ii = (kMaxSel / kRowThreads) * tid + e;
-          if (ii < n_w) bw[ii] = v[e];
+        for (uint32_t i = tid; i < n_w; i += kRowThreads) {
+          const int32_t v = bw[i];
+          const uint32_t rk = i + lower_bound_lds(up, n_up, v);
+          if (rk < static_cast<uint32_t>(cap)) out[rk] = v;
         }
+        n_keep = min(n_up + n_w, static_cast<uint32_t>(topk));
       }
-      __syncthreads();
-      // ---- merge the two ascending lists by rank
-      for (uint32_t i = tid; i < n_up; i += kRowThreads) {
-        const int32_t v = up[i];
-        const uint32_t rk = i + lower_bound_lds(bw, n_w, v);
-        if (rk < static_cast<uint32_t>(cap)) out[rk] = v;
-      }
-      for (uint32_t i = tid; i < n_w; i += kRowThreads) {
-        const int32_t v = bw[i];
-        const uint32_t rk = i + lower_bound_lds(up, n_up, v);
-        if (rk < static_cast<uint32_t>(cap)) out[rk] = v;
-      }
-      n_keep = min(n_up + n_w, static_cast<uint32_t>(topk));
     }
   } else {
     __syncthreads();
@@ -2262,13 +2491,10 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
 // last one ending at first), a block's importance is the largest importance of
 // its tokens, and the top_k / bs best blocks are kept, ties to the lower block
 // index; the window is forced as in the token-level selection.  Both kernels
-// below (fused, from the candidate lists, and from given scores) fill one
-// 64-bit key per block in LDS (0 = no key: below every real key), take the
-// threshold with the radix select of the token path, and emit.
-
-constexpr int kMaxBlocks = 16384;   // blocks per row held in LDS
-
-constexpr int kMaxSelBlocks = 256;  // top_k / block <= 4096 / 16
+// below (the fused decode step, from the candidate lists, and from given
+// scores) fill one 64-bit key per block in LDS (0 = no key: below every real
+// key), take the threshold with the radix select of the token path, and emit.
+// A prefill chunk selects blocks in prefill_select_kernel<true>.
 
 // Select from the block keys (LDS, one per block, 0 = no key) and write the
 // row: the selected blocks' tokens in ascending order, the window, -1 padding,
@@ -2557,10 +2783,8 @@ hipError_t launch_subtile_cand(const Plan& p, void* ws, hipStream_t st) {
 hipError_t launch_fused_select(const Plan& p, const u16* q, const u16* k, int32_t* idx,
                                int32_t* n_sel, float* lse, void* ws, hipStream_t st) {
   char* w = static_cast<char*>(ws);
-  const float* stmax = reinterpret_cast<const float*>(w + p.off_stmax);
   const double* lse2 = reinterpret_cast<const double*>(w + p.off_lse2);
   const float* ytop = reinterpret_cast<const float*>(w + p.off_ytop);
-  uint32_t* hist = reinterpret_cast<uint32_t*>(w + p.off_hist);
   uint32_t* hist_c = reinterpret_cast<uint32_t*>(w + p.off_hist_c);
   double* cand_y = reinterpret_cast<double*>(w + p.off_cand_y);
   int32_t* cand_idx = reinterpret_cast<int32_t*>(w + p.off_cand_idx);
@@ -2599,7 +2823,8 @@ hipError_t launch_prefill_select(const Plan& p, const u16* q, const u16* k, int3
   char* w = static_cast<char*>(ws);
   const double c2 = p.scale * 1.4426950408889634;
   const float c2_hi = static_cast<float>(c2);
-  hipLaunchKernelGGL(prefill_select_kernel, dim3(p.R), dim3(kRowThreads), 0, st,
+  auto kern = p.bs > 0 ? prefill_select_kernel<true> : prefill_select_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3(p.R), dim3(kRowThreads), 0, st,
                      reinterpret_cast<const u16*>(w + p.off_ybuf),
                      reinterpret_cast<const uint32_t*>(w + p.off_kmax),
                      (p.T + kImportanceTok - 1) / kImportanceTok,
@@ -2610,7 +2835,7 @@ hipError_t launch_prefill_select(const Plan& p, const u16* q, const u16* k, int3
                      reinterpret_cast<RefineStat*>(w + p.off_ref_stat), q, k,
                      reinterpret_cast<int32_t*>(w + p.off_band_idx),
                      reinterpret_cast<uint64_t*>(w + p.off_band_key), p.band_cap, idx, n_sel, p.S,
-                     p.Spad, p.T, p.Hkv, p.k, p.w, p.cap, c2, c2_hi, p.kvp);
+                     p.Spad, p.T, p.Hkv, p.k, p.w, p.cap, p.bs, c2, c2_hi, p.kvp);
   return hipGetLastError();
 }
 

@@ -154,17 +154,19 @@ def test_decode_split_override_changes_the_plan():
         hs2.workspace_bytes(chunk, 0)
 
 
-def test_timed_step_rejects_block_selection_on_a_chunk():
-    """Block-level selection inside a prefill chunk's fused step is refused by
-    the timed entry point exactly as by the step itself."""
-    lib = hs2.raw()
-    c = good().c()
-    c.select_block = 16
-    c.n_q_tokens = 4
-    ms = (ctypes.c_float * 4)()
-    st = lib.hs2_cross_decoder_step_timed(ctypes.byref(c), 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                                          FAKE, FAKE, FAKE, 1 << 40, None, 1, ms)
-    assert st == hs2.HS2_ERR_UNSUPPORTED
+def test_block_selection_on_a_chunk_lists_a_band_entry_per_block():
+    """Block selection in a prefill chunk ranks any band of blocks exactly: the
+    per-row band list (a 32-bit index and a 64-bit key per entry) grows to one
+    entry per block where that exceeds the token path's 8192."""
+    tok = dataclasses.replace(good(), n_q_tokens=4, ctx_len=200000, top_k=1024, window=128)
+    rows = tok.batch * 4 * tok.n_kv_heads
+    extra = rows * (200000 // 16 - 8192) * 12
+    d = hs2.workspace_bytes(dataclasses.replace(tok, select_block=16), 0) - \
+        hs2.workspace_bytes(tok, 0)
+    assert extra <= d < extra + 4096
+    # blocks of 128: 1563 blocks, within the token path's list
+    assert hs2.workspace_bytes(dataclasses.replace(tok, select_block=128), 0) == \
+        hs2.workspace_bytes(tok, 0)
 
 
 def test_status_strings():
@@ -231,12 +233,6 @@ def test_block_selection_limits():
     assert lib.hs2_workspace_bytes(ctypes.byref(c), 2) > 0
     c.ctx_len = 16384 * 32 + 1               # more than 16384 blocks
     assert lib.hs2_workspace_bytes(ctypes.byref(c), 2) == 0
-    c = good().c()
-    c.select_block = 16
-    c.n_q_tokens = 4                         # the fused step: decode only
-    st = lib.hs2_cross_decoder_step(ctypes.byref(c), 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                                    FAKE, None, None, FAKE, 1 << 40, None)
-    assert st == hs2.HS2_ERR_UNSUPPORTED
 
 
 def test_static_step_rejects_shapes_beyond_its_scratch():
