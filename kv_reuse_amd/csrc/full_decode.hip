@@ -28,6 +28,10 @@
 //    bytes of K/V).  Once lse is known this bounds every key's importance from
 //    above, and the bound is attained by one of the subtile's own keys; the
 //    selection uses that to find the few subtiles that can hold selected keys.
+//    Beside it, for each 4-key quad of the subtile, how far the quad's own
+//    maximum lies below (one byte per quad and head, rounded down, so the
+//    subtile maximum minus it still bounds the quad): the selection re-reads
+//    only the quads that can reach its threshold.
 //    (Writing all logits, 32 bytes per key row, cost about 45% of the kernel's
 //    time on MI355X: the write stream slows the 2 GiB read stream far more than
 //    its byte count.)
@@ -101,9 +105,17 @@ __device__ __forceinline__ void tile_logits(const bf16x8 (&ka)[2][4], const bf16
     }
 }
 
+// The quad's distance below its subtile's maximum in 1/kQuadSteps octave
+// steps, rounded down (so never more than the true distance), 255 at most.
+__device__ __forceinline__ uint32_t quad_steps(float sub_max, float quad_max) {
+  const float d = (sub_max - quad_max) * static_cast<float>(kQuadSteps);
+  return static_cast<uint32_t>(__builtin_amdgcn_fmed3f(d, 0.f, 255.f));
+}
+
 __device__ __forceinline__ void process_tile(const KVTile& t, SoftmaxState& st,
                                              const bf16x8 (&qb)[4], u16* __restrict__ vw,
-                                             float* __restrict__ stmax_row, int64_t st_base,
+                                             float* __restrict__ stmax_row,
+                                             unsigned char* __restrict__ qd_row, int64_t st_base,
                                              int64_t t0, int64_t key_end, int col, int grp,
                                              float c2_hi, float c2_lo) {
   float sv[8];
@@ -124,6 +136,20 @@ __device__ __forceinline__ void process_tile(const KVTile& t, SoftmaxState& st,
   // (then indexed from the split's first subtile)
   if (col < kG && grp < 2 && t0 + 16 * grp < key_end)
     stmax_row[(t0 / 16 + grp - st_base) * kG + col] = mx;   // row grp: subtile grp
+  // m0 and m1 are quad grp's maxima in subtiles 0 and 1; a row swap of mx
+  // gives every lane both subtiles' maxima (rows 0 and 2 hold subtile 0's)
+  {
+    const auto sm = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                     false, false);
+    if (col < kG) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        if (t0 + 16 * mt < key_end)
+          qd_row[(t0 / 16 + mt - st_base) * (4 * kG) + grp * kG + col] = static_cast<unsigned char>(
+              quad_steps(__uint_as_float(sm[mt]), mt == 0 ? m0 : m1));
+      }
+    }
+  }
   // ---- online softmax (per head = per lane % 16); the tile's maximum joins
   // the two subtiles' (rows 0|1 and 2|3)
   const float tm = max_xor16(mx);
@@ -159,17 +185,19 @@ __device__ __forceinline__ void load_q_operand(const u16* __restrict__ qr, int c
                      : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
 }
 
-// kStaged: the split is at most kStageKeys keys and its subtile maxima go to
-// LDS first.  A template parameter rather than a run-time choice, so that the
-// maxima's stores are LDS stores: a vector-memory store among the stream's
-// loads makes the compiler wait for every load in flight (the counter no
-// longer drains in order), which serialises the prefetch with the tile.
+// kStaged: the split is at most kStageKeys keys and its subtile maxima and
+// quad distances go to LDS first.  A template parameter rather than a run-time
+// choice, so that their stores are LDS stores: a vector-memory store among the
+// stream's loads makes the compiler wait for every load in flight (the counter
+// no longer drains in order), which serialises the prefetch with the tile.
+// The staged form holds about 100 KB of LDS, one work-group per CU (the plan
+// launches one per CU).
 template <bool kStaged>
-__global__ __launch_bounds__(kWaves * 64, 2) void full_decode_split_kernel(
+__global__ __launch_bounds__(kWaves * 64, kStaged ? 1 : 2) void full_decode_split_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
-    float* __restrict__ stmax, float* __restrict__ part_m, double* __restrict__ part_l,
-    float* __restrict__ part_o, int64_t S, int64_t Spad, int kps, int n_split, float c2_hi,
-    float c2_lo, int64_t kvp) {
+    float* __restrict__ stmax, unsigned char* __restrict__ qdiff, float* __restrict__ part_m,
+    double* __restrict__ part_l, float* __restrict__ part_o, int64_t S, int64_t Spad, int kps,
+    int n_split, float c2_hi, float c2_lo, int64_t kvp) {
   // V tiles during the stream; reused for the cross-wave merge afterwards
   __shared__ __align__(16) unsigned char smem[kWaves * kTile * kVPitch * 2];
   __shared__ float sm_m[kWaves][kG];
@@ -177,6 +205,7 @@ __global__ __launch_bounds__(kWaves * 64, 2) void full_decode_split_kernel(
   // the split's subtile maxima, written to HBM in one burst at the end (when
   // the split is at most kStageKeys keys)
   __shared__ __align__(16) float st_stage[kStageKeys / 16 * kG];
+  __shared__ __align__(16) unsigned char qd_stage[kStageKeys / 16 * 4 * kG];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -191,6 +220,8 @@ __global__ __launch_bounds__(kWaves * 64, 2) void full_decode_split_kernel(
   float* stmax_row = stmax + static_cast<size_t>(r) * (Spad / 16) * kG;
   constexpr bool staged = kStaged;
   float* st_dst = staged ? st_stage : stmax_row;
+  unsigned char* qd_row = qdiff + static_cast<size_t>(r) * (Spad / 16) * (4 * kG);
+  unsigned char* qd_dst = staged ? qd_stage : qd_row;
   const int64_t st_base = staged ? key_begin / 16 : 0;
   u16* vw = reinterpret_cast<u16*>(smem) + wave * kTile * kVPitch;
 
@@ -218,13 +249,13 @@ __global__ __launch_bounds__(kWaves * 64, 2) void full_decode_split_kernel(
       int64_t t1 = t0 + stride;
       bool more = t1 < key_end;
       load_tile(tb, kr, vr, t1, key_last, col, grp);
-      process_tile(ta, st, qb, vw, st_dst, st_base, t0, key_end, col, grp, c2_hi, c2_lo);
+      process_tile(ta, st, qb, vw, st_dst, qd_dst, st_base, t0, key_end, col, grp, c2_hi, c2_lo);
       if (!more) break;
       t0 = t1;
       t1 = t0 + stride;
       more = t1 < key_end;
       load_tile(ta, kr, vr, t1, key_last, col, grp);
-      process_tile(tb, st, qb, vw, st_dst, st_base, t0, key_end, col, grp, c2_hi, c2_lo);
+      process_tile(tb, st, qb, vw, st_dst, qd_dst, st_base, t0, key_end, col, grp, c2_hi, c2_lo);
       if (!more) break;
       t0 = t1;
     }
@@ -238,6 +269,11 @@ __global__ __launch_bounds__(kWaves * 64, 2) void full_decode_split_kernel(
     float* dst = stmax_row + (key_begin / 16) * kG;
     for (int i = threadIdx.x; i < n4; i += blockDim.x)
       *reinterpret_cast<f32x4*>(dst + 4 * i) = *reinterpret_cast<const f32x4*>(st_stage + 4 * i);
+    // and their quads' distances: 32 bytes per subtile
+    const int n16 = static_cast<int>((key_end - key_begin + 15) / 16) * 2;
+    unsigned char* qdst = qd_row + (key_begin / 16) * (4 * kG);
+    for (int i = threadIdx.x; i < n16; i += blockDim.x)
+      *reinterpret_cast<u32x4*>(qdst + 16 * i) = *reinterpret_cast<const u32x4*>(qd_stage + 16 * i);
   }
   float* sm_o = reinterpret_cast<float*>(smem);  // [kWaves][kG][kD]
   if (col < kG) {
@@ -706,6 +742,7 @@ hipError_t launch_full_decode_split(const Plan& p, const u16* q, const u16* k, c
   auto kern = p.kps <= kStageKeys ? full_decode_split_kernel<true> : full_decode_split_kernel<false>;
   hipLaunchKernelGGL(kern, grid, dim3(kWaves * 64), 0, st, q, k, v,
                      reinterpret_cast<float*>(w + p.off_stmax),
+                     reinterpret_cast<unsigned char*>(w + p.off_qdiff),
                      reinterpret_cast<float*>(w + p.off_part_m),
                      reinterpret_cast<double*>(w + p.off_part_l),
                      reinterpret_cast<float*>(w + p.off_part_o), p.S, p.Spad, p.kps, p.n_split,

@@ -32,6 +32,11 @@ constexpr float kDomLog2 = -8.0f;
 // of subtiles allows (the heaviest first).
 constexpr float kDomFloorLog2 = -14.0f;
 constexpr int kDomCap = 2304;      // dominant keys listed per prefill row
+// Decode: for each subtile of 16 keys, each of its four 4-key quads and each
+// head, how far the quad's largest base-2 logit lies below the subtile's, in
+// steps of 1/kQuadSteps octave rounded down (255: that far or farther), one
+// byte each, 32 bytes per subtile ([quad][head]).
+constexpr int kQuadSteps = 16;
 // A prefill chunk's selection bands its stored importance allowing for a
 // refinement of lse2 of up to this many octaves (the change is checked).
 constexpr double kDl2Allow = 0x1p-12;
@@ -79,7 +84,7 @@ struct Plan {
   double scale;
   // full attention (decode split kernel) and the merge of its splits
   int n_split, kps;
-  size_t off_part_m, off_part_l, off_part_o, off_stmax, off_lse2, off_ytop;
+  size_t off_part_m, off_part_l, off_part_o, off_stmax, off_qdiff, off_lse2, off_ytop;
   // selection state shared by both selection paths
   size_t off_hist, off_info;
   // selection from given scores
@@ -128,7 +133,8 @@ int record_hip_error(hipError_t e);
 // Each returns the hipError_t of its launches (hipGetLastError()).
 
 // Full attention, decode (T == 1): split-context flash-decode writing per-split
-// partial (m, l, O) and per-subtile (16 keys) maxima of every head's logits.
+// partial (m, l, O), per-subtile (16 keys) maxima of every head's logits and
+// each quad's distance below them.
 hipError_t launch_full_decode_split(const Plan& p, const u16* q, const u16* k, const u16* v,
                                     void* ws, hipStream_t st);
 // Merge the splits: out (bf16), lse (nullable), lse2 (fp64, base 2) and each

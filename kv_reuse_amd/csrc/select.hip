@@ -725,8 +725,18 @@ __global__ __launch_bounds__(kThreads) void subtile_hist_kernel(
 // row's lower bin for the next kernel.  The same pass lists, in dlist / dcnt,
 // the subtiles whose bound reaches the refinement's cut (refine_cut_wave): the
 // ones the refinement of lse2 sums again.
+// A list entry is the subtile's index with, in bits kQuadShift.., the mask of
+// its quads (4 keys each) whose own bound (the subtile's maximum of head h
+// less the quad's stored distance below it) reaches the bottom of the bin
+// below the lower bin for some head: the only quads whose keys the scoring
+// kernel's float32 filter can pass.  The stored distances are rounded down,
+// so these bounds are never below the quads' maxima (the subtraction's
+// rounding aside, far inside the filter's one-bin margin).
+constexpr int kQuadShift = 27;   // subtile indices are below 2^31 / 16
+constexpr int32_t kSubMask = (1 << kQuadShift) - 1;
 __global__ __launch_bounds__(kThreads) void subtile_cand_kernel(
-    const float* __restrict__ stmax, const double* __restrict__ lse2,
+    const float* __restrict__ stmax, const unsigned char* __restrict__ qdiff,
+    const double* __restrict__ lse2,
     const float* __restrict__ ytop_h, const uint32_t* __restrict__ hist,
     int32_t* __restrict__ clist, uint32_t* __restrict__ ccnt, int32_t* __restrict__ lo_out,
     int32_t* __restrict__ dlist, uint32_t* __restrict__ dcnt, float* __restrict__ cut_out,
@@ -765,13 +775,19 @@ __global__ __launch_bounds__(kThreads) void subtile_cand_kernel(
 #pragma unroll
   for (int u = 0; u < kNB / kThreads; ++u)
     hv[u] = hist[static_cast<size_t>(r) * kNB + tid + kThreads * u];
+  const unsigned char* qd_row = qdiff + static_cast<size_t>(r) * (Spad / kSubKeys) * (4 * kG);
   f32x4 mx[2];
-  {
-    const int64_t st = st0 + tid;
+  u32x4 qd[2];   // quad q, head h: byte h % 4 of word 2 q + h / 4
+  auto load_round = [&](int64_t st) {
     const bool ld = st < st1;
     mx[0] = ld ? *reinterpret_cast<const f32x4*>(stmax_row + st * kG) : f32x4{0.f, 0.f, 0.f, 0.f};
     mx[1] = ld ? *reinterpret_cast<const f32x4*>(stmax_row + st * kG + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+      qd[u] = ld ? *reinterpret_cast<const u32x4*>(qd_row + st * (4 * kG) + 16 * u)
+                 : u32x4{0u, 0u, 0u, 0u};
+  };
+  load_round(st0 + tid);
   if (tid < kG) lse2f[tid] = static_cast<float>(lse2[static_cast<size_t>(r) * kG + tid]);
   if (tid == 0) s_ybase = row_ybase(ytop_h, r);
 #pragma unroll
@@ -800,14 +816,15 @@ __global__ __launch_bounds__(kThreads) void subtile_cand_kernel(
   int32_t* out = clist + (static_cast<size_t>(r) * n_chunks + blockIdx.x) * chunk;
   int32_t* dout = dlist + (static_cast<size_t>(r) * n_chunks + blockIdx.x) * chunk;
   uint32_t written = 0, dwritten = 0;
+  // a quad may hold a key the filter passes when, for some head, its bound
+  // less lse2 reaches the bottom of the bin below lo_bin
+  const float qthr = lo_bin - 1 <= 0 ? -INFINITY
+                                     : ybase + static_cast<float>(lo_bin - 1) * (kYRange / kNB);
   for (int64_t sr0 = st0; sr0 < st1; sr0 += kThreads) {
     const int64_t st = sr0 + tid;
-    if (sr0 != st0) {
-      const bool ld = st < st1;
-      mx[0] = ld ? *reinterpret_cast<const f32x4*>(stmax_row + st * kG) : f32x4{0.f, 0.f, 0.f, 0.f};
-      mx[1] = ld ? *reinterpret_cast<const f32x4*>(stmax_row + st * kG + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    if (sr0 != st0) load_round(st);
     bool cand = false, dom = false;
+    uint32_t qmask = 0xFu;
     if (st < st1) {
       float ub = mx[0][0] - l2v[0];
       ub = fmaxf(ub, mx[0][1] - l2v[1]);
@@ -820,10 +837,26 @@ __global__ __launch_bounds__(kThreads) void subtile_cand_kernel(
       cand = all_mode || st >= n_counted ||
              static_cast<int>(key_from_log2(ub, ybase) >> kBinShift) >= lo_bin;
       dom = ub >= cut;
+      if (cand && !all_mode && st < n_counted) {
+        qmask = 0u;
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          float qb = -INFINITY;
+#pragma unroll
+          for (int h = 0; h < kG; ++h) {
+            const uint32_t word = qd[qq >> 1][2 * (qq & 1) + (h >> 2)];
+            const float dq = static_cast<float>((word >> (8 * (h & 3))) & 0xFFu) *
+                             (1.f / static_cast<float>(kQuadSteps));
+            qb = fmaxf(qb, (mx[h >> 2][h & 3] - dq) - l2v[h]);
+          }
+          qmask |= static_cast<uint32_t>(qb >= qthr) << qq;
+        }
+      }
     }
     uint32_t o_list, o_dom;
     reserve_two(cand ? 1u : 0u, dom ? 1u : 0u, nullptr, nullptr, s_cnt, s_base, o_list, o_dom);
-    if (cand) out[written + o_list] = static_cast<int32_t>(st);   // ascending: thread order
+    if (cand)   // ascending: thread order
+      out[written + o_list] = static_cast<int32_t>(st | (static_cast<int64_t>(qmask) << kQuadShift));
     if (dom) dout[dwritten + o_dom] = static_cast<int32_t>(st);
     written += s_base[2];
     dwritten += s_base[3];
@@ -999,16 +1032,19 @@ __global__ __launch_bounds__(kThreads, 3) void subtile_score_kernel(
     for (uint32_t p0 = 0; p0 < n_local; p0 += kStageSub) {
       const uint32_t np = min(static_cast<uint32_t>(kStageSub), n_local - p0);
       // ---- float64 importance of the pass's candidates, one subtile per wave
-      // subtile st's K rows (uniform base, fixed lane offsets); a subtile that
-      // runs past the cache's rows reads the last row instead
-      auto load_sub = [&](int32_t st, u32x4 (&ka)[4]) {
-        const int64_t key0 = static_cast<int64_t>(st) * kSubKeys;
+      // list entry e: subtile e & kSubMask, its quad mask above kQuadShift.
+      // The subtile's K rows (uniform base, fixed lane offsets); a subtile that
+      // runs past the cache's rows reads the last row instead, and the lanes
+      // of a masked quad read the head's row 0 (one cached row for all)
+      auto load_sub = [&](int32_t e, u32x4 (&ka)[4]) {
+        const int64_t key0 = static_cast<int64_t>(e & kSubMask) * kSubKeys;
+        const bool use = ((static_cast<uint32_t>(e) >> (kQuadShift + (col >> 2))) & 1u) != 0u;
         if (key0 + kSubKeys <= kvp) {
-          const u16* base = kr + key0 * kD;
+          const u16* base = use ? kr + key0 * kD + lane_off : kr + 32 * grp;
 #pragma unroll
-          for (int c = 0; c < 4; ++c) ka[c] = load_u32x4(base + lane_off + 8 * c);
+          for (int c = 0; c < 4; ++c) ka[c] = load_u32x4(base + 8 * c);
         } else {
-          const int64_t key = min(key0 + col, kvp - 1);
+          const int64_t key = use ? min(key0 + col, kvp - 1) : 0;
 #pragma unroll
           for (int c = 0; c < 4; ++c) ka[c] = load_u32x4(kr + key * kD + 32 * grp + 8 * c);
         }
@@ -1023,8 +1059,8 @@ __global__ __launch_bounds__(kThreads, 3) void subtile_score_kernel(
       // buffer is copied, so each wait is for the oldest buffer only.
       constexpr uint32_t kW = kThreads / 64;
       // pass entry i (this wave's entries i = wave + kW t) is subtile st
-      auto score_sub = [&](uint32_t i, int32_t st, const u32x4 (&ka)[4]) {
-        const int64_t key0 = static_cast<int64_t>(st) * kSubKeys;
+      auto score_sub = [&](uint32_t i, int32_t e, const u32x4 (&ka)[4]) {
+        const int64_t key0 = static_cast<int64_t>(e & kSubMask) * kSubKeys;
         // ---- float32 logits of the 16 keys on the bf16 MFMA (Q . K^T, 16
         // heads of which 8 are used x 16 keys): lane (col, grp) gets heads
         // 4 grp + e against key col
@@ -1038,6 +1074,11 @@ __global__ __launch_bounds__(kThreads, 3) void subtile_score_kernel(
         const uint64_t hit = __ballot(sf[0] >= t4[0] || sf[1] >= t4[1] || sf[2] >= t4[2] ||
                                       sf[3] >= t4[3]);
         uint32_t promising = static_cast<uint32_t>(hit | (hit >> 16)) & 0xFFFFu;
+        // only the quads whose keys were loaded (the others cannot pass)
+        const uint32_t qm = static_cast<uint32_t>(e) >> kQuadShift;
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq)
+          if (!((qm >> qq) & 1u)) promising &= ~(0xFu << (4 * qq));
         // only keys before `first` are candidates
         const int64_t room = first - key0;
         if (room < kSubKeys) promising &= room <= 0 ? 0u : (1u << room) - 1u;
@@ -1124,7 +1165,7 @@ __global__ __launch_bounds__(kThreads, 3) void subtile_score_kernel(
       uint32_t keep = 0;
       int64_t key0 = 0;
       if (static_cast<uint32_t>(tid) < np) {
-        key0 = static_cast<int64_t>(s_list[p0 + tid]) * kSubKeys;
+        key0 = static_cast<int64_t>(s_list[p0 + tid] & kSubMask) * kSubKeys;
 #pragma unroll
         for (int e = 0; e < kSubKeys; ++e) {
           const double yy = stage_y[tid * kSubKeys + e];
@@ -2767,6 +2808,7 @@ hipError_t launch_subtile_cand(const Plan& p, void* ws, hipStream_t st) {
   char* w = static_cast<char*>(ws);
   hipLaunchKernelGGL(subtile_cand_kernel, dim3(p.cc_nchunk, p.R), dim3(kThreads), 0, st,
                      reinterpret_cast<const float*>(w + p.off_stmax),
+                     reinterpret_cast<const unsigned char*>(w + p.off_qdiff),
                      reinterpret_cast<const double*>(w + p.off_lse2),
                      reinterpret_cast<const float*>(w + p.off_ytop),
                      reinterpret_cast<const uint32_t*>(w + p.off_hist),
