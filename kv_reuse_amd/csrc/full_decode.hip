@@ -112,6 +112,7 @@ __device__ __forceinline__ uint32_t quad_steps(float sub_max, float quad_max) {
   return static_cast<uint32_t>(__builtin_amdgcn_fmed3f(d, 0.f, 255.f));
 }
 
+template <bool kQuads>
 __device__ __forceinline__ void process_tile(const KVTile& t, SoftmaxState& st,
                                              const bf16x8 (&qb)[4], u16* __restrict__ vw,
                                              float* __restrict__ stmax_row,
@@ -138,7 +139,7 @@ __device__ __forceinline__ void process_tile(const KVTile& t, SoftmaxState& st,
     stmax_row[(t0 / 16 + grp - st_base) * kG + col] = mx;   // row grp: subtile grp
   // m0 and m1 are quad grp's maxima in subtiles 0 and 1; a row swap of mx
   // gives every lane both subtiles' maxima (rows 0 and 2 hold subtile 0's)
-  {
+  if (kQuads) {
     const auto sm = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                      false, false);
     if (col < kG) {
@@ -190,10 +191,12 @@ __device__ __forceinline__ void load_q_operand(const u16* __restrict__ qr, int c
 // choice, so that their stores are LDS stores: a vector-memory store among the
 // stream's loads makes the compiler wait for every load in flight (the counter
 // no longer drains in order), which serialises the prefetch with the tile.
-// The staged form holds about 100 KB of LDS, one work-group per CU (the plan
-// launches one per CU).
-template <bool kStaged>
-__global__ __launch_bounds__(kWaves * 64, kStaged ? 1 : 2) void full_decode_split_kernel(
+// kQuads: the quads' distances are written too (the plan's choice: they pay
+// where the selection re-reads many subtiles, and their write stream costs
+// the full layer about 1% of its time).  The staged form with them holds
+// about 100 KB of LDS, one work-group per CU (the plan launches one per CU).
+template <bool kStaged, bool kQuads>
+__global__ __launch_bounds__(kWaves * 64, kStaged && kQuads ? 1 : 2) void full_decode_split_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const u16* __restrict__ v,
     float* __restrict__ stmax, unsigned char* __restrict__ qdiff, float* __restrict__ part_m,
     double* __restrict__ part_l, float* __restrict__ part_o, int64_t S, int64_t Spad, int kps,
@@ -205,7 +208,7 @@ __global__ __launch_bounds__(kWaves * 64, kStaged ? 1 : 2) void full_decode_spli
   // the split's subtile maxima, written to HBM in one burst at the end (when
   // the split is at most kStageKeys keys)
   __shared__ __align__(16) float st_stage[kStageKeys / 16 * kG];
-  __shared__ __align__(16) unsigned char qd_stage[kStageKeys / 16 * 4 * kG];
+  __shared__ __align__(16) unsigned char qd_stage[kQuads ? kStageKeys / 16 * 4 * kG : 16];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -249,13 +252,13 @@ __global__ __launch_bounds__(kWaves * 64, kStaged ? 1 : 2) void full_decode_spli
       int64_t t1 = t0 + stride;
       bool more = t1 < key_end;
       load_tile(tb, kr, vr, t1, key_last, col, grp);
-      process_tile(ta, st, qb, vw, st_dst, qd_dst, st_base, t0, key_end, col, grp, c2_hi, c2_lo);
+      process_tile<kQuads>(ta, st, qb, vw, st_dst, qd_dst, st_base, t0, key_end, col, grp, c2_hi, c2_lo);
       if (!more) break;
       t0 = t1;
       t1 = t0 + stride;
       more = t1 < key_end;
       load_tile(ta, kr, vr, t1, key_last, col, grp);
-      process_tile(tb, st, qb, vw, st_dst, qd_dst, st_base, t0, key_end, col, grp, c2_hi, c2_lo);
+      process_tile<kQuads>(tb, st, qb, vw, st_dst, qd_dst, st_base, t0, key_end, col, grp, c2_hi, c2_lo);
       if (!more) break;
       t0 = t1;
     }
@@ -270,10 +273,12 @@ __global__ __launch_bounds__(kWaves * 64, kStaged ? 1 : 2) void full_decode_spli
     for (int i = threadIdx.x; i < n4; i += blockDim.x)
       *reinterpret_cast<f32x4*>(dst + 4 * i) = *reinterpret_cast<const f32x4*>(st_stage + 4 * i);
     // and their quads' distances: 32 bytes per subtile
-    const int n16 = static_cast<int>((key_end - key_begin + 15) / 16) * 2;
-    unsigned char* qdst = qd_row + (key_begin / 16) * (4 * kG);
-    for (int i = threadIdx.x; i < n16; i += blockDim.x)
-      *reinterpret_cast<u32x4*>(qdst + 16 * i) = *reinterpret_cast<const u32x4*>(qd_stage + 16 * i);
+    if (kQuads) {
+      const int n16 = static_cast<int>((key_end - key_begin + 15) / 16) * 2;
+      unsigned char* qdst = qd_row + (key_begin / 16) * (4 * kG);
+      for (int i = threadIdx.x; i < n16; i += blockDim.x)
+        *reinterpret_cast<u32x4*>(qdst + 16 * i) = *reinterpret_cast<const u32x4*>(qd_stage + 16 * i);
+    }
   }
   float* sm_o = reinterpret_cast<float*>(smem);  // [kWaves][kG][kD]
   if (col < kG) {
@@ -739,10 +744,12 @@ hipError_t launch_full_decode_split(const Plan& p, const u16* q, const u16* k, c
   const float c2_hi = static_cast<float>(c2);
   const float c2_lo = static_cast<float>(c2 - static_cast<double>(c2_hi));
   dim3 grid(p.n_split, p.R);
-  auto kern = p.kps <= kStageKeys ? full_decode_split_kernel<true> : full_decode_split_kernel<false>;
+  const bool staged = p.kps <= kStageKeys;
+  auto kern = p.quads ? (staged ? full_decode_split_kernel<true, true> : full_decode_split_kernel<false, true>)
+                      : (staged ? full_decode_split_kernel<true, false> : full_decode_split_kernel<false, false>);
   hipLaunchKernelGGL(kern, grid, dim3(kWaves * 64), 0, st, q, k, v,
                      reinterpret_cast<float*>(w + p.off_stmax),
-                     reinterpret_cast<unsigned char*>(w + p.off_qdiff),
+                     p.quads ? reinterpret_cast<unsigned char*>(w + p.off_qdiff) : nullptr,
                      reinterpret_cast<float*>(w + p.off_part_m),
                      reinterpret_cast<double*>(w + p.off_part_l),
                      reinterpret_cast<float*>(w + p.off_part_o), p.S, p.Spad, p.kps, p.n_split,

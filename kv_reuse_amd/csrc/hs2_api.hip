@@ -157,7 +157,11 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
   q.off_part_l = take(decode ? nsplit_rows * kG * sizeof(double) : 0);
   q.off_part_o = take(decode ? nsplit_rows * kG * kD * sizeof(float) : 0);
   q.off_stmax = take(decode ? Rz * nst * kG * sizeof(float) : 0);
-  q.off_qdiff = take(decode ? Rz * nst * 4 * kG : 0);
+  // the quads' distances pay where the selection re-reads many subtiles: when
+  // top_k is at least 1/64 of the context (a subtile then holds a selected
+  // key with probability about 1/4 or more)
+  q.quads = decode && q.k > 0 && q.S <= int64_t{64} * q.k;
+  q.off_qdiff = take(q.quads ? Rz * nst * 4 * kG : 0);
   q.off_lse2 = take(Rz * kG * sizeof(double));
   q.off_ytop = take(Rz * kG * sizeof(float));
   q.off_hist = take(Rz * kNB * sizeof(uint32_t));

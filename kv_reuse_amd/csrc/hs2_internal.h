@@ -85,6 +85,7 @@ struct Plan {
   // full attention (decode split kernel) and the merge of its splits
   int n_split, kps;
   size_t off_part_m, off_part_l, off_part_o, off_stmax, off_qdiff, off_lse2, off_ytop;
+  bool quads;                // decode: the quads' distances are written and used
   // selection state shared by both selection paths
   size_t off_hist, off_info;
   // selection from given scores

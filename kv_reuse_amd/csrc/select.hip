@@ -726,7 +726,8 @@ __global__ __launch_bounds__(kThreads) void subtile_hist_kernel(
 // the subtiles whose bound reaches the refinement's cut (refine_cut_wave): the
 // ones the refinement of lse2 sums again.
 // A list entry is the subtile's index with, in bits kQuadShift.., the mask of
-// its quads (4 keys each) whose own bound (the subtile's maximum of head h
+// its quads (4 keys each; all four when the plan writes no quad distances)
+// whose own bound (the subtile's maximum of head h
 // less the quad's stored distance below it) reaches the bottom of the bin
 // below the lower bin for some head: the only quads whose keys the scoring
 // kernel's float32 filter can pass.  The stored distances are rounded down,
@@ -775,7 +776,9 @@ __global__ __launch_bounds__(kThreads) void subtile_cand_kernel(
 #pragma unroll
   for (int u = 0; u < kNB / kThreads; ++u)
     hv[u] = hist[static_cast<size_t>(r) * kNB + tid + kThreads * u];
-  const unsigned char* qd_row = qdiff + static_cast<size_t>(r) * (Spad / kSubKeys) * (4 * kG);
+  // no quad distances (qdiff null): every quad of a candidate is kept
+  const bool use_quads = qdiff != nullptr;
+  const unsigned char* qd_row = qdiff + (use_quads ? static_cast<size_t>(r) * (Spad / kSubKeys) * (4 * kG) : 0);
   f32x4 mx[2];
   u32x4 qd[2];   // quad q, head h: byte h % 4 of word 2 q + h / 4
   auto load_round = [&](int64_t st) {
@@ -784,8 +787,8 @@ __global__ __launch_bounds__(kThreads) void subtile_cand_kernel(
     mx[1] = ld ? *reinterpret_cast<const f32x4*>(stmax_row + st * kG + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < 2; ++u)
-      qd[u] = ld ? *reinterpret_cast<const u32x4*>(qd_row + st * (4 * kG) + 16 * u)
-                 : u32x4{0u, 0u, 0u, 0u};
+      qd[u] = ld && use_quads ? *reinterpret_cast<const u32x4*>(qd_row + st * (4 * kG) + 16 * u)
+                              : u32x4{0u, 0u, 0u, 0u};
   };
   load_round(st0 + tid);
   if (tid < kG) lse2f[tid] = static_cast<float>(lse2[static_cast<size_t>(r) * kG + tid]);
@@ -837,7 +840,7 @@ __global__ __launch_bounds__(kThreads) void subtile_cand_kernel(
       cand = all_mode || st >= n_counted ||
              static_cast<int>(key_from_log2(ub, ybase) >> kBinShift) >= lo_bin;
       dom = ub >= cut;
-      if (cand && !all_mode && st < n_counted) {
+      if (use_quads && cand && !all_mode && st < n_counted) {
         qmask = 0u;
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) {
@@ -2808,7 +2811,7 @@ hipError_t launch_subtile_cand(const Plan& p, void* ws, hipStream_t st) {
   char* w = static_cast<char*>(ws);
   hipLaunchKernelGGL(subtile_cand_kernel, dim3(p.cc_nchunk, p.R), dim3(kThreads), 0, st,
                      reinterpret_cast<const float*>(w + p.off_stmax),
-                     reinterpret_cast<const unsigned char*>(w + p.off_qdiff),
+                     p.quads ? reinterpret_cast<const unsigned char*>(w + p.off_qdiff) : nullptr,
                      reinterpret_cast<const double*>(w + p.off_lse2),
                      reinterpret_cast<const float*>(w + p.off_ytop),
                      reinterpret_cast<const uint32_t*>(w + p.off_hist),
