@@ -139,7 +139,8 @@ int hs2_topk_select(const hs2_shape* shape, const float* scores, int32_t* idx, i
  * over i in idx[b][t][g][0..n_sel).  q [N][B][T][Hq][D], out [N][B][T][Hq][D];
  * idx / n_sel as written by hs2_topk_select (entries must be in [0, P_t];
  * an entry outside [0, S) is clamped into it, so a malformed list gives wrong
- * numbers for its row but never an out-of-bounds read).
+ * numbers for its row but never an out-of-bounds read, and every entry
+ * outside [0, P_t] is counted in the workspace: HS2_WS_INDEX_CHECK).
  * Rows with n_sel = 0 get zero outputs.  News page, section
  * "两级KV共享：让模型少跑一半" (the sparse layers reuse the cache and the
  * selection). */
@@ -269,9 +270,17 @@ int hs2_kv_bridge(const hs2_bridge_shape* shape, const hs2_bf16* hidden, const h
  *                [2] prefill dominant keys beyond the per-row list capacity
  *                (not summed again; expected 0), [3] reserved.  Valid after
  *                hs2_cross_decoder_step (and, in decode, hs2_full_attn_scores).
+ *   HS2_WS_INDEX_CHECK uint32 [B*T*Hkv rows][n_parts]: the sparse layers' index
+ *                check.  Summed over a row's n_parts (bytes / (rows * 4)), the
+ *                number of the entries idx[row][0..n_sel) that lie outside
+ *                [0, P_t] (each is clamped into the cache and read there, never
+ *                out of bounds, so the row's outputs are then wrong); 0 for a
+ *                list the selection wrote.  Valid after a call that ran at least
+ *                one sparse layer (for the separate-window variant: of the
+ *                entries below the window).
  * Returns HS2_OK; HS2_ERR_INVALID_ARG for a null pointer or an unknown region;
  * the status of hs2_workspace_bytes' checks for an invalid shape. */
-enum { HS2_WS_LSE2 = 1, HS2_WS_REFINE = 2 };
+enum { HS2_WS_LSE2 = 1, HS2_WS_REFINE = 2, HS2_WS_INDEX_CHECK = 3 };
 int hs2_workspace_region(const hs2_shape* shape, int32_t n_sparse_layers, int32_t region,
                          size_t* offset, size_t* bytes);
 

@@ -202,6 +202,7 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
   q.off_sp_m = take(sp_parts * sizeof(float));
   q.off_sp_l = take(sp_parts * sizeof(float));
   q.off_sp_o = take(sp_parts * kD * sizeof(float));
+  q.off_idx_bad = take(Rz * q.sp_nch * sizeof(uint32_t));
   q.off_swa = take(Rz * static_cast<size_t>(n_layers) * kG * kD * sizeof(float));
   q.total = off;
   *p = q;
@@ -545,6 +546,10 @@ int hs2_workspace_region(const hs2_shape* shape, int32_t n_sparse_layers, int32_
     case HS2_WS_REFINE:
       *offset = p.off_ref_stat;
       *bytes = static_cast<size_t>(p.R) * sizeof(RefineStat);
+      return HS2_OK;
+    case HS2_WS_INDEX_CHECK:
+      *offset = p.off_idx_bad;
+      *bytes = static_cast<size_t>(p.R) * p.sp_nch * sizeof(uint32_t);
       return HS2_OK;
     default:
       return HS2_ERR_INVALID_ARG;

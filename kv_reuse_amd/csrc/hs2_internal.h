@@ -111,6 +111,7 @@ struct Plan {
   // sparse
   int sp_nch;
   size_t off_sp_m, off_sp_l, off_sp_o;
+  size_t off_idx_bad;        // the gather's index check: uint32 [R][sp_nch]
   size_t off_swa;            // the window branch's outputs [L][R][G][D] float32
   size_t total;
 };

@@ -44,10 +44,11 @@ __global__ __launch_bounds__(NCT * 64) void sparse_kernel(
     float* __restrict__ part_m, float* __restrict__ part_l, float* __restrict__ part_o,
     int64_t S, int T, int Hkv, int L, int layer0, int cap, int nch, int keys_per_wg,
     float c2_hi, float c2_lo, size_t layer_stride, int64_t kvp, int w_drop,
-    const float* __restrict__ swa_add) {
+    const float* __restrict__ swa_add, uint32_t* __restrict__ bad) {
   __shared__ __align__(16) u16 klds[kSub * kPitch];
   __shared__ __align__(16) u16 vlds[kSub * kPitch];
   __shared__ int32_t sidx[kSub];
+  __shared__ uint32_t s_bad;
 
   const int r = blockIdx.y;
   const int ch = blockIdx.x;
@@ -72,6 +73,11 @@ __global__ __launch_bounds__(NCT * 64) void sparse_kernel(
   }
   const int pos_begin = ch * keys_per_wg;
   const int pos_end = min(ns, pos_begin + keys_per_wg);
+  // the index check: entries this work-group reads that lie outside [0, P]
+  // (they are still clamped into the cache, never read out of bounds) are
+  // counted, and the count is written to bad[r][ch] whatever it is
+  const int64_t P_row = S - T + (r / Hkv) % T;
+  if (tid == 0) s_bad = 0u;
 
   const int layer = layer0 + 2 * wave + (col >> 3);  // this lane's column
   const int head = col & 7;
@@ -93,8 +99,11 @@ __global__ __launch_bounds__(NCT * 64) void sparse_kernel(
   for (int sc = pos_begin; sc < pos_end; sc += kSub) {
     const int n_here = min(kSub, pos_end - sc);
     __syncthreads();  // the previous sub-chunk is consumed
-    for (int i = tid; i < kSub; i += blockDim.x)
-      sidx[i] = i < n_here ? idx[static_cast<size_t>(r) * cap + sc + i] : -1;
+    for (int i = tid; i < kSub; i += blockDim.x) {
+      const int32_t j = i < n_here ? idx[static_cast<size_t>(r) * cap + sc + i] : -1;
+      sidx[i] = j;
+      if (i < n_here && (j < 0 || j > P_row)) atomicAdd(&s_bad, 1u);
+    }
     __syncthreads();
     // every thread's 16-byte pieces of the sub-chunk, 8 (K, V) pairs at a
     // time: all loads of a batch first, then its LDS stores, so a 256-thread
@@ -168,6 +177,8 @@ __global__ __launch_bounds__(NCT * 64) void sparse_kernel(
     }
   }
   l_run = sum_rows(l_run);
+  __syncthreads();   // (every count is in)
+  if (tid == 0) bad[static_cast<size_t>(r) * nch + ch] = s_bad;
   if (!col_ok) return;
   if (nch == 1) {
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
@@ -378,7 +389,8 @@ hipError_t launch_sparse(const Plan& p, const u16* q, const u16* k, const u16* v
     auto go = [&](auto kern) {
       hipLaunchKernelGGL(kern, grid, dim3(nct * 64), 0, st, q, k, v, idx, n_sel, out, pm, pl, po,
                          p.S, p.T, p.Hkv, p.n_layers, layer0, p.cap, p.sp_nch, keys_per_wg, c2_hi,
-                         c2_lo, layer_stride, p.kvp, swa ? p.w : -1, swa_out);
+                         c2_lo, layer_stride, p.kvp, swa ? p.w : -1, swa_out,
+                         reinterpret_cast<uint32_t*>(w + p.off_idx_bad));
     };
     if (p.sp_nch == 1) {
       switch (nct) {

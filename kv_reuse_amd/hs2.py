@@ -16,7 +16,9 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libhs2.so")
+# HS2_LIBRARY may name another build of the same library (the host-sanitizer
+# build of kv_reuse_amd.build --asan-host, for instance)
+LIB_PATH = os.environ.get("HS2_LIBRARY") or os.path.join(_HERE, "libhs2.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it first (python -m kv_reuse_amd.build "
@@ -183,6 +185,7 @@ def alloc_workspace(s: ShapeArgs, n_sparse_layers: int = 0, device="cuda") -> to
 
 HS2_WS_LSE2 = 1
 HS2_WS_REFINE = 2
+HS2_WS_INDEX_CHECK = 3
 
 
 def workspace_region(s: ShapeArgs, n_sparse_layers: int, region: int):
@@ -205,6 +208,13 @@ def workspace_refine_stats(s: ShapeArgs, n_sparse_layers: int, ws: torch.Tensor)
     int32): dominant units, float32 replica mismatches, list overflow, 0."""
     off, nb = workspace_region(s, n_sparse_layers, HS2_WS_REFINE)
     return ws[off:off + nb].view(torch.int32).view(s.rows, 4)
+
+
+def workspace_index_check(s: ShapeArgs, n_sparse_layers: int, ws: torch.Tensor) -> torch.Tensor:
+    """Per-row count [rows] (int64) of the index-list entries that the last
+    sparse layers found outside [0, P_t] (hs2_workspace_region, HS2_WS_INDEX_CHECK)."""
+    off, nb = workspace_region(s, n_sparse_layers, HS2_WS_INDEX_CHECK)
+    return ws[off:off + nb].view(torch.int32).view(s.rows, -1).to(torch.int64).sum(dim=1)
 
 
 def full_attn_scores(s: ShapeArgs, q, k, v, out, lse=None, scores=None, ws=None):

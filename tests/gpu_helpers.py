@@ -91,6 +91,7 @@ def run_step(w: wl.Workload, x, with_scores=True, with_lse=True, kv_capacity=0, 
            "refine": hs2.workspace_refine_stats(s, L, ws).cpu().numpy()}
     if L:
         res["out_sparse"] = host_f64(outs)
+        res["idx_bad"] = hs2.workspace_index_check(s, L, ws).cpu().numpy()
     if with_lse:
         res["lse"] = lse.cpu().numpy().astype(np.float64)
     if with_scores:
@@ -200,6 +201,9 @@ def compare_step(w: wl.Workload, x, res, check_scores=True, rows=None, block=0,
         assert np.all(res["refine"][:, 1] == 0), "float32 logit replica mismatch"
         assert np.all(res["refine"][:, 2] == 0), "dominant-key list overflow"
         stats["dominant"] = int(res["refine"][:, 0].max())
+    if "idx_bad" in res:
+        # the sparse layers found every entry of the step's own lists in [0, P_t]
+        assert np.all(res["idx_bad"] == 0), "index check: entries outside [0, P_t]"
     rtol_scores = SCORES_RTOL_DECODE if w.n_q_tokens == 1 else SCORES_RTOL_PREFILL
     gpu_idx_oracle_sparse = []
     for (b, t, g), rr in ref.items():

@@ -124,7 +124,9 @@ def test_workspace_regions(T):
     s = dataclasses.replace(good(), n_q_tokens=T)
     total = hs2.workspace_bytes(s, 2)
     rows = s.batch * T * s.n_kv_heads
-    for region, size in ((hs2.HS2_WS_LSE2, rows * 8 * 8), (hs2.HS2_WS_REFINE, rows * 16)):
+    parts = 1 if rows >= 256 else -(-(s.top_k + s.window) // 128)   # sparse slices per row
+    for region, size in ((hs2.HS2_WS_LSE2, rows * 8 * 8), (hs2.HS2_WS_REFINE, rows * 16),
+                         (hs2.HS2_WS_INDEX_CHECK, rows * parts * 4)):
         off, nb = hs2.workspace_region(s, 2, region)
         assert nb == size and off % 256 == 0 and off + nb <= total
     lib = hs2.raw()

@@ -240,6 +240,50 @@ def test_sparse_attn_standalone(hs2):
     assert np.all(got[:, 1, 0, 8:16] == 0.0)
 
 
+def test_sparse_attn_index_check(hs2):
+    """Malformed index lists: every entry outside [0, P_t] among the n_sel read
+    is counted per row in the workspace (HS2_WS_INDEX_CHECK), the read stays in
+    the cache (an entry below 0 reads row 0, one at or past S reads row S-1,
+    one in (P_t, S) reads that row), and the outputs equal the oracle's on the
+    clamped list.  Three query tokens, so that P_t < S - 1 for two of them."""
+    w = wl.small(batch=2, n_q_tokens=3, n_q_heads=16, n_kv_heads=2, ctx_len=2500,
+                 n_sparse_layers=3, top_k=300, window=50, config_id=27)
+    x = wl.generate(w)
+    ref = orc.cross_decoder_step(x["q_full"], x["k"], x["v"], None, top_k=w.top_k,
+                                 window=w.window, scale=w.scale, keep_scores=False)
+    s = hs2.shape_of(w)
+    S, T = w.ctx_len, w.n_q_tokens
+    idx = np.full((w.batch, T, w.n_kv_heads, s.cap), -1, dtype=np.int32)
+    ns = np.zeros((w.batch, T, w.n_kv_heads), dtype=np.int32)
+    for (b, t, g), rr in ref.items():
+        idx[b, t, g, : rr["idx"].size] = rr["idx"]
+        ns[b, t, g] = rr["idx"].size
+    idx[0, 0, 0, [3, 40, 299]] = [-1, S + 7, S - 1]      # below 0, past S, past P_0 = S - 3
+    idx[0, 2, 1, 10] = -(1 << 30)
+    idx[1, 1, 0, 200] = S - 1                             # past P_1 = S - 2
+    idx[1, 1, 1, 100] = 2_000_000_000
+    idx[1, 0, 0, s.cap - 20:] = -1      # as if padding, and a count past the capacity reads it
+    ns[1, 0, 0] = s.cap + 500
+    rd = np.minimum(ns, s.cap)
+    P = S - T + np.arange(T)[None, :, None]
+    col = np.arange(s.cap)[None, None, None, :]
+    want_bad = ((col < rd[..., None]) & ((idx < 0) | (idx > P[..., None]))).sum(axis=3)
+    assert want_bad[1, 0, 0] == 20 and want_bad[0, 0, 0] == 3 and want_bad[1, 1, 0] == 1
+    L = w.n_sparse_layers
+    out = torch.empty((L, w.batch, T, w.n_q_heads, 128), dtype=torch.bfloat16, device="cuda")
+    ws = hs2.alloc_workspace(s, L)
+    hs2.sparse_attn(s, gh.dev(x["q_sparse"]), gh.dev(x["k"]), gh.dev(x["v"]),
+                    torch.from_numpy(idx).cuda(), torch.from_numpy(ns).cuda(), out, ws=ws)
+    torch.cuda.synchronize()
+    bad = hs2.workspace_index_check(s, L, ws).cpu().numpy().reshape(w.batch, T, w.n_kv_heads)
+    gh.log(f"[index check] counted {bad.ravel().tolist()}")
+    assert bad.tolist() == want_bad.tolist()
+    got = gh.host_f64(out)
+    want = orc.sparse_step(x["q_sparse"], x["k"], x["v"], np.clip(idx, 0, S - 1), rd,
+                           scale=w.scale)
+    gh.check_outputs(got, want, "sparse on a malformed list (clamped)")
+
+
 def test_full_attn_scores_standalone(hs2):
     w = wl.small(batch=2, n_q_heads=16, n_kv_heads=2, ctx_len=1777, n_sparse_layers=0, top_k=64,
                  window=16, n_needles=5, config_id=26)
