@@ -438,7 +438,7 @@ def early_exit(steps: int = 5, warmup: int = 2, n_groups: int = 4, n_sparse: int
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None,
                     help="one workload alone (default: the headline line with every workload)")

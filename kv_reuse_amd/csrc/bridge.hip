@@ -12,9 +12,10 @@
 //
 // Two kernels:
 //  * many tokens (a prefill chunk or a whole prompt): 256 tokens x 256
-//    features (two heads' K or V) per work-group of 4 waves, each wave 128 x
-//    128 (its accumulators fill the accumulation registers, one wave per
-//    SIMD), so every operand read from LDS serves 8 MFMAs; the reduction is
+//    features (two heads' K or V) per work-group of 8 waves, each wave 64
+//    tokens x 128 features (two waves per SIMD, so that one's waits and
+//    barriers are covered by the other's MFMAs), every feature operand read
+//    from LDS serving 4 MFMAs and every token operand 8; the reduction is
 //    staged through LDS 32 deep, four stages in flight, by LDS-direct loads
 //    issued three stages ahead, and each stage's operands are read into
 //    registers while the previous stage's MFMAs run; the work-groups of one
@@ -34,6 +35,7 @@ constexpr int kBM = 256;      // tokens per work-group (large kernel)
 constexpr int kBN = 256;      // features per work-group: two heads' K or V
 constexpr int kBK = 32;       // reduction depth of one LDS stage (64-byte rows)
 constexpr int kBStages = 4;   // LDS stages in flight
+constexpr int kBWaves = 8;    // waves per work-group (large kernel)
 constexpr int kSmallWaves = 16;
 
 __device__ __forceinline__ int xcd_group(int id, int n) {
@@ -61,8 +63,8 @@ __device__ __forceinline__ void store4(const BridgeArgs& a, int f, int m, f32x4 
 // line, at different offsets; the swizzle separates rows 4 apart).
 __device__ __forceinline__ int bslot(int r, int c) { return c ^ ((r >> 2) & 3); }
 
-// grid: Hkv * ceil(M / 256) work-groups of 256 threads.
-__global__ __launch_bounds__(256, 1) void bridge_gemm_kernel(BridgeArgs a) {
+// grid: Hkv * ceil(M / 256) work-groups of 512 threads.
+__global__ __launch_bounds__(kBWaves * 64, 1) void bridge_gemm_kernel(BridgeArgs a) {
   __shared__ __align__(16) u16 wl[kBStages][kBN * kBK];
   __shared__ __align__(16) u16 hl[kBStages][kBM * kBK];
   const int tid = threadIdx.x;
@@ -73,9 +75,9 @@ __global__ __launch_bounds__(256, 1) void bridge_gemm_kernel(BridgeArgs a) {
   const int ft = lin % n_ft;
   const int m0 = (lin / n_ft) * kBM;
   const int f0 = ft * kBN;
-  const int wm = wave & 1, wn = wave >> 1;     // the wave's 128 tokens and 128 features
+  const int wm = wave & 3, wn = wave >> 2;     // the wave's 64 tokens and 128 features
 
-  // One stage: 16 LDS-direct loads of 1 KB (16 rows each) per operand, 4 per
+  // One stage: 16 LDS-direct loads of 1 KB (16 rows each) per operand, 2 per
   // wave and operand: lane l fills slot l & 3 of row 16 i + (l >> 2) with that
   // row's chunk (l & 3) ^ swizzle.  Hidden rows past M repeat the last.  Each
   // load is a scalar base (the work-group's first row at the stage's column)
@@ -83,10 +85,10 @@ __global__ __launch_bounds__(256, 1) void bridge_gemm_kernel(BridgeArgs a) {
   // from inline assembly, so that the compiler, which cannot tell the stage
   // buffers apart, does not wait for them before every LDS read; the waits
   // are explicit (vector memory operations complete in order).
-  uint32_t w_off[4], h_off[4];
+  uint32_t w_off[2], h_off[2];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int r = 64 * wave + 16 * u + (lane >> 2);
+  for (int u = 0; u < 2; ++u) {
+    const int r = 32 * wave + 16 * u + (lane >> 2);
     const int c = bslot(r, lane & 3);         // chunk for slot lane & 3 (an involution)
     w_off[u] = static_cast<uint32_t>((static_cast<size_t>(r) * a.dm + 8 * c) * 2);
     const int m = min(m0 + r, a.M - 1);
@@ -95,11 +97,11 @@ __global__ __launch_bounds__(256, 1) void bridge_gemm_kernel(BridgeArgs a) {
   const u16* w_base = a.w + static_cast<size_t>(f0) * a.dm;
   const u16* h_base = a.hidden + static_cast<size_t>(m0) * a.dm;
   const uint32_t wl0 = __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&wl[0][64 * wave * kBK])));
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&wl[0][32 * wave * kBK])));
   const uint32_t hl0 = __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&hl[0][64 * wave * kBK])));
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(&hl[0][32 * wave * kBK])));
   constexpr uint32_t kStageBytes = kBN * kBK * 2;
-  // load number i (0..7) of stage kt: rows 16 (i >> 1) .. of this wave's 64,
+  // load number i (0..3) of stage kt: rows 16 (i >> 1) .. of this wave's 32,
   // of the weights (i even) or the hidden states (i odd)
   auto dma_one = [&](int kt, int i) {
     const uint32_t sb = (kt % kBStages) * kStageBytes + 16 * (i >> 1) * kBK * 2;
@@ -112,25 +114,28 @@ __global__ __launch_bounds__(256, 1) void bridge_gemm_kernel(BridgeArgs a) {
   };
   auto dma_stage = [&](int kt) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dma_one(kt, i);
+    for (int i = 0; i < 4; ++i) dma_one(kt, i);
   };
-  // the wave's operands of one stage: 8 feature blocks and 8 token blocks
-  auto read_ops = [&](int kt, bf16x8 (&wa)[8], bf16x8 (&hb)[8]) {
+  // the wave's operands of one stage: 8 feature blocks and 4 token blocks
+  auto read_ops = [&](int kt, bf16x8 (&wa)[8], bf16x8 (&hb)[4]) {
     const int buf = kt % kBStages;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int rw = 128 * wn + 16 * i + col;
-      const int rh = 128 * wm + 16 * i + col;
       wa[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(&wl[buf][rw * kBK + 8 * bslot(rw, grp)]));
-      hb[i] = as_bf16x8(*reinterpret_cast<const u32x4*>(&hl[buf][rh * kBK + 8 * bslot(rh, grp)]));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int rh = 64 * wm + 16 * j + col;
+      hb[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(&hl[buf][rh * kBK + 8 * bslot(rh, grp)]));
     }
   };
 
-  f32x4 acc[8][8];
+  f32x4 acc[8][4];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Stage kt + 3 is loaded at the start of stage kt (into the buffer of stage
   // kt - 1, whose operands were read during stage kt - 2); stage kt + 1 must
@@ -142,7 +147,7 @@ __global__ __launch_bounds__(256, 1) void bridge_gemm_kernel(BridgeArgs a) {
   if (nk > 2) dma_stage(2);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  bf16x8 wa[2][8], hb[2][8];
+  bf16x8 wa[2][8], hb[2][4];
   read_ops(0, wa[0], hb[0]);
   for (int kt = 0; kt < nk; kt += 2) {
     // two stages per trip (nk is even), so that the register sets are named
@@ -156,10 +161,10 @@ __global__ __launch_bounds__(256, 1) void bridge_gemm_kernel(BridgeArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = mfma_16x16x32(wa[h][i], hb[h][j], acc[i][j]);
-      // stage s + 2 (read during stage s + 1): only stage s + 3's 8 loads,
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma_16x16x32(wa[h][i], hb[h][j], acc[i][j]);
+      // stage s + 2 (read during stage s + 1): only stage s + 3's 4 loads,
       // if issued, are newer
-      if (more) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      if (more) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
       else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
     }
@@ -167,8 +172,8 @@ __global__ __launch_bounds__(256, 1) void bridge_gemm_kernel(BridgeArgs a) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   // C[feature 4 grp + e][token col] of block (i, j)
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int m = m0 + 128 * wm + 16 * j + col;
+  for (int j = 0; j < 4; ++j) {
+    const int m = m0 + 64 * wm + 16 * j + col;
     if (m >= a.M) continue;
 #pragma unroll
     for (int i = 0; i < 8; ++i) store4(a, f0 + 128 * wn + 16 * i + 4 * grp, m, acc[i][j]);
@@ -220,7 +225,7 @@ hipError_t launch_kv_bridge(const BridgeArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(bridge_small_kernel, grid, dim3(kSmallWaves * 64), 0, st, a);
   } else {
     const int n_wg = a.Hkv * ((a.M + kBM - 1) / kBM);
-    hipLaunchKernelGGL(bridge_gemm_kernel, dim3(n_wg), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(bridge_gemm_kernel, dim3(n_wg), dim3(kBWaves * 64), 0, st, a);
   }
   return hipGetLastError();
 }
