@@ -94,7 +94,13 @@ typedef struct hs2_shape {
                          per row of the decode full layer (clamped to 1 .. min(1024,
                          ceil(ctx_len / 128))), e.g. to check that the results do not
                          depend on the plan.  Ignored for a prefill chunk. */
-  int32_t reserved;   /* must be 0 */
+  int32_t decode_select;/* 0: the library's plan.  1: the decode selection from the full
+                         layer's 16-key subtile bounds (re-reading the K rows of the
+                         candidates only); 2: from every key's importance (one pass over
+                         K, then the same ranking as a prefill chunk's rows).  The plan
+                         takes 2 where all of K is small (short contexts).  Both give the
+                         same selection; e.g. to test both.  Ignored for a prefill chunk;
+                         other values give HS2_ERR_INVALID_ARG. */
 } hs2_shape;          /* 64 bytes, no padding */
 
 enum {

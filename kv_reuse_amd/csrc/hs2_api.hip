@@ -54,7 +54,7 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
   if (!sh || !p) return HS2_ERR_INVALID_ARG;
   if (sh->ctx_len < 1 || sh->batch < 1 || sh->n_q_tokens < 1 || sh->n_q_heads < 1 ||
       sh->n_kv_heads < 1 || sh->head_dim < 1 || sh->top_k < 0 || sh->window < 0 ||
-      n_layers < 0 || sh->decode_splits < 0 || sh->reserved != 0)
+      n_layers < 0 || sh->decode_splits < 0 || sh->decode_select < 0 || sh->decode_select > 2)
     return HS2_ERR_INVALID_ARG;
   const int32_t bs = sh->select_block;
   if (bs != 0) {
@@ -162,6 +162,13 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
   // key with probability about 1/4 or more)
   q.quads = decode && q.k > 0 && q.S <= int64_t{64} * q.k;
   q.off_qdiff = take(q.quads ? Rz * nst * 4 * kG : 0);
+  // the dense decode selection (short contexts): every key's importance, then
+  // the prefill chunk's per-row selection; the caller may choose either way
+  q.dense_dec = decode && (sh->decode_select == 2 ||
+                           (sh->decode_select == 0 &&
+                            Rz * static_cast<size_t>(q.S) * kD * 2 <= static_cast<size_t>(kDenseDecodeBytes)));
+  q.n_ib = static_cast<int>(decode ? ceil_div(q.S, kDecImpKeys) : ceil_div(q.T, kImportanceTok));
+  const bool row_select = !decode || q.dense_dec;   // the per-row selection kernel runs
   q.off_lse2 = take(Rz * kG * sizeof(double));
   q.off_ytop = take(Rz * kG * sizeof(float));
   q.off_hist = take(Rz * kNB * sizeof(uint32_t));
@@ -181,23 +188,22 @@ int make_plan(const hs2_shape* sh, int n_layers, Plan* p) {
   // band lists: a whole row's worth in decode; in a prefill chunk (many rows)
   // a bounded list per row, but one entry per block for block selection, so
   // that any band of blocks is ranked exactly
-  q.band_cap = decode ? 0 : std::min<int64_t>(q.Spad, kPrefillBandCap);
-  if (!decode && q.bs > 0) q.band_cap = std::max<int64_t>(q.band_cap, ceil_div(q.S, q.bs));
+  q.band_cap = row_select ? std::min<int64_t>(q.Spad, kPrefillBandCap) : 0;
+  if (row_select && q.bs > 0) q.band_cap = std::max<int64_t>(q.band_cap, ceil_div(q.S, q.bs));
   q.off_band_idx = take(Rz * q.band_cap * sizeof(int32_t));
   q.off_band_key = take(Rz * q.band_cap * sizeof(uint64_t));
   // the fixed-point importance of a prefill chunk shares the key buffer of the
   // selection from given scores: no call uses both
   q.off_ybuf = q.off_ukey;
-  // per (batch, KV head, importance token block): that block's share of max |k|
-  q.off_kmax = take(decode ? 0 : static_cast<size_t>(q.B) * q.Hkv *
-                                      ceil_div(q.T, kImportanceTok) * sizeof(uint32_t));
+  // per (batch, KV head, importance work-group): that work-group's share of max |k|
+  q.off_kmax = take(row_select ? static_cast<size_t>(q.B) * q.Hkv * q.n_ib * sizeof(uint32_t) : 0);
   q.off_ref_part = take(decode ? Rz * q.ref_nwg * sizeof(RefinePart) : 0);
   q.off_dsub = take(decode ? Rz * q.cc_nchunk * static_cast<size_t>(q.cc_chunk) * sizeof(int32_t) : 0);
   q.off_dsub_cnt = take(decode ? Rz * q.cc_nchunk * sizeof(uint32_t) : 0);
   q.off_cut = take(decode ? Rz * sizeof(float) : 0);
   q.off_lse2r = take(Rz * kG * sizeof(double));
   q.off_ref_stat = take(Rz * sizeof(RefineStat));
-  q.off_dom_list = take(decode ? 0 : Rz * kDomCap * sizeof(int32_t));
+  q.off_dom_list = take(row_select ? Rz * kDomCap * sizeof(int32_t) : 0);
   const size_t sp_parts = q.sp_nch > 1 ? Rz * q.sp_nch * n_layers * kG : 0;
   q.off_sp_m = take(sp_parts * sizeof(float));
   q.off_sp_l = take(sp_parts * sizeof(float));
@@ -341,7 +347,12 @@ int run_step(const Plan& p, int32_t n_sparse_layers, const hs2_bf16* q_full,
     return HS2_OK;
   }
   if ((st = run_full(p, q_full, k, v, out_full, lse, ws, s)) != HS2_OK) return st;
-  HS2_TRY(launch_fused_select(p, q_full, k, idx, n_sel, lse, ws, s));
+  if (p.dense_dec) {
+    HS2_TRY(launch_decode_importance(p, q_full, k, ws, s));
+    HS2_TRY(launch_prefill_select(p, q_full, k, idx, n_sel, lse, ws, s));
+  } else {
+    HS2_TRY(launch_fused_select(p, q_full, k, idx, n_sel, lse, ws, s));
+  }
   if (scores) HS2_TRY(launch_full_scores(p, q_full, k, scores, ws, s));
   if (n_sparse_layers > 0)
     HS2_TRY(launch_sparse(p, q_sparse, k, v, idx, n_sel, out_sparse, ws, s));
@@ -464,10 +475,12 @@ int hs2_cross_decoder_step_timed(const hs2_shape* shape, int32_t n_sparse_layers
     if (rc == HS2_OK) rc = hip_status(hipEventRecord(ev[1], s));
     if (rc == HS2_OK && decode) rc = hip_status(launch_full_combine(p, out_full, nullptr, ws, s));
     if (rc == HS2_OK) rc = hip_status(hipEventRecord(ev[2], s));
+    const bool by_rows = !decode || p.dense_dec;   // importance pass, then the per-row selection
     if (rc == HS2_OK)
-      rc = hip_status(decode ? launch_fused_select(p, q_full, k, idx, n_sel, nullptr, ws, s)
-                             : launch_prefill_importance(p, q_full, k, ws, s));
-    if (rc == HS2_OK && !decode)
+      rc = hip_status(!by_rows ? launch_fused_select(p, q_full, k, idx, n_sel, nullptr, ws, s)
+                      : decode ? launch_decode_importance(p, q_full, k, ws, s)
+                               : launch_prefill_importance(p, q_full, k, ws, s));
+    if (rc == HS2_OK && by_rows)
       rc = hip_status(launch_prefill_select(p, q_full, k, idx, n_sel, nullptr, ws, s));
     if (rc == HS2_OK) rc = hip_status(hipEventRecord(ev[3], s));
     if (rc == HS2_OK && n_sparse_layers > 0)

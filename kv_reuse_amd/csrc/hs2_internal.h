@@ -20,6 +20,10 @@ constexpr int kSparseChunk = 128;  // selected keys per sparse work-group (a dec
 constexpr float kYRange = 64.0f;   // log2 range below the row's top score that the bins span
 constexpr int kYFixBits = 10;      // prefill importance: fixed point, 2^-10 log2 units per step
 constexpr int kImportanceTok = 64;  // prefill importance pass: chunk tokens per work-group
+constexpr int kDecImpKeys = 256;    // decode importance pass (dense selection): keys per work-group
+// the plan's dense decode selection: when all of K (the rows' K caches, 256
+// bytes per key row) is at most this much
+constexpr int64_t kDenseDecodeBytes = int64_t{64} << 20;
 constexpr int kMaxSplits = 1024;   // context splits per row (full layer, decode)
 constexpr int kDefaultCUs = 256;   // compute units assumed when no device can be queried
 // Refinement of the log-normaliser: a key is dominant for head h when its
@@ -86,6 +90,8 @@ struct Plan {
   int n_split, kps;
   size_t off_part_m, off_part_l, off_part_o, off_stmax, off_qdiff, off_lse2, off_ytop;
   bool quads;                // decode: the quads' distances are written and used
+  bool dense_dec;            // decode: selection from every key's importance
+  int n_ib;                  // importance work-groups per row (decode) / token blocks (prefill)
   // selection state shared by both selection paths
   size_t off_hist, off_info;
   // selection from given scores
@@ -178,8 +184,13 @@ hipError_t launch_prefill_importance(const Plan& p, const u16* q, const u16* k, 
 // logits and an exactly recomputed normaliser (no workspace).
 hipError_t launch_prefill_scores(const Plan& p, const u16* q, const u16* k, float* scores,
                                  hipStream_t st);
-// Prefill chunk selection: one work-group per row.  It first refines lse2
-// over the row's dominant keys (and writes lse, when non-null, from it).
+// Decode importance for the dense selection: every key's fixed-point y and
+// each work-group's largest |k|, in the workspace (as the prefill pass writes).
+hipError_t launch_decode_importance(const Plan& p, const u16* q, const u16* k, void* ws,
+                                    hipStream_t st);
+// Selection of a prefill chunk's rows, or of decode rows in the dense mode:
+// one work-group per row.  It first refines lse2 over the row's dominant keys
+// (and writes lse, when non-null, from it).
 hipError_t launch_prefill_select(const Plan& p, const u16* q, const u16* k, int32_t* idx,
                                  int32_t* n_sel, float* lse, void* ws, hipStream_t st);
 

@@ -822,6 +822,100 @@ __global__ __launch_bounds__(kXThreads) void prefill_scores_kernel(
   for (int64_t key = P + 1 + tid; key < S; key += kXThreads) sr[key] = 0.f;
 }
 
+// Importance of a decode row's keys for the dense selection (short contexts):
+// the same 16-bit fixed-point y as the prefill chunk's importance pass, for
+// every key j < S of row (b, g),
+//   y[row][j] = max_h(s2_h[j] - lse2_h), stored as round((y - ybase) 2^10)
+//               clamped to 0..65535, ybase = the row's top log-weight minus 64,
+// with the same float32 arithmetic (the MFMA's float32 sum of exact bf16
+// products, one fma per head with the scale's high part), so that the
+// selection's error bound holds unchanged.  grid: (ceil(S / kDKeys), R); a
+// work-group of 4 waves takes kDKeys keys, a wave 16-key subtiles in turn:
+// S^T = K . Q^T on the bf16 MFMA with the 8 heads padded to 16 (lane (col,
+// grp) holds head col of keys 4 grp .. 4 grp + 3), the maximum over the heads
+// across lanes col 0..7.  kmax[row][wg] = the largest |k| (bf16 bits) of the
+// keys the work-group read.
+constexpr int kDKeys = kDecImpKeys;
+constexpr int kDThreads = 256;
+__global__ __launch_bounds__(kDThreads) void decode_importance_kernel(
+    const u16* __restrict__ q, const u16* __restrict__ k, const double* __restrict__ lse2,
+    const float* __restrict__ ytop_h, u16* __restrict__ y, uint32_t* __restrict__ kmax,
+    int64_t S, int64_t Spad, float c2_hi, int64_t kvp) {
+  __shared__ uint32_t s_kmax;
+  const int r = blockIdx.y;
+  const int wg = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  if (tid == 0) s_kmax = 0u;
+  const u16* kr = k + static_cast<size_t>(r) * kvp * kD;
+  // the B operand: head col (zero for the padding heads), dims 32 c + 8 grp
+  bf16x8 qb[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    qb[c] = col < kG ? as_bf16x8(load_u32x4(q + (static_cast<size_t>(r) * kG + col) * kD + 32 * c + 8 * grp))
+                     : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+  float yt = -INFINITY;
+  for (int h = 0; h < kG; ++h) yt = fmaxf(yt, ytop_h[static_cast<size_t>(r) * kG + h]);
+  const float ybase = yt - kYRange;
+  // 2^10 ybase is exact, and so is its sum with 0.5 (|ybase| < 2^12)
+  const float yoff = 0.5f - ybase * static_cast<float>(1 << kYFixBits);
+  const float nl2r = col < kG ? fmaf(-static_cast<float>(lse2[static_cast<size_t>(r) * kG + col]),
+                                     static_cast<float>(1 << kYFixBits), yoff)
+                              : -INFINITY;
+  const float c2s = c2_hi * static_cast<float>(1 << kYFixBits);   // exact
+  u16* yrow = y + static_cast<size_t>(r) * Spad;
+  const int64_t k0 = static_cast<int64_t>(wg) * kDKeys;
+  const int64_t k1 = min(S, k0 + kDKeys);
+  u16x2 kabs{0, 0};
+  __syncthreads();
+  for (int64_t key0 = k0 + 16 * wave; key0 < k1; key0 += 16 * (kDThreads / 64)) {
+    // the A operand: key key0 + col (rows past S repeat the last), dims 32 c + 8 grp
+    const int64_t key = min(key0 + col, S - 1);
+    u32x4 ka[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) ka[c] = load_u32x4(kr + key * kD + 32 * c + 8 * grp);
+    f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) sacc = mfma_16x16x32(as_bf16x8(ka[c]), qb[c], sacc);
+    if (key0 + col < k1) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          kabs = __builtin_elementwise_max(kabs, __builtin_bit_cast(u16x2, ka[c][e] & 0x7FFF7FFFu));
+    }
+    // y in fixed-point steps plus 0.5 for head col, then the maximum over the
+    // 8 heads: lanes col ^ 1, ^ 2, then the other quad of the 8
+    float yv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float m = fmaf(sacc[i], c2s, nl2r);
+      m = fmaxf(m, dpp_f32<0xB1>(m));
+      m = fmaxf(m, dpp_f32<0x4E>(m));
+      m = fmaxf(m, dpp_f32<0x141>(m));
+      yv[i] = m;
+    }
+    // lane (0, grp) stores keys 4 grp .. 4 grp + 3 (8 bytes; keys at or past S
+    // land in the row's unread tail below Spad)
+    if (col == 0) {
+      uint32_t v4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        // clamp to 0..65535, then truncate: rounds to nearest
+        v4[i] = static_cast<uint32_t>(__builtin_amdgcn_fmed3f(yv[i], 0.f, 65535.f));
+      *reinterpret_cast<uint2*>(yrow + key0 + 4 * grp) =
+          uint2{v4[0] | (v4[1] << 16), v4[2] | (v4[3] << 16)};
+    }
+  }
+  uint32_t m = max(static_cast<uint32_t>(kabs[0]), static_cast<uint32_t>(kabs[1]));
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(static_cast<int>(m), off)));
+  if (lane == 0) atomicMax(&s_kmax, m);
+  __syncthreads();
+  if (tid == 0) kmax[static_cast<size_t>(r) * gridDim.x + wg] = s_kmax;
+}
+
 }  // namespace
 
 hipError_t launch_full_prefill(const Plan& p, const u16* q, const u16* k, const u16* v, u16* out,
@@ -853,6 +947,19 @@ hipError_t launch_prefill_importance(const Plan& p, const u16* q, const u16* k, 
                      reinterpret_cast<u16*>(w + p.off_ybuf),
                      reinterpret_cast<uint32_t*>(w + p.off_kmax), p.S, p.Spad, p.T, p.Hkv, p.w,
                      n_tblk, c2_hi, p.kvp);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_importance(const Plan& p, const u16* q, const u16* k, void* ws,
+                                    hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  const double c2 = p.scale * 1.4426950408889634;
+  hipLaunchKernelGGL(decode_importance_kernel, dim3(p.n_ib, p.R), dim3(kDThreads), 0, st, q, k,
+                     reinterpret_cast<const double*>(w + p.off_lse2),
+                     reinterpret_cast<const float*>(w + p.off_ytop),
+                     reinterpret_cast<u16*>(w + p.off_ybuf),
+                     reinterpret_cast<uint32_t*>(w + p.off_kmax), p.S, p.Spad,
+                     static_cast<float>(c2), p.kvp);
   return hipGetLastError();
 }
 

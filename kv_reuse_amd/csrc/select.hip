@@ -1825,7 +1825,7 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, int32_t* __restrict__ band_idx,
     uint64_t* __restrict__ band_key, int64_t band_cap, int32_t* __restrict__ idx_out,
     int32_t* __restrict__ nsel_out, int64_t S, int64_t Spad, int T, int Hkv, int topk, int w,
-    int cap, int bs, double c2, float c2_hi, int64_t kvp) {
+    int cap, int bs, double c2, float c2_hi, float c2_lo, bool split_logits, int64_t kvp) {
   static_assert(kMaxBlocks * sizeof(uint16_t) <= kPList * sizeof(uint32_t), "block maxima fit the list");
   static_assert(3 * (kMaxSel / 4) + 2 * kMaxSelBlocks <= kMaxSel, "block lists fit bw");
   __shared__ __align__(16) int32_t up[kMaxSel];
@@ -1970,8 +1970,13 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
             }
           }
           // the term's change 2^(y - lse2) - 2^(a2 - lse2) = p (e^d - 1), d = (y - a2) ln 2,
-          // p = 2^(a2 - lse2); |d| is below 1e-4, so d + d^2 / 2 leaves 2e-13 of p
-          const double a2 = static_cast<double>(acc[i]) * static_cast<double>(c2_hi);   // exact
+          // p = 2^(a2 - lse2); |d| is below 1e-4, so d + d^2 / 2 leaves 2e-13 of p.
+          // a2 is the base-2 logit as the full layer formed it: a c2_hi (exact
+          // here) for a prefill chunk; for decode rows the split kernel's
+          // two-term product, the same float32 operations
+          const double a2 = split_logits
+                                ? static_cast<double>(fmaf(acc[i], c2_hi, acc[i] * c2_lo))
+                                : static_cast<double>(acc[i]) * static_cast<double>(c2_hi);
           const double dd = (c2 * dot - a2) * M_LN2;
           const float pw = __builtin_amdgcn_exp2f(static_cast<float>(a2 - l2h));
           const double term = static_cast<double>(pw) * (dd + 0.5 * dd * dd);
@@ -2868,11 +2873,11 @@ hipError_t launch_prefill_select(const Plan& p, const u16* q, const u16* k, int3
   char* w = static_cast<char*>(ws);
   const double c2 = p.scale * 1.4426950408889634;
   const float c2_hi = static_cast<float>(c2);
+  const float c2_lo = static_cast<float>(c2 - static_cast<double>(c2_hi));
   auto kern = p.bs > 0 ? prefill_select_kernel<true> : prefill_select_kernel<false>;
   hipLaunchKernelGGL(kern, dim3(p.R), dim3(kRowThreads), 0, st,
                      reinterpret_cast<const u16*>(w + p.off_ybuf),
-                     reinterpret_cast<const uint32_t*>(w + p.off_kmax),
-                     (p.T + kImportanceTok - 1) / kImportanceTok,
+                     reinterpret_cast<const uint32_t*>(w + p.off_kmax), p.n_ib,
                      reinterpret_cast<const double*>(w + p.off_lse2),
                      reinterpret_cast<double*>(w + p.off_lse2r), lse,
                      reinterpret_cast<const float*>(w + p.off_ytop),
@@ -2880,7 +2885,7 @@ hipError_t launch_prefill_select(const Plan& p, const u16* q, const u16* k, int3
                      reinterpret_cast<RefineStat*>(w + p.off_ref_stat), q, k,
                      reinterpret_cast<int32_t*>(w + p.off_band_idx),
                      reinterpret_cast<uint64_t*>(w + p.off_band_key), p.band_cap, idx, n_sel, p.S,
-                     p.Spad, p.T, p.Hkv, p.k, p.w, p.cap, p.bs, c2, c2_hi, p.kvp);
+                     p.Spad, p.T, p.Hkv, p.k, p.w, p.cap, p.bs, c2, c2_hi, c2_lo, p.T == 1, p.kvp);
   return hipGetLastError();
 }
 

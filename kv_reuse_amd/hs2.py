@@ -42,7 +42,7 @@ class Shape(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("select_block", ctypes.c_int32),
                 ("kv_capacity", ctypes.c_int64), ("decode_splits", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("decode_select", ctypes.c_int32)]
 
 
 class BridgeShape(ctypes.Structure):
@@ -113,6 +113,7 @@ class ShapeArgs:
     kv_capacity: int = 0      # token rows per KV head in k / v; 0 = ctx_len
     select_block: int = 0     # 0: token-level selection; else the block-level variant's block
     decode_splits: int = 0    # 0: the library's plan; else context splits per decode row
+    decode_select: int = 0    # 0: the library's plan; 1: from subtile bounds; 2: from every key
 
     def c(self) -> Shape:
         scale = self.scale if self.scale is not None else 1.0 / math.sqrt(self.head_dim)
@@ -120,7 +121,8 @@ class ShapeArgs:
                      n_q_tokens=self.n_q_tokens, n_q_heads=self.n_q_heads,
                      n_kv_heads=self.n_kv_heads, head_dim=self.head_dim, top_k=self.top_k,
                      window=self.window, select_block=self.select_block,
-                     kv_capacity=self.kv_capacity, decode_splits=self.decode_splits, reserved=0)
+                     kv_capacity=self.kv_capacity, decode_splits=self.decode_splits,
+                     decode_select=self.decode_select)
 
     @property
     def rows(self) -> int:

@@ -66,11 +66,11 @@ def cache_with_capacity(bits: np.ndarray, capacity: int) -> torch.Tensor:
 
 
 def run_step(w: wl.Workload, x, with_scores=True, with_lse=True, kv_capacity=0, block=0,
-             decode_splits=0):
+             decode_splits=0, decode_select=0):
     import dataclasses
     from kv_reuse_amd import hs2
     s = dataclasses.replace(hs2.shape_of(w), kv_capacity=kv_capacity, select_block=block,
-                            decode_splits=decode_splits)
+                            decode_splits=decode_splits, decode_select=decode_select)
     B, T, Hq, Hkv, D, S, L = (w.batch, w.n_q_tokens, w.n_q_heads, w.n_kv_heads, w.head_dim,
                               w.ctx_len, w.n_sparse_layers)
     q = dev(x["q_full"])

@@ -76,7 +76,8 @@ def test_workspace_bytes_valid_and_monotone():
     ("kv_capacity", -1, hs2.HS2_ERR_INVALID_ARG),
     ("kv_capacity", 1 << 40, hs2.HS2_ERR_UNSUPPORTED),
     ("decode_splits", -1, hs2.HS2_ERR_INVALID_ARG),
-    ("reserved", 1, hs2.HS2_ERR_INVALID_ARG),
+    ("decode_select", 3, hs2.HS2_ERR_INVALID_ARG),
+    ("decode_select", -1, hs2.HS2_ERR_INVALID_ARG),
 ])
 def test_bad_shapes_rejected(field, value, code):
     c = good().c()

@@ -42,12 +42,13 @@ STEP = [
 ]
 
 
+@pytest.mark.parametrize("path", [1, 2], ids=["subtile_path", "dense_path"])
 @pytest.mark.parametrize("name,kw,bs", STEP, ids=[s[0] for s in STEP])
-def test_block_step(hs2, name, kw, bs):
+def test_block_step(hs2, name, kw, bs, path):
     w = wl.small(name=name, **kw)
     x = wl.generate(w)
-    gh.log(f"[block step] {name} S={w.ctx_len} k={w.top_k} block={bs}")
-    res = gh.run_step(w, x, block=bs)
+    gh.log(f"[block step] {name} S={w.ctx_len} k={w.top_k} block={bs} selection path {path}")
+    res = gh.run_step(w, x, block=bs, decode_select=path)
     st = gh.compare_step(w, x, res, block=bs)
     gh.log(f"  {st}")
 

@@ -43,12 +43,19 @@ SMALL = [
 ]
 
 
+# the two decode selections: from the full layer's subtile bounds (1), and
+# from every key's importance with the per-row ranking of a prefill chunk (2)
+PATHS = [1, 2]
+
+
+@pytest.mark.parametrize("path", PATHS, ids=["subtile_path", "dense_path"])
 @pytest.mark.parametrize("name,kw", SMALL, ids=[s[0] for s in SMALL])
-def test_step_small(hs2, name, kw):
+def test_step_small(hs2, name, kw, path):
     w = wl.small(name=name, **kw)
     x = wl.generate(w)
-    gh.log(f"[step] {name} S={w.ctx_len} B={w.batch} Hkv={w.n_kv_heads} L={w.n_sparse_layers}")
-    res = gh.run_step(w, x)
+    gh.log(f"[step] {name} S={w.ctx_len} B={w.batch} Hkv={w.n_kv_heads} L={w.n_sparse_layers} "
+           f"selection path {path}")
+    res = gh.run_step(w, x, decode_select=path)
     st = gh.compare_step(w, x, res)
     gh.log(f"  {st}")
 
@@ -83,43 +90,47 @@ def test_step_decode_2k_workload(hs2):
     gh.log(f"  {gh.compare_step(w, x, res)}")
 
 
-def test_k_covers_context_sparse_equals_dense(hs2):
+@pytest.mark.parametrize("path", PATHS, ids=["subtile_path", "dense_path"])
+def test_k_covers_context_sparse_equals_dense(hs2, path):
     """k >= |C|: every key is selected, so a sparse layer fed the full layer's
     queries must reproduce the full layer's output."""
     w = wl.small(batch=2, n_q_heads=16, n_kv_heads=2, ctx_len=900, n_sparse_layers=2, top_k=1024,
                  window=128, config_id=21)
     x = wl.generate(w)
     x["q_sparse"][0] = x["q_full"]
-    res = gh.run_step(w, x)
+    res = gh.run_step(w, x, decode_select=path)
     gh.compare_step(w, x, res)
     assert np.all(res["n_sel"] == 900)
     err = np.abs(res["out_sparse"][0] - res["out_full"])
     assert err.max() <= 2e-2 and err.mean() <= 5e-3
 
 
-def test_k_zero_is_sliding_window(hs2):
+@pytest.mark.parametrize("path", PATHS, ids=["subtile_path", "dense_path"])
+def test_k_zero_is_sliding_window(hs2, path):
     w = wl.small(batch=1, n_q_heads=8, n_kv_heads=1, ctx_len=500, n_sparse_layers=2, top_k=0,
                  window=32, config_id=22)
     x = wl.generate(w)
-    res = gh.run_step(w, x)
+    res = gh.run_step(w, x, decode_select=path)
     gh.compare_step(w, x, res)
     assert res["n_sel"][0, 0, 0] == 32
     assert res["idx"][0, 0, 0, :32].tolist() == list(range(468, 500))
 
 
-def test_identical_keys_take_lowest_indices(hs2):
+@pytest.mark.parametrize("path", PATHS, ids=["subtile_path", "dense_path"])
+def test_identical_keys_take_lowest_indices(hs2, path):
     """All keys equal: every importance ties, so the lowest indices win.  The
     tie spans more keys than fit in LDS, which exercises the exact radix path."""
     w = wl.small(batch=1, n_q_heads=8, n_kv_heads=1, ctx_len=6000, n_sparse_layers=1, top_k=100,
                  window=16, config_id=23)
     x = wl.generate(w)
     x["k"][:] = x["k"][:, :, :1, :]
-    res = gh.run_step(w, x)
+    res = gh.run_step(w, x, decode_select=path)
     gh.compare_step(w, x, res, check_lse2=False)
     assert res["idx"][0, 0, 0, :116].tolist() == list(range(100)) + list(range(5984, 6000))
 
 
-def test_small_band_ties_take_lowest_indices(hs2):
+@pytest.mark.parametrize("path", PATHS, ids=["subtile_path", "dense_path"])
+def test_small_band_ties_take_lowest_indices(hs2, path):
     """40 identical keys scoring far above the rest, top_k 16: the bin of the
     k-th key holds just those 40 ties (a band small enough for the one-wave
     rank), so the 16 lowest of their positions win."""
@@ -130,12 +141,13 @@ def test_small_band_ties_take_lowest_indices(hs2):
     vec = wl.f32_to_bf16_bits((4.0 * qf[0, 0, :, :].mean(axis=0)).astype(np.float32))
     pos = np.sort(np.random.default_rng(2025).choice(1984, 40, replace=False))
     x["k"][0, 0, pos, :] = vec[None, :]
-    res = gh.run_step(w, x)
+    res = gh.run_step(w, x, decode_select=path)
     gh.compare_step(w, x, res)
     assert res["idx"][0, 0, 0, :32].tolist() == pos[:16].tolist() + list(range(1984, 2000))
 
 
-def test_large_band_distinct_keys(hs2):
+@pytest.mark.parametrize("path", PATHS, ids=["subtile_path", "dense_path"])
+def test_large_band_distinct_keys(hs2, path):
     """200 keys near one needle vector (distinct, within about one bin of each
     other) far above the rest, top_k 100: the bin of the k-th key holds more
     than 64 distinct entries, so the radix threshold (not the one-wave rank)
@@ -149,7 +161,7 @@ def test_large_band_distinct_keys(hs2):
     pos = np.sort(rng.choice(5984, 200, replace=False))
     noise = rng.standard_normal((200, 128)).astype(np.float32) * 0.003
     x["k"][0, 0, pos, :] = wl.f32_to_bf16_bits((base[None, :] + noise).astype(np.float32))
-    res = gh.run_step(w, x)
+    res = gh.run_step(w, x, decode_select=path)
     gh.compare_step(w, x, res)
 
 
