@@ -269,13 +269,17 @@ int hs2_kv_bridge(const hs2_bridge_shape* shape, const hs2_bf16* hidden, const h
  *                Valid after hs2_cross_decoder_step, and in decode after
  *                hs2_full_attn_scores.
  *   HS2_WS_REFINE uint32 [B*T*Hkv rows][4]: the refinement of that normaliser
- *                over the keys that carry weight (see hs2_cross_decoder_step):
- *                [0] dominant units summed again (decode: 16-key subtiles,
- *                prefill chunk: keys), [1] decode subtiles whose recomputed
- *                float32 maximum differed from the full layer's (expected 0),
- *                [2] prefill dominant keys beyond the per-row list capacity
- *                (not summed again; expected 0), [3] reserved.  Valid after
- *                hs2_cross_decoder_step (and, in decode, hs2_full_attn_scores).
+ *                over the keys that carry weight (see hs2_cross_decoder_step).
+ *                Decode with the subtile selection (and hs2_full_attn_scores):
+ *                [0] dominant 16-key subtiles summed again, [1] subtiles whose
+ *                recomputed float32 maximum differed from the full layer's
+ *                (expected 0), [2] 0.  A prefill chunk, and decode with the
+ *                dense selection (shape.decode_select): [0] dominant keys
+ *                summed again, [1] heads whose normaliser moved by more than
+ *                the selection's error bound allows (expected 0), [2] dominant
+ *                keys beyond the per-row list capacity (not summed again;
+ *                expected 0).  [3] reserved.  Valid after hs2_cross_decoder_step
+ *                (and, in decode, hs2_full_attn_scores).
  *   HS2_WS_INDEX_CHECK uint32 [B*T*Hkv rows][n_parts]: the sparse layers' index
  *                check.  Summed over a row's n_parts (bytes / (rows * 4)), the
  *                number of the entries idx[row][0..n_sel) that lie outside

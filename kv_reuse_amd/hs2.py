@@ -207,7 +207,9 @@ def workspace_lse2(s: ShapeArgs, n_sparse_layers: int, ws: torch.Tensor) -> torc
 
 def workspace_refine_stats(s: ShapeArgs, n_sparse_layers: int, ws: torch.Tensor) -> torch.Tensor:
     """Per-row statistics of the normaliser's refinement [rows][4] (uint32 as
-    int32): dominant units, float32 replica mismatches, list overflow, 0."""
+    int32): dominant units summed again; a count expected 0 (float32 replica
+    mismatches, or heads whose normaliser moved beyond the selection's bound);
+    dominant keys beyond the list (expected 0); 0."""
     off, nb = workspace_region(s, n_sparse_layers, HS2_WS_REFINE)
     return ws[off:off + nb].view(torch.int32).view(s.rows, 4)
 
