@@ -388,6 +388,10 @@ def measure_workload(w, args, *, select_block=0, swa=False, graph=False, graph_i
     rec["after_full_frac"] = round((phases[2] + phases[3]) / full_ms, 4) if full_ms > 0 else None
     rec["sparse_frac"] = round(phases[3] / full_ms, 4) if full_ms > 0 else None
     rec["roofline"] = roofline_of(w, phases[0], stream_gbs)
+    # a diagnostic of the selection's output (not a pass criterion): the share
+    # of the planted needles among older keys that the last step kept
+    torch.cuda.synchronize()
+    rec["needle_recall"] = wl.needle_recall(w, x["needles"], idx.cpu().numpy(), nsel.cpu().numpy())
     del q, k, v, qs, out, outs, idx, nsel, ws
     torch.cuda.empty_cache()
     return rec, (x if keep_inputs else None)
@@ -528,6 +532,7 @@ def main():
         "phases_ms": rec_w["phases_ms"],
         "after_full_frac": rec_w["after_full_frac"],
         "sparse_frac": rec_w["sparse_frac"],
+        "needle_recall": rec_w["needle_recall"],
         "wall_s_timed": rec_w.get("wall_s_timed"),
     }
     if stream:

@@ -187,6 +187,7 @@ def generate(w: Workload, seed: Optional[int] = None,
         with cf.ThreadPoolExecutor(max_workers=workers) as ex:
             list(ex.map(make_row, range(n_rows)))
 
+    needles = []   # (b, g, query token the needle is planted for, key position)
     if w.n_needles > 0:
         qf = bf16_bits_to_f32(q_full).astype(np.float64)
         pos_all = w.positions()
@@ -198,6 +199,7 @@ def generate(w: Workload, seed: Optional[int] = None,
                     pos = rneedle.choice(S, size=n, replace=False)
                     vec = w.needle_scale * qf[b, 0, heads, :].mean(axis=0)
                     k[b, g, pos] = f32_to_bf16_bits(vec.astype(np.float32))[None, :]
+                    needles.extend((b, g, 0, int(p)) for p in pos)
                 else:
                     for _ in range(w.n_needles):
                         t = int(rneedle.integers(0, T))
@@ -207,8 +209,15 @@ def generate(w: Workload, seed: Optional[int] = None,
                         p = int(rneedle.integers(0, hi))
                         vec = w.needle_scale * qf[b, t, heads, :].mean(axis=0)
                         k[b, g, p] = f32_to_bf16_bits(vec.astype(np.float32))
+                        needles.append((b, g, t, p))
 
-    out = {"q_full": q_full, "k": k, "v": v}
+    # a later needle at the same key overwrites an earlier one: keep the last
+    last = {}
+    for (b, g, t, p) in needles:
+        last[(b, g, p)] = t
+    out = {"q_full": q_full, "k": k, "v": v,
+           "needles": np.array([(b, g, t, p) for (b, g, p), t in sorted(last.items())],
+                               dtype=np.int64).reshape(-1, 4)}
     if with_sparse:
         qs = np.empty((w.n_sparse_layers, B, T, Hq, D), dtype=np.uint16)
         for n in range(w.n_sparse_layers):
@@ -216,6 +225,24 @@ def generate(w: Workload, seed: Optional[int] = None,
             qs[n] = f32_to_bf16_bits(_normal_f32(r, (B, T, Hq, D)))
         out["q_sparse"] = qs
     return out
+
+
+def needle_recall(w: "Workload", needles: np.ndarray, idx: np.ndarray,
+                  n_sel: np.ndarray) -> dict:
+    """A diagnostic, not a pass criterion: of the planted needles that lie among
+    their query row's older keys (below P_t - w + 1, so not forced in by the
+    window), how many the selection kept.  idx [B][T][Hkv][cap], n_sel [B][T][Hkv]."""
+    pos = w.positions()
+    found = total = 0
+    for b, g, t, p in needles:
+        first = int(pos[t]) - w.window + 1
+        if p >= first:
+            continue
+        total += 1
+        row = idx[b, t, g, : int(n_sel[b, t, g])]
+        found += int(np.any(row == p))
+    return {"needles": total, "found": found,
+            "recall": round(found / total, 4) if total else None, "kind": "diagnostic"}
 
 
 def small(name: str = "small", *, batch=1, n_q_tokens=1, n_q_heads=8, n_kv_heads=1,

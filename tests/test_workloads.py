@@ -38,6 +38,26 @@ def test_decode_needles_planted():
             vec = wl.f32_to_bf16_bits((4.0 * q[b, 0, g * 4:(g + 1) * 4].mean(axis=0)).astype(np.float32))
             hits = np.all(x["k"][b, g] == vec[None, :], axis=1)
             assert hits.sum() == 7
+            # the returned positions are exactly those rows
+            pos = x["needles"][(x["needles"][:, 0] == b) & (x["needles"][:, 1] == g), 3]
+            assert sorted(pos.tolist()) == np.flatnonzero(hits).tolist()
+
+
+def test_needle_recall_diagnostic():
+    """needle_recall counts the older-key needles kept by a selection: all of
+    them for a list holding every older key, none for the window alone."""
+    w = wl.small(batch=1, n_q_heads=8, n_kv_heads=1, ctx_len=300, n_needles=9, top_k=16,
+                 window=8)
+    x = wl.generate(w, with_sparse=False)
+    older = x["needles"][x["needles"][:, 3] < 300 - 8 + 1]
+    cap = 400
+    every = np.full((1, 1, 1, cap), -1, dtype=np.int32)
+    every[0, 0, 0, :300] = np.arange(300)
+    r = wl.needle_recall(w, x["needles"], every, np.array([[[300]]]))
+    assert r["needles"] == len(older) and r["found"] == len(older)
+    window = np.full((1, 1, 1, cap), -1, dtype=np.int32)
+    window[0, 0, 0, :8] = np.arange(292, 300)
+    assert wl.needle_recall(w, x["needles"], window, np.array([[[8]]]))["found"] == 0
 
 
 def test_prefill_needles_are_candidates_of_their_query():
