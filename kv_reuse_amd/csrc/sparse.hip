@@ -47,7 +47,7 @@ __global__ __launch_bounds__(NCT * 64) void sparse_kernel(
     const float* __restrict__ swa_add, uint32_t* __restrict__ bad) {
   __shared__ __align__(16) u16 klds[kSub * kPitch];
   __shared__ __align__(16) u16 vlds[kSub * kPitch];
-  __shared__ int32_t sidx[kSub];
+  __shared__ int32_t sidx[2 * kSub];   // (two buffers when the gather is pipelined)
   __shared__ uint32_t s_bad;
 
   const int r = blockIdx.y;
@@ -96,84 +96,125 @@ __global__ __launch_bounds__(NCT * 64) void sparse_kernel(
   for (int nb = 0; nb < 8; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  for (int sc = pos_begin; sc < pos_end; sc += kSub) {
-    const int n_here = min(kSub, pos_end - sc);
-    __syncthreads();  // the previous sub-chunk is consumed
-    for (int i = tid; i < kSub; i += blockDim.x) {
-      const int32_t j = i < n_here ? idx[static_cast<size_t>(r) * cap + sc + i] : -1;
-      sidx[i] = j;
-      if (i < n_here && (j < 0 || j > P_row)) atomicAdd(&s_bad, 1u);
-    }
-    __syncthreads();
-    // every thread's 16-byte pieces of the sub-chunk, 8 (K, V) pairs at a
-    // time: all loads of a batch first, then its LDS stores, so a 256-thread
-    // work-group gathers the sub-chunk in one memory round trip
-    constexpr int kPieces = (kSub * 16 + NCT * 64 - 1) / (NCT * 64);
-    constexpr int kBatch = kPieces < 8 ? kPieces : 8;
-#pragma unroll
-    for (int u0 = 0; u0 < kPieces; u0 += kBatch) {
-      u32x4 kv_k[kBatch], kv_v[kBatch];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        // (pieces past the sub-chunk, when the thread count does not divide
-        // it, read piece 0 and are not stored)
-        const int pc0 = tid + (u0 + u) * NCT * 64;
-        const int pc = pc0 < kSub * 16 ? pc0 : 0;
-        const int key = pc >> 4, c16 = pc & 15;
-        // entries outside [0, S) (padding, or a malformed list) read row 0 /
-        // S-1 instead of faulting; padding is masked out of the softmax below
-        const int j = sidx[key];
-        const size_t jj = j < 0 ? 0 : static_cast<size_t>(min(static_cast<int64_t>(j), S - 1));
-        kv_k[u] = load_u32x4(kr + jj * kD + 8 * c16);
-        kv_v[u] = load_u32x4(vr + jj * kD + 8 * c16);
-      }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int pc = tid + (u0 + u) * NCT * 64;
-        if (pc >= kSub * 16) continue;
-        const int key = pc >> 4, c16 = pc & 15;
-        *reinterpret_cast<u32x4*>(klds + key * kPitch + 8 * c16) = kv_k[u];
-        *reinterpret_cast<u32x4*>(vlds + key * kPitch + 8 * c16) = kv_v[u];
-      }
-    }
-    __syncthreads();
-    for (int kb = 0; kb < n_here; kb += 32) {
-      f32x4 sacc[2];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        sacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const u16* krow = klds + (kb + 16 * mt + col) * kPitch + 8 * grp;
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          sacc[mt] = mfma_16x16x32(as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 32 * c)),
-                                   qb[c], sacc[mt]);
-      }
-      float sv[8];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int kk = kb + 16 * mt + 4 * grp + i;
-          const float a = sacc[mt][i];
-          sv[mt * 4 + i] = kk < n_here ? fmaf(a, c2_hi, a * c2_lo) : -INFINITY;
+  // a sub-chunk's attention from LDS (its n_here keys), all layers of the wave
+  auto compute = [&](int n_here) {
+      for (int kb = 0; kb < n_here; kb += 32) {
+        f32x4 sacc[2];
+  #pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          sacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          const u16* krow = klds + (kb + 16 * mt + col) * kPitch + 8 * grp;
+  #pragma unroll
+          for (int c = 0; c < 4; ++c)
+            sacc[mt] = mfma_16x16x32(as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 32 * c)),
+                                     qb[c], sacc[mt]);
         }
-      float tm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
-                       fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
-      tm = max_xor32(max_xor16(tm));
-      const float m_new = fmaxf(m_run, tm);
-      const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      float p[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(sv[e] - m_new);
-      l_run = l_run * alpha + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
-      m_run = m_new;
-      const bf16x8 pb = as_bf16x8(u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                                        pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])});
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        o[nb] *= alpha;
-        o[nb] = mfma_16x16x32(lds_vt_operand(vlds + kb * kPitch, kPitch, nb, col, grp), pb, o[nb]);
+        float sv[8];
+  #pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int kk = kb + 16 * mt + 4 * grp + i;
+            const float a = sacc[mt][i];
+            sv[mt * 4 + i] = kk < n_here ? fmaf(a, c2_hi, a * c2_lo) : -INFINITY;
+          }
+        float tm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                         fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+        tm = max_xor32(max_xor16(tm));
+        const float m_new = fmaxf(m_run, tm);
+        const float alpha = (m_run == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        float p[8];
+  #pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] = __builtin_amdgcn_exp2f(sv[e] - m_new);
+        l_run = l_run * alpha + (((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7])));
+        m_run = m_new;
+        const bf16x8 pb = as_bf16x8(u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                          pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])});
+  #pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+          o[nb] *= alpha;
+          o[nb] = mfma_16x16x32(lds_vt_operand(vlds + kb * kPitch, kPitch, nb, col, grp), pb, o[nb]);
+        }
       }
+  };
+  // the sub-chunk's pieces: 16 bytes of one key's K and V rows per thread and
+  // piece, (key, c16) = piece >> 4, piece & 15
+  constexpr int kPieces = (kSub * 16 + NCT * 64 - 1) / (NCT * 64);
+  constexpr int kBatch = kPieces < 8 ? kPieces : 8;
+  // entries outside [0, S) (padding, or a malformed list) read row 0 / S-1
+  // instead of faulting; padding is masked out of the softmax
+  auto load_pieces = [&](const int32_t* sx, int u0, u32x4 (&kv_k)[kBatch], u32x4 (&kv_v)[kBatch]) {
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      // (pieces past the sub-chunk, when the thread count does not divide
+      // it, read piece 0 and are not stored)
+      const int pc0 = tid + (u0 + u) * NCT * 64;
+      const int pc = pc0 < kSub * 16 ? pc0 : 0;
+      const int key = pc >> 4, c16 = pc & 15;
+      const int j = sx[key];
+      const size_t jj = j < 0 ? 0 : static_cast<size_t>(min(static_cast<int64_t>(j), S - 1));
+      kv_k[u] = load_u32x4(kr + jj * kD + 8 * c16);
+      kv_v[u] = load_u32x4(vr + jj * kD + 8 * c16);
+    }
+  };
+  auto store_pieces = [&](int u0, const u32x4 (&kv_k)[kBatch], const u32x4 (&kv_v)[kBatch]) {
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int pc = tid + (u0 + u) * NCT * 64;
+      if (pc >= kSub * 16) continue;
+      const int key = pc >> 4, c16 = pc & 15;
+      *reinterpret_cast<u32x4*>(klds + key * kPitch + 8 * c16) = kv_k[u];
+      *reinterpret_cast<u32x4*>(vlds + key * kPitch + 8 * c16) = kv_v[u];
+    }
+  };
+  // entry i of the sub-chunk at list position sc: its index (-1 past the
+  // slice), counted when outside [0, P]
+  auto take_index = [&](int sc, int i, int32_t raw) -> int32_t {
+    const bool in = sc + i < pos_end;
+    if (in && (raw < 0 || raw > P_row)) atomicAdd(&s_bad, 1u);
+    return in ? raw : -1;
+  };
+  // (loads of list entries are clamped into the list, used or not)
+  auto index_at = [&](int pos) { return idx[static_cast<size_t>(r) * cap + min(pos, cap - 1)]; };
+  if constexpr (kPieces <= kBatch && kPieces <= 4) {
+    // One batch of loads holds a sub-chunk: the next sub-chunk's rows are
+    // gathered into registers while this one is computed from LDS, and the
+    // indices two sub-chunks ahead are loaded meanwhile.  The prefetches are
+    // unconditional (past the slice they read list entry cap - 1 or key row
+    // 0), so the compiler waits for each only where it is used.
+    int32_t jn = -1;
+    if (tid < kSub) sidx[tid] = take_index(pos_begin, tid, index_at(pos_begin + tid));
+    __syncthreads();
+    u32x4 kv_k[kBatch], kv_v[kBatch];
+    load_pieces(sidx, 0, kv_k, kv_v);
+    if (tid < kSub) jn = index_at(pos_begin + kSub + tid);
+    int buf = 0;
+    for (int sc = pos_begin; sc < pos_end; sc += kSub) {
+      __syncthreads();  // the previous sub-chunk is consumed, and its index buffer free
+      store_pieces(0, kv_k, kv_v);
+      if (tid < kSub) sidx[kSub * (buf ^ 1) + tid] = take_index(sc + kSub, tid, jn);
+      __syncthreads();
+      load_pieces(sidx + kSub * (buf ^ 1), 0, kv_k, kv_v);
+      if (tid < kSub) jn = index_at(sc + 2 * kSub + tid);
+      compute(min(kSub, pos_end - sc));
+      buf ^= 1;
+    }
+  } else {
+    for (int sc = pos_begin; sc < pos_end; sc += kSub) {
+      const int n_here = min(kSub, pos_end - sc);
+      __syncthreads();  // the previous sub-chunk is consumed
+      for (int i = tid; i < kSub; i += blockDim.x) sidx[i] = take_index(sc, i, index_at(sc + i));
+      __syncthreads();
+      // all loads of a batch first, then its LDS stores, so a 256-thread
+      // work-group gathers the sub-chunk in one memory round trip
+#pragma unroll
+      for (int u0 = 0; u0 < kPieces; u0 += kBatch) {
+        u32x4 kv_k[kBatch], kv_v[kBatch];
+        load_pieces(sidx, u0, kv_k, kv_v);
+        store_pieces(u0, kv_k, kv_v);
+      }
+      __syncthreads();
+      compute(n_here);
     }
   }
   l_run = sum_rows(l_run);
