@@ -57,14 +57,6 @@ __device__ __forceinline__ void require_loaded(const bf16x8& x) {
   asm volatile("" : : "v"(__builtin_bit_cast(u32x4, x)));
 }
 
-// Q^T as the B operand: column col of a query block = (token tok, head col & 7).
-__device__ __forceinline__ void load_q_block(const u16* __restrict__ qtok, int col, int grp,
-                                             bf16x8 (&qb)[4]) {
-  const u16* p = qtok + (col & 7) * kD + 8 * grp;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) qb[c] = as_bf16x8(load_u32x4(p + 32 * c));
-}
-
 // ---- attention kernel
 //
 // grid: B * Hkv * ceil(T / 16) work-groups of 256 threads.  A work-group takes
@@ -455,11 +447,14 @@ __global__ __launch_bounds__(kPThreads, QC == 1 ? 2 : 1) void full_prefill_kerne
 }
 
 // Importance pass.  grid: B * Hkv * ceil(T / 64) work-groups of 8 waves; a
-// work-group takes 64 chunk tokens, each wave 4 query blocks (2 tokens x 8
-// heads each), so every K operand read from LDS serves 64 query rows.
-// Here the MFMA computes S = Q . K^T (query rows, key columns): a lane holds 4
-// heads of one token for one key, and the max over the token's 8 heads is 3
-// in-lane steps and one exchange with the partner lane.
+// work-group takes 64 chunk tokens, each wave 8 of them as two row blocks of
+// 32 (4 tokens x 8 heads each), so every K operand read from LDS serves 64
+// query rows.  The MFMA is the 32x32x16 bf16 form computing S = Q . K^T
+// (query rows, key columns): a lane holds, for one key, 4 heads of each of its
+// block's 4 tokens, and the max over a token's 8 heads is 3 in-lane steps and
+// one exchange with the lane 32 away.  Beside a 32x32 MFMA the VALU has room
+// for about four instructions, four times what the 16x16x32 form leaves at the
+// same matrix rate, which is where the other group's epilogue runs.
 // The waves form two groups of four, one wave of each per SIMD, that take
 // turns: while one group runs a tile's MFMAs the other turns its previous
 // tile into importance values (VALU and stores), so the matrix cores stay
@@ -470,36 +465,46 @@ __global__ __launch_bounds__(kPThreads, QC == 1 ? 2 : 1) void full_prefill_kerne
 // Writes, for every row (b, t, g) it owns:
 //   y[row][j] = max_h(s2_h[j] - lse2_h) for older keys j < first_t, as
 //               round((y - ybase) 2^10) clamped to 0..65535, with ybase the
-//               row's top log-weight (over its 8 heads) minus 64 (when y is
-//               non-null);
+//               row's top log-weight (over its 8 heads) minus 64;
 //   kmax[b][g][tb] = the largest |k| over this work-group's share of the KV
 //               head's keys 0..S-1 (bf16 bits; when kmax is non-null): whole
 //               key tile i belongs to token block i % n_tblk when that block
 //               reads all of it, else to the last block, which reads every key.
 constexpr int kIWaves = 8;
 constexpr int kIThreads = 64 * kIWaves;
-constexpr int kIQB = 4;                        // query blocks per wave
-static_assert(kIWaves * 2 * kIQB == kImportanceTok, "64 chunk tokens per work-group");
+constexpr int kIMB = 2;                        // 32-row blocks (4 tokens) per wave
+static_assert(kIWaves * 4 * kIMB == kImportanceTok, "64 chunk tokens per work-group");
 
-// K tile in LDS as unpadded 256-byte rows, the 16-byte chunk c of row r at
-// slot c ^ (r & 15): the operand reads of 16 consecutive rows (one chunk each)
-// cover all banks once, and one LDS-direct load fills 4 whole rows.
-__device__ __forceinline__ bf16x8 lds_k_swizzled(const u16* kt, int sub, int c, int col, int grp) {
-  const int slot = (4 * c + grp) ^ col;
-  return as_bf16x8(*reinterpret_cast<const u32x4*>(kt + (16 * sub + col) * kD + 8 * slot));
-}
+constexpr int kIRing = 4;                      // K tiles in LDS (3 in flight)
+constexpr int kIAhead = 6;                     // K operand reads in flight per wave
 
-__device__ __forceinline__ void wait_lgkm_all() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0), other counters untouched
+// vmcnt waits (the other counters untouched): all of this wave's vector
+// memory operations; all but the last 4 (the prologue's tiles 1 and 2: tile 0
+// has landed); all but the last 16 (tile it + 1 landed, in the steady tile
+// loop).  The counts hold only for the issue order the tile loop lays out, so
+// no memory access may cross a wait (the empty asm statements).
+template <int kImm>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kImm);
+  asm volatile("" ::: "memory");
 }
+__device__ __forceinline__ void wait_vm_all() { wait_vm<0x0F70>(); }
+__device__ __forceinline__ void wait_vm_ring_start() { wait_vm<0x0F74>(); }
+__device__ __forceinline__ void wait_vm_ring_steady() { wait_vm<0x4F70>(); }
 
 // A work-group barrier that waits for no memory operation: the importance
 // values' global stores stay in flight across it.  Whatever must be visible
-// past it is waited for explicitly (the tile's LDS writes), and the empty asm
-// statements keep the compiler from moving memory accesses across it.
+// past it is waited for explicitly (the tile's LDS writes); the empty asm
+// statements keep the compiler from moving memory accesses across it, and the
+// scheduling barriers keep every other instruction on its side too (left to
+// itself the scheduler sinks a phase's later MFMAs past the barrier, into the
+// phase meant for the other group's).
 __device__ __forceinline__ void phase_barrier() {
   asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
   asm volatile("" ::: "memory");
 }
 
@@ -507,16 +512,24 @@ __global__ __launch_bounds__(kIThreads, 1) void prefill_importance_kernel(
     const u16* __restrict__ q, const u16* __restrict__ k, const double* __restrict__ lse2,
     const float* __restrict__ ytop_h, u16* __restrict__ y, uint32_t* __restrict__ kmax,
     int64_t S, int64_t Spad, int T, int Hkv, int w, int n_tblk, float c2_hi, int64_t kvp) {
-  __shared__ __align__(16) u16 kbuf[2][kPKeys * kD];
+  (void)w;
+  // the ring of K tiles: four separate arrays, each named at compile time
+  // wherever it is filled or read, so that the compiler can tell a tile's
+  // reads from the fills in flight into the others (and waits for none)
+  __shared__ __align__(16) u16 kq0[kPKeys * kD];
+  __shared__ __align__(16) u16 kq1[kPKeys * kD];
+  __shared__ __align__(16) u16 kq2[kPKeys * kD];
+  __shared__ __align__(16) u16 kq3[kPKeys * kD];
   __shared__ uint32_t s_kmax[kIWaves];
-  constexpr int QB = kIQB;
+  constexpr int MB = kIMB;
   constexpr int kTok = kImportanceTok;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  // waves w and w + 4 share a SIMD; the group is wave-uniform (read as such)
-  const bool group_b = __builtin_amdgcn_readfirstlane(wave) >= kIWaves / 2;
-  const int col = lane & 15, grp = lane >> 4;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  // waves w and w + 4 share a SIMD; the group is wave-uniform
+  const bool group_b = wave_u >= kIWaves / 2;
+  const int n = lane & 31, hf = lane >> 5;
   const int lin = xcd_linear(blockIdx.x, gridDim.x);
   const int tb = lin % n_tblk;
   const int bg = lin / n_tblk;
@@ -524,43 +537,48 @@ __global__ __launch_bounds__(kIThreads, 1) void prefill_importance_kernel(
   const int Hq = Hkv * kG;
   const u16* kr = k + static_cast<size_t>(bg) * kvp * kD;
   const int64_t pos0 = S - T;
-  bf16x8 qop[QB][4];
-  bool t_ok[QB];
-  int64_t P[QB], first[QB];
+  const int tw = tb * kTok + 4 * MB * wave;   // this wave's first token
+  // Q as the A operand: row n of block mb = (token tw + 4 mb + (n >> 3),
+  // head n & 7), k-step ks = dims 16 ks + 8 hf .. + 7
+  bf16x8 qop[MB][8];
   // y in fixed-point steps plus 0.5 is s c2 2^10 + (0.5 - 2^10 (lse2_h + ybase)):
-  // one fma per head
-  float nl2r[QB][4];     // 0.5 - 2^10 (lse2_h + ybase) for the lane's 4 heads
-  u16* yrow[QB];
+  // one fma per head.  nl2r[mb][j][i] is that offset for token tw + 4 mb + j,
+  // head 4 hf + i (the lane's rows of S)
+  float nl2r[MB][4][4];
+  // after the head max the low half of the wave holds tokens 4 mb + {0, 2},
+  // the high half 4 mb + {1, 3}: the rows this lane stores
+  u16* yrow[MB][2];
 #pragma unroll
-  for (int qbk = 0; qbk < QB; ++qbk) {
-    // the A operand: query row col = (token .. + (col >> 3), head col & 7)
-    int tq = tb * kTok + 2 * QB * wave + 2 * qbk + (col >> 3);
-    tq = tq < T ? tq : T - 1;
-    load_q_block(q + (static_cast<size_t>(b) * T + tq) * Hq * kD + static_cast<size_t>(g) * kG * kD,
-                 col, grp, qop[qbk]);
-    // this lane's rows of S: 4*grp + i = (token .. + (grp >> 1), head 4*(grp & 1) + i)
-    int t = tb * kTok + 2 * QB * wave + 2 * qbk + (grp >> 1);
-    t_ok[qbk] = t < T;
-    t = t_ok[qbk] ? t : T - 1;
-    P[qbk] = pos0 + t;
-    first[qbk] = max(static_cast<int64_t>(0), P[qbk] - w + 1);
-    const size_t row = (static_cast<size_t>(b) * T + t) * Hkv + g;
-    float yt = -INFINITY;
-    for (int h = 0; h < kG; ++h) yt = fmaxf(yt, ytop_h[row * kG + h]);
-    const float ybase = yt - kYRange;
-    // 2^10 ybase is exact, and so is its sum with 0.5 (|ybase| < 2^12)
-    const float yoff = 0.5f - ybase * static_cast<float>(1 << kYFixBits);
+  for (int mb = 0; mb < MB; ++mb) {
+    const int tq = min(tw + 4 * mb + (n >> 3), T - 1);   // past the chunk: repeat the last token
+    const u16* qp = q + (static_cast<size_t>(b) * T + tq) * Hq * kD +
+                    (static_cast<size_t>(g) * kG + (n & 7)) * kD + 8 * hf;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      nl2r[qbk][i] = fmaf(-static_cast<float>(lse2[row * kG + 4 * (grp & 1) + i]),
-                          static_cast<float>(1 << kYFixBits), yoff);
-    yrow[qbk] = y ? y + row * Spad : nullptr;
+    for (int ks = 0; ks < 8; ++ks) qop[mb][ks] = as_bf16x8(load_u32x4(qp + 16 * ks));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = min(tw + 4 * mb + j, T - 1);
+      const size_t row = (static_cast<size_t>(b) * T + t) * Hkv + g;
+      float yt = -INFINITY;
+      for (int h = 0; h < kG; ++h) yt = fmaxf(yt, ytop_h[row * kG + h]);
+      const float ybase = yt - kYRange;
+      // 2^10 ybase is exact, and so is its sum with 0.5 (|ybase| < 2^12)
+      const float yoff = 0.5f - ybase * static_cast<float>(1 << kYFixBits);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        nl2r[mb][j][i] = fmaf(-static_cast<float>(lse2[row * kG + 4 * hf + i]),
+                              static_cast<float>(1 << kYFixBits), yoff);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int t = min(tw + 4 * mb + 2 * u + hf, T - 1);
+      const size_t row = (static_cast<size_t>(b) * T + t) * Hkv + g;
+      yrow[mb][u] = y + row * Spad + 2 * n;   // at the lane's keys 2 n, 2 n + 1
+    }
   }
   const int t_last = min(T - 1, tb * kTok + kTok - 1);
   const int64_t p_last = pos0 + t_last;
   const int n_tiles = static_cast<int>((p_last + kPKeys) / kPKeys);
-  // after the head max a lane owns key subtiles 2*(grp & 1) and 2*(grp & 1) + 1
-  const int sub0 = 2 * (grp & 1);
   const float c2s = c2_hi * static_cast<float>(1 << kYFixBits);   // exact
   // this work-group's share of max |k|: whole tiles i with i % n_tblk == tb
   // (or, when that block does not read all of tile i, the last block's)
@@ -571,131 +589,220 @@ __global__ __launch_bounds__(kIThreads, 1) void prefill_importance_kernel(
   };
   u16x2 kabs{0, 0};
 
-  // this wave's 8 rows of a tile, staged through registers: lane l holds
-  // bytes 32 (l & 7) .. + 31 of row 8 wave + (l >> 3)
-  const int srow_ = 8 * wave + (lane >> 3);
-  const int sc0 = 2 * (lane & 7);
-  u32x4 stg[2];
-  auto stage_load = [&](int64_t key0) {
-    const int64_t key = min(key0 + srow_, p_last);
-    const u16* src = kr + key * kD + 8 * sc0;
-    stg[0] = load_u32x4(src);
-    stg[1] = load_u32x4(src + 8);
+  // Tiles travel straight from memory to LDS, kIRing - 1 tiles ahead of use
+  // (tile i in buffer i % kIRing).  A tile is unpadded 256-byte rows, the
+  // 16-byte chunk c of row r at slot c ^ (r & 15): the operand reads of 16
+  // consecutive rows (one chunk each) cover all banks once.  Wave w fills
+  // rows 8 w .. 8 w + 7, 4 rows (1 KB) per load: lane l writes slot l & 15 of
+  // row 8 w + 4 j + (l >> 4), so it reads that row's chunk (l & 15) ^ (row &
+  // 15).  Rows past p_last repeat it (their importance values land in the
+  // unread tail), so every load stays inside the KV head's keys.  The loads
+  // are the buffer form (a resource based at the tile's first row, 32-bit
+  // offsets within it), not the flat-global one: while a flat load is
+  // outstanding the compiler cannot count LDS reads and waits for all of
+  // them, which would undo the operand prefetch in the MFMA phase.
+  auto ring = [&](auto slot_tag) -> u16* {
+    constexpr int kS = decltype(slot_tag)::value % kIRing;
+    return kS == 0 ? kq0 : kS == 1 ? kq1 : kS == 2 ? kq2 : kq3;
   };
-  auto stage_store = [&](u16* kt, int tile) {
-    u16* dst = kt + srow_ * kD;
-    *reinterpret_cast<u32x4*>(dst + 8 * (sc0 ^ (srow_ & 15))) = stg[0];
-    *reinterpret_cast<u32x4*>(dst + 8 * ((sc0 + 1) ^ (srow_ & 15))) = stg[1];
-    if (kmax && tile < n_tiles && owns_tile(tile)) {
+  // tile is in buffer kSlot (tile % kIRing)
+  auto fill = [&](int tile, auto slot_tag) {
+    u16* dst = ring(slot_tag);
+    const int64_t key0 = static_cast<int64_t>(tile) * kPKeys;
+    const int64_t kf = min(key0, p_last);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<u16*>(kr + kf * kD), 0, kPKeys * kD * 2, 0x00020000);
 #pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          kabs = __builtin_elementwise_max(kabs, __builtin_bit_cast(u16x2, stg[u][e] & 0x7FFF7FFFu));
+    for (int j = 0; j < 2; ++j) {
+      const int r = 8 * wave_u + 4 * j + (lane >> 4);
+      const int row = static_cast<int>(min(key0 + r, p_last) - kf);   // 0 .. 63
+      const uint32_t off = 256u * row + 16u * ((lane & 15) ^ (r & 15));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_ptr(dst, (8 * wave_u + 4 * j) * 256), 16, off, 0, 0, 0);
     }
+    asm volatile("" ::: "memory");   // issued before whatever follows (the waits count on it)
   };
-
-  // prologue: tile 0 by every wave; group B loads its rows of tile 1 in the
-  // phase it spends behind group A
-  stage_load(0);
-  stage_store(kbuf[0], 0);
-#pragma unroll
-  for (int qbk = 0; qbk < QB; ++qbk)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) require_loaded(qop[qbk][c]);
-  __syncthreads();
-  // the tile loop, as a separate copy per group: each group's copy has only
-  // its own loads and stores in flight, so the compiler waits on exactly those
-  // a tile's MFMAs: S for this wave's 4 query blocks x 64 keys
-  auto mfma_phase = [&](const u16* kt, f32x4 (&sacc)[QB][4]) {
-#pragma unroll
-    for (int sub = 0; sub < 4; ++sub) {
-#pragma unroll
-      for (int qbk = 0; qbk < QB; ++qbk) sacc[qbk][sub] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const bf16x8 kb = lds_k_swizzled(kt, sub, c, col, grp);
-#pragma unroll
-        for (int qbk = 0; qbk < QB; ++qbk)
-          sacc[qbk][sub] = mfma_16x16x32(qop[qbk][c], kb, sacc[qbk][sub]);
-      }
-    }
-  };
-  // a tile's epilogue: importance values from S, and their stores
-  auto epilogue = [&](const f32x4 (&sacc)[QB][4], int64_t key0) {
-#pragma unroll
-    for (int qbk = 0; qbk < QB; ++qbk) {
-      // y per (token, key), in fixed-point steps plus 0.5: max over the 8
-      // heads = 4 here x the partner lane.  One fma per head: the scale's low
-      // part (below 1e-7 of s c2) is dropped; the selection allows for it and
-      // re-ranks every key near its threshold in float64
-      float yv[4];
-#pragma unroll
-      for (int sub = 0; sub < 4; ++sub) {
-        float m = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaf(sacc[qbk][sub][i], c2s, nl2r[qbk][i]));
-        // the partner lane (lane ^ 16) holds the other 4 heads: one VALU
-        // row swap gives both lanes both halves
-        const auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m),
-                                                         false, false);
-        yv[sub] = fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
-      }
+  // this work-group's share of max |k|, from the rows this wave filled (the
+  // tile has landed and is visible): lane l takes chunks 2 (l & 7) and
+  // 2 (l & 7) + 1 of row 8 w + (l >> 3)
+  auto take_kmax = [&](int tile, const u16* kt) {
+    if (kmax && owns_tile(tile)) {
+      const int r = 8 * wave_u + (lane >> 3);
+      const int c0 = 2 * (lane & 7);
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const int sub = sub0 + u;
-        const float yy = sub == 0 ? yv[0] : sub == 1 ? yv[1] : sub == 2 ? yv[2] : yv[3];
-        const int64_t key = key0 + 16 * sub + col;
-        // clamp to 0..65535, then truncate: rounds to nearest
-        const u16 v = static_cast<u16>(static_cast<uint32_t>(__builtin_amdgcn_fmed3f(yy, 0.f, 65535.f)));
-        // every lane stores (a fixed count of stores per phase, so the
-        // tile loads can be waited for alone): keys at or past first_t
-        // land in the row's unread tail (key < Spad), and a block past
-        // the chunk's end repeats the last token, value for value
-        yrow[qbk][key] = v;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(kt + r * kD + 8 * ((c0 + u) ^ (r & 15)));
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          kabs = __builtin_elementwise_max(kabs, __builtin_bit_cast(u16x2, v[e] & 0x7FFF7FFFu));
       }
     }
   };
-  // The tile loops, one per group, each laid out so that a tile's staging
-  // loads and LDS writes fall in one loop iteration: the compiler then waits
-  // for the loads alone, not for the importance stores issued after them.
-  if (!group_b) {
-    // phases 2 it (MFMAs of tile it, loads of tile it + 1) and 2 it + 1
-    // (epilogue of tile it, LDS writes of tile it + 1)
-    for (int it = 0; it < n_tiles; ++it) {
-      const int64_t key0 = static_cast<int64_t>(it) * kPKeys;
-      f32x4 sacc[QB][4];
-      // past the last tile the rows repeat key p_last and the LDS writes land
-      // in a buffer nobody reads again: unconditional, so every load is
-      // waited for on every path
-      stage_load(key0 + kPKeys);
-      asm volatile("" ::: "memory");   // issue the loads before the phase's work
-      mfma_phase(kbuf[it & 1], sacc);
-      phase_barrier();
-      stage_store(kbuf[(it & 1) ^ 1], it + 1);
-      epilogue(sacc, key0);
-      wait_lgkm_all();
-      phase_barrier();
-    }
-    phase_barrier();   // group B's last phase
-  } else {
-    // phases 2 it (epilogue of tile it - 1, loads of tile it + 1) and 2 it + 1
-    // (MFMAs of tile it, LDS writes of tile it + 1); the first of these phases
-    // has no epilogue and puts group B one phase behind group A
-    f32x4 sacc[QB][4];
-    for (int it = 0; it < n_tiles; ++it) {
-      const int64_t key0 = static_cast<int64_t>(it) * kPKeys;
-      stage_load(key0 + kPKeys);
-      if (it > 0) epilogue(sacc, key0 - kPKeys);
-      phase_barrier();
-      stage_store(kbuf[(it & 1) ^ 1], it + 1);
-      mfma_phase(kbuf[it & 1], sacc);
-      wait_lgkm_all();
-      phase_barrier();
-    }
-    epilogue(sacc, static_cast<int64_t>(n_tiles - 1) * kPKeys);
-    phase_barrier();
+  // K as the B operand: column n of key block kb is key 2 n + kb of the tile,
+  // so that a lane's two blocks hold two neighbouring keys and its importance
+  // values go out as one 32-bit store.  K-step ks reads chunk 2 ks + hf of
+  // row 2 n + kb, at byte kbase[kb] ^ 32 ks (the 8 rows that one 128-byte
+  // read phase touches, 2 n + kb for 8 consecutive n, still fall on 8
+  // different slots)
+  uint32_t kbase[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int r = 2 * n + kb;
+    kbase[kb] = 256u * r + 16u * (hf ^ (r & 15));
   }
+  auto k_operand = [&](const u16* kt, int kb, int ks) {
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(kt) +
+                                                     (kbase[kb] ^ (32u * ks))));
+  };
+
+  // prologue: the first kIRing - 1 tiles; tile 0 must have landed
+  using Slot0 = std::integral_constant<int, 0>;
+  using Slot1 = std::integral_constant<int, 1>;
+  using Slot2 = std::integral_constant<int, 2>;
+  using Slot3 = std::integral_constant<int, 3>;
+  fill(0, Slot0{});
+  fill(1, Slot1{});
+  fill(2, Slot2{});
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) require_loaded(qop[mb][ks]);
+  wait_vm_ring_start();
+  __syncthreads();
+  // a tile's MFMAs: S for this wave's 2 row blocks x 2 key blocks
+  auto mfma_phase = [&](const u16* kt, f32x16 (&sacc)[MB][2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) sacc[mb][kb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 kop = k_operand(kt, kb, ks);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) sacc[mb][kb] = mfma_32x32x16(qop[mb][ks], kop, sacc[mb][kb]);
+      }
+    }
+    // the order of issue: kIAhead operand reads first, then one more after
+    // every MFMA pair, so that each read is issued kIAhead - 1 pairs (about
+    // 64 clocks each) before its MFMAs, which covers LDS latency under the
+    // other waves' reads
+#pragma unroll
+    for (int i = 0; i < kIAhead; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+    for (int i = 0; i < 16 - kIAhead; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * kIAhead, 0);
+  };
+  // a tile's epilogue: importance values from S, and their stores.  In S's
+  // accumulators register 4 j + i of lane (n, hf) is row 8 j + 4 hf + i of
+  // the block: token j, head 4 hf + i, key column n (key 2 n + kb)
+  auto epilogue = [&](const f32x16 (&sacc)[MB][2], int64_t key0) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      uint32_t yv[2][2];   // [kb][token pair: 0 = tokens hf, 1 = tokens 2 + hf]
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        // y per (token, key), in fixed-point steps plus 0.5: max over the 8
+        // heads = 4 here x the lane 32 away.  One fma per head: the scale's
+        // low part (below 1e-7 of s c2) is dropped; the selection allows for
+        // it and re-ranks every key near its threshold in float64.  The max
+        // starts at 0, the clamp's lower end, so what crosses lanes is a
+        // non-negative float (or -0), whose bits order as signed integers
+        uint32_t m[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float v = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v = fmaxf(v, fmaf(sacc[mb][kb][4 * j + i], c2s, nl2r[mb][j][i]));
+          m[j] = __float_as_uint(v);
+        }
+        // the swap trades the high half of its first operand for the low half
+        // of its second: the low half then holds both head halves of token j,
+        // the high half both of token j + 1
+        const auto p01 = __builtin_amdgcn_permlane32_swap(m[0], m[1], false, false);
+        const auto p23 = __builtin_amdgcn_permlane32_swap(m[2], m[3], false, false);
+        // the clamp's upper end, 65535 (as float bits), then truncate: rounds
+        // to nearest
+        constexpr int kTop = 0x477FFF00;
+        const int y01 = min(max(static_cast<int>(p01[0]), static_cast<int>(p01[1])), kTop);
+        const int y23 = min(max(static_cast<int>(p23[0]), static_cast<int>(p23[1])), kTop);
+        yv[kb][0] = static_cast<uint32_t>(__int_as_float(y01));
+        yv[kb][1] = static_cast<uint32_t>(__int_as_float(y23));
+      }
+      // Every lane stores (a fixed count of stores per phase, so the tile
+      // loads can be waited for alone): keys at or past first_t land in the
+      // row's unread tail (key < Spad), and a block past the chunk's end
+      // repeats the last token, value for value
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        *reinterpret_cast<uint32_t*>(yrow[mb][u] + key0) = yv[0][u] | (yv[1][u] << 16);
+    }
+  };
+  // The tile loops, one per group.  Phase 2 it is group A's MFMAs of tile
+  // it beside group B's epilogue of tile it - 1, phase 2 it + 1 group A's
+  // epilogue of tile it beside group B's MFMAs of tile it; a barrier ends
+  // every phase.  Tile i's buffer is free once tile i - kIRing's last reads
+  // (group B's MFMAs, phase 2 i - 7) are over: both groups fill it in phase
+  // 2 i - 6 (group A before its MFMAs of tile i - 3, group B before its
+  // epilogue of tile i - 4).  Tile it + 1 is read from phase 2 it + 2 on, so
+  // every wave waits for its loads of that tile before the barrier that ends
+  // phase 2 it + 1.  Per tile a wave issues its 2 loads and then its
+  // epilogue's 4 stores, and vector memory operations count down in issue
+  // order, so once the pattern is steady tile it + 1's loads are done when at
+  // most 16 operations are outstanding: the stores and the later tiles' loads
+  // stay in flight.  Fills past the last tile repeat key p_last into buffers
+  // that nobody reads again.  Both loops are unrolled by the ring's length,
+  // so that every buffer is named statically.
+  if (!group_b) {
+    auto step = [&](int it, auto slot_tag) {
+      constexpr int kS = decltype(slot_tag)::value;
+      f32x16 sacc[MB][2];
+      fill(it + kIRing - 1, std::integral_constant<int, kS + kIRing - 1>{});
+      take_kmax(it, ring(slot_tag));
+      mfma_phase(ring(slot_tag), sacc);
+      phase_barrier();
+      epilogue(sacc, static_cast<int64_t>(it) * kPKeys);
+      if (it >= 2) wait_vm_ring_steady(); else wait_vm_all();
+      phase_barrier();
+    };
+    for (int it = 0; it < n_tiles; it += kIRing) {
+      step(it, Slot0{});
+      if (it + 1 >= n_tiles) break;
+      step(it + 1, Slot1{});
+      if (it + 2 >= n_tiles) break;
+      step(it + 2, Slot2{});
+      if (it + 3 >= n_tiles) break;
+      step(it + 3, Slot3{});
+    }
+    phase_barrier();   // group B's last epilogue
+  } else {
+    // phase 0: group A's MFMAs of tile 0.  Its fill is waited for at once
+    // (once per work-group), so that no fill is pending where the loop starts
+    fill(kIRing - 1, Slot3{});
+    wait_vm_all();
+    phase_barrier();
+    auto step = [&](int it, auto slot_tag) {
+      f32x16 sacc[MB][2];
+      take_kmax(it, ring(slot_tag));
+      mfma_phase(ring(slot_tag), sacc);
+      if (it >= 3) wait_vm_ring_steady(); else wait_vm_all();
+      phase_barrier();
+      fill(it + kIRing, slot_tag);   // into the buffer this tile leaves
+      epilogue(sacc, static_cast<int64_t>(it) * kPKeys);
+      phase_barrier();
+    };
+    for (int it = 0; it < n_tiles; it += kIRing) {
+      step(it, Slot0{});
+      if (it + 1 >= n_tiles) break;
+      step(it + 1, Slot1{});
+      if (it + 2 >= n_tiles) break;
+      step(it + 2, Slot2{});
+      if (it + 3 >= n_tiles) break;
+      step(it + 3, Slot3{});
+    }
+  }
+  wait_vm_all();   // no fill may land after the work-group's LDS is released
   if (kmax) {
     uint32_t m = max(static_cast<uint32_t>(kabs[0]), static_cast<uint32_t>(kabs[1]));
 #pragma unroll
