@@ -739,21 +739,21 @@ __global__ __launch_bounds__(kIThreads, 1) void prefill_importance_kernel(
         *reinterpret_cast<uint32_t*>(yrow[mb][u] + key0) = yv[0][u] | (yv[1][u] << 16);
     }
   };
-  // The tile loops, one per group.  Phase 2 it is group A's MFMAs of tile
-  // it beside group B's epilogue of tile it - 1, phase 2 it + 1 group A's
-  // epilogue of tile it beside group B's MFMAs of tile it; a barrier ends
-  // every phase.  Tile i's buffer is free once tile i - kIRing's last reads
-  // (group B's MFMAs, phase 2 i - 7) are over: both groups fill it in phase
-  // 2 i - 6 (group A before its MFMAs of tile i - 3, group B before its
-  // epilogue of tile i - 4).  Tile it + 1 is read from phase 2 it + 2 on, so
-  // every wave waits for its loads of that tile before the barrier that ends
-  // phase 2 it + 1.  Per tile a wave issues its 2 loads and then its
-  // epilogue's 4 stores, and vector memory operations count down in issue
-  // order, so once the pattern is steady tile it + 1's loads are done when at
-  // most 16 operations are outstanding: the stores and the later tiles' loads
-  // stay in flight.  Fills past the last tile repeat key p_last into buffers
-  // that nobody reads again.  Both loops are unrolled by the ring's length,
-  // so that every buffer is named statically.
+  // The tile loops, one per group, one barrier per tile.  Between barriers
+  // it and it + 1 group A runs the MFMAs of tile it and then its epilogue,
+  // group B its epilogue of tile it - 1 and then the MFMAs of tile it, so
+  // that on every SIMD one wave's epilogue runs beside the other's MFMAs.
+  // Tile i's buffer is free once tile i - kIRing's reads (both groups' MFMAs,
+  // before barrier i - kIRing + 1) are over: both groups fill it right after
+  // barrier i - 3.  Tile it + 1 is read after barrier it + 1, so every wave
+  // waits for its loads of that tile before that barrier.  Per tile a wave
+  // issues its 2 loads and then its epilogue's 4 stores, and vector memory
+  // operations count down in issue order, so once the pattern is steady tile
+  // it + 1's loads are done when at most 16 operations are outstanding: the
+  // stores and the later tiles' loads stay in flight.  Fills past the last
+  // tile repeat key p_last into buffers that nobody reads again.  Both loops
+  // are unrolled by the ring's length, so that every buffer is named
+  // statically.
   if (!group_b) {
     auto step = [&](int it, auto slot_tag) {
       constexpr int kS = decltype(slot_tag)::value;
@@ -761,7 +761,6 @@ __global__ __launch_bounds__(kIThreads, 1) void prefill_importance_kernel(
       fill(it + kIRing - 1, std::integral_constant<int, kS + kIRing - 1>{});
       take_kmax(it, ring(slot_tag));
       mfma_phase(ring(slot_tag), sacc);
-      phase_barrier();
       epilogue(sacc, static_cast<int64_t>(it) * kPKeys);
       if (it >= 2) wait_vm_ring_steady(); else wait_vm_all();
       phase_barrier();
@@ -775,13 +774,12 @@ __global__ __launch_bounds__(kIThreads, 1) void prefill_importance_kernel(
       if (it + 3 >= n_tiles) break;
       step(it + 3, Slot3{});
     }
-    phase_barrier();   // group B's last epilogue
   } else {
-    // phase 0: group A's MFMAs of tile 0.  Its fill is waited for at once
-    // (once per work-group), so that no fill is pending where the loop starts
+    // group B's share of tile 3 (group A's comes with its first step); waited
+    // for at once (once per work-group), so that no fill is pending where
+    // the loop starts
     fill(kIRing - 1, Slot3{});
     wait_vm_all();
-    phase_barrier();
     auto step = [&](int it, auto slot_tag) {
       f32x16 sacc[MB][2];
       take_kmax(it, ring(slot_tag));
@@ -790,7 +788,6 @@ __global__ __launch_bounds__(kIThreads, 1) void prefill_importance_kernel(
       phase_barrier();
       fill(it + kIRing, slot_tag);   // into the buffer this tile leaves
       epilogue(sacc, static_cast<int64_t>(it) * kPKeys);
-      phase_barrier();
     };
     for (int it = 0; it < n_tiles; it += kIRing) {
       step(it, Slot0{});
