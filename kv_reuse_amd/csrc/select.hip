@@ -52,6 +52,9 @@ __device__ __forceinline__ int64_t row_first(int P, int w) {
 }
 
 
+// Two packed 16-bit values.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
 // Histogram bin of a candidate's exact log2 importance (monotone in y).
 __device__ __forceinline__ int cand_bin(double y, float ybase) {
   return static_cast<int>(key_from_log2(static_cast<float>(y), ybase) >> kBinShift);
@@ -2084,19 +2087,20 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
         // dominant keys for the refinement
         constexpr int kV = 32;
         const int lpb = bs / kV;   // lanes per block (0: bs = 16)
-        const int64_t prounds = (first + kV * kRowThreads - 1) / (kV * kRowThreads);
-        auto load_pround = [&](int64_t rr, u32x4 (&yv)[4]) {
-          const int64_t i0 = kV * (static_cast<int64_t>(tid) + rr * kRowThreads);
+        // (32-bit round counts: the loop's test stays a scalar compare)
+        const int prounds = static_cast<int>((first + kV * kRowThreads - 1) / (kV * kRowThreads));
+        // The row as a buffer resource of whole 16-byte groups (a load past its
+        // end reads zeros) and two named register sets, loaded a round ahead:
+        // no branch and no copy between a load and its use.
+        const auto yrs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<u16*>(yr), 0, static_cast<int>(2 * ((first + 7) & ~int64_t{7})), 0x00020000);
+        auto load_pround = [&](int rr, u32x4 (&yv)[4]) {
+          const int off = 2 * kV * (tid + rr * kRowThreads);
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            yv[u] = i0 + 8 * u < first ? *reinterpret_cast<const u32x4*>(yr + i0 + 8 * u)
-                                       : u32x4{0u, 0u, 0u, 0u};
+          for (int u = 0; u < 4; ++u) yv[u] = __builtin_amdgcn_raw_buffer_load_b128(yrs, off + 16 * u, 0, 0);
         };
-        u32x4 ycur[4], ynxt[4];
-        if (prounds > 0) load_pround(0, ycur);
-        for (int64_t rr = 0; rr < prounds; ++rr) {
-          const int64_t i0 = kV * (static_cast<int64_t>(tid) + rr * kRowThreads);
-          if (rr + 1 < prounds) load_pround(rr + 1, ynxt);
+        auto bround = [&](int rr, const u32x4 (&ycur)[4]) __attribute__((always_inline)) {
+          const int64_t i0 = kV * (static_cast<int64_t>(tid) + static_cast<int64_t>(rr) * kRowThreads);
           const int nv = static_cast<int>(max(static_cast<int64_t>(0), min(static_cast<int64_t>(kV), first - i0)));
           uint32_t m0 = 0, m1 = 0, md = 0;
 #pragma unroll
@@ -2127,8 +2131,16 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
               atomicAdd(&lh[m >> kVBinShift], 1u);
             }
           }
-#pragma unroll
-          for (int u = 0; u < 4; ++u) ycur[u] = ynxt[u];
+        };
+        // two rounds per iteration, no exit between them (an odd count's last
+        // round lies past the row: every value masked)
+        u32x4 ya[4], yb[4];
+        load_pround(0, ya);
+        for (int rr = 0; rr < prounds; rr += 2) {
+          load_pround(rr + 1, yb);
+          bround(rr, ya);
+          load_pround(rr + 2, ya);
+          bround(rr + 1, yb);
         }
       }
       refine_row();   // (l2s refined before the band is ranked with it)
@@ -2282,29 +2294,57 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
         // 32 values per thread and round here (four 16-byte loads), so half as
         // many rounds, and barriers, as the second pass below
         constexpr int kV = 32;
-        const int64_t prounds = (first + kV * kRowThreads - 1) / (kV * kRowThreads);
-        auto load_pround = [&](int64_t rr, u32x4 (&yv)[4]) {
-          const int64_t i0 = kV * (static_cast<int64_t>(tid) + rr * kRowThreads);
+        // (32-bit round counts: the loop's test stays a scalar compare)
+        const int prounds = static_cast<int>((first + kV * kRowThreads - 1) / (kV * kRowThreads));
+        // The row as a buffer resource of whole 16-byte groups: a load past
+        // its end reads zeros, so the loads need no branch (values of the last
+        // group past first are masked below).  The next round's loads go to
+        // the other of two named register sets before this round is processed,
+        // so that no copy and no branch stands between a load and its use and
+        // the waits count only the loads they need.
+        const auto yrs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<u16*>(yr), 0, static_cast<int>(2 * ((first + 7) & ~int64_t{7})), 0x00020000);
+        auto load_pround = [&](int rr, u32x4 (&yv)[4]) {
+          const int off = 2 * kV * (tid + rr * kRowThreads);
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            yv[u] = i0 + 8 * u < first ? *reinterpret_cast<const u32x4*>(yr + i0 + 8 * u)
-                                       : u32x4{0u, 0u, 0u, 0u};
+          for (int u = 0; u < 4; ++u) yv[u] = __builtin_amdgcn_raw_buffer_load_b128(yrs, off + 16 * u, 0, 0);
         };
         auto val_at = [](const u32x4 (&yv)[4], int e) -> uint32_t {
           const uint32_t word = yv[e >> 3][(e >> 1) & 3];
           return (e & 1) ? (word >> 16) : (word & 0xFFFFu);
         };
-        u32x4 ycur[4], ynxt[4];
-        if (prounds > 0) load_pround(0, ycur);
-        for (int64_t rr = 0; rr < prounds; ++rr) {
+        auto pround = [&](int rr, const u32x4 (&ycur)[4]) __attribute__((always_inline)) {
           const int64_t i0 = kV * (static_cast<int64_t>(tid) + rr * kRowThreads);
-          if (rr + 1 < prounds) load_pround(rr + 1, ynxt);
           const int nv = static_cast<int>(min(static_cast<int64_t>(kV), first - i0));
-          int fl = *static_cast<volatile int*>(&s_floor);
+          // (an LDS atomic read: a volatile one through a generic pointer would
+          // be a flat load, and its wait would also wait for the prefetch)
+          int fl = __hip_atomic_load(&s_floor, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          // After the first round the floor sits near the row's k-th value and
+          // most of a thread's kV values lie below everything that counts
+          // (the floor's bin, the list's reach, the dominant value): their
+          // largest, in packed 16-bit maxima, lets the thread skip them all
+          // (exactly: a skipped value would add no count and no list entry).
+          // The maximum is taken in every round: it reads all the round's
+          // registers outside any branch, so that their loads are waited for
+          // here and none is left pending at the loop's head.
+          u16x2 m2{0, 0};
 #pragma unroll
-          for (int e = 0; e < kV; ++e) {
-            const int bn = static_cast<int>(val_at(ycur, e) >> kVBinShift);
-            if (e < nv && bn >= fl) atomicAdd(&lh[bn], 1u);
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              // (a plain copy first: a vector element is not an object to
+              // reinterpret in place)
+              const uint32_t word = ycur[u][e];
+              m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, word));
+            }
+          const int mx = max(static_cast<int>(m2[0]), static_cast<int>(m2[1]));
+          const bool skip = (rr > 0) & (mx < min((fl << kVBinShift) - E, vdom));
+          if (!skip) {
+#pragma unroll
+            for (int e = 0; e < kV; ++e) {
+              const int bn = static_cast<int>(val_at(ycur, e) >> kVBinShift);
+              if (e < nv && bn >= fl) atomicAdd(&lh[bn], 1u);
+            }
           }
           if (rr == 0) {
             __syncthreads();
@@ -2317,11 +2357,13 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
           }
           const int vmin = (fl << kVBinShift) - E;
           uint32_t ml = 0, md = 0;
+          if (!skip) {
 #pragma unroll
-          for (int e = 0; e < kV; ++e) {
-            const int v = static_cast<int>(val_at(ycur, e));
-            ml |= static_cast<uint32_t>(e < nv && v >= vmin) << e;
-            md |= static_cast<uint32_t>(e < nv && v >= vdom) << e;
+            for (int e = 0; e < kV; ++e) {
+              const int v = static_cast<int>(val_at(ycur, e));
+              ml |= static_cast<uint32_t>(e < nv && v >= vmin) << e;
+              md |= static_cast<uint32_t>(e < nv && v >= vdom) << e;
+            }
           }
           for (uint32_t m = md; m; m &= m - 1) list_dom(i0 + __builtin_ctz(m));   // rare
           uint32_t ol, o_dummy, tot, t_dummy;
@@ -2344,8 +2386,19 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
               ++ol;
             }
           }
-#pragma unroll
-          for (int u = 0; u < 4; ++u) ycur[u] = ynxt[u];
+        };
+        u32x4 ya[4], yb[4];
+        load_pround(0, ya);
+        // Two rounds per iteration and no exit between them, so that every
+        // path back to the loop's head has used the loads it issued: with an
+        // odd number of rounds the last one lies past the row, reads zeros and
+        // counts and lists nothing (every value is masked), at the cost of
+        // one barrier.
+        for (int rr = 0; rr < prounds; rr += 2) {
+          load_pround(rr + 1, yb);
+          pround(rr, ya);
+          load_pround(rr + 2, ya);
+          pround(rr + 1, yb);
         }
       }
       refine_row();   // (l2s refined before the band is ranked with it)
