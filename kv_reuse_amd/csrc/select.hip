@@ -31,6 +31,7 @@
 //                      (ascending) plus the window is written.
 
 #include <algorithm>
+#include <type_traits>
 
 #include "hs2_internal.h"
 
@@ -2313,20 +2314,66 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
           const uint32_t word = yv[e >> 3][(e >> 1) & 3];
           return (e & 1) ? (word >> 16) : (word & 0xFFFFu);
         };
-        auto pround = [&](int rr, const u32x4 (&ycur)[4]) __attribute__((always_inline)) {
-          const int64_t i0 = kV * (static_cast<int64_t>(tid) + rr * kRowThreads);
-          const int nv = static_cast<int>(min(static_cast<int64_t>(kV), first - i0));
+        // The value at a position known only at run time (each lane its own):
+        // a four-level select over the 16 words, then the half.  The words come
+        // as vector values and every level selects between values (no array:
+        // a select among loads from one would become a load from a selected
+        // address, and the array would go to memory).
+        auto val_pick = [](u32x4 y0, u32x4 y1, u32x4 y2, u32x4 y3, int e) -> uint32_t {
+          // (scalar selects: a two-element vector would want an aligned
+          // register pair, and the words would be copied into pairs)
+          const int w = e >> 1;
+          const bool s0 = w & 1, s1 = w & 2, s2 = w & 4, s3 = w & 8;
+          const uint32_t a00 = s0 ? y0[1] : y0[0], a01 = s0 ? y0[3] : y0[2];
+          const uint32_t a10 = s0 ? y1[1] : y1[0], a11 = s0 ? y1[3] : y1[2];
+          const uint32_t a20 = s0 ? y2[1] : y2[0], a21 = s0 ? y2[3] : y2[2];
+          const uint32_t a30 = s0 ? y3[1] : y3[0], a31 = s0 ? y3[3] : y3[2];
+          const uint32_t b0 = s1 ? a01 : a00, b1 = s1 ? a11 : a10;
+          const uint32_t b2 = s1 ? a21 : a20, b3 = s1 ? a31 : a30;
+          const uint32_t c0 = s2 ? b1 : b0, c1 = s2 ? b3 : b2;
+          const uint32_t word = s3 ? c1 : c0;
+          return __builtin_amdgcn_ubfe(word, static_cast<uint32_t>(e & 1) << 4, 16);
+        };
+        // Bit e set where value e >= T, in packed 16-bit arithmetic: the
+        // saturating difference v - (T - 1), capped at 1, is 1 exactly there
+        // (two packed instructions per word, written out: the compiler would
+        // otherwise turn them into a compare and a select per value).  Word w
+        // gives bits w (its low value) and 16 + w (its high value); an outer
+        // perfect shuffle of the 32 bits then puts value e at bit e.
+        auto mask_ge = [](u32x4 y0, u32x4 y1, u32x4 y2, u32x4 y3, int T) -> uint32_t {
+          const uint32_t t1 = static_cast<uint32_t>(min(max(T, 1), 65536) - 1);
+          const uint32_t tt = t1 | (t1 << 16), one = 0x00010001u;
+          uint32_t p = 0;
+#pragma unroll
+          for (int w = 0; w < 16; ++w) {
+            const uint32_t word = (w < 4 ? y0 : w < 8 ? y1 : w < 12 ? y2 : y3)[w & 3];
+            uint32_t d;
+            asm("v_pk_sub_u16 %0, %1, %2 clamp" : "=v"(d) : "v"(word), "v"(tt));
+            asm("v_pk_min_u16 %0, %1, %2" : "=v"(d) : "v"(d), "v"(one));
+            p |= d << w;
+          }
+          uint32_t t;
+          t = (p ^ (p >> 8)) & 0x0000FF00u;
+          p ^= t ^ (t << 8);
+          t = (p ^ (p >> 4)) & 0x00F000F0u;
+          p ^= t ^ (t << 4);
+          t = (p ^ (p >> 2)) & 0x0C0C0C0Cu;
+          p ^= t ^ (t << 2);
+          t = (p ^ (p >> 1)) & 0x22222222u;
+          p ^= t ^ (t << 1);
+          return T <= 0 ? 0xFFFFFFFFu : (T > 65535 ? 0u : p);
+        };
+        auto pround = [&](auto may_be_first, int rr, const u32x4 (&ycur)[4]) __attribute__((always_inline)) {
+          const int64_t i0 = kV * (static_cast<int64_t>(tid) + static_cast<int64_t>(rr) * kRowThreads);
+          const int nv = static_cast<int>(max(static_cast<int64_t>(0), min(static_cast<int64_t>(kV), first - i0)));
+          const uint32_t valid = nv >= kV ? 0xFFFFFFFFu : ((1u << nv) - 1u);
           // (an LDS atomic read: a volatile one through a generic pointer would
           // be a flat load, and its wait would also wait for the prefetch)
           int fl = __hip_atomic_load(&s_floor, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-          // After the first round the floor sits near the row's k-th value and
-          // most of a thread's kV values lie below everything that counts
-          // (the floor's bin, the list's reach, the dominant value): their
-          // largest, in packed 16-bit maxima, lets the thread skip them all
-          // (exactly: a skipped value would add no count and no list entry).
-          // The maximum is taken in every round: it reads all the round's
-          // registers outside any branch, so that their loads are waited for
-          // here and none is left pending at the loop's head.
+          // the largest of the round's values, in packed 16-bit maxima: it
+          // reads every register of the round outside any branch, so that
+          // their loads are waited for here and none is left pending at the
+          // loop's head; it also tells whether any value reaches vdom
           u16x2 m2{0, 0};
 #pragma unroll
           for (int u = 0; u < 4; ++u)
@@ -2338,15 +2385,17 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
               m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, word));
             }
           const int mx = max(static_cast<int>(m2[0]), static_cast<int>(m2[1]));
-          const bool skip = (rr > 0) & (mx < min((fl << kVBinShift) - E, vdom));
-          if (!skip) {
+          const u32x4 y0 = ycur[0], y1 = ycur[1], y2 = ycur[2], y3 = ycur[3];
+          if (decltype(may_be_first)::value && rr == 0) {
+            // the first round counts every value (the floor starts at bin 0),
+            // then sets the floor before anything is listed
+            if (nv >= kV) {
 #pragma unroll
-            for (int e = 0; e < kV; ++e) {
-              const int bn = static_cast<int>(val_at(ycur, e) >> kVBinShift);
-              if (e < nv && bn >= fl) atomicAdd(&lh[bn], 1u);
+              for (int e = 0; e < kV; ++e) atomicAdd(&lh[val_at(ycur, e) >> kVBinShift], 1u);
+            } else {
+              for (uint32_t m = valid; m; m &= m - 1)
+                atomicAdd(&lh[val_pick(y0, y1, y2, y3, __builtin_ctz(m)) >> kVBinShift], 1u);
             }
-          }
-          if (rr == 0) {
             __syncthreads();
             if (wave == 0) {
               const KthBin kb = kth_bin_wave_n<kPNB>(lh, static_cast<uint32_t>(topk));
@@ -2355,36 +2404,36 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
             __syncthreads();
             fl = s_floor;
           }
+          // the values to list (>= vmin) and the dominant ones (>= vdom); the
+          // histogram's values (bin >= floor) are among the listed ones
           const int vmin = (fl << kVBinShift) - E;
-          uint32_t ml = 0, md = 0;
-          if (!skip) {
-#pragma unroll
-            for (int e = 0; e < kV; ++e) {
-              const int v = static_cast<int>(val_at(ycur, e));
-              ml |= static_cast<uint32_t>(e < nv && v >= vmin) << e;
-              md |= static_cast<uint32_t>(e < nv && v >= vdom) << e;
-            }
-          }
-          for (uint32_t m = md; m; m &= m - 1) list_dom(i0 + __builtin_ctz(m));   // rare
+          const uint32_t ml = mask_ge(y0, y1, y2, y3, vmin) & valid;
+          const uint32_t md = mx >= vdom ? (mask_ge(y0, y1, y2, y3, vdom) & valid) : 0u;
           uint32_t ol, o_dummy, tot, t_dummy;
           block_offsets2<kRowThreads / 64>(__popc(ml), 0u, s_off[rr & 1], ol, o_dummy, tot, t_dummy);
-          // the round's atomics are complete: raise the floor
+          // raise the floor from the counts so far (this round's, counted
+          // below, may be seen in part: any subset of the row's values gives
+          // a k-th bin no higher than the row's own)
           if (wave == 0) {
             const KthBin kb = kth_bin_wave_n<kPNB>(lh, static_cast<uint32_t>(topk));
             if (lane == 0 && kb.found && kb.bstar > fl) atomicMax(&s_floor, kb.bstar);
           }
           ol += n_list;
           n_list += tot;
-          if (ml) {
-#pragma unroll
-            for (int e = 0; e < kV; ++e) {
-              if (!((ml >> e) & 1u)) continue;
+          // each lane walks its own selected values in key order: the wave
+          // takes as many steps as its busiest lane has values, not kV
+          for (uint32_t m = ml | md; m; m &= m - 1) {
+            const int e = __builtin_ctz(m);
+            const uint32_t v = val_pick(y0, y1, y2, y3, e);
+            if ((ml >> e) & 1u) {
+              if (rr > 0 && static_cast<int>(v >> kVBinShift) >= fl) atomicAdd(&lh[v >> kVBinShift], 1u);
               if (ol < static_cast<uint32_t>(kPList)) {
                 lidx[ol] = static_cast<int32_t>(i0 + e);
-                lval[ol] = static_cast<uint16_t>(val_at(ycur, e));
+                lval[ol] = static_cast<uint16_t>(v);
               }
               ++ol;
             }
+            if ((md >> e) & 1u) list_dom(i0 + e);   // rare
           }
         };
         u32x4 ya[4], yb[4];
@@ -2396,9 +2445,9 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
         // one barrier.
         for (int rr = 0; rr < prounds; rr += 2) {
           load_pround(rr + 1, yb);
-          pround(rr, ya);
+          pround(std::true_type{}, rr, ya);
           load_pround(rr + 2, ya);
-          pround(rr + 1, yb);
+          pround(std::false_type{}, rr + 1, yb);
         }
       }
       refine_row();   // (l2s refined before the band is ranked with it)
