@@ -278,8 +278,12 @@ int hs2_kv_bridge(const hs2_bridge_shape* shape, const hs2_bf16* hidden, const h
  *                summed again, [1] heads whose normaliser moved by more than
  *                the selection's error bound allows (expected 0), [2] dominant
  *                keys beyond the per-row list capacity (not summed again;
- *                expected 0).  [3] reserved.  Valid after hs2_cross_decoder_step
- *                (and, in decode, hs2_full_attn_scores).
+ *                expected 0).  [3]: the token-level per-row selection (a
+ *                prefill chunk, or decode with the dense selection), the
+ *                older keys its pass listed as within reach of the band
+ *                (above 8192 the band is found by a second read of the row);
+ *                otherwise 0.  Valid after hs2_cross_decoder_step (and, in
+ *                decode, hs2_full_attn_scores).
  *   HS2_WS_INDEX_CHECK uint32 [B*T*Hkv rows][n_parts]: the sparse layers' index
  *                check.  Summed over a row's n_parts (bytes / (rows * 4)), the
  *                number of the entries idx[row][0..n_sel) that lie outside

@@ -2451,6 +2451,7 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
         }
       }
       refine_row();   // (l2s refined before the band is ranked with it)
+      if (tid == 0) stat[r].pad = n_list;   // (thread 0 also wrote the rest)
       const bool listed = n_list <= static_cast<uint32_t>(kPList);
       if (tid < 128) h256[tid] = 0u;
       __syncthreads();

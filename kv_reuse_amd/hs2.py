@@ -209,7 +209,10 @@ def workspace_refine_stats(s: ShapeArgs, n_sparse_layers: int, ws: torch.Tensor)
     """Per-row statistics of the normaliser's refinement [rows][4] (uint32 as
     int32): dominant units summed again; a count expected 0 (float32 replica
     mismatches, or heads whose normaliser moved beyond the selection's bound);
-    dominant keys beyond the list (expected 0); 0."""
+    dominant keys beyond the list (expected 0); for the token-level per-row
+    selection (a prefill chunk, or decode with the dense selection) the older
+    keys its pass listed (above 8192 a second read of the row finds the band),
+    else 0."""
     off, nb = workspace_region(s, n_sparse_layers, HS2_WS_REFINE)
     return ws[off:off + nb].view(torch.int32).view(s.rows, 4)
 

@@ -126,15 +126,24 @@ def check_index_row(gi: np.ndarray, n: int, ref: dict, what: str, top_k: int, wi
     return len(sym)
 
 
-def check_index_rows_all(idx: np.ndarray, n_sel: np.ndarray, w: wl.Workload):
+def check_index_rows_all(idx: np.ndarray, n_sel: np.ndarray, w: wl.Workload,
+                         refine: np.ndarray = None):
     """Structural checks on every row of a step's index lists (no oracle needed):
     n_sel = min(k, older keys) + window length, the entries strictly ascending and
     inside [0, P_t], the window [P_t - w + 1, P_t] present as the last entries, and
-    -1 past n_sel."""
+    -1 past n_sel.  With a token-level selection's refinement stats, also the
+    count its pass listed: at least min(k, older keys) (every key of the top k
+    is at or above the list's threshold throughout the pass), 0 without older
+    keys."""
     B, T, Hkv, cap = idx.shape
     pos = w.positions()                                       # [T]
     first = np.maximum(0, pos - w.window + 1)
     want_n = np.minimum(w.top_k, first) + (pos - first + 1)   # [T]
+    if refine is not None:
+        listed = refine[:, 3].astype(np.int64).reshape(B, T, Hkv)
+        need = np.broadcast_to(np.minimum(w.top_k, first)[None, :, None], listed.shape)
+        assert np.all(listed >= need), "a row listed fewer keys than its top k"
+        assert np.all(listed[need == 0] == 0), "a row without older keys listed some"
     assert np.array_equal(n_sel, np.broadcast_to(want_n[None, :, None], n_sel.shape)), "n_sel"
     j = np.arange(cap)
     valid = j[None, None, None, :] < n_sel[..., None]

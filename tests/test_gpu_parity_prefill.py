@@ -102,8 +102,9 @@ def test_prefill_4k_over_128k_sampled_rows(hs2):
     x = wl.generate(w)
     gh.log("[prefill] prefill_4k_over_128k: GPU step")
     res = gh.run_step(w, x, with_scores=False)
-    # every row: count, order, window and padding (structure only)
-    gh.check_index_rows_all(res["idx"], res["n_sel"], w)
+    # every row: count, order, window and padding (structure only), and the
+    # count the selection's pass listed
+    gh.check_index_rows_all(res["idx"], res["n_sel"], w, refine=res["refine"])
     # against the oracle: every 16th query token (and the chunk's first and last
     # few) on all four KV heads, about 1,030 rows
     ts = sorted(set(range(0, w.n_q_tokens, 16)) | {1, 15, 2047, 4094, 4095})
