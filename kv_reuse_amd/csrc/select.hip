@@ -2436,6 +2436,45 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
             if ((md >> e) & 1u) list_dom(i0 + e);   // rare
           }
         };
+        // A row of one round (a short row, where a large share of the values
+        // are candidates once the floor is set): fixed loops over the 32
+        // positions, each value read at a fixed place, cost less than the walk.
+        // Every value is counted, the floor set, then the list written; the
+        // count is whole before the k-th bin is read again after the pass.
+        auto pround_single = [&](const u32x4 (&ycur)[4]) {
+          const int64_t i0 = kV * static_cast<int64_t>(tid);
+          const int nv = static_cast<int>(max(static_cast<int64_t>(0), min(static_cast<int64_t>(kV), first - i0)));
+#pragma unroll
+          for (int e = 0; e < kV; ++e)
+            if (e < nv) atomicAdd(&lh[val_at(ycur, e) >> kVBinShift], 1u);
+          __syncthreads();
+          if (wave == 0) {
+            const KthBin kb = kth_bin_wave_n<kPNB>(lh, static_cast<uint32_t>(topk));
+            if (lane == 0 && kb.found) s_floor = kb.bstar;
+          }
+          __syncthreads();
+          const int vmin = (s_floor << kVBinShift) - E;
+          uint32_t ml = 0, md = 0;
+#pragma unroll
+          for (int e = 0; e < kV; ++e) {
+            const int v = static_cast<int>(val_at(ycur, e));
+            ml |= static_cast<uint32_t>(e < nv && v >= vmin) << e;
+            md |= static_cast<uint32_t>(e < nv && v >= vdom) << e;
+          }
+          for (uint32_t m = md; m; m &= m - 1) list_dom(i0 + __builtin_ctz(m));   // rare
+          uint32_t ol, o_dummy, tot, t_dummy;
+          block_offsets2<kRowThreads / 64>(__popc(ml), 0u, s_off[0], ol, o_dummy, tot, t_dummy);
+          n_list = tot;
+#pragma unroll
+          for (int e = 0; e < kV; ++e) {
+            if (!((ml >> e) & 1u)) continue;
+            if (ol < static_cast<uint32_t>(kPList)) {
+              lidx[ol] = static_cast<int32_t>(i0 + e);
+              lval[ol] = static_cast<uint16_t>(val_at(ycur, e));
+            }
+            ++ol;
+          }
+        };
         u32x4 ya[4], yb[4];
         load_pround(0, ya);
         // Two rounds per iteration and no exit between them, so that every
@@ -2443,11 +2482,15 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
         // odd number of rounds the last one lies past the row, reads zeros and
         // counts and lists nothing (every value is masked), at the cost of
         // one barrier.
-        for (int rr = 0; rr < prounds; rr += 2) {
-          load_pround(rr + 1, yb);
-          pround(std::true_type{}, rr, ya);
-          load_pround(rr + 2, ya);
-          pround(std::false_type{}, rr + 1, yb);
+        if (prounds == 1) {
+          pround_single(ya);
+        } else {
+          for (int rr = 0; rr < prounds; rr += 2) {
+            load_pround(rr + 1, yb);
+            pround(std::true_type{}, rr, ya);
+            load_pround(rr + 2, ya);
+            pround(std::false_type{}, rr + 1, yb);
+          }
         }
       }
       refine_row();   // (l2s refined before the band is ranked with it)
