@@ -1593,7 +1593,7 @@ struct KThr {
   uint32_t nd_t;
   bool incl;
 };
-__device__ KThr key_threshold(const uint64_t* keys, uint32_t n, uint32_t need, uint32_t* h256,
+__device__ __forceinline__ KThr key_threshold(const uint64_t* keys, uint32_t n, uint32_t need, uint32_t* h256,
                               uint32_t* s_red, uint64_t* s_hi, uint32_t* s_need, int* s_done) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1709,7 +1709,7 @@ __device__ __forceinline__ uint32_t lower_bound_lds(const int32_t* a, uint32_t n
 // `take`, ascending, to win (at most win_cap of them); ties go to the earlier
 // entry.  Returns how many won.  The band is only read.  All kRowThreads
 // threads call it.
-__device__ uint32_t rank_band(const uint64_t* bk, const int32_t* bi, uint32_t n_band,
+__device__ __forceinline__ uint32_t rank_band(const uint64_t* bk, const int32_t* bi, uint32_t n_band,
                               uint32_t take, int32_t* win, uint32_t win_cap, uint32_t* s_count,
                               uint32_t* h256, uint32_t* s_red, uint64_t* s_hi, uint32_t* s_need,
                               int* s_done, uint32_t (*s_cnt)[16], uint32_t* s_base) {
@@ -2534,8 +2534,6 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
         int32_t* gbi = band_idx + static_cast<size_t>(r) * band_cap;
         uint64_t* gbk = band_key + static_cast<size_t>(r) * band_cap;
         bool band_lds = false, band_glob = false;
-        int32_t* bi = gbi;
-        uint64_t* bk = gbk;
         uint32_t cu = 0, ca = 0;
         if (listed) {
           // ---- split the list: each thread takes kPListPer consecutive
@@ -2558,8 +2556,6 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
           block_offsets2<kRowThreads / 64>(__popc(mu), __popc(ma), s_off[0], ou, oa, cu, ca);
           band_lds = ca <= static_cast<uint32_t>(kUncCap);
           band_glob = !band_lds && ca <= static_cast<uint64_t>(band_cap);
-          bi = band_lds ? lbi : gbi;
-          bk = band_lds ? lbk : gbk;
 #pragma unroll
           for (int j = 0; j < kPListPer; ++j) {
             if ((mu >> j) & 1u) {
@@ -2567,7 +2563,8 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
               ++ou;
             }
             if ((ma >> j) & 1u) {
-              if (band_lds || band_glob) bi[oa] = li[j];
+              if (band_lds) lbi[oa] = li[j];
+              else if (band_glob) gbi[oa] = li[j];
               ++oa;
             }
           }
@@ -2610,17 +2607,22 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
         const uint32_t n_up = min(cu, static_cast<uint32_t>(topk));
         const uint32_t take = static_cast<uint32_t>(topk) - n_up;
         uint32_t n_w = 0;
-        if (band_lds || band_glob) {
-          const uint32_t n_band = min(ca, band_lds ? static_cast<uint32_t>(kUncCap)
-                                                   : static_cast<uint32_t>(band_cap));
-          // ---- exact importance of the band keys
+        // ---- exact importance of the band keys, then their ranking: one copy
+        // for a band in LDS and one for a band in global memory, so that each
+        // access has a known memory (a pointer to either would be a flat one)
+        auto band_rank = [&](int32_t* bi_, uint64_t* bk_, uint32_t n_band) -> uint32_t {
           for (uint32_t i = static_cast<uint32_t>(tid) >> 4; i < n_band; i += kRowThreads / 16) {
-            const double yy = exact_importance(bi[i], tid & 15);
-            if ((tid & 15) == 0) bk[i] = ordered_u64(yy);
+            const double yy = exact_importance(bi_[i], tid & 15);
+            if ((tid & 15) == 0) bk_[i] = ordered_u64(yy);
           }
           __syncthreads();
-          n_w = rank_band(bk, bi, n_band, take, bw, kMaxSel, &s_count, h256, s_red, &s_hi,
-                          &s_need, &s_done, s_cnt, s_base);
+          return rank_band(bk_, bi_, n_band, take, bw, kMaxSel, &s_count, h256, s_red, &s_hi,
+                           &s_need, &s_done, s_cnt, s_base);
+        };
+        if (band_lds) {
+          n_w = band_rank(lbi, lbk, min(ca, static_cast<uint32_t>(kUncCap)));
+        } else if (band_glob) {
+          n_w = band_rank(gbi, gbk, min(ca, static_cast<uint32_t>(band_cap)));
         } else if (take > 0) {
           // the band is too large to list: rank it by its stored importance
           // (unordered winners, then sorted)
