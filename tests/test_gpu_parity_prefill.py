@@ -36,6 +36,14 @@ SMALL = [
     ("chunk_17_drift", dict(batch=2, n_q_tokens=17, n_q_heads=8, n_kv_heads=1, ctx_len=3001,
                             n_sparse_layers=1, top_k=64, window=16, drift_sd=0.05,
                             n_needles=5, config_id=35)),
+    # rows of three and of five rounds of the selection's pass (16,384 older
+    # keys a round): an odd count above one, whose last round runs beside one
+    # past the row, and a ragged last round
+    ("chunk_6_over_40000", dict(batch=1, n_q_tokens=6, n_q_heads=8, n_kv_heads=1, ctx_len=40000,
+                                n_sparse_layers=1, top_k=512, window=64, n_needles=3,
+                                config_id=61)),
+    ("chunk_3_over_70000", dict(batch=1, n_q_tokens=3, n_q_heads=8, n_kv_heads=1, ctx_len=70000,
+                                n_sparse_layers=1, top_k=2048, window=256, config_id=62)),
 ]
 
 
@@ -49,12 +57,15 @@ def test_prefill_small(hs2, name, kw):
     gh.log(f"  {st}")
 
 
-@pytest.mark.parametrize("ctx,T", [(900, 24), (7000, 8), (9500, 6)],
-                         ids=["listed", "list_overflow_band_in_memory", "list_overflow_band_by_f16"])
+@pytest.mark.parametrize("ctx,T", [(900, 24), (7000, 8), (9500, 6), (20000, 3)],
+                         ids=["listed", "band_in_memory", "list_overflow_band_by_f16",
+                              "two_rounds_list_overflow"])
 def test_prefill_identical_keys(hs2, ctx, T):
     # every key the same: all importances of a row tie, the lowest indices win.
-    # Past 6144 older keys the tie overflows the selection's LDS list (a second
-    # pass over the importance); past 8192 the band is ranked by its float16 value.
+    # Past 2048 older keys the tied band leaves LDS for global memory; past 8192
+    # it also overflows the selection's LDS list (a second read of the row) and
+    # is ranked by its stored value.  At 20000 the pass takes two rounds, every
+    # value of the second a candidate.
     w = wl.small(name="ties", batch=1, n_q_tokens=T, n_q_heads=8, n_kv_heads=1, ctx_len=ctx,
                  n_sparse_layers=1, top_k=50, window=10, config_id=36)
     gh.log(f"[prefill] identical keys S={ctx} T={T}")
