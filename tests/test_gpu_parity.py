@@ -40,6 +40,9 @@ SMALL = [
                    top_k=4, window=2, config_id=17)),
     ("ten_layers", dict(batch=1, n_q_heads=8, n_kv_heads=1, ctx_len=700, n_sparse_layers=10,
                         top_k=50, window=20, config_id=18)),
+    # three rounds of the dense path's per-row pass (16,384 older keys a round)
+    ("mid_35000", dict(batch=1, n_q_heads=8, n_kv_heads=1, ctx_len=35000, n_sparse_layers=1,
+                       top_k=256, window=32, config_id=63)),
 ]
 
 
