@@ -2195,57 +2195,64 @@ __global__ __launch_bounds__(kRowThreads, 2) void prefill_select_kernel(
         // the band fits LDS or the row's global band list (the plan gives
         // block selection a list of at least one entry per block)
         const bool band_lds = ca <= static_cast<uint32_t>(kBandBlk);
-        int32_t* bi = band_lds ? lbi_b : band_idx + static_cast<size_t>(r) * band_cap;
-        uint64_t* bk = band_lds ? lbk_b : band_key + static_cast<size_t>(r) * band_cap;
         const uint32_t bcap = band_lds ? static_cast<uint32_t>(kBandBlk)
                                        : static_cast<uint32_t>(min(band_cap, static_cast<int64_t>(nblk)));
         for (uint32_t m = mu; m; m &= m - 1) {
           if (ou < static_cast<uint32_t>(kMaxSelBlocks)) up[ou] = c0 + __builtin_ctz(m);
           ++ou;
         }
-        for (uint32_t m = ma; m; m &= m - 1) {
-          if (oa < bcap) bi[oa] = c0 + __builtin_ctz(m);
-          ++oa;
-        }
-        __syncthreads();
         const uint32_t n_up = min(cu, static_cast<uint32_t>(n_take));
         const uint32_t take = static_cast<uint32_t>(n_take) - n_up;
         const uint32_t n_band = min(ca, bcap);
-        // ---- each band block's exact importance, a wave per block: its
-        // tokens stored at or above (block value) - E, four at a time (16
-        // lanes each), the largest key over the wave
-        const int part = lane & 15, grp = lane >> 4;
-        for (uint32_t i = wave; i < n_band; i += kRowThreads / 64) {
-          const int blk = bi[i];
-          const int64_t j0 = static_cast<int64_t>(blk) << bs_log2;
-          const int64_t j1 = min(first, j0 + bs);
-          const int thr = static_cast<int>(bmx[blk]) - E;
-          uint64_t best = 0ull;
-          for (int64_t jb = j0; jb < j1; jb += 64) {
-            const int64_t j = jb + lane;
-            uint64_t m = __ballot(j < j1 && static_cast<int>(yr[min(j, j1 - 1)]) >= thr);
-            while (m) {
-              uint64_t mg = m;   // this group's candidate: the grp-th of m
-              for (int s = 0; s < grp; ++s) mg &= mg - 1;
-              const int64_t key = jb + __builtin_ctzll(mg ? mg : m);
-              const double yy = exact_importance(key, part);
-              if (mg) best = max(best, ordered_u64(yy));
+        // the band's blocks, their exact importance and their ranking: one copy
+        // for a band in LDS and one for a band in global memory, so that each
+        // access has a known memory (a pointer to either would be a flat one)
+        auto band_blocks = [&](int32_t* bi, uint64_t* bk) -> uint32_t {
+          for (uint32_t m = ma, o = oa; m; m &= m - 1) {
+            if (o < bcap) bi[o] = c0 + __builtin_ctz(m);
+            ++o;
+          }
+          __syncthreads();
+          // ---- each band block's exact importance, a wave per block: its
+          // tokens stored at or above (block value) - E, four at a time (16
+          // lanes each), the largest key over the wave
+          const int part = lane & 15, grp = lane >> 4;
+          for (uint32_t i = wave; i < n_band; i += kRowThreads / 64) {
+            const int blk = bi[i];
+            const int64_t j0 = static_cast<int64_t>(blk) << bs_log2;
+            const int64_t j1 = min(first, j0 + bs);
+            const int thr = static_cast<int>(bmx[blk]) - E;
+            uint64_t best = 0ull;
+            for (int64_t jb = j0; jb < j1; jb += 64) {
+              const int64_t j = jb + lane;
+              uint64_t m = __ballot(j < j1 && static_cast<int>(yr[min(j, j1 - 1)]) >= thr);
+              while (m) {
+                uint64_t mg = m;   // this group's candidate: the grp-th of m
+                for (int s = 0; s < grp; ++s) mg &= mg - 1;
+                const int64_t key = jb + __builtin_ctzll(mg ? mg : m);
+                const double yy = exact_importance(key, part);
+                if (mg) best = max(best, ordered_u64(yy));
 #pragma unroll
-              for (int s = 0; s < 4; ++s) m &= m - 1;
+                for (int s = 0; s < 4; ++s) m &= m - 1;
+              }
             }
-          }
 #pragma unroll
-          for (int off = 32; off > 0; off >>= 1) {
-            const uint64_t o = (static_cast<uint64_t>(static_cast<uint32_t>(
-                                    __shfl_xor(static_cast<int>(best >> 32), off))) << 32) |
-                               static_cast<uint32_t>(__shfl_xor(static_cast<int>(best), off));
-            best = max(best, o);
+            for (int off = 32; off > 0; off >>= 1) {
+              const uint64_t o = (static_cast<uint64_t>(static_cast<uint32_t>(
+                                      __shfl_xor(static_cast<int>(best >> 32), off))) << 32) |
+                                 static_cast<uint32_t>(__shfl_xor(static_cast<int>(best), off));
+              best = max(best, o);
+            }
+            if (lane == 0) bk[i] = best;
           }
-          if (lane == 0) bk[i] = best;
-        }
-        __syncthreads();
-        const uint32_t n_w = rank_band(bk, bi, n_band, take, bwin, kMaxSelBlocks, &s_count, h256,
-                                       s_red, &s_hi, &s_need, &s_done, s_cnt, s_base);
+          __syncthreads();
+          return rank_band(bk, bi, n_band, take, bwin, kMaxSelBlocks, &s_count, h256, s_red,
+                           &s_hi, &s_need, &s_done, s_cnt, s_base);
+        };
+        const uint32_t n_w = band_lds
+                                 ? band_blocks(lbi_b, lbk_b)
+                                 : band_blocks(band_idx + static_cast<size_t>(r) * band_cap,
+                                               band_key + static_cast<size_t>(r) * band_cap);
         __syncthreads();
         // ---- merge the two ascending block lists by rank
         for (uint32_t i = tid; i < n_up; i += kRowThreads) {
